@@ -1,0 +1,317 @@
+"""CPU oracle for the MoE routing front-end (test infrastructure only).
+
+This module is test infrastructure. Only the tests, the smoke check and the
+CPU-baseline leg of the benchmark may import it. The product path (the HIP
+library and its Python binding) never calls it, and it shares no code with
+that path: no kernels, helpers, tables or constant generators. Both sides are
+fed from the seeded generators in ``router_gemv_top_amd.inputs``, which hold
+none of the method's arithmetic.
+
+It is deliberately plain and slow: fp64 arithmetic, library primitives
+(matmul, argmax, stable argsort) used as whole steps, no blocking or fusion.
+
+Sources (titles of the pages this follows):
+  [GEMV]  "MiniMax-M3: Triton split-K router GEMV with in-kernel split-K fixup"
+          (sglang PR #36557), opening summary: logits[M,N] fp32 =
+          x[M,K] bf16 . W[N,K]^T bf16.
+  [M31K]  MiniMax-M3.1-Flash MoE/GEMM kernels (sglang PR #46691), Summary
+          (router, MoE sorting + quant) and "Changes to existing kernels"
+          (fp64 accuracy and determinism test of the router).
+  [K3]    "Kimi-K3: fused MoE routing, sort, quant and epilogue"
+          (sglang PR #46652), Modifications and the review snippet on the
+          stable rank (a pair's rank counts earlier tokens on the same expert).
+  [MONO]  "minimax_m31: Run MiniMax-M3.1-Flash's decode FFN as one monokernel
+          launch a layer" (sgl-amd-mono PR #56), the MXFP8 shared-expert
+          commit (group-32 scales).
+  [OCP]   OCP Microscaling Formats (MX) v1.0: e4m3 element format (bias 7,
+          max normal 448, no infinities), e8m0 shared scale (bias 127), shared
+          exponent = floor(log2(amax)) - emax_elem with emax_elem = 8 for e4m3.
+
+Readings taken where the pages are silent (each is listed in the design
+notes):
+  * Gate scores: s = fp32(L + bias) when a bias is given, else s = L.
+  * Top-k order: score descending, expert index ascending on ties; -0 == +0.
+  * Weights: w_j = exp(s_j - s_0) / sum_{i<k} exp(s_i - s_0), i.e. full
+    softmax then renormalisation over the selected k, evaluated by one written
+    fp64 recipe (``exp64`` below) so that a second implementation can match it
+    bit for bit.
+  * Sort: pair id p = m*k + j; segments by ascending expert, pairs inside a
+    segment in ascending p, each segment padded up to a multiple of the block
+    size with the sentinel P = M*k; empty experts get no block.
+  * MXFP8: OCP floor rule for the shared exponent, round to nearest even,
+    saturation to +-448, sign kept (so -0 encodes as 0x80).
+
+Parity pins: every function here is checked by the ``-m "not gpu"`` tests
+against brute force, exact rationals, closed forms or invariants.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# bf16 helpers
+# ---------------------------------------------------------------------------
+
+
+def bf16_bits_to_f64(h: np.ndarray) -> np.ndarray:
+    """Exact value of bf16 bit patterns as fp64."""
+    u = np.asarray(h, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Router logits [GEMV]
+# ---------------------------------------------------------------------------
+
+
+def router_logits(x_bits: np.ndarray, w_bits: np.ndarray) -> np.ndarray:
+    """logits[m][n] = fp32( sum_i x[m][i] * W[n][i] ), summed in fp64.
+
+    [GEMV] opening summary: the router gate is [M,K] bf16 x [N,K] bf16 ->
+    [M,N] fp32. Products of two bf16 values are exact in fp64; the fp64 sum
+    (a library matmul) is then rounded once, to nearest even, to fp32. The
+    fp64 accumulation error is far below one fp32 ulp of any logit that
+    matters for the tolerance used against the GPU. [M31K] names an fp64
+    accuracy test for the router; this is that reference.
+    """
+    x = bf16_bits_to_f64(x_bits)
+    w = bf16_bits_to_f64(w_bits)
+    assert np.all(np.isfinite(x)) and np.all(np.isfinite(w))
+    return (x @ w.T).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Softmax top-k gate (reading: softmax, top-k, renormalise)
+# ---------------------------------------------------------------------------
+
+
+def gate_scores(logits: np.ndarray, bias: np.ndarray | None) -> np.ndarray:
+    """s = fp32(L + bias) (one IEEE fp32 add per element) or s = L."""
+    s = np.asarray(logits, dtype=np.float32)
+    if bias is not None:
+        s = (s + np.asarray(bias, dtype=np.float32)[None, :]).astype(np.float32)
+    assert np.all(np.isfinite(s)), "scores must be finite"
+    return s
+
+
+def topk_ids(scores: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest scores per row, largest first.
+
+    Order key: score descending, then expert index ascending; -0 and +0 are
+    equal (IEEE compare). Selection by k rounds of "first index of the
+    maximum" over the experts not yet chosen.
+    """
+    s = np.asarray(scores, dtype=np.float32)
+    s = np.where(s == 0, np.float32(0), s)  # -0 -> +0, so they tie
+    m, n = s.shape
+    assert 1 <= k <= n
+    taken = np.zeros((m, n), dtype=bool)
+    out = np.empty((m, k), dtype=np.int32)
+    rows = np.arange(m)
+    for j in range(k):
+        masked = np.where(taken, -np.inf, s.astype(np.float64))
+        idx = np.argmax(masked, axis=1)  # first occurrence -> lowest index on ties
+        out[:, j] = idx
+        taken[rows, idx] = True
+    return out
+
+
+# exp64 recipe constants. Each is the fp64 number nearest to the stated
+# mathematical value, except LN2_HI, which is ln 2 cut to 24 significant bits
+# so that n * LN2_HI is exact for |n| < 2**29 (Cody & Waite range reduction).
+LOG2E = float.fromhex("0x1.71547652b82fep+0")      # 1/ln 2
+LN2_HI = float.fromhex("0x1.62e42e0000000p-1")     # ln 2, 24 bits
+LN2_LO = float.fromhex("0x1.efa39ef35793cp-25")    # ln 2 - LN2_HI
+INV_FACT = [float.fromhex(h) for h in (             # 1/j!, j = 0..13
+    "0x1.0000000000000p+0", "0x1.0000000000000p+0", "0x1.0000000000000p-1",
+    "0x1.5555555555555p-3", "0x1.5555555555555p-5", "0x1.1111111111111p-7",
+    "0x1.6c16c16c16c17p-10", "0x1.a01a01a01a01ap-13", "0x1.a01a01a01a01ap-16",
+    "0x1.71de3a556c734p-19", "0x1.27e4fb7789f5cp-22", "0x1.ae64567f544e4p-26",
+    "0x1.1eed8eff8d898p-29", "0x1.6124613a86d09p-33")]
+EXP64_CUTOFF = -200.0  # exp(d) for d < -200 is returned as 0 (w rounds to 0 in fp32 anyway)
+
+
+def exp64(d: np.ndarray) -> np.ndarray:
+    """exp(d) for d <= 0 in fp64 by a fixed sequence of IEEE operations.
+
+    1. n = rint(d * LOG2E)                    (round half to even)
+    2. r = (d - n * LN2_HI) - n * LN2_LO      (Cody-Waite reduction, |r| <= ln2/2)
+    3. p = sum_{j=0}^{13} r^j / j!            (Horner; each step one multiply,
+                                               then one add, no fused multiply-add)
+    4. e = p * 2^n                            (exact scaling)
+    d < -200 gives 0. Truncation error of the degree-13 polynomial is below
+    2^-57 relative on |r| <= ln2/2; the whole recipe is within a few fp64 ulp
+    of exp(d).
+    """
+    d = np.asarray(d, dtype=np.float64)
+    n = np.rint(d * LOG2E)
+    r = (d - n * LN2_HI) - n * LN2_LO
+    p = np.full_like(d, INV_FACT[13])
+    for j in range(12, -1, -1):
+        p = p * r
+        p = p + INV_FACT[j]
+    n_int = np.where(d < EXP64_CUTOFF, 0, n).astype(np.int64)
+    e = np.ldexp(p, n_int)
+    return np.where(d < EXP64_CUTOFF, 0.0, e)
+
+
+def topk_weights(sel_scores: np.ndarray) -> np.ndarray:
+    """Renormalised softmax weights of the selected scores (slot 0 = largest).
+
+    w_j = exp(s_j - s_0) / sum_{i<k} exp(s_i - s_0). Equal to taking the full
+    softmax over all N experts and dividing the k selected probabilities by
+    their sum, since the common factor cancels. fp64 throughout: the
+    differences, exp64, the sum in slot order, the division; one RNE rounding
+    to fp32 at the end.
+    """
+    s = np.asarray(sel_scores, dtype=np.float32).astype(np.float64)
+    d = s - s[:, :1]
+    e = exp64(d)
+    total = e[:, 0].copy()
+    for j in range(1, e.shape[1]):
+        total = total + e[:, j]
+    return (e / total[:, None]).astype(np.float32)
+
+
+def topk_gate(logits: np.ndarray, bias: np.ndarray | None, k: int):
+    """(ids int32 [M][k], w fp32 [M][k]) of the softmax top-k gate."""
+    s = gate_scores(logits, bias)
+    ids = topk_ids(s, k)
+    sel = np.take_along_axis(s, ids.astype(np.int64), axis=1)
+    return ids, topk_weights(sel)
+
+
+# ---------------------------------------------------------------------------
+# Token -> expert sort [M31K, K3]
+# ---------------------------------------------------------------------------
+
+
+def sort_capacity(m: int, n: int, k: int, block: int) -> int:
+    """Upper bound on the padded total: P + min(N, P)*(B-1), rounded up to B."""
+    p = m * k
+    cap = p + min(n, p) * (block - 1)
+    return (cap + block - 1) // block * block
+
+
+def moe_sort(ids: np.ndarray, n: int, block: int):
+    """Counting sort of (token, slot) pairs into block-padded expert segments.
+
+    Returns (sorted_ids int32 [total], expert_ids int32 [total/B],
+    offsets int32 [N+1], total). Pair p = m*k + j goes to expert ids[m][j].
+    Segment e starts at offsets[e] and holds cnt[e] pair ids in ascending p
+    (the stable rank of [K3]: earlier tokens on the same expert come first),
+    then the sentinel P = M*k up to the next multiple of B.
+    """
+    ids = np.asarray(ids, dtype=np.int64)
+    m, k = ids.shape
+    p_total = m * k
+    e_of_pair = ids.reshape(-1)
+    assert np.all((e_of_pair >= 0) & (e_of_pair < n))
+    cnt = np.bincount(e_of_pair, minlength=n)
+    padded = (cnt + block - 1) // block * block
+    offsets = np.zeros(n + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(padded)
+    total = int(offsets[n])
+    sorted_ids = np.full(total, p_total, dtype=np.int32)
+    order = np.argsort(e_of_pair, kind="stable")  # by expert, ascending p inside
+    start = 0
+    for e in range(n):
+        c = int(cnt[e])
+        sorted_ids[offsets[e]:offsets[e] + c] = order[start:start + c]
+        start += c
+    expert_ids = np.repeat(np.arange(n, dtype=np.int32), padded // block)
+    return sorted_ids, expert_ids, offsets.astype(np.int32), total
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 quantisation [OCP], [MONO] group-32 scales
+# ---------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+E4M3_EMAX = 8          # floor(log2(448))
+MX_BLOCK = 32
+
+
+def e4m3_code(y: np.ndarray, neg: np.ndarray) -> np.ndarray:
+    """e4m3fn code of |y| (fp64, >= 0, exact) with the given sign.
+
+    Round to nearest, ties to even, over normals (3 mantissa bits, exponent
+    >= -6) and subnormals (step 2^-9); magnitudes above 448 saturate to 448.
+    """
+    a = np.asarray(y, dtype=np.float64)
+    _, ex = np.frexp(a)                        # a = f * 2^ex, f in [0.5, 1)
+    binade = np.maximum(ex - 1, -6)            # floor(log2 a), at least -6
+    qexp = binade - 3                          # spacing of representable values
+    units = np.rint(np.ldexp(a, -qexp))        # RNE to a multiple of the spacing
+    val = np.ldexp(units, qexp)
+    val = np.where(a > E4M3_MAX, E4M3_MAX, val)
+    val = np.minimum(val, E4M3_MAX)
+    # encode the (now representable) magnitude
+    _, vex = np.frexp(val)
+    vb = vex - 1
+    is_norm = (val > 0) & (vb >= -6)
+    mant_norm = np.ldexp(val, -(vb - 3)) - 8.0          # 0..7
+    code_norm = ((vb + 7) << 3) + mant_norm.astype(np.int64)
+    code_sub = np.ldexp(val, 9).astype(np.int64)        # 0..7 (0 for zero)
+    code = np.where(is_norm, code_norm, code_sub).astype(np.int64)
+    code = code | (np.asarray(neg, dtype=np.int64) << 7)
+    return code.astype(np.uint8)
+
+
+def mxfp8_quant_rows(x_bits: np.ndarray):
+    """MXFP8 of bf16 rows: (codes u8 [R][K], scales u8 [R][K/32]).
+
+    Per 32-element block: amax = max |v|; E = floor(log2 amax) (exact, from the
+    binary exponent); shared exponent se = clamp(E - 8, -127, 127) (0 scale
+    byte when amax = 0); scale byte = se + 127 (e8m0); element code =
+    e4m3(v / 2^se).
+    """
+    h = np.asarray(x_bits, dtype=np.uint16)
+    r, k = h.shape
+    assert k % MX_BLOCK == 0
+    v = bf16_bits_to_f64(h).reshape(r, k // MX_BLOCK, MX_BLOCK)
+    neg = ((h >> np.uint16(15)) & np.uint16(1)).reshape(v.shape).astype(bool)
+    av = np.abs(v)
+    amax = av.max(axis=2)
+    _, ex = np.frexp(amax)
+    e_floor = ex - 1
+    se = np.where(amax > 0, np.clip(e_floor - E4M3_EMAX, -127, 127), -127).astype(np.int64)
+    scale = (se + 127).astype(np.uint8)
+    y = np.ldexp(av, -se[:, :, None])          # exact: power-of-two scaling
+    codes = e4m3_code(y, neg)
+    return codes.reshape(r, k), scale
+
+
+def moe_sort_quant(ids: np.ndarray, x_bits: np.ndarray, n: int, block: int,
+                   rows_per_chunk: int = 2048):
+    """Sort pairs into padded expert segments and MXFP8-quantise gathered rows.
+
+    Returns dict with sorted_ids, expert_ids, offsets, total, a_q [total][K]
+    (pad rows zero and marked invalid), a_scale [total][K/32], valid [total].
+    Row p (valid) holds the quantised activations of token sorted_ids[p] // k.
+    """
+    ids = np.asarray(ids)
+    m, k = ids.shape
+    sorted_ids, expert_ids, offsets, total = moe_sort(ids, n, block)
+    kdim = x_bits.shape[1]
+    valid = sorted_ids != m * k
+    a_q = np.zeros((total, kdim), dtype=np.uint8)
+    a_scale = np.zeros((total, kdim // MX_BLOCK), dtype=np.uint8)
+    pos = np.nonzero(valid)[0]
+    for c in range(0, len(pos), rows_per_chunk):
+        pc = pos[c:c + rows_per_chunk]
+        tok = sorted_ids[pc] // k
+        q, s = mxfp8_quant_rows(x_bits[tok])
+        a_q[pc] = q
+        a_scale[pc] = s
+    return dict(sorted_ids=sorted_ids, expert_ids=expert_ids, offsets=offsets,
+                total=total, a_q=a_q, a_scale=a_scale, valid=valid)
+
+
+def route_sort_quant(x_bits, w_bits, bias, k: int, block: int):
+    """The whole front-end chained: logits -> gate -> sort -> MXFP8 quant."""
+    logits = router_logits(x_bits, w_bits)
+    ids, w = topk_gate(logits, bias, k)
+    out = moe_sort_quant(ids, x_bits, w_bits.shape[0], block)
+    out.update(logits=logits, topk_ids=ids, topk_w=w)
+    return out

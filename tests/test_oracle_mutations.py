@@ -1,0 +1,111 @@
+"""The oracle's pins catch plausible mistakes (CPU only).
+
+Each case plants one mistake in a copy of an oracle function (a dropped term,
+a transposed operand, a wrong tie-break, a missing renormalisation, an
+unstable sort, the wrong rounding) and checks that the pin written for that
+function rejects it. The real oracle is never modified.
+"""
+import json
+import os
+
+import numpy as np
+
+from oracle import rgt_oracle as O
+from router_gemv_top_amd.inputs import f32_to_bf16_bits
+
+import test_oracle_gate as G
+import test_oracle_quant as Q
+import test_oracle_sort as S
+
+
+def test_dropped_term_in_logits_is_caught():
+    rng = np.random.default_rng(21)
+    xi, wi = rng.integers(-2, 3, (3, 64)), rng.integers(-2, 3, (4, 64))
+    x, w = f32_to_bf16_bits(xi.astype(np.float32)), f32_to_bf16_bits(wi.astype(np.float32))
+
+    def mutant(xb, wb):
+        return O.router_logits(xb[:, :-1], wb[:, :-1])
+
+    want = (xi @ wi.T).astype(np.float32)
+    assert np.array_equal(O.router_logits(x, w), want)
+    assert not np.array_equal(mutant(x, w), want)
+
+
+def test_transposed_weight_is_caught():
+    x = f32_to_bf16_bits(np.array([[1, 0, 0], [0, 0, 2]], np.float32))
+    w = f32_to_bf16_bits(np.array([[3, 5, 7], [11, 13, 17], [19, 23, 29]], np.float32))
+    good = O.router_logits(x, w)
+
+    def mutant(xb, wb):
+        return O.router_logits(xb, wb.T.copy())
+
+    assert not np.array_equal(mutant(x, w), good)
+
+
+def test_last_index_tie_break_is_caught():
+    def mutant(s, k):
+        r = O.topk_ids(s[:, ::-1].copy(), k)
+        return s.shape[1] - 1 - r
+
+    s = np.array([[1.0, 2.0, 2.0, 0.0, 2.0]], np.float32)
+    assert O.topk_ids(s, 2)[0].tolist() == G.brute_topk(s[0], 2)
+    assert mutant(s, 2)[0].tolist() != G.brute_topk(s[0], 2)
+
+
+def test_missing_renormalisation_is_caught():
+    s_full = np.array([[2.0, 1.5, 0.25, -1.0, -3.0]], np.float32)
+    sel = s_full[:, :2]
+
+    def mutant(sel_scores):  # softmax over all experts, not renormalised over the k
+        e = np.exp(s_full.astype(np.float64) - s_full[:, :1])
+        return (e[:, :sel_scores.shape[1]] / e.sum(axis=1, keepdims=True)).astype(np.float32)
+
+    ex = G.exact_weights(sel[0])
+    got = mutant(sel)
+    assert any(abs(float(got[0, j]) - float(ex[j])) > 1e-3 for j in range(2))
+    good = O.topk_weights(sel)
+    assert all(abs(float(good[0, j]) - float(ex[j])) < 1e-7 for j in range(2))
+
+
+def test_unstable_sort_is_caught():
+    ids = np.array([[0, 1], [1, 0], [0, 2]], np.int32)
+
+    def mutant(i, n, b):
+        s, e, off, t = O.moe_sort(i, n, b)
+        p = i.size
+        for ex in range(n):
+            seg = s[off[ex]:off[ex + 1]]
+            real = seg[seg != p][::-1]
+            s[off[ex]:off[ex] + len(real)] = real
+        return s, e, off, t
+
+    want = S.nested_loop_sort(ids, 3, 2)[0]
+    assert O.moe_sort(ids, 3, 2)[0].tolist() == want
+    assert mutant(ids, 3, 2)[0].tolist() != want
+
+
+def test_round_half_away_is_caught():
+    def mutant(y, neg):
+        a = np.asarray(y, np.float64)
+        _, ex = np.frexp(a)
+        qexp = np.maximum(ex - 1, -6) - 3
+        units = np.floor(np.ldexp(a, -qexp) + 0.5)   # half away from zero
+        return O.e4m3_code(np.ldexp(units, qexp), neg)
+
+    h = Q.all_finite_bf16()
+    v = Q.bf16_bits_to_f32(h).astype(np.float64)
+    y = np.abs(v)
+    neg = (h >> 15).astype(bool)
+    want = Q.table_nearest(y) | (neg.astype(np.int64) << 7)
+    assert np.array_equal(O.e4m3_code(y, neg).astype(np.int64), want)
+    assert not np.array_equal(mutant(y, neg).astype(np.int64), want)
+
+
+def test_ceil_scale_rule_is_caught():
+    with open(os.path.join(Q.GOLDEN, "mxfp8_hand_cases.json")) as f:
+        case = [c for c in json.load(f)["blocks"] if c["name"] == "saturation"][0]
+    vals = np.zeros(32, np.float32)
+    vals[:len(case["x"])] = [float.fromhex(s) for s in case["x"]]
+    amax = np.abs(vals).max()
+    se_ceil = int(np.ceil(np.log2(amax / 448.0)))   # the non-saturating rule
+    assert se_ceil + 127 != int(case["scale"], 16)
