@@ -1,0 +1,168 @@
+/*
+ * rgt.h - C ABI of the MI355X (gfx950) MoE routing front-end.
+ *
+ * The library computes, on one GPU:
+ *   1. router logits   logits[M][N] fp32 = x[M][K] bf16 . W[N][K]^T bf16,
+ *      as a split-K GEMV whose split-K reduction is finished inside the same
+ *      launch by the last workgroup to arrive at each output tile, which then
+ *      resets its arrival counter ("MiniMax-M3: Triton split-K router GEMV with
+ *      in-kernel split-K fixup", sglang PR #36557, opening summary);
+ *   2. a softmax top-k gate with renormalised weights (the gate of the
+ *      MiniMax-M3.1-Flash MoE/GEMM kernels page, sglang PR #46691, Summary:
+ *      Router; the routing step of "Kimi-K3: fused MoE routing, sort, quant
+ *      and epilogue", sglang PR #46652, Modifications);
+ *   3. the token -> expert sort into block-padded expert segments
+ *      (sglang PR #46691, Summary: MoE sorting + quant; sglang PR #46652,
+ *      review snippet: a pair's rank counts pairs of earlier tokens on the
+ *      same expert);
+ *   4. MXFP8 quantisation of the gathered activations: e4m3 codes plus one
+ *      e8m0 scale per 32 elements (OCP Microscaling Formats v1.0; group-32
+ *      scales as in the MXFP8 shared-expert commit of sgl-amd-mono PR #56).
+ *
+ * Conventions shared by every entry point
+ *   - All data pointers are DEVICE pointers owned by the caller. The library
+ *     never allocates device memory and never synchronises the stream, except
+ *     rgt_check_workspace, which synchronises to read the error word.
+ *   - bf16 tensors are passed as const void* holding IEEE bf16 bit patterns.
+ *     x is row-major [M][ldx] with the K used elements of each row contiguous;
+ *     W is row-major [N][ldw]. ldx, ldw count elements and must be >= K and
+ *     multiples of 8 (16-byte aligned rows).
+ *   - Every entry point is asynchronous on `stream` (0 = the null stream).
+ *   - The workspace is caller-owned device memory of at least
+ *     rgt_workspace_bytes(...) bytes, aligned to 256 bytes. It must be
+ *     zero-filled ONCE when created (rgt_reset_workspace does this); every
+ *     call leaves its counters at zero again on exit, so no memset is needed
+ *     between calls. One workspace serves one stream: two calls that overlap
+ *     in time on one workspace race on its counters.
+ *   - Coverage. A shape outside coverage returns RGT_ERR_UNSUPPORTED and the
+ *     caller may fall back to another implementation; this is the only status
+ *     meant for fallback. Covered: 1 <= K, K % 512 == 0; 1 <= N <= 1024,
+ *     N % 16 == 0; 1 <= topk <= min(N, 32); block in {16, 32, 64};
+ *     0 <= M <= 8192.
+ *   - M == 0 is a no-op returning RGT_OK (outputs untouched).
+ *   - Null required pointers, misaligned pointers (x, W: 16 bytes; fp32/int32
+ *     outputs: 4 bytes; a_q: 16 bytes), ld < K or ld % 8 != 0 return
+ *     RGT_ERR_INVALID. A workspace that is null, misaligned or too small
+ *     returns RGT_ERR_WORKSPACE. A failed kernel launch returns RGT_ERR_HIP.
+ *     Argument checks happen before any HIP call, so they never touch the GPU.
+ *   - Inputs must be finite (no NaN or Inf in x, W, bias); results for
+ *     non-finite inputs are unspecified.
+ */
+#ifndef RGT_H
+#define RGT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RGT_OK = 0,
+  RGT_ERR_UNSUPPORTED = 1, /* shape outside coverage: caller may fall back   */
+  RGT_ERR_INVALID = 2,     /* bad pointer, stride or argument                  */
+  RGT_ERR_WORKSPACE = 3,   /* workspace null, misaligned or too small          */
+  RGT_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed       */
+  RGT_ERR_TIMEOUT = 5      /* a device-side wait passed its deadline           */
+} rgt_status;
+
+/* Static string naming a status code. */
+const char* rgt_status_string(rgt_status s);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int rgt_version(void);
+
+/* Bytes of workspace needed for every call with 1 <= M <= max_m at this
+ * (N, K, topk, block). Returns 0 when the shape is outside coverage. */
+size_t rgt_workspace_bytes(int max_m, int n, int k, int topk, int block);
+
+/* Sort capacity `cap`: an upper bound on the padded total, equal to
+ * P + min(N, P)*(block-1) rounded up to a multiple of block, with P = M*topk.
+ * Callers size sorted_ids to cap, expert_ids to cap/block, a_q to cap*K
+ * bytes and a_scale to cap*K/32 bytes. Returns -1 outside coverage. */
+int64_t rgt_sort_capacity(int m, int n, int topk, int block);
+
+/* RGT_OK when (m, n, k) is inside the router's coverage, else
+ * RGT_ERR_UNSUPPORTED. Host-only; never touches the GPU. */
+rgt_status rgt_router_supported(int m, int n, int k);
+
+/* Zero-fill a workspace on `stream` (recovery after RGT_ERR_TIMEOUT or an
+ * interrupted call, and first-time initialisation). */
+rgt_status rgt_reset_workspace(void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Synchronise `stream`, then read the workspace's error word: RGT_OK or
+ * RGT_ERR_TIMEOUT (a device-side wait expired; outputs of that call are
+ * undefined and the workspace must be reset before reuse). */
+rgt_status rgt_check_workspace(const void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Router logits (split-K GEMV; split-K GEMV split-K fixup page, opening
+ * summary). logits[m][n] = fp32 sum over i < K of x[m][i]*W[n][i], accumulated
+ * in fp32 in a fixed order (deterministic: equal inputs give equal bits).
+ *   x      : bf16 [M][ldx], device          w      : bf16 [N][ldw], device
+ *   logits : fp32 [M][N] row-major, device, written
+ * One launch for M <= 64 (the split-K partials are reduced in order by the
+ * last workgroup to arrive at each output tile, which then zeroes its
+ * counter); larger M uses the MFMA path. */
+rgt_status rgt_router_logits(const void* x, int64_t ldx, const void* w, int64_t ldw,
+                             float* logits, int m, int n, int k,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Softmax top-k gate. For each row: s = fp32(logits + bias) (bias may be
+ * NULL); ids = the topk experts by (s descending, expert index ascending,
+ * -0 == +0), slot 0 the largest; w_j = exp(s_j - s_0) / sum_i exp(s_i - s_0)
+ * over the selected slots, evaluated in fp64 by a fixed operation sequence
+ * and rounded once to fp32.
+ *   logits   : fp32 [M][N], device       bias : fp32 [N], device, or NULL
+ *   topk_ids : int32 [M][topk], written  topk_w : fp32 [M][topk], written */
+rgt_status rgt_topk_gate(const float* logits, const float* bias, int m, int n, int topk,
+                         int32_t* topk_ids, float* topk_w, hipStream_t stream);
+
+/* Sort (token, slot) pairs into block-padded expert segments and quantise
+ * the gathered activations to MXFP8. Pair p = m*topk + j has expert
+ * topk_ids[m][j] (each in [0, N)).
+ *   sorted_ids : int32 [cap]; segment e occupies [offsets[e], offsets[e+1]);
+ *                its first cnt[e] entries are the pair ids on expert e in
+ *                ascending order, the rest the sentinel P = M*topk.
+ *   expert_ids : int32 [cap/block]; expert of each block of sorted_ids.
+ *   offsets    : int32 [N+1]; offsets[N] is the padded total. Entries of
+ *                sorted_ids / expert_ids / a_q / a_scale at or past the total
+ *                are not written.
+ *   a_q        : uint8 [cap][K]; row p (for a non-sentinel entry) holds the
+ *                e4m3fn codes of x[sorted_ids[p] / topk]; pad rows are not
+ *                written.
+ *   a_scale    : uint8 [cap][K/32]; e8m0 scale byte of each 32-element block:
+ *                se + 127 with se = clamp(floor(log2 amax) - 8, -127, 127),
+ *                0 for an all-zero block. Codes are e4m3(v / 2^se), round to
+ *                nearest even, saturating at +-448, sign kept. */
+rgt_status rgt_moe_sort_quant(const int32_t* topk_ids, const void* x, int64_t ldx,
+                              int m, int n, int k, int topk, int block,
+                              int32_t* sorted_ids, int32_t* expert_ids, int32_t* offsets,
+                              uint8_t* a_q, uint8_t* a_scale,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The whole front end: router logits -> top-k gate -> sort -> MXFP8 quant.
+ * Outputs are bit-identical to rgt_router_logits, rgt_topk_gate and
+ * rgt_moe_sort_quant chained on the same inputs. `logits` may be NULL (then
+ * the logits stay in the workspace). For M <= 64 this is ONE kernel launch
+ * whose workgroups wait for one another on device counters; the grid is
+ * sized to be co-resident, and every wait is bounded by a deadline (expiry
+ * sets the workspace error word, see rgt_check_workspace). */
+rgt_status rgt_route_sort_quant(const void* x, int64_t ldx, const void* w, int64_t ldw,
+                                const float* bias, int m, int n, int k, int topk, int block,
+                                float* logits, int32_t* topk_ids, float* topk_w,
+                                int32_t* sorted_ids, int32_t* expert_ids, int32_t* offsets,
+                                uint8_t* a_q, uint8_t* a_scale,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Number of kernel launches the last successful call of each entry point made
+ * on this thread (diagnostics for launch-count checks). */
+int rgt_last_launch_count(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RGT_H */

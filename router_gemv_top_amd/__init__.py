@@ -1,0 +1,22 @@
+"""MI355X (gfx950) MoE routing front-end: split-K router GEMV with in-launch
+fixup, softmax top-k gate, token -> expert sort and MXFP8 quantisation, behind
+the C ABI of include/rgt.h.
+
+The binding (``router_gemv_top_amd._binding``) is imported lazily so that the
+seeded input generators (``router_gemv_top_amd.inputs``) can be used without
+loading the HIP library.
+"""
+
+_API = (
+    "router_logits", "topk_gate", "moe_sort_quant", "route_sort_quant", "Workspace",
+    "workspace_bytes", "sort_capacity", "router_supported", "reset_workspace", "check_workspace",
+    "status_string", "last_launch_count", "alloc_sort_outputs", "RgtError", "RgtUnsupported", "lib",
+    "exported_symbols", "version",
+)
+
+
+def __getattr__(name):
+    if name in _API:
+        from . import _binding
+        return getattr(_binding, name)
+    raise AttributeError(name)

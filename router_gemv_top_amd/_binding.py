@@ -1,0 +1,240 @@
+"""ctypes binding of ``librgt.so`` (the C ABI declared in include/rgt.h).
+
+Argument marshalling only: every step of the routing path runs in the HIP
+kernels of the library. torch is used for device memory and the current
+stream. The library must be built (``python -m router_gemv_top_amd.build``);
+without it every call raises, there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librgt.so")
+
+RGT_OK, RGT_ERR_UNSUPPORTED, RGT_ERR_INVALID, RGT_ERR_WORKSPACE, RGT_ERR_HIP, RGT_ERR_TIMEOUT = range(6)
+
+_lib = None
+_lock = threading.Lock()
+
+
+class RgtError(RuntimeError):
+    """A non-OK status from the library."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class RgtUnsupported(RgtError):
+    """Shape outside coverage: the caller may fall back to another path."""
+
+
+def _hip_runtimes_loaded():
+    with open("/proc/self/maps") as f:
+        return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library once (after torch, so torch's HIP runtime is the one
+    it binds to) and declare the signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m router_gemv_top_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+        sigs = {
+            "rgt_status_string": ([i32], ctypes.c_char_p),
+            "rgt_version": ([], i32),
+            "rgt_workspace_bytes": ([i32, i32, i32, i32, i32], sz),
+            "rgt_sort_capacity": ([i32, i32, i32, i32], i64),
+            "rgt_router_supported": ([i32, i32, i32], i32),
+            "rgt_reset_workspace": ([vp, sz, vp], i32),
+            "rgt_check_workspace": ([vp, sz, vp], i32),
+            "rgt_router_logits": ([vp, i64, vp, i64, vp, i32, i32, i32, vp, sz, vp], i32),
+            "rgt_topk_gate": ([vp, vp, i32, i32, i32, vp, vp, vp], i32),
+            "rgt_moe_sort_quant": ([vp, vp, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp], i32),
+            "rgt_route_sort_quant": ([vp, i64, vp, i64, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
+                                      vp, vp, vp, sz, vp], i32),
+            "rgt_last_launch_count": ([], i32),
+        }
+        for name, (args, res) in sigs.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        runtimes = _hip_runtimes_loaded()
+        if len(runtimes) > 1:
+            raise RuntimeError(f"more than one HIP runtime loaded in this process: {runtimes}")
+        _lib = L
+    return _lib
+
+
+def exported_symbols():
+    return [n for n in dir(lib()) if n.startswith("rgt_")]
+
+
+def status_string(status: int) -> str:
+    return lib().rgt_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status == RGT_OK:
+        return
+    if status == RGT_ERR_UNSUPPORTED:
+        raise RgtUnsupported(status, where)
+    raise RgtError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def version() -> int:
+    return lib().rgt_version()
+
+
+def workspace_bytes(max_m: int, n: int, k: int, topk: int, block: int) -> int:
+    return lib().rgt_workspace_bytes(max_m, n, k, topk, block)
+
+
+def sort_capacity(m: int, n: int, topk: int, block: int) -> int:
+    return lib().rgt_sort_capacity(m, n, topk, block)
+
+
+def router_supported(m: int, n: int, k: int) -> bool:
+    return lib().rgt_router_supported(m, n, k) == RGT_OK
+
+
+def last_launch_count() -> int:
+    return lib().rgt_last_launch_count()
+
+
+class Workspace:
+    """Caller-owned, zero-initialised device workspace for one stream."""
+
+    def __init__(self, max_m: int, n: int, k: int, topk: int, block: int, device="cuda"):
+        nbytes = workspace_bytes(max_m, n, k, topk, block)
+        if nbytes == 0:
+            raise RgtUnsupported(RGT_ERR_UNSUPPORTED, "workspace_bytes")
+        self.nbytes = nbytes
+        self.buf = torch.zeros(nbytes, dtype=torch.uint8, device=device)  # zero-filled once
+
+    def reset(self, stream=None):
+        _check(lib().rgt_reset_workspace(_ptr(self.buf), self.nbytes, _stream(stream)), "reset_workspace")
+
+    def check(self, stream=None) -> int:
+        return lib().rgt_check_workspace(_ptr(self.buf), self.nbytes, _stream(stream))
+
+
+def reset_workspace(ws: Workspace, stream=None):
+    ws.reset(stream)
+
+
+def check_workspace(ws: Workspace, stream=None) -> int:
+    return ws.check(stream)
+
+
+def _bf16_2d(t, name):
+    if t.dtype != torch.bfloat16 or t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D bfloat16 tensor with a contiguous last dimension")
+    return t
+
+
+def router_logits(x, w, ws: Workspace, logits=None, stream=None):
+    """logits[M][N] fp32 = x[M][K] . W[N][K]^T (bf16 in, fp32 out)."""
+    _bf16_2d(x, "x"), _bf16_2d(w, "w")
+    m, k = x.shape
+    n = w.shape[0]
+    if logits is None:
+        logits = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _check(lib().rgt_router_logits(_ptr(x), x.stride(0), _ptr(w), w.stride(0), _ptr(logits), m, n, k,
+                                   _ptr(ws.buf), ws.nbytes, _stream(stream)), "router_logits")
+    return logits
+
+
+def topk_gate(logits, topk: int, bias=None, ids=None, weights=None, stream=None):
+    """(topk_ids int32 [M][topk], topk_w fp32 [M][topk]) of the softmax top-k gate."""
+    m, n = logits.shape
+    if ids is None:
+        ids = torch.empty((m, topk), dtype=torch.int32, device=logits.device)
+    if weights is None:
+        weights = torch.empty((m, topk), dtype=torch.float32, device=logits.device)
+    _check(lib().rgt_topk_gate(_ptr(logits), _ptr(bias), m, n, topk, _ptr(ids), _ptr(weights), _stream(stream)),
+           "topk_gate")
+    return ids, weights
+
+
+def alloc_sort_outputs(m: int, n: int, k: int, topk: int, block: int, device="cuda", fill: int | None = None):
+    """Device buffers sized to the sort capacity (optionally pre-filled with a
+    canary byte so that writes past the padded total can be detected)."""
+    cap = sort_capacity(m, n, topk, block)
+    if cap < 0:
+        raise RgtUnsupported(RGT_ERR_UNSUPPORTED, "sort_capacity")
+    cap = max(cap, block)
+
+    def mk(shape, dt):
+        if fill is None:
+            return torch.empty(shape, dtype=dt, device=device)
+        nbytes = torch.tensor([], dtype=dt).element_size()
+        numel = 1
+        for d in shape:
+            numel *= d
+        # every byte set to `fill`, whatever the element type
+        return torch.full((numel * nbytes,), fill, dtype=torch.uint8, device=device).view(dt).view(shape)
+    return dict(
+        sorted_ids=mk((cap,), torch.int32),
+        expert_ids=mk((cap // block,), torch.int32),
+        offsets=mk((n + 1,), torch.int32),
+        a_q=mk((cap, k), torch.uint8),
+        a_scale=mk((cap, k // 32), torch.uint8),
+    )
+
+
+def moe_sort_quant(topk_ids, x, n: int, block: int, ws: Workspace, out=None, stream=None):
+    """Sort pairs into block-padded expert segments and MXFP8-quantise the
+    gathered rows of x. Returns the dict of output buffers."""
+    _bf16_2d(x, "x")
+    m, k = x.shape
+    topk = topk_ids.shape[1]
+    if out is None:
+        out = alloc_sort_outputs(m, n, k, topk, block, x.device)
+    _check(lib().rgt_moe_sort_quant(_ptr(topk_ids), _ptr(x), x.stride(0), m, n, k, topk, block,
+                                    _ptr(out["sorted_ids"]), _ptr(out["expert_ids"]), _ptr(out["offsets"]),
+                                    _ptr(out["a_q"]), _ptr(out["a_scale"]), _ptr(ws.buf), ws.nbytes,
+                                    _stream(stream)), "moe_sort_quant")
+    return out
+
+
+def route_sort_quant(x, w, topk: int, block: int, ws: Workspace, bias=None, out=None, want_logits=True,
+                     stream=None):
+    """The whole front end (one launch for M <= 64). Returns a dict with
+    logits (if requested), topk_ids, topk_w and the sort/quant buffers."""
+    _bf16_2d(x, "x"), _bf16_2d(w, "w")
+    m, k = x.shape
+    n = w.shape[0]
+    if out is None:
+        out = alloc_sort_outputs(m, n, k, topk, block, x.device)
+        out["topk_ids"] = torch.empty((m, topk), dtype=torch.int32, device=x.device)
+        out["topk_w"] = torch.empty((m, topk), dtype=torch.float32, device=x.device)
+        out["logits"] = torch.empty((m, n), dtype=torch.float32, device=x.device) if want_logits else None
+    _check(lib().rgt_route_sort_quant(_ptr(x), x.stride(0), _ptr(w), w.stride(0), _ptr(bias), m, n, k, topk, block,
+                                      _ptr(out.get("logits")), _ptr(out["topk_ids"]), _ptr(out["topk_w"]),
+                                      _ptr(out["sorted_ids"]), _ptr(out["expert_ids"]), _ptr(out["offsets"]),
+                                      _ptr(out["a_q"]), _ptr(out["a_scale"]), _ptr(ws.buf), ws.nbytes,
+                                      _stream(stream)), "route_sort_quant")
+    return out

@@ -1,0 +1,79 @@
+// gate.h - softmax top-k gate, one wave64 per token row.
+//
+// The gate of the MiniMax-M3.1-Flash MoE/GEMM kernels page (sglang PR #46691,
+// Summary: Router) and the routing step of "Kimi-K3: fused MoE routing, sort,
+// quant and epilogue" (sglang PR #46652, Modifications): choose the k experts
+// with the largest scores and renormalise their softmax weights.
+//
+//   s[n]  = fp32(logits[n] + bias[n])      (bias optional)
+//   ids   = top k of s by (s descending, n ascending), -0 == +0
+//   w_j   = exp(s_j - s_0) / sum_{i<k} exp(s_i - s_0)     (fp64, then fp32)
+//
+// Lane l holds the scores of experts l, l+64, l+128, ... as order-preserving
+// u32 keys. Each of the k rounds takes the wave maximum of the keys and the
+// lowest expert index holding it (ballots over the lane's slots in expert
+// order), then clears that key.
+#pragma once
+
+#include "device.h"
+
+namespace rgt {
+
+template <int NV>   // NV = ceil(N / 64) score slots per lane
+__device__ __forceinline__ void wave_topk_row(const float* logits_row, const float* bias, int n, int k,
+                                              int32_t* ids_out, float* w_out) {
+  const int lane = lane_id();
+  u32 key[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = lane + 64 * i;
+    if (e < n) {
+      float s = logits_row[e];
+      if (bias) s = __fadd_rn(s, bias[e]);
+      key[i] = score_key(s);
+    } else {
+      key[i] = 0u;
+    }
+  }
+  int my_id = 0;
+  float my_s = 0.f;
+  for (int j = 0; j < k; ++j) {
+    u32 best = key[0];
+#pragma unroll
+    for (int i = 1; i < NV; ++i) best = key[i] > best ? key[i] : best;
+    const u32 top = wave_max_u32(best);
+    int win = -1;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const u64 b = ballot64(key[i] == top);
+      if (win < 0 && b != 0ull) win = 64 * i + (int)__builtin_ctzll(b);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (64 * i + lane == win) key[i] = 0u;
+    if (lane == j) {
+      my_id = win;
+      my_s = key_score(top);
+    }
+  }
+  // Renormalised softmax over the k selected scores, slot 0 the largest.
+  const double s0 = (double)__shfl(my_s, 0, kWave);
+  double e = 0.0;
+  if (lane < k) e = exp64_recipe((double)my_s - s0);
+  double total = __shfl(e, 0, kWave);
+  for (int j = 1; j < k; ++j) total = total + __shfl(e, j, kWave);
+  if (lane < k) {
+    ids_out[lane] = my_id;
+    w_out[lane] = (float)(e / total);
+  }
+}
+
+template <int NV>
+__global__ void __launch_bounds__(256) topk_gate_kernel(const float* logits, const float* bias, int m, int n, int k,
+                                                        int32_t* ids, float* w) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= m) return;
+  wave_topk_row<NV>(logits + (int64_t)row * n, bias, n, k, ids + (int64_t)row * k, w + (int64_t)row * k);
+}
+
+}  // namespace rgt

@@ -1,0 +1,197 @@
+// gemv.h - split-K router GEMV tiles for gfx950 and the in-launch fixup.
+//
+// logits[M][N] fp32 = x[M][K] bf16 . W[N][K]^T bf16 ("MiniMax-M3: Triton
+// split-K router GEMV with in-kernel split-K fixup", opening summary). The
+// grid is split over (row tile, n-block, k-slice). Each workgroup writes an
+// fp32 partial for its tile and k-slice to the workspace and arrives on the
+// tile's counter; the last workgroup to arrive sums the partials in k-slice
+// order (deterministic), writes the logits and puts the counter back to zero,
+// so no memset launch and no separate reduce launch is needed.
+//
+// Two tile kinds, chosen per M bucket (the page's per-M-bucket configs):
+//   * VALU tile (M <= 8): each wave streams RPW rows of W with 16-byte loads
+//     (a wave load covers 512 consecutive k of one row, fully coalesced) and
+//     forms dot products with v_dot2_f32_bf16; a wave64 butterfly reduces.
+//   * MFMA tile (8 < M): v_mfma_f32_16x16x32_bf16 with x as the A operand
+//     (16 rows) and W as the B operand (16 experts); the four waves of a
+//     workgroup split the k-slice and their 16x16 accumulators are summed in
+//     wave order through LDS.
+#pragma once
+
+#include "device.h"
+
+namespace rgt {
+
+typedef uint16_t u16;
+
+struct GemvArgs {
+  const u16* x;
+  int64_t ldx;
+  const u16* w;
+  int64_t ldw;
+  float* logits;   // [M][N]
+  float* part;     // [S][M][N] fp32 partials (workspace)
+  u32* ctr;        // [MB*NB] arrival counters (workspace, zero between calls)
+  int m, n, k;
+  int s_count;     // S: number of k-slices
+  int nb_count;    // NB: number of n-blocks
+};
+
+__device__ __forceinline__ uint4 ld16(const u16* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// ---------------------------------------------------------------------------
+// VALU tile. Workgroup = 4 waves; wave w owns rows n0 + w*RPW .. +RPW of the
+// n-block, over the workgroup's k-slice of 512*L elements. Lane l covers the
+// 8 elements at k = kslice + j*512 + 8*l for j < L.
+// ---------------------------------------------------------------------------
+template <int MT, int RPW, int L>
+__device__ __forceinline__ void valu_tile(const GemvArgs& a, int nb, int s) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nrow0 = nb * (4 * RPW) + wave * RPW;
+  const int kb = s * (512 * L) + lane * 8;
+  uint4 wv[RPW][L];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int j = 0; j < L; ++j) wv[r][j] = ld16(a.w + (int64_t)(nrow0 + r) * a.ldw + kb + j * 512);
+  float acc[RPW][MT];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[r][m] = 0.f;
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    if (m < a.m) {
+#pragma unroll
+      for (int j = 0; j < L; ++j) {
+        const uint4 xv = ld16(a.x + (int64_t)m * a.ldx + kb + j * 512);
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) acc[r][m] = dot8_bf16(wv[r][j], xv, acc[r][m]);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[r][m] = wave_sum(acc[r][m]);
+  float* part = a.part + (int64_t)s * a.m * a.n;
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      if (lane == r * MT + m && m < a.m) part[(int64_t)m * a.n + nrow0 + r] = acc[r][m];
+}
+
+// ---------------------------------------------------------------------------
+// MFMA tile. Workgroup = 4 waves over a k-slice of 4*32*KS elements and a
+// tile of 16*MT rows of x by 16 experts. Wave w takes the w-th quarter of the
+// slice; inside it, lane group g = lane/16 takes a contiguous run of 8*KS
+// elements, and k-step j feeds elements [8j, 8j+8) of that run to the MFMA.
+// (The dot product does not depend on how k is assigned to MFMA slots, as
+// long as A and B use the same assignment.)
+// A lane l: x[row0 + l%16][k-run of group l/16]; B lane l: W[n0 + l%16][same k].
+// D lane l: rows 4*(l/16)+i (i < 4) of the 16x16 tile, column l%16.
+// ---------------------------------------------------------------------------
+template <int MT, int KS>
+__device__ __forceinline__ void mfma_tile(const GemvArgs& a, int mb, int nb, int s, float* lds) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r16 = lane & 15, grp = lane >> 4;
+  const int kslice = 4 * 32 * KS;
+  const int krun = s * kslice + wave * (32 * KS) + grp * (8 * KS);
+  const int n = nb * 16 + r16;
+  uint4 bw[KS];
+#pragma unroll
+  for (int j = 0; j < KS; ++j) bw[j] = ld16(a.w + (int64_t)n * a.ldw + krun + 8 * j);
+  floatx4_t acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  const int row_base = mb * (16 * MT);
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int m = row_base + t * 16 + r16;
+    const bool ok = m < a.m;
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+      uint4 xv = ok ? ld16(a.x + (int64_t)m * a.ldx + krun + 8 * j) : make_uint4(0, 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xv),
+                                                      __builtin_bit_cast(bf16x8_t, bw[j]), acc[t], 0, 0, 0);
+    }
+  }
+  // Sum the four waves' accumulators in wave order through LDS.
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds[((wave * MT + t) * 16 + grp * 4 + i) * 16 + r16] = acc[t][i];
+  __syncthreads();
+  float* part = a.part + (int64_t)s * a.m * a.n;
+  for (int idx = threadIdx.x; idx < MT * 256; idx += 256) {
+    const int t = idx >> 8, rc = idx & 255, rr = rc >> 4, cc = rc & 15;
+    const int m = row_base + t * 16 + rr;
+    float v = lds[((0 * MT + t) * 16 + rr) * 16 + cc];
+    v += lds[((1 * MT + t) * 16 + rr) * 16 + cc];
+    v += lds[((2 * MT + t) * 16 + rr) * 16 + cc];
+    v += lds[((3 * MT + t) * 16 + rr) * 16 + cc];
+    if (m < a.m) part[(int64_t)m * a.n + nb * 16 + cc] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split-K fixup. Every thread publishes its partial stores, then one thread
+// arrives on the tile counter. Returns true in the last workgroup to arrive,
+// after an acquire so the other workgroups' partials are visible.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool arrive_last(u32* ctr, u32 arrivals) {
+  __shared__ u32 s_last;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = (atomic_add_agent(ctr, 1u) == arrivals - 1u) ? 1u : 0u;
+  __syncthreads();
+  const bool last = s_last != 0u;
+  if (last) __threadfence();
+  return last;
+}
+
+// Sum the S partials of rows [r0, r1) x columns [c0, c0+bn) in k-slice order
+// into dst (row stride n).
+__device__ __forceinline__ void reduce_partials(const GemvArgs& a, int r0, int r1, int c0, int bn, float* dst) {
+  const int rows = r1 - r0;
+  for (int idx = threadIdx.x; idx < rows * bn; idx += blockDim.x) {
+    const int m = r0 + idx / bn, c = c0 + idx % bn;
+    const float* p = a.part + (int64_t)m * a.n + c;
+    const int64_t stride = (int64_t)a.m * a.n;
+    float v = 0.f;
+#pragma unroll 8
+    for (int s = 0; s < a.s_count; ++s) v += p[s * stride];
+    dst[(int64_t)m * a.n + c] = v;
+  }
+}
+
+// Standalone router kernels: tile, then fixup by the last arriver.
+template <int MT, int RPW, int L>
+__global__ void __launch_bounds__(256) router_valu_kernel(GemvArgs a) {
+  const int nb = blockIdx.x % a.nb_count, s = blockIdx.x / a.nb_count;
+  valu_tile<MT, RPW, L>(a, nb, s);
+  if (arrive_last(a.ctr + nb, (u32)a.s_count)) {
+    reduce_partials(a, 0, a.m, nb * 4 * RPW, 4 * RPW, a.logits);
+    if (threadIdx.x == 0) atomic_store_agent(a.ctr + nb, 0u);
+  }
+}
+
+template <int MT, int KS>
+__global__ void __launch_bounds__(256) router_mfma_kernel(GemvArgs a) {
+  __shared__ float lds[4 * MT * 256];
+  const int tiles = a.nb_count;
+  const int nb = blockIdx.x % tiles;
+  const int s = (blockIdx.x / tiles) % a.s_count;
+  const int mb = blockIdx.x / (tiles * a.s_count);
+  mfma_tile<MT, KS>(a, mb, nb, s, lds);
+  u32* ctr = a.ctr + mb * a.nb_count + nb;
+  if (arrive_last(ctr, (u32)a.s_count)) {
+    const int r0 = mb * 16 * MT;
+    const int r1 = min(a.m, r0 + 16 * MT);
+    reduce_partials(a, r0, r1, nb * 16, 16, a.logits);
+    if (threadIdx.x == 0) atomic_store_agent(ctr, 0u);
+  }
+}
+
+}  // namespace rgt

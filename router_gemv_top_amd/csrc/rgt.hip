@@ -1,0 +1,505 @@
+// rgt.hip - host side of the routing front-end library (C ABI in rgt.h).
+//
+// Validation happens before any HIP call, so every argument error is reported
+// without touching the GPU. Plans (tile kind and split) are picked per M
+// bucket, in the spirit of the per-M-bucket configs of "MiniMax-M3: Triton
+// split-K router GEMV with in-kernel split-K fixup" (opening summary), but
+// sized for 256 CUs in 8 XCDs.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "rgt.h"
+#include "device.h"
+#include "fused.h"
+#include "gate.h"
+#include "gemv.h"
+#include "sortq.h"
+
+using namespace rgt;
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+constexpr size_t kAlign = 256;
+constexpr size_t kCtlBytes = 256;          // control words (error, phase counters)
+constexpr int kMaxTileCounters = 8192;     // arrival counters for GEMV tiles
+constexpr int kSmallSortMaxP = 8192;       // one-workgroup sort up to this many pairs
+constexpr int kLargeSortChunk = 512;       // pairs per workgroup in the large sort
+constexpr int kFusedMaxM = 64;
+
+thread_local int g_last_launches = 0;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int env_int(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  return v && *v ? std::atoi(v) : dflt;
+}
+
+bool covered(int m, int n, int k) {
+  return m >= 0 && m <= 8192 && n >= 16 && n <= 1024 && n % 16 == 0 && k >= 512 && k % 512 == 0;
+}
+
+bool gate_covered(int n, int topk) { return topk >= 1 && topk <= 32 && topk <= n; }
+
+bool block_covered(int b) { return b == 16 || b == 32 || b == 64; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// ---------------------------------------------------------------------------
+// GEMV plan for one call.
+// ---------------------------------------------------------------------------
+struct Plan {
+  bool valu;     // VALU tile (M <= 8) or MFMA tile
+  int mt;        // VALU: rows in the template (1,2,4,8); MFMA: 16-row tiles (1..4)
+  int rpw;       // VALU rows of W per wave
+  int ks;        // MFMA k-steps of 32 per wave
+  int nb;        // n-blocks
+  int s;         // k-slices
+  int mb;        // row blocks (MFMA)
+  int grid;      // workgroups
+  int bn;        // experts per n-block
+};
+
+int pow2_at_least(int v) {
+  int p = 1;
+  while (p < v) p <<= 1;
+  return p;
+}
+
+Plan make_plan(int m, int n, int k) {
+  Plan p{};
+  if (m <= 8) {
+    p.valu = true;
+    p.mt = pow2_at_least(std::max(m, 1));
+    p.rpw = n <= 256 ? 1 : 2;
+    p.bn = 4 * p.rpw;
+    p.nb = n / p.bn;
+    p.s = k / 512;
+    p.mb = 1;
+  } else {
+    p.valu = false;
+    p.mt = std::min(4, (m + 15) / 16);
+    p.mb = (m + 16 * p.mt - 1) / (16 * p.mt);
+    p.bn = 16;
+    p.nb = n / 16;
+    p.ks = (p.nb * p.mb * (k / 512) >= 128) ? 4 : 2;
+    p.s = k / (128 * p.ks);
+  }
+  p.grid = p.nb * p.s * p.mb;
+  return p;
+}
+
+// ---------------------------------------------------------------------------
+// Workspace layout for one call (offsets depend on the call's own shape,
+// except the control words and tile counters, which sit at fixed offsets and
+// are the only state that must stay zero between calls).
+// ---------------------------------------------------------------------------
+struct Layout {
+  size_t ctl, ctr, part, logits, pos, ghist, offws, total;
+};
+
+int large_sort_groups(int P) { return (P + kLargeSortChunk - 1) / kLargeSortChunk; }
+
+Layout make_layout(int m, int n, int k, int topk) {
+  Layout L{};
+  const Plan p = make_plan(m, n, k);
+  const int P = m * topk;
+  size_t o = 0;
+  L.ctl = o; o += kCtlBytes;
+  L.ctr = o; o = align_up(o + sizeof(u32) * kMaxTileCounters, kAlign);
+  L.part = o; o = align_up(o + sizeof(float) * (size_t)p.s * m * n, kAlign);
+  L.logits = o; o = align_up(o + sizeof(float) * (size_t)m * n, kAlign);
+  L.pos = o; o = align_up(o + sizeof(int32_t) * (size_t)P, kAlign);
+  L.ghist = o;
+  if (P > kSmallSortMaxP) o = align_up(o + sizeof(int32_t) * (size_t)large_sort_groups(P) * n, kAlign);
+  L.offws = o; o = align_up(o + sizeof(int32_t) * (size_t)(n + 1), kAlign);
+  L.total = o;
+  return L;
+}
+
+size_t ws_need(int m, int n, int k, int topk) { return make_layout(m, n, k, topk).total; }
+
+// ---------------------------------------------------------------------------
+// Device facts, cached per device.
+// ---------------------------------------------------------------------------
+struct DevInfo {
+  int cus = 0;
+  bool init = false;
+};
+std::mutex g_mu;
+DevInfo g_dev[64];
+
+bool dev_info(DevInfo& out) {
+  int d = 0;
+  if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= 64) return false;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_dev[d].init) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, d) != hipSuccess) return false;
+    g_dev[d].cus = prop.multiProcessorCount;
+    g_dev[d].init = true;
+  }
+  out = g_dev[d];
+  return true;
+}
+
+u64 wait_budget_ticks() {
+  static const long us = env_int("RGT_WAIT_BUDGET_US", 100000);  // 100 ms default
+  return (u64)std::max(1L, us) * 100ull;                            // 100 MHz clock
+}
+
+rgt_status launched() {
+  return hipGetLastError() == hipSuccess ? RGT_OK : RGT_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel dispatch helpers (template instantiation by switch).
+// ---------------------------------------------------------------------------
+int nv_bucket(int n) {
+  const int nv = (n + 63) / 64;
+  if (nv <= 2) return 2;
+  if (nv <= 4) return 4;
+  if (nv <= 8) return 8;
+  if (nv <= 14) return 14;
+  return 16;
+}
+
+template <int MT, int RPW>
+void launch_router_valu(const GemvArgs& a, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((router_valu_kernel<MT, RPW, 1>), dim3(grid), dim3(256), 0, st, a);
+}
+
+template <int MT>
+void launch_router_valu_rpw(const GemvArgs& a, const Plan& p, hipStream_t st) {
+  if (p.rpw == 1) launch_router_valu<MT, 1>(a, p.grid, st);
+  else launch_router_valu<MT, 2>(a, p.grid, st);
+}
+
+template <int MT>
+void launch_router_mfma(const GemvArgs& a, const Plan& p, hipStream_t st) {
+  if (p.ks == 2) hipLaunchKernelGGL((router_mfma_kernel<MT, 2>), dim3(p.grid), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((router_mfma_kernel<MT, 4>), dim3(p.grid), dim3(256), 0, st, a);
+}
+
+void launch_router(const GemvArgs& a, const Plan& p, hipStream_t st) {
+  if (p.valu) {
+    switch (p.mt) {
+      case 1: launch_router_valu_rpw<1>(a, p, st); break;
+      case 2: launch_router_valu_rpw<2>(a, p, st); break;
+      case 4: launch_router_valu_rpw<4>(a, p, st); break;
+      default: launch_router_valu_rpw<8>(a, p, st); break;
+    }
+  } else {
+    switch (p.mt) {
+      case 1: launch_router_mfma<1>(a, p, st); break;
+      case 2: launch_router_mfma<2>(a, p, st); break;
+      case 3: launch_router_mfma<3>(a, p, st); break;
+      default: launch_router_mfma<4>(a, p, st); break;
+    }
+  }
+}
+
+void launch_gate(const float* logits, const float* bias, int m, int n, int k, int32_t* ids, float* w,
+                 hipStream_t st) {
+  const dim3 grid((m + 3) / 4), blk(256);
+  switch (nv_bucket(n)) {
+    case 2: hipLaunchKernelGGL((topk_gate_kernel<2>), grid, blk, 0, st, logits, bias, m, n, k, ids, w); break;
+    case 4: hipLaunchKernelGGL((topk_gate_kernel<4>), grid, blk, 0, st, logits, bias, m, n, k, ids, w); break;
+    case 8: hipLaunchKernelGGL((topk_gate_kernel<8>), grid, blk, 0, st, logits, bias, m, n, k, ids, w); break;
+    case 14: hipLaunchKernelGGL((topk_gate_kernel<14>), grid, blk, 0, st, logits, bias, m, n, k, ids, w); break;
+    default: hipLaunchKernelGGL((topk_gate_kernel<16>), grid, blk, 0, st, logits, bias, m, n, k, ids, w); break;
+  }
+}
+
+// Sort + quant as separate launches. Returns the number of launches.
+int launch_sort_quant(const int32_t* ids, const uint16_t* x, int64_t ldx, int m, int n, int k, int topk, int block,
+                      int32_t* sorted_ids, int32_t* expert_ids, int32_t* offsets, uint8_t* a_q, uint8_t* a_scale,
+                      char* ws, const Layout& L, hipStream_t st) {
+  const int P = m * topk;
+  int32_t* pos = reinterpret_cast<int32_t*>(ws + L.pos);
+  int launches = 0;
+  if (P <= kSmallSortMaxP) {
+    const size_t lds = sizeof(int) * ((size_t)P + 4 * n + n + (n + 1) + 256);
+    hipLaunchKernelGGL(sort_small_kernel, dim3(1), dim3(256), lds, st, ids, P, n, block, sorted_ids, expert_ids,
+                       offsets, pos);
+    ++launches;
+  } else {
+    const int G = large_sort_groups(P);
+    int32_t* ghist = reinterpret_cast<int32_t*>(ws + L.ghist);
+    int32_t* offws = reinterpret_cast<int32_t*>(ws + L.offws);
+    hipLaunchKernelGGL(sort_hist_kernel, dim3(G), dim3(256), sizeof(int) * n, st, ids, P, n, kLargeSortChunk,
+                       ghist);
+    hipLaunchKernelGGL(sort_scan_kernel, dim3(1), dim3(1024), sizeof(int) * ((size_t)n + (n + 1) + 1024), st, ghist,
+                       G, P, n, block, sorted_ids, expert_ids, offsets, offws);
+    hipLaunchKernelGGL(sort_scatter_kernel, dim3(G), dim3(256), sizeof(int) * (4 * (size_t)n + n), st, ids, P, n,
+                       kLargeSortChunk, ghist, offws, sorted_ids, pos);
+    launches += 3;
+  }
+  const int units = m * (k / 16);
+  hipLaunchKernelGGL(quant_kernel, dim3((units + 255) / 256), dim3(256), 0, st, x, ldx, m, k, topk, pos, a_q,
+                     a_scale);
+  return launches + 1;
+}
+
+// ---------------------------------------------------------------------------
+// Fused launch (M <= 64).
+// ---------------------------------------------------------------------------
+size_t fused_lds_bytes(const Plan& p, int m, int n, int topk) {
+  const size_t P = (size_t)m * topk;
+  const size_t sort = sizeof(int) * (2 * P + 4 * (size_t)n + n + (n + 1) + 256);
+  const size_t tile = p.valu ? 0 : sizeof(float) * 4 * p.mt * 256;
+  return std::max(sort, tile);
+}
+
+template <int NV>
+const void* fused_kernel_ptr(const Plan& p) {
+  if (p.valu) {
+    if (p.rpw == 1) {
+      switch (p.mt) {
+        case 1: return (const void*)fused_valu_kernel<NV, 1, 1, 1>;
+        case 2: return (const void*)fused_valu_kernel<NV, 2, 1, 1>;
+        case 4: return (const void*)fused_valu_kernel<NV, 4, 1, 1>;
+        default: return (const void*)fused_valu_kernel<NV, 8, 1, 1>;
+      }
+    }
+    switch (p.mt) {
+      case 1: return (const void*)fused_valu_kernel<NV, 1, 2, 1>;
+      case 2: return (const void*)fused_valu_kernel<NV, 2, 2, 1>;
+      case 4: return (const void*)fused_valu_kernel<NV, 4, 2, 1>;
+      default: return (const void*)fused_valu_kernel<NV, 8, 2, 1>;
+    }
+  }
+  if (p.ks == 2) {
+    switch (p.mt) {
+      case 1: return (const void*)fused_mfma_kernel<NV, 1, 2>;
+      case 2: return (const void*)fused_mfma_kernel<NV, 2, 2>;
+      case 3: return (const void*)fused_mfma_kernel<NV, 3, 2>;
+      default: return (const void*)fused_mfma_kernel<NV, 4, 2>;
+    }
+  }
+  switch (p.mt) {
+    case 1: return (const void*)fused_mfma_kernel<NV, 1, 4>;
+    case 2: return (const void*)fused_mfma_kernel<NV, 2, 4>;
+    case 3: return (const void*)fused_mfma_kernel<NV, 3, 4>;
+    default: return (const void*)fused_mfma_kernel<NV, 4, 4>;
+  }
+}
+
+const void* fused_kernel_for(const Plan& p, int n) {
+  switch (nv_bucket(n)) {
+    case 2: return fused_kernel_ptr<2>(p);
+    case 4: return fused_kernel_ptr<4>(p);
+    case 8: return fused_kernel_ptr<8>(p);
+    case 14: return fused_kernel_ptr<14>(p);
+    default: return fused_kernel_ptr<16>(p);
+  }
+}
+
+// Largest co-resident grid for a kernel at this dynamic LDS size (cached).
+struct OccKey {
+  const void* fn;
+  size_t lds;
+  int dev;
+  int blocks;
+};
+OccKey g_occ[256];
+int g_occ_n = 0;
+
+int coresident_blocks(const void* fn, size_t lds, int cus) {
+  int d = 0;
+  if (hipGetDevice(&d) != hipSuccess) d = 0;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    for (int i = 0; i < g_occ_n; ++i)
+      if (g_occ[i].fn == fn && g_occ[i].lds == lds && g_occ[i].dev == d) return g_occ[i].blocks;
+  }
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, lds) != hipSuccess) per_cu = 0;
+  const int blocks = per_cu * cus;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (g_occ_n < 256) g_occ[g_occ_n++] = OccKey{fn, lds, d, blocks};
+  return blocks;
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+const char* rgt_status_string(rgt_status s) {
+  switch (s) {
+    case RGT_OK: return "ok";
+    case RGT_ERR_UNSUPPORTED: return "shape outside coverage";
+    case RGT_ERR_INVALID: return "invalid argument";
+    case RGT_ERR_WORKSPACE: return "workspace null, misaligned or too small";
+    case RGT_ERR_HIP: return "HIP runtime error";
+    case RGT_ERR_TIMEOUT: return "device-side wait timed out";
+  }
+  return "unknown status";
+}
+
+int rgt_version(void) { return kVersion; }
+
+int rgt_last_launch_count(void) { return g_last_launches; }
+
+int64_t rgt_sort_capacity(int m, int n, int topk, int block) {
+  if (m < 0 || m > 8192 || n < 1 || n > 1024 || !gate_covered(n, topk) || !block_covered(block)) return -1;
+  const int64_t P = (int64_t)m * topk;
+  const int64_t cap = P + std::min<int64_t>(n, P) * (block - 1);
+  return (cap + block - 1) / block * block;
+}
+
+size_t rgt_workspace_bytes(int max_m, int n, int k, int topk, int block) {
+  if (max_m < 1 || !covered(max_m, n, k) || !gate_covered(n, topk) || !block_covered(block)) return 0;
+  size_t need = 0;
+  for (int m = 1; m <= max_m; ++m) need = std::max(need, ws_need(m, n, k, topk));
+  return need;
+}
+
+rgt_status rgt_router_supported(int m, int n, int k) {
+  return covered(m, n, k) ? RGT_OK : RGT_ERR_UNSUPPORTED;
+}
+
+rgt_status rgt_reset_workspace(void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!ws || !aligned(ws, kAlign) || ws_bytes < kCtlBytes) return RGT_ERR_WORKSPACE;
+  g_last_launches = 0;
+  return hipMemsetAsync(ws, 0, ws_bytes, stream) == hipSuccess ? RGT_OK : RGT_ERR_HIP;
+}
+
+rgt_status rgt_check_workspace(const void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!ws || !aligned(ws, kAlign) || ws_bytes < kCtlBytes) return RGT_ERR_WORKSPACE;
+  if (hipStreamSynchronize(stream) != hipSuccess) return RGT_ERR_HIP;
+  u32 err = 0;
+  if (hipMemcpy(&err, ws, sizeof(err), hipMemcpyDeviceToHost) != hipSuccess) return RGT_ERR_HIP;
+  return (err & kErrTimeout) ? RGT_ERR_TIMEOUT : RGT_OK;
+}
+
+static rgt_status check_gemv_args(const void* x, int64_t ldx, const void* w, int64_t ldw, int m, int n, int k) {
+  if (!covered(m, n, k)) return RGT_ERR_UNSUPPORTED;
+  if (m == 0) return RGT_OK;
+  if (!x || !w || !aligned(x, 16) || !aligned(w, 16)) return RGT_ERR_INVALID;
+  if (ldx < k || ldw < k || ldx % 8 || ldw % 8) return RGT_ERR_INVALID;
+  return RGT_OK;
+}
+
+static rgt_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (!ws || !aligned(ws, kAlign) || ws_bytes < need) return RGT_ERR_WORKSPACE;
+  return RGT_OK;
+}
+
+rgt_status rgt_router_logits(const void* x, int64_t ldx, const void* w, int64_t ldw, float* logits, int m, int n,
+                             int k, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_last_launches = 0;
+  rgt_status st = check_gemv_args(x, ldx, w, ldw, m, n, k);
+  if (st != RGT_OK || m == 0) return st;
+  if (!logits || !aligned(logits, 4)) return RGT_ERR_INVALID;
+  const Layout L = make_layout(m, n, k, 1);
+  if ((st = check_ws(ws, ws_bytes, L.total)) != RGT_OK) return st;
+  const Plan p = make_plan(m, n, k);
+  if (p.mb * p.nb > kMaxTileCounters) return RGT_ERR_UNSUPPORTED;
+  char* base = static_cast<char*>(ws);
+  GemvArgs a{static_cast<const u16*>(x), ldx, static_cast<const u16*>(w), ldw, logits,
+             reinterpret_cast<float*>(base + L.part), reinterpret_cast<u32*>(base + L.ctr), m, n, k, p.s, p.nb};
+  launch_router(a, p, stream);
+  g_last_launches = 1;
+  return launched();
+}
+
+rgt_status rgt_topk_gate(const float* logits, const float* bias, int m, int n, int topk, int32_t* topk_ids,
+                         float* topk_w, hipStream_t stream) {
+  g_last_launches = 0;
+  if (m < 0 || m > 8192 || n < 16 || n > 1024 || n % 16 || !gate_covered(n, topk)) return RGT_ERR_UNSUPPORTED;
+  if (m == 0) return RGT_OK;
+  if (!logits || !topk_ids || !topk_w || !aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) ||
+      (bias && !aligned(bias, 4)))
+    return RGT_ERR_INVALID;
+  launch_gate(logits, bias, m, n, topk, topk_ids, topk_w, stream);
+  g_last_launches = 1;
+  return launched();
+}
+
+static rgt_status check_sort_args(const void* x, int64_t ldx, int m, int n, int k, int topk, int block,
+                                  const void* sorted_ids, const void* expert_ids, const void* offsets,
+                                  const void* a_q, const void* a_scale) {
+  if (!covered(m, n, k) || !gate_covered(n, topk) || !block_covered(block)) return RGT_ERR_UNSUPPORTED;
+  if (m == 0) return RGT_OK;
+  if (!x || !aligned(x, 16) || ldx < k || ldx % 8) return RGT_ERR_INVALID;
+  if (!sorted_ids || !expert_ids || !offsets || !a_q || !a_scale) return RGT_ERR_INVALID;
+  if (!aligned(sorted_ids, 4) || !aligned(expert_ids, 4) || !aligned(offsets, 4) || !aligned(a_q, 16))
+    return RGT_ERR_INVALID;
+  return RGT_OK;
+}
+
+rgt_status rgt_moe_sort_quant(const int32_t* topk_ids, const void* x, int64_t ldx, int m, int n, int k, int topk,
+                              int block, int32_t* sorted_ids, int32_t* expert_ids, int32_t* offsets, uint8_t* a_q,
+                              uint8_t* a_scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_last_launches = 0;
+  rgt_status st = check_sort_args(x, ldx, m, n, k, topk, block, sorted_ids, expert_ids, offsets, a_q, a_scale);
+  if (st != RGT_OK || m == 0) return st;
+  if (!topk_ids || !aligned(topk_ids, 4)) return RGT_ERR_INVALID;
+  const Layout L = make_layout(m, n, k, topk);
+  if ((st = check_ws(ws, ws_bytes, L.total)) != RGT_OK) return st;
+  g_last_launches = launch_sort_quant(topk_ids, static_cast<const uint16_t*>(x), ldx, m, n, k, topk, block,
+                                      sorted_ids, expert_ids, offsets, a_q, a_scale, static_cast<char*>(ws), L,
+                                      stream);
+  return launched();
+}
+
+rgt_status rgt_route_sort_quant(const void* x, int64_t ldx, const void* w, int64_t ldw, const float* bias, int m,
+                                int n, int k, int topk, int block, float* logits, int32_t* topk_ids, float* topk_w,
+                                int32_t* sorted_ids, int32_t* expert_ids, int32_t* offsets, uint8_t* a_q,
+                                uint8_t* a_scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_last_launches = 0;
+  rgt_status st = check_gemv_args(x, ldx, w, ldw, m, n, k);
+  if (st != RGT_OK) return st;
+  st = check_sort_args(x, ldx, m, n, k, topk, block, sorted_ids, expert_ids, offsets, a_q, a_scale);
+  if (st != RGT_OK || m == 0) return st;
+  if (!topk_ids || !topk_w || !aligned(topk_ids, 4) || !aligned(topk_w, 4)) return RGT_ERR_INVALID;
+  if ((logits && !aligned(logits, 4)) || (bias && !aligned(bias, 4))) return RGT_ERR_INVALID;
+  const Layout L = make_layout(m, n, k, topk);
+  if ((st = check_ws(ws, ws_bytes, L.total)) != RGT_OK) return st;
+  const Plan p = make_plan(m, n, k);
+  if (p.mb * p.nb > kMaxTileCounters) return RGT_ERR_UNSUPPORTED;
+  char* base = static_cast<char*>(ws);
+  float* lg = logits ? logits : reinterpret_cast<float*>(base + L.logits);
+  GemvArgs g{static_cast<const u16*>(x), ldx, static_cast<const u16*>(w), ldw, lg,
+             reinterpret_cast<float*>(base + L.part), reinterpret_cast<u32*>(base + L.ctr), m, n, k, p.s, p.nb};
+
+  bool fuse = m <= kFusedMaxM && !env_int("RGT_NO_FUSE", 0);
+  const void* fn = nullptr;
+  size_t lds = 0;
+  if (fuse) {
+    DevInfo di;
+    if (!dev_info(di)) return RGT_ERR_HIP;
+    fn = fused_kernel_for(p, n);
+    lds = fused_lds_bytes(p, m, n, topk);
+    const int units = m * (k / 16);
+    // Co-residency is required for the device-side waits; each thread owns at
+    // most one quant unit.
+    if (p.grid > coresident_blocks(fn, lds, di.cus) || units > p.grid * 256) fuse = false;
+  }
+  if (fuse) {
+    FusedArgs a{g, bias, topk, block, topk_ids, topk_w, sorted_ids, expert_ids, offsets, a_q, a_scale,
+                reinterpret_cast<u32*>(base + L.ctl), wait_budget_ticks(), env_int("RGT_FAULT_INJECT", 0)};
+    void* args[] = {&a};
+    if (hipLaunchKernel(fn, dim3(p.grid), dim3(256), args, lds, stream) != hipSuccess) return RGT_ERR_HIP;
+    g_last_launches = 1;
+    return launched();
+  }
+  launch_router(g, p, stream);
+  launch_gate(lg, bias, m, n, topk, topk_ids, topk_w, stream);
+  const int nl = launch_sort_quant(topk_ids, static_cast<const uint16_t*>(x), ldx, m, n, k, topk, block, sorted_ids,
+                                   expert_ids, offsets, a_q, a_scale, base, L, stream);
+  g_last_launches = 2 + nl;
+  return launched();
+}
+
+}  // extern "C"

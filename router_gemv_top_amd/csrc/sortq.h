@@ -1,0 +1,309 @@
+// sortq.h - token -> expert sort into block-padded segments, and the MXFP8
+// gather-quant of the activations.
+//
+// Sort (sglang PR #46691, Summary: MoE sorting + quant; "Kimi-K3: fused MoE
+// routing, sort, quant and epilogue", review snippet on the stable rank):
+// pair p = m*k + j goes to expert e = ids[m][j]; segment e starts at
+// offsets[e] = sum_{e'<e} roundup(cnt[e'], B) and lists its pairs in
+// ascending p, then the sentinel P = M*k up to the block boundary.
+//
+// GPU method: histogram -> exclusive scan -> stable scatter. Stable ranks are
+// built from wave batches of 64 pairs: lanes holding the same expert find one
+// another with one ballot per bit of the expert id, so a lane's rank inside
+// its batch is a popcount; a per-(wave, expert) running count in LDS carries
+// the rank across batches. For decode sizes one workgroup does everything; for
+// large P the histogram is split over workgroups and a scan launch joins them.
+//
+// Quant (OCP MX: e8m0 scale per 32 elements, e4m3fn elements; group-32 scales
+// as in the MXFP8 shared-expert commit of sgl-amd-mono PR #56): each lane
+// quantises 16 consecutive elements of a token row; two neighbouring lanes
+// form a 32-element block and exchange their maxima. A token row is read once
+// and its codes are stored to all k padded positions of its pairs.
+#pragma once
+
+#include "device.h"
+
+namespace rgt {
+
+// Lanes in the active mask whose expert id equals mine (bits of e < 2^bits).
+__device__ __forceinline__ u64 match_peers(int e, bool valid, int bits) {
+  u64 peers = ballot64(valid);
+  for (int b = 0; b < bits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const u64 m = ballot64(bit);
+    peers &= bit ? m : ~m;
+  }
+  return peers;
+}
+
+__device__ __forceinline__ int ceil_log2(int n) {
+  int b = 0;
+  while ((1 << b) < n) ++b;
+  return b;
+}
+
+// Exclusive scan of vals[0..n) in LDS (in place), n <= 4 * blockDim.x.
+// Returns the total. Uses scratch[blockDim.x] of LDS.
+__device__ __forceinline__ int block_exclusive_scan(int* vals, int n, int* scratch) {
+  const int t = threadIdx.x, nt = blockDim.x;
+  const int per = (n + nt - 1) / nt;
+  const int b0 = min(n, t * per), b1 = min(n, b0 + per);
+  int local = 0;
+  for (int i = b0; i < b1; ++i) local += vals[i];
+  scratch[t] = local;
+  __syncthreads();
+  // Hillis-Steele inclusive scan of the thread sums.
+  for (int o = 1; o < nt; o <<= 1) {
+    const int v = t >= o ? scratch[t - o] : 0;
+    __syncthreads();
+    scratch[t] += v;
+    __syncthreads();
+  }
+  int run = scratch[t] - local;
+  const int total = scratch[nt - 1];
+  for (int i = b0; i < b1; ++i) {
+    const int v = vals[i];
+    vals[i] = run;
+    run += v;
+  }
+  __syncthreads();
+  return total;
+}
+
+// One-workgroup sort of P pairs. LDS (caller-provided):
+//   s_e[P]      expert of each pair
+//   s_hist[W*N] per-wave counts, turned into per-wave bases
+//   s_cnt[N]    total count per expert
+//   s_off[N+1]  padded segment starts
+//   s_scr[blockDim.x]
+// Results: s_off, s_cnt in LDS; pos[p] (LDS or global) = padded position of p.
+// Returns the padded total.
+template <typename PosPtr>
+__device__ int wg_sort(const int32_t* ids, int P, int N, int B, int* s_e, int* s_hist, int* s_cnt, int* s_off,
+                       int* s_scr, PosPtr pos) {
+  const int t = threadIdx.x, nt = blockDim.x, nw = nt >> 6;
+  const int wave = t >> 6, lane = t & 63;
+  for (int p = t; p < P; p += nt) s_e[p] = ids[p];
+  for (int i = t; i < nw * N; i += nt) s_hist[i] = 0;
+  __syncthreads();
+  // Pass 1: per-wave histograms over contiguous chunks of pairs.
+  const int chunk = ((P + nw - 1) / nw + 63) & ~63;
+  const int c0 = min(P, wave * chunk), c1 = min(P, c0 + chunk);
+  for (int p = c0 + lane; p < c1; p += 64) {
+    const int e = s_e[p];
+    if ((unsigned)e < (unsigned)N) atomicAdd(&s_hist[wave * N + e], 1);
+  }
+  __syncthreads();
+  // Per-expert totals; per-wave counts become exclusive per-wave bases.
+  for (int e = t; e < N; e += nt) {
+    int run = 0;
+    for (int w = 0; w < nw; ++w) {
+      const int c = s_hist[w * N + e];
+      s_hist[w * N + e] = run;
+      run += c;
+    }
+    s_cnt[e] = run;
+    s_off[e] = (run + B - 1) / B * B;
+  }
+  __syncthreads();
+  const int total = block_exclusive_scan(s_off, N, s_scr);
+  if (t == 0) s_off[N] = total;
+  __syncthreads();
+  // Pass 2: stable ranks inside each wave's chunk, batch by batch.
+  const int bits = ceil_log2(N);
+  for (int base = c0; base < c1; base += 64) {
+    const int p = base + lane;
+    const int e = p < c1 ? s_e[p] : 0;
+    // Expert ids outside [0, N) are a caller error: such pairs are left out
+    // of the sort (position -1) instead of indexing out of bounds.
+    const bool valid = p < c1 && (unsigned)e < (unsigned)N;
+    const u64 peers = match_peers(e, valid, bits);
+    if (valid) {
+      const int rank = __popcll(peers & lanemask_lt());
+      pos[p] = s_off[e] + s_hist[wave * N + e] + rank;
+    } else if (p < c1) {
+      pos[p] = -1;
+    }
+    // Order the reads above before the leader's update (same wave, LDS is in order).
+    if (valid && (peers & lanemask_lt()) == 0ull) s_hist[wave * N + e] += __popcll(peers);
+  }
+  __syncthreads();
+  return total;
+}
+
+// Write offsets, sentinel pads of sorted_ids and expert_ids from the LDS
+// results of a sort. Pair entries of sorted_ids are written by the caller.
+__device__ __forceinline__ void write_sort_layout(const int* s_cnt, const int* s_off, int N, int B, int P,
+                                                  int32_t* sorted_ids, int32_t* expert_ids, int32_t* offsets) {
+  for (int e = threadIdx.x; e <= N; e += blockDim.x) offsets[e] = s_off[e];
+  for (int e = threadIdx.x; e < N; e += blockDim.x) {
+    const int a = s_off[e], b = s_off[e + 1];
+    for (int q = a + s_cnt[e]; q < b; ++q) sorted_ids[q] = P;
+    for (int blk = a / B; blk < b / B; ++blk) expert_ids[blk] = e;
+  }
+}
+
+// Decode-size sort: one workgroup. pos goes to the workspace for the quant.
+__global__ void __launch_bounds__(256) sort_small_kernel(const int32_t* ids, int P, int N, int B,
+                                                         int32_t* sorted_ids, int32_t* expert_ids,
+                                                         int32_t* offsets, int32_t* pos_ws) {
+  extern __shared__ int smem[];
+  int* s_e = smem;
+  int* s_hist = s_e + P;
+  int* s_cnt = s_hist + 4 * N;
+  int* s_off = s_cnt + N;
+  int* s_scr = s_off + N + 1;
+  wg_sort(ids, P, N, B, s_e, s_hist, s_cnt, s_off, s_scr, pos_ws);
+  for (int p = threadIdx.x; p < P; p += blockDim.x) {
+    const int q = pos_ws[p];
+    if (q >= 0) sorted_ids[q] = p;
+  }
+  write_sort_layout(s_cnt, s_off, N, B, P, sorted_ids, expert_ids, offsets);
+}
+
+// ---------------------------------------------------------------------------
+// Large-P sort: per-workgroup histograms -> one scan workgroup -> scatter.
+// Workgroup g owns pairs [g*chunk, (g+1)*chunk).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) sort_hist_kernel(const int32_t* ids, int P, int N, int chunk, int32_t* ghist) {
+  extern __shared__ int s_h[];
+  for (int e = threadIdx.x; e < N; e += blockDim.x) s_h[e] = 0;
+  __syncthreads();
+  const int p0 = blockIdx.x * chunk, p1 = min(P, p0 + chunk);
+  for (int p = p0 + threadIdx.x; p < p1; p += blockDim.x) {
+    const int e = ids[p];
+    if ((unsigned)e < (unsigned)N) atomicAdd(&s_h[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < N; e += blockDim.x) ghist[(int64_t)blockIdx.x * N + e] = s_h[e];
+}
+
+__global__ void __launch_bounds__(1024) sort_scan_kernel(int32_t* ghist, int G, int P, int N, int B,
+                                                         int32_t* sorted_ids, int32_t* expert_ids,
+                                                         int32_t* offsets, int32_t* off_ws) {
+  extern __shared__ int smem[];
+  int* s_cnt = smem;
+  int* s_off = s_cnt + N;
+  int* s_scr = s_off + N + 1;
+  for (int e = threadIdx.x; e < N; e += blockDim.x) {
+    int run = 0;
+    for (int g = 0; g < G; ++g) {
+      const int c = ghist[(int64_t)g * N + e];
+      ghist[(int64_t)g * N + e] = run;
+      run += c;
+    }
+    s_cnt[e] = run;
+    s_off[e] = (run + B - 1) / B * B;
+  }
+  __syncthreads();
+  const int total = block_exclusive_scan(s_off, N, s_scr);
+  if (threadIdx.x == 0) s_off[N] = total;
+  __syncthreads();
+  for (int e = threadIdx.x; e <= N; e += blockDim.x) off_ws[e] = s_off[e];
+  write_sort_layout(s_cnt, s_off, N, B, P, sorted_ids, expert_ids, offsets);
+}
+
+__global__ void __launch_bounds__(256) sort_scatter_kernel(const int32_t* ids, int P, int N, int chunk,
+                                                           const int32_t* ghist, const int32_t* off_ws,
+                                                           int32_t* sorted_ids, int32_t* pos_ws) {
+  extern __shared__ int smem[];
+  int* s_hist = smem;            // [4][N] per-wave counts -> bases
+  int* s_base = s_hist + 4 * N;  // [N] offsets + this workgroup's global base
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int p0 = blockIdx.x * chunk, p1 = min(P, p0 + chunk);
+  for (int i = t; i < 4 * N; i += blockDim.x) s_hist[i] = 0;
+  for (int e = t; e < N; e += blockDim.x) s_base[e] = off_ws[e] + ghist[(int64_t)blockIdx.x * N + e];
+  __syncthreads();
+  const int sub = ((p1 - p0 + 3) / 4 + 63) & ~63;
+  const int c0 = min(p1, p0 + wave * sub), c1 = min(p1, c0 + sub);
+  for (int p = c0 + lane; p < c1; p += 64) {
+    const int e = ids[p];
+    if ((unsigned)e < (unsigned)N) atomicAdd(&s_hist[wave * N + e], 1);
+  }
+  __syncthreads();
+  for (int e = t; e < N; e += blockDim.x) {
+    int run = 0;
+    for (int w = 0; w < 4; ++w) {
+      const int c = s_hist[w * N + e];
+      s_hist[w * N + e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  const int bits = ceil_log2(N);
+  for (int base = c0; base < c1; base += 64) {
+    const int p = base + lane;
+    const int e = p < c1 ? ids[p] : 0;
+    const bool valid = p < c1 && (unsigned)e < (unsigned)N;
+    const u64 peers = match_peers(e, valid, bits);
+    if (valid) {
+      const int q = s_base[e] + s_hist[wave * N + e] + __popcll(peers & lanemask_lt());
+      pos_ws[p] = q;
+      sorted_ids[q] = p;
+    } else if (p < c1) {
+      pos_ws[p] = -1;
+    }
+    if (valid && (peers & lanemask_lt()) == 0ull) s_hist[wave * N + e] += __popcll(peers);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MXFP8 of 16 consecutive bf16 elements (two 16-byte loads). The partner lane
+// (lane ^ 1) holds the other half of the 32-element block. Returns the 16
+// codes packed little-endian in a uint4 and the block's scale byte.
+// Must be called by both lanes of a pair.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint4 mx_quant16(const uint16_t* src, u32& scale_byte) {
+  const uint4 a = *reinterpret_cast<const uint4*>(src);
+  const uint4 b = *reinterpret_cast<const uint4*>(src + 8);
+  const u32 w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  u32 amax = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const u32 lo = w[i] & 0x7fffu, hi = (w[i] >> 16) & 0x7fffu;
+    amax = lo > amax ? lo : amax;
+    amax = hi > amax ? hi : amax;
+  }
+  const u32 other = (u32)__shfl_xor((int)amax, 1, kWave);
+  amax = other > amax ? other : amax;
+  const int se = mx_shared_exp(amax);
+  scale_byte = (u32)(se + 127);
+  u32 c[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const u32 w0 = w[2 * q], w1 = w[2 * q + 1];
+    c[q] = e4m3_of_bf16(w0 & 0xffffu, se) | (e4m3_of_bf16(w0 >> 16, se) << 8) |
+           (e4m3_of_bf16(w1 & 0xffffu, se) << 16) | (e4m3_of_bf16(w1 >> 16, se) << 24);
+  }
+  return make_uint4(c[0], c[1], c[2], c[3]);
+}
+
+// Quantise unit u (token t = u / (K/16), chunk c = u % (K/16)) and store it to
+// the padded positions pos[t*k + j], j < k. Lanes of a pair call together.
+__device__ __forceinline__ void quant_unit_store(const uint16_t* x, int64_t ldx, int K, int k, int u, bool active,
+                                                 const int32_t* pos, uint8_t* a_q, uint8_t* a_scale) {
+  const int cpr = K >> 4;  // 16-element chunks per row
+  const int t = u / cpr, c = u - t * cpr;
+  u32 sb = 0;
+  uint4 codes = make_uint4(0, 0, 0, 0);
+  // Both lanes of a pair are active together (unit counts are even), so the
+  // shuffle inside mx_quant16 always has its partner.
+  if (active) codes = mx_quant16(x + (int64_t)t * ldx + 16 * c, sb);
+  if (!active) return;
+  const int64_t kscale = K >> 5;
+  for (int j = 0; j < k; ++j) {
+    const int64_t d = pos[t * k + j];
+    if (d < 0) continue;
+    *reinterpret_cast<uint4*>(a_q + d * K + 16 * c) = codes;
+    if ((c & 1) == 0) a_scale[d * kscale + (c >> 1)] = (uint8_t)sb;
+  }
+}
+
+__global__ void __launch_bounds__(256) quant_kernel(const uint16_t* x, int64_t ldx, int M, int K, int k,
+                                                    const int32_t* pos, uint8_t* a_q, uint8_t* a_scale) {
+  const int units = M * (K >> 4);
+  const int u = blockIdx.x * blockDim.x + threadIdx.x;
+  quant_unit_store(x, ldx, K, k, u, u < units, pos, a_q, a_scale);
+}
+
+}  // namespace rgt

@@ -1,0 +1,169 @@
+"""GPU parity of the fused front end (rgt_route_sort_quant).
+
+For M <= 64 it is one launch; its outputs must be bit-identical to the
+unfused chain (router_logits -> topk_gate -> moe_sort_quant) on the same
+inputs, logits within tolerance of the oracle, and every later stage
+bit-exact against the oracle fed the GPU's own logits.
+"""
+import numpy as np
+import pytest
+
+from _helpers import CANARY, check_logits, check_sort_quant, say, to_dev, to_dev_bf16
+from oracle import rgt_oracle as O
+from router_gemv_top_amd.inputs import (Workload, gen_skew_bias, gen_w, gen_x, workload_prefill_896,
+                                        workload_tiny, workloads_decode_128, workloads_decode_896,
+                                        workloads_wide_128)
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def R():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import router_gemv_top_amd as R
+    R.lib()
+    return R
+
+
+def fused(R, x, w, bias, k, block, ws, want_logits=True):
+    m, kdim = x.shape
+    n = w.shape[0]
+    out = R.alloc_sort_outputs(m, n, kdim, k, block, fill=CANARY)
+    out["topk_ids"] = torch.empty((m, k), dtype=torch.int32, device="cuda")
+    out["topk_w"] = torch.empty((m, k), dtype=torch.float32, device="cuda")
+    out["logits"] = torch.empty((m, n), dtype=torch.float32, device="cuda") if want_logits else None
+    R.route_sort_quant(to_dev_bf16(x), to_dev_bf16(w), k, block, ws, bias=None if bias is None else to_dev(bias),
+                       out=out)
+    launches = R.last_launch_count()
+    torch.cuda.synchronize()
+    return out, launches
+
+
+def chain(R, x, w, bias, k, block, ws):
+    m, kdim = x.shape
+    n = w.shape[0]
+    xd = to_dev_bf16(x)
+    logits = R.router_logits(xd, to_dev_bf16(w), ws)
+    ids, tw = R.topk_gate(logits, k, bias=None if bias is None else to_dev(bias))
+    out = R.alloc_sort_outputs(m, n, kdim, k, block, fill=CANARY)
+    R.moe_sort_quant(ids, xd, n, block, ws, out=out)
+    out.update(logits=logits, topk_ids=ids, topk_w=tw)
+    torch.cuda.synchronize()
+    return out
+
+
+def np_out(out):
+    return {k: (v.cpu().numpy() if v is not None else None) for k, v in out.items()}
+
+
+def check_against_oracle(x, w, bias, k, block, o):
+    check_logits(x, w, o["logits"])
+    rid, rw = O.topk_gate(o["logits"], bias, k)
+    np.testing.assert_array_equal(o["topk_ids"], rid)
+    np.testing.assert_array_equal(o["topk_w"].view(np.uint32), rw.view(np.uint32))
+    return rid
+
+
+def sort_out(o):
+    return {k: torch.from_numpy(o[k]) for k in ("sorted_ids", "expert_ids", "offsets", "a_q", "a_scale")}
+
+
+DECODE = ([workload_tiny()] + workloads_decode_128() + workloads_decode_896() +
+          [Workload(f"ragged_M{m}", m, 128, 6144, 8, 16) for m in (3, 13, 33, 50)] +
+          [Workload("b64_M24", 24, 128, 6144, 8, 64), Workload("b32_k4_M16", 16, 128, 6144, 4, 32)])
+
+
+@pytest.mark.parametrize("wl", DECODE, ids=lambda w: w.name)
+def test_fused_decode_matches_chain_and_oracle(R, wl):
+    say(f"fused {wl.name} M={wl.m} N={wl.n} K={wl.k} k={wl.topk} B={wl.block}")
+    x, w, b = wl.make()
+    ws = R.Workspace(wl.m, wl.n, wl.k, wl.topk, wl.block)
+    f, launches = fused(R, x, w, b, wl.topk, wl.block, ws)
+    assert launches == 1, "decode sizes must run as one launch"
+    fo = np_out(f)
+    c = np_out(chain(R, x, w, b, wl.topk, wl.block, ws))
+    for key in ("logits", "topk_ids", "topk_w", "offsets"):
+        np.testing.assert_array_equal(fo[key].view(np.uint32) if fo[key].dtype == np.float32 else fo[key],
+                                      c[key].view(np.uint32) if c[key].dtype == np.float32 else c[key],
+                                      err_msg=key)
+    total = int(fo["offsets"][-1])
+    for key in ("sorted_ids", "a_q", "a_scale"):
+        np.testing.assert_array_equal(fo[key][:total], c[key][:total], err_msg=key)
+    ids = check_against_oracle(x, w, b, wl.topk, wl.block, fo)
+    check_sort_quant(sort_out(fo), ids, x, wl.n, wl.block)
+    ctl = ws.buf[: 256 + 4 * 8192].view(torch.int32).cpu().numpy()
+    assert np.all(ctl == 0), "counters and flags must be back at zero"
+
+
+def test_fused_without_logits_output(R):
+    say("fused without logits output")
+    wl = Workload("nolog_M16", 16, 896, 3584, 16, 16, bias=True)
+    x, w, b = wl.make()
+    ws = R.Workspace(wl.m, wl.n, wl.k, wl.topk, wl.block)
+    f, launches = fused(R, x, w, b, wl.topk, wl.block, ws, want_logits=False)
+    g, _ = fused(R, x, w, b, wl.topk, wl.block, ws, want_logits=True)
+    assert launches == 1
+    for key in ("topk_ids", "topk_w", "sorted_ids", "offsets"):
+        np.testing.assert_array_equal(f[key].cpu().numpy(), g[key].cpu().numpy())
+
+
+def test_fused_random_m_sequence_one_workspace(R):
+    say("fused random M sequence on one workspace")
+    n, kdim, k, block = 128, 6144, 8, 16
+    w = gen_w(n, kdim, seed=21)
+    ws = R.Workspace(64, n, kdim, k, block)
+    rng = np.random.default_rng(22)
+    for i, m in enumerate(rng.integers(1, 65, size=10).tolist() + [64, 1, 9, 8]):
+        x = gen_x(m, kdim, seed=200 + i)
+        f, launches = fused(R, x, w, None, k, block, ws)
+        assert launches == 1
+        fo = np_out(f)
+        ids = check_against_oracle(x, w, None, k, block, fo)
+        check_sort_quant(sort_out(fo), ids, x, n, block)
+    ctl = ws.buf[: 256 + 4 * 8192].view(torch.int32).cpu().numpy()
+    assert np.all(ctl == 0)
+
+
+def test_fused_deterministic_and_skewed(R):
+    say("fused determinism with skewed routing")
+    n, kdim, k, block, m = 128, 6144, 8, 16, 48
+    x = gen_x(m, kdim, seed=31)
+    x[5] = x[40]
+    w = gen_w(n, kdim, seed=31)
+    b = gen_skew_bias(n, hot=9, seed=31)
+    ws = R.Workspace(m, n, kdim, k, block)
+    outs = [np_out(fused(R, x, w, b, k, block, ws)[0]) for _ in range(3)]
+    for o in outs[1:]:
+        for key in ("logits", "topk_ids", "topk_w", "sorted_ids", "a_q", "a_scale", "offsets"):
+            np.testing.assert_array_equal(o[key], outs[0][key], err_msg=key)
+    np.testing.assert_array_equal(outs[0]["logits"][5].view(np.uint32), outs[0]["logits"][40].view(np.uint32))
+    ids = check_against_oracle(x, w, b, k, block, outs[0])
+    check_sort_quant(sort_out(outs[0]), ids, x, n, block)
+
+
+@pytest.mark.parametrize("wl", workloads_wide_128(), ids=lambda w: w.name)
+def test_route_sort_quant_wide(R, wl):
+    say(f"route_sort_quant wide {wl.name}")
+    x, w, b = wl.make()
+    ws = R.Workspace(wl.m, wl.n, wl.k, wl.topk, wl.block)
+    f, launches = fused(R, x, w, b, wl.topk, wl.block, ws)
+    fo = np_out(f)
+    ids = check_against_oracle(x, w, b, wl.topk, wl.block, fo)
+    rng = np.random.default_rng(3)
+    check_sort_quant(sort_out(fo), ids, x, wl.n, wl.block,
+                     sample_rows=lambda nv: rng.choice(nv, size=min(nv, 600), replace=False))
+
+
+def test_route_sort_quant_prefill(R):
+    wl = workload_prefill_896()
+    say(f"route_sort_quant prefill {wl.name} M={wl.m}")
+    x, w, b = wl.make()
+    ws = R.Workspace(wl.m, wl.n, wl.k, wl.topk, wl.block)
+    f, launches = fused(R, x, w, b, wl.topk, wl.block, ws)
+    fo = np_out(f)
+    ids = check_against_oracle(x, w, b, wl.topk, wl.block, fo)
+    rng = np.random.default_rng(4)
+    check_sort_quant(sort_out(fo), ids, x, wl.n, wl.block,
+                     sample_rows=lambda nv: rng.choice(nv, size=800, replace=False))

@@ -1,0 +1,88 @@
+"""GPU parity of the softmax top-k gate (rgt_topk_gate): bit-exact against the
+oracle fed the same logits (ids and fp32 weights)."""
+import numpy as np
+import pytest
+
+from _helpers import say, to_dev, to_dev_bf16
+from oracle import rgt_oracle as O
+from router_gemv_top_amd.inputs import gen_bias, gen_skew_bias, gen_w, gen_x
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def R():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import router_gemv_top_amd as R
+    R.lib()
+    return R
+
+
+def run_gate(R, logits, k, bias=None):
+    ids, w = R.topk_gate(to_dev(logits), k, bias=None if bias is None else to_dev(bias))
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), w.cpu().numpy()
+
+
+def check_gate(R, logits, k, bias=None):
+    ids, w = run_gate(R, logits, k, bias)
+    rid, rw = O.topk_gate(logits, bias, k)
+    np.testing.assert_array_equal(ids, rid)
+    np.testing.assert_array_equal(w.view(np.uint32), rw.view(np.uint32))
+    assert R.last_launch_count() == 1
+    return ids, w
+
+
+@pytest.mark.parametrize("m,n,k,bias", [(1, 128, 8, False), (64, 128, 8, False), (512, 128, 8, False),
+                                        (1, 896, 16, True), (32, 896, 16, True), (8192, 896, 16, False),
+                                        (5, 16, 4, False), (7, 1024, 32, True), (3, 64, 1, False),
+                                        (9, 48, 32, False)])
+def test_gate_on_router_logits(R, m, n, k, bias):
+    say(f"gate M={m} N={n} k={k} bias={bias}")
+    kdim = 512
+    x = gen_x(m, kdim, seed=m)
+    w = gen_w(n, kdim, seed=n, std=0.5)
+    logits = O.router_logits(x, w)   # any fp32 logits will do: the gate is checked alone
+    b = gen_bias(n, seed=1) if bias else None
+    check_gate(R, logits, k, b)
+
+
+def test_gate_ties_signed_zeros_and_zero_rows(R):
+    say("gate ties / signed zeros / zero rows")
+    rng = np.random.default_rng(0)
+    n, k = 128, 8
+    vals = np.array([-1.0, -0.0, 0.0, 0.5, 2.0, 2.0, -3.0], np.float32)
+    logits = rng.choice(vals, size=(40, n)).astype(np.float32)
+    logits[0] = 0.0
+    logits[1] = -0.0
+    logits[2, ::2] = -0.0
+    check_gate(R, logits, k)
+
+
+def test_gate_duplicate_expert_rows(R):
+    say("gate with duplicated W rows (index tie-break)")
+    n, kdim, k = 896, 3584, 16
+    x = gen_x(16, kdim, seed=2)
+    w = gen_w(n, kdim, seed=2, tie_rows=200)
+    check_gate(R, O.router_logits(x, w), k, gen_bias(n, seed=2))
+
+
+def test_gate_skewed_bias(R):
+    say("gate with a skewing bias")
+    n, kdim, k = 128, 6144, 8
+    x = gen_x(64, kdim, seed=3)
+    w = gen_w(n, kdim, seed=3)
+    ids, _ = check_gate(R, O.router_logits(x, w), k, gen_skew_bias(n, hot=10, seed=3))
+    assert len(np.unique(ids)) <= 10 + 8 * 64
+
+
+def test_gate_extreme_spread(R):
+    say("gate with far-apart scores (weights underflow to 0)")
+    logits = np.zeros((4, 128), np.float32)
+    logits[:, 5] = 300.0
+    logits[:, 7] = 100.0
+    logits[:, 9] = -250.0
+    logits[1] *= -1
+    check_gate(R, logits, 8)
