@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused MoE routing front-end on one MI355X.
+
+Workload: the MiniMax-M3-shaped decode sweep, M in {1,2,4,8,16,32,64} tokens,
+N = 128 experts, K = 6144, bf16 x ~ N(0,1), W ~ N(0, 0.02^2), softmax top-8,
+block-16 padded sort, MXFP8 quant of the gathered rows. One step is one
+rgt_route_sort_quant call per M of the sweep (seven calls, one launch each).
+
+Inputs are synthetic and resident in HBM before timing. Each call reads its
+own copy of W and x, rotating over enough copies (>= 2x the 256 MB last-level
+cache) that the weight read streams from HBM. The timed steps are replayed
+from a HIP graph captured on the launch stream, bracketed by HIP events on
+that stream.
+
+Prints ONE JSON line: value = algorithmic bytes of the K steps / their time
+(GB/s), the per-M microseconds per call, the roofline of the dominant kernel
+and the CPU oracle's rate on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs/call + achieved HBM GB/s, fused route+sort+quant, M=1..64, N=128, K=6144"
+SWEEP = (1, 2, 4, 8, 16, 32, 64)
+N, K, TOPK, BLOCK = 128, 6144, 8, 16
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def algorithmic_bytes(m: int, total: int) -> int:
+    """Bytes the method must move for one call: W and x read once; top-k ids
+    and weights, sorted_ids, expert_ids, offsets, a_q and scales written (only
+    valid rows of a_q; logits stay internal)."""
+    p = m * TOPK
+    return (N * K * 2 + m * K * 2 + p * 8 + total * 4 + (total // BLOCK) * 4 + (N + 1) * 4 +
+            p * K + p * (K // 32))
+
+
+def cpu_baseline(budget_s: float = 12.0):
+    """The oracle (numpy, fp64) on the host: whole sweeps until ~budget_s."""
+    from oracle import rgt_oracle as O
+    from router_gemv_top_amd.inputs import gen_w, gen_x
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # threadpoolctl missing: numpy BLAS threads unknown
+        threads = os.cpu_count() or 1
+    w = gen_w(N, K)
+    xs = {m: gen_x(m, K) for m in SWEEP}
+    nbytes, sweeps = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        for m in SWEEP:
+            out = O.route_sort_quant(xs[m], w, None, TOPK, BLOCK)
+            nbytes += algorithmic_bytes(m, out["total"])
+        sweeps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(nbytes / dt / 1e9, 6), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{sweeps} full sweeps (M=1..64, N=128, K=6144, top-8, B=16) of the fp64 numpy oracle, "
+                      f"{dt:.1f} s; BLAS matmul multithreaded, the rest single-threaded",
+            "seconds": round(dt, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--copies", type=int, default=0, help="W/x copies to rotate over (0 = enough to evict the MALL)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--hot", action="store_true", help="also time with one resident W copy")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
+              f"(the routing front-end has no multi-GPU path in this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import router_gemv_top_amd as R
+    from router_gemv_top_amd.inputs import gen_w, gen_x
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    w_bytes = N * K * 2
+    copies = args.copies or int(np.ceil(2 * MALL_BYTES / w_bytes))
+    w0 = torch.from_numpy(gen_w(N, K).view(np.int16)).view(torch.bfloat16).to(dev)
+    w_all = w0.unsqueeze(0).repeat(copies, 1, 1)                  # [copies][N][K]
+    x_all, outs = {}, {}
+    for m in SWEEP:
+        x0 = torch.from_numpy(gen_x(m, K).view(np.int16)).view(torch.bfloat16).to(dev)
+        x_all[m] = x0.unsqueeze(0).repeat(copies, 1, 1)           # [copies][M][K]
+        o = R.alloc_sort_outputs(m, N, K, TOPK, BLOCK, device=dev)
+        o["topk_ids"] = torch.empty((m, TOPK), dtype=torch.int32, device=dev)
+        o["topk_w"] = torch.empty((m, TOPK), dtype=torch.float32, device=dev)
+        o["logits"] = None
+        outs[m] = o
+    ws = R.Workspace(max(SWEEP), N, K, TOPK, BLOCK, device=dev)
+
+    def call(m, c):
+        R.route_sort_quant(x_all[m][c], w_all[c], TOPK, BLOCK, ws, out=outs[m])
+
+    # Warmup: eager steps (also sizes the co-resident grids once).
+    launches = {}
+    for s in range(args.warmup):
+        for i, m in enumerate(SWEEP):
+            call(m, (s * len(SWEEP) + i) % copies)
+            launches[m] = R.last_launch_count()
+    torch.cuda.synchronize()
+    if ws.check() != 0:
+        raise RuntimeError("device-side wait timed out during warmup")
+    eager_ref = {m: {k: v.clone() for k, v in outs[m].items() if v is not None} for m in SWEEP}
+    totals = {m: int(outs[m]["offsets"][-1].item()) for m in SWEEP}
+    step_bytes = sum(algorithmic_bytes(m, totals[m]) for m in SWEEP)
+
+    def capture(calls):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for (m, c) in calls:
+                call(m, c)
+        return g
+
+    # Timed region: exactly K steps, replayed from one graph.
+    plan = [(m, (s * len(SWEEP) + i) % copies) for s in range(args.steps) for i, m in enumerate(SWEEP)]
+    g_steps = capture(plan)
+    g_steps.replay()                     # untimed replay of the captured graph
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    g_steps.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_steps_ms = ev0.elapsed_time(ev1)
+    if ws.check() != 0:
+        raise RuntimeError("device-side wait timed out in the timed region")
+    for m in SWEEP:   # every replayed call must reproduce the eager outputs
+        for k, v in eager_ref[m].items():
+            if not torch.equal(outs[m][k], v):
+                raise RuntimeError(f"graph replay output {k} differs from eager at M={m}")
+
+    # Per-M launch duration: a graph of `copies` calls of one M, events around it.
+    us_per_call, us_hot = {}, {}
+    for m in SWEEP:
+        g = capture([(m, c) for c in range(copies)])
+        g.replay()
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        g.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        us_per_call[m] = ev0.elapsed_time(ev1) * 1e3 / copies
+        if args.hot:
+            gh = capture([(m, 0)] * 64)
+            gh.replay()
+            torch.cuda.synchronize()
+            ev0.record(stream)
+            gh.replay()
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            us_hot[m] = ev0.elapsed_time(ev1) * 1e3 / 64
+    torch.cuda.synchronize()
+
+    # Floors: a pure streaming read of one W copy, and an almost empty launch.
+    sink = torch.empty(4096, dtype=torch.int32, device=dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in range(copies):
+            R.diag_read(w_all[c], sink, 384, nbytes=w_bytes)
+    g.replay()
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    g.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    read_floor_us = ev0.elapsed_time(ev1) * 1e3 / copies
+    empty_g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(empty_g):
+        for c in range(copies):
+            R.diag_read(w_all[c], sink, 1, nbytes=16)
+    empty_g.replay()
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    empty_g.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    launch_floor_us = ev0.elapsed_time(ev1) * 1e3 / copies
+
+    sweep_bytes = {m: algorithmic_bytes(m, totals[m]) for m in SWEEP}
+    kernel_us_total = sum(us_per_call.values())
+    achieved = sum(sweep_bytes.values()) / (kernel_us_total * 1e-6) / 1e9
+    value = step_bytes * args.steps / (t_steps_ms * 1e-3) / 1e9
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_steps_ms / args.steps, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "MiniMax-M3 decode sweep: M=1,2,4,8,16,32,64; N=128; K=6144; top-8; "
+                               "block 16; MXFP8 quant; cold W (rotating copies)",
+                   "w_copies": copies, "timing": "HIP graph replay, HIP events on the launch stream"},
+        "us_per_call": {str(m): round(us_per_call[m], 3) for m in SWEEP},
+        "gbs_per_call": {str(m): round(sweep_bytes[m] / (us_per_call[m] * 1e-6) / 1e9, 1) for m in SWEEP},
+        "w_read_gbs": {str(m): round(w_bytes / (us_per_call[m] * 1e-6) / 1e9, 1) for m in SWEEP},
+        "launches_per_call": {str(m): launches[m] for m in SWEEP},
+        "floor_us": {"empty_launch": round(launch_floor_us, 3),
+                     "stream_read_W": round(read_floor_us, 3)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": None,
+                     "kernel": "fused route_sort_quant (one launch per call), averaged over the sweep"},
+    }
+    if args.hot:
+        line["us_per_call_hot"] = {str(m): round(us_hot[m], 3) for m in SWEEP}
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -31,9 +31,11 @@
  *   - The workspace is caller-owned device memory of at least
  *     rgt_workspace_bytes(...) bytes, aligned to 256 bytes. It must be
  *     zero-filled ONCE when created (rgt_reset_workspace does this); every
- *     call leaves its counters at zero again on exit, so no memset is needed
- *     between calls. One workspace serves one stream: two calls that overlap
- *     in time on one workspace race on its counters.
+ *     call leaves it ready for the next one (arrival counters back at zero;
+ *     one phase counter only grows and is read relative to its value at the
+ *     start of each call), so no memset is needed between calls. One
+ *     workspace serves one stream: two calls that overlap in time on one
+ *     workspace race on its counters.
  *   - Coverage. A shape outside coverage returns RGT_ERR_UNSUPPORTED and the
  *     caller may fall back to another implementation; this is the only status
  *     meant for fallback. Covered: 1 <= K, K % 512 == 0; 1 <= N <= 1024,
@@ -160,6 +162,17 @@ rgt_status rgt_route_sort_quant(const void* x, int64_t ldx, const void* w, int64
 /* Number of kernel launches the last successful call of each entry point made
  * on this thread (diagnostics for launch-count checks). */
 int rgt_last_launch_count(void);
+
+/* Measurement helpers (not part of the routing path).
+ * rgt_diag_read: one launch of `grid` workgroups that streams `bytes` (a
+ *   multiple of 16) from device memory `src` with 16-byte loads; `sink` is a
+ *   device uint32 array of `grid` words that receives one word per workgroup.
+ *   It is the floor of any kernel that must read the same bytes.
+ * rgt_diag_copy: one launch copying `bytes` (a multiple of 16) from `src` to
+ *   `dst` (device, 16-byte aligned, not overlapping): a kernel of known
+ *   traffic for calibrating hardware byte counters. */
+rgt_status rgt_diag_read(const void* src, size_t bytes, uint32_t* sink, int grid, hipStream_t stream);
+rgt_status rgt_diag_copy(const void* src, void* dst, size_t bytes, int grid, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -11,7 +11,7 @@ _API = (
     "router_logits", "topk_gate", "moe_sort_quant", "route_sort_quant", "Workspace",
     "workspace_bytes", "sort_capacity", "router_supported", "reset_workspace", "check_workspace",
     "status_string", "last_launch_count", "alloc_sort_outputs", "RgtError", "RgtUnsupported", "lib",
-    "exported_symbols", "version",
+    "exported_symbols", "version", "diag_read", "diag_copy",
 )
 
 

@@ -14,7 +14,8 @@ import threading
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "librgt.so")
+# RGT_LIBRARY selects another build of the same ABI (e.g. librgt_trace.so).
+LIB_PATH = os.environ.get("RGT_LIBRARY") or os.path.join(_HERE, "librgt.so")
 
 RGT_OK, RGT_ERR_UNSUPPORTED, RGT_ERR_INVALID, RGT_ERR_WORKSPACE, RGT_ERR_HIP, RGT_ERR_TIMEOUT = range(6)
 
@@ -66,6 +67,8 @@ def lib() -> ctypes.CDLL:
             "rgt_route_sort_quant": ([vp, i64, vp, i64, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
                                       vp, vp, vp, sz, vp], i32),
             "rgt_last_launch_count": ([], i32),
+            "rgt_diag_read": ([vp, sz, vp, i32, vp], i32),
+            "rgt_diag_copy": ([vp, vp, sz, i32, vp], i32),
         }
         for name, (args, res) in sigs.items():
             fn = getattr(L, name)
@@ -238,3 +241,15 @@ def route_sort_quant(x, w, topk: int, block: int, ws: Workspace, bias=None, out=
                                       _ptr(out["a_q"]), _ptr(out["a_scale"]), _ptr(ws.buf), ws.nbytes,
                                       _stream(stream)), "route_sort_quant")
     return out
+
+
+def diag_read(src, sink, grid: int, nbytes: int | None = None, stream=None):
+    """Stream-read `nbytes` of `src` (default: all of it) in one launch."""
+    nbytes = src.numel() * src.element_size() if nbytes is None else nbytes
+    _check(lib().rgt_diag_read(_ptr(src), nbytes, _ptr(sink), grid, _stream(stream)), "diag_read")
+
+
+def diag_copy(src, dst, grid: int, nbytes: int | None = None, stream=None):
+    """Copy `nbytes` of `src` to `dst` in one launch."""
+    nbytes = src.numel() * src.element_size() if nbytes is None else nbytes
+    _check(lib().rgt_diag_copy(_ptr(src), _ptr(dst), nbytes, grid, _stream(stream)), "diag_copy")

@@ -27,6 +27,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+TRACE_LIB = os.path.join(PKG, "librgt_trace.so")
+
+
 def build_cmd(out: str = LIB, extra=()) -> list:
     return [
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -42,9 +45,13 @@ def build_cmd(out: str = LIB, extra=()) -> list:
     ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = build_cmd(tmp)
+def build(verbose: bool = False, trace: bool = False) -> str:
+    """Build librgt.so, or with trace=True the phase-stamping variant
+    librgt_trace.so (same ABI; the fused kernel writes per-workgroup clock
+    stamps after the regular workspace regions)."""
+    lib = TRACE_LIB if trace else LIB
+    tmp = lib + ".tmp"
+    cmd = build_cmd(tmp, ("-DRGT_TRACE",) if trace else ())
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -53,9 +60,9 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed building librgt.so")
     if verbose and r.stderr.strip():
         sys.stderr.write(r.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, trace="--trace" in sys.argv))

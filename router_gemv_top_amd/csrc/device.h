@@ -19,6 +19,10 @@ constexpr int kWave = 64;
 // Error bits kept in the workspace error word.
 constexpr u32 kErrTimeout = 1u;
 
+// Every counter sits in its own 128-byte line, so atomics and polls on one
+// counter do not queue behind traffic on another.
+constexpr int kCtrStride = 32;  // u32 words between neighbouring counters
+
 // ---------------------------------------------------------------------------
 // bf16 helpers: a 32-bit word holds two bf16 values, element 0 in the low half.
 // ---------------------------------------------------------------------------
@@ -46,23 +50,51 @@ __device__ __forceinline__ float dot8_bf16(uint4 a, uint4 b, float acc) {
 }
 
 // ---------------------------------------------------------------------------
-// Wave64 reductions. The xor butterfly leaves the same bits in every lane
-// (each step adds the same two operands on both sides), so the result is
-// deterministic and uniform.
+// Wave64 reductions with DPP. Inside each row of 16 lanes four DPP steps
+// (quad_perm xor 1, quad_perm xor 2, row_half_mirror, row_mirror) combine
+// every lane with a partner, so every lane ends with the row result; the four
+// row results are then read as scalars and combined in a fixed order. Every
+// step combines the same two operands on both sides, so the result is
+// deterministic and the same in every lane.
 // ---------------------------------------------------------------------------
+constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror
+constexpr int kDppMirror = 0x140;     // row_mirror
+
+template <int CTRL>
+__device__ __forceinline__ u32 dpp_u32(u32 v) {
+  return (u32)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ u32 umax(u32 a, u32 b) { return a > b ? a : b; }
+__device__ __forceinline__ u32 readlane_u32(u32 v, int l) { return (u32)__builtin_amdgcn_readlane((int)v, l); }
+__device__ __forceinline__ float readlane_f32(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const u64 b = __double_as_longlong(v);
+  const u32 lo = readlane_u32((u32)b, l), hi = readlane_u32((u32)(b >> 32), l);
+  return __longlong_as_double((long long)(((u64)hi << 32) | lo));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp_f32<kDppQuadXor1>(v);
+  v += dpp_f32<kDppQuadXor2>(v);
+  v += dpp_f32<kDppHalfMirror>(v);
+  v += dpp_f32<kDppMirror>(v);
+  return (readlane_f32(v, 0) + readlane_f32(v, 16)) + (readlane_f32(v, 32) + readlane_f32(v, 48));
 }
 
 __device__ __forceinline__ u32 wave_max_u32(u32 v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    u32 t = (u32)__shfl_xor((int)v, o, kWave);
-    v = t > v ? t : v;
-  }
-  return v;
+  v = umax(v, dpp_u32<kDppQuadXor1>(v));
+  v = umax(v, dpp_u32<kDppQuadXor2>(v));
+  v = umax(v, dpp_u32<kDppHalfMirror>(v));
+  v = umax(v, dpp_u32<kDppMirror>(v));
+  return umax(umax(readlane_u32(v, 0), readlane_u32(v, 16)), umax(readlane_u32(v, 32), readlane_u32(v, 48)));
 }
 
 __device__ __forceinline__ u64 ballot64(bool p) { return __ballot(p); }
@@ -76,33 +108,106 @@ __device__ __forceinline__ u64 lanemask_lt() {
 }
 
 // ---------------------------------------------------------------------------
-// Agent-scope arrival counters and bounded waits. Counters live in the
-// caller's workspace; they start at zero and every launch leaves them at zero.
+// Arrival counters and bounded waits. Counters live in the caller's
+// workspace; they start at zero and every launch leaves them at zero.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ u32 atomic_add_agent(u32* p, u32 v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ u32 atomic_load_agent(const u32* p) {
-  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void atomic_store_agent(u32* p, u32 v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void atomic_or_agent(u32* p, u32 v) {
+__device__ __forceinline__ void or_agent(u32* p, u32 v) {
   __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Cross-workgroup data. Values one workgroup hands to another in the same
+// launch (split-K partials, logits, top-k results) are moved with agent-scope
+// relaxed atomic loads and stores: on gfx950 these are device-coherent memory
+// operations (they bypass the non-coherent cache levels), so no L2 write-back
+// or invalidate of the whole cache is needed to hand them over.
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t ld_agent(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ u32 ld_agent(const u32* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ u32 add_agent(u32* p, u32 v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(u32* p, u32 v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(u64* p, u64 v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ u64 ld_agent(const u64* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Tagged words: a 32-bit payload and the 32-bit tag of the call that wrote
+// it, stored and loaded as one 8-byte atomic. A reader polls the word itself
+// until the tag is its own call's, so data and "ready" arrive together and no
+// counter, drain or separate load is needed for that hand-off.
+__device__ __forceinline__ u64 tag_word(u32 payload, u32 tag) { return ((u64)tag << 32) | payload; }
+__device__ __forceinline__ bool tag_ok(u64 w, u32 tag) { return (u32)(w >> 32) == tag; }
+
+// 16-byte device-coherent load (buffer_load_dwordx4 with the sc1 cache
+// policy) from a buffer of `bytes` bytes; out-of-range reads return zeros.
+typedef u32 u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base, u32 bytes) {
+  // 0x00020000: raw 32-bit data format in the descriptor's last word.
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t ld_agent16(__amdgpu_buffer_rsrc_t r, u32 byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 16 /* sc1 */);
+}
+
+// Wait until every vector memory operation this wave issued has completed
+// (stores acknowledged at their scope), and keep the compiler from moving
+// memory operations across this point. Publishing a hand-off is: each wave
+// drains, the workgroup meets at a barrier, then one thread bumps the
+// counter with an agent-scope atomic.
+__device__ __forceinline__ void vm_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Publish this workgroup's agent-scope stores and arrive on a counter.
+// Returns the counter value before the add (in thread 0 only; 0 elsewhere).
+__device__ __forceinline__ u32 publish_arrive(u32* ctr) {
+  vm_drain();
+  __syncthreads();
+  u32 old = 0;
+  if (threadIdx.x == 0) old = add_agent(ctr, 1u);
+  return old;
 }
 
 // Real-time clock at a constant 100 MHz.
 __device__ __forceinline__ u64 rt_clock() { return wall_clock64(); }
 
-// Spin (one thread) until *ctr >= target or the deadline passes. On expiry
-// the error word gets kErrTimeout and false is returned.
-__device__ __forceinline__ bool wait_geq(const u32* ctr, u32 target, u64 budget_ticks, u32* err) {
+// Phase stamps of the trace build (compile with -DRGT_TRACE): thread 0 of each
+// workgroup writes the real-time clock into trace[blockIdx.x * 16 + slot].
+#ifdef RGT_TRACE
+#define RGT_STAMP(trace, slot)                                                         \
+  do {                                                                                 \
+    if (threadIdx.x == 0 && (trace)) (trace)[blockIdx.x * 16 + (slot)] = rgt::rt_clock(); \
+  } while (0)
+#else
+#define RGT_STAMP(trace, slot) \
+  do {                         \
+  } while (0)
+#endif
+
+// Spin (one thread) until *ctr - base >= target (unsigned, so a counter that
+// only grows may wrap) or the deadline passes. On expiry the error word gets
+// kErrTimeout and false is returned.
+__device__ __forceinline__ bool wait_reach(const u32* ctr, u32 base, u32 target, u64 budget_ticks, u32* err) {
   u64 t0 = rt_clock();
-  while (atomic_load_agent(ctr) < target) {
-    __builtin_amdgcn_s_sleep(1);
+  while (ld_agent(ctr) - base < target) {
+    __builtin_amdgcn_s_sleep(2);
     if (rt_clock() - t0 > budget_ticks) {
-      atomic_or_agent(err, kErrTimeout);
+      or_agent(err, kErrTimeout);
       return false;
     }
   }

@@ -19,23 +19,29 @@
 
 namespace rgt {
 
-template <int NV>   // NV = ceil(N / 64) score slots per lane
-__device__ __forceinline__ void wave_topk_row(const float* logits_row, const float* bias, int n, int k,
-                                              int32_t* ids_out, float* w_out) {
+// Add the optional bias to a row held in registers: sv[i] is the score of
+// expert lane + 64*i.
+template <int NV>
+__device__ __forceinline__ void add_bias(float (&sv)[NV], const float* bias, int n) {
+  if (!bias) return;
+  const int lane = lane_id();
+  float bv[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) bv[i] = bias[min(lane + 64 * i, n - 1)];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) sv[i] = __fadd_rn(sv[i], bv[i]);
+}
+
+// Top-k of one row of scores held in registers (sv[i]: expert lane + 64*i,
+// valid below n). Lane j < k ends with the j-th expert in my_id and its
+// renormalised weight in my_w.
+template <int NV>
+__device__ __forceinline__ void wave_topk_regs(const float (&sv)[NV], int n, int k, int& my_id, float& my_w) {
   const int lane = lane_id();
   u32 key[NV];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int e = lane + 64 * i;
-    if (e < n) {
-      float s = logits_row[e];
-      if (bias) s = __fadd_rn(s, bias[e]);
-      key[i] = score_key(s);
-    } else {
-      key[i] = 0u;
-    }
-  }
-  int my_id = 0;
+  for (int i = 0; i < NV; ++i) key[i] = lane + 64 * i < n ? score_key(sv[i]) : 0u;
+  my_id = 0;
   float my_s = 0.f;
   for (int j = 0; j < k; ++j) {
     u32 best = key[0];
@@ -57,14 +63,31 @@ __device__ __forceinline__ void wave_topk_row(const float* logits_row, const flo
     }
   }
   // Renormalised softmax over the k selected scores, slot 0 the largest.
-  const double s0 = (double)__shfl(my_s, 0, kWave);
+  const double s0 = (double)readlane_f32(my_s, 0);
   double e = 0.0;
   if (lane < k) e = exp64_recipe((double)my_s - s0);
-  double total = __shfl(e, 0, kWave);
-  for (int j = 1; j < k; ++j) total = total + __shfl(e, j, kWave);
+  double total = readlane_f64(e, 0);
+  for (int j = 1; j < k; ++j) total = total + readlane_f64(e, j);
+  my_w = lane < k ? (float)(e / total) : 0.f;
+}
+
+// Load a row of logits (all loads issued before any is used: addresses are
+// clamped into the row and there are no branches between them), add the bias
+// and run the top-k; lanes j < k write slot j.
+template <int NV>
+__device__ __forceinline__ void wave_topk_row(const float* logits_row, const float* bias, int n, int k,
+                                              int32_t* ids_out, float* w_out) {
+  const int lane = lane_id();
+  float sv[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) sv[i] = logits_row[min(lane + 64 * i, n - 1)];
+  add_bias<NV>(sv, bias, n);
+  int id;
+  float w;
+  wave_topk_regs<NV>(sv, n, k, id, w);
   if (lane < k) {
-    ids_out[lane] = my_id;
-    w_out[lane] = (float)(e / total);
+    ids_out[lane] = id;
+    w_out[lane] = w;
   }
 }
 

@@ -31,7 +31,7 @@ struct GemvArgs {
   int64_t ldw;
   float* logits;   // [M][N]
   float* part;     // [S][M][N] fp32 partials (workspace)
-  u32* ctr;        // [MB*NB] arrival counters (workspace, zero between calls)
+  u32* ctr;        // [MB*NB] arrival counters, kCtrStride words apart (zero between calls)
   int m, n, k;
   int s_count;     // S: number of k-slices
   int nb_count;    // NB: number of n-blocks
@@ -79,7 +79,7 @@ __device__ __forceinline__ void valu_tile(const GemvArgs& a, int nb, int s) {
   for (int r = 0; r < RPW; ++r)
 #pragma unroll
     for (int m = 0; m < MT; ++m)
-      if (lane == r * MT + m && m < a.m) part[(int64_t)m * a.n + nrow0 + r] = acc[r][m];
+      if (lane == r * MT + m && m < a.m) st_agent(&part[(int64_t)m * a.n + nrow0 + r], acc[r][m]);
 }
 
 // ---------------------------------------------------------------------------
@@ -131,49 +131,78 @@ __device__ __forceinline__ void mfma_tile(const GemvArgs& a, int mb, int nb, int
     v += lds[((1 * MT + t) * 16 + rr) * 16 + cc];
     v += lds[((2 * MT + t) * 16 + rr) * 16 + cc];
     v += lds[((3 * MT + t) * 16 + rr) * 16 + cc];
-    if (m < a.m) part[(int64_t)m * a.n + nb * 16 + cc] = v;
+    if (m < a.m) st_agent(&part[(int64_t)m * a.n + nb * 16 + cc], v);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Split-K fixup. Every thread publishes its partial stores, then one thread
-// arrives on the tile counter. Returns true in the last workgroup to arrive,
-// after an acquire so the other workgroups' partials are visible.
+// Split-K fixup. The partials were stored with agent-scope stores; the
+// workgroup drains them, then one thread arrives on the tile counter. Returns
+// true in the last workgroup to arrive: by then every other workgroup's
+// partials are complete, and agent-scope loads read them coherently.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ bool arrive_last(u32* ctr, u32 arrivals) {
   __shared__ u32 s_last;
-  __threadfence();
+  const u32 old = publish_arrive(ctr);
+  if (threadIdx.x == 0) s_last = (old == arrivals - 1u) ? 1u : 0u;
   __syncthreads();
-  if (threadIdx.x == 0) s_last = (atomic_add_agent(ctr, 1u) == arrivals - 1u) ? 1u : 0u;
-  __syncthreads();
-  const bool last = s_last != 0u;
-  if (last) __threadfence();
-  return last;
+  return s_last != 0u;
 }
 
 // Sum the S partials of rows [r0, r1) x columns [c0, c0+bn) in k-slice order
-// into dst (row stride n).
-__device__ __forceinline__ void reduce_partials(const GemvArgs& a, int r0, int r1, int c0, int bn, float* dst) {
-  const int rows = r1 - r0;
-  for (int idx = threadIdx.x; idx < rows * bn; idx += blockDim.x) {
-    const int m = r0 + idx / bn, c = c0 + idx % bn;
-    const float* p = a.part + (int64_t)m * a.n + c;
-    const int64_t stride = (int64_t)a.m * a.n;
-    float v = 0.f;
-#pragma unroll 8
-    for (int s = 0; s < a.s_count; ++s) v += p[s * stride];
-    dst[(int64_t)m * a.n + c] = v;
+// (s = 0, 1, ..., S-1 for every output, so every path that reduces the same
+// partials gets the same bits). Each thread takes 4 neighbouring columns of one
+// row and loads their partials with 16-byte coherent loads, 12 k-slices in
+// flight at a time; out(m, c, sums) receives the 4 sums of columns c..c+3.
+constexpr int kReduceBatch = 12;
+
+template <class Out>
+__device__ __forceinline__ void reduce_partials(const GemvArgs& a, int r0, int r1, int c0, int bn, Out out) {
+  const int rows = r1 - r0, quads = bn >> 2;
+  const u32 slice = (u32)a.m * (u32)a.n * 4u;
+  const auto rsrc = coherent_rsrc(a.part, slice * (u32)a.s_count);
+  for (int idx = threadIdx.x; idx < rows * quads; idx += blockDim.x) {
+    const int m = r0 + idx / quads, c = c0 + 4 * (idx % quads);
+    const u32 off = ((u32)m * (u32)a.n + (u32)c) * 4u;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s0 = 0; s0 < a.s_count; s0 += kReduceBatch) {
+      u32x4_t v[kReduceBatch];
+      // Slices past S read beyond the buffer and come back as zeros; they are
+      // not added.
+#pragma unroll
+      for (int j = 0; j < kReduceBatch; ++j) v[j] = ld_agent16(rsrc, off + (u32)(s0 + j) * slice);
+#pragma unroll
+      for (int j = 0; j < kReduceBatch; ++j) {
+        if (s0 + j < a.s_count) {
+          acc.x += __uint_as_float(v[j].x);
+          acc.y += __uint_as_float(v[j].y);
+          acc.z += __uint_as_float(v[j].z);
+          acc.w += __uint_as_float(v[j].w);
+        }
+      }
+    }
+    out(m, c, acc);
   }
 }
+
+// Writer of plain fp32 logits (read by later launches).
+struct LogitsOut {
+  float* logits;
+  int n;
+  __device__ __forceinline__ void operator()(int m, int c, float4 v) const {
+    *reinterpret_cast<float4*>(logits + (int64_t)m * n + c) = v;
+  }
+};
 
 // Standalone router kernels: tile, then fixup by the last arriver.
 template <int MT, int RPW, int L>
 __global__ void __launch_bounds__(256) router_valu_kernel(GemvArgs a) {
   const int nb = blockIdx.x % a.nb_count, s = blockIdx.x / a.nb_count;
   valu_tile<MT, RPW, L>(a, nb, s);
-  if (arrive_last(a.ctr + nb, (u32)a.s_count)) {
-    reduce_partials(a, 0, a.m, nb * 4 * RPW, 4 * RPW, a.logits);
-    if (threadIdx.x == 0) atomic_store_agent(a.ctr + nb, 0u);
+  u32* ctr = a.ctr + nb * kCtrStride;
+  if (arrive_last(ctr, (u32)a.s_count)) {
+    reduce_partials(a, 0, a.m, nb * 4 * RPW, 4 * RPW, LogitsOut{a.logits, a.n});
+    if (threadIdx.x == 0) st_agent(ctr, 0u);
   }
 }
 
@@ -185,12 +214,12 @@ __global__ void __launch_bounds__(256) router_mfma_kernel(GemvArgs a) {
   const int s = (blockIdx.x / tiles) % a.s_count;
   const int mb = blockIdx.x / (tiles * a.s_count);
   mfma_tile<MT, KS>(a, mb, nb, s, lds);
-  u32* ctr = a.ctr + mb * a.nb_count + nb;
+  u32* ctr = a.ctr + (mb * a.nb_count + nb) * kCtrStride;
   if (arrive_last(ctr, (u32)a.s_count)) {
     const int r0 = mb * 16 * MT;
     const int r1 = min(a.m, r0 + 16 * MT);
-    reduce_partials(a, r0, r1, nb * 16, 16, a.logits);
-    if (threadIdx.x == 0) atomic_store_agent(ctr, 0u);
+    reduce_partials(a, r0, r1, nb * 16, 16, LogitsOut{a.logits, a.n});
+    if (threadIdx.x == 0) st_agent(ctr, 0u);
   }
 }
 

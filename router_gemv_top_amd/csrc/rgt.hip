@@ -15,6 +15,7 @@
 
 #include "rgt.h"
 #include "device.h"
+#include "diag.h"
 #include "fused.h"
 #include "gate.h"
 #include "gemv.h"
@@ -26,7 +27,7 @@ namespace {
 
 constexpr int kVersion = 100;  // 0.1.0
 constexpr size_t kAlign = 256;
-constexpr size_t kCtlBytes = 256;          // control words (error, phase counters)
+constexpr size_t kCtlBytes = 512;          // control words (error, phase counters), 128 B apart
 constexpr int kMaxTileCounters = 8192;     // arrival counters for GEMV tiles
 constexpr int kSmallSortMaxP = 8192;       // one-workgroup sort up to this many pairs
 constexpr int kLargeSortChunk = 512;       // pairs per workgroup in the large sort
@@ -77,7 +78,7 @@ Plan make_plan(int m, int n, int k) {
   if (m <= 8) {
     p.valu = true;
     p.mt = pow2_at_least(std::max(m, 1));
-    p.rpw = n <= 256 ? 1 : 2;
+    p.rpw = n <= 256 ? 1 : 4;
     p.bn = 4 * p.rpw;
     p.nb = n / p.bn;
     p.s = k / 512;
@@ -101,7 +102,7 @@ Plan make_plan(int m, int n, int k) {
 // are the only state that must stay zero between calls).
 // ---------------------------------------------------------------------------
 struct Layout {
-  size_t ctl, ctr, part, logits, pos, ghist, offws, total;
+  size_t ctl, ctr, part, logits, tlog, tids, pos, ghist, offws, trace, total;
 };
 
 int large_sort_groups(int P) { return (P + kLargeSortChunk - 1) / kLargeSortChunk; }
@@ -112,13 +113,21 @@ Layout make_layout(int m, int n, int k, int topk) {
   const int P = m * topk;
   size_t o = 0;
   L.ctl = o; o += kCtlBytes;
-  L.ctr = o; o = align_up(o + sizeof(u32) * kMaxTileCounters, kAlign);
+  L.ctr = o; o = align_up(o + sizeof(u32) * kCtrStride * (size_t)kMaxTileCounters, kAlign);
   L.part = o; o = align_up(o + sizeof(float) * (size_t)p.s * m * n, kAlign);
   L.logits = o; o = align_up(o + sizeof(float) * (size_t)m * n, kAlign);
+  L.tlog = L.tids = o;
+  if (m <= kFusedMaxM) {  // tagged hand-off words of the one-launch path
+    L.tlog = o; o = align_up(o + sizeof(u64) * (size_t)m * n, kAlign);
+    L.tids = o; o = align_up(o + sizeof(u64) * (size_t)P, kAlign);
+  }
   L.pos = o; o = align_up(o + sizeof(int32_t) * (size_t)P, kAlign);
   L.ghist = o;
   if (P > kSmallSortMaxP) o = align_up(o + sizeof(int32_t) * (size_t)large_sort_groups(P) * n, kAlign);
   L.offws = o; o = align_up(o + sizeof(int32_t) * (size_t)(n + 1), kAlign);
+#ifdef RGT_TRACE
+  L.trace = o; o = align_up(o + sizeof(u64) * 16 * (size_t)p.grid, kAlign);
+#endif
   L.total = o;
   return L;
 }
@@ -178,7 +187,7 @@ void launch_router_valu(const GemvArgs& a, int grid, hipStream_t st) {
 template <int MT>
 void launch_router_valu_rpw(const GemvArgs& a, const Plan& p, hipStream_t st) {
   if (p.rpw == 1) launch_router_valu<MT, 1>(a, p.grid, st);
-  else launch_router_valu<MT, 2>(a, p.grid, st);
+  else launch_router_valu<MT, 4>(a, p.grid, st);
 }
 
 template <int MT>
@@ -225,7 +234,7 @@ int launch_sort_quant(const int32_t* ids, const uint16_t* x, int64_t ldx, int m,
   int32_t* pos = reinterpret_cast<int32_t*>(ws + L.pos);
   int launches = 0;
   if (P <= kSmallSortMaxP) {
-    const size_t lds = sizeof(int) * ((size_t)P + 4 * n + n + (n + 1) + 256);
+    const size_t lds = sizeof(int) * ((size_t)P + std::max<size_t>(P, 4 * (size_t)n) + n + (n + 1) + 256);
     hipLaunchKernelGGL(sort_small_kernel, dim3(1), dim3(256), lds, st, ids, P, n, block, sorted_ids, expert_ids,
                        offsets, pos);
     ++launches;
@@ -252,7 +261,7 @@ int launch_sort_quant(const int32_t* ids, const uint16_t* x, int64_t ldx, int m,
 // ---------------------------------------------------------------------------
 size_t fused_lds_bytes(const Plan& p, int m, int n, int topk) {
   const size_t P = (size_t)m * topk;
-  const size_t sort = sizeof(int) * (2 * P + 4 * (size_t)n + n + (n + 1) + 256);
+  const size_t sort = sizeof(int) * (3 * P + n + (n + 1));  // s_e, s_rank, s_pos, s_cnt, s_off
   const size_t tile = p.valu ? 0 : sizeof(float) * 4 * p.mt * 256;
   return std::max(sort, tile);
 }
@@ -269,10 +278,10 @@ const void* fused_kernel_ptr(const Plan& p) {
       }
     }
     switch (p.mt) {
-      case 1: return (const void*)fused_valu_kernel<NV, 1, 2, 1>;
-      case 2: return (const void*)fused_valu_kernel<NV, 2, 2, 1>;
-      case 4: return (const void*)fused_valu_kernel<NV, 4, 2, 1>;
-      default: return (const void*)fused_valu_kernel<NV, 8, 2, 1>;
+      case 1: return (const void*)fused_valu_kernel<NV, 1, 4, 1>;
+      case 2: return (const void*)fused_valu_kernel<NV, 2, 4, 1>;
+      case 4: return (const void*)fused_valu_kernel<NV, 4, 4, 1>;
+      default: return (const void*)fused_valu_kernel<NV, 8, 4, 1>;
     }
   }
   if (p.ks == 2) {
@@ -484,11 +493,19 @@ rgt_status rgt_route_sort_quant(const void* x, int64_t ldx, const void* w, int64
     const int units = m * (k / 16);
     // Co-residency is required for the device-side waits; each thread owns at
     // most one quant unit.
-    if (p.grid > coresident_blocks(fn, lds, di.cus) || units > p.grid * 256) fuse = false;
+    if (p.grid > coresident_blocks(fn, lds, di.cus) || units > p.grid * 256 || m * topk > kWaveSortMaxP)
+      fuse = false;
   }
   if (fuse) {
-    FusedArgs a{g, bias, topk, block, topk_ids, topk_w, sorted_ids, expert_ids, offsets, a_q, a_scale,
-                reinterpret_cast<u32*>(base + L.ctl), wait_budget_ticks(), env_int("RGT_FAULT_INJECT", 0)};
+    FusedArgs a{g, bias, topk, block, logits, topk_ids, topk_w, sorted_ids, expert_ids, offsets, a_q, a_scale,
+                reinterpret_cast<u32*>(base + L.ctl), reinterpret_cast<u64*>(base + L.tlog),
+                reinterpret_cast<u64*>(base + L.tids), wait_budget_ticks(), env_int("RGT_FAULT_INJECT", 0),
+#ifdef RGT_TRACE
+                reinterpret_cast<u64*>(base + L.trace)
+#else
+                nullptr
+#endif
+    };
     void* args[] = {&a};
     if (hipLaunchKernel(fn, dim3(p.grid), dim3(256), args, lds, stream) != hipSuccess) return RGT_ERR_HIP;
     g_last_launches = 1;
@@ -499,6 +516,35 @@ rgt_status rgt_route_sort_quant(const void* x, int64_t ldx, const void* w, int64
   const int nl = launch_sort_quant(topk_ids, static_cast<const uint16_t*>(x), ldx, m, n, k, topk, block, sorted_ids,
                                    expert_ids, offsets, a_q, a_scale, base, L, stream);
   g_last_launches = 2 + nl;
+  return launched();
+}
+
+#ifdef RGT_TRACE
+// Trace build only: byte offset of the phase stamps inside the workspace for a
+// fused call of this shape, and the number of workgroups that write them.
+size_t rgt_trace_offset(int m, int n, int k, int topk, int* grid) {
+  if (grid) *grid = make_plan(m, n, k).grid;
+  return make_layout(m, n, k, topk).trace;
+}
+#endif
+
+rgt_status rgt_diag_read(const void* src, size_t bytes, uint32_t* sink, int grid, hipStream_t stream) {
+  g_last_launches = 0;
+  if (!src || !sink || !aligned(src, 16) || !aligned(sink, 4) || bytes % 16 || grid < 1 || grid > 65536)
+    return RGT_ERR_INVALID;
+  hipLaunchKernelGGL(diag_read_kernel, dim3(grid), dim3(256), 0, stream, static_cast<const uint4*>(src), bytes / 16,
+                     sink);
+  g_last_launches = 1;
+  return launched();
+}
+
+rgt_status rgt_diag_copy(const void* src, void* dst, size_t bytes, int grid, hipStream_t stream) {
+  g_last_launches = 0;
+  if (!src || !dst || !aligned(src, 16) || !aligned(dst, 16) || bytes % 16 || grid < 1 || grid > 65536)
+    return RGT_ERR_INVALID;
+  hipLaunchKernelGGL(diag_copy_kernel, dim3(grid), dim3(256), 0, stream, static_cast<const uint4*>(src),
+                     static_cast<uint4*>(dst), bytes / 16);
+  g_last_launches = 1;
   return launched();
 }
 

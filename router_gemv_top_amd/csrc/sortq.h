@@ -78,12 +78,13 @@ __device__ __forceinline__ int block_exclusive_scan(int* vals, int n, int* scrat
 //   s_scr[blockDim.x]
 // Results: s_off, s_cnt in LDS; pos[p] (LDS or global) = padded position of p.
 // Returns the padded total.
-template <typename PosPtr>
+// COH: the ids were written by other workgroups of the same launch.
+template <bool COH, typename PosPtr>
 __device__ int wg_sort(const int32_t* ids, int P, int N, int B, int* s_e, int* s_hist, int* s_cnt, int* s_off,
                        int* s_scr, PosPtr pos) {
   const int t = threadIdx.x, nt = blockDim.x, nw = nt >> 6;
   const int wave = t >> 6, lane = t & 63;
-  for (int p = t; p < P; p += nt) s_e[p] = ids[p];
+  for (int p = t; p < P; p += nt) s_e[p] = COH ? ld_agent(ids + p) : ids[p];
   for (int i = t; i < nw * N; i += nt) s_hist[i] = 0;
   __syncthreads();
   // Pass 1: per-wave histograms over contiguous chunks of pairs.
@@ -131,6 +132,70 @@ __device__ int wg_sort(const int32_t* ids, int P, int N, int B, int* s_e, int* s
   return total;
 }
 
+// One-wave sort of up to a few thousand pairs (called by one whole wave, no
+// barriers: LDS accesses of one wave are performed in program order).
+// Batches of 64 pairs are taken in pair order; a lane's stable rank is the
+// running count of its expert before the batch plus its rank among the batch's
+// lanes with the same expert, and the batch's first lane of each expert then
+// advances that count. LDS: s_e[P], s_rank[P], s_cnt[N], s_off[N+1].
+// Results: s_cnt, s_off (N+1 entries) and pos[p] (LDS or global), -1 for a
+// pair whose expert id is outside [0, N). Returns the padded total.
+// With ids == nullptr, s_e already holds the experts.
+template <typename PosPtr>
+__device__ int wave_sort(const int32_t* ids, int P, int N, int B, int* s_e, int* s_rank, int* s_cnt, int* s_off,
+                         PosPtr pos) {
+  const int lane = lane_id();
+  for (int e = lane; e < N; e += 64) s_cnt[e] = 0;
+  if (ids) {
+    // Load the ids 8 per lane at a time with clamped addresses and no branches
+    // between the loads, so each group costs one memory round trip.
+    for (int p0 = 0; p0 < P; p0 += 8 * 64) {
+      int v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = ids[min(p0 + j * 64 + lane, P - 1)];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (p0 + j * 64 + lane < P) s_e[p0 + j * 64 + lane] = v[j];
+    }
+  }
+  const int bits = ceil_log2(N);
+  for (int base = 0; base < P; base += 64) {
+    const int p = base + lane;
+    const int e = p < P ? s_e[p] : 0;
+    const bool valid = p < P && (unsigned)e < (unsigned)N;
+    const u64 peers = match_peers(e, valid, bits);
+    if (valid) {
+      const u64 below = peers & lanemask_lt();
+      const int c = s_cnt[e];
+      s_rank[p] = c + __popcll(below);
+      if (below == 0ull) s_cnt[e] = c + __popcll(peers);
+    }
+  }
+  // Padded counts -> exclusive segment offsets. Lane l owns C consecutive experts.
+  const int C = (N + 63) / 64;
+  const int e0 = min(N, lane * C), e1 = min(N, e0 + C);
+  int local = 0;
+  for (int e = e0; e < e1; ++e) local += (s_cnt[e] + B - 1) / B * B;
+  int incl = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += t;
+  }
+  const int total = (int)readlane_u32((u32)incl, 63);
+  int run = incl - local;
+  for (int e = e0; e < e1; ++e) {
+    s_off[e] = run;
+    run += (s_cnt[e] + B - 1) / B * B;
+  }
+  if (lane == 0) s_off[N] = total;
+  for (int p = lane; p < P; p += 64) {
+    const int e = s_e[p];
+    pos[p] = (unsigned)e < (unsigned)N ? s_off[e] + s_rank[p] : -1;
+  }
+  return total;
+}
+
 // Write offsets, sentinel pads of sorted_ids and expert_ids from the LDS
 // results of a sort. Pair entries of sorted_ids are written by the caller.
 __device__ __forceinline__ void write_sort_layout(const int* s_cnt, const int* s_off, int N, int B, int P,
@@ -143,17 +208,26 @@ __device__ __forceinline__ void write_sort_layout(const int* s_cnt, const int* s
   }
 }
 
-// Decode-size sort: one workgroup. pos goes to the workspace for the quant.
+// Decode-size sort: one workgroup (one wave sorts up to kWaveSortMaxP pairs,
+// the whole workgroup above). pos goes to the workspace for the quant.
+constexpr int kWaveSortMaxP = 2048;
+
 __global__ void __launch_bounds__(256) sort_small_kernel(const int32_t* ids, int P, int N, int B,
                                                          int32_t* sorted_ids, int32_t* expert_ids,
                                                          int32_t* offsets, int32_t* pos_ws) {
   extern __shared__ int smem[];
   int* s_e = smem;
-  int* s_hist = s_e + P;
-  int* s_cnt = s_hist + 4 * N;
+  int* s_hist = s_e + P;          // wave sort: per-pair ranks; workgroup sort: per-wave counts
+  int* s_cnt = s_hist + (P > 4 * N ? P : 4 * N);
   int* s_off = s_cnt + N;
   int* s_scr = s_off + N + 1;
-  wg_sort(ids, P, N, B, s_e, s_hist, s_cnt, s_off, s_scr, pos_ws);
+  if (P <= kWaveSortMaxP) {
+    if (threadIdx.x < 64) wave_sort(ids, P, N, B, s_e, s_hist, s_cnt, s_off, pos_ws);
+    vm_drain();
+    __syncthreads();
+  } else {
+    wg_sort<false>(ids, P, N, B, s_e, s_hist, s_cnt, s_off, s_scr, pos_ws);
+  }
   for (int p = threadIdx.x; p < P; p += blockDim.x) {
     const int q = pos_ws[p];
     if (q >= 0) sorted_ids[q] = p;
@@ -264,7 +338,7 @@ __device__ __forceinline__ uint4 mx_quant16(const uint16_t* src, u32& scale_byte
     amax = lo > amax ? lo : amax;
     amax = hi > amax ? hi : amax;
   }
-  const u32 other = (u32)__shfl_xor((int)amax, 1, kWave);
+  const u32 other = dpp_u32<kDppQuadXor1>(amax);  // partner lane (lane ^ 1)
   amax = other > amax ? other : amax;
   const int se = mx_shared_exp(amax);
   scale_byte = (u32)(se + 127);

@@ -8,7 +8,7 @@ bit-exact against the oracle fed the GPU's own logits.
 import numpy as np
 import pytest
 
-from _helpers import CANARY, check_logits, check_sort_quant, say, to_dev, to_dev_bf16
+from _helpers import CANARY, check_logits, check_sort_quant, say, to_dev, to_dev_bf16, workspace_state
 from oracle import rgt_oracle as O
 from router_gemv_top_amd.inputs import (Workload, gen_skew_bias, gen_w, gen_x, workload_prefill_896,
                                         workload_tiny, workloads_decode_128, workloads_decode_896,
@@ -54,6 +54,14 @@ def chain(R, x, w, bias, k, block, ws):
     return out
 
 
+def assert_workspace_ready(ws):
+    """Error word and every tile counter are zero after a call (the call
+    epoch only advances)."""
+    err, _, _, tiles = workspace_state(ws)
+    assert err == 0, "error word set"
+    assert np.all(tiles == 0), "tile counters must be back at zero"
+
+
 def np_out(out):
     return {k: (v.cpu().numpy() if v is not None else None) for k, v in out.items()}
 
@@ -93,8 +101,7 @@ def test_fused_decode_matches_chain_and_oracle(R, wl):
         np.testing.assert_array_equal(fo[key][:total], c[key][:total], err_msg=key)
     ids = check_against_oracle(x, w, b, wl.topk, wl.block, fo)
     check_sort_quant(sort_out(fo), ids, x, wl.n, wl.block)
-    ctl = ws.buf[: 256 + 4 * 8192].view(torch.int32).cpu().numpy()
-    assert np.all(ctl == 0), "counters and flags must be back at zero"
+    assert_workspace_ready(ws)
 
 
 def test_fused_without_logits_output(R):
@@ -122,8 +129,7 @@ def test_fused_random_m_sequence_one_workspace(R):
         fo = np_out(f)
         ids = check_against_oracle(x, w, None, k, block, fo)
         check_sort_quant(sort_out(fo), ids, x, n, block)
-    ctl = ws.buf[: 256 + 4 * 8192].view(torch.int32).cpu().numpy()
-    assert np.all(ctl == 0)
+    assert_workspace_ready(ws)
 
 
 def test_fused_deterministic_and_skewed(R):

@@ -7,7 +7,7 @@ one-hot inputs, whatever the summation order. Deterministic across calls.
 import numpy as np
 import pytest
 
-from _helpers import check_logits, say, to_dev_bf16
+from _helpers import check_logits, say, to_dev_bf16, workspace_state
 from oracle import rgt_oracle as O
 from router_gemv_top_amd.inputs import (Workload, f32_to_bf16_bits, gen_w, gen_x, workloads_decode_128,
                                         workloads_decode_896, workloads_wide_128)
@@ -42,8 +42,9 @@ def test_router_logits_parity(R, wl):
     torch.cuda.synchronize()
     check_logits(x, w, got.cpu().numpy())
     assert R.last_launch_count() == 1
-    ctl = ws.buf[: 256 + 4 * 8192].view(torch.int32).cpu().numpy()
-    assert np.all(ctl == 0), "counters must be back at zero after the call"
+    err, epoch, spare, tiles = workspace_state(ws)
+    assert err == 0 and epoch == 0 and spare == 0 and np.all(tiles == 0), \
+        "counters must be back at zero after the call"
 
 
 @pytest.mark.parametrize("m", [1, 2, 8, 16, 24, 64, 200])
