@@ -81,6 +81,11 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--hot", action="store_true", help="also time with one resident W copy")
+    ap.add_argument("--only-m", type=int, default=0,
+                    help="profiling mode: run --calls fused calls at this M (rotating cold W), print a summary")
+    ap.add_argument("--calls", type=int, default=64)
+    ap.add_argument("--calibrate-copy", type=int, default=0,
+                    help="profiling mode: one plain device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
@@ -94,6 +99,17 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+
+    if args.calibrate_copy:
+        src = torch.randint(0, 255, (args.calibrate_copy,), dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        R.diag_copy(src, dst, 2048)
+        torch.cuda.synchronize()
+        assert torch.equal(src, dst)
+        print(json.dumps({"mode": "calibrate_copy", "bytes_read": args.calibrate_copy,
+                          "bytes_written": args.calibrate_copy}), flush=True)
+        return
 
     w_bytes = N * K * 2
     copies = args.copies or int(np.ceil(2 * MALL_BYTES / w_bytes))
@@ -112,6 +128,20 @@ def main():
 
     def call(m, c):
         R.route_sort_quant(x_all[m][c], w_all[c], TOPK, BLOCK, ws, out=outs[m])
+
+    if args.only_m:
+        m = args.only_m
+        if m not in x_all:
+            raise SystemExit(f"--only-m must be one of {SWEEP}")
+        for c in range(args.calls):
+            call(m, c % copies)
+        torch.cuda.synchronize()
+        if ws.check() != 0:
+            raise RuntimeError("device-side wait timed out")
+        total = int(outs[m]["offsets"][-1].item())
+        print(json.dumps({"mode": "only_m", "m": m, "calls": args.calls, "launches_per_call": R.last_launch_count(),
+                          "algorithmic_bytes_per_call": algorithmic_bytes(m, total)}), flush=True)
+        return
 
     # Warmup: eager steps (also sizes the co-resident grids once).
     launches = {}
@@ -200,6 +230,11 @@ def main():
     launch_floor_us = ev0.elapsed_time(ev1) * 1e3 / copies
 
     sweep_bytes = {m: algorithmic_bytes(m, totals[m]) for m in SWEEP}
+    from router_gemv_top_amd.profile_report import recorded_traffic
+    rec = recorded_traffic(os.path.join(ROOT, "profiles"))
+    traffic = None
+    if rec is not None and all(m in rec for m in SWEEP):
+        traffic = round(sum(rec[m] for m in SWEEP) / len(SWEEP), 1)   # HBM bytes per launch, sweep average
     kernel_us_total = sum(us_per_call.values())
     achieved = sum(sweep_bytes.values()) / (kernel_us_total * 1e-6) / 1e9
     value = step_bytes * args.steps / (t_steps_ms * 1e-3) / 1e9
@@ -227,7 +262,8 @@ def main():
         "floor_us": {"empty_launch": round(launch_floor_us, 3),
                      "stream_read_W": round(read_floor_us, 3)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": round(sum(sweep_bytes.values()) / len(SWEEP), 1),
                      "kernel": "fused route_sort_quant (one launch per call), averaged over the sweep"},
     }
     if args.hot:

@@ -43,7 +43,7 @@
  *     0 <= M <= 8192.
  *   - M == 0 is a no-op returning RGT_OK (outputs untouched).
  *   - Null required pointers, misaligned pointers (x, W: 16 bytes; fp32/int32
- *     outputs: 4 bytes; a_q: 16 bytes), ld < K or ld % 8 != 0 return
+ *     outputs and a_scale: 4 bytes; a_q: 16 bytes), ld < K or ld % 8 != 0 return
  *     RGT_ERR_INVALID. A workspace that is null, misaligned or too small
  *     returns RGT_ERR_WORKSPACE. A failed kernel launch returns RGT_ERR_HIP.
  *     Argument checks happen before any HIP call, so they never touch the GPU.

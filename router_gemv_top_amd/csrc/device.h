@@ -62,6 +62,24 @@ constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // row_half_mirror
 constexpr int kDppMirror = 0x140;     // row_mirror
 
+// row_shl:n (lane i of a 16-lane row takes lane i+n; lanes past the row end
+// take 0).
+template <int N>
+__device__ __forceinline__ u32 dpp_row_shl(u32 v) {
+  return (u32)__builtin_amdgcn_update_dpp(0, (int)v, 0x100 + N, 0xF, 0xF, true);
+}
+
+// Workgroups are dispatched to the 8 XCDs round-robin (block b runs on XCD
+// b % 8). Map block b to tile t so that each XCD gets one contiguous run of
+// tiles: tiles that share an x slice (consecutive t) then share an L2, and x
+// is fetched from memory once per slice instead of once per XCD.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_tile(int b, int tiles) {
+  const int x = b % kXcds, local = b / kXcds;
+  const int per = tiles / kXcds, rem = tiles % kXcds;
+  return x * per + min(x, rem) + local;
+}
+
 template <int CTRL>
 __device__ __forceinline__ u32 dpp_u32(u32 v) {
   return (u32)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);

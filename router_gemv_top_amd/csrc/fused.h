@@ -183,17 +183,8 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
       if (s_pos[p] >= 0) a.sorted_ids[s_pos[p]] = p;
     write_sort_layout(s_cnt, s_off, n, a.block, P, a.sorted_ids, a.expert_ids, a.offsets);
   }
-  if (have_unit) {
-    const int K = g.k, cpr = K >> 4;
-    const int t = unit / cpr, c = unit - t * cpr;
-    const int64_t kscale = K >> 5;
-    for (int j = 0; j < k; ++j) {
-      const int64_t d = s_pos[t * k + j];
-      if (d < 0) continue;
-      *reinterpret_cast<uint4*>(a.a_q + d * K + 16 * c) = codes_in;
-      if ((c & 1) == 0) a.a_scale[d * kscale + (c >> 1)] = (uint8_t)sb_in;
-    }
-  }
+  const u32 scales4 = pack_scales(sb_in);  // all lanes: DPP reads neighbouring lanes
+  if (have_unit) store_unit(a.a_q, a.a_scale, g.k, k, unit, s_pos, codes_in, scales4);
   RGT_STAMP(a.trace, 9);
 }
 
@@ -206,7 +197,8 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, int bn
   const int units = g.m * (g.k >> 4);
   const int unit = blockIdx.x * 256 + threadIdx.x;
   const bool have_unit = unit < units;
-  const int nb = blockIdx.x % g.nb_count;
+  const int tile_id = xcd_tile(blockIdx.x, gridDim.x);
+  const int nb = tile_id % g.nb_count;
   RGT_STAMP(a.trace, 0);
   // The epoch load completes before this workgroup's arrival (the arrival
   // drains every outstanding memory operation first).
@@ -214,7 +206,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, int bn
     const u32 t = ld_agent(a.ctl + kCtlEpoch) + 1u;
     s_tag = t ? t : 1u;  // tag 0 is never used, so zero-filled words never look ready
   }
-  tile(nb, blockIdx.x / g.nb_count);
+  tile(nb, tile_id / g.nb_count);
   RGT_STAMP(a.trace, 1);
   u32* tile_ctr = g.ctr + nb * kCtrStride;
   const bool last = arrive_last(tile_ctr, (u32)g.s_count);  // has barriers: s_tag is visible after it

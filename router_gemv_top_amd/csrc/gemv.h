@@ -197,7 +197,8 @@ struct LogitsOut {
 // Standalone router kernels: tile, then fixup by the last arriver.
 template <int MT, int RPW, int L>
 __global__ void __launch_bounds__(256) router_valu_kernel(GemvArgs a) {
-  const int nb = blockIdx.x % a.nb_count, s = blockIdx.x / a.nb_count;
+  const int t = xcd_tile(blockIdx.x, gridDim.x);
+  const int nb = t % a.nb_count, s = t / a.nb_count;
   valu_tile<MT, RPW, L>(a, nb, s);
   u32* ctr = a.ctr + nb * kCtrStride;
   if (arrive_last(ctr, (u32)a.s_count)) {
@@ -209,10 +210,10 @@ __global__ void __launch_bounds__(256) router_valu_kernel(GemvArgs a) {
 template <int MT, int KS>
 __global__ void __launch_bounds__(256) router_mfma_kernel(GemvArgs a) {
   __shared__ float lds[4 * MT * 256];
-  const int tiles = a.nb_count;
-  const int nb = blockIdx.x % tiles;
-  const int s = (blockIdx.x / tiles) % a.s_count;
-  const int mb = blockIdx.x / (tiles * a.s_count);
+  const int t = xcd_tile(blockIdx.x, gridDim.x);
+  const int nb = t % a.nb_count;
+  const int s = (t / a.nb_count) % a.s_count;
+  const int mb = t / (a.nb_count * a.s_count);
   mfma_tile<MT, KS>(a, mb, nb, s, lds);
   u32* ctr = a.ctr + (mb * a.nb_count + nb) * kCtrStride;
   if (arrive_last(ctr, (u32)a.s_count)) {

@@ -442,7 +442,8 @@ static rgt_status check_sort_args(const void* x, int64_t ldx, int m, int n, int 
   if (m == 0) return RGT_OK;
   if (!x || !aligned(x, 16) || ldx < k || ldx % 8) return RGT_ERR_INVALID;
   if (!sorted_ids || !expert_ids || !offsets || !a_q || !a_scale) return RGT_ERR_INVALID;
-  if (!aligned(sorted_ids, 4) || !aligned(expert_ids, 4) || !aligned(offsets, 4) || !aligned(a_q, 16))
+  if (!aligned(sorted_ids, 4) || !aligned(expert_ids, 4) || !aligned(offsets, 4) || !aligned(a_q, 16) ||
+      !aligned(a_scale, 4))
     return RGT_ERR_INVALID;
   return RGT_OK;
 }

@@ -352,24 +352,29 @@ __device__ __forceinline__ uint4 mx_quant16(const uint16_t* src, u32& scale_byte
   return make_uint4(c[0], c[1], c[2], c[3]);
 }
 
-// Quantise unit u (token t = u / (K/16), chunk c = u % (K/16)) and store it to
-// the padded positions pos[t*k + j], j < k. Lanes of a pair call together.
-__device__ __forceinline__ void quant_unit_store(const uint16_t* x, int64_t ldx, int K, int k, int u, bool active,
-                                                 const int32_t* pos, uint8_t* a_q, uint8_t* a_scale) {
+// Units (16-element chunks) are numbered row-major, one per lane, so lanes
+// 8q..8q+7 hold chunks 8c'..8c'+7 of one row (rows are multiples of 32
+// chunks), i.e. the 4 scale bytes of blocks 4c'..4c'+3. The first lane of each
+// group of 8 gathers them (DPP within the 16-lane row) into one 4-byte word.
+// Called by every lane of the wave.
+__device__ __forceinline__ u32 pack_scales(u32 sb) {
+  const u32 s2 = dpp_row_shl<2>(sb), s4 = dpp_row_shl<4>(sb), s6 = dpp_row_shl<6>(sb);
+  return (sb & 0xffu) | ((s2 & 0xffu) << 8) | ((s4 & 0xffu) << 16) | ((s6 & 0xffu) << 24);
+}
+
+// Store unit u's 16 codes to the padded rows pos[t*k + j] of its token's pairs;
+// lanes with u % 8 == 0 also store the packed scales of their 4 blocks.
+template <typename PosPtr>
+__device__ __forceinline__ void store_unit(uint8_t* a_q, uint8_t* a_scale, int K, int k, int u, PosPtr pos,
+                                           const uint4& codes, u32 scales4) {
   const int cpr = K >> 4;  // 16-element chunks per row
   const int t = u / cpr, c = u - t * cpr;
-  u32 sb = 0;
-  uint4 codes = make_uint4(0, 0, 0, 0);
-  // Both lanes of a pair are active together (unit counts are even), so the
-  // shuffle inside mx_quant16 always has its partner.
-  if (active) codes = mx_quant16(x + (int64_t)t * ldx + 16 * c, sb);
-  if (!active) return;
   const int64_t kscale = K >> 5;
   for (int j = 0; j < k; ++j) {
     const int64_t d = pos[t * k + j];
     if (d < 0) continue;
     *reinterpret_cast<uint4*>(a_q + d * K + 16 * c) = codes;
-    if ((c & 1) == 0) a_scale[d * kscale + (c >> 1)] = (uint8_t)sb;
+    if ((c & 7) == 0) *reinterpret_cast<u32*>(a_scale + d * kscale + (c >> 1)) = scales4;
   }
 }
 
@@ -377,7 +382,14 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* x, int64_t l
                                                     const int32_t* pos, uint8_t* a_q, uint8_t* a_scale) {
   const int units = M * (K >> 4);
   const int u = blockIdx.x * blockDim.x + threadIdx.x;
-  quant_unit_store(x, ldx, K, k, u, u < units, pos, a_q, a_scale);
+  const int cpr = K >> 4;
+  // Units come in whole groups of 8 lanes (unit counts are multiples of 32),
+  // so every lane of a pair or group is active together.
+  u32 sb = 0;
+  uint4 codes = make_uint4(0, 0, 0, 0);
+  if (u < units) codes = mx_quant16(x + (int64_t)(u / cpr) * ldx + 16 * (u % cpr), sb);
+  const u32 s4 = pack_scales(sb);
+  if (u < units) store_unit(a_q, a_scale, K, k, u, pos, codes, s4);
 }
 
 }  // namespace rgt

@@ -1,0 +1,141 @@
+"""Summaries of rocprofv3 output for the fused decode sweep.
+
+Reads the CSV directories that the commands below leave in a results folder
+and writes the short text summaries kept under ``profiles/``:
+
+    rocprofv3 --kernel-trace --stats --output-format csv -d RES/prof_stats -o fused \\
+        -- python3 bench.py --steps 5 --warmup 2 --no-cpu
+    for M in 1 2 4 8 16 32 64; for C in FETCH_SIZE WRITE_SIZE:
+        rocprofv3 --pmc C --output-format csv -d RES/pmc_C_mM -o p -- python3 bench.py --only-m M --calls 32
+    for C in FETCH_SIZE WRITE_SIZE:
+        rocprofv3 --pmc C --output-format csv -d RES/pmc_C_copy -o p -- python3 bench.py --calibrate-copy 268435456
+    python -m router_gemv_top_amd.profile_report RES profiles
+
+The counter values are KiB per dispatch. Each counter is scaled by what it
+reads for the plain copy kernel of known size (bytes moved / counter bytes).
+The traffic file records a hash of the kernel sources, so the benchmark can
+report the traffic as unknown once the kernels change.
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+SWEEP = (1, 2, 4, 8, 16, 32, 64)
+COPY_BYTES = 268435456
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the HIP sources and headers of the library."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(PKG, "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def _counter(path: str, pattern: str):
+    vals = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if pattern in r["Kernel_Name"]:
+                vals.append(float(r["Counter_Value"]))
+    return vals
+
+
+def _find(folder: str, name: str):
+    hits = glob.glob(os.path.join(folder, "**", name), recursive=True)
+    if not hits:
+        raise FileNotFoundError(f"{name} under {folder}")
+    return hits[0]
+
+
+def build(res: str, out: str):
+    os.makedirs(out, exist_ok=True)
+    # --- kernel durations ---------------------------------------------------
+    stats_path = _find(os.path.join(res, "prof_stats"), "*kernel_stats.csv")
+    rows = list(csv.DictReader(open(stats_path)))
+    lines = ["# Fused route+sort+quant, decode sweep: kernel durations (rocprofv3)", "",
+             "Workload: M = 1, 2, 4, 8, 16, 32, 64; N = 128; K = 6144; top-8; block 16; MXFP8 quant;",
+             "cold W (342 rotating copies). One launch per call; the seven template instances below are",
+             "the seven M values (VALU tile `<NV, MT, RPW, L>` for M <= 8, MFMA tile `<NV, MT, KS>` above).",
+             "", "Command (from the repository root, results folder RES):", "",
+             "    rocprofv3 --kernel-trace --stats --output-format csv -d RES/prof_stats -o fused "
+             "-- python3 bench.py --steps 5 --warmup 2 --no-cpu",
+             f"    python -m router_gemv_top_amd.profile_report RES profiles", "",
+             "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"].replace("rgt::", "")
+        if not ("fused" in name or "diag" in name or "router" in name or "topk" in name or "sort" in name
+                or "quant" in name):
+            continue
+        short = name.split("(")[0].replace("void ", "")
+        lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
+                     f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} |")
+    lines += ["", "`diag_read_kernel` is the streaming-read floor (one cold W copy, 384 workgroups) and an almost",
+              "empty launch (1 workgroup, 16 bytes); the bench reports both under `floor_us`."]
+    with open(os.path.join(out, "fused_decode_sweep_kernel_stats.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    # --- traffic ----------------------------------------------------------------
+    cal = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        v = _counter(_find(os.path.join(res, f"pmc_{c}_copy"), "*counter_collection.csv"), "diag_copy")
+        cal[c] = {"counter_kib": v[0], "true_kib": COPY_BYTES / 1024, "factor": (COPY_BYTES / 1024) / v[0]}
+    per_m = {}
+    for m in SWEEP:
+        d = {}
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            folder = os.path.join(res, f"pmc_{c}_m{m}")
+            if not os.path.isdir(folder):
+                break
+            v = _counter(_find(folder, "*counter_collection.csv"), "fused")
+            d[c] = statistics.median(v)
+        if len(d) == 2:
+            per_m[str(m)] = {"fetch_kib_raw": d["FETCH_SIZE"], "write_kib_raw": d["WRITE_SIZE"],
+                             "bytes": d["FETCH_SIZE"] * cal["FETCH_SIZE"]["factor"] * 1024 +
+                             d["WRITE_SIZE"] * cal["WRITE_SIZE"]["factor"] * 1024}
+    data = {"kernel_source_sha256": kernel_source_hash(), "calibration": cal, "per_m": per_m,
+            "commands": ["rocprofv3 --pmc FETCH_SIZE --output-format csv -d RES/pmc_FETCH_SIZE_mM -o p "
+                         "-- python3 bench.py --only-m M --calls 32",
+                         "rocprofv3 --pmc WRITE_SIZE --output-format csv -d RES/pmc_WRITE_SIZE_mM -o p "
+                         "-- python3 bench.py --only-m M --calls 32",
+                         "rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE --output-format csv -d RES/pmc_C_copy -o p "
+                         "-- python3 bench.py --calibrate-copy 268435456",
+                         "python -m router_gemv_top_amd.profile_report RES profiles"]}
+    with open(os.path.join(out, "fused_decode_sweep_traffic.json"), "w") as f:
+        json.dump(data, f, indent=1)
+    md = ["# Fused route+sort+quant, decode sweep: HBM traffic per launch (rocprofv3 counters)", "",
+          "Counters are KiB per dispatch, median over 32 calls with rotating cold W copies. Calibration: a",
+          f"plain {COPY_BYTES // 2**20} MiB device copy reads FETCH_SIZE = "
+          f"{cal['FETCH_SIZE']['counter_kib']:.1f} KiB (factor {cal['FETCH_SIZE']['factor']:.3f}) and "
+          f"WRITE_SIZE = {cal['WRITE_SIZE']['counter_kib']:.1f} KiB (factor {cal['WRITE_SIZE']['factor']:.3f}).",
+          "", "Commands: see `fused_decode_sweep_traffic.json`.", "",
+          "| M | FETCH_SIZE raw KiB | WRITE_SIZE raw KiB | calibrated bytes |", "|---|---|---|---|"]
+    for m, d in per_m.items():
+        md.append(f"| {m} | {d['fetch_kib_raw']:.1f} | {d['write_kib_raw']:.1f} | {d['bytes']:.0f} |")
+    with open(os.path.join(out, "fused_decode_sweep_traffic.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+    return data
+
+
+def recorded_traffic(profiles_dir: str):
+    """Per-M calibrated traffic from the profiles, or None if the kernel
+    sources changed since the counters were taken."""
+    path = os.path.join(profiles_dir, "fused_decode_sweep_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    if data.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return {int(m): d["bytes"] for m, d in data["per_m"].items()}
+
+
+if __name__ == "__main__":
+    build(sys.argv[1], sys.argv[2])

@@ -108,6 +108,7 @@ def test_sort_quant_argument_errors(L):
     assert call(topk=0) == 1
     assert call(ids=None) == 2
     assert call(q=FAKE + 4) == 2
+    assert call(sc=FAKE + 2) == 2
     assert call(s=None) == 2
     assert call(wsb=100) == 3
 
