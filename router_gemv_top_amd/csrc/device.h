@@ -107,6 +107,20 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (readlane_f32(v, 0) + readlane_f32(v, 16)) + (readlane_f32(v, 32) + readlane_f32(v, 48));
 }
 
+// Inclusive prefix sum over the 64 lanes: DPP row_shr steps inside each row
+// of 16 lanes (shifted-in lanes read 0), then the row totals are read as
+// scalars and added to the later rows.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
+            r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = __lane_id() >> 4;
+  return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+
 __device__ __forceinline__ u32 wave_max_u32(u32 v) {
   v = umax(v, dpp_u32<kDppQuadXor1>(v));
   v = umax(v, dpp_u32<kDppQuadXor2>(v));
@@ -298,7 +312,7 @@ __device__ __forceinline__ int mx_shared_exp(u32 amax_bits) {
 //   d < -200 gives 0.
 // LN2_HI is ln 2 cut to 24 significant bits, so n*LN2_HI is exact.
 // ---------------------------------------------------------------------------
-__device__ __noinline__ double exp64_recipe(double d) {
+__device__ __forceinline__ double exp64_recipe(double d) {
 #pragma clang fp contract(off)
   if (d < -200.0) return 0.0;
   const double kLog2e = 0x1.71547652b82fep+0;

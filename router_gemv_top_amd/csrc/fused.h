@@ -11,21 +11,22 @@
 //      the partials in k-slice order and zeroes the counter ("MiniMax-M3:
 //      Triton split-K router GEMV with in-kernel split-K fixup", opening
 //      summary), then publishes the n-block's logits as tagged words;
-//   2. row-owner workgroups (one wave per token row) poll their row's tagged
-//      logits, run the softmax top-k gate and publish the row's expert ids as
-//      tagged words;
-//   3. workgroup 0 and every workgroup that owns a quant chunk poll the tagged
-//      ids, sort the M*k pairs in LDS with one wave (tiny at decode sizes, so
-//      redundant sorting beats another hand-off) and store their MXFP8 chunk
-//      (quantised in registers while waiting) to the padded rows of the
-//      token's pairs; workgroup 0 also writes sorted_ids, expert_ids and
-//      offsets and advances the call epoch.
+//   2. the softmax top-k gate. Small M (each wave's rows fit in registers):
+//      workgroup 0 and every workgroup that owns a quant chunk poll the
+//      tagged logits and run the gate for every row themselves, so no further
+//      hand-off is needed. Larger M: row-owner workgroups (one wave per row)
+//      run it and publish the ids as tagged words, which the others poll;
+//   3. the same workgroups sort the M*k pairs in LDS with one wave (tiny at
+//      decode sizes, so redundant sorting beats another hand-off) and store
+//      their MXFP8 chunk (quantised in registers while waiting) to the padded
+//      rows of the token's pairs; workgroup 0 also writes topk_ids, topk_w,
+//      sorted_ids, expert_ids and offsets and advances the call epoch.
 //
 // A tagged word is a 32-bit payload plus the tag (epoch + 1) of the call that
 // wrote it, stored as one 8-byte atomic; readers poll the words themselves, so
 // these hand-offs need no counter. The epoch is read by every workgroup at
-// start and advanced by workgroup 0 only after every id is in, which implies
-// every workgroup has arrived in step 1, hence has read it. Every wait is
+// start and advanced by workgroup 0 only after all logits are in, which
+// implies every workgroup has arrived in step 1, hence has read it. Every wait is
 // bounded by a deadline that sets the workspace error word.
 #pragma once
 
@@ -55,7 +56,7 @@ struct FusedArgs {
   u64* tlogits;        // [M][N] tagged logits (workspace)
   u64* tids;           // [M*topk] tagged expert ids (workspace)
   u64 budget;          // deadline of each wait, in 100 MHz ticks
-  int fault_skip;      // host-forced fault: 1 = row owners never publish ids
+  int fault_skip;      // host-forced fault: 1 = the fixup never publishes logits
   u64* trace;          // phase stamps (trace build only), 16 per workgroup
 };
 
@@ -65,8 +66,10 @@ struct TaggedLogitsOut {
   u64* tlogits;
   int n;
   u32 tag;
+  int skip;  // host-forced fault: publish nothing, so every reader's wait expires
   __device__ __forceinline__ void operator()(int m, int c, float4 v) const {
     if (logits_out) *reinterpret_cast<float4*>(logits_out + (int64_t)m * n + c) = v;
+    if (skip) return;
     u64* t = tlogits + (int64_t)m * n + c;
     st_agent(t + 0, tag_word(__float_as_uint(v.x), tag));
     st_agent(t + 1, tag_word(__float_as_uint(v.y), tag));
@@ -77,104 +80,189 @@ struct TaggedLogitsOut {
 
 __device__ __forceinline__ void set_timeout(const FusedArgs& a) { or_agent(a.ctl + kCtlErr, kErrTimeout); }
 
-// One wave polls its row of tagged logits until every word carries `tag`.
+// Rows of tagged logits one wave holds at once (register budget: 8 score
+// slots per lane).
 template <int NV>
-__device__ __forceinline__ bool poll_row(const u64* trow, int n, u32 tag, const FusedArgs& a, float (&sv)[NV]) {
+struct RowsHeld {
+  static constexpr int value = NV >= 8 ? 1 : 8 / NV;
+};
+
+// Small mode: every participating workgroup runs the gate for every row
+// itself (no ids hand-off), possible while each wave's rows fit in registers.
+template <int NV>
+__host__ __device__ constexpr bool small_mode(int m) {
+  return (m + 3) / 4 <= RowsHeld<NV>::value;
+}
+
+// One wave polls `cnt` rows of tagged logits (rows r0, r0 + 4, ...) until
+// every word carries `tag`. Two polls are kept in flight, so a hand-off is
+// seen about one memory round trip after it lands.
+template <int NV, int R>
+__device__ __forceinline__ bool poll_rows(const u64* tlog, int n, int r0, int cnt, u32 tag, const FusedArgs& a,
+                                          float (&sv)[R][NV]) {
   const int lane = lane_id();
-  const u64 t0 = rt_clock();
-  for (;;) {
-    u64 w[NV];
+  auto issue = [&](u64 (&w)[R][NV]) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) w[i] = ld_agent(trow + min(lane + 64 * i, n - 1));
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int row = r < cnt ? r0 + 4 * r : r0;
+        w[r][i] = ld_agent(tlog + (int64_t)row * n + min(lane + 64 * i, n - 1));
+      }
+  };
+  auto ready = [&](const u64 (&w)[R][NV]) {
     bool ok = true;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) ok = ok && tag_ok(w[i], tag);
-    if (__all(ok)) {
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int i = 0; i < NV; ++i) sv[i] = __uint_as_float((u32)w[i]);
-      return true;
-    }
+      for (int i = 0; i < NV; ++i) ok = ok && tag_ok(w[r][i], tag);
+    return __all(ok);
+  };
+  auto take = [&](const u64 (&w)[R][NV]) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int i = 0; i < NV; ++i) sv[r][i] = __uint_as_float((u32)w[r][i]);
+  };
+  const u64 t0 = rt_clock();
+  u64 wa[R][NV], wb[R][NV];
+  issue(wa);
+  issue(wb);
+  for (;;) {
+    if (ready(wa)) { take(wa); return true; }
+    issue(wa);
+    if (ready(wb)) { take(wb); return true; }
+    issue(wb);
     if (rt_clock() - t0 > a.budget) {
       if (lane == 0) set_timeout(a);
       return false;
     }
-    __builtin_amdgcn_s_sleep(1);
   }
 }
 
 // The workgroup polls all P tagged ids until every word carries `tag`, then
-// leaves the experts in s_e.
+// leaves the experts in s_e. Two polls in flight, as above.
 __device__ __forceinline__ bool poll_ids(const u64* tids, int P, u32 tag, const FusedArgs& a, int* s_e) {
   __shared__ u32 s_late;
   constexpr int kPer = 8;  // words per thread per pass (P <= 2048)
-  const u64 t0 = rt_clock();
-  for (;;) {
-    u64 w[kPer];
+  auto issue = [&](u64 (&w)[kPer]) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) w[j] = ld_agent(tids + min((int)threadIdx.x + 256 * j, P - 1));
+  };
+  auto ready = [&](const u64 (&w)[kPer]) {
     bool ok = true;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) ok = ok && tag_ok(w[j], tag);
-    if (__syncthreads_and(ok)) {
+    return __syncthreads_and(ok) != 0;
+  };
+  auto take = [&](const u64 (&w)[kPer]) {
 #pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        const int p = threadIdx.x + 256 * j;
-        if (p < P) s_e[p] = (int)(u32)w[j];
-      }
-      __syncthreads();
-      return true;
+    for (int j = 0; j < kPer; ++j) {
+      const int p = threadIdx.x + 256 * j;
+      if (p < P) s_e[p] = (int)(u32)w[j];
     }
+    __syncthreads();
+  };
+  const u64 t0 = rt_clock();
+  u64 wa[kPer], wb[kPer];
+  issue(wa);
+  issue(wb);
+  for (;;) {
+    if (ready(wa)) { take(wa); return true; }
+    issue(wa);
+    if (ready(wb)) { take(wb); return true; }
+    issue(wb);
     if (threadIdx.x == 0) s_late = rt_clock() - t0 > a.budget ? 1u : 0u;
     __syncthreads();
     if (s_late) {
       if (threadIdx.x == 0) set_timeout(a);
       return false;
     }
-    __builtin_amdgcn_s_sleep(2);
   }
 }
 
 template <int NV>
 __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 tag, bool have_unit, int unit,
                                            const uint4& codes_in, u32 sb_in) {
+  __shared__ u32 s_fail;
   const GemvArgs& g = a.g;
   const int m = g.m, n = g.n, k = a.topk;
-  const int lane = threadIdx.x & 63;
-  const int row_groups = (m + 3) >> 2;
-  // Step 2: top-k by the row owners, one wave per token row.
-  if ((int)blockIdx.x < row_groups) {
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row < m) {
-      float sv[NV];
-      if (poll_row<NV>(a.tlogits + (int64_t)row * n, n, tag, a, sv)) {
-        RGT_STAMP(a.trace, 5);
-        add_bias<NV>(sv, a.bias, n);
-        int id;
-        float w;
-        wave_topk_regs<NV>(sv, n, k, id, w);
-        if (lane < k) {
-          a.topk_ids[(int64_t)row * k + lane] = id;
-          a.topk_w[(int64_t)row * k + lane] = w;
-          if (!a.fault_skip) st_agent(a.tids + (int64_t)row * k + lane, tag_word((u32)id, tag));
-        }
-        RGT_STAMP(a.trace, 6);
-      }
-    }
-  }
-  // Step 3: workgroup 0 and the quant owners wait for every id.
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int units = m * (g.k >> 4);
-  if (blockIdx.x != 0 && (int)blockIdx.x * 256 >= units) return;
+  const bool participant = blockIdx.x == 0 || (int)blockIdx.x * 256 < units;
   const int P = m * k;
   int* s_e = smem;
   int* s_rank = s_e + P;
   int* s_pos = s_rank + P;
   int* s_cnt = s_pos + P;
   int* s_off = s_cnt + n;
-  if (!poll_ids(a.tids, P, tag, a, s_e)) return;
+  if (small_mode<NV>(m)) {
+    // Step 2 (small): each participant runs the gate for every row; wave w
+    // takes rows w, w + 4, ... straight from the tagged logits.
+    if (!participant) return;
+    if (threadIdx.x == 0) s_fail = 0u;
+    __syncthreads();
+    constexpr int R = RowsHeld<NV>::value;
+    const int cnt = wave < m ? (m - 1 - wave) / 4 + 1 : 0;
+    if (cnt > 0) {
+      float sv[R][NV];
+      if (poll_rows<NV, R>(a.tlogits, n, wave, cnt, tag, a, sv)) {
+        RGT_STAMP(a.trace, 5);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          if (r < cnt) {
+            const int row = wave + 4 * r;
+            add_bias<NV>(sv[r], a.bias, n);
+            int id;
+            float w;
+            wave_topk_regs<NV>(sv[r], n, k, id, w);
+            if (lane < k) {
+              s_e[row * k + lane] = id;
+              if (blockIdx.x == 0) {
+                a.topk_ids[(int64_t)row * k + lane] = id;
+                a.topk_w[(int64_t)row * k + lane] = w;
+              }
+            }
+          }
+        }
+        RGT_STAMP(a.trace, 6);
+      } else if (lane == 0) {
+        s_fail = 1u;
+      }
+    }
+    __syncthreads();
+    if (s_fail) return;
+  } else {
+    // Step 2 (large): row owners, one wave per row, publish tagged ids.
+    const int row_groups = (m + 3) >> 2;
+    if ((int)blockIdx.x < row_groups) {
+      const int row = blockIdx.x * 4 + wave;
+      if (row < m) {
+        float sv[1][NV];
+        if (poll_rows<NV, 1>(a.tlogits, n, row, 1, tag, a, sv)) {
+          RGT_STAMP(a.trace, 5);
+          add_bias<NV>(sv[0], a.bias, n);
+          int id;
+          float w;
+          wave_topk_regs<NV>(sv[0], n, k, id, w);
+          if (lane < k) {
+            a.topk_ids[(int64_t)row * k + lane] = id;
+            a.topk_w[(int64_t)row * k + lane] = w;
+            st_agent(a.tids + (int64_t)row * k + lane, tag_word((u32)id, tag));
+          }
+          RGT_STAMP(a.trace, 6);
+        }
+      }
+    }
+    if (!participant) return;
+    if (!poll_ids(a.tids, P, tag, a, s_e)) return;
+  }
   RGT_STAMP(a.trace, 7);
-  // Every workgroup has read the epoch (all ids are in, so every workgroup
-  // arrived in step 1): advance it for the next call.
+  // Every workgroup has read the epoch (all logits are in, so every
+  // workgroup arrived in step 1): advance it for the next call.
   if (blockIdx.x == 0 && threadIdx.x == 0) st_agent(a.ctl + kCtlEpoch, tag);
+  // Step 3: one wave sorts the pairs in LDS; the workgroup stores its
+  // quantised chunk to the padded rows of the token's pairs.
   if (threadIdx.x < 64) wave_sort((const int32_t*)nullptr, P, n, a.block, s_e, s_rank, s_cnt, s_off, s_pos);
   __syncthreads();
   RGT_STAMP(a.trace, 8);
@@ -213,7 +301,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, int bn
   const u32 tag = s_tag;
   if (last) {
     RGT_STAMP(a.trace, 2);
-    reduce_partials(g, 0, g.m, nb * bn, bn, TaggedLogitsOut{a.logits_out, a.tlogits, g.n, tag});
+    reduce_partials(g, 0, g.m, nb * bn, bn, TaggedLogitsOut{a.logits_out, a.tlogits, g.n, tag, a.fault_skip});
     if (threadIdx.x == 0) st_agent(tile_ctr, 0u);
     RGT_STAMP(a.trace, 3);
   }

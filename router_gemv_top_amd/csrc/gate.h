@@ -41,22 +41,42 @@ __device__ __forceinline__ void wave_topk_regs(const float (&sv)[NV], int n, int
   u32 key[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) key[i] = lane + 64 * i < n ? score_key(sv[i]) : 0u;
+  // Each lane keeps its best key and the lowest slot holding it; a round
+  // takes the wave maximum, finds the owning lane (the lowest expert index on
+  // ties across lanes), and only that lane drops the key and rescans.
+  u32 best;
+  int bslot;
+  auto rescan = [&]() {
+    best = key[0];
+    bslot = 0;
+#pragma unroll
+    for (int i = 1; i < NV; ++i)
+      if (key[i] > best) {  // strict: the lowest slot wins ties inside a lane
+        best = key[i];
+        bslot = i;
+      }
+  };
+  rescan();
   my_id = 0;
   float my_s = 0.f;
   for (int j = 0; j < k; ++j) {
-    u32 best = key[0];
-#pragma unroll
-    for (int i = 1; i < NV; ++i) best = key[i] > best ? key[i] : best;
     const u32 top = wave_max_u32(best);
-    int win = -1;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const u64 b = ballot64(key[i] == top);
-      if (win < 0 && b != 0ull) win = 64 * i + (int)__builtin_ctzll(b);
+    const u64 owners = ballot64(best == top);
+    int win;
+    if (__popcll(owners) == 1) {
+      const int wl = (int)__builtin_ctzll(owners);
+      win = 64 * __builtin_amdgcn_readlane(bslot, wl) + wl;
+    } else {
+      // equal maxima in several lanes: the lowest expert index among them
+      const u32 cand = best == top ? (u32)(64 * bslot + lane) : 0xffffffffu;
+      win = (int)~wave_max_u32(~cand);
     }
+    if (lane == (win & 63)) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i)
-      if (64 * i + lane == win) key[i] = 0u;
+      for (int i = 0; i < NV; ++i)
+        if (i == (win >> 6)) key[i] = 0u;
+      rescan();
+    }
     if (lane == j) {
       my_id = win;
       my_s = key_score(top);
@@ -67,7 +87,9 @@ __device__ __forceinline__ void wave_topk_regs(const float (&sv)[NV], int n, int
   double e = 0.0;
   if (lane < k) e = exp64_recipe((double)my_s - s0);
   double total = readlane_f64(e, 0);
-  for (int j = 1; j < k; ++j) total = total + readlane_f64(e, j);
+#pragma unroll
+  for (int j = 1; j < 32; ++j)
+    if (j < k) total = total + readlane_f64(e, j);
   my_w = lane < k ? (float)(e / total) : 0.f;
 }
 

@@ -158,11 +158,11 @@ constexpr int kReduceBatch = 12;
 
 template <class Out>
 __device__ __forceinline__ void reduce_partials(const GemvArgs& a, int r0, int r1, int c0, int bn, Out out) {
-  const int rows = r1 - r0, quads = bn >> 2;
+  const int rows = r1 - r0, quads = bn >> 2, lq = __ffs(quads) - 1;  // quads is 1, 2 or 4
   const u32 slice = (u32)a.m * (u32)a.n * 4u;
   const auto rsrc = coherent_rsrc(a.part, slice * (u32)a.s_count);
   for (int idx = threadIdx.x; idx < rows * quads; idx += blockDim.x) {
-    const int m = r0 + idx / quads, c = c0 + 4 * (idx % quads);
+    const int m = r0 + (idx >> lq), c = c0 + 4 * (idx & (quads - 1));
     const u32 off = ((u32)m * (u32)a.n + (u32)c) * 4u;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int s0 = 0; s0 < a.s_count; s0 += kReduceBatch) {

@@ -36,11 +36,13 @@ __device__ __forceinline__ u64 match_peers(int e, bool valid, int bits) {
   return peers;
 }
 
-__device__ __forceinline__ int ceil_log2(int n) {
-  int b = 0;
-  while ((1 << b) < n) ++b;
-  return b;
-}
+__device__ __forceinline__ int ceil_log2(int n) { return n <= 1 ? 0 : 32 - __clz(n - 1); }
+
+// Block sizes are powers of two: round up / divide with masks and shifts (a
+// GPU has no integer divide instruction; a runtime division costs ~40
+// instructions).
+__device__ __forceinline__ int pad_to(int c, int B) { return (c + B - 1) & -B; }
+__device__ __forceinline__ int div_pow2(int a, int B) { return a >> (__ffs(B) - 1); }
 
 // Exclusive scan of vals[0..n) in LDS (in place), n <= 4 * blockDim.x.
 // Returns the total. Uses scratch[blockDim.x] of LDS.
@@ -104,7 +106,7 @@ __device__ int wg_sort(const int32_t* ids, int P, int N, int B, int* s_e, int* s
       run += c;
     }
     s_cnt[e] = run;
-    s_off[e] = (run + B - 1) / B * B;
+    s_off[e] = pad_to(run, B);
   }
   __syncthreads();
   const int total = block_exclusive_scan(s_off, N, s_scr);
@@ -171,22 +173,24 @@ __device__ int wave_sort(const int32_t* ids, int P, int N, int B, int* s_e, int*
       if (below == 0ull) s_cnt[e] = c + __popcll(peers);
     }
   }
-  // Padded counts -> exclusive segment offsets. Lane l owns C consecutive experts.
+  // Padded counts -> exclusive segment offsets. Lane l owns C consecutive
+  // experts (C <= 16); their counts are read once into registers.
   const int C = (N + 63) / 64;
   const int e0 = min(N, lane * C), e1 = min(N, e0 + C);
+  int pc[16];
   int local = 0;
-  for (int e = e0; e < e1; ++e) local += (s_cnt[e] + B - 1) / B * B;
-  int incl = local;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += t;
+  for (int i = 0; i < 16; ++i) {
+    pc[i] = (i < C && e0 + i < e1) ? pad_to(s_cnt[e0 + i], B) : 0;
+    local += pc[i];
   }
+  const int incl = wave_inclusive_scan(local);
   const int total = (int)readlane_u32((u32)incl, 63);
   int run = incl - local;
-  for (int e = e0; e < e1; ++e) {
-    s_off[e] = run;
-    run += (s_cnt[e] + B - 1) / B * B;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (i < C && e0 + i < e1) s_off[e0 + i] = run;
+    run += pc[i];
   }
   if (lane == 0) s_off[N] = total;
   for (int p = lane; p < P; p += 64) {
@@ -204,7 +208,7 @@ __device__ __forceinline__ void write_sort_layout(const int* s_cnt, const int* s
   for (int e = threadIdx.x; e < N; e += blockDim.x) {
     const int a = s_off[e], b = s_off[e + 1];
     for (int q = a + s_cnt[e]; q < b; ++q) sorted_ids[q] = P;
-    for (int blk = a / B; blk < b / B; ++blk) expert_ids[blk] = e;
+    for (int blk = div_pow2(a, B); blk < div_pow2(b, B); ++blk) expert_ids[blk] = e;
   }
 }
 
@@ -267,7 +271,7 @@ __global__ void __launch_bounds__(1024) sort_scan_kernel(int32_t* ghist, int G, 
       run += c;
     }
     s_cnt[e] = run;
-    s_off[e] = (run + B - 1) / B * B;
+    s_off[e] = pad_to(run, B);
   }
   __syncthreads();
   const int total = block_exclusive_scan(s_off, N, s_scr);
