@@ -121,12 +121,17 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
 }
 
+// Wave maximum: the row maximum by DPP, then row_bcast:15 carries rows 0 and
+// 2 into rows 1 and 3 and row_bcast:31 carries row 1 into rows 2 and 3, so
+// lane 63 ends with the maximum of all 64 lanes.
 __device__ __forceinline__ u32 wave_max_u32(u32 v) {
   v = umax(v, dpp_u32<kDppQuadXor1>(v));
   v = umax(v, dpp_u32<kDppQuadXor2>(v));
   v = umax(v, dpp_u32<kDppHalfMirror>(v));
   v = umax(v, dpp_u32<kDppMirror>(v));
-  return umax(umax(readlane_u32(v, 0), readlane_u32(v, 16)), umax(readlane_u32(v, 32), readlane_u32(v, 48)));
+  v = umax(v, (u32)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = umax(v, (u32)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return readlane_u32(v, 63);
 }
 
 __device__ __forceinline__ u64 ballot64(bool p) { return __ballot(p); }
@@ -247,45 +252,21 @@ __device__ __forceinline__ bool wait_reach(const u32* ctr, u32 base, u32 target,
 }
 
 // ---------------------------------------------------------------------------
-// MXFP8 element encoder: e4m3fn code of v / 2^se, where v is a bf16 given by
-// its bits. Integer-only: v = sig * 2^e0 exactly, so v / 2^se = sig * 2^(e0-se)
-// and rounding to the e4m3 grid is a shift with round-to-nearest-even.
-// Saturates at 448 (code 0x7e), keeps the sign (so -0 -> 0x80).
+// e4m3fn codes of four bf16 values divided by 2^se. The division is a
+// power-of-two scaling in fp32, exact whenever the result is a normal fp32
+// (anything smaller is far below 2^-10 and rounds to zero in e4m3 anyway);
+// clamping to +-448 makes every value that would round above 448 saturate to
+// 448 (code 0x7e) and keeps the conversion clear of overflow; v_cvt_pk_fp8_f32
+// then rounds to nearest, ties to even, onto the e4m3fn grid, normals and
+// subnormals alike, and keeps the sign of zero (-0 -> 0x80).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ u32 e4m3_of_bf16(u32 h, int se) {
-  const u32 sign = (h >> 8) & 0x80u;
-  const u32 ef = (h >> 7) & 0xffu;
-  const u32 mf = h & 0x7fu;
-  if ((h & 0x7fffu) == 0) return sign;
-  const int sig = ef ? (int)(mf | 0x80u) : (int)mf;
-  const int ey = (ef ? (int)ef - 134 : -133) - se;  // value = sig * 2^ey
-  const int msb = 31 - __clz(sig);
-  const int binade = msb + ey;                       // floor(log2 value)
-  if (binade > 8) return sign | 0x7eu;               // >= 512: saturate
-  const int b = binade < -6 ? -6 : binade;           // subnormal grid below 2^-6
-  const int sh = (b - 3) - ey;                       // grid spacing is 2^(b-3)
-  u32 units;
-  if (sh <= 0) {
-    units = (u32)sig << (-sh);
-  } else if (sh >= 9) {
-    units = 0;                                       // sig < 2^8: below half a step
-  } else {
-    const u32 q = (u32)sig >> sh;
-    const u32 rem = (u32)sig & ((1u << sh) - 1u);
-    const u32 half = 1u << (sh - 1);
-    units = q + ((rem > half || (rem == half && (q & 1u))) ? 1u : 0u);
-  }
-  if (units == 0) return sign;
-  u32 code;
-  if (b == -6 && units < 8) {
-    code = units;                                    // subnormal
-  } else {
-    int bb = b;
-    if (units >= 16) { units >>= 1; ++bb; }          // rounded up into the next binade
-    code = ((u32)(bb + 7) << 3) | (units - 8);
-  }
-  if (code > 0x7eu) code = 0x7eu;                    // above 448 saturates
-  return sign | code;
+__device__ __forceinline__ float scaled_bf16(u32 bits_hi16, int se) {
+  return __builtin_amdgcn_fmed3f(__builtin_amdgcn_ldexpf(__uint_as_float(bits_hi16), -se), -448.f, 448.f);
+}
+__device__ __forceinline__ u32 e4m3x4_of_bf16(u32 w0, u32 w1, int se) {
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(scaled_bf16(w0 << 16, se), scaled_bf16(w0 & 0xffff0000u, se), 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(scaled_bf16(w1 << 16, se), scaled_bf16(w1 & 0xffff0000u, se), r, true);
+  return (u32)r;
 }
 
 // Shared exponent of a 32-element block from the largest magnitude's bits

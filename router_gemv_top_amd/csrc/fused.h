@@ -4,30 +4,31 @@
 // launch (MiniMax-M3.1-Flash MoE/GEMM kernels, Summary: Router; Kimi-K3 fused
 // routing, sort, quant, Motivation). On gfx950 each hand-off between
 // workgroups costs a device-coherent memory round trip (about a microsecond),
-// so the chain below is laid out to have as few of them as possible:
+// so the chain below has as few of them as possible:
 //
-//   1. every workgroup computes one split-K GEMV tile and stores its fp32
-//      partial; the last workgroup to arrive at the n-block's counter sums
-//      the partials in k-slice order and zeroes the counter ("MiniMax-M3:
-//      Triton split-K router GEMV with in-kernel split-K fixup", opening
-//      summary), then publishes the n-block's logits as tagged words;
-//   2. the softmax top-k gate. Small M (each wave's rows fit in registers):
-//      workgroup 0 and every workgroup that owns a quant chunk poll the
-//      tagged logits and run the gate for every row themselves, so no further
-//      hand-off is needed. Larger M: row-owner workgroups (one wave per row)
-//      run it and publish the ids as tagged words, which the others poll;
+//   1. every workgroup computes one split-K GEMV tile and publishes its fp32
+//      partials as tagged words. The split-K fixup ("MiniMax-M3: Triton
+//      split-K router GEMV with in-kernel split-K fixup", opening summary) is
+//      done by the consumers of the logits themselves: they poll the partials
+//      of their rows and sum them in k-slice order, which gives the same bits
+//      as the last-arriver fixup of the standalone router;
+//   2. the softmax top-k gate. Small mode (all rows' partials fit one poll
+//      per thread): workgroup 0 and every workgroup that owns a quant chunk
+//      gather every row and run the gate themselves, so no further hand-off
+//      is needed. Large mode: workgroup r gathers row r, runs its gate and
+//      publishes the ids as tagged words, which the others poll;
 //   3. the same workgroups sort the M*k pairs in LDS with one wave (tiny at
 //      decode sizes, so redundant sorting beats another hand-off) and store
 //      their MXFP8 chunk (quantised in registers while waiting) to the padded
 //      rows of the token's pairs; workgroup 0 also writes topk_ids, topk_w,
-//      sorted_ids, expert_ids and offsets and advances the call epoch.
+//      logits, sorted_ids, expert_ids and offsets and advances the call epoch.
 //
 // A tagged word is a 32-bit payload plus the tag (epoch + 1) of the call that
-// wrote it, stored as one 8-byte atomic; readers poll the words themselves, so
-// these hand-offs need no counter. The epoch is read by every workgroup at
-// start and advanced by workgroup 0 only after all logits are in, which
-// implies every workgroup has arrived in step 1, hence has read it. Every wait is
-// bounded by a deadline that sets the workspace error word.
+// wrote it, stored as one 8-byte store; readers poll the words themselves, so
+// no hand-off needs a counter. Every wave reads the epoch before it loads its
+// tile; workgroup 0 advances it only after it has seen every partial (small
+// mode) or every id (large mode), which implies that every wave has read it.
+// Every wait is bounded by a deadline that sets the workspace error word.
 #pragma once
 
 #include "device.h"
@@ -40,10 +41,16 @@ namespace rgt {
 // Control words at the head of the workspace, 128 bytes apart.
 enum : int { kCtlErr = 0, kCtlEpoch = kCtrStride };
 
+// LDS of the tail, in ints: s_e[P], s_rank[P], s_pos[P], s_cnt[N], s_off[N+1],
+// then the gathered logits (16-byte aligned).
+__host__ __device__ constexpr int fused_log_offset(int P, int n) { return (3 * P + 2 * n + 1 + 3) & ~3; }
+
 struct FusedArgs {
-  GemvArgs g;          // g.logits unused here
+  GemvArgs g;          // g.logits, g.part and g.ctr unused here
   const float* bias;   // [N] or null
   int topk, block;
+  int small;           // 1: small mode, 0: large mode (chosen by the host)
+  int upw_log;         // log2 of the quant units per participating workgroup (6, 7 or 8)
   float* logits_out;   // [M][N] or null
   int32_t* topk_ids;
   float* topk_w;
@@ -53,281 +60,340 @@ struct FusedArgs {
   uint8_t* a_q;
   uint8_t* a_scale;
   u32* ctl;
-  u64* tlogits;        // [M][N] tagged logits (workspace)
-  u64* tids;           // [M*topk] tagged expert ids (workspace)
+  u64* tpart;          // [S][M][N] tagged partials (workspace)
+  u64* tids;           // [M*topk] tagged expert ids (workspace, padded to 16 bytes)
   u64 budget;          // deadline of each wait, in 100 MHz ticks
-  int fault_skip;      // host-forced fault: 1 = the fixup never publishes logits
+  int fault_skip;      // host-forced fault: 1 = no partial is ever published
   u64* trace;          // phase stamps (trace build only), 16 per workgroup
 };
 
-// Writer of the finisher's sums: optional plain logits, and tagged logits.
-struct TaggedLogitsOut {
-  float* logits_out;
-  u64* tlogits;
-  int n;
+// The call's tag, read by every wave on its own (no barrier): epoch + 1,
+// skipping 0 so zero-filled words never look ready.
+__device__ __forceinline__ u32 call_tag(const u32* ctl) {
+  const u32 t = (u32)__builtin_amdgcn_readfirstlane((int)ld_agent(ctl + kCtlEpoch)) + 1u;
+  return t ? t : 1u;
+}
+
+// Publisher of a tile's partials as tagged words tpart[s][m][c].
+struct TaggedPartials {
+  u64* tpart;
+  int m, n;
   u32 tag;
   int skip;  // host-forced fault: publish nothing, so every reader's wait expires
-  __device__ __forceinline__ void operator()(int m, int c, float4 v) const {
-    if (logits_out) *reinterpret_cast<float4*>(logits_out + (int64_t)m * n + c) = v;
+  __device__ __forceinline__ void operator()(int s, int row, int col, float v) const {
     if (skip) return;
-    u64* t = tlogits + (int64_t)m * n + c;
-    st_agent(t + 0, tag_word(__float_as_uint(v.x), tag));
-    st_agent(t + 1, tag_word(__float_as_uint(v.y), tag));
-    st_agent(t + 2, tag_word(__float_as_uint(v.z), tag));
-    st_agent(t + 3, tag_word(__float_as_uint(v.w), tag));
+    st_agent(tpart + ((int64_t)s * m + row) * n + col, tag_word(__float_as_uint(v), tag));
   }
 };
 
 __device__ __forceinline__ void set_timeout(const FusedArgs& a) { or_agent(a.ctl + kCtlErr, kErrTimeout); }
 
-// Rows of tagged logits one wave holds at once (register budget: 8 score
-// slots per lane).
-template <int NV>
-struct RowsHeld {
-  static constexpr int value = NV >= 8 ? 1 : 8 / NV;
-};
+// 16-byte loads one thread keeps in flight per poll (two polls in flight).
+constexpr int kPollLoads = 16;
 
-// Small mode: every participating workgroup runs the gate for every row
-// itself (no ids hand-off), possible while each wave's rows fit in registers.
-template <int NV>
-__host__ __device__ constexpr bool small_mode(int m) {
-  return (m + 3) / 4 <= RowsHeld<NV>::value;
-}
-
-// One wave polls `cnt` rows of tagged logits (rows r0, r0 + 4, ...) until
-// every word carries `tag`. Two polls are kept in flight, so a hand-off is
-// seen about one memory round trip after it lands.
-template <int NV, int R>
-__device__ __forceinline__ bool poll_rows(const u64* tlog, int n, int r0, int cnt, u32 tag, const FusedArgs& a,
-                                          float (&sv)[R][NV]) {
-  const int lane = lane_id();
-  auto issue = [&](u64 (&w)[R][NV]) {
+// The workgroup gathers rows [r0, r0 + rows) of the logits from the tagged
+// partials into s_log[(row - r0) * n + col]. An item is one column pair of
+// one row (one 16-byte load per k-slice); thread t takes items t, t + 256,
+// ... and their S slices, nl <= NL loads in all (a thread with fewer items
+// repeats its last one). Each thread polls its own loads until every word
+// carries the tag, then sums each item's slices in k-slice order. Returns
+// false (error word set) if the deadline passes.
+template <int NL>
+__device__ __forceinline__ bool gather_logits(const FusedArgs& a, int r0, int rows, u32 tag, float* s_log) {
+  __shared__ u32 s_bad;
+  const int n = a.g.n, S = a.g.s_count;
+  const int pairs = n >> 1, items = rows * pairs;
+  const u32 slice = (u32)a.g.m * (u32)n * 8u;
+  const int t = threadIdx.x;
+  if (t == 0) s_bad = 0u;
+  __syncthreads();
+  if (t < items) {
+    const auto rsrc = coherent_rsrc(a.tpart, slice * (u32)S);
+    const u32 row_base = (u32)r0 * (u32)n * 8u;
+    auto item_off = [&](int it) {
+      const int rr = it / pairs;
+      return row_base + ((u32)rr * (u32)n + 2u * (u32)(it - rr * pairs)) * 8u;
+    };
+    u32 off[NL];
+    {
+      int it = t, s = 0;
+      u32 base = item_off(it);
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const int row = r < cnt ? r0 + 4 * r : r0;
-        w[r][i] = ld_agent(tlog + (int64_t)row * n + min(lane + 64 * i, n - 1));
+      for (int l = 0; l < NL; ++l) {
+        off[l] = base + (u32)s * slice;
+        if (++s == S) {
+          s = 0;
+          it += 256;
+          if (it < items) base = item_off(it);
+        }
       }
-  };
-  auto ready = [&](const u64 (&w)[R][NV]) {
-    bool ok = true;
+    }
+    auto issue = [&](u32x4_t (&v)[NL]) {
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+      for (int l = 0; l < NL; ++l) v[l] = ld_agent16(rsrc, off[l]);
+    };
+    auto ready = [&](const u32x4_t (&v)[NL]) {
+      bool ok = true;
 #pragma unroll
-      for (int i = 0; i < NV; ++i) ok = ok && tag_ok(w[r][i], tag);
-    return __all(ok);
-  };
-  auto take = [&](const u64 (&w)[R][NV]) {
+      for (int l = 0; l < NL; ++l) ok = ok & (v[l].y == tag) & (v[l].w == tag);
+      return ok;
+    };
+    auto take = [&](const u32x4_t (&v)[NL]) {
+      int s = 0, it = t;
+      float2 acc = make_float2(0.f, 0.f);
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int i = 0; i < NV; ++i) sv[r][i] = __uint_as_float((u32)w[r][i]);
-  };
-  const u64 t0 = rt_clock();
-  u64 wa[R][NV], wb[R][NV];
-  issue(wa);
-  issue(wb);
-  for (;;) {
-    if (ready(wa)) { take(wa); return true; }
-    issue(wa);
-    if (ready(wb)) { take(wb); return true; }
-    issue(wb);
-    if (rt_clock() - t0 > a.budget) {
-      if (lane == 0) set_timeout(a);
-      return false;
+      for (int l = 0; l < NL; ++l) {
+        acc.x += __uint_as_float(v[l].x);
+        acc.y += __uint_as_float(v[l].z);
+        if (++s == S) {
+          if (it < items) {
+            const u32 d = ((off[l] - (u32)(S - 1) * slice - row_base) >> 3);
+            *reinterpret_cast<float2*>(s_log + d) = acc;
+          }
+          acc = make_float2(0.f, 0.f);
+          s = 0;
+          it += 256;
+        }
+      }
+    };
+    const u64 t0 = rt_clock();
+    u32x4_t va[NL], vb[NL];
+    issue(va);
+    issue(vb);
+    for (;;) {
+      if (ready(va)) { take(va); break; }
+      issue(va);
+      if (ready(vb)) { take(vb); break; }
+      issue(vb);
+      if (rt_clock() - t0 > a.budget) {
+        set_timeout(a);
+        s_bad = 1u;
+        break;
+      }
     }
   }
+  __syncthreads();
+  return s_bad == 0u;
 }
 
-// The workgroup polls all P tagged ids until every word carries `tag`, then
-// leaves the experts in s_e. Two polls in flight, as above.
-__device__ __forceinline__ bool poll_ids(const u64* tids, int P, u32 tag, const FusedArgs& a, int* s_e) {
-  __shared__ u32 s_late;
-  constexpr int kPer = 8;  // words per thread per pass (P <= 2048)
-  auto issue = [&](u64 (&w)[kPer]) {
+// Loads per thread that a gather of `rows` rows needs.
+__host__ __device__ constexpr int gather_loads(int rows, int n, int s) { return (rows * (n / 2) + 255) / 256 * s; }
+
+__device__ __forceinline__ bool gather_any(const FusedArgs& a, int r0, int rows, u32 tag, float* s_log) {
+  const int nl = gather_loads(rows, a.g.n, a.g.s_count);
+  if (nl <= 4) return gather_logits<4>(a, r0, rows, tag, s_log);
+  if (nl <= 8) return gather_logits<8>(a, r0, rows, tag, s_log);
+  return gather_logits<kPollLoads>(a, r0, rows, tag, s_log);
+}
+
+// The workgroup polls the P tagged ids (16-byte loads, two words each; thread
+// t takes word pairs t, t + 256, ...) until every word carries the tag, then
+// leaves the experts in s_e.
+template <int NL>
+__device__ __forceinline__ bool poll_ids(const FusedArgs& a, int P, u32 tag, int* s_e) {
+  __shared__ u32 s_bad;
+  const int t = threadIdx.x;
+  const int pairs = (P + 1) >> 1;
+  if (t == 0) s_bad = 0u;
+  __syncthreads();
+  if (t < pairs) {
+    const auto rsrc = coherent_rsrc(a.tids, (u32)pairs * 16u);
+    auto pair_of = [&](int l) { return min(t + 256 * l, pairs - 1); };
+    auto issue = [&](u32x4_t (&v)[NL]) {
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) w[j] = ld_agent(tids + min((int)threadIdx.x + 256 * j, P - 1));
-  };
-  auto ready = [&](const u64 (&w)[kPer]) {
-    bool ok = true;
+      for (int l = 0; l < NL; ++l) v[l] = ld_agent16(rsrc, (u32)pair_of(l) * 16u);
+    };
+    auto ready = [&](const u32x4_t (&v)[NL]) {
+      bool ok = true;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) ok = ok && tag_ok(w[j], tag);
-    return __syncthreads_and(ok) != 0;
-  };
-  auto take = [&](const u64 (&w)[kPer]) {
+      for (int l = 0; l < NL; ++l) ok = ok & (v[l].y == tag) & ((2 * pair_of(l) + 1 >= P) | (v[l].w == tag));
+      return ok;
+    };
+    auto take = [&](const u32x4_t (&v)[NL]) {
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int p = threadIdx.x + 256 * j;
-      if (p < P) s_e[p] = (int)(u32)w[j];
-    }
-    __syncthreads();
-  };
-  const u64 t0 = rt_clock();
-  u64 wa[kPer], wb[kPer];
-  issue(wa);
-  issue(wb);
-  for (;;) {
-    if (ready(wa)) { take(wa); return true; }
-    issue(wa);
-    if (ready(wb)) { take(wb); return true; }
-    issue(wb);
-    if (threadIdx.x == 0) s_late = rt_clock() - t0 > a.budget ? 1u : 0u;
-    __syncthreads();
-    if (s_late) {
-      if (threadIdx.x == 0) set_timeout(a);
-      return false;
+      for (int l = 0; l < NL; ++l) {
+        const int q = t + 256 * l;
+        if (q < pairs) {
+          s_e[2 * q] = (int)v[l].x;
+          if (2 * q + 1 < P) s_e[2 * q + 1] = (int)v[l].z;
+        }
+      }
+    };
+    const u64 t0 = rt_clock();
+    u32x4_t va[NL], vb[NL];
+    issue(va);
+    issue(vb);
+    for (;;) {
+      if (ready(va)) { take(va); break; }
+      issue(va);
+      if (ready(vb)) { take(vb); break; }
+      issue(vb);
+      if (rt_clock() - t0 > a.budget) {
+        set_timeout(a);
+        s_bad = 1u;
+        break;
+      }
     }
   }
+  __syncthreads();
+  return s_bad == 0u;
+}
+
+__device__ __forceinline__ bool poll_ids_any(const FusedArgs& a, int P, u32 tag, int* s_e) {
+  const int nl = (P + 511) / 512;
+  if (nl <= 1) return poll_ids<1>(a, P, tag, s_e);
+  if (nl <= 2) return poll_ids<2>(a, P, tag, s_e);
+  return poll_ids<4>(a, P, tag, s_e);
+}
+
+// One wave runs the gate of one row held in LDS (lane-major loads).
+template <int NV>
+__device__ __forceinline__ void row_gate(const FusedArgs& a, const float* row_log, int& id, float& w) {
+  const int n = a.g.n, c0 = lane_id() * NV;
+  float sv[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) sv[i] = row_log[min(c0 + i, n - 1)];
+  add_bias<NV>(sv, a.bias, n);
+  wave_topk_regs<NV>(sv, n, a.topk, id, w);
 }
 
 template <int NV>
 __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 tag, bool have_unit, int unit,
                                            const uint4& codes_in, u32 sb_in) {
-  __shared__ u32 s_fail;
   const GemvArgs& g = a.g;
   const int m = g.m, n = g.n, k = a.topk;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int units = m * (g.k >> 4);
-  const bool participant = blockIdx.x == 0 || (int)blockIdx.x * 256 < units;
+  // The sort outputs are written by the workgroup after the last one with
+  // quant units (if the grid has one), so that they overlap the stores.
+  const int layout_wg = min((int)gridDim.x - 1, ((units - 1) >> a.upw_log) + 1);
+  const bool participant = blockIdx.x == 0 || ((int)blockIdx.x << a.upw_log) < units || (int)blockIdx.x == layout_wg;
   const int P = m * k;
   int* s_e = smem;
   int* s_rank = s_e + P;
   int* s_pos = s_rank + P;
   int* s_cnt = s_pos + P;
   int* s_off = s_cnt + n;
-  if (small_mode<NV>(m)) {
-    // Step 2 (small): each participant runs the gate for every row; wave w
-    // takes rows w, w + 4, ... straight from the tagged logits.
+  int* s_hist = s_off + n + 1;  // 4*n, past s_off; reuses the gathered logits' space
+  float* s_log = reinterpret_cast<float*>(smem + fused_log_offset(P, n));
+  if (a.small) {
+    // Step 2 (small): each participant gathers every row and runs every gate;
+    // wave w takes rows w, w + 4, ...
     if (!participant) return;
-    if (threadIdx.x == 0) s_fail = 0u;
-    __syncthreads();
-    constexpr int R = RowsHeld<NV>::value;
-    const int cnt = wave < m ? (m - 1 - wave) / 4 + 1 : 0;
-    if (cnt > 0) {
-      float sv[R][NV];
-      if (poll_rows<NV, R>(a.tlogits, n, wave, cnt, tag, a, sv)) {
-        RGT_STAMP(a.trace, 5);
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          if (r < cnt) {
-            const int row = wave + 4 * r;
-            add_bias<NV>(sv[r], a.bias, n);
-            int id;
-            float w;
-            wave_topk_regs<NV>(sv[r], n, k, id, w);
-            if (lane < k) {
-              s_e[row * k + lane] = id;
-              if (blockIdx.x == 0) {
-                a.topk_ids[(int64_t)row * k + lane] = id;
-                a.topk_w[(int64_t)row * k + lane] = w;
-              }
-            }
-          }
+    if (!gather_any(a, 0, m, tag, s_log)) return;
+    RGT_STAMP(a.trace, 5);
+    for (int row = wave; row < m; row += 4) {
+      int id;
+      float w;
+      row_gate<NV>(a, s_log + row * n, id, w);
+      if (lane < k) {
+        s_e[row * k + lane] = id;
+        if (blockIdx.x == 0) {
+          a.topk_ids[row * k + lane] = id;
+          a.topk_w[row * k + lane] = w;
         }
-        RGT_STAMP(a.trace, 6);
-      } else if (lane == 0) {
-        s_fail = 1u;
       }
     }
+    if (blockIdx.x == 0 && a.logits_out)
+      for (int i = threadIdx.x; i < m * n; i += 256) a.logits_out[i] = s_log[i];
     __syncthreads();
-    if (s_fail) return;
+    RGT_STAMP(a.trace, 6);
   } else {
-    // Step 2 (large): row owners, one wave per row, publish tagged ids.
-    const int row_groups = (m + 3) >> 2;
-    if ((int)blockIdx.x < row_groups) {
-      const int row = blockIdx.x * 4 + wave;
-      if (row < m) {
-        float sv[1][NV];
-        if (poll_rows<NV, 1>(a.tlogits, n, row, 1, tag, a, sv)) {
-          RGT_STAMP(a.trace, 5);
-          add_bias<NV>(sv[0], a.bias, n);
-          int id;
-          float w;
-          wave_topk_regs<NV>(sv[0], n, k, id, w);
-          if (lane < k) {
-            a.topk_ids[(int64_t)row * k + lane] = id;
-            a.topk_w[(int64_t)row * k + lane] = w;
-            st_agent(a.tids + (int64_t)row * k + lane, tag_word((u32)id, tag));
-          }
-          RGT_STAMP(a.trace, 6);
+    // Step 2 (large): workgroup r gathers row r, runs its gate and publishes
+    // the ids; then every participant polls all ids.
+    if ((int)blockIdx.x < m) {
+      const int row = blockIdx.x;
+      if (!gather_any(a, row, 1, tag, s_log)) return;
+      RGT_STAMP(a.trace, 5);
+      if (wave == 0) {
+        int id;
+        float w;
+        row_gate<NV>(a, s_log, id, w);
+        if (lane < k) {
+          st_agent(a.tids + row * k + lane, tag_word((u32)id, tag));
+          a.topk_ids[row * k + lane] = id;
+          a.topk_w[row * k + lane] = w;
         }
       }
+      if (a.logits_out)
+        for (int i = threadIdx.x; i < n; i += 256) a.logits_out[(int64_t)row * n + i] = s_log[i];
+      RGT_STAMP(a.trace, 6);
     }
     if (!participant) return;
-    if (!poll_ids(a.tids, P, tag, a, s_e)) return;
+    if (!poll_ids_any(a, P, tag, s_e)) return;
   }
   RGT_STAMP(a.trace, 7);
-  // Every workgroup has read the epoch (all logits are in, so every
-  // workgroup arrived in step 1): advance it for the next call.
+  // Every wave of the grid has read the epoch (see the top of this file):
+  // advance it for the next call.
   if (blockIdx.x == 0 && threadIdx.x == 0) st_agent(a.ctl + kCtlEpoch, tag);
   // Step 3: one wave sorts the pairs in LDS; the workgroup stores its
   // quantised chunk to the padded rows of the token's pairs.
-  if (threadIdx.x < 64) wave_sort((const int32_t*)nullptr, P, n, a.block, s_e, s_rank, s_cnt, s_off, s_pos);
-  __syncthreads();
-  RGT_STAMP(a.trace, 8);
-  if (blockIdx.x == 0) {
-    for (int p = threadIdx.x; p < P; p += blockDim.x)
-      if (s_pos[p] >= 0) a.sorted_ids[s_pos[p]] = p;
-    write_sort_layout(s_cnt, s_off, n, a.block, P, a.sorted_ids, a.expert_ids, a.offsets);
+  if (P <= kWaveSortSmallP) {
+    if (threadIdx.x < 64) wave_sort_small<NV>(P, n, a.block, s_e, s_cnt, s_off, s_pos);
+    __syncthreads();
+  } else {
+    wg4_sort<NV>(P, n, a.block, s_e, s_rank, s_hist, s_cnt, s_off, s_pos);
   }
+  RGT_STAMP(a.trace, 8);
+  if ((int)blockIdx.x == layout_wg)
+    write_sort_outputs<256>(s_e, s_pos, s_cnt, s_off, n, a.block, P, a.sorted_ids, a.expert_ids, a.offsets);
   const u32 scales4 = pack_scales(sb_in);  // all lanes: DPP reads neighbouring lanes
   if (have_unit) store_unit(a.a_q, a.a_scale, g.k, k, unit, s_pos, codes_in, scales4);
   RGT_STAMP(a.trace, 9);
 }
 
-// Shared head of both kernels: read the epoch, run the tile, fix up, quantise.
-// tile(nb, s) computes this workgroup's GEMV tile; bn is experts per n-block.
+// Shared head of both kernels: read the tag, run the tile, quantise, then the
+// tail. tile(nb, s, sink) computes this workgroup's GEMV tile.
 template <int NV, class Tile>
-__device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, int bn, Tile tile) {
-  __shared__ u32 s_tag;
+__device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, Tile tile) {
   const GemvArgs& g = a.g;
   const int units = g.m * (g.k >> 4);
-  const int unit = blockIdx.x * 256 + threadIdx.x;
-  const bool have_unit = unit < units;
+  const int unit = ((int)blockIdx.x << a.upw_log) + threadIdx.x;
+  const bool have_unit = (int)threadIdx.x < (1 << a.upw_log) && unit < units;
   const int tile_id = xcd_tile(blockIdx.x, gridDim.x);
-  const int nb = tile_id % g.nb_count;
   RGT_STAMP(a.trace, 0);
-  // The epoch load completes before this workgroup's arrival (the arrival
-  // drains every outstanding memory operation first).
-  if (threadIdx.x == 0) {
-    const u32 t = ld_agent(a.ctl + kCtlEpoch) + 1u;
-    s_tag = t ? t : 1u;  // tag 0 is never used, so zero-filled words never look ready
-  }
-  tile(nb, tile_id / g.nb_count);
+  const u32 tag = call_tag(a.ctl);  // issued before the tile's loads
+  // The thread's quant chunk of x is loaded right after the tile's W loads
+  // are issued, and quantised once the tile is done.
+  uint4 xa = make_uint4(0, 0, 0, 0), xb = make_uint4(0, 0, 0, 0);
+  auto prefetch = [&]() {
+    if (have_unit) {
+      const int cpr = g.k >> 4, t = unit / cpr, c = unit - t * cpr;
+      const u16* src = g.x + (int64_t)t * g.ldx + 16 * c;
+      xa = ld16(src);
+      xb = ld16(src + 8);
+    }
+  };
+  tile(tile_id, TaggedPartials{a.tpart, g.m, g.n, tag, a.fault_skip}, prefetch);
   RGT_STAMP(a.trace, 1);
-  u32* tile_ctr = g.ctr + nb * kCtrStride;
-  const bool last = arrive_last(tile_ctr, (u32)g.s_count);  // has barriers: s_tag is visible after it
-  const u32 tag = s_tag;
-  if (last) {
-    RGT_STAMP(a.trace, 2);
-    reduce_partials(g, 0, g.m, nb * bn, bn, TaggedLogitsOut{a.logits_out, a.tlogits, g.n, tag, a.fault_skip});
-    if (threadIdx.x == 0) st_agent(tile_ctr, 0u);
-    RGT_STAMP(a.trace, 3);
-  }
   u32 sb = 0;
-  uint4 codes = make_uint4(0, 0, 0, 0);
-  if (have_unit) {
-    const int cpr = g.k >> 4, t = unit / cpr, c = unit - t * cpr;
-    codes = mx_quant16(g.x + (int64_t)t * g.ldx + 16 * c, sb);
-  }
+  const uint4 codes = mx_quant16_regs(xa, xb, sb);  // all lanes: the scale exchange reads the partner lane
   __syncthreads();  // the tile's LDS is reused below
+  RGT_STAMP(a.trace, 4);
   fused_tail<NV>(a, smem, tag, have_unit, unit, codes, sb);
 }
 
-// Quant unit of a thread: unit = global thread id (the host guarantees
-// M*K/16 <= grid*256).
+// Quant units (16-element chunks of x, row-major) go 2^upw_log to a
+// workgroup, to its first threads (the host guarantees M*K/16 <= grid *
+// 2^upw_log): fewer units per workgroup spread the stores of the tail over
+// more CUs.
 template <int NV, int MT, int RPW, int L>
 __global__ void __launch_bounds__(256) fused_valu_kernel(FusedArgs a) {
   extern __shared__ int smem[];
-  fused_body<NV>(a, smem, 4 * RPW, [&](int nb, int s) { valu_tile<MT, RPW, L>(a.g, nb, s); });
+  fused_body<NV>(a, smem, [&](int t, const TaggedPartials& sink, auto&& pre) {
+    valu_tile<MT, RPW, L>(a.g, t % a.g.nb_count, t / a.g.nb_count, sink, pre);
+  });
 }
 
 template <int NV, int MT, int KS>
 __global__ void __launch_bounds__(256) fused_mfma_kernel(FusedArgs a) {
   extern __shared__ int smem[];
-  fused_body<NV>(a, smem, 16,
-                 [&](int nb, int s) { mfma_tile<MT, KS>(a.g, 0, nb, s, reinterpret_cast<float*>(smem)); });
+  fused_body<NV>(a, smem, [&](int t, const TaggedPartials& sink, auto&& pre) {
+    const int nb = t % a.g.nb_count;
+    const int s = (t / a.g.nb_count) % a.g.s_count;
+    const int mb = t / (a.g.nb_count * a.g.s_count);
+    mfma_tile<MT, KS>(a.g, mb, nb, s, reinterpret_cast<float*>(smem), sink, pre);
+  });
 }
 
 }  // namespace rgt

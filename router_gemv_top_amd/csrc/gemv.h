@@ -39,13 +39,29 @@ struct GemvArgs {
 
 __device__ __forceinline__ uint4 ld16(const u16* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// Receiver of a tile's partial sums: sink(s, m, c, v) gets the fp32 partial of
+// row m, expert c, k-slice s. This one stores it with an agent-scope store to
+// part[s][m][c] for the fixup by the last arriver.
+struct PartialSink {
+  float* part;
+  int m, n;
+  __device__ __forceinline__ void operator()(int s, int row, int col, float v) const {
+    st_agent(part + ((int64_t)s * m + row) * n + col, v);
+  }
+};
+
 // ---------------------------------------------------------------------------
 // VALU tile. Workgroup = 4 waves; wave w owns rows n0 + w*RPW .. +RPW of the
 // n-block, over the workgroup's k-slice of 512*L elements. Lane l covers the
 // 8 elements at k = kslice + j*512 + 8*l for j < L.
 // ---------------------------------------------------------------------------
-template <int MT, int RPW, int L>
-__device__ __forceinline__ void valu_tile(const GemvArgs& a, int nb, int s) {
+// pre() runs once the tile's W loads are issued (other loads to overlap).
+struct NoPrefetch {
+  __device__ __forceinline__ void operator()() const {}
+};
+
+template <int MT, int RPW, int L, class Sink, class Pre = NoPrefetch>
+__device__ __forceinline__ void valu_tile(const GemvArgs& a, int nb, int s, const Sink& sink, Pre&& pre = Pre()) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nrow0 = nb * (4 * RPW) + wave * RPW;
   const int kb = s * (512 * L) + lane * 8;
@@ -54,6 +70,7 @@ __device__ __forceinline__ void valu_tile(const GemvArgs& a, int nb, int s) {
   for (int r = 0; r < RPW; ++r)
 #pragma unroll
     for (int j = 0; j < L; ++j) wv[r][j] = ld16(a.w + (int64_t)(nrow0 + r) * a.ldw + kb + j * 512);
+  pre();
   float acc[RPW][MT];
 #pragma unroll
   for (int r = 0; r < RPW; ++r)
@@ -74,12 +91,11 @@ __device__ __forceinline__ void valu_tile(const GemvArgs& a, int nb, int s) {
   for (int r = 0; r < RPW; ++r)
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[r][m] = wave_sum(acc[r][m]);
-  float* part = a.part + (int64_t)s * a.m * a.n;
 #pragma unroll
   for (int r = 0; r < RPW; ++r)
 #pragma unroll
     for (int m = 0; m < MT; ++m)
-      if (lane == r * MT + m && m < a.m) st_agent(&part[(int64_t)m * a.n + nrow0 + r], acc[r][m]);
+      if (lane == r * MT + m && m < a.m) sink(s, m, nrow0 + r, acc[r][m]);
 }
 
 // ---------------------------------------------------------------------------
@@ -92,8 +108,9 @@ __device__ __forceinline__ void valu_tile(const GemvArgs& a, int nb, int s) {
 // A lane l: x[row0 + l%16][k-run of group l/16]; B lane l: W[n0 + l%16][same k].
 // D lane l: rows 4*(l/16)+i (i < 4) of the 16x16 tile, column l%16.
 // ---------------------------------------------------------------------------
-template <int MT, int KS>
-__device__ __forceinline__ void mfma_tile(const GemvArgs& a, int mb, int nb, int s, float* lds) {
+template <int MT, int KS, class Sink, class Pre = NoPrefetch>
+__device__ __forceinline__ void mfma_tile(const GemvArgs& a, int mb, int nb, int s, float* lds, const Sink& sink,
+                                          Pre&& pre = Pre()) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r16 = lane & 15, grp = lane >> 4;
   const int kslice = 4 * 32 * KS;
@@ -102,6 +119,7 @@ __device__ __forceinline__ void mfma_tile(const GemvArgs& a, int mb, int nb, int
   uint4 bw[KS];
 #pragma unroll
   for (int j = 0; j < KS; ++j) bw[j] = ld16(a.w + (int64_t)n * a.ldw + krun + 8 * j);
+  pre();
   floatx4_t acc[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
@@ -123,7 +141,6 @@ __device__ __forceinline__ void mfma_tile(const GemvArgs& a, int mb, int nb, int
 #pragma unroll
     for (int i = 0; i < 4; ++i) lds[((wave * MT + t) * 16 + grp * 4 + i) * 16 + r16] = acc[t][i];
   __syncthreads();
-  float* part = a.part + (int64_t)s * a.m * a.n;
   for (int idx = threadIdx.x; idx < MT * 256; idx += 256) {
     const int t = idx >> 8, rc = idx & 255, rr = rc >> 4, cc = rc & 15;
     const int m = row_base + t * 16 + rr;
@@ -131,7 +148,7 @@ __device__ __forceinline__ void mfma_tile(const GemvArgs& a, int mb, int nb, int
     v += lds[((1 * MT + t) * 16 + rr) * 16 + cc];
     v += lds[((2 * MT + t) * 16 + rr) * 16 + cc];
     v += lds[((3 * MT + t) * 16 + rr) * 16 + cc];
-    if (m < a.m) st_agent(&part[(int64_t)m * a.n + nb * 16 + cc], v);
+    if (m < a.m) sink(s, m, nb * 16 + cc, v);
   }
 }
 
@@ -161,7 +178,7 @@ __device__ __forceinline__ void reduce_partials(const GemvArgs& a, int r0, int r
   const int rows = r1 - r0, quads = bn >> 2, lq = __ffs(quads) - 1;  // quads is 1, 2 or 4
   const u32 slice = (u32)a.m * (u32)a.n * 4u;
   const auto rsrc = coherent_rsrc(a.part, slice * (u32)a.s_count);
-  for (int idx = threadIdx.x; idx < rows * quads; idx += blockDim.x) {
+  for (int idx = threadIdx.x; idx < rows * quads; idx += 256) {  // 256-thread workgroups
     const int m = r0 + (idx >> lq), c = c0 + 4 * (idx & (quads - 1));
     const u32 off = ((u32)m * (u32)a.n + (u32)c) * 4u;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -199,7 +216,7 @@ template <int MT, int RPW, int L>
 __global__ void __launch_bounds__(256) router_valu_kernel(GemvArgs a) {
   const int t = xcd_tile(blockIdx.x, gridDim.x);
   const int nb = t % a.nb_count, s = t / a.nb_count;
-  valu_tile<MT, RPW, L>(a, nb, s);
+  valu_tile<MT, RPW, L>(a, nb, s, PartialSink{a.part, a.m, a.n});
   u32* ctr = a.ctr + nb * kCtrStride;
   if (arrive_last(ctr, (u32)a.s_count)) {
     reduce_partials(a, 0, a.m, nb * 4 * RPW, 4 * RPW, LogitsOut{a.logits, a.n});
@@ -214,7 +231,7 @@ __global__ void __launch_bounds__(256) router_mfma_kernel(GemvArgs a) {
   const int nb = t % a.nb_count;
   const int s = (t / a.nb_count) % a.s_count;
   const int mb = t / (a.nb_count * a.s_count);
-  mfma_tile<MT, KS>(a, mb, nb, s, lds);
+  mfma_tile<MT, KS>(a, mb, nb, s, lds, PartialSink{a.part, a.m, a.n});
   u32* ctr = a.ctr + (mb * a.nb_count + nb) * kCtrStride;
   if (arrive_last(ctr, (u32)a.s_count)) {
     const int r0 = mb * 16 * MT;

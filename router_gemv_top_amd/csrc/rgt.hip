@@ -59,7 +59,8 @@ struct Plan {
   bool valu;     // VALU tile (M <= 8) or MFMA tile
   int mt;        // VALU: rows in the template (1,2,4,8); MFMA: 16-row tiles (1..4)
   int rpw;       // VALU rows of W per wave
-  int ks;        // MFMA k-steps of 32 per wave
+  int l;         // VALU 512-element k-chunks per lane (1, 2, 4 or 7)
+  int ks;        // MFMA k-steps of 32 per wave (2, 4 or 8)
   int nb;        // n-blocks
   int s;         // k-slices
   int mb;        // row blocks (MFMA)
@@ -73,24 +74,55 @@ int pow2_at_least(int v) {
   return p;
 }
 
+// Fewest k-slices that still give this many workgroups: every k-slice is one
+// more partial per output for the fixup to read, and every workgroup one
+// more to dispatch, so decode shapes aim at about a third of the CUs.
+#ifndef RGT_MIN_GRID
+#define RGT_MIN_GRID 96
+#endif
+#ifndef RGT_MFMA_ROWS_GRID
+#define RGT_MFMA_ROWS_GRID 192
+#endif
+
 Plan make_plan(int m, int n, int k) {
   Plan p{};
   if (m <= 8) {
     p.valu = true;
     p.mt = pow2_at_least(std::max(m, 1));
-    p.rpw = n <= 256 ? 1 : 4;
-    p.bn = 4 * p.rpw;
-    p.nb = n / p.bn;
-    p.s = k / 512;
+    p.rpw = 1;
+    p.bn = 4;
+    p.nb = n / 4;
     p.mb = 1;
+    const int chunks = k / 512;
+    p.l = 1;
+    for (int l : {7, 4, 2}) {
+      if (chunks % l == 0 && p.nb * (chunks / l) >= RGT_MIN_GRID) {
+        p.l = l;
+        break;
+      }
+    }
+    p.s = chunks / p.l;
   } else {
+    // Fewest k-slices that give RGT_MIN_GRID workgroups with the tallest row
+    // tile; then shorter row tiles while the grid stays under
+    // RGT_MFMA_ROWS_GRID (each workgroup streams 16*MT rows of x from L2).
     p.valu = false;
-    p.mt = std::min(4, (m + 15) / 16);
-    p.mb = (m + 16 * p.mt - 1) / (16 * p.mt);
     p.bn = 16;
     p.nb = n / 16;
-    p.ks = (p.nb * p.mb * (k / 512) >= 128) ? 4 : 2;
+    p.mt = std::min(4, (m + 15) / 16);
+    p.mb = (m + 16 * p.mt - 1) / (16 * p.mt);
+    p.ks = 2;
+    for (int ks : {8, 4}) {
+      if (k % (128 * ks) == 0 && p.nb * p.mb * (k / (128 * ks)) >= RGT_MIN_GRID) {
+        p.ks = ks;
+        break;
+      }
+    }
     p.s = k / (128 * p.ks);
+    while (p.mt > 1 && p.nb * p.s * p.mb < RGT_MFMA_ROWS_GRID) {
+      p.mt = p.mt == 4 ? 2 : 1;
+      p.mb = (m + 16 * p.mt - 1) / (16 * p.mt);
+    }
   }
   p.grid = p.nb * p.s * p.mb;
   return p;
@@ -102,7 +134,7 @@ Plan make_plan(int m, int n, int k) {
 // are the only state that must stay zero between calls).
 // ---------------------------------------------------------------------------
 struct Layout {
-  size_t ctl, ctr, part, logits, tlog, tids, pos, ghist, offws, trace, total;
+  size_t ctl, ctr, part, logits, tpart, tids, pos, ghist, offws, trace, total;
 };
 
 int large_sort_groups(int P) { return (P + kLargeSortChunk - 1) / kLargeSortChunk; }
@@ -116,10 +148,10 @@ Layout make_layout(int m, int n, int k, int topk) {
   L.ctr = o; o = align_up(o + sizeof(u32) * kCtrStride * (size_t)kMaxTileCounters, kAlign);
   L.part = o; o = align_up(o + sizeof(float) * (size_t)p.s * m * n, kAlign);
   L.logits = o; o = align_up(o + sizeof(float) * (size_t)m * n, kAlign);
-  L.tlog = L.tids = o;
+  L.tpart = L.tids = o;
   if (m <= kFusedMaxM) {  // tagged hand-off words of the one-launch path
-    L.tlog = o; o = align_up(o + sizeof(u64) * (size_t)m * n, kAlign);
-    L.tids = o; o = align_up(o + sizeof(u64) * (size_t)P, kAlign);
+    L.tpart = o; o = align_up(o + sizeof(u64) * (size_t)p.s * m * n, kAlign);
+    L.tids = o; o = align_up(o + sizeof(u64) * (size_t)(P + 1), kAlign);
   }
   L.pos = o; o = align_up(o + sizeof(int32_t) * (size_t)P, kAlign);
   L.ghist = o;
@@ -179,21 +211,23 @@ int nv_bucket(int n) {
   return 16;
 }
 
-template <int MT, int RPW>
-void launch_router_valu(const GemvArgs& a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((router_valu_kernel<MT, RPW, 1>), dim3(grid), dim3(256), 0, st, a);
-}
-
 template <int MT>
 void launch_router_valu_rpw(const GemvArgs& a, const Plan& p, hipStream_t st) {
-  if (p.rpw == 1) launch_router_valu<MT, 1>(a, p.grid, st);
-  else launch_router_valu<MT, 4>(a, p.grid, st);
+  switch (p.l) {
+    case 1: hipLaunchKernelGGL((router_valu_kernel<MT, 1, 1>), dim3(p.grid), dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((router_valu_kernel<MT, 1, 2>), dim3(p.grid), dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((router_valu_kernel<MT, 1, 4>), dim3(p.grid), dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL((router_valu_kernel<MT, 1, 7>), dim3(p.grid), dim3(256), 0, st, a); break;
+  }
 }
 
 template <int MT>
 void launch_router_mfma(const GemvArgs& a, const Plan& p, hipStream_t st) {
-  if (p.ks == 2) hipLaunchKernelGGL((router_mfma_kernel<MT, 2>), dim3(p.grid), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((router_mfma_kernel<MT, 4>), dim3(p.grid), dim3(256), 0, st, a);
+  switch (p.ks) {
+    case 2: hipLaunchKernelGGL((router_mfma_kernel<MT, 2>), dim3(p.grid), dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((router_mfma_kernel<MT, 4>), dim3(p.grid), dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL((router_mfma_kernel<MT, 8>), dim3(p.grid), dim3(256), 0, st, a); break;
+  }
 }
 
 void launch_router(const GemvArgs& a, const Plan& p, hipStream_t st) {
@@ -259,44 +293,53 @@ int launch_sort_quant(const int32_t* ids, const uint16_t* x, int64_t ldx, int m,
 // ---------------------------------------------------------------------------
 // Fused launch (M <= 64).
 // ---------------------------------------------------------------------------
-size_t fused_lds_bytes(const Plan& p, int m, int n, int topk) {
-  const size_t P = (size_t)m * topk;
-  const size_t sort = sizeof(int) * (3 * P + n + (n + 1));  // s_e, s_rank, s_pos, s_cnt, s_off
+// Small mode when one gather of every row fits the per-thread loads.
+bool fused_small(const Plan& p, int m, int n) { return gather_loads(m, n, p.s) <= kPollLoads; }
+
+size_t fused_lds_bytes(const Plan& p, int m, int n, int topk, bool small) {
+  const int P = m * topk;
+  // s_e, s_rank, s_pos, s_cnt, s_off, then the gathered logits, which the
+  // sort's per-wave counts (4*N) reuse.
+  const size_t tail = sizeof(int) * std::max((size_t)fused_log_offset(P, n) + (size_t)(small ? m : 1) * n,
+                                             (size_t)3 * P + 6 * (size_t)n + 4);
   const size_t tile = p.valu ? 0 : sizeof(float) * 4 * p.mt * 256;
-  return std::max(sort, tile);
+  return std::max(tail, tile);
+}
+
+template <int NV, int MT>
+const void* fused_valu_ptr(int l) {
+  switch (l) {
+    case 1: return (const void*)fused_valu_kernel<NV, MT, 1, 1>;
+    case 2: return (const void*)fused_valu_kernel<NV, MT, 1, 2>;
+    case 4: return (const void*)fused_valu_kernel<NV, MT, 1, 4>;
+    default: return (const void*)fused_valu_kernel<NV, MT, 1, 7>;
+  }
+}
+
+template <int NV, int MT>
+const void* fused_mfma_ptr(int ks) {
+  switch (ks) {
+    case 2: return (const void*)fused_mfma_kernel<NV, MT, 2>;
+    case 4: return (const void*)fused_mfma_kernel<NV, MT, 4>;
+    default: return (const void*)fused_mfma_kernel<NV, MT, 8>;
+  }
 }
 
 template <int NV>
 const void* fused_kernel_ptr(const Plan& p) {
   if (p.valu) {
-    if (p.rpw == 1) {
-      switch (p.mt) {
-        case 1: return (const void*)fused_valu_kernel<NV, 1, 1, 1>;
-        case 2: return (const void*)fused_valu_kernel<NV, 2, 1, 1>;
-        case 4: return (const void*)fused_valu_kernel<NV, 4, 1, 1>;
-        default: return (const void*)fused_valu_kernel<NV, 8, 1, 1>;
-      }
-    }
     switch (p.mt) {
-      case 1: return (const void*)fused_valu_kernel<NV, 1, 4, 1>;
-      case 2: return (const void*)fused_valu_kernel<NV, 2, 4, 1>;
-      case 4: return (const void*)fused_valu_kernel<NV, 4, 4, 1>;
-      default: return (const void*)fused_valu_kernel<NV, 8, 4, 1>;
-    }
-  }
-  if (p.ks == 2) {
-    switch (p.mt) {
-      case 1: return (const void*)fused_mfma_kernel<NV, 1, 2>;
-      case 2: return (const void*)fused_mfma_kernel<NV, 2, 2>;
-      case 3: return (const void*)fused_mfma_kernel<NV, 3, 2>;
-      default: return (const void*)fused_mfma_kernel<NV, 4, 2>;
+      case 1: return fused_valu_ptr<NV, 1>(p.l);
+      case 2: return fused_valu_ptr<NV, 2>(p.l);
+      case 4: return fused_valu_ptr<NV, 4>(p.l);
+      default: return fused_valu_ptr<NV, 8>(p.l);
     }
   }
   switch (p.mt) {
-    case 1: return (const void*)fused_mfma_kernel<NV, 1, 4>;
-    case 2: return (const void*)fused_mfma_kernel<NV, 2, 4>;
-    case 3: return (const void*)fused_mfma_kernel<NV, 3, 4>;
-    default: return (const void*)fused_mfma_kernel<NV, 4, 4>;
+    case 1: return fused_mfma_ptr<NV, 1>(p.ks);
+    case 2: return fused_mfma_ptr<NV, 2>(p.ks);
+    case 3: return fused_mfma_ptr<NV, 3>(p.ks);
+    default: return fused_mfma_ptr<NV, 4>(p.ks);
   }
 }
 
@@ -484,22 +527,27 @@ rgt_status rgt_route_sort_quant(const void* x, int64_t ldx, const void* w, int64
              reinterpret_cast<float*>(base + L.part), reinterpret_cast<u32*>(base + L.ctr), m, n, k, p.s, p.nb};
 
   bool fuse = m <= kFusedMaxM && !env_int("RGT_NO_FUSE", 0);
+  const bool small = fused_small(p, m, n);
+  int upw_log = 8;
   const void* fn = nullptr;
   size_t lds = 0;
   if (fuse) {
     DevInfo di;
     if (!dev_info(di)) return RGT_ERR_HIP;
     fn = fused_kernel_for(p, n);
-    lds = fused_lds_bytes(p, m, n, topk);
+    lds = fused_lds_bytes(p, m, n, topk, small);
     const int units = m * (k / 16);
+    upw_log = 6;
+    while (upw_log < 8 && ((units + (1 << upw_log) - 1) >> upw_log) > p.grid) ++upw_log;
     // Co-residency is required for the device-side waits; each thread owns at
-    // most one quant unit.
-    if (p.grid > coresident_blocks(fn, lds, di.cus) || units > p.grid * 256 || m * topk > kWaveSortMaxP)
+    // most one quant unit; in large mode workgroup r gathers row r.
+    if (p.grid > coresident_blocks(fn, lds, di.cus) || units > (p.grid << upw_log) || m * topk > kSortWg4MaxP ||
+        (!small && (m > p.grid || gather_loads(1, n, p.s) > kPollLoads)))
       fuse = false;
   }
   if (fuse) {
-    FusedArgs a{g, bias, topk, block, logits, topk_ids, topk_w, sorted_ids, expert_ids, offsets, a_q, a_scale,
-                reinterpret_cast<u32*>(base + L.ctl), reinterpret_cast<u64*>(base + L.tlog),
+    FusedArgs a{g, bias, topk, block, small ? 1 : 0, upw_log, logits, topk_ids, topk_w, sorted_ids, expert_ids, offsets,
+                a_q, a_scale, reinterpret_cast<u32*>(base + L.ctl), reinterpret_cast<u64*>(base + L.tpart),
                 reinterpret_cast<u64*>(base + L.tids), wait_budget_ticks(), env_int("RGT_FAULT_INJECT", 0),
 #ifdef RGT_TRACE
                 reinterpret_cast<u64*>(base + L.trace)

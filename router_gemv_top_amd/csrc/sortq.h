@@ -36,6 +36,22 @@ __device__ __forceinline__ u64 match_peers(int e, bool valid, int bits) {
   return peers;
 }
 
+// The same with a compile-time bound on the id bits (ids < 2^BITS): the
+// ballots are unrolled, and bits above the ids' range are skipped at run time.
+template <int BITS>
+__device__ __forceinline__ u64 match_peers_n(int e, bool valid, int bits) {
+  u64 peers = ballot64(valid);
+#pragma unroll
+  for (int b = 0; b < BITS; ++b) {
+    if (b < bits) {
+      const bool bit = (e >> b) & 1;
+      const u64 m = ballot64(bit);
+      peers &= bit ? m : ~m;
+    }
+  }
+  return peers;
+}
+
 __device__ __forceinline__ int ceil_log2(int n) { return n <= 1 ? 0 : 32 - __clz(n - 1); }
 
 // Block sizes are powers of two: round up / divide with masks and shifts (a
@@ -134,6 +150,35 @@ __device__ int wg_sort(const int32_t* ids, int P, int N, int B, int* s_e, int* s
   return total;
 }
 
+// Padded counts -> exclusive segment offsets, by one wave. Lane l owns the C
+// consecutive experts from l*C (C = ceil(N/64) <= CMAX). All CMAX counts are
+// read from clamped addresses with no branch between the reads, so their LDS
+// latencies overlap. Writes s_off[0..N]; returns the padded total.
+template <int CMAX>
+__device__ __forceinline__ int wave_scan_offsets(const int* s_cnt, int* s_off, int N, int B) {
+  const int lane = lane_id();
+  const int C = (N + 63) >> 6;
+  const int e0 = lane * C;
+  int pc[CMAX];
+  int local = 0;
+#pragma unroll
+  for (int i = 0; i < CMAX; ++i) {
+    const int v = s_cnt[min(e0 + i, N - 1)];
+    pc[i] = (i < C && e0 + i < N) ? pad_to(v, B) : 0;
+    local += pc[i];
+  }
+  const int incl = wave_inclusive_scan(local);
+  const int total = (int)readlane_u32((u32)incl, 63);
+  int run = incl - local;
+#pragma unroll
+  for (int i = 0; i < CMAX; ++i) {
+    if (i < C && e0 + i < N) s_off[e0 + i] = run;
+    run += pc[i];
+  }
+  if (lane == 0) s_off[N] = total;
+  return total;
+}
+
 // One-wave sort of up to a few thousand pairs (called by one whole wave, no
 // barriers: LDS accesses of one wave are performed in program order).
 // Batches of 64 pairs are taken in pair order; a lane's stable rank is the
@@ -143,7 +188,7 @@ __device__ int wg_sort(const int32_t* ids, int P, int N, int B, int* s_e, int* s
 // Results: s_cnt, s_off (N+1 entries) and pos[p] (LDS or global), -1 for a
 // pair whose expert id is outside [0, N). Returns the padded total.
 // With ids == nullptr, s_e already holds the experts.
-template <typename PosPtr>
+template <int CMAX, typename PosPtr>
 __device__ int wave_sort(const int32_t* ids, int P, int N, int B, int* s_e, int* s_rank, int* s_cnt, int* s_off,
                          PosPtr pos) {
   const int lane = lane_id();
@@ -173,30 +218,36 @@ __device__ int wave_sort(const int32_t* ids, int P, int N, int B, int* s_e, int*
       if (below == 0ull) s_cnt[e] = c + __popcll(peers);
     }
   }
-  // Padded counts -> exclusive segment offsets. Lane l owns C consecutive
-  // experts (C <= 16); their counts are read once into registers.
-  const int C = (N + 63) / 64;
-  const int e0 = min(N, lane * C), e1 = min(N, e0 + C);
-  int pc[16];
-  int local = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    pc[i] = (i < C && e0 + i < e1) ? pad_to(s_cnt[e0 + i], B) : 0;
-    local += pc[i];
-  }
-  const int incl = wave_inclusive_scan(local);
-  const int total = (int)readlane_u32((u32)incl, 63);
-  int run = incl - local;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    if (i < C && e0 + i < e1) s_off[e0 + i] = run;
-    run += pc[i];
-  }
-  if (lane == 0) s_off[N] = total;
+  const int total = wave_scan_offsets<CMAX>(s_cnt, s_off, N, B);
   for (int p = lane; p < P; p += 64) {
     const int e = s_e[p];
     pos[p] = (unsigned)e < (unsigned)N ? s_off[e] + s_rank[p] : -1;
   }
+  return total;
+}
+
+// One-wave sort of at most 64 pairs (pair p in lane p), no loops: stable ranks
+// from one batch of peer ballots, counts and padded offsets through LDS.
+// s_e[P] holds the experts; results as for wave_sort.
+constexpr int kWaveSortSmallP = 64;
+
+template <int CMAX, typename PosPtr>
+__device__ int wave_sort_small(int P, int N, int B, const int* s_e, int* s_cnt, int* s_off, PosPtr pos) {
+  const int lane = lane_id();
+  const int C = (N + 63) >> 6;
+  const int e0 = lane * C;
+#pragma unroll
+  for (int i = 0; i < CMAX; ++i)
+    if (i < C && e0 + i < N) s_cnt[e0 + i] = 0;
+  const int e = s_e[min(lane, P - 1)];
+  const bool valid = lane < P && (unsigned)e < (unsigned)N;
+  const u64 peers = match_peers_n<6 + (CMAX > 1) + (CMAX > 2) + (CMAX > 4) + (CMAX > 8)>(e, valid, ceil_log2(N));
+  const u64 below = peers & lanemask_lt();
+  const int rank = __popcll(below);
+  if (valid && below == 0ull) s_cnt[e] = __popcll(peers);  // after the zeroing (one wave: LDS in order)
+  const int total = wave_scan_offsets<CMAX>(s_cnt, s_off, N, B);
+  const int o = s_off[valid ? e : 0];
+  if (lane < P) pos[lane] = valid ? o + rank : -1;
   return total;
 }
 
@@ -209,6 +260,124 @@ __device__ __forceinline__ void write_sort_layout(const int* s_cnt, const int* s
     const int a = s_off[e], b = s_off[e + 1];
     for (int q = a + s_cnt[e]; q < b; ++q) sorted_ids[q] = P;
     for (int blk = div_pow2(a, B); blk < div_pow2(b, B); ++blk) expert_ids[blk] = e;
+  }
+}
+
+// Four-wave sort of P <= kSortWg4MaxP pairs held in s_e (LDS), called by the
+// whole 256-thread workgroup. Wave w takes the contiguous chunk of pairs
+// [w*Q, (w+1)*Q) (Q a multiple of 64) in batches of 64: a pair's rank is the
+// running count of its expert in the wave's chunk (s_hist[w][e]) plus its
+// rank among the batch's lanes with the same expert. One wave then turns the
+// per-wave counts into padded segment offsets and per-wave bases, and every
+// pair's position is base + rank. LDS: s_rank[P], s_hist[4*N], s_cnt[N],
+// s_off[N+1]. Results as for wave_sort.
+constexpr int kSortWg4MaxP = 2048;
+
+template <int CMAX, typename PosPtr>
+__device__ int wg4_sort(int P, int N, int B, const int* s_e, int* s_rank, int* s_hist, int* s_cnt, int* s_off,
+                        PosPtr pos) {
+  constexpr int BITS = 6 + (CMAX > 1) + (CMAX > 2) + (CMAX > 4) + (CMAX > 8);
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  for (int i = t; i < 4 * N; i += 256) s_hist[i] = 0;
+  __syncthreads();
+  const int Q = (((P + 3) >> 2) + 63) & ~63;
+  const int c0 = min(P, wave * Q), c1 = min(P, c0 + Q);
+  const int bits = ceil_log2(N);
+  int* run = s_hist + wave * N;
+  for (int base = c0; base < c1; base += 64) {
+    const int p = base + lane;
+    const int e = s_e[min(p, P - 1)];
+    const bool valid = p < c1 && (unsigned)e < (unsigned)N;
+    const u64 peers = match_peers_n<BITS>(e, valid, bits);
+    const u64 below = peers & lanemask_lt();
+    if (valid) {
+      const int c = run[e];
+      s_rank[p] = c + __popcll(below);
+      if (below == 0ull) run[e] = c + __popcll(peers);  // one wave: LDS in order
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // Lane l owns experts [l*C, l*C + C); the 4*C per-wave counts are read
+    // from clamped addresses with no branch between the reads.
+    const int C = (N + 63) >> 6;
+    const int e0 = lane * C;
+    int h[4][CMAX], pc[CMAX];
+    int local = 0;
+#pragma unroll
+    for (int i = 0; i < CMAX; ++i)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) h[w][i] = s_hist[w * N + min(e0 + i, N - 1)];
+#pragma unroll
+    for (int i = 0; i < CMAX; ++i) {
+      const int tot = h[0][i] + h[1][i] + h[2][i] + h[3][i];
+      pc[i] = (i < C && e0 + i < N) ? pad_to(tot, B) : 0;
+      local += pc[i];
+    }
+    const int incl = wave_inclusive_scan(local);
+    const int total = (int)readlane_u32((u32)incl, 63);
+    int off = incl - local;
+#pragma unroll
+    for (int i = 0; i < CMAX; ++i) {
+      if (i < C && e0 + i < N) {
+        const int e = e0 + i;
+        s_off[e] = off;
+        s_cnt[e] = h[0][i] + h[1][i] + h[2][i] + h[3][i];
+        s_hist[e] = off;
+        s_hist[N + e] = off + h[0][i];
+        s_hist[2 * N + e] = off + h[0][i] + h[1][i];
+        s_hist[3 * N + e] = off + h[0][i] + h[1][i] + h[2][i];
+      }
+      off += pc[i];
+    }
+    if (lane == 0) s_off[N] = total;
+  }
+  __syncthreads();
+  for (int p = c0 + lane; p < c1; p += 64) {
+    const int e = s_e[p];
+    pos[p] = (unsigned)e < (unsigned)N ? run[e] + s_rank[p] : -1;
+  }
+  __syncthreads();
+  return s_off[N];
+}
+
+// Sort outputs of a decode-size sort held in LDS (s_e, pos, s_cnt, s_off):
+// offsets; each pair's sorted_ids entry and the expert_ids entry of its block
+// (every block of a segment holds at least one pair, so this covers every
+// block; pairs of one block write the same value); and the sentinel pads,
+// one item (e, j) per slot j < B after expert e's pairs, eight items per
+// thread with their LDS reads issued together.
+// Called by all NT threads of the workgroup.
+template <int NT, typename PosPtr>
+__device__ __forceinline__ void write_sort_outputs(const int* s_e, PosPtr pos, const int* s_cnt, const int* s_off,
+                                                   int N, int B, int P, int32_t* sorted_ids, int32_t* expert_ids,
+                                                   int32_t* offsets) {
+  const int lb = __ffs(B) - 1;
+  const int t = threadIdx.x;
+  for (int e = t; e <= N; e += NT) offsets[e] = s_off[e];
+  for (int p = t; p < P; p += NT) {
+    const int q = pos[p];
+    if (q >= 0) {
+      sorted_ids[q] = p;
+      expert_ids[q >> lb] = s_e[p];
+    }
+  }
+  const int items = N << lb;
+  for (int it0 = 0; it0 < items; it0 += 8 * NT) {
+    int a[8], b[8], c[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = min((it0 + t + u * NT) >> lb, N - 1);
+      a[u] = s_off[e];
+      b[u] = s_off[e + 1];
+      c[u] = s_cnt[e];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int it = it0 + t + u * NT;
+      const int q = a[u] + c[u] + (it & (B - 1));
+      if (it < items && q < b[u]) sorted_ids[q] = P;
+    }
   }
 }
 
@@ -226,7 +395,7 @@ __global__ void __launch_bounds__(256) sort_small_kernel(const int32_t* ids, int
   int* s_off = s_cnt + N;
   int* s_scr = s_off + N + 1;
   if (P <= kWaveSortMaxP) {
-    if (threadIdx.x < 64) wave_sort(ids, P, N, B, s_e, s_hist, s_cnt, s_off, pos_ws);
+    if (threadIdx.x < 64) wave_sort<16>(ids, P, N, B, s_e, s_hist, s_cnt, s_off, pos_ws);
     vm_drain();
     __syncthreads();
   } else {
@@ -331,9 +500,7 @@ __global__ void __launch_bounds__(256) sort_scatter_kernel(const int32_t* ids, i
 // codes packed little-endian in a uint4 and the block's scale byte.
 // Must be called by both lanes of a pair.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint4 mx_quant16(const uint16_t* src, u32& scale_byte) {
-  const uint4 a = *reinterpret_cast<const uint4*>(src);
-  const uint4 b = *reinterpret_cast<const uint4*>(src + 8);
+__device__ __forceinline__ uint4 mx_quant16_regs(const uint4& a, const uint4& b, u32& scale_byte) {
   const u32 w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   u32 amax = 0;
 #pragma unroll
@@ -346,14 +513,12 @@ __device__ __forceinline__ uint4 mx_quant16(const uint16_t* src, u32& scale_byte
   amax = other > amax ? other : amax;
   const int se = mx_shared_exp(amax);
   scale_byte = (u32)(se + 127);
-  u32 c[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const u32 w0 = w[2 * q], w1 = w[2 * q + 1];
-    c[q] = e4m3_of_bf16(w0 & 0xffffu, se) | (e4m3_of_bf16(w0 >> 16, se) << 8) |
-           (e4m3_of_bf16(w1 & 0xffffu, se) << 16) | (e4m3_of_bf16(w1 >> 16, se) << 24);
-  }
-  return make_uint4(c[0], c[1], c[2], c[3]);
+  return make_uint4(e4m3x4_of_bf16(w[0], w[1], se), e4m3x4_of_bf16(w[2], w[3], se), e4m3x4_of_bf16(w[4], w[5], se),
+                    e4m3x4_of_bf16(w[6], w[7], se));
+}
+
+__device__ __forceinline__ uint4 mx_quant16(const uint16_t* src, u32& scale_byte) {
+  return mx_quant16_regs(*reinterpret_cast<const uint4*>(src), *reinterpret_cast<const uint4*>(src + 8), scale_byte);
 }
 
 // Units (16-element chunks) are numbered row-major, one per lane, so lanes
@@ -367,19 +532,33 @@ __device__ __forceinline__ u32 pack_scales(u32 sb) {
 }
 
 // Store unit u's 16 codes to the padded rows pos[t*k + j] of its token's pairs;
-// lanes with u % 8 == 0 also store the packed scales of their 4 blocks.
-template <typename PosPtr>
-__device__ __forceinline__ void store_unit(uint8_t* a_q, uint8_t* a_scale, int K, int k, int u, PosPtr pos,
-                                           const uint4& codes, u32 scales4) {
+// lanes with u % 8 == 0 also store the packed scales of their 4 blocks. All
+// KMAX >= k positions are read (clamped addresses, no branch between the
+// reads) before the first store, so their latencies overlap.
+template <int KMAX, typename PosPtr>
+__device__ __forceinline__ void store_unit_k(uint8_t* a_q, uint8_t* a_scale, int K, int k, int u, PosPtr pos,
+                                             const uint4& codes, u32 scales4) {
   const int cpr = K >> 4;  // 16-element chunks per row
   const int t = u / cpr, c = u - t * cpr;
   const int64_t kscale = K >> 5;
-  for (int j = 0; j < k; ++j) {
-    const int64_t d = pos[t * k + j];
-    if (d < 0) continue;
-    *reinterpret_cast<uint4*>(a_q + d * K + 16 * c) = codes;
-    if ((c & 7) == 0) *reinterpret_cast<u32*>(a_scale + d * kscale + (c >> 1)) = scales4;
+  int d[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) d[j] = pos[t * k + min(j, k - 1)];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (j < k && d[j] >= 0) {
+      *reinterpret_cast<uint4*>(a_q + (int64_t)d[j] * K + 16 * c) = codes;
+      if ((c & 7) == 0) *reinterpret_cast<u32*>(a_scale + (int64_t)d[j] * kscale + (c >> 1)) = scales4;
+    }
   }
+}
+
+template <typename PosPtr>
+__device__ __forceinline__ void store_unit(uint8_t* a_q, uint8_t* a_scale, int K, int k, int u, PosPtr pos,
+                                           const uint4& codes, u32 scales4) {
+  if (k <= 8) store_unit_k<8>(a_q, a_scale, K, k, u, pos, codes, scales4);
+  else if (k <= 16) store_unit_k<16>(a_q, a_scale, K, k, u, pos, codes, scales4);
+  else store_unit_k<32>(a_q, a_scale, K, k, u, pos, codes, scales4);
 }
 
 __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* x, int64_t ldx, int M, int K, int k,
