@@ -41,9 +41,14 @@ namespace rgt {
 // Control words at the head of the workspace, 128 bytes apart.
 enum : int { kCtlErr = 0, kCtlEpoch = kCtrStride };
 
-// LDS of the tail, in ints: s_e[P], s_rank[P], s_pos[P], s_cnt[N], s_off[N+1],
-// then the gathered logits (16-byte aligned).
-__host__ __device__ constexpr int fused_log_offset(int P, int n) { return (3 * P + 2 * n + 1 + 3) & ~3; }
+// LDS of the tail, in ints: s_e[P], s_rank[P], s_pos[P], s_key[P], s_cnt[N],
+// s_off[N+1], then the gathered logits (16-byte aligned), whose space the
+// sort's per-wave counts (4*N) reuse.
+__host__ __device__ constexpr int fused_log_offset(int P, int n) { return (4 * P + 2 * n + 1 + 3) & ~3; }
+__host__ __device__ constexpr int fused_tail_ints(int P, int n, int rows) {
+  return fused_log_offset(P, n) + rows * n > 4 * P + 6 * n + 4 ? fused_log_offset(P, n) + rows * n
+                                                                 : 4 * P + 6 * n + 4;
+}
 
 struct FusedArgs {
   GemvArgs g;          // g.logits, g.part and g.ctr unused here
@@ -68,23 +73,13 @@ struct FusedArgs {
 };
 
 // The call's tag, read by every wave on its own (no barrier): epoch + 1,
-// skipping 0 so zero-filled words never look ready.
+// skipping 0 so zero-filled words never look ready. It stays a per-lane
+// value (every lane loads the same word): moving it to a scalar register
+// would make the wave wait for this load before issuing the tile's loads.
 __device__ __forceinline__ u32 call_tag(const u32* ctl) {
-  const u32 t = (u32)__builtin_amdgcn_readfirstlane((int)ld_agent(ctl + kCtlEpoch)) + 1u;
+  const u32 t = ld_agent(ctl + kCtlEpoch) + 1u;
   return t ? t : 1u;
 }
-
-// Publisher of a tile's partials as tagged words tpart[s][m][c].
-struct TaggedPartials {
-  u64* tpart;
-  int m, n;
-  u32 tag;
-  int skip;  // host-forced fault: publish nothing, so every reader's wait expires
-  __device__ __forceinline__ void operator()(int s, int row, int col, float v) const {
-    if (skip) return;
-    st_agent(tpart + ((int64_t)s * m + row) * n + col, tag_word(__float_as_uint(v), tag));
-  }
-};
 
 __device__ __forceinline__ void set_timeout(const FusedArgs& a) { or_agent(a.ctl + kCtlErr, kErrTimeout); }
 
@@ -246,15 +241,26 @@ __device__ __forceinline__ bool poll_ids_any(const FusedArgs& a, int P, u32 tag,
   return poll_ids<4>(a, P, tag, s_e);
 }
 
-// One wave runs the gate of one row held in LDS (lane-major loads).
+// One wave selects the top-k of one row held in LDS (lane-major loads).
 template <int NV>
-__device__ __forceinline__ void row_gate(const FusedArgs& a, const float* row_log, int& id, float& w) {
+__device__ __forceinline__ void row_select(const FusedArgs& a, const float* row_log, int& id, u32& key) {
+  __shared__ int s_slot[4][32];
   const int n = a.g.n, c0 = lane_id() * NV;
   float sv[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) sv[i] = row_log[min(c0 + i, n - 1)];
   add_bias<NV>(sv, a.bias, n);
-  wave_topk_regs<NV>(sv, n, a.topk, id, w);
+  wave_select<NV>(sv, n, a.topk, id, key, s_slot[threadIdx.x >> 6]);
+}
+
+// Workgroup 0 of small mode: the weights of rows r0, r0 + step, ... from the
+// selected keys in s_key (one wave per row at a time).
+__device__ __forceinline__ void rows_weights(const FusedArgs& a, const u32* s_key, int r0, int step) {
+  const int k = a.topk, lane = lane_id();
+  for (int row = r0; row < a.g.m; row += step) {
+    const float w = wave_weights(s_key[row * k + min(lane, k - 1)], k);
+    if (lane < k) a.topk_w[row * k + lane] = w;
+  }
 }
 
 template <int NV>
@@ -272,7 +278,8 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
   int* s_e = smem;
   int* s_rank = s_e + P;
   int* s_pos = s_rank + P;
-  int* s_cnt = s_pos + P;
+  u32* s_key = reinterpret_cast<u32*>(s_pos + P);
+  int* s_cnt = s_pos + 2 * P;
   int* s_off = s_cnt + n;
   int* s_hist = s_off + n + 1;  // 4*n, past s_off; reuses the gathered logits' space
   float* s_log = reinterpret_cast<float*>(smem + fused_log_offset(P, n));
@@ -282,16 +289,16 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
     if (!participant) return;
     if (!gather_any(a, 0, m, tag, s_log)) return;
     RGT_STAMP(a.trace, 5);
+    // (The weights only feed topk_w: workgroup 0 computes them off the
+    // sort-and-store path, below.)
     for (int row = wave; row < m; row += 4) {
       int id;
-      float w;
-      row_gate<NV>(a, s_log + row * n, id, w);
+      u32 key;
+      row_select<NV>(a, s_log + row * n, id, key);
       if (lane < k) {
         s_e[row * k + lane] = id;
-        if (blockIdx.x == 0) {
-          a.topk_ids[row * k + lane] = id;
-          a.topk_w[row * k + lane] = w;
-        }
+        s_key[row * k + lane] = key;
+        if (blockIdx.x == 0) a.topk_ids[row * k + lane] = id;
       }
     }
     if (blockIdx.x == 0 && a.logits_out)
@@ -307,13 +314,14 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
       RGT_STAMP(a.trace, 5);
       if (wave == 0) {
         int id;
-        float w;
-        row_gate<NV>(a, s_log, id, w);
+        u32 key;
+        row_select<NV>(a, s_log, id, key);
         if (lane < k) {
           st_agent(a.tids + row * k + lane, tag_word((u32)id, tag));
           a.topk_ids[row * k + lane] = id;
-          a.topk_w[row * k + lane] = w;
         }
+        const float w = wave_weights(key, k);  // after the ids are published
+        if (lane < k) a.topk_w[row * k + lane] = w;
       }
       if (a.logits_out)
         for (int i = threadIdx.x; i < n; i += 256) a.logits_out[(int64_t)row * n + i] = s_log[i];
@@ -328,8 +336,10 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
   if (blockIdx.x == 0 && threadIdx.x == 0) st_agent(a.ctl + kCtlEpoch, tag);
   // Step 3: one wave sorts the pairs in LDS; the workgroup stores its
   // quantised chunk to the padded rows of the token's pairs.
+  const bool wg0_weights = a.small && blockIdx.x == 0;
   if (P <= kWaveSortSmallP) {
     if (threadIdx.x < 64) wave_sort_small<NV>(P, n, a.block, s_e, s_cnt, s_off, s_pos);
+    else if (wg0_weights) rows_weights(a, s_key, wave - 1, 3);  // while wave 0 sorts
     __syncthreads();
   } else {
     wg4_sort<NV>(P, n, a.block, s_e, s_rank, s_hist, s_cnt, s_off, s_pos);
@@ -339,6 +349,7 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
     write_sort_outputs<256>(s_e, s_pos, s_cnt, s_off, n, a.block, P, a.sorted_ids, a.expert_ids, a.offsets);
   const u32 scales4 = pack_scales(sb_in);  // all lanes: DPP reads neighbouring lanes
   if (have_unit) store_unit(a.a_q, a.a_scale, g.k, k, unit, s_pos, codes_in, scales4);
+  if (wg0_weights && P > kWaveSortSmallP) rows_weights(a, s_key, wave, 4);
   RGT_STAMP(a.trace, 9);
 }
 
@@ -352,11 +363,13 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, Tile t
   const bool have_unit = (int)threadIdx.x < (1 << a.upw_log) && unit < units;
   const int tile_id = xcd_tile(blockIdx.x, gridDim.x);
   RGT_STAMP(a.trace, 0);
-  const u32 tag = call_tag(a.ctl);  // issued before the tile's loads
-  // The thread's quant chunk of x is loaded right after the tile's W loads
-  // are issued, and quantised once the tile is done.
+  // Right after the tile's W loads are issued: the call's tag (loads return
+  // in order, so issued earlier it would hold up the tile's arithmetic) and
+  // the thread's quant chunk of x, quantised once the tile is done.
+  u32 tag = 0;
   uint4 xa = make_uint4(0, 0, 0, 0), xb = make_uint4(0, 0, 0, 0);
   auto prefetch = [&]() {
+    tag = call_tag(a.ctl);
     if (have_unit) {
       const int cpr = g.k >> 4, t = unit / cpr, c = unit - t * cpr;
       const u16* src = g.x + (int64_t)t * g.ldx + 16 * c;
@@ -364,7 +377,9 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, Tile t
       xb = ld16(src + 8);
     }
   };
-  tile(tile_id, TaggedPartials{a.tpart, g.m, g.n, tag, a.fault_skip}, prefetch);
+  tile(tile_id, [&](int s, int row, int col, float v) {
+    if (!a.fault_skip) st_agent(a.tpart + ((int64_t)s * g.m + row) * g.n + col, tag_word(__float_as_uint(v), tag));
+  }, prefetch);
   RGT_STAMP(a.trace, 1);
   u32 sb = 0;
   const uint4 codes = mx_quant16_regs(xa, xb, sb);  // all lanes: the scale exchange reads the partner lane
@@ -380,7 +395,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, Tile t
 template <int NV, int MT, int RPW, int L>
 __global__ void __launch_bounds__(256) fused_valu_kernel(FusedArgs a) {
   extern __shared__ int smem[];
-  fused_body<NV>(a, smem, [&](int t, const TaggedPartials& sink, auto&& pre) {
+  fused_body<NV>(a, smem, [&](int t, auto&& sink, auto&& pre) {
     valu_tile<MT, RPW, L>(a.g, t % a.g.nb_count, t / a.g.nb_count, sink, pre);
   });
 }
@@ -388,7 +403,7 @@ __global__ void __launch_bounds__(256) fused_valu_kernel(FusedArgs a) {
 template <int NV, int MT, int KS>
 __global__ void __launch_bounds__(256) fused_mfma_kernel(FusedArgs a) {
   extern __shared__ int smem[];
-  fused_body<NV>(a, smem, [&](int t, const TaggedPartials& sink, auto&& pre) {
+  fused_body<NV>(a, smem, [&](int t, auto&& sink, auto&& pre) {
     const int nb = t % a.g.nb_count;
     const int s = (t / a.g.nb_count) % a.g.s_count;
     const int mb = t / (a.g.nb_count * a.g.s_count);

@@ -44,15 +44,13 @@ __device__ __forceinline__ double slot_sum(double e) {
   return total;
 }
 
-// Top-k of one row of scores held in registers (lane-major, valid below n).
-// Lane j < k ends with the j-th expert in my_id and its renormalised weight
-// in my_w.
+// Exact selection: k rounds; in each, the wave maximum of the lanes' best
+// keys, the lowest lane holding it (ballot, find-first-set) and its slot.
+// The winner clears that key and every lane rescans. Lane j < k ends with the
+// j-th key and expert.
 template <int NV>
-__device__ __forceinline__ void wave_topk_regs(const float (&sv)[NV], int n, int k, int& my_id, float& my_w) {
+__device__ __forceinline__ void select_exact(u32 (&key)[NV], int k, u32& my_key, int& my_id) {
   const int lane = lane_id();
-  u32 key[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) key[i] = lane * NV + i < n ? score_key(sv[i]) : 0u;
   u32 best;
   int bslot;
   auto rescan = [&]() {
@@ -66,8 +64,6 @@ __device__ __forceinline__ void wave_topk_regs(const float (&sv)[NV], int n, int
     }
   };
   rescan();
-  my_id = 0;
-  u32 my_key = 0u;
   for (int j = 0; j < k; ++j) {
     const u32 top = wave_max_u32(best);
     const int wl = (int)__builtin_ctzll(ballot64(best == top));
@@ -81,13 +77,85 @@ __device__ __forceinline__ void wave_topk_regs(const float (&sv)[NV], int n, int
       my_key = top;
     }
   }
-  // Renormalised softmax over the k selected scores, slot 0 the largest.
+}
+
+// Fast selection for two keys per lane. Each lane orders its pair once; a
+// round is then only the wave maximum of the lanes' first keys and a shift in
+// the lane(s) holding it, with the round's key kept in lane j. The experts
+// are found afterwards: an element with key v is selected when v >= the k-th
+// key, and its slot is the number of selected keys above v; it writes its
+// expert to s_slot[slot] (this wave's LDS) for lane slot to read. This needs
+// the k selected keys to be distinct and held by exactly k elements; when
+// they are not (exact ties), true is returned and the caller runs the exact
+// selection instead.
+__device__ __forceinline__ bool select_fast2(const u32 (&key)[2], int k, u32& my_key, int& my_id, int* s_slot) {
+  const int lane = lane_id();
+  const bool sw = key[1] > key[0];
+  u32 b1 = sw ? key[1] : key[0], b2 = sw ? key[0] : key[1];
+  for (int j = 0; j < k; ++j) {
+    const u32 top = wave_max_u32(b1);
+    const bool hit = b1 == top;
+    b1 = hit ? b2 : b1;
+    b2 = hit ? 0u : b2;
+    my_key = lane == j ? top : my_key;
+  }
+  const u32 kth = readlane_u32(my_key, k - 1);
+  // distinct keys: the k kept keys strictly decrease
+  const u32 prev = (u32)__builtin_amdgcn_ds_bpermute(4 * max(lane - 1, 0), (int)my_key);
+  const bool dup = lane >= 1 && lane < k && prev == my_key;
+  const bool sel0 = key[0] >= kth, sel1 = key[1] >= kth;
+  const int nsel = __popcll(ballot64(sel0)) + __popcll(ballot64(sel1));
+  if (__popcll(ballot64(dup)) != 0 || nsel != k) return true;
+  // slot = number of kept keys above the element's key (lanes 0..k-1 hold them)
+  int r0 = 0, r1 = 0;
+  for (int j = 0; j < k; ++j) {
+    const u32 t = readlane_u32(my_key, j);
+    r0 += t > key[0];
+    r1 += t > key[1];
+  }
+  if (sel0) s_slot[r0] = 2 * lane;
+  if (sel1) s_slot[r1] = 2 * lane + 1;
+  my_id = s_slot[min(lane, k - 1)];  // one wave: the LDS writes above land first
+  return false;
+}
+
+// Top-k of one row of scores held in registers (lane-major, valid below n).
+// Lane j < k ends with the j-th expert in my_id and its renormalised weight
+// in my_w.
+// Selection only: lane j < k ends with the j-th expert in my_id and its
+// score key in my_key. s_slot: 32 ints of LDS owned by the calling wave.
+template <int NV>
+__device__ __forceinline__ void wave_select(const float (&sv)[NV], int n, int k, int& my_id, u32& my_key,
+                                            int* s_slot) {
+  const int lane = lane_id();
+  u32 key[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) key[i] = lane * NV + i < n ? score_key(sv[i]) : 0u;
+  my_id = 0;
+  my_key = 0u;
+  bool exact = true;
+  if constexpr (NV == 2) exact = select_fast2(key, k, my_key, my_id, s_slot);
+  if (exact) select_exact<NV>(key, k, my_key, my_id);
+}
+
+// Renormalised softmax over the k selected scores (lane j holds the key of
+// slot j; slot 0 the largest): the weight of lane j < k.
+__device__ __forceinline__ float wave_weights(u32 my_key, int k) {
+  const int lane = lane_id();
   const float my_s = key_score(my_key);
   const double s0 = (double)readlane_f32(my_s, 0);
   double e = 0.0;
   if (lane < k) e = exp64_recipe((double)my_s - s0);
   const double total = k <= 8 ? slot_sum<8>(e) : (k <= 16 ? slot_sum<16>(e) : slot_sum<32>(e));
-  my_w = lane < k ? (float)(e / total) : 0.f;
+  return lane < k ? (float)(e / total) : 0.f;
+}
+
+template <int NV>
+__device__ __forceinline__ void wave_topk_regs(const float (&sv)[NV], int n, int k, int& my_id, float& my_w,
+                                               int* s_slot) {
+  u32 my_key;
+  wave_select<NV>(sv, n, k, my_id, my_key, s_slot);
+  my_w = wave_weights(my_key, k);
 }
 
 // Load a row of logits lane-major (all loads issued before any is used:
@@ -95,7 +163,7 @@ __device__ __forceinline__ void wave_topk_regs(const float (&sv)[NV], int n, int
 // j < k write slot j.
 template <int NV>
 __device__ __forceinline__ void wave_topk_row(const float* logits_row, const float* bias, int n, int k,
-                                              int32_t* ids_out, float* w_out) {
+                                              int32_t* ids_out, float* w_out, int* s_slot) {
   const int c0 = lane_id() * NV;
   float sv[NV];
 #pragma unroll
@@ -103,7 +171,7 @@ __device__ __forceinline__ void wave_topk_row(const float* logits_row, const flo
   add_bias<NV>(sv, bias, n);
   int id;
   float w;
-  wave_topk_regs<NV>(sv, n, k, id, w);
+  wave_topk_regs<NV>(sv, n, k, id, w, s_slot);
   if (lane_id() < k) {
     ids_out[lane_id()] = id;
     w_out[lane_id()] = w;
@@ -113,9 +181,11 @@ __device__ __forceinline__ void wave_topk_row(const float* logits_row, const flo
 template <int NV>
 __global__ void __launch_bounds__(256) topk_gate_kernel(const float* logits, const float* bias, int m, int n, int k,
                                                         int32_t* ids, float* w) {
+  __shared__ int s_slot[4][32];
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= m) return;
-  wave_topk_row<NV>(logits + (int64_t)row * n, bias, n, k, ids + (int64_t)row * k, w + (int64_t)row * k);
+  wave_topk_row<NV>(logits + (int64_t)row * n, bias, n, k, ids + (int64_t)row * k, w + (int64_t)row * k,
+                    s_slot[threadIdx.x >> 6]);
 }
 
 }  // namespace rgt

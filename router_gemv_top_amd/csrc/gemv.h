@@ -55,7 +55,7 @@ struct PartialSink {
 // n-block, over the workgroup's k-slice of 512*L elements. Lane l covers the
 // 8 elements at k = kslice + j*512 + 8*l for j < L.
 // ---------------------------------------------------------------------------
-// pre() runs once the tile's W loads are issued (other loads to overlap).
+// pre() runs once the tile's loads are issued (other loads to overlap).
 struct NoPrefetch {
   __device__ __forceinline__ void operator()() const {}
 };
@@ -70,6 +70,13 @@ __device__ __forceinline__ void valu_tile(const GemvArgs& a, int nb, int s, cons
   for (int r = 0; r < RPW; ++r)
 #pragma unroll
     for (int j = 0; j < L; ++j) wv[r][j] = ld16(a.w + (int64_t)(nrow0 + r) * a.ldw + kb + j * 512);
+  // x rows past M read row M-1 (no branch between the loads, so they are all
+  // in flight together); their sums are never stored.
+  uint4 xv[MT][L];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int j = 0; j < L; ++j) xv[m][j] = ld16(a.x + (int64_t)min(m, a.m - 1) * a.ldx + kb + j * 512);
   pre();
   float acc[RPW][MT];
 #pragma unroll
@@ -77,16 +84,11 @@ __device__ __forceinline__ void valu_tile(const GemvArgs& a, int nb, int s, cons
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[r][m] = 0.f;
 #pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    if (m < a.m) {
+  for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int j = 0; j < L; ++j) {
-        const uint4 xv = ld16(a.x + (int64_t)m * a.ldx + kb + j * 512);
+    for (int j = 0; j < L; ++j)
 #pragma unroll
-        for (int r = 0; r < RPW; ++r) acc[r][m] = dot8_bf16(wv[r][j], xv, acc[r][m]);
-      }
-    }
-  }
+      for (int r = 0; r < RPW; ++r) acc[r][m] = dot8_bf16(wv[r][j], xv[m][j], acc[r][m]);
 #pragma unroll
   for (int r = 0; r < RPW; ++r)
 #pragma unroll
@@ -119,19 +121,27 @@ __device__ __forceinline__ void mfma_tile(const GemvArgs& a, int mb, int nb, int
   uint4 bw[KS];
 #pragma unroll
   for (int j = 0; j < KS; ++j) bw[j] = ld16(a.w + (int64_t)n * a.ldw + krun + 8 * j);
-  pre();
   floatx4_t acc[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   const int row_base = mb * (16 * MT);
+  // x rows past M are loaded from row M-1 (no branch between the loads, so
+  // they are all in flight together) and replaced by zeros.
+  uint4 xv[MT][KS];
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
-    const int m = row_base + t * 16 + r16;
-    const bool ok = m < a.m;
+    const int m = min(row_base + t * 16 + r16, a.m - 1);
+#pragma unroll
+    for (int j = 0; j < KS; ++j) xv[t][j] = ld16(a.x + (int64_t)m * a.ldx + krun + 8 * j);
+  }
+  pre();
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const bool ok = row_base + t * 16 + r16 < a.m;
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
-      uint4 xv = ok ? ld16(a.x + (int64_t)m * a.ldx + krun + 8 * j) : make_uint4(0, 0, 0, 0);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xv),
+      const uint4 v = ok ? xv[t][j] : make_uint4(0, 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, v),
                                                       __builtin_bit_cast(bf16x8_t, bw[j]), acc[t], 0, 0, 0);
     }
   }

@@ -298,10 +298,7 @@ bool fused_small(const Plan& p, int m, int n) { return gather_loads(m, n, p.s) <
 
 size_t fused_lds_bytes(const Plan& p, int m, int n, int topk, bool small) {
   const int P = m * topk;
-  // s_e, s_rank, s_pos, s_cnt, s_off, then the gathered logits, which the
-  // sort's per-wave counts (4*N) reuse.
-  const size_t tail = sizeof(int) * std::max((size_t)fused_log_offset(P, n) + (size_t)(small ? m : 1) * n,
-                                             (size_t)3 * P + 6 * (size_t)n + 4);
+  const size_t tail = sizeof(int) * (size_t)fused_tail_ints(P, n, small ? m : 1);
   const size_t tile = p.valu ? 0 : sizeof(float) * 4 * p.mt * 256;
   return std::max(tail, tile);
 }
