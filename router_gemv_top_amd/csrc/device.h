@@ -121,6 +121,10 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
 }
 
+// u / d for u * d < 2^32, with magic = ceil(2^32 / d) (d >= 2) from the
+// host: the high word of u * magic (one multiply instead of a division).
+__device__ __forceinline__ int div_magic(int u, u32 magic) { return (int)__umulhi((u32)u, magic); }
+
 // Wave maximum: the row maximum by DPP, then row_bcast:15 carries rows 0 and
 // 2 into rows 1 and 3 and row_bcast:31 carries row 1 into rows 2 and 3, so
 // lane 63 ends with the maximum of all 64 lanes.

@@ -41,14 +41,17 @@ namespace rgt {
 // Control words at the head of the workspace, 128 bytes apart.
 enum : int { kCtlErr = 0, kCtlEpoch = kCtrStride };
 
-// LDS of the tail, in ints: s_e[P], s_rank[P], s_pos[P], s_key[P], s_cnt[N],
-// s_off[N+1], then the gathered logits (16-byte aligned), whose space the
-// sort's per-wave counts (4*N) reuse.
-__host__ __device__ constexpr int fused_log_offset(int P, int n) { return (4 * P + 2 * n + 1 + 3) & ~3; }
-__host__ __device__ constexpr int fused_tail_ints(int P, int n, int rows) {
-  return fused_log_offset(P, n) + rows * n > 4 * P + 6 * n + 4 ? fused_log_offset(P, n) + rows * n
-                                                                 : 4 * P + 6 * n + 4;
-}
+// LDS of the tail, in ints: s_e[P], s_key[P], s_pos[64], s_cnt[N], s_pre[N],
+// s_off[N+1], then the gathered logits (16-byte aligned).
+__host__ __device__ constexpr int fused_log_offset(int P, int n) { return (2 * P + 64 + 3 * n + 1 + 3) & ~3; }
+__host__ __device__ constexpr int fused_tail_ints(int P, int n, int rows) { return fused_log_offset(P, n) + rows * n; }
+
+// Positions of a workgroup's own pairs, indexed by pair number.
+struct OffsetPos {
+  const int* s_pos;
+  int p0;
+  __device__ __forceinline__ int operator[](int p) const { return s_pos[p - p0]; }
+};
 
 struct FusedArgs {
   GemvArgs g;          // g.logits, g.part and g.ctr unused here
@@ -56,6 +59,7 @@ struct FusedArgs {
   int topk, block;
   int small;           // 1: small mode, 0: large mode (chosen by the host)
   int upw_log;         // log2 of the quant units per participating workgroup (6, 7 or 8)
+  u32 cpr_magic;       // ceil(2^32 / (K/16)): token of a quant unit by multiplication
   float* logits_out;   // [M][N] or null
   int32_t* topk_ids;
   float* topk_w;
@@ -83,43 +87,39 @@ __device__ __forceinline__ u32 call_tag(const u32* ctl) {
 
 __device__ __forceinline__ void set_timeout(const FusedArgs& a) { or_agent(a.ctl + kCtlErr, kErrTimeout); }
 
-// 16-byte loads one thread keeps in flight per poll (two polls in flight).
+// 16-byte loads one thread keeps in flight per poll.
 constexpr int kPollLoads = 16;
 
 // The workgroup gathers rows [r0, r0 + rows) of the logits from the tagged
 // partials into s_log[(row - r0) * n + col]. An item is one column pair of
-// one row (one 16-byte load per k-slice); thread t takes items t, t + 256,
-// ... and their S slices, nl <= NL loads in all (a thread with fewer items
-// repeats its last one). Each thread polls its own loads until every word
-// carries the tag, then sums each item's slices in k-slice order. Returns
-// false (error word set) if the deadline passes.
+// one row: item it of the gathered rows sits at byte 16*it of every k-slice
+// and lands at s_log[2*it]. Thread t takes items t, t + 256, ... and their S
+// slices, nl <= NL loads in all (a thread with fewer items repeats its last
+// one). Each thread polls its own loads until every word carries the tag (two
+// polls in flight, so a hand-off is seen about one memory round trip after it
+// lands), then sums each item's slices in k-slice order. Returns false (error
+// word set) if the deadline passes.
 template <int NL>
 __device__ __forceinline__ bool gather_logits(const FusedArgs& a, int r0, int rows, u32 tag, float* s_log) {
   __shared__ u32 s_bad;
   const int n = a.g.n, S = a.g.s_count;
-  const int pairs = n >> 1, items = rows * pairs;
+  const int items = rows * (n >> 1);
   const u32 slice = (u32)a.g.m * (u32)n * 8u;
+  const u32 row_base = (u32)r0 * (u32)n * 8u;
   const int t = threadIdx.x;
   if (t == 0) s_bad = 0u;
   __syncthreads();
   if (t < items) {
     const auto rsrc = coherent_rsrc(a.tpart, slice * (u32)S);
-    const u32 row_base = (u32)r0 * (u32)n * 8u;
-    auto item_off = [&](int it) {
-      const int rr = it / pairs;
-      return row_base + ((u32)rr * (u32)n + 2u * (u32)(it - rr * pairs)) * 8u;
-    };
     u32 off[NL];
     {
       int it = t, s = 0;
-      u32 base = item_off(it);
 #pragma unroll
       for (int l = 0; l < NL; ++l) {
-        off[l] = base + (u32)s * slice;
+        off[l] = row_base + 16u * (u32)it + (u32)s * slice;
         if (++s == S) {
           s = 0;
-          it += 256;
-          if (it < items) base = item_off(it);
+          if (it + 256 < items) it += 256;
         }
       }
     }
@@ -141,10 +141,7 @@ __device__ __forceinline__ bool gather_logits(const FusedArgs& a, int r0, int ro
         acc.x += __uint_as_float(v[l].x);
         acc.y += __uint_as_float(v[l].z);
         if (++s == S) {
-          if (it < items) {
-            const u32 d = ((off[l] - (u32)(S - 1) * slice - row_base) >> 3);
-            *reinterpret_cast<float2*>(s_log + d) = acc;
-          }
+          if (it < items) *reinterpret_cast<float2*>(s_log + 2 * it) = acc;
           acc = make_float2(0.f, 0.f);
           s = 0;
           it += 256;
@@ -155,7 +152,13 @@ __device__ __forceinline__ bool gather_logits(const FusedArgs& a, int r0, int ro
     u32x4_t va[NL], vb[NL];
     issue(va);
     issue(vb);
+#ifdef RGT_TRACE
+    int polls = 0;
+#endif
     for (;;) {
+#ifdef RGT_TRACE
+      ++polls;
+#endif
       if (ready(va)) { take(va); break; }
       issue(va);
       if (ready(vb)) { take(vb); break; }
@@ -166,6 +169,12 @@ __device__ __forceinline__ bool gather_logits(const FusedArgs& a, int r0, int ro
         break;
       }
     }
+#ifdef RGT_TRACE
+    if (t == 0 && a.trace) {  // poll rounds and the gather's start time
+      a.trace[blockIdx.x * 16 + 10] = (u64)polls;
+      a.trace[blockIdx.x * 16 + 11] = t0;
+    }
+#endif
   }
   __syncthreads();
   return s_bad == 0u;
@@ -185,7 +194,8 @@ __device__ __forceinline__ bool gather_any(const FusedArgs& a, int r0, int rows,
 // t takes word pairs t, t + 256, ...) until every word carries the tag, then
 // leaves the experts in s_e.
 template <int NL>
-__device__ __forceinline__ bool poll_ids(const FusedArgs& a, int P, u32 tag, int* s_e) {
+__device__ __forceinline__ bool poll_ids(const FusedArgs& a, int P, u32 tag, int* s_e, int p0, int* s_cnt,
+                                         int* s_pre) {
   __shared__ u32 s_bad;
   const int t = threadIdx.x;
   const int pairs = (P + 1) >> 1;
@@ -210,7 +220,11 @@ __device__ __forceinline__ bool poll_ids(const FusedArgs& a, int P, u32 tag, int
         const int q = t + 256 * l;
         if (q < pairs) {
           s_e[2 * q] = (int)v[l].x;
-          if (2 * q + 1 < P) s_e[2 * q + 1] = (int)v[l].z;
+          hist_add((int)v[l].x, 2 * q, p0, a.g.n, s_cnt, s_pre);
+          if (2 * q + 1 < P) {
+            s_e[2 * q + 1] = (int)v[l].z;
+            hist_add((int)v[l].z, 2 * q + 1, p0, a.g.n, s_cnt, s_pre);
+          }
         }
       }
     };
@@ -234,23 +248,27 @@ __device__ __forceinline__ bool poll_ids(const FusedArgs& a, int P, u32 tag, int
   return s_bad == 0u;
 }
 
-__device__ __forceinline__ bool poll_ids_any(const FusedArgs& a, int P, u32 tag, int* s_e) {
-  const int nl = (P + 511) / 512;
-  if (nl <= 1) return poll_ids<1>(a, P, tag, s_e);
-  if (nl <= 2) return poll_ids<2>(a, P, tag, s_e);
-  return poll_ids<4>(a, P, tag, s_e);
+__device__ __forceinline__ bool poll_ids_any(const FusedArgs& a, int P, u32 tag, int* s_e, int p0, int* s_cnt,
+                                             int* s_pre) {
+  if (P <= 512) return poll_ids<1>(a, P, tag, s_e, p0, s_cnt, s_pre);
+  return poll_ids<4>(a, P, tag, s_e, p0, s_cnt, s_pre);
 }
 
-// One wave selects the top-k of one row held in LDS (lane-major loads).
-template <int NV>
-__device__ __forceinline__ void row_select(const FusedArgs& a, const float* row_log, int& id, u32& key) {
-  __shared__ int s_slot[4][32];
+// One wave selects the top-k of R rows held in LDS (lane-major loads);
+// rows[r] is the row's logits.
+template <int NV, int R>
+__device__ __forceinline__ void row_select(const FusedArgs& a, const float* const (&rows)[R], int (&id)[R],
+                                           u32 (&key)[R]) {
+  __shared__ int s_slot[4][32 * R];
   const int n = a.g.n, c0 = lane_id() * NV;
-  float sv[NV];
+  float sv[R][NV];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) sv[i] = row_log[min(c0 + i, n - 1)];
-  add_bias<NV>(sv, a.bias, n);
-  wave_select<NV>(sv, n, a.topk, id, key, s_slot[threadIdx.x >> 6]);
+  for (int r = 0; r < R; ++r) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) sv[r][i] = rows[r][min(c0 + i, n - 1)];
+    add_bias<NV>(sv[r], a.bias, n);
+  }
+  wave_select_rows<NV, R>(sv, n, a.topk, id, key, s_slot[threadIdx.x >> 6]);
 }
 
 // Workgroup 0 of small mode: the weights of rows r0, r0 + step, ... from the
@@ -276,13 +294,24 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
   const bool participant = blockIdx.x == 0 || ((int)blockIdx.x << a.upw_log) < units || (int)blockIdx.x == layout_wg;
   const int P = m * k;
   int* s_e = smem;
-  int* s_rank = s_e + P;
-  int* s_pos = s_rank + P;
-  u32* s_key = reinterpret_cast<u32*>(s_pos + P);
-  int* s_cnt = s_pos + 2 * P;
-  int* s_off = s_cnt + n;
-  int* s_hist = s_off + n + 1;  // 4*n, past s_off; reuses the gathered logits' space
+  u32* s_key = reinterpret_cast<u32*>(s_e + P);
+  int* s_pos = s_e + 2 * P;   // 64 entries
+  int* s_cnt = s_pos + 64;
+  int* s_pre = s_cnt + n;
+  int* s_off = s_pre + n;
   float* s_log = reinterpret_cast<float*>(smem + fused_log_offset(P, n));
+  // This workgroup's tokens (those its quant units touch) and their pairs.
+  const int cpr = g.k >> 4;
+  const int u0 = (int)blockIdx.x << a.upw_log;
+  const int t0 = min(m, div_magic(u0, a.cpr_magic)), t1 = min(m, div_magic(u0 + (1 << a.upw_log) - 1, a.cpr_magic) + 1);
+  const int p0 = u0 < units ? t0 * k : 0, p1 = u0 < units ? t1 * k : 0;
+  // The expert histograms are filled as the ids become known (zeroed here;
+  // the barriers of the gather or of the id poll come before any add).
+  if (participant)
+    for (int e = threadIdx.x; e < n; e += 256) {
+      s_cnt[e] = 0;
+      s_pre[e] = 0;
+    }
   if (a.small) {
     // Step 2 (small): each participant gathers every row and runs every gate;
     // wave w takes rows w, w + 4, ...
@@ -291,15 +320,20 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
     RGT_STAMP(a.trace, 5);
     // (The weights only feed topk_w: workgroup 0 computes them off the
     // sort-and-store path, below.)
-    for (int row = wave; row < m; row += 4) {
-      int id;
-      u32 key;
-      row_select<NV>(a, s_log + row * n, id, key);
+    auto keep = [&](int row, int id, u32 key) {
       if (lane < k) {
         s_e[row * k + lane] = id;
         s_key[row * k + lane] = key;
+        hist_add(id, row * k + lane, p0, n, s_cnt, s_pre);
         if (blockIdx.x == 0) a.topk_ids[row * k + lane] = id;
       }
+    };
+    for (int row = wave; row < m; row += 4) {
+      const float* rows[1] = {s_log + row * n};
+      int id[1];
+      u32 key[1];
+      row_select<NV, 1>(a, rows, id, key);
+      keep(row, id[0], key[0]);
     }
     if (blockIdx.x == 0 && a.logits_out)
       for (int i = threadIdx.x; i < m * n; i += 256) a.logits_out[i] = s_log[i];
@@ -313,9 +347,12 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
       if (!gather_any(a, row, 1, tag, s_log)) return;
       RGT_STAMP(a.trace, 5);
       if (wave == 0) {
-        int id;
-        u32 key;
-        row_select<NV>(a, s_log, id, key);
+        const float* rows[1] = {s_log};
+        int ids[1];
+        u32 keys[1];
+        row_select<NV, 1>(a, rows, ids, keys);
+        const int id = ids[0];
+        const u32 key = keys[0];
         if (lane < k) {
           st_agent(a.tids + row * k + lane, tag_word((u32)id, tag));
           a.topk_ids[row * k + lane] = id;
@@ -328,28 +365,29 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
       RGT_STAMP(a.trace, 6);
     }
     if (!participant) return;
-    if (!poll_ids_any(a, P, tag, s_e)) return;
+    if (!poll_ids_any(a, P, tag, s_e, p0, s_cnt, s_pre)) return;
   }
   RGT_STAMP(a.trace, 7);
   // Every wave of the grid has read the epoch (see the top of this file):
   // advance it for the next call.
   if (blockIdx.x == 0 && threadIdx.x == 0) st_agent(a.ctl + kCtlEpoch, tag);
-  // Step 3: one wave sorts the pairs in LDS; the workgroup stores its
-  // quantised chunk to the padded rows of the token's pairs.
-  const bool wg0_weights = a.small && blockIdx.x == 0;
-  if (P <= kWaveSortSmallP) {
-    if (threadIdx.x < 64) wave_sort_small<NV>(P, n, a.block, s_e, s_cnt, s_off, s_pos);
-    else if (wg0_weights) rows_weights(a, s_key, wave - 1, 3);  // while wave 0 sorts
-    __syncthreads();
-  } else {
-    wg4_sort<NV>(P, n, a.block, s_e, s_rank, s_hist, s_cnt, s_off, s_pos);
-  }
+  // Step 3: positions of the pairs of this workgroup's tokens (a counting
+  // sort from the expert histogram), then the workgroup stores its quantised
+  // chunk to the padded rows of those pairs. The token's pairs' sorted_ids
+  // entries are written by the workgroup holding its first quant unit; the
+  // layout workgroup writes offsets, expert_ids and the pads.
+  if (threadIdx.x < 64) pair_positions<NV>(P, n, a.block, p0, p1, s_e, s_cnt, s_pre, s_off, s_pos);
+  else if (a.small && blockIdx.x == 0) rows_weights(a, s_key, wave - 1, 3);  // while wave 0 works
+  __syncthreads();
   RGT_STAMP(a.trace, 8);
-  if ((int)blockIdx.x == layout_wg)
-    write_sort_outputs<256>(s_e, s_pos, s_cnt, s_off, n, a.block, P, a.sorted_ids, a.expert_ids, a.offsets);
+  if ((int)blockIdx.x == layout_wg) write_layout<256>(s_cnt, s_off, n, a.block, P, a.sorted_ids, a.expert_ids, a.offsets);
+  if ((int)threadIdx.x < p1 - p0) {
+    const int p = p0 + threadIdx.x, q = s_pos[threadIdx.x];
+    const int tok = p / k;
+    if (q >= 0 && (tok * cpr) >> a.upw_log == (int)blockIdx.x) a.sorted_ids[q] = p;
+  }
   const u32 scales4 = pack_scales(sb_in);  // all lanes: DPP reads neighbouring lanes
-  if (have_unit) store_unit(a.a_q, a.a_scale, g.k, k, unit, s_pos, codes_in, scales4);
-  if (wg0_weights && P > kWaveSortSmallP) rows_weights(a, s_key, wave, 4);
+  if (have_unit) store_unit(a.a_q, a.a_scale, g.k, k, unit, OffsetPos{s_pos, p0}, codes_in, scales4, a.cpr_magic);
   RGT_STAMP(a.trace, 9);
 }
 
@@ -371,7 +409,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, Tile t
   auto prefetch = [&]() {
     tag = call_tag(a.ctl);
     if (have_unit) {
-      const int cpr = g.k >> 4, t = unit / cpr, c = unit - t * cpr;
+      const int cpr = g.k >> 4, t = div_magic(unit, a.cpr_magic), c = unit - t * cpr;
       const u16* src = g.x + (int64_t)t * g.ldx + 16 * c;
       xa = ld16(src);
       xb = ld16(src + 8);

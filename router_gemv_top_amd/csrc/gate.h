@@ -88,35 +88,77 @@ __device__ __forceinline__ void select_exact(u32 (&key)[NV], int k, u32& my_key,
 // the k selected keys to be distinct and held by exactly k elements; when
 // they are not (exact ties), true is returned and the caller runs the exact
 // selection instead.
-__device__ __forceinline__ bool select_fast2(const u32 (&key)[2], int k, u32& my_key, int& my_id, int* s_slot) {
+template <int R>
+__device__ __forceinline__ void select_fast2(const u32 (&key)[R][2], int k, u32 (&my_key)[R], int (&my_id)[R],
+                                             bool (&retry)[R], int* s_slot) {
   const int lane = lane_id();
-  const bool sw = key[1] > key[0];
-  u32 b1 = sw ? key[1] : key[0], b2 = sw ? key[0] : key[1];
-  for (int j = 0; j < k; ++j) {
-    const u32 top = wave_max_u32(b1);
-    const bool hit = b1 == top;
-    b1 = hit ? b2 : b1;
-    b2 = hit ? 0u : b2;
-    my_key = lane == j ? top : my_key;
+  u32 b1[R], b2[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const bool sw = key[r][1] > key[r][0];
+    b1[r] = sw ? key[r][1] : key[r][0];
+    b2[r] = sw ? key[r][0] : key[r][1];
   }
-  const u32 kth = readlane_u32(my_key, k - 1);
-  // distinct keys: the k kept keys strictly decrease
-  const u32 prev = (u32)__builtin_amdgcn_ds_bpermute(4 * max(lane - 1, 0), (int)my_key);
-  const bool dup = lane >= 1 && lane < k && prev == my_key;
-  const bool sel0 = key[0] >= kth, sel1 = key[1] >= kth;
-  const int nsel = __popcll(ballot64(sel0)) + __popcll(ballot64(sel1));
-  if (__popcll(ballot64(dup)) != 0 || nsel != k) return true;
-  // slot = number of kept keys above the element's key (lanes 0..k-1 hold them)
-  int r0 = 0, r1 = 0;
+  // R independent rows advance together, so their reductions interleave.
   for (int j = 0; j < k; ++j) {
-    const u32 t = readlane_u32(my_key, j);
-    r0 += t > key[0];
-    r1 += t > key[1];
+    u32 top[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) top[r] = wave_max_u32(b1[r]);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const bool hit = b1[r] == top[r];
+      b1[r] = hit ? b2[r] : b1[r];
+      b2[r] = hit ? 0u : b2[r];
+      my_key[r] = lane == j ? top[r] : my_key[r];
+    }
   }
-  if (sel0) s_slot[r0] = 2 * lane;
-  if (sel1) s_slot[r1] = 2 * lane + 1;
-  my_id = s_slot[min(lane, k - 1)];  // one wave: the LDS writes above land first
-  return false;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const u32 kth = readlane_u32(my_key[r], k - 1);
+    // distinct keys: the k kept keys strictly decrease
+    const u32 prev = (u32)__builtin_amdgcn_ds_bpermute(4 * max(lane - 1, 0), (int)my_key[r]);
+    const bool dup = lane >= 1 && lane < k && prev == my_key[r];
+    const bool sel0 = key[r][0] >= kth, sel1 = key[r][1] >= kth;
+    const int nsel = __popcll(ballot64(sel0)) + __popcll(ballot64(sel1));
+    retry[r] = __popcll(ballot64(dup)) != 0 || nsel != k;
+    if (retry[r]) continue;
+    // slot = number of kept keys above the element's key (lanes 0..k-1 hold them)
+    int r0 = 0, r1 = 0;
+    for (int j = 0; j < k; ++j) {
+      const u32 t = readlane_u32(my_key[r], j);
+      r0 += t > key[r][0];
+      r1 += t > key[r][1];
+    }
+    int* slot = s_slot + 32 * r;
+    if (sel0) slot[r0] = 2 * lane;
+    if (sel1) slot[r1] = 2 * lane + 1;
+    my_id[r] = slot[min(lane, k - 1)];  // one wave: the LDS writes above land first
+  }
+}
+
+// Selection only for R rows at once (R = 1 or 2): lane j < k ends with the
+// j-th expert of row r in my_id[r] and its score key in my_key[r]. s_slot:
+// 32*R ints of LDS owned by the calling wave.
+template <int NV, int R>
+__device__ __forceinline__ void wave_select_rows(const float (&sv)[R][NV], int n, int k, int (&my_id)[R],
+                                                 u32 (&my_key)[R], int* s_slot) {
+  const int lane = lane_id();
+  u32 key[R][NV];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int i = 0; i < NV; ++i) key[r][i] = lane * NV + i < n ? score_key(sv[r][i]) : 0u;
+  bool retry[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    my_id[r] = 0;
+    my_key[r] = 0u;
+    retry[r] = true;
+  }
+  if constexpr (NV == 2) select_fast2<R>(key, k, my_key, my_id, retry, s_slot);
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (retry[r]) select_exact<NV>(key[r], k, my_key[r], my_id[r]);
 }
 
 // Top-k of one row of scores held in registers (lane-major, valid below n).
@@ -127,15 +169,14 @@ __device__ __forceinline__ bool select_fast2(const u32 (&key)[2], int k, u32& my
 template <int NV>
 __device__ __forceinline__ void wave_select(const float (&sv)[NV], int n, int k, int& my_id, u32& my_key,
                                             int* s_slot) {
-  const int lane = lane_id();
-  u32 key[NV];
+  float sv1[1][NV];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) key[i] = lane * NV + i < n ? score_key(sv[i]) : 0u;
-  my_id = 0;
-  my_key = 0u;
-  bool exact = true;
-  if constexpr (NV == 2) exact = select_fast2(key, k, my_key, my_id, s_slot);
-  if (exact) select_exact<NV>(key, k, my_key, my_id);
+  for (int i = 0; i < NV; ++i) sv1[0][i] = sv[i];
+  int id[1];
+  u32 key[1];
+  wave_select_rows<NV, 1>(sv1, n, k, id, key, s_slot);
+  my_id = id[0];
+  my_key = key[0];
 }
 
 // Renormalised softmax over the k selected scores (lane j holds the key of

@@ -298,7 +298,8 @@ bool fused_small(const Plan& p, int m, int n) { return gather_loads(m, n, p.s) <
 
 size_t fused_lds_bytes(const Plan& p, int m, int n, int topk, bool small) {
   const int P = m * topk;
-  const size_t tail = sizeof(int) * (size_t)fused_tail_ints(P, n, small ? m : 1);
+  const int rows = small ? m : 1;
+  const size_t tail = sizeof(int) * (size_t)fused_tail_ints(P, n, rows);
   const size_t tile = p.valu ? 0 : sizeof(float) * 4 * p.mt * 256;
   return std::max(tail, tile);
 }
@@ -536,14 +537,20 @@ rgt_status rgt_route_sort_quant(const void* x, int64_t ldx, const void* w, int64
     const int units = m * (k / 16);
     upw_log = 6;
     while (upw_log < 8 && ((units + (1 << upw_log) - 1) >> upw_log) > p.grid) ++upw_log;
+    // A workgroup's quant units cover at most this many tokens; their pairs
+    // must fit one wave.
+    const int cpr = k / 16;
+    const bool pairs_fit = (((1 << upw_log) - 1) / cpr + 2) * topk <= 64 &&
+                           (uint64_t)(p.grid << upw_log) * (uint64_t)cpr < (1ull << 32);  // exact magic division
     // Co-residency is required for the device-side waits; each thread owns at
     // most one quant unit; in large mode workgroup r gathers row r.
-    if (p.grid > coresident_blocks(fn, lds, di.cus) || units > (p.grid << upw_log) || m * topk > kSortWg4MaxP ||
+    if (p.grid > coresident_blocks(fn, lds, di.cus) || units > (p.grid << upw_log) || !pairs_fit ||
         (!small && (m > p.grid || gather_loads(1, n, p.s) > kPollLoads)))
       fuse = false;
   }
   if (fuse) {
-    FusedArgs a{g, bias, topk, block, small ? 1 : 0, upw_log, logits, topk_ids, topk_w, sorted_ids, expert_ids, offsets,
+    const u32 cpr_magic = 0xFFFFFFFFu / (u32)(k / 16) + 1u;  // exact for unit * (K/16) < 2^32
+    FusedArgs a{g, bias, topk, block, small ? 1 : 0, upw_log, cpr_magic, logits, topk_ids, topk_w, sorted_ids, expert_ids, offsets,
                 a_q, a_scale, reinterpret_cast<u32*>(base + L.ctl), reinterpret_cast<u64*>(base + L.tpart),
                 reinterpret_cast<u64*>(base + L.tids), wait_budget_ticks(), env_int("RGT_FAULT_INJECT", 0),
 #ifdef RGT_TRACE

@@ -341,6 +341,75 @@ __device__ int wg4_sort(int P, int N, int B, const int* s_e, int* s_rank, int* s
   return s_off[N];
 }
 
+// Counting sort of the pairs by expert, from histograms alone (no full
+// stable sort): with cnt[e] the number of pairs of expert e,
+//   off[e] = sum over e' < e of roundup(cnt[e'], B),
+//   pos(p) = off[e_p] + #{p' < p : e_p' = e_p}.
+// A workgroup needs the positions of its own pairs [p0, p1) only; the pairs
+// before p0 are counted by a second histogram pre[e] over p' < p0, and the
+// earlier own pairs by peer ballots.
+//
+// hist_add: called once per pair as its expert becomes known (LDS atomics
+// into s_cnt and s_pre, zeroed beforehand).
+__device__ __forceinline__ void hist_add(int e, int p, int p0, int N, int* s_cnt, int* s_pre) {
+  if ((unsigned)e < (unsigned)N) {
+    atomicAdd(&s_cnt[e], 1);
+    if (p < p0) atomicAdd(&s_pre[e], 1);
+  }
+}
+
+// pair_positions: one wave, after the histograms are complete (a barrier
+// after the last hist_add). Writes s_off[0..N] and s_pos[p - p0] for the own
+// pairs (p1 - p0 <= 64; -1 for an expert id outside [0, N)).
+template <int CMAX>
+__device__ __forceinline__ void pair_positions(int P, int N, int B, int p0, int p1, const int* s_e, const int* s_cnt,
+                                               const int* s_pre, int* s_off, int* s_pos) {
+  constexpr int BITS = 6 + (CMAX > 1) + (CMAX > 2) + (CMAX > 4) + (CMAX > 8);
+  const int lane = lane_id();
+  const int p = p0 + lane;
+  const int e = s_e[min(p, P - 1)];
+  wave_scan_offsets<CMAX>(s_cnt, s_off, N, B);
+  const bool valid = p < p1 && (unsigned)e < (unsigned)N;
+  const u64 peers = match_peers_n<BITS>(e, valid, ceil_log2(N));
+  const int rank = __popcll(peers & lanemask_lt());
+  const int ee = valid ? e : 0;
+  const int q = s_off[ee] + s_pre[ee] + rank;  // one wave: after the scan's writes
+  if (p < p1) s_pos[lane] = valid ? q : -1;
+}
+
+// Offsets, expert_ids and the sentinel pads of sorted_ids from the histogram
+// and offsets in LDS (the pairs' own entries are written by their owners).
+// Pads: one item (e, j) per slot j < B after expert e's pairs, eight items
+// per thread with their LDS reads issued together. Called by all NT threads.
+template <int NT>
+__device__ __forceinline__ void write_layout(const int* s_cnt, const int* s_off, int N, int B, int P,
+                                             int32_t* sorted_ids, int32_t* expert_ids, int32_t* offsets) {
+  const int lb = __ffs(B) - 1;
+  const int t = threadIdx.x;
+  for (int e = t; e <= N; e += NT) offsets[e] = s_off[e];
+  for (int e = t; e < N; e += NT) {
+    const int b0 = s_off[e] >> lb, b1 = s_off[e + 1] >> lb;
+    for (int blk = b0; blk < b1; ++blk) expert_ids[blk] = e;
+  }
+  const int items = N << lb;
+  for (int it0 = 0; it0 < items; it0 += 8 * NT) {
+    int a[8], b[8], c[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = min((it0 + t + u * NT) >> lb, N - 1);
+      a[u] = s_off[e];
+      b[u] = s_off[e + 1];
+      c[u] = s_cnt[e];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int it = it0 + t + u * NT;
+      const int q = a[u] + c[u] + (it & (B - 1));
+      if (it < items && q < b[u]) sorted_ids[q] = P;
+    }
+  }
+}
+
 // Sort outputs of a decode-size sort held in LDS (s_e, pos, s_cnt, s_off):
 // offsets; each pair's sorted_ids entry and the expert_ids entry of its block
 // (every block of a segment holds at least one pair, so this covers every
@@ -537,9 +606,9 @@ __device__ __forceinline__ u32 pack_scales(u32 sb) {
 // reads) before the first store, so their latencies overlap.
 template <int KMAX, typename PosPtr>
 __device__ __forceinline__ void store_unit_k(uint8_t* a_q, uint8_t* a_scale, int K, int k, int u, PosPtr pos,
-                                             const uint4& codes, u32 scales4) {
+                                             const uint4& codes, u32 scales4, u32 cpr_magic) {
   const int cpr = K >> 4;  // 16-element chunks per row
-  const int t = u / cpr, c = u - t * cpr;
+  const int t = cpr_magic ? div_magic(u, cpr_magic) : u / cpr, c = u - t * cpr;
   const int64_t kscale = K >> 5;
   int d[KMAX];
 #pragma unroll
@@ -553,12 +622,14 @@ __device__ __forceinline__ void store_unit_k(uint8_t* a_q, uint8_t* a_scale, int
   }
 }
 
+// cpr_magic: ceil(2^32 / (K/16)) for a multiply in place of the division of
+// u by the chunks per row, or 0.
 template <typename PosPtr>
 __device__ __forceinline__ void store_unit(uint8_t* a_q, uint8_t* a_scale, int K, int k, int u, PosPtr pos,
-                                           const uint4& codes, u32 scales4) {
-  if (k <= 8) store_unit_k<8>(a_q, a_scale, K, k, u, pos, codes, scales4);
-  else if (k <= 16) store_unit_k<16>(a_q, a_scale, K, k, u, pos, codes, scales4);
-  else store_unit_k<32>(a_q, a_scale, K, k, u, pos, codes, scales4);
+                                           const uint4& codes, u32 scales4, u32 cpr_magic = 0) {
+  if (k <= 8) store_unit_k<8>(a_q, a_scale, K, k, u, pos, codes, scales4, cpr_magic);
+  else if (k <= 16) store_unit_k<16>(a_q, a_scale, K, k, u, pos, codes, scales4, cpr_magic);
+  else store_unit_k<32>(a_q, a_scale, K, k, u, pos, codes, scales4, cpr_magic);
 }
 
 __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* x, int64_t ldx, int M, int K, int k,
