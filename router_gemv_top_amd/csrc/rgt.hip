@@ -190,9 +190,10 @@ bool dev_info(DevInfo& out) {
   return true;
 }
 
+// Read at every call, so a process can change it between calls.
 u64 wait_budget_ticks() {
-  static const long us = env_int("RGT_WAIT_BUDGET_US", 100000);  // 100 ms default
-  return (u64)std::max(1L, us) * 100ull;                            // 100 MHz clock
+  const long us = env_int("RGT_WAIT_BUDGET_US", 100000);  // 100 ms default
+  return (u64)std::max(1L, us) * 100ull;                   // 100 MHz clock
 }
 
 rgt_status launched() {

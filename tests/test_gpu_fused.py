@@ -80,7 +80,11 @@ def sort_out(o):
 
 DECODE = ([workload_tiny()] + workloads_decode_128() + workloads_decode_896() +
           [Workload(f"ragged_M{m}", m, 128, 6144, 8, 16) for m in (3, 13, 33, 50)] +
-          [Workload("b64_M24", 24, 128, 6144, 8, 64), Workload("b32_k4_M16", 16, 128, 6144, 4, 32)])
+          [Workload("b64_M24", 24, 128, 6144, 8, 64), Workload("b32_k4_M16", 16, 128, 6144, 4, 32)] +
+          # coverage edges: smallest N and K with k = 1; largest N with k = 32;
+          # a mid N with two k-slices; MFMA with two k-steps, 32-row tiles and B = 64
+          [Workload("n16_K512_k1_M1", 1, 16, 512, 1, 16), Workload("n1024_K1024_k32_M2", 2, 1024, 1024, 32, 16),
+           Workload("n256_K2048_b32_M5", 5, 256, 2048, 8, 32), Workload("n512_K1024_k16_b64_M40", 40, 512, 1024, 16, 64)])
 
 
 @pytest.mark.parametrize("wl", DECODE, ids=lambda w: w.name)
@@ -173,3 +177,27 @@ def test_route_sort_quant_prefill(R):
     rng = np.random.default_rng(4)
     check_sort_quant(sort_out(fo), ids, x, wl.n, wl.block,
                      sample_rows=lambda nv: rng.choice(nv, size=800, replace=False))
+
+
+def test_fused_wait_deadline_sets_error_and_reset_recovers(R, monkeypatch):
+    """A host-forced fault: the tiles publish nothing, so every device-side
+    wait runs into its (shortened) deadline and exits; the error word
+    reports RGT_ERR_TIMEOUT, and after a reset the same workspace gives
+    correct results again."""
+    say("fused wait deadline (host-forced: nothing published)")
+    wl = Workload("deadline_M4", 4, 128, 6144, 8, 16)
+    x, w, b = wl.make()
+    ws = R.Workspace(wl.m, wl.n, wl.k, wl.topk, wl.block)
+    monkeypatch.setenv("RGT_FAULT_INJECT", "1")
+    monkeypatch.setenv("RGT_WAIT_BUDGET_US", "2000")
+    _, launches = fused(R, x, w, b, wl.topk, wl.block, ws)
+    assert launches == 1
+    assert R.check_workspace(ws) == 5, "expected RGT_ERR_TIMEOUT in the workspace error word"
+    monkeypatch.delenv("RGT_FAULT_INJECT")
+    monkeypatch.delenv("RGT_WAIT_BUDGET_US")
+    R.reset_workspace(ws)
+    f, _ = fused(R, x, w, b, wl.topk, wl.block, ws)
+    assert R.check_workspace(ws) == 0
+    fo = np_out(f)
+    ids = check_against_oracle(x, w, b, wl.topk, wl.block, fo)
+    check_sort_quant(sort_out(fo), ids, x, wl.n, wl.block)
