@@ -107,6 +107,15 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (readlane_f32(v, 0) + readlane_f32(v, 16)) + (readlane_f32(v, 32) + readlane_f32(v, 48));
 }
 
+__device__ __forceinline__ int wave_sum_i32(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, kDppQuadXor1, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppQuadXor2, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppHalfMirror, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppMirror, 0xF, 0xF, false);
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) + __builtin_amdgcn_readlane(v, 32) +
+         __builtin_amdgcn_readlane(v, 48);
+}
+
 // Inclusive prefix sum over the 64 lanes: DPP row_shr steps inside each row
 // of 16 lanes (shifted-in lanes read 0), then the row totals are read as
 // scalars and added to the later rows.

@@ -288,10 +288,12 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
   const int m = g.m, n = g.n, k = a.topk;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int units = m * (g.k >> 4);
-  // The sort outputs are written by the workgroup after the last one with
-  // quant units (if the grid has one), so that they overlap the stores.
-  const int layout_wg = min((int)gridDim.x - 1, ((units - 1) >> a.upw_log) + 1);
-  const bool participant = blockIdx.x == 0 || ((int)blockIdx.x << a.upw_log) < units || (int)blockIdx.x == layout_wg;
+  // Layout workgroups (one per 256 experts, after the last one with quant
+  // units if the grid has room) write offsets, expert_ids and pads.
+  const int n_layout = (n + 255) >> 8;
+  const int layout_wg = min((int)gridDim.x - n_layout, ((units - 1) >> a.upw_log) + 1);
+  const int li = (int)blockIdx.x - layout_wg;  // this workgroup's layout share, if 0 <= li < n_layout
+  const bool participant = blockIdx.x == 0 || ((int)blockIdx.x << a.upw_log) < units || (li >= 0 && li < n_layout);
   const int P = m * k;
   int* s_e = smem;
   u32* s_key = reinterpret_cast<u32*>(s_e + P);
@@ -380,7 +382,9 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
   else if (a.small && blockIdx.x == 0) rows_weights(a, s_key, wave - 1, 3);  // while wave 0 works
   __syncthreads();
   RGT_STAMP(a.trace, 8);
-  if ((int)blockIdx.x == layout_wg) write_layout<256>(s_cnt, s_off, n, a.block, P, a.sorted_ids, a.expert_ids, a.offsets);
+  if (li >= 0 && li < n_layout)
+    write_layout<256>(s_cnt, s_off, n, a.block, P, li << 8, min(n, (li + 1) << 8), a.sorted_ids, a.expert_ids,
+                      a.offsets);
   if ((int)threadIdx.x < p1 - p0) {
     const int p = p0 + threadIdx.x, q = s_pos[threadIdx.x];
     const int tok = p / k;

@@ -136,6 +136,69 @@ __device__ __forceinline__ void select_fast2(const u32 (&key)[R][2], int k, u32 
   }
 }
 
+// Descending sort of NV keys in registers: Batcher's odd-even merge sort
+// (every loop bound is a compile-time constant, so it unrolls into a fixed
+// network of max/min pairs).
+template <int NV>
+__device__ __forceinline__ void sort_desc(u32 (&b)[NV]) {
+#pragma unroll
+  for (int p = 1; p < NV; p <<= 1)
+#pragma unroll
+    for (int k = p; k >= 1; k >>= 1)
+#pragma unroll
+      for (int j = k % p; j + k < NV; j += 2 * k)
+#pragma unroll
+        for (int i = 0; i < k; ++i)
+          if (i + j + k < NV && (i + j) / (2 * p) == (i + j + k) / (2 * p)) {
+            const u32 hi = umax(b[i + j], b[i + j + k]), lo = b[i + j] + b[i + j + k] - hi;
+            b[i + j] = hi;
+            b[i + j + k] = lo;
+          }
+}
+
+// Fast selection for NV > 2 keys per lane: each lane sorts its keys once; a
+// round is the wave maximum of the lanes' first keys and a shift of the list
+// in the lane(s) holding it, which also note their lane in s_slot[j]. Lane
+// j then finds the expert by reading the winner lane's original keys
+// (ds_bpermute) for the one equal to its key. As for two keys, ties make the
+// caller run the exact selection: a round won by two lanes (more shifts than
+// rounds), or equal kept keys.
+template <int NV>
+__device__ __forceinline__ bool select_fast_sorted(const u32 (&key)[NV], int k, u32& my_key, int& my_id,
+                                                   int* s_slot) {
+  const int lane = lane_id();
+  u32 b[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) b[i] = key[i];
+  sort_desc<NV>(b);
+  int hits = 0;
+  for (int j = 0; j < k; ++j) {
+    const u32 top = wave_max_u32(b[0]);
+    const bool hit = b[0] == top;
+    // the shift as bit selects (v_bfi): a conditional select would be turned
+    // into a computed register index
+    const u32 msk = 0u - (u32)hit;
+#pragma unroll
+    for (int i = 0; i + 1 < NV; ++i) b[i] = (b[i + 1] & msk) | (b[i] & ~msk);
+    b[NV - 1] &= ~msk;
+    hits += hit ? 1 : 0;
+    if (hit) s_slot[j] = lane;
+    my_key = lane == j ? top : my_key;
+  }
+  const u32 prev = (u32)__builtin_amdgcn_ds_bpermute(4 * max(lane - 1, 0), (int)my_key);
+  const bool dup = lane >= 1 && lane < k && prev == my_key;
+  if (__popcll(ballot64(dup)) != 0 || wave_sum_i32(hits) != k) return true;
+  const int wl = s_slot[min(lane, k - 1)];  // one wave: the LDS writes above land first
+  int slot = 0;
+#pragma unroll
+  for (int i = NV - 1; i >= 0; --i) {  // the lowest matching slot wins
+    const u32 v = (u32)__builtin_amdgcn_ds_bpermute(4 * wl, (int)key[i]);
+    slot = v == my_key ? i : slot;
+  }
+  my_id = wl * NV + slot;
+  return false;
+}
+
 // Selection only for R rows at once (R = 1 or 2): lane j < k ends with the
 // j-th expert of row r in my_id[r] and its score key in my_key[r]. s_slot:
 // 32*R ints of LDS owned by the calling wave.
@@ -155,7 +218,12 @@ __device__ __forceinline__ void wave_select_rows(const float (&sv)[R][NV], int n
     my_key[r] = 0u;
     retry[r] = true;
   }
-  if constexpr (NV == 2) select_fast2<R>(key, k, my_key, my_id, retry, s_slot);
+  if constexpr (NV == 2) {
+    select_fast2<R>(key, k, my_key, my_id, retry, s_slot);
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r) retry[r] = select_fast_sorted<NV>(key[r], k, my_key[r], my_id[r], s_slot + 32 * r);
+  }
 #pragma unroll
   for (int r = 0; r < R; ++r)
     if (retry[r]) select_exact<NV>(key[r], k, my_key[r], my_id[r]);

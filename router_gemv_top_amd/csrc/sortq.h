@@ -377,26 +377,27 @@ __device__ __forceinline__ void pair_positions(int P, int N, int B, int p0, int 
   if (p < p1) s_pos[lane] = valid ? q : -1;
 }
 
-// Offsets, expert_ids and the sentinel pads of sorted_ids from the histogram
-// and offsets in LDS (the pairs' own entries are written by their owners).
-// Pads: one item (e, j) per slot j < B after expert e's pairs, eight items
-// per thread with their LDS reads issued together. Called by all NT threads.
+// Offsets, expert_ids and the sentinel pads of sorted_ids of experts
+// [e0, e1) from the histogram and offsets in LDS (the pairs' own entries are
+// written by their owners; offsets[N] by the range that ends at N). Pads:
+// one item (e, j) per slot j < B after expert e's pairs, eight items per
+// thread with their LDS reads issued together. Called by all NT threads.
 template <int NT>
-__device__ __forceinline__ void write_layout(const int* s_cnt, const int* s_off, int N, int B, int P,
+__device__ __forceinline__ void write_layout(const int* s_cnt, const int* s_off, int N, int B, int P, int e0, int e1,
                                              int32_t* sorted_ids, int32_t* expert_ids, int32_t* offsets) {
   const int lb = __ffs(B) - 1;
   const int t = threadIdx.x;
-  for (int e = t; e <= N; e += NT) offsets[e] = s_off[e];
-  for (int e = t; e < N; e += NT) {
+  for (int e = e0 + t; e < e1 + (e1 == N ? 1 : 0); e += NT) offsets[e] = s_off[e];
+  for (int e = e0 + t; e < e1; e += NT) {
     const int b0 = s_off[e] >> lb, b1 = s_off[e + 1] >> lb;
     for (int blk = b0; blk < b1; ++blk) expert_ids[blk] = e;
   }
-  const int items = N << lb;
+  const int items = (e1 - e0) << lb;
   for (int it0 = 0; it0 < items; it0 += 8 * NT) {
     int a[8], b[8], c[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int e = min((it0 + t + u * NT) >> lb, N - 1);
+      const int e = e0 + min((it0 + t + u * NT) >> lb, e1 - e0 - 1);
       a[u] = s_off[e];
       b[u] = s_off[e + 1];
       c[u] = s_cnt[e];
