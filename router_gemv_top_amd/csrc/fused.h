@@ -259,7 +259,7 @@ __device__ __forceinline__ bool poll_ids_any(const FusedArgs& a, int P, u32 tag,
 template <int NV, int R>
 __device__ __forceinline__ void row_select(const FusedArgs& a, const float* const (&rows)[R], int (&id)[R],
                                            u32 (&key)[R]) {
-  __shared__ int s_slot[4][32 * R];
+  __shared__ __align__(16) int s_slot[4][64 * R];
   const int n = a.g.n, c0 = lane_id() * NV;
   float sv[R][NV];
 #pragma unroll

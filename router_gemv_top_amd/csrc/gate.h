@@ -122,14 +122,21 @@ __device__ __forceinline__ void select_fast2(const u32 (&key)[R][2], int k, u32 
     const int nsel = __popcll(ballot64(sel0)) + __popcll(ballot64(sel1));
     retry[r] = __popcll(ballot64(dup)) != 0 || nsel != k;
     if (retry[r]) continue;
-    // slot = number of kept keys above the element's key (lanes 0..k-1 hold them)
+    // slot = number of kept keys above the element's key: the kept keys go to
+    // LDS (zeros past k) and every lane reads them back four at a time (one
+    // LDS broadcast per four keys instead of a readlane per key)
+    int* slot = s_slot + 64 * r;
+    u32* s_k = reinterpret_cast<u32*>(slot + 32);
+    if (lane < 32) s_k[lane] = lane < k ? my_key[r] : 0u;
     int r0 = 0, r1 = 0;
-    for (int j = 0; j < k; ++j) {
-      const u32 t = readlane_u32(my_key[r], j);
-      r0 += t > key[r][0];
-      r1 += t > key[r][1];
+#pragma unroll
+    for (int j0 = 0; j0 < 32; j0 += 4) {
+      if (j0 < k) {
+        const uint4 t = *reinterpret_cast<const uint4*>(s_k + j0);
+        r0 += (t.x > key[r][0]) + (t.y > key[r][0]) + (t.z > key[r][0]) + (t.w > key[r][0]);
+        r1 += (t.x > key[r][1]) + (t.y > key[r][1]) + (t.z > key[r][1]) + (t.w > key[r][1]);
+      }
     }
-    int* slot = s_slot + 32 * r;
     if (sel0) slot[r0] = 2 * lane;
     if (sel1) slot[r1] = 2 * lane + 1;
     my_id[r] = slot[min(lane, k - 1)];  // one wave: the LDS writes above land first
@@ -201,7 +208,7 @@ __device__ __forceinline__ bool select_fast_sorted(const u32 (&key)[NV], int k, 
 
 // Selection only for R rows at once (R = 1 or 2): lane j < k ends with the
 // j-th expert of row r in my_id[r] and its score key in my_key[r]. s_slot:
-// 32*R ints of LDS owned by the calling wave.
+// 64*R ints of LDS owned by the calling wave (16-byte aligned).
 template <int NV, int R>
 __device__ __forceinline__ void wave_select_rows(const float (&sv)[R][NV], int n, int k, int (&my_id)[R],
                                                  u32 (&my_key)[R], int* s_slot) {
@@ -222,7 +229,7 @@ __device__ __forceinline__ void wave_select_rows(const float (&sv)[R][NV], int n
     select_fast2<R>(key, k, my_key, my_id, retry, s_slot);
   } else {
 #pragma unroll
-    for (int r = 0; r < R; ++r) retry[r] = select_fast_sorted<NV>(key[r], k, my_key[r], my_id[r], s_slot + 32 * r);
+    for (int r = 0; r < R; ++r) retry[r] = select_fast_sorted<NV>(key[r], k, my_key[r], my_id[r], s_slot + 64 * r);
   }
 #pragma unroll
   for (int r = 0; r < R; ++r)
@@ -233,7 +240,7 @@ __device__ __forceinline__ void wave_select_rows(const float (&sv)[R][NV], int n
 // Lane j < k ends with the j-th expert in my_id and its renormalised weight
 // in my_w.
 // Selection only: lane j < k ends with the j-th expert in my_id and its
-// score key in my_key. s_slot: 32 ints of LDS owned by the calling wave.
+// score key in my_key. s_slot: 64 ints of LDS owned by the calling wave.
 template <int NV>
 __device__ __forceinline__ void wave_select(const float (&sv)[NV], int n, int k, int& my_id, u32& my_key,
                                             int* s_slot) {
@@ -290,7 +297,7 @@ __device__ __forceinline__ void wave_topk_row(const float* logits_row, const flo
 template <int NV>
 __global__ void __launch_bounds__(256) topk_gate_kernel(const float* logits, const float* bias, int m, int n, int k,
                                                         int32_t* ids, float* w) {
-  __shared__ int s_slot[4][32];
+  __shared__ __align__(16) int s_slot[4][64];
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= m) return;
   wave_topk_row<NV>(logits + (int64_t)row * n, bias, n, k, ids + (int64_t)row * k, w + (int64_t)row * k,

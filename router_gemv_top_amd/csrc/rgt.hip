@@ -295,7 +295,9 @@ int launch_sort_quant(const int32_t* ids, const uint16_t* x, int64_t ldx, int m,
 // Fused launch (M <= 64).
 // ---------------------------------------------------------------------------
 // Small mode when one gather of every row fits the per-thread loads.
-bool fused_small(const Plan& p, int m, int n) { return gather_loads(m, n, p.s) <= kPollLoads; }
+// (and while every wave has at most one row's gate to run: beyond that, one
+// more hand-off costs less than a second gate in series).
+bool fused_small(const Plan& p, int m, int n) { return m <= 4 && gather_loads(m, n, p.s) <= kPollLoads; }
 
 size_t fused_lds_bytes(const Plan& p, int m, int n, int topk, bool small) {
   const int P = m * topk;
