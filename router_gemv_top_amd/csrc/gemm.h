@@ -1,0 +1,112 @@
+// gemm.h - router logits for large batches as an LDS-tiled MFMA GEMM.
+//
+// logits[M][N] fp32 = x[M][K] bf16 . W[N][K]^T bf16, the same contraction as
+// the split-K GEMV ("MiniMax-M3: Triton split-K router GEMV with in-kernel
+// split-K fixup", opening summary) at a size where every workgroup already
+// has the whole k range to itself (prefill: thousands of tokens), so there is
+// no split and no fixup: the dense-GEMM regime the configurations name for
+// prefill routing.
+//
+// Workgroup tile 128 rows of x by 128 experts, k-step 64. The next k-step's
+// tiles are loaded into registers while the current one is multiplied from
+// LDS (one LDS buffer, two barriers per step). 4 waves in 2 x 2, each owning
+// 64 x 64 outputs as 4 x 4 v_mfma_f32_16x16x32_bf16 tiles. LDS rows are 64
+// bf16 plus 8 of padding (144 bytes), which spreads the 16 rows one
+// ds_read_b128 touches over disjoint banks.
+#pragma once
+
+#include "device.h"
+
+namespace rgt {
+
+constexpr int kGemmBM = 128, kGemmBN = 128, kGemmBK = 64;
+constexpr int kGemmLds = kGemmBK + 8;  // bf16 per LDS row
+
+// Tiles (row block, expert block) are numbered row-block major, and the
+// XCD-aware map gives each XCD a contiguous run of them, so the x rows a run
+// shares stay in one L2.
+__global__ void __launch_bounds__(256) router_gemm_kernel(const uint16_t* x, int64_t ldx, const uint16_t* w,
+                                                          int64_t ldw, float* logits, int M, int N, int K) {
+  __shared__ __align__(16) uint16_t sA[kGemmBM * kGemmLds];
+  __shared__ __align__(16) uint16_t sB[kGemmBN * kGemmLds];
+  const int nbn = (N + kGemmBN - 1) / kGemmBN;
+  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int m0 = (tile / nbn) * kGemmBM, n0 = (tile % nbn) * kGemmBN;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int r16 = lane & 15, grp = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  // global -> register mapping: thread t moves the 16-byte column chunk t % 8
+  // of rows t / 8 + 32*i (i < 4), for A and for B; rows past M or N read the
+  // last row (never stored). Named registers, not arrays: the values cross
+  // the loop's back edge, and an array there ends up in scratch memory.
+  const int lc = t & 7, lr = t >> 3;
+  const uint16_t* ga0 = x + (int64_t)min(m0 + lr, M - 1) * ldx + 8 * lc;
+  const uint16_t* ga1 = x + (int64_t)min(m0 + lr + 32, M - 1) * ldx + 8 * lc;
+  const uint16_t* ga2 = x + (int64_t)min(m0 + lr + 64, M - 1) * ldx + 8 * lc;
+  const uint16_t* ga3 = x + (int64_t)min(m0 + lr + 96, M - 1) * ldx + 8 * lc;
+  const uint16_t* gb0 = w + (int64_t)min(n0 + lr, N - 1) * ldw + 8 * lc;
+  const uint16_t* gb1 = w + (int64_t)min(n0 + lr + 32, N - 1) * ldw + 8 * lc;
+  const uint16_t* gb2 = w + (int64_t)min(n0 + lr + 64, N - 1) * ldw + 8 * lc;
+  const uint16_t* gb3 = w + (int64_t)min(n0 + lr + 96, N - 1) * ldw + 8 * lc;
+  auto ld = [](const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); };
+  uint4 ra0 = ld(ga0), ra1 = ld(ga1), ra2 = ld(ga2), ra3 = ld(ga3);
+  uint4 rb0 = ld(gb0), rb1 = ld(gb1), rb2 = ld(gb2), rb3 = ld(gb3);
+  floatx4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  uint16_t* la = sA + lr * kGemmLds + 8 * lc;
+  uint16_t* lb = sB + lr * kGemmLds + 8 * lc;
+  for (int k0 = 0; k0 < K; k0 += kGemmBK) {
+    __syncthreads();  // the previous step's LDS reads are done
+    *reinterpret_cast<uint4*>(la) = ra0;
+    *reinterpret_cast<uint4*>(la + 32 * kGemmLds) = ra1;
+    *reinterpret_cast<uint4*>(la + 64 * kGemmLds) = ra2;
+    *reinterpret_cast<uint4*>(la + 96 * kGemmLds) = ra3;
+    *reinterpret_cast<uint4*>(lb) = rb0;
+    *reinterpret_cast<uint4*>(lb + 32 * kGemmLds) = rb1;
+    *reinterpret_cast<uint4*>(lb + 64 * kGemmLds) = rb2;
+    *reinterpret_cast<uint4*>(lb + 96 * kGemmLds) = rb3;
+    __syncthreads();
+    // prefetch the next step (the last step reloads itself: no branch)
+    const int kn = min(k0 + kGemmBK, K - kGemmBK);
+    ra0 = ld(ga0 + kn);
+    ra1 = ld(ga1 + kn);
+    ra2 = ld(ga2 + kn);
+    ra3 = ld(ga3 + kn);
+    rb0 = ld(gb0 + kn);
+    rb1 = ld(gb1 + kn);
+    rb2 = ld(gb2 + kn);
+    rb3 = ld(gb3 + kn);
+#pragma unroll
+    for (int kk = 0; kk < kGemmBK; kk += 32) {
+      uint4 fa[4], fb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        fa[i] = *reinterpret_cast<const uint4*>(sA + (wm * 64 + 16 * i + r16) * kGemmLds + kk + 8 * grp);
+        fb[i] = *reinterpret_cast<const uint4*>(sB + (wn * 64 + 16 * i + r16) * kGemmLds + kk + 8 * grp);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fa[i]),
+                                                             __builtin_bit_cast(bf16x8_t, fb[j]), acc[i][j], 0, 0, 0);
+    }
+  }
+  // D lane l: rows 4*(l/16) + r of the 16 x 16 tile, column l % 16
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + wn * 64 + 16 * j + r16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + wm * 64 + 16 * i + 4 * grp + r;
+        if (row < M && col < N) logits[(int64_t)row * N + col] = acc[i][j][r];
+      }
+    }
+}
+
+}  // namespace rgt

@@ -18,6 +18,7 @@
 #include "diag.h"
 #include "fused.h"
 #include "gate.h"
+#include "gemm.h"
 #include "gemv.h"
 #include "sortq.h"
 
@@ -56,6 +57,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 // GEMV plan for one call.
 // ---------------------------------------------------------------------------
 struct Plan {
+  bool gemm;     // large batches: LDS-tiled MFMA GEMM, no split-K
   bool valu;     // VALU tile (M <= 8) or MFMA tile
   int mt;        // VALU: rows in the template (1,2,4,8); MFMA: 16-row tiles (1..4)
   int rpw;       // VALU rows of W per wave
@@ -84,8 +86,20 @@ int pow2_at_least(int v) {
 #define RGT_MFMA_ROWS_GRID 192
 #endif
 
+// Batches with at least this many 128 x 128 output tiles use the GEMM.
+constexpr int kGemmMinTiles = 256;
+
 Plan make_plan(int m, int n, int k) {
   Plan p{};
+  if (m > kFusedMaxM && ((m + kGemmBM - 1) / kGemmBM) * ((n + kGemmBN - 1) / kGemmBN) >= kGemmMinTiles) {
+    p.gemm = true;
+    p.s = 1;
+    p.mb = (m + kGemmBM - 1) / kGemmBM;
+    p.nb = (n + kGemmBN - 1) / kGemmBN;
+    p.bn = kGemmBN;
+    p.grid = p.mb * p.nb;
+    return p;
+  }
   if (m <= 8) {
     p.valu = true;
     p.mt = pow2_at_least(std::max(m, 1));
@@ -232,6 +246,11 @@ void launch_router_mfma(const GemvArgs& a, const Plan& p, hipStream_t st) {
 }
 
 void launch_router(const GemvArgs& a, const Plan& p, hipStream_t st) {
+  if (p.gemm) {
+    hipLaunchKernelGGL(router_gemm_kernel, dim3(p.grid), dim3(256), 0, st, a.x, a.ldx, a.w, a.ldw, a.logits, a.m,
+                       a.n, a.k);
+    return;
+  }
   if (p.valu) {
     switch (p.mt) {
       case 1: launch_router_valu_rpw<1>(a, p, st); break;

@@ -30,7 +30,9 @@ CASES = ([w for w in workloads_decode_128()] + [w for w in workloads_decode_896(
          [Workload(f"ragged_M{m}", m, 128, 6144, 8, 16) for m in (3, 5, 17, 33, 47, 63)] +
          [Workload(f"ragged896_M{m}", m, 896, 3584, 16, 16) for m in (7, 9, 25)] +
          [w for w in workloads_wide_128()] +
-         [Workload("n16_k512_M3", 3, 16, 512, 4, 16), Workload("n1024_k1024_M40", 40, 1024, 1024, 32, 16)])
+         [Workload("n16_k512_M3", 3, 16, 512, 4, 16), Workload("n1024_k1024_M40", 40, 1024, 1024, 32, 16)] +
+         # the tiled GEMM of large batches, with ragged row and expert tiles
+         [Workload("gemm_M4600_n1008", 4600, 1008, 1024, 8, 16), Workload("gemm_M8192_n896", 8192, 896, 3584, 16, 64)])
 
 
 @pytest.mark.parametrize("wl", CASES, ids=lambda w: w.name)
@@ -47,7 +49,7 @@ def test_router_logits_parity(R, wl):
         "counters must be back at zero after the call"
 
 
-@pytest.mark.parametrize("m", [1, 2, 8, 16, 24, 64, 200])
+@pytest.mark.parametrize("m", [1, 2, 8, 16, 24, 64, 200, 4700])
 @pytest.mark.parametrize("n,k", [(128, 6144), (896, 3584)])
 def test_router_integer_inputs_bit_exact(R, m, n, k):
     say(f"router integer inputs M={m} N={n} K={k}")
