@@ -298,11 +298,12 @@ int launch_sort_quant(const int32_t* ids, const uint16_t* x, int64_t ldx, int m,
     int32_t* offws = reinterpret_cast<int32_t*>(ws + L.offws);
     hipLaunchKernelGGL(sort_hist_kernel, dim3(G), dim3(256), sizeof(int) * n, st, ids, P, n, kLargeSortChunk,
                        ghist);
-    hipLaunchKernelGGL(sort_scan_kernel, dim3(1), dim3(1024), sizeof(int) * ((size_t)n + (n + 1) + 1024), st, ghist,
-                       G, P, n, block, sorted_ids, expert_ids, offsets, offws);
+    hipLaunchKernelGGL(sort_colscan_kernel, dim3((n + 63) / 64), dim3(256), 0, st, ghist, G, n, offws);
+    hipLaunchKernelGGL(sort_scan_kernel, dim3(1), dim3(1024), sizeof(int) * ((size_t)n + (n + 1) + 1024), st, P, n,
+                       block, sorted_ids, expert_ids, offsets, offws);
     hipLaunchKernelGGL(sort_scatter_kernel, dim3(G), dim3(256), sizeof(int) * (4 * (size_t)n + n), st, ids, P, n,
                        kLargeSortChunk, ghist, offws, sorted_ids, pos);
-    launches += 3;
+    launches += 4;
   }
   const int units = m * (k / 16);
   hipLaunchKernelGGL(quant_kernel, dim3((units + 255) / 256), dim3(256), 0, st, x, ldx, m, k, topk, pos, a_q,

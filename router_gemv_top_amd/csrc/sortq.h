@@ -495,22 +495,56 @@ __global__ void __launch_bounds__(256) sort_hist_kernel(const int32_t* ids, int 
   for (int e = threadIdx.x; e < N; e += blockDim.x) ghist[(int64_t)blockIdx.x * N + e] = s_h[e];
 }
 
-__global__ void __launch_bounds__(1024) sort_scan_kernel(int32_t* ghist, int G, int P, int N, int B,
-                                                         int32_t* sorted_ids, int32_t* expert_ids,
-                                                         int32_t* offsets, int32_t* off_ws) {
+// Per-group bases of the large sort: for every expert, an exclusive prefix
+// of its counts over the G groups (in place in ghist) and its total (to
+// cnt[e]). Workgroup b takes experts [64b, 64b + 64) (lane = expert); wave w
+// takes a quarter of the groups, and the four quarters are joined through
+// LDS. Loads go 8 at a time so their latencies overlap.
+__global__ void __launch_bounds__(256) sort_colscan_kernel(int32_t* ghist, int G, int N, int32_t* cnt) {
+  __shared__ int s_part[4][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 64 + lane;
+  const int ec = min(e, N - 1);
+  const int gq = (G + 3) >> 2, g0 = min(G, wave * gq), g1 = min(G, g0 + gq);
+  int sum = 0;
+  for (int g = g0; g < g1; g += 8) {
+    int v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = ghist[(int64_t)min(g + j, g1 - 1) * N + ec];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sum += g + j < g1 ? v[j] : 0;
+  }
+  s_part[wave][lane] = sum;
+  __syncthreads();
+  int run = 0;
+  for (int w = 0; w < wave; ++w) run += s_part[w][lane];
+  if (wave == 0 && e < N) cnt[e] = s_part[0][lane] + s_part[1][lane] + s_part[2][lane] + s_part[3][lane];
+  if (e >= N) return;
+  for (int g = g0; g < g1; g += 8) {
+    int v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = ghist[(int64_t)min(g + j, g1 - 1) * N + e];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (g + j < g1) {
+        ghist[(int64_t)(g + j) * N + e] = run;
+        run += v[j];
+      }
+  }
+}
+
+// Padded offsets and the layout of the large sort from the per-expert
+// totals in off_ws (replaced by the offsets).
+__global__ void __launch_bounds__(1024) sort_scan_kernel(int P, int N, int B, int32_t* sorted_ids,
+                                                         int32_t* expert_ids, int32_t* offsets, int32_t* off_ws) {
   extern __shared__ int smem[];
   int* s_cnt = smem;
   int* s_off = s_cnt + N;
   int* s_scr = s_off + N + 1;
   for (int e = threadIdx.x; e < N; e += blockDim.x) {
-    int run = 0;
-    for (int g = 0; g < G; ++g) {
-      const int c = ghist[(int64_t)g * N + e];
-      ghist[(int64_t)g * N + e] = run;
-      run += c;
-    }
-    s_cnt[e] = run;
-    s_off[e] = pad_to(run, B);
+    const int c = off_ws[e];
+    s_cnt[e] = c;
+    s_off[e] = pad_to(c, B);
   }
   __syncthreads();
   const int total = block_exclusive_scan(s_off, N, s_scr);
