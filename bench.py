@@ -14,7 +14,10 @@ that stream.
 
 Prints ONE JSON line: value = algorithmic bytes of the K steps / their time
 (GB/s), the per-M microseconds per call, the roofline of the dominant kernel
-and the CPU oracle's rate on a bounded sample.
+and the CPU oracle's rate on a bounded sample. Secondary figures ride along
+in the same line: the resident-W (hot) times, the wide-batch and many-expert
+shapes, the prefill call with its router GEMM against the bf16 MFMA peak, and
+the host cost of one eager call.
 """
 from __future__ import annotations
 
@@ -34,6 +37,7 @@ SWEEP = (1, 2, 4, 8, 16, 32, 64)
 N, K, TOPK, BLOCK = 128, 6144, 8, 16
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
 def algorithmic_bytes(m: int, total: int) -> int:
@@ -72,6 +76,104 @@ def cpu_baseline(budget_s: float = 12.0):
             "seconds": round(dt, 2)}
 
 
+def _graph_us(torch, stream, calls, fn):
+    """Average µs per call of `fn(i)` for i in range(calls), captured in one
+    HIP graph and replayed once untimed, then once between events."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(calls):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / calls
+
+
+def secondary(torch, R, dev, stream, copies_128: int):
+    """The other routing shapes, timed like the headline sweep (graph replay,
+    cold W by rotating copies), plus the prefill router GEMM alone against the
+    bf16 MFMA peak and the host cost of one eager call."""
+    from router_gemv_top_amd.inputs import workloads_wide_128, workloads_decode_896, workload_prefill_896
+
+    def dev_bf16(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def outputs(wl, logits=False):
+        o = R.alloc_sort_outputs(wl.m, wl.n, wl.k, wl.topk, wl.block, device=dev)
+        o["topk_ids"] = torch.empty((wl.m, wl.topk), dtype=torch.int32, device=dev)
+        o["topk_w"] = torch.empty((wl.m, wl.topk), dtype=torch.float32, device=dev)
+        o["logits"] = torch.empty((wl.m, wl.n), dtype=torch.float32, device=dev) if logits else None
+        return o
+
+    res = {}
+    for group, wls in (("wide_N128_K6144_top8_B32", workloads_wide_128()),
+                       ("decode_N896_K3584_top16_bias_B16", workloads_decode_896())):
+        x, w, b = wls[0].make()
+        w_bytes = w.size * 2
+        copies = min(copies_128, int(np.ceil(2 * MALL_BYTES / w_bytes)))
+        w_all = dev_bf16(w).unsqueeze(0).repeat(copies, 1, 1)
+        bias = torch.from_numpy(b).to(dev) if b is not None else None
+        per = {}
+        for wl in wls:
+            xw = dev_bf16(wl.make()[0]).unsqueeze(0).repeat(copies, 1, 1)
+            ws = R.Workspace(wl.m, wl.n, wl.k, wl.topk, wl.block, device=dev)
+            o = outputs(wl)
+            us = _graph_us(torch, stream, copies, lambda i: R.route_sort_quant(
+                xw[i], w_all[i], wl.topk, wl.block, ws, bias=bias, out=o))
+            if ws.check() != 0:
+                raise RuntimeError(f"device-side wait timed out ({wl.name})")
+            total = int(o["offsets"][-1].item())
+            p = wl.m * wl.topk
+            nbytes = (wl.n * wl.k * 2 + wl.m * wl.k * 2 + p * 8 + total * 4 + (total // wl.block) * 4 +
+                      (wl.n + 1) * 4 + p * wl.k + p * (wl.k // 32))
+            per[str(wl.m)] = {"us": round(us, 3), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                              "launches": R.last_launch_count()}
+            del xw
+        res[group] = {"w_copies": copies, "per_m": per}
+        del w_all
+
+    wl = workload_prefill_896()
+    x, w, _ = wl.make()
+    xd, wd = dev_bf16(x), dev_bf16(w)
+    ws = R.Workspace(wl.m, wl.n, wl.k, wl.topk, wl.block, device=dev)
+    o = outputs(wl, logits=True)
+    full = _graph_us(torch, stream, 10, lambda i: R.route_sort_quant(xd, wd, wl.topk, wl.block, ws, out=o))
+    launches = R.last_launch_count()
+    if ws.check() != 0:
+        raise RuntimeError("device-side wait timed out (prefill)")
+    router = _graph_us(torch, stream, 20, lambda i: R.router_logits(xd, wd, ws, logits=o["logits"]))
+    flop = 2.0 * wl.m * wl.n * wl.k
+    tflops = flop / (router * 1e-6) / 1e12
+    res["prefill_M8192_N896_K3584_top16_B64_dup5pct"] = {
+        "us": round(full, 2), "launches": launches, "router_gemm_us": round(router, 2),
+        "router_gemm_tflops": round(tflops, 1), "mfma_frac_bf16": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+    # Host cost of one eager call at M=1 (argument marshalling + launch), and
+    # the eager wall time per call once the queue has drained.
+    wl = workloads_decode_896((1,))[0]
+    x, w, b = wl.make()
+    xd, wd, bias = dev_bf16(x), dev_bf16(w), torch.from_numpy(b).to(dev)
+    ws = R.Workspace(1, wl.n, wl.k, wl.topk, wl.block, device=dev)
+    o = outputs(wl)
+    for _ in range(50):
+        R.route_sort_quant(xd, wd, wl.topk, wl.block, ws, bias=bias, out=o)
+    torch.cuda.synchronize()
+    calls = 1000
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        R.route_sort_quant(xd, wd, wl.topk, wl.block, ws, bias=bias, out=o)
+    t1 = time.perf_counter()
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    res["host_us_per_call_M1_N896"] = {"enqueue": round((t1 - t0) * 1e6 / calls, 2),
+                                       "eager_wall": round((t2 - t0) * 1e6 / calls, 2)}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -80,10 +182,15 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="W/x copies to rotate over (0 = enough to evict the MALL)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--hot", action="store_true", help="also time with one resident W copy")
+    ap.add_argument("--no-hot", action="store_true", help="skip the resident-W (hot) timing")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the other routing shapes (wide, many-expert, prefill) and host timing")
     ap.add_argument("--only-m", type=int, default=0,
                     help="profiling mode: run --calls fused calls at this M (rotating cold W), print a summary")
     ap.add_argument("--calls", type=int, default=64)
+    ap.add_argument("--only-prefill", action="store_true",
+                    help="profiling mode: --calls prefill calls (M=8192, N=896, K=3584, top-16, B=64), "
+                         "then --calls router GEMM calls alone")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="profiling mode: one plain device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
@@ -109,6 +216,29 @@ def main():
         assert torch.equal(src, dst)
         print(json.dumps({"mode": "calibrate_copy", "bytes_read": args.calibrate_copy,
                           "bytes_written": args.calibrate_copy}), flush=True)
+        return
+
+    if args.only_prefill:
+        from router_gemv_top_amd.inputs import workload_prefill_896
+        wl = workload_prefill_896()
+        x, w, _ = wl.make()
+        xd = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        wd = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).to(dev)
+        ws = R.Workspace(wl.m, wl.n, wl.k, wl.topk, wl.block, device=dev)
+        o = R.alloc_sort_outputs(wl.m, wl.n, wl.k, wl.topk, wl.block, device=dev)
+        o["topk_ids"] = torch.empty((wl.m, wl.topk), dtype=torch.int32, device=dev)
+        o["topk_w"] = torch.empty((wl.m, wl.topk), dtype=torch.float32, device=dev)
+        o["logits"] = torch.empty((wl.m, wl.n), dtype=torch.float32, device=dev)
+        for _ in range(args.calls):
+            R.route_sort_quant(xd, wd, wl.topk, wl.block, ws, out=o)
+        launches = R.last_launch_count()
+        for _ in range(args.calls):
+            R.router_logits(xd, wd, ws, logits=o["logits"])
+        torch.cuda.synchronize()
+        if ws.check() != 0:
+            raise RuntimeError("device-side wait timed out")
+        print(json.dumps({"mode": "only_prefill", "calls": args.calls, "launches_per_call": launches,
+                          "router_flop_per_call": 2 * wl.m * wl.n * wl.k}), flush=True)
         return
 
     w_bytes = N * K * 2
@@ -193,7 +323,7 @@ def main():
         ev1.record(stream)
         torch.cuda.synchronize()
         us_per_call[m] = ev0.elapsed_time(ev1) * 1e3 / copies
-        if args.hot:
+        if not args.no_hot:
             gh = capture([(m, 0)] * 64)
             gh.replay()
             torch.cuda.synchronize()
@@ -266,8 +396,10 @@ def main():
                      "algorithmic_bytes_per_launch": round(sum(sweep_bytes.values()) / len(SWEEP), 1),
                      "kernel": "fused route_sort_quant (one launch per call), averaged over the sweep"},
     }
-    if args.hot:
+    if not args.no_hot:
         line["us_per_call_hot"] = {str(m): round(us_hot[m], 3) for m in SWEEP}
+    if not args.no_secondary:
+        line["secondary"] = secondary(torch, R, dev, stream, copies)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(line), flush=True)

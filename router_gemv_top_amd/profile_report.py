@@ -4,7 +4,7 @@ Reads the CSV directories that the commands below leave in a results folder
 and writes the short text summaries kept under ``profiles/``:
 
     rocprofv3 --kernel-trace --stats --output-format csv -d RES/prof_stats -o fused \\
-        -- python3 bench.py --steps 5 --warmup 2 --no-cpu
+        -- python3 bench.py --steps 5 --warmup 2 --no-cpu --no-hot --no-secondary
     for M in 1 2 4 8 16 32 64; for C in FETCH_SIZE WRITE_SIZE:
         rocprofv3 --pmc C --output-format csv -d RES/pmc_C_mM -o p -- python3 bench.py --only-m M --calls 32
     for C in FETCH_SIZE WRITE_SIZE:
@@ -67,7 +67,7 @@ def build(res: str, out: str):
              "the seven M values (VALU tile `<NV, MT, RPW, L>` for M <= 8, MFMA tile `<NV, MT, KS>` above).",
              "", "Command (from the repository root, results folder RES):", "",
              "    rocprofv3 --kernel-trace --stats --output-format csv -d RES/prof_stats -o fused "
-             "-- python3 bench.py --steps 5 --warmup 2 --no-cpu",
+             "-- python3 bench.py --steps 5 --warmup 2 --no-cpu --no-hot --no-secondary",
              f"    python -m router_gemv_top_amd.profile_report RES profiles", "",
              "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
     for r in rows:
