@@ -17,10 +17,12 @@
 #include "device.h"
 #include "diag.h"
 #include "fused.h"
+#include "fused_pick.h"
 #include "gate.h"
 #include "gemm.h"
 #include "gemv.h"
 #include "sortq.h"
+#include "sortq_kernels.h"
 
 using namespace rgt;
 
@@ -327,50 +329,13 @@ size_t fused_lds_bytes(const Plan& p, int m, int n, int topk, bool small) {
   return std::max(tail, tile);
 }
 
-template <int NV, int MT>
-const void* fused_valu_ptr(int l) {
-  switch (l) {
-    case 1: return (const void*)fused_valu_kernel<NV, MT, 1, 1>;
-    case 2: return (const void*)fused_valu_kernel<NV, MT, 1, 2>;
-    case 4: return (const void*)fused_valu_kernel<NV, MT, 1, 4>;
-    default: return (const void*)fused_valu_kernel<NV, MT, 1, 7>;
-  }
-}
-
-template <int NV, int MT>
-const void* fused_mfma_ptr(int ks) {
-  switch (ks) {
-    case 2: return (const void*)fused_mfma_kernel<NV, MT, 2>;
-    case 4: return (const void*)fused_mfma_kernel<NV, MT, 4>;
-    default: return (const void*)fused_mfma_kernel<NV, MT, 8>;
-  }
-}
-
-template <int NV>
-const void* fused_kernel_ptr(const Plan& p) {
-  if (p.valu) {
-    switch (p.mt) {
-      case 1: return fused_valu_ptr<NV, 1>(p.l);
-      case 2: return fused_valu_ptr<NV, 2>(p.l);
-      case 4: return fused_valu_ptr<NV, 4>(p.l);
-      default: return fused_valu_ptr<NV, 8>(p.l);
-    }
-  }
-  switch (p.mt) {
-    case 1: return fused_mfma_ptr<NV, 1>(p.ks);
-    case 2: return fused_mfma_ptr<NV, 2>(p.ks);
-    case 3: return fused_mfma_ptr<NV, 3>(p.ks);
-    default: return fused_mfma_ptr<NV, 4>(p.ks);
-  }
-}
-
 const void* fused_kernel_for(const Plan& p, int n) {
   switch (nv_bucket(n)) {
-    case 2: return fused_kernel_ptr<2>(p);
-    case 4: return fused_kernel_ptr<4>(p);
-    case 8: return fused_kernel_ptr<8>(p);
-    case 14: return fused_kernel_ptr<14>(p);
-    default: return fused_kernel_ptr<16>(p);
+    case 2: return fused_pick_nv2(p.valu, p.mt, p.l, p.ks);
+    case 4: return fused_pick_nv4(p.valu, p.mt, p.l, p.ks);
+    case 8: return fused_pick_nv8(p.valu, p.mt, p.l, p.ks);
+    case 14: return fused_pick_nv14(p.valu, p.mt, p.l, p.ks);
+    default: return fused_pick_nv16(p.valu, p.mt, p.l, p.ks);
   }
 }
 

@@ -455,149 +455,6 @@ __device__ __forceinline__ void write_sort_outputs(const int* s_e, PosPtr pos, c
 // the whole workgroup above). pos goes to the workspace for the quant.
 constexpr int kWaveSortMaxP = 2048;
 
-__global__ void __launch_bounds__(256) sort_small_kernel(const int32_t* ids, int P, int N, int B,
-                                                         int32_t* sorted_ids, int32_t* expert_ids,
-                                                         int32_t* offsets, int32_t* pos_ws) {
-  extern __shared__ int smem[];
-  int* s_e = smem;
-  int* s_hist = s_e + P;          // wave sort: per-pair ranks; workgroup sort: per-wave counts
-  int* s_cnt = s_hist + (P > 4 * N ? P : 4 * N);
-  int* s_off = s_cnt + N;
-  int* s_scr = s_off + N + 1;
-  if (P <= kWaveSortMaxP) {
-    if (threadIdx.x < 64) wave_sort<16>(ids, P, N, B, s_e, s_hist, s_cnt, s_off, pos_ws);
-    vm_drain();
-    __syncthreads();
-  } else {
-    wg_sort<false>(ids, P, N, B, s_e, s_hist, s_cnt, s_off, s_scr, pos_ws);
-  }
-  for (int p = threadIdx.x; p < P; p += blockDim.x) {
-    const int q = pos_ws[p];
-    if (q >= 0) sorted_ids[q] = p;
-  }
-  write_sort_layout(s_cnt, s_off, N, B, P, sorted_ids, expert_ids, offsets);
-}
-
-// ---------------------------------------------------------------------------
-// Large-P sort: per-workgroup histograms -> one scan workgroup -> scatter.
-// Workgroup g owns pairs [g*chunk, (g+1)*chunk).
-// ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) sort_hist_kernel(const int32_t* ids, int P, int N, int chunk, int32_t* ghist) {
-  extern __shared__ int s_h[];
-  for (int e = threadIdx.x; e < N; e += blockDim.x) s_h[e] = 0;
-  __syncthreads();
-  const int p0 = blockIdx.x * chunk, p1 = min(P, p0 + chunk);
-  for (int p = p0 + threadIdx.x; p < p1; p += blockDim.x) {
-    const int e = ids[p];
-    if ((unsigned)e < (unsigned)N) atomicAdd(&s_h[e], 1);
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < N; e += blockDim.x) ghist[(int64_t)blockIdx.x * N + e] = s_h[e];
-}
-
-// Per-group bases of the large sort: for every expert, an exclusive prefix
-// of its counts over the G groups (in place in ghist) and its total (to
-// cnt[e]). Workgroup b takes experts [64b, 64b + 64) (lane = expert); wave w
-// takes a quarter of the groups, and the four quarters are joined through
-// LDS. Loads go 8 at a time so their latencies overlap.
-__global__ void __launch_bounds__(256) sort_colscan_kernel(int32_t* ghist, int G, int N, int32_t* cnt) {
-  __shared__ int s_part[4][64];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 64 + lane;
-  const int ec = min(e, N - 1);
-  const int gq = (G + 3) >> 2, g0 = min(G, wave * gq), g1 = min(G, g0 + gq);
-  int sum = 0;
-  for (int g = g0; g < g1; g += 8) {
-    int v[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = ghist[(int64_t)min(g + j, g1 - 1) * N + ec];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) sum += g + j < g1 ? v[j] : 0;
-  }
-  s_part[wave][lane] = sum;
-  __syncthreads();
-  int run = 0;
-  for (int w = 0; w < wave; ++w) run += s_part[w][lane];
-  if (wave == 0 && e < N) cnt[e] = s_part[0][lane] + s_part[1][lane] + s_part[2][lane] + s_part[3][lane];
-  if (e >= N) return;
-  for (int g = g0; g < g1; g += 8) {
-    int v[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = ghist[(int64_t)min(g + j, g1 - 1) * N + e];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (g + j < g1) {
-        ghist[(int64_t)(g + j) * N + e] = run;
-        run += v[j];
-      }
-  }
-}
-
-// Padded offsets and the layout of the large sort from the per-expert
-// totals in off_ws (replaced by the offsets).
-__global__ void __launch_bounds__(1024) sort_scan_kernel(int P, int N, int B, int32_t* sorted_ids,
-                                                         int32_t* expert_ids, int32_t* offsets, int32_t* off_ws) {
-  extern __shared__ int smem[];
-  int* s_cnt = smem;
-  int* s_off = s_cnt + N;
-  int* s_scr = s_off + N + 1;
-  for (int e = threadIdx.x; e < N; e += blockDim.x) {
-    const int c = off_ws[e];
-    s_cnt[e] = c;
-    s_off[e] = pad_to(c, B);
-  }
-  __syncthreads();
-  const int total = block_exclusive_scan(s_off, N, s_scr);
-  if (threadIdx.x == 0) s_off[N] = total;
-  __syncthreads();
-  for (int e = threadIdx.x; e <= N; e += blockDim.x) off_ws[e] = s_off[e];
-  write_sort_layout(s_cnt, s_off, N, B, P, sorted_ids, expert_ids, offsets);
-}
-
-__global__ void __launch_bounds__(256) sort_scatter_kernel(const int32_t* ids, int P, int N, int chunk,
-                                                           const int32_t* ghist, const int32_t* off_ws,
-                                                           int32_t* sorted_ids, int32_t* pos_ws) {
-  extern __shared__ int smem[];
-  int* s_hist = smem;            // [4][N] per-wave counts -> bases
-  int* s_base = s_hist + 4 * N;  // [N] offsets + this workgroup's global base
-  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
-  const int p0 = blockIdx.x * chunk, p1 = min(P, p0 + chunk);
-  for (int i = t; i < 4 * N; i += blockDim.x) s_hist[i] = 0;
-  for (int e = t; e < N; e += blockDim.x) s_base[e] = off_ws[e] + ghist[(int64_t)blockIdx.x * N + e];
-  __syncthreads();
-  const int sub = ((p1 - p0 + 3) / 4 + 63) & ~63;
-  const int c0 = min(p1, p0 + wave * sub), c1 = min(p1, c0 + sub);
-  for (int p = c0 + lane; p < c1; p += 64) {
-    const int e = ids[p];
-    if ((unsigned)e < (unsigned)N) atomicAdd(&s_hist[wave * N + e], 1);
-  }
-  __syncthreads();
-  for (int e = t; e < N; e += blockDim.x) {
-    int run = 0;
-    for (int w = 0; w < 4; ++w) {
-      const int c = s_hist[w * N + e];
-      s_hist[w * N + e] = run;
-      run += c;
-    }
-  }
-  __syncthreads();
-  const int bits = ceil_log2(N);
-  for (int base = c0; base < c1; base += 64) {
-    const int p = base + lane;
-    const int e = p < c1 ? ids[p] : 0;
-    const bool valid = p < c1 && (unsigned)e < (unsigned)N;
-    const u64 peers = match_peers(e, valid, bits);
-    if (valid) {
-      const int q = s_base[e] + s_hist[wave * N + e] + __popcll(peers & lanemask_lt());
-      pos_ws[p] = q;
-      sorted_ids[q] = p;
-    } else if (p < c1) {
-      pos_ws[p] = -1;
-    }
-    if (valid && (peers & lanemask_lt()) == 0ull) s_hist[wave * N + e] += __popcll(peers);
-  }
-}
-
 // ---------------------------------------------------------------------------
 // MXFP8 of 16 consecutive bf16 elements (two 16-byte loads). The partner lane
 // (lane ^ 1) holds the other half of the 32-element block. Returns the 16
@@ -665,20 +522,6 @@ __device__ __forceinline__ void store_unit(uint8_t* a_q, uint8_t* a_scale, int K
   if (k <= 8) store_unit_k<8>(a_q, a_scale, K, k, u, pos, codes, scales4, cpr_magic);
   else if (k <= 16) store_unit_k<16>(a_q, a_scale, K, k, u, pos, codes, scales4, cpr_magic);
   else store_unit_k<32>(a_q, a_scale, K, k, u, pos, codes, scales4, cpr_magic);
-}
-
-__global__ void __launch_bounds__(256) quant_kernel(const uint16_t* x, int64_t ldx, int M, int K, int k,
-                                                    const int32_t* pos, uint8_t* a_q, uint8_t* a_scale) {
-  const int units = M * (K >> 4);
-  const int u = blockIdx.x * blockDim.x + threadIdx.x;
-  const int cpr = K >> 4;
-  // Units come in whole groups of 8 lanes (unit counts are multiples of 32),
-  // so every lane of a pair or group is active together.
-  u32 sb = 0;
-  uint4 codes = make_uint4(0, 0, 0, 0);
-  if (u < units) codes = mx_quant16(x + (int64_t)(u / cpr) * ldx + 16 * (u % cpr), sb);
-  const u32 s4 = pack_scales(sb);
-  if (u < units) store_unit(a_q, a_scale, K, k, u, pos, codes, s4);
 }
 
 }  // namespace rgt
