@@ -25,7 +25,10 @@ Sources (titles of the pages this follows):
           commit (group-32 scales).
   [OCP]   OCP Microscaling Formats (MX) v1.0: e4m3 element format (bias 7,
           max normal 448, no infinities), e8m0 shared scale (bias 127), shared
-          exponent = floor(log2(amax)) - emax_elem with emax_elem = 8 for e4m3.
+          exponent = floor(log2(amax)) - emax_elem with emax_elem = 8 for e4m3;
+          e2m1 element format (1 sign bit, 2 exponent bits with bias 1, 1
+          mantissa bit: 0, 0.5, 1, 1.5, 2, 3, 4, 6; no infinities or NaN) with
+          emax_elem = 2.
 
 Readings taken where the pages are silent (each is listed in the design
 notes):
@@ -40,6 +43,10 @@ notes):
     size with the sentinel P = M*k; empty experts get no block.
   * MXFP8: OCP floor rule for the shared exponent, round to nearest even,
     saturation to +-448, sign kept (so -0 encodes as 0x80).
+  * MXFP4 (the stage-1 activation quant of [M31K], Summary: MoE sorting +
+    quant): the same floor rule with emax_elem = 2 for e2m1, round to nearest
+    even, saturation to +-6, sign kept (-0 -> 0x8); two codes a byte, the
+    even element in the low nibble.
 
 Parity pins: every function here is checked by the ``-m "not gpu"`` tests
 against brute force, exact rationals, closed forms or invariants.
@@ -282,36 +289,96 @@ def mxfp8_quant_rows(x_bits: np.ndarray):
     return codes.reshape(r, k), scale
 
 
-def moe_sort_quant(ids: np.ndarray, x_bits: np.ndarray, n: int, block: int,
-                   rows_per_chunk: int = 2048):
-    """Sort pairs into padded expert segments and MXFP8-quantise gathered rows.
+# ---------------------------------------------------------------------------
+# MXFP4 quantisation [OCP] e2m1 elements, [M31K] stage-1 activation quant
+# ---------------------------------------------------------------------------
 
-    Returns dict with sorted_ids, expert_ids, offsets, total, a_q [total][K]
-    (pad rows zero and marked invalid), a_scale [total][K/32], valid [total].
-    Row p (valid) holds the quantised activations of token sorted_ids[p] // k.
+E2M1_MAX = 6.0
+E2M1_EMAX = 2          # floor(log2(6))
+
+
+def e2m1_code(y: np.ndarray, neg: np.ndarray) -> np.ndarray:
+    """e2m1 code (4 bits) of |y| (fp64, >= 0, exact) with the given sign.
+
+    Round to nearest, ties to even, over normals (1 mantissa bit, exponent
+    >= 0) and the subnormal 0.5 (step 2^-1); magnitudes above 6 saturate to 6.
     """
+    a = np.asarray(y, dtype=np.float64)
+    _, ex = np.frexp(a)                        # a = f * 2^ex, f in [0.5, 1)
+    binade = np.maximum(ex - 1, 0)             # floor(log2 a), at least 0
+    qexp = binade - 1                          # spacing of representable values
+    units = np.rint(np.ldexp(a, -qexp))        # RNE to a multiple of the spacing
+    val = np.minimum(np.ldexp(units, qexp), E2M1_MAX)
+    # encode the (now representable) magnitude
+    _, vex = np.frexp(val)
+    vb = vex - 1
+    is_norm = val >= 1.0
+    mant_norm = np.ldexp(val, -(vb - 1)) - 2.0          # 0 or 1
+    code_norm = ((vb + 1) << 1) + mant_norm.astype(np.int64)
+    code_sub = np.ldexp(val, 1).astype(np.int64)        # 0 or 1
+    code = np.where(is_norm, code_norm, code_sub).astype(np.int64)
+    code = code | (np.asarray(neg, dtype=np.int64) << 3)
+    return code.astype(np.uint8)
+
+
+def mxfp4_quant_rows(x_bits: np.ndarray):
+    """MXFP4 of bf16 rows: (packed codes u8 [R][K/2], scales u8 [R][K/32]).
+
+    Per 32-element block: amax = max |v|; E = floor(log2 amax); shared
+    exponent se = clamp(E - 2, -127, 127) (0 scale byte when amax = 0); scale
+    byte = se + 127 (e8m0); element code = e2m1(v / 2^se). Byte j of a row
+    holds element 2j in its low nibble and element 2j+1 in its high nibble.
+    """
+    h = np.asarray(x_bits, dtype=np.uint16)
+    r, k = h.shape
+    assert k % MX_BLOCK == 0
+    v = bf16_bits_to_f64(h).reshape(r, k // MX_BLOCK, MX_BLOCK)
+    neg = ((h >> np.uint16(15)) & np.uint16(1)).reshape(v.shape).astype(bool)
+    av = np.abs(v)
+    amax = av.max(axis=2)
+    _, ex = np.frexp(amax)
+    e_floor = ex - 1
+    se = np.where(amax > 0, np.clip(e_floor - E2M1_EMAX, -127, 127), -127).astype(np.int64)
+    scale = (se + 127).astype(np.uint8)
+    y = np.ldexp(av, -se[:, :, None])          # exact: power-of-two scaling
+    codes = e2m1_code(y, neg).reshape(r, k)
+    packed = codes[:, 0::2] | (codes[:, 1::2] << np.uint8(4))
+    return packed.astype(np.uint8), scale
+
+
+def moe_sort_quant(ids: np.ndarray, x_bits: np.ndarray, n: int, block: int,
+                   rows_per_chunk: int = 2048, fmt: str = "mxfp8"):
+    """Sort pairs into padded expert segments and quantise the gathered rows
+    (fmt "mxfp8": e4m3 codes, a_q [total][K]; fmt "mxfp4": packed e2m1
+    codes, a_q [total][K/2]).
+
+    Returns dict with sorted_ids, expert_ids, offsets, total, a_q (pad rows
+    zero and marked invalid), a_scale [total][K/32], valid [total]. Row p
+    (valid) holds the quantised activations of token sorted_ids[p] // k.
+    """
+    quant = {"mxfp8": mxfp8_quant_rows, "mxfp4": mxfp4_quant_rows}[fmt]
     ids = np.asarray(ids)
     m, k = ids.shape
     sorted_ids, expert_ids, offsets, total = moe_sort(ids, n, block)
     kdim = x_bits.shape[1]
     valid = sorted_ids != m * k
-    a_q = np.zeros((total, kdim), dtype=np.uint8)
+    a_q = np.zeros((total, kdim if fmt == "mxfp8" else kdim // 2), dtype=np.uint8)
     a_scale = np.zeros((total, kdim // MX_BLOCK), dtype=np.uint8)
     pos = np.nonzero(valid)[0]
     for c in range(0, len(pos), rows_per_chunk):
         pc = pos[c:c + rows_per_chunk]
         tok = sorted_ids[pc] // k
-        q, s = mxfp8_quant_rows(x_bits[tok])
+        q, s = quant(x_bits[tok])
         a_q[pc] = q
         a_scale[pc] = s
     return dict(sorted_ids=sorted_ids, expert_ids=expert_ids, offsets=offsets,
                 total=total, a_q=a_q, a_scale=a_scale, valid=valid)
 
 
-def route_sort_quant(x_bits, w_bits, bias, k: int, block: int):
-    """The whole front-end chained: logits -> gate -> sort -> MXFP8 quant."""
+def route_sort_quant(x_bits, w_bits, bias, k: int, block: int, fmt: str = "mxfp8"):
+    """The whole front-end chained: logits -> gate -> sort -> MX quant."""
     logits = router_logits(x_bits, w_bits)
     ids, w = topk_gate(logits, bias, k)
-    out = moe_sort_quant(ids, x_bits, w_bits.shape[0], block)
+    out = moe_sort_quant(ids, x_bits, w_bits.shape[0], block, fmt=fmt)
     out.update(logits=logits, topk_ids=ids, topk_w=w)
     return out

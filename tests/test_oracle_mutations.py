@@ -109,3 +109,45 @@ def test_ceil_scale_rule_is_caught():
     amax = np.abs(vals).max()
     se_ceil = int(np.ceil(np.log2(amax / 448.0)))   # the non-saturating rule
     assert se_ceil + 127 != int(case["scale"], 16)
+
+
+def test_fp4_round_half_away_is_caught():
+    import test_oracle_quant_fp4 as Q4
+
+    def mutant(y, neg):
+        a = np.asarray(y, np.float64)
+        _, ex = np.frexp(a)
+        qexp = np.maximum(ex - 1, 0) - 1
+        units = np.floor(np.ldexp(a, -qexp) + 0.5)   # half away from zero
+        return O.e2m1_code(np.minimum(np.ldexp(units, qexp), 6.0), neg)
+
+    h = Q4.all_finite_bf16()
+    y = np.ldexp(np.abs(Q4.bf16_bits_to_f32(h).astype(np.float64)), 2)
+    neg = (h >> 15).astype(bool)
+    want = Q4.table_nearest(y) | (neg.astype(np.int64) << 3)
+    assert np.array_equal(O.e2m1_code(y, neg).astype(np.int64), want)
+    assert not np.array_equal(mutant(y, neg).astype(np.int64), want)
+
+
+def test_fp4_swapped_nibbles_are_caught():
+    import test_oracle_quant_fp4 as Q4
+    with open(os.path.join(Q4.GOLDEN, "mxfp4_hand_cases.json")) as f:
+        case = [c for c in json.load(f)["blocks"] if c["name"] == "grid_and_ties"][0]
+    vals = np.zeros(32, np.float32)
+    vals[:len(case["x"])] = [float.fromhex(s) for s in case["x"]]
+    q, _ = O.mxfp4_quant_rows(f32_to_bf16_bits(vals)[None, :])
+    swapped = ((q & 0x0F) << 4) | (q >> 4)
+    want = [int(s, 16) for s in case["bytes"]]
+    assert q[0, :len(want)].tolist() == want
+    assert swapped[0, :len(want)].tolist() != want
+
+
+def test_fp4_with_fp8_emax_is_caught():
+    import test_oracle_quant_fp4 as Q4
+    with open(os.path.join(Q4.GOLDEN, "mxfp4_hand_cases.json")) as f:
+        case = [c for c in json.load(f)["blocks"] if c["name"] == "ones"][0]
+    amax = float.fromhex(case["x"][0])
+    se_wrong = int(np.floor(np.log2(amax))) - O.E4M3_EMAX   # the e4m3 emax in the fp4 rule
+    assert se_wrong + 127 != int(case["scale"], 16)
+    se_ok = int(np.floor(np.log2(amax))) - O.E2M1_EMAX
+    assert se_ok + 127 == int(case["scale"], 16)
