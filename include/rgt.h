@@ -159,6 +159,31 @@ rgt_status rgt_route_sort_quant(const void* x, int64_t ldx, const void* w, int64
                                 uint8_t* a_q, uint8_t* a_scale,
                                 void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* MXFP4 variants (the stage-1 activation quant of the MoE sort; MiniMax-M3.1-
+ * Flash MoE/GEMM kernels page, Summary: MoE sorting + quant, and "Changes to
+ * existing kernels": 128-expert top-4 routing at hidden 6144 sorted in one
+ * launch with the stage-1 MXFP4 activation quant). Arguments, sort outputs,
+ * coverage, errors and launch counts are those of rgt_moe_sort_quant and
+ * rgt_route_sort_quant; only the element format and the a_q layout differ:
+ *   a_q     : uint8 [cap][K/2]; byte j of row p holds the e2m1 codes of
+ *             elements 2j (low nibble) and 2j+1 (high nibble) of
+ *             x[sorted_ids[p] / topk]; pad rows are not written.
+ *   a_scale : uint8 [cap][K/32]; se + 127 with se = clamp(floor(log2 amax) - 2,
+ *             -127, 127) (OCP MX v1.0, e2m1 emax 2), 0 for an all-zero block.
+ *             Codes are e2m1(v / 2^se): values 0, 0.5, 1, 1.5, 2, 3, 4, 6, round
+ *             to nearest even, saturating at +-6, sign in bit 3 (-0 -> 0x8). */
+rgt_status rgt_moe_sort_quant_mxfp4(const int32_t* topk_ids, const void* x, int64_t ldx,
+                                    int m, int n, int k, int topk, int block,
+                                    int32_t* sorted_ids, int32_t* expert_ids, int32_t* offsets,
+                                    uint8_t* a_q, uint8_t* a_scale,
+                                    void* ws, size_t ws_bytes, hipStream_t stream);
+rgt_status rgt_route_sort_quant_mxfp4(const void* x, int64_t ldx, const void* w, int64_t ldw,
+                                      const float* bias, int m, int n, int k, int topk, int block,
+                                      float* logits, int32_t* topk_ids, float* topk_w,
+                                      int32_t* sorted_ids, int32_t* expert_ids, int32_t* offsets,
+                                      uint8_t* a_q, uint8_t* a_scale,
+                                      void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Number of kernel launches the last successful call of each entry point made
  * on this thread (diagnostics for launch-count checks). */
 int rgt_last_launch_count(void);

@@ -1,5 +1,5 @@
 """MI355X (gfx950) MoE routing front-end: split-K router GEMV with in-launch
-fixup, softmax top-k gate, token -> expert sort and MXFP8 quantisation, behind
+fixup, softmax top-k gate, token -> expert sort and MXFP8 (or MXFP4) quantisation, behind
 the C ABI of include/rgt.h.
 
 The binding (``router_gemv_top_amd._binding``) is imported lazily so that the
@@ -8,7 +8,8 @@ loading the HIP library.
 """
 
 _API = (
-    "router_logits", "topk_gate", "moe_sort_quant", "route_sort_quant", "Workspace",
+    "router_logits", "topk_gate", "moe_sort_quant", "route_sort_quant", "moe_sort_quant_mxfp4",
+    "route_sort_quant_mxfp4", "Workspace",
     "workspace_bytes", "sort_capacity", "router_supported", "reset_workspace", "check_workspace",
     "status_string", "last_launch_count", "alloc_sort_outputs", "RgtError", "RgtUnsupported", "lib",
     "exported_symbols", "version", "diag_read", "diag_copy",

@@ -66,6 +66,10 @@ def lib() -> ctypes.CDLL:
             "rgt_moe_sort_quant": ([vp, vp, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp], i32),
             "rgt_route_sort_quant": ([vp, i64, vp, i64, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
                                       vp, vp, vp, sz, vp], i32),
+            "rgt_moe_sort_quant_mxfp4": ([vp, vp, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp],
+                                         i32),
+            "rgt_route_sort_quant_mxfp4": ([vp, i64, vp, i64, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
+                                            vp, vp, vp, sz, vp], i32),
             "rgt_last_launch_count": ([], i32),
             "rgt_diag_read": ([vp, sz, vp, i32, vp], i32),
             "rgt_diag_copy": ([vp, vp, sz, i32, vp], i32),
@@ -182,9 +186,13 @@ def topk_gate(logits, topk: int, bias=None, ids=None, weights=None, stream=None)
     return ids, weights
 
 
-def alloc_sort_outputs(m: int, n: int, k: int, topk: int, block: int, device="cuda", fill: int | None = None):
+def alloc_sort_outputs(m: int, n: int, k: int, topk: int, block: int, device="cuda", fill: int | None = None,
+                       fmt: str = "mxfp8"):
     """Device buffers sized to the sort capacity (optionally pre-filled with a
-    canary byte so that writes past the padded total can be detected)."""
+    canary byte so that writes past the padded total can be detected). a_q
+    has K bytes a row for MXFP8, K/2 for MXFP4."""
+    if fmt not in ("mxfp8", "mxfp4"):
+        raise ValueError(f"unknown activation format {fmt!r}")
     cap = sort_capacity(m, n, topk, block)
     if cap < 0:
         raise RgtUnsupported(RGT_ERR_UNSUPPORTED, "sort_capacity")
@@ -203,7 +211,7 @@ def alloc_sort_outputs(m: int, n: int, k: int, topk: int, block: int, device="cu
         sorted_ids=mk((cap,), torch.int32),
         expert_ids=mk((cap // block,), torch.int32),
         offsets=mk((n + 1,), torch.int32),
-        a_q=mk((cap, k), torch.uint8),
+        a_q=mk((cap, k if fmt == "mxfp8" else k // 2), torch.uint8),
         a_scale=mk((cap, k // 32), torch.uint8),
     )
 
@@ -211,15 +219,24 @@ def alloc_sort_outputs(m: int, n: int, k: int, topk: int, block: int, device="cu
 def moe_sort_quant(topk_ids, x, n: int, block: int, ws: Workspace, out=None, stream=None):
     """Sort pairs into block-padded expert segments and MXFP8-quantise the
     gathered rows of x. Returns the dict of output buffers."""
+    return _moe_sort_quant(lib().rgt_moe_sort_quant, "mxfp8", topk_ids, x, n, block, ws, out, stream)
+
+
+def moe_sort_quant_mxfp4(topk_ids, x, n: int, block: int, ws: Workspace, out=None, stream=None):
+    """As moe_sort_quant, with MXFP4 rows (K/2 bytes of packed e2m1 codes)."""
+    return _moe_sort_quant(lib().rgt_moe_sort_quant_mxfp4, "mxfp4", topk_ids, x, n, block, ws, out, stream)
+
+
+def _moe_sort_quant(fn, fmt, topk_ids, x, n, block, ws, out, stream):
     _bf16_2d(x, "x")
     m, k = x.shape
     topk = topk_ids.shape[1]
     if out is None:
-        out = alloc_sort_outputs(m, n, k, topk, block, x.device)
-    _check(lib().rgt_moe_sort_quant(_ptr(topk_ids), _ptr(x), x.stride(0), m, n, k, topk, block,
-                                    _ptr(out["sorted_ids"]), _ptr(out["expert_ids"]), _ptr(out["offsets"]),
-                                    _ptr(out["a_q"]), _ptr(out["a_scale"]), _ptr(ws.buf), ws.nbytes,
-                                    _stream(stream)), "moe_sort_quant")
+        out = alloc_sort_outputs(m, n, k, topk, block, x.device, fmt=fmt)
+    _check(fn(_ptr(topk_ids), _ptr(x), x.stride(0), m, n, k, topk, block,
+              _ptr(out["sorted_ids"]), _ptr(out["expert_ids"]), _ptr(out["offsets"]),
+              _ptr(out["a_q"]), _ptr(out["a_scale"]), _ptr(ws.buf), ws.nbytes,
+              _stream(stream)), fn.__name__[4:])
     return out
 
 
@@ -227,19 +244,31 @@ def route_sort_quant(x, w, topk: int, block: int, ws: Workspace, bias=None, out=
                      stream=None):
     """The whole front end (one launch for M <= 64). Returns a dict with
     logits (if requested), topk_ids, topk_w and the sort/quant buffers."""
+    return _route_sort_quant(lib().rgt_route_sort_quant, "mxfp8", x, w, topk, block, ws, bias, out, want_logits,
+                             stream)
+
+
+def route_sort_quant_mxfp4(x, w, topk: int, block: int, ws: Workspace, bias=None, out=None, want_logits=True,
+                           stream=None):
+    """As route_sort_quant, with MXFP4 rows (K/2 bytes of packed e2m1 codes)."""
+    return _route_sort_quant(lib().rgt_route_sort_quant_mxfp4, "mxfp4", x, w, topk, block, ws, bias, out,
+                             want_logits, stream)
+
+
+def _route_sort_quant(fn, fmt, x, w, topk, block, ws, bias, out, want_logits, stream):
     _bf16_2d(x, "x"), _bf16_2d(w, "w")
     m, k = x.shape
     n = w.shape[0]
     if out is None:
-        out = alloc_sort_outputs(m, n, k, topk, block, x.device)
+        out = alloc_sort_outputs(m, n, k, topk, block, x.device, fmt=fmt)
         out["topk_ids"] = torch.empty((m, topk), dtype=torch.int32, device=x.device)
         out["topk_w"] = torch.empty((m, topk), dtype=torch.float32, device=x.device)
         out["logits"] = torch.empty((m, n), dtype=torch.float32, device=x.device) if want_logits else None
-    _check(lib().rgt_route_sort_quant(_ptr(x), x.stride(0), _ptr(w), w.stride(0), _ptr(bias), m, n, k, topk, block,
-                                      _ptr(out.get("logits")), _ptr(out["topk_ids"]), _ptr(out["topk_w"]),
-                                      _ptr(out["sorted_ids"]), _ptr(out["expert_ids"]), _ptr(out["offsets"]),
-                                      _ptr(out["a_q"]), _ptr(out["a_scale"]), _ptr(ws.buf), ws.nbytes,
-                                      _stream(stream)), "route_sort_quant")
+    _check(fn(_ptr(x), x.stride(0), _ptr(w), w.stride(0), _ptr(bias), m, n, k, topk, block,
+              _ptr(out.get("logits")), _ptr(out["topk_ids"]), _ptr(out["topk_w"]),
+              _ptr(out["sorted_ids"]), _ptr(out["expert_ids"]), _ptr(out["offsets"]),
+              _ptr(out["a_q"]), _ptr(out["a_scale"]), _ptr(ws.buf), ws.nbytes,
+              _stream(stream)), fn.__name__[4:])
     return out
 
 

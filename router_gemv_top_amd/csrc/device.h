@@ -282,19 +282,51 @@ __device__ __forceinline__ u32 e4m3x4_of_bf16(u32 w0, u32 w1, int se) {
   return (u32)r;
 }
 
+// ---------------------------------------------------------------------------
+// e2m1 (MXFP4 element) code of one bf16 value (in the high 16 bits) divided
+// by 2^se. y = |v| / 2^se is exact in fp32 (or far below 0.25, where every
+// rounding gives 0), and below 8 for every element of a block whose shared
+// exponent follows the floor rule. The e2m1 grid (0, 0.5, 1, 1.5, 2, 3, 4, 6)
+// has spacing 0.5 below 2, 1 below 4 and 2 above, so rounding to it is one
+// round-to-nearest-even (v_rndne_f32) of y in units of its spacing, plus the
+// code of the binade's first grid point; a result past 7 (y rounding to 8) is
+// the saturation to 6. Sign in bit 3, so -0 gives 0x8.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ u32 e2m1_of_bf16(u32 bits_hi16, int se) {
+  const float y = __builtin_amdgcn_ldexpf(__uint_as_float(bits_hi16 & 0x7fff0000u), -se);
+  const bool lo = y < 2.f, mid = y < 4.f;
+  const float units = lo ? 2.f : (mid ? 1.f : 0.5f);   // grid points per unit of y
+  const float first = lo ? 0.f : (mid ? 2.f : 4.f);    // code of the binade's first point, minus its units
+  const float c = __builtin_fminf(__builtin_rintf(y * units) + first, 7.f);
+  return (u32)c | ((bits_hi16 >> 28) & 8u);
+}
+// Eight e2m1 codes of four bf16 pairs (the pair's low half is the earlier
+// element), element 0 in bits 0-3, element 7 in bits 28-31.
+__device__ __forceinline__ u32 e2m1x8_of_bf16(u32 w0, u32 w1, u32 w2, u32 w3, int se) {
+  const u32 w[4] = {w0, w1, w2, w3};
+  u32 r = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r |= (e2m1_of_bf16(w[i] << 16, se) << (8 * i)) | (e2m1_of_bf16(w[i] & 0xffff0000u, se) << (8 * i + 4));
+  return r;
+}
+
 // Shared exponent of a 32-element block from the largest magnitude's bits
 // (bits & 0x7fff, all finite): clamp(floor(log2 amax) - 8, -127, 127), and
 // -127 for an all-zero block.
-__device__ __forceinline__ int mx_shared_exp(u32 amax_bits) {
+// EMAX is the element format's largest binade: 8 for e4m3, 2 for e2m1.
+template <int EMAX>
+__device__ __forceinline__ int mx_shared_exp_e(u32 amax_bits) {
   const u32 ef = amax_bits >> 7;
   const u32 mf = amax_bits & 0x7fu;
   int e;
   if (ef) e = (int)ef - 127;
   else if (mf) e = (31 - __clz((int)mf)) - 133;
   else return -127;
-  int se = e - 8;
+  int se = e - EMAX;
   return se < -127 ? -127 : (se > 127 ? 127 : se);
 }
+__device__ __forceinline__ int mx_shared_exp(u32 amax_bits) { return mx_shared_exp_e<8>(amax_bits); }
 
 // ---------------------------------------------------------------------------
 // exp(d) for d <= 0 in fp64 by a fixed operation sequence (Cody & Waite range

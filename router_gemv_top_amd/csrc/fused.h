@@ -19,8 +19,8 @@
 //      publishes the ids as tagged words, which the others poll;
 //   3. the same workgroups sort the M*k pairs in LDS with one wave (tiny at
 //      decode sizes, so redundant sorting beats another hand-off) and store
-//      their MXFP8 chunk (quantised in registers while waiting) to the padded
-//      rows of the token's pairs; workgroup 0 also writes topk_ids, topk_w,
+//      their MXFP8 or MXFP4 chunk (quantised in registers while waiting) to
+//      the padded rows of the token's pairs; workgroup 0 also writes topk_ids, topk_w,
 //      logits, sorted_ids, expert_ids and offsets and advances the call epoch.
 //
 // A tagged word is a 32-bit payload plus the tag (epoch + 1) of the call that
@@ -58,6 +58,7 @@ struct FusedArgs {
   const float* bias;   // [N] or null
   int topk, block;
   int small;           // 1: small mode, 0: large mode (chosen by the host)
+  int fp4;             // 1: MXFP4 rows (K/2 bytes of packed e2m1 codes), 0: MXFP8
   int upw_log;         // log2 of the quant units per participating workgroup (6, 7 or 8)
   u32 cpr_magic;       // ceil(2^32 / (K/16)): token of a quant unit by multiplication
   float* logits_out;   // [M][N] or null
@@ -391,7 +392,8 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
     if (q >= 0 && (tok * cpr) >> a.upw_log == (int)blockIdx.x) a.sorted_ids[q] = p;
   }
   const u32 scales4 = pack_scales(sb_in);  // all lanes: DPP reads neighbouring lanes
-  if (have_unit) store_unit(a.a_q, a.a_scale, g.k, k, unit, OffsetPos{s_pos, p0}, codes_in, scales4, a.cpr_magic);
+  if (have_unit) store_unit(a.a_q, a.a_scale, g.k, k, unit, OffsetPos{s_pos, p0}, codes_in, scales4, a.cpr_magic,
+                             a.fp4 != 0);
   RGT_STAMP(a.trace, 9);
 }
 
@@ -424,7 +426,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, Tile t
   }, prefetch);
   RGT_STAMP(a.trace, 1);
   u32 sb = 0;
-  const uint4 codes = mx_quant16_regs(xa, xb, sb);  // all lanes: the scale exchange reads the partner lane
+  const uint4 codes = mx_quant16_fmt(xa, xb, sb, a.fp4 != 0);  // all lanes: the scale exchange reads the partner lane
   __syncthreads();  // the tile's LDS is reused below
   RGT_STAMP(a.trace, 4);
   fused_tail<NV>(a, smem, tag, have_unit, unit, codes, sb);

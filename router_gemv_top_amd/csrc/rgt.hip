@@ -285,7 +285,7 @@ void launch_gate(const float* logits, const float* bias, int m, int n, int k, in
 // Sort + quant as separate launches. Returns the number of launches.
 int launch_sort_quant(const int32_t* ids, const uint16_t* x, int64_t ldx, int m, int n, int k, int topk, int block,
                       int32_t* sorted_ids, int32_t* expert_ids, int32_t* offsets, uint8_t* a_q, uint8_t* a_scale,
-                      char* ws, const Layout& L, hipStream_t st) {
+                      bool fp4, char* ws, const Layout& L, hipStream_t st) {
   const int P = m * topk;
   int32_t* pos = reinterpret_cast<int32_t*>(ws + L.pos);
   int launches = 0;
@@ -309,7 +309,7 @@ int launch_sort_quant(const int32_t* ids, const uint16_t* x, int64_t ldx, int m,
   }
   const int units = m * (k / 16);
   hipLaunchKernelGGL(quant_kernel, dim3((units + 255) / 256), dim3(256), 0, st, x, ldx, m, k, topk, pos, a_q,
-                     a_scale);
+                     a_scale, fp4 ? 1 : 0);
   return launches + 1;
 }
 
@@ -477,9 +477,10 @@ static rgt_status check_sort_args(const void* x, int64_t ldx, int m, int n, int 
   return RGT_OK;
 }
 
-rgt_status rgt_moe_sort_quant(const int32_t* topk_ids, const void* x, int64_t ldx, int m, int n, int k, int topk,
-                              int block, int32_t* sorted_ids, int32_t* expert_ids, int32_t* offsets, uint8_t* a_q,
-                              uint8_t* a_scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+static rgt_status moe_sort_quant_impl(const int32_t* topk_ids, const void* x, int64_t ldx, int m, int n, int k,
+                                      int topk, int block, int32_t* sorted_ids, int32_t* expert_ids,
+                                      int32_t* offsets, uint8_t* a_q, uint8_t* a_scale, bool fp4, void* ws,
+                                      size_t ws_bytes, hipStream_t stream) {
   g_last_launches = 0;
   rgt_status st = check_sort_args(x, ldx, m, n, k, topk, block, sorted_ids, expert_ids, offsets, a_q, a_scale);
   if (st != RGT_OK || m == 0) return st;
@@ -487,15 +488,30 @@ rgt_status rgt_moe_sort_quant(const int32_t* topk_ids, const void* x, int64_t ld
   const Layout L = make_layout(m, n, k, topk);
   if ((st = check_ws(ws, ws_bytes, L.total)) != RGT_OK) return st;
   g_last_launches = launch_sort_quant(topk_ids, static_cast<const uint16_t*>(x), ldx, m, n, k, topk, block,
-                                      sorted_ids, expert_ids, offsets, a_q, a_scale, static_cast<char*>(ws), L,
+                                      sorted_ids, expert_ids, offsets, a_q, a_scale, fp4, static_cast<char*>(ws), L,
                                       stream);
   return launched();
 }
 
-rgt_status rgt_route_sort_quant(const void* x, int64_t ldx, const void* w, int64_t ldw, const float* bias, int m,
-                                int n, int k, int topk, int block, float* logits, int32_t* topk_ids, float* topk_w,
-                                int32_t* sorted_ids, int32_t* expert_ids, int32_t* offsets, uint8_t* a_q,
-                                uint8_t* a_scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+rgt_status rgt_moe_sort_quant(const int32_t* topk_ids, const void* x, int64_t ldx, int m, int n, int k, int topk,
+                              int block, int32_t* sorted_ids, int32_t* expert_ids, int32_t* offsets, uint8_t* a_q,
+                              uint8_t* a_scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return moe_sort_quant_impl(topk_ids, x, ldx, m, n, k, topk, block, sorted_ids, expert_ids, offsets, a_q, a_scale,
+                             false, ws, ws_bytes, stream);
+}
+
+rgt_status rgt_moe_sort_quant_mxfp4(const int32_t* topk_ids, const void* x, int64_t ldx, int m, int n, int k,
+                                    int topk, int block, int32_t* sorted_ids, int32_t* expert_ids, int32_t* offsets,
+                                    uint8_t* a_q, uint8_t* a_scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return moe_sort_quant_impl(topk_ids, x, ldx, m, n, k, topk, block, sorted_ids, expert_ids, offsets, a_q, a_scale,
+                             true, ws, ws_bytes, stream);
+}
+
+static rgt_status route_sort_quant_impl(const void* x, int64_t ldx, const void* w, int64_t ldw, const float* bias,
+                                        int m, int n, int k, int topk, int block, float* logits, int32_t* topk_ids,
+                                        float* topk_w, int32_t* sorted_ids, int32_t* expert_ids, int32_t* offsets,
+                                        uint8_t* a_q, uint8_t* a_scale, bool fp4, void* ws, size_t ws_bytes,
+                                        hipStream_t stream) {
   g_last_launches = 0;
   rgt_status st = check_gemv_args(x, ldx, w, ldw, m, n, k);
   if (st != RGT_OK) return st;
@@ -538,7 +554,7 @@ rgt_status rgt_route_sort_quant(const void* x, int64_t ldx, const void* w, int64
   }
   if (fuse) {
     const u32 cpr_magic = 0xFFFFFFFFu / (u32)(k / 16) + 1u;  // exact for unit * (K/16) < 2^32
-    FusedArgs a{g, bias, topk, block, small ? 1 : 0, upw_log, cpr_magic, logits, topk_ids, topk_w, sorted_ids, expert_ids, offsets,
+    FusedArgs a{g, bias, topk, block, small ? 1 : 0, fp4 ? 1 : 0, upw_log, cpr_magic, logits, topk_ids, topk_w, sorted_ids, expert_ids, offsets,
                 a_q, a_scale, reinterpret_cast<u32*>(base + L.ctl), reinterpret_cast<u64*>(base + L.tpart),
                 reinterpret_cast<u64*>(base + L.tids), wait_budget_ticks(), env_int("RGT_FAULT_INJECT", 0),
 #ifdef RGT_TRACE
@@ -555,9 +571,26 @@ rgt_status rgt_route_sort_quant(const void* x, int64_t ldx, const void* w, int64
   launch_router(g, p, stream);
   launch_gate(lg, bias, m, n, topk, topk_ids, topk_w, stream);
   const int nl = launch_sort_quant(topk_ids, static_cast<const uint16_t*>(x), ldx, m, n, k, topk, block, sorted_ids,
-                                   expert_ids, offsets, a_q, a_scale, base, L, stream);
+                                   expert_ids, offsets, a_q, a_scale, fp4, base, L, stream);
   g_last_launches = 2 + nl;
   return launched();
+}
+
+rgt_status rgt_route_sort_quant(const void* x, int64_t ldx, const void* w, int64_t ldw, const float* bias, int m,
+                                int n, int k, int topk, int block, float* logits, int32_t* topk_ids, float* topk_w,
+                                int32_t* sorted_ids, int32_t* expert_ids, int32_t* offsets, uint8_t* a_q,
+                                uint8_t* a_scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return route_sort_quant_impl(x, ldx, w, ldw, bias, m, n, k, topk, block, logits, topk_ids, topk_w, sorted_ids,
+                               expert_ids, offsets, a_q, a_scale, false, ws, ws_bytes, stream);
+}
+
+rgt_status rgt_route_sort_quant_mxfp4(const void* x, int64_t ldx, const void* w, int64_t ldw, const float* bias,
+                                      int m, int n, int k, int topk, int block, float* logits, int32_t* topk_ids,
+                                      float* topk_w, int32_t* sorted_ids, int32_t* expert_ids, int32_t* offsets,
+                                      uint8_t* a_q, uint8_t* a_scale, void* ws, size_t ws_bytes,
+                                      hipStream_t stream) {
+  return route_sort_quant_impl(x, ldx, w, ldw, bias, m, n, k, topk, block, logits, topk_ids, topk_w, sorted_ids,
+                               expert_ids, offsets, a_q, a_scale, true, ws, ws_bytes, stream);
 }
 
 #ifdef RGT_TRACE

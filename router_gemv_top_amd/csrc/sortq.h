@@ -456,13 +456,14 @@ __device__ __forceinline__ void write_sort_outputs(const int* s_e, PosPtr pos, c
 constexpr int kWaveSortMaxP = 2048;
 
 // ---------------------------------------------------------------------------
-// MXFP8 of 16 consecutive bf16 elements (two 16-byte loads). The partner lane
-// (lane ^ 1) holds the other half of the 32-element block. Returns the 16
-// codes packed little-endian in a uint4 and the block's scale byte.
-// Must be called by both lanes of a pair.
+// MX quantisation of 16 consecutive bf16 elements (two 16-byte loads). The
+// partner lane (lane ^ 1) holds the other half of the 32-element block.
+// MXFP8: the 16 e4m3 codes, packed little-endian in a uint4. MXFP4: the 16
+// e2m1 codes two a byte (low nibble first) in .x and .y. Either way the
+// block's scale byte goes to scale_byte. Must be called by both lanes of a
+// pair.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint4 mx_quant16_regs(const uint4& a, const uint4& b, u32& scale_byte) {
-  const u32 w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+__device__ __forceinline__ u32 block_amax16(const u32 (&w)[8]) {
   u32 amax = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -471,15 +472,32 @@ __device__ __forceinline__ uint4 mx_quant16_regs(const uint4& a, const uint4& b,
     amax = hi > amax ? hi : amax;
   }
   const u32 other = dpp_u32<kDppQuadXor1>(amax);  // partner lane (lane ^ 1)
-  amax = other > amax ? other : amax;
-  const int se = mx_shared_exp(amax);
+  return other > amax ? other : amax;
+}
+
+__device__ __forceinline__ uint4 mx_quant16_regs(const uint4& a, const uint4& b, u32& scale_byte) {
+  const u32 w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  const int se = mx_shared_exp(block_amax16(w));
   scale_byte = (u32)(se + 127);
   return make_uint4(e4m3x4_of_bf16(w[0], w[1], se), e4m3x4_of_bf16(w[2], w[3], se), e4m3x4_of_bf16(w[4], w[5], se),
                     e4m3x4_of_bf16(w[6], w[7], se));
 }
 
-__device__ __forceinline__ uint4 mx_quant16(const uint16_t* src, u32& scale_byte) {
-  return mx_quant16_regs(*reinterpret_cast<const uint4*>(src), *reinterpret_cast<const uint4*>(src + 8), scale_byte);
+__device__ __forceinline__ uint4 mx4_quant16_regs(const uint4& a, const uint4& b, u32& scale_byte) {
+  const u32 w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  const int se = mx_shared_exp_e<2>(block_amax16(w));
+  scale_byte = (u32)(se + 127);
+  return make_uint4(e2m1x8_of_bf16(w[0], w[1], w[2], w[3], se), e2m1x8_of_bf16(w[4], w[5], w[6], w[7], se), 0u, 0u);
+}
+
+// fp4 is uniform across the wave (a launch argument).
+__device__ __forceinline__ uint4 mx_quant16_fmt(const uint4& a, const uint4& b, u32& scale_byte, bool fp4) {
+  return fp4 ? mx4_quant16_regs(a, b, scale_byte) : mx_quant16_regs(a, b, scale_byte);
+}
+
+__device__ __forceinline__ uint4 mx_quant16(const uint16_t* src, u32& scale_byte, bool fp4) {
+  return mx_quant16_fmt(*reinterpret_cast<const uint4*>(src), *reinterpret_cast<const uint4*>(src + 8), scale_byte,
+                        fp4);
 }
 
 // Units (16-element chunks) are numbered row-major, one per lane, so lanes
@@ -496,19 +514,23 @@ __device__ __forceinline__ u32 pack_scales(u32 sb) {
 // lanes with u % 8 == 0 also store the packed scales of their 4 blocks. All
 // KMAX >= k positions are read (clamped addresses, no branch between the
 // reads) before the first store, so their latencies overlap.
+// MXFP4 rows are K/2 bytes and a unit's codes 8 bytes.
 template <int KMAX, typename PosPtr>
 __device__ __forceinline__ void store_unit_k(uint8_t* a_q, uint8_t* a_scale, int K, int k, int u, PosPtr pos,
-                                             const uint4& codes, u32 scales4, u32 cpr_magic) {
+                                             const uint4& codes, u32 scales4, u32 cpr_magic, bool fp4) {
   const int cpr = K >> 4;  // 16-element chunks per row
   const int t = cpr_magic ? div_magic(u, cpr_magic) : u / cpr, c = u - t * cpr;
   const int64_t kscale = K >> 5;
+  const int64_t row_bytes = fp4 ? (K >> 1) : K;
   int d[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) d[j] = pos[t * k + min(j, k - 1)];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
     if (j < k && d[j] >= 0) {
-      *reinterpret_cast<uint4*>(a_q + (int64_t)d[j] * K + 16 * c) = codes;
+      uint8_t* row = a_q + (int64_t)d[j] * row_bytes;
+      if (fp4) *reinterpret_cast<uint2*>(row + 8 * c) = make_uint2(codes.x, codes.y);
+      else *reinterpret_cast<uint4*>(row + 16 * c) = codes;
       if ((c & 7) == 0) *reinterpret_cast<u32*>(a_scale + (int64_t)d[j] * kscale + (c >> 1)) = scales4;
     }
   }
@@ -518,10 +540,10 @@ __device__ __forceinline__ void store_unit_k(uint8_t* a_q, uint8_t* a_scale, int
 // u by the chunks per row, or 0.
 template <typename PosPtr>
 __device__ __forceinline__ void store_unit(uint8_t* a_q, uint8_t* a_scale, int K, int k, int u, PosPtr pos,
-                                           const uint4& codes, u32 scales4, u32 cpr_magic = 0) {
-  if (k <= 8) store_unit_k<8>(a_q, a_scale, K, k, u, pos, codes, scales4, cpr_magic);
-  else if (k <= 16) store_unit_k<16>(a_q, a_scale, K, k, u, pos, codes, scales4, cpr_magic);
-  else store_unit_k<32>(a_q, a_scale, K, k, u, pos, codes, scales4, cpr_magic);
+                                           const uint4& codes, u32 scales4, u32 cpr_magic, bool fp4) {
+  if (k <= 8) store_unit_k<8>(a_q, a_scale, K, k, u, pos, codes, scales4, cpr_magic, fp4);
+  else if (k <= 16) store_unit_k<16>(a_q, a_scale, K, k, u, pos, codes, scales4, cpr_magic, fp4);
+  else store_unit_k<32>(a_q, a_scale, K, k, u, pos, codes, scales4, cpr_magic, fp4);
 }
 
 }  // namespace rgt

@@ -153,8 +153,9 @@ __global__ void __launch_bounds__(256) sort_scatter_kernel(const int32_t* ids, i
   }
 }
 
+// fp4: MXFP4 rows (K/2 bytes of packed e2m1 codes), else MXFP8.
 __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* x, int64_t ldx, int M, int K, int k,
-                                                    const int32_t* pos, uint8_t* a_q, uint8_t* a_scale) {
+                                                    const int32_t* pos, uint8_t* a_q, uint8_t* a_scale, int fp4) {
   const int units = M * (K >> 4);
   const int u = blockIdx.x * blockDim.x + threadIdx.x;
   const int cpr = K >> 4;
@@ -162,9 +163,9 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* x, int64_t l
   // so every lane of a pair or group is active together.
   u32 sb = 0;
   uint4 codes = make_uint4(0, 0, 0, 0);
-  if (u < units) codes = mx_quant16(x + (int64_t)(u / cpr) * ldx + 16 * (u % cpr), sb);
+  if (u < units) codes = mx_quant16(x + (int64_t)(u / cpr) * ldx + 16 * (u % cpr), sb, fp4 != 0);
   const u32 s4 = pack_scales(sb);
-  if (u < units) store_unit(a_q, a_scale, K, k, u, pos, codes, s4);
+  if (u < units) store_unit(a_q, a_scale, K, k, u, pos, codes, s4, 0u, fp4 != 0);
 }
 
 }  // namespace rgt

@@ -71,9 +71,11 @@ def check_logits(x_bits, w_bits, got, ref=None):
     return ref
 
 
-def check_sort_quant(out, ids, x_bits, n, block, sample_rows=None):
+def check_sort_quant(out, ids, x_bits, n, block, sample_rows=None, fmt="mxfp8"):
     """Bit-exact comparison of GPU sort/quant buffers with the oracle fed the
-    GPU's own top-k ids. Entries past the padded total must be untouched."""
+    GPU's own top-k ids (fmt "mxfp8" or "mxfp4"). Entries past the padded
+    total must be untouched."""
+    quant = {"mxfp8": O.mxfp8_quant_rows, "mxfp4": O.mxfp4_quant_rows}[fmt]
     m, k = ids.shape
     ref_s, ref_e, ref_off, total = O.moe_sort(ids, n, block)
     off = out["offsets"].cpu().numpy()
@@ -91,7 +93,8 @@ def check_sort_quant(out, ids, x_bits, n, block, sample_rows=None):
     valid = np.nonzero(ref_s != p_total)[0]
     pads = np.nonzero(ref_s == p_total)[0]
     rows = valid if sample_rows is None else valid[sample_rows(len(valid))]
-    q_tok, s_tok = O.mxfp8_quant_rows(x_bits[np.unique(ref_s[rows] // k)])
+    assert a_q.shape[1] == (x_bits.shape[1] if fmt == "mxfp8" else x_bits.shape[1] // 2)
+    q_tok, s_tok = quant(x_bits[np.unique(ref_s[rows] // k)])
     tok_index = {t: i for i, t in enumerate(np.unique(ref_s[rows] // k))}
     for p in rows:
         t = ref_s[p] // k

@@ -24,12 +24,13 @@ def L():
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(rgt_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(rgt_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
     assert len(names) >= 12
+    assert {"rgt_moe_sort_quant_mxfp4", "rgt_route_sort_quant_mxfp4"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -94,8 +95,9 @@ def test_gate_argument_errors(L):
     assert f(FAKE, FAKE + 1, 4, 128, 8, FAKE, FAKE, None) == 2
 
 
-def test_sort_quant_argument_errors(L):
-    f = L.rgt_moe_sort_quant
+@pytest.mark.parametrize("entry", ["rgt_moe_sort_quant", "rgt_moe_sort_quant_mxfp4"])
+def test_sort_quant_argument_errors(L, entry):
+    f = getattr(L, entry)
     ok = dict(ids=FAKE, x=FAKE, ldx=6144, m=4, n=128, k=6144, topk=8, block=16, s=FAKE, e=FAKE, o=FAKE,
               q=FAKE, sc=FAKE, ws=FAKE, wsb=1 << 30)
 
@@ -113,8 +115,9 @@ def test_sort_quant_argument_errors(L):
     assert call(wsb=100) == 3
 
 
-def test_route_sort_quant_argument_errors(L):
-    f = L.rgt_route_sort_quant
+@pytest.mark.parametrize("entry", ["rgt_route_sort_quant", "rgt_route_sort_quant_mxfp4"])
+def test_route_sort_quant_argument_errors(L, entry):
+    f = getattr(L, entry)
 
     def call(x=FAKE, w=FAKE, bias=None, m=4, n=128, k=6144, topk=8, block=16, logits=None, ids=FAKE,
              tw=FAKE, ws=FAKE, wsb=1 << 30):

@@ -201,3 +201,78 @@ def test_fused_wait_deadline_sets_error_and_reset_recovers(R, monkeypatch):
     fo = np_out(f)
     ids = check_against_oracle(x, w, b, wl.topk, wl.block, fo)
     check_sort_quant(sort_out(fo), ids, x, wl.n, wl.block)
+
+
+# MXFP4 (rgt_route_sort_quant_mxfp4): the M3.1 decode point (128 experts,
+# top-4, hidden 6144) over the decode sweep, a ragged M, the many-expert shape
+# with bias, and a wide batch (launch chain).
+FP4 = ([Workload(f"m31_fp4_M{m}", m, 128, 6144, 4, 16) for m in (1, 2, 4, 8, 16, 32, 64)] +
+       [Workload("m31_fp4_ragged_M13", 13, 128, 6144, 4, 16),
+        Workload("n896_fp4_k16_bias_M8", 8, 896, 3584, 16, 16, bias=True),
+        Workload("m31_fp4_wide_M256", 256, 128, 6144, 4, 32)])
+
+
+@pytest.mark.parametrize("wl", FP4, ids=lambda w: w.name)
+def test_fused_mxfp4_matches_chain_and_oracle(R, wl):
+    say(f"fused mxfp4 {wl.name} M={wl.m} N={wl.n} K={wl.k} k={wl.topk} B={wl.block}")
+    x, w, b = wl.make()
+    m, n, kdim, k, block = wl.m, wl.n, wl.k, wl.topk, wl.block
+    ws = R.Workspace(m, n, kdim, k, block)
+    out = R.alloc_sort_outputs(m, n, kdim, k, block, fill=CANARY, fmt="mxfp4")
+    out["topk_ids"] = torch.empty((m, k), dtype=torch.int32, device="cuda")
+    out["topk_w"] = torch.empty((m, k), dtype=torch.float32, device="cuda")
+    out["logits"] = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    bd = None if b is None else to_dev(b)
+    xd, wd = to_dev_bf16(x), to_dev_bf16(w)
+    R.route_sort_quant_mxfp4(xd, wd, k, block, ws, bias=bd, out=out)
+    launches = R.last_launch_count()
+    torch.cuda.synchronize()
+    if m <= 64:
+        assert launches == 1, "decode sizes must run as one launch"
+    fo = np_out(out)
+    # the unfused chain with the standalone MXFP4 sort+quant
+    logits = R.router_logits(xd, wd, ws)
+    ids, tw = R.topk_gate(logits, k, bias=bd)
+    c = R.alloc_sort_outputs(m, n, kdim, k, block, fill=CANARY, fmt="mxfp4")
+    R.moe_sort_quant_mxfp4(ids, xd, n, block, ws, out=c)
+    torch.cuda.synchronize()
+    c = np_out(c)
+    np.testing.assert_array_equal(fo["logits"].view(np.uint32), logits.cpu().numpy().view(np.uint32))
+    np.testing.assert_array_equal(fo["topk_ids"], ids.cpu().numpy())
+    np.testing.assert_array_equal(fo["topk_w"].view(np.uint32), tw.cpu().numpy().view(np.uint32))
+    np.testing.assert_array_equal(fo["offsets"], c["offsets"])
+    total = int(fo["offsets"][-1])
+    for key in ("sorted_ids", "a_q", "a_scale"):
+        np.testing.assert_array_equal(fo[key][:total], c[key][:total], err_msg=key)
+    rid = check_against_oracle(x, w, b, k, block, fo)
+    rng = np.random.default_rng(5)
+    sample = None if m * k <= 4096 else (lambda nv: rng.choice(nv, size=min(nv, 600), replace=False))
+    check_sort_quant(sort_out(fo), rid, x, n, block, sample_rows=sample, fmt="mxfp4")
+    assert_workspace_ready(ws)
+
+
+def test_fused_formats_share_routing(R):
+    """MXFP8 and MXFP4 calls on one workspace, alternating: the routing
+    outputs agree and each call's codes match its own format's oracle."""
+    say("fused mxfp8/mxfp4 alternating on one workspace")
+    wl = Workload("alt_M16", 16, 128, 6144, 4, 16)
+    x, w, _ = wl.make()
+    ws = R.Workspace(wl.m, wl.n, wl.k, wl.topk, wl.block)
+    o8, _ = fused(R, x, w, None, wl.topk, wl.block, ws)
+    o4 = R.alloc_sort_outputs(wl.m, wl.n, wl.k, wl.topk, wl.block, fill=CANARY, fmt="mxfp4")
+    o4["topk_ids"] = torch.empty((wl.m, wl.topk), dtype=torch.int32, device="cuda")
+    o4["topk_w"] = torch.empty((wl.m, wl.topk), dtype=torch.float32, device="cuda")
+    o4["logits"] = torch.empty((wl.m, wl.n), dtype=torch.float32, device="cuda")
+    R.route_sort_quant_mxfp4(to_dev_bf16(x), to_dev_bf16(w), wl.topk, wl.block, ws, out=o4)
+    o8b, _ = fused(R, x, w, None, wl.topk, wl.block, ws)
+    torch.cuda.synchronize()
+    o8, o4, o8b = np_out(o8), np_out(o4), np_out(o8b)
+    for key in ("topk_ids", "offsets", "sorted_ids"):
+        t = int(o8["offsets"][-1])
+        np.testing.assert_array_equal(o8[key][:t] if key == "sorted_ids" else o8[key],
+                                      o4[key][:t] if key == "sorted_ids" else o4[key])
+        np.testing.assert_array_equal(o8b[key][:t] if key == "sorted_ids" else o8b[key],
+                                      o8[key][:t] if key == "sorted_ids" else o8[key])
+    ids = check_against_oracle(x, w, None, wl.topk, wl.block, o4)
+    check_sort_quant(sort_out(o4), ids, x, wl.n, wl.block, fmt="mxfp4")
+    check_sort_quant(sort_out(o8b), ids, x, wl.n, wl.block, fmt="mxfp8")

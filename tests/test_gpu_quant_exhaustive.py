@@ -1,8 +1,9 @@
-"""MXFP8 encoder over its whole input space: every finite bf16 value, placed
-in blocks whose largest element sets the shared exponent 0 to 17 binades above
-the value's own (saturation, every normal and subnormal e4m3 binade, and
-rounding to zero), quantised on the GPU through
-rgt_moe_sort_quant and compared bit for bit with the oracle."""
+"""MXFP8 and MXFP4 encoders over their whole input space: every finite bf16
+value, placed in blocks whose largest element sets the shared exponent 0 to 17
+binades above the value's own (saturation, every normal and subnormal element
+binade, and rounding to zero), quantised on the GPU through
+rgt_moe_sort_quant / rgt_moe_sort_quant_mxfp4 and compared bit for bit with
+the oracle."""
 import numpy as np
 import pytest
 
@@ -84,4 +85,29 @@ def test_mxfp8_encoder_every_bf16():
         raise AssertionError(f"{len(bad)} codes differ; first row {r} col {c}: bf16 0x{x[r, c]:04x} "
                              f"block max 0x{x[r, c - c % BLOCK]:04x} got 0x{got_q[r, c]:02x} "
                              f"want 0x{codes[r, c]:02x}")
+    np.testing.assert_array_equal(got_s, scales)
+
+
+def test_mxfp4_encoder_every_bf16():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import router_gemv_top_amd as R
+    x = exhaustive_rows(seed=1)
+    m = x.shape[0]
+    say(f"exhaustive MXFP4: {m} rows x {K}")
+    n, topk, block = 16, 1, 16
+    ids = np.zeros((m, topk), dtype=np.int32)       # every token to expert 0: a_q row p = token p
+    ws = R.Workspace(m, n, K, topk, block)
+    out = R.moe_sort_quant_mxfp4(to_dev(ids), to_dev_bf16(x), n, block, ws)
+    torch.cuda.synchronize()
+    packed, scales = O.mxfp4_quant_rows(x)
+    got_q = out["a_q"][:m].cpu().numpy()
+    got_s = out["a_scale"][:m].cpu().numpy()
+    assert got_q.shape == packed.shape
+    bad = np.argwhere(got_q != packed)
+    if bad.size:
+        r, c = bad[0]
+        raise AssertionError(f"{len(bad)} bytes differ; first row {r} byte {c}: bf16 0x{x[r, 2 * c]:04x} "
+                             f"0x{x[r, 2 * c + 1]:04x} block max 0x{x[r, 2 * c - 2 * c % BLOCK]:04x} "
+                             f"got 0x{got_q[r, c]:02x} want 0x{packed[r, c]:02x}")
     np.testing.assert_array_equal(got_s, scales)

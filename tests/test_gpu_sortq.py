@@ -1,6 +1,6 @@
-"""GPU parity of the expert sort + MXFP8 quant (rgt_moe_sort_quant): bit-exact
-against the oracle fed the same top-k ids; nothing written past the padded
-total or into pad rows."""
+"""GPU parity of the expert sort + MX quant (rgt_moe_sort_quant for MXFP8,
+rgt_moe_sort_quant_mxfp4 for MXFP4): bit-exact against the oracle fed the same
+top-k ids; nothing written past the padded total or into pad rows."""
 import numpy as np
 import pytest
 
@@ -26,12 +26,13 @@ def random_ids(m, n, k, seed, hot=None):
     return np.stack([rng.choice(pool, size=k, replace=False) for _ in range(m)]).astype(np.int32)
 
 
-def run(R, ids, x, n, block):
+def run(R, ids, x, n, block, fmt="mxfp8"):
     m, kdim = x.shape
     k = ids.shape[1]
     ws = R.Workspace(m, n, kdim, k, block)
-    out = R.alloc_sort_outputs(m, n, kdim, k, block, fill=CANARY)
-    R.moe_sort_quant(to_dev(ids), to_dev_bf16(x), n, block, ws, out=out)
+    out = R.alloc_sort_outputs(m, n, kdim, k, block, fill=CANARY, fmt=fmt)
+    fn = R.moe_sort_quant if fmt == "mxfp8" else R.moe_sort_quant_mxfp4
+    fn(to_dev(ids), to_dev_bf16(x), n, block, ws, out=out)
     torch.cuda.synchronize()
     return out
 
@@ -79,3 +80,40 @@ def test_sort_quant_prefill_size(R):
     out = run(R, ids, x, n, block)
     rng = np.random.default_rng(1)
     check_sort_quant(out, ids, x, n, block, sample_rows=lambda nv: rng.choice(nv, size=800, replace=False))
+
+
+# MXFP4: the M3.1 point (128 experts, top-4, hidden 6144) over decode and
+# wide batches, the many-expert shape, the multi-workgroup sort, and a ragged
+# small shape.
+CASES_FP4 = [
+    (1, 128, 6144, 4, 16, None), (8, 128, 6144, 4, 16, None), (64, 128, 6144, 4, 16, None),
+    (1024, 128, 6144, 4, 32, None), (3, 16, 512, 4, 64, None), (32, 896, 3584, 16, 16, None),
+    (2048, 128, 1024, 8, 64, 8),
+]
+
+
+@pytest.mark.parametrize("m,n,kdim,k,block,hot", CASES_FP4)
+def test_sort_quant_mxfp4_parity(R, m, n, kdim, k, block, hot):
+    say(f"sort_quant_mxfp4 M={m} N={n} K={kdim} k={k} B={block} hot={hot}")
+    ids = random_ids(m, n, k, seed=m + n + 7, hot=hot)
+    x = gen_x(m, kdim, seed=m + 7)
+    out = run(R, ids, x, n, block, fmt="mxfp4")
+    rng = np.random.default_rng(2)
+    sample = None if m * k <= 4096 else (lambda nv: rng.choice(nv, size=min(nv, 600), replace=False))
+    check_sort_quant(out, ids, x, n, block, sample_rows=sample, fmt="mxfp4")
+
+
+def test_sort_quant_mxfp4_special_values(R):
+    say("sort_quant_mxfp4 with zero, tiny, huge, negative-zero and tie blocks")
+    m, n, kdim, k, block = 4, 16, 512, 2, 16
+    x = gen_x(m, kdim, seed=5)
+    x[0, :32] = 0x0000
+    x[0, 32:64] = 0x8000                      # -0 block
+    x[1, :32] = 0x0001                        # smallest subnormal
+    x[1, 40] = 0x7F7F                         # largest finite bf16
+    x[2, 64:96] = 0x3F80                      # all 1.0
+    x[3, 96:128] = np.array([0x40E0] * 32)    # 7.0: ties past 6, saturating
+    x[3, 128:160] = np.array([0x4080, 0x3E80, 0x3F40, 0x3FA0, 0x3FE0, 0x4020, 0x4060, 0x40A0] * 4)  # midpoints
+    ids = random_ids(m, n, k, seed=6)
+    out = run(R, ids, x, n, block, fmt="mxfp4")
+    check_sort_quant(out, ids, x, n, block, fmt="mxfp4")
