@@ -16,8 +16,9 @@ Prints ONE JSON line: value = algorithmic bytes of the K steps / their time
 (GB/s), the per-M microseconds per call, the roofline of the dominant kernel
 and the CPU oracle's rate on a bounded sample. Secondary figures ride along
 in the same line: the resident-W (hot) times, the wide-batch and many-expert
-shapes, the prefill call with its router GEMM against the bf16 MFMA peak, and
-the host cost of one eager call.
+shapes, the MXFP4 variant at the 128-expert top-4 point, the prefill call with
+its router GEMM against the bf16 MFMA peak, and the host cost of one eager
+call.
 """
 from __future__ import annotations
 
@@ -97,21 +98,25 @@ def secondary(torch, R, dev, stream, copies_128: int):
     """The other routing shapes, timed like the headline sweep (graph replay,
     cold W by rotating copies), plus the prefill router GEMM alone against the
     bf16 MFMA peak and the host cost of one eager call."""
-    from router_gemv_top_amd.inputs import workloads_wide_128, workloads_decode_896, workload_prefill_896
+    from router_gemv_top_amd.inputs import (workloads_wide_128, workloads_decode_896, workload_prefill_896,
+                                            workloads_decode_128_top4)
 
     def dev_bf16(a):
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
 
-    def outputs(wl, logits=False):
-        o = R.alloc_sort_outputs(wl.m, wl.n, wl.k, wl.topk, wl.block, device=dev)
+    def outputs(wl, logits=False, fmt="mxfp8"):
+        o = R.alloc_sort_outputs(wl.m, wl.n, wl.k, wl.topk, wl.block, device=dev, fmt=fmt)
         o["topk_ids"] = torch.empty((wl.m, wl.topk), dtype=torch.int32, device=dev)
         o["topk_w"] = torch.empty((wl.m, wl.topk), dtype=torch.float32, device=dev)
         o["logits"] = torch.empty((wl.m, wl.n), dtype=torch.float32, device=dev) if logits else None
         return o
 
     res = {}
-    for group, wls in (("wide_N128_K6144_top8_B32", workloads_wide_128()),
-                       ("decode_N896_K3584_top16_bias_B16", workloads_decode_896())):
+    for group, wls, fmt in (("wide_N128_K6144_top8_B32", workloads_wide_128(), "mxfp8"),
+                            ("decode_N896_K3584_top16_bias_B16", workloads_decode_896(), "mxfp8"),
+                            ("mxfp4_decode_N128_K6144_top4_B16", workloads_decode_128_top4(), "mxfp4")):
+        entry = R.route_sort_quant if fmt == "mxfp8" else R.route_sort_quant_mxfp4
+        q_bytes_per_elem = 1.0 if fmt == "mxfp8" else 0.5
         x, w, b = wls[0].make()
         w_bytes = w.size * 2
         copies = min(copies_128, int(np.ceil(2 * MALL_BYTES / w_bytes)))
@@ -121,15 +126,15 @@ def secondary(torch, R, dev, stream, copies_128: int):
         for wl in wls:
             xw = dev_bf16(wl.make()[0]).unsqueeze(0).repeat(copies, 1, 1)
             ws = R.Workspace(wl.m, wl.n, wl.k, wl.topk, wl.block, device=dev)
-            o = outputs(wl)
-            us = _graph_us(torch, stream, copies, lambda i: R.route_sort_quant(
+            o = outputs(wl, fmt=fmt)
+            us = _graph_us(torch, stream, copies, lambda i: entry(
                 xw[i], w_all[i], wl.topk, wl.block, ws, bias=bias, out=o))
             if ws.check() != 0:
                 raise RuntimeError(f"device-side wait timed out ({wl.name})")
             total = int(o["offsets"][-1].item())
             p = wl.m * wl.topk
             nbytes = (wl.n * wl.k * 2 + wl.m * wl.k * 2 + p * 8 + total * 4 + (total // wl.block) * 4 +
-                      (wl.n + 1) * 4 + p * wl.k + p * (wl.k // 32))
+                      (wl.n + 1) * 4 + int(p * wl.k * q_bytes_per_elem) + p * (wl.k // 32))
             per[str(wl.m)] = {"us": round(us, 3), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
                               "launches": R.last_launch_count()}
             del xw

@@ -139,3 +139,10 @@ def workloads_decode_896(ms=(1, 4, 8, 16, 32)):
 def workload_prefill_896(m: int = 8192):
     """Prefill-sized routing: N=896, K=3584, top-16, block 64, 5% duplicate tokens."""
     return Workload(f"k3_prefill_M{m}", m, 896, 3584, 16, 64, dup_frac=0.05)
+
+
+def workloads_decode_128_top4(ms=(1, 2, 4, 8, 16, 32, 64)):
+    """The 128-expert, top-4, hidden-6144 decode point whose sort carries the
+    stage-1 MXFP4 activation quant (MiniMax-M3.1-Flash MoE/GEMM kernels,
+    "Changes to existing kernels"); same input recipe as the top-8 sweep."""
+    return [Workload(f"decode_top4_M{m}", m, 128, 6144, 4, 16) for m in ms]
