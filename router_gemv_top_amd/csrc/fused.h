@@ -13,21 +13,28 @@
 //      of their rows and sum them in k-slice order, which gives the same bits
 //      as the last-arriver fixup of the standalone router;
 //   2. the softmax top-k gate. Small mode (all rows' partials fit one poll
-//      per thread): workgroup 0 and every workgroup that owns a quant chunk
-//      gather every row and run the gate themselves, so no further hand-off
-//      is needed. Large mode: workgroup r gathers row r, runs its gate and
-//      publishes the ids as tagged words, which the others poll;
+//      per thread): every workgroup that owns a quant chunk, the layout
+//      workgroup and the gate workgroup gather every row and run the gate
+//      themselves, so no further hand-off is needed. Large mode: workgroup r
+//      gathers row r, runs its gate and publishes the ids as tagged words,
+//      which the others poll;
 //   3. the same workgroups sort the M*k pairs in LDS with one wave (tiny at
 //      decode sizes, so redundant sorting beats another hand-off) and store
 //      their MXFP8 or MXFP4 chunk (quantised in registers while waiting) to
-//      the padded rows of the token's pairs; workgroup 0 also writes topk_ids, topk_w,
-//      logits, sorted_ids, expert_ids and offsets and advances the call epoch.
+//      the padded rows of the token's pairs and their sorted_ids entries;
+//      the layout workgroup writes offsets, expert_ids and the pads.
+//
+// topk_ids, topk_w and the logits come from the gate workgroup in small mode
+// (the first one past the layout workgroup, so the fp64 weights stay off the
+// path of the workgroups that store; workgroup 0 if the grid has no spare)
+// and from workgroup r for row r in large mode.
 //
 // A tagged word is a 32-bit payload plus the tag (epoch + 1) of the call that
 // wrote it, stored as one 8-byte store; readers poll the words themselves, so
 // no hand-off needs a counter. Every wave reads the epoch before it loads its
-// tile; workgroup 0 advances it only after it has seen every partial (small
-// mode) or every id (large mode), which implies that every wave has read it.
+// tile; the gate workgroup advances it only after it has seen every partial
+// (small mode), workgroup 0 only after every id (large mode), which implies
+// that every wave has read it.
 // Every wait is bounded by a deadline that sets the workspace error word.
 #pragma once
 
@@ -96,10 +103,12 @@ constexpr int kPollLoads = 16;
 // one row: item it of the gathered rows sits at byte 16*it of every k-slice
 // and lands at s_log[2*it]. Thread t takes items t, t + 256, ... and their S
 // slices, nl <= NL loads in all (a thread with fewer items repeats its last
-// one). Each thread polls its own loads until every word carries the tag (two
-// polls in flight, so a hand-off is seen about one memory round trip after it
-// lands), then sums each item's slices in k-slice order. Returns false (error
-// word set) if the deadline passes.
+// one). Each thread polls its own loads until every word carries the tag,
+// re-issuing them as soon as they return short of it (one poll in flight: a
+// second poll issued with the first sees the same memory state, and the loads
+// it leaves in flight at the exit cost a wait at the next register reuse),
+// then sums each item's slices in k-slice order. Returns false (error word
+// set) if the deadline passes.
 template <int NL>
 __device__ __forceinline__ bool gather_logits(const FusedArgs& a, int r0, int rows, u32 tag, float* s_log) {
   __shared__ u32 s_bad;
@@ -150,9 +159,8 @@ __device__ __forceinline__ bool gather_logits(const FusedArgs& a, int r0, int ro
       }
     };
     const u64 t0 = rt_clock();
-    u32x4_t va[NL], vb[NL];
+    u32x4_t va[NL];
     issue(va);
-    issue(vb);
 #ifdef RGT_TRACE
     int polls = 0;
 #endif
@@ -162,8 +170,6 @@ __device__ __forceinline__ bool gather_logits(const FusedArgs& a, int r0, int ro
 #endif
       if (ready(va)) { take(va); break; }
       issue(va);
-      if (ready(vb)) { take(vb); break; }
-      issue(vb);
       if (rt_clock() - t0 > a.budget) {
         set_timeout(a);
         s_bad = 1u;
@@ -230,14 +236,11 @@ __device__ __forceinline__ bool poll_ids(const FusedArgs& a, int P, u32 tag, int
       }
     };
     const u64 t0 = rt_clock();
-    u32x4_t va[NL], vb[NL];
+    u32x4_t va[NL];
     issue(va);
-    issue(vb);
     for (;;) {
       if (ready(va)) { take(va); break; }
       issue(va);
-      if (ready(vb)) { take(vb); break; }
-      issue(vb);
       if (rt_clock() - t0 > a.budget) {
         set_timeout(a);
         s_bad = 1u;
@@ -294,7 +297,13 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
   const int n_layout = (n + 255) >> 8;
   const int layout_wg = min((int)gridDim.x - n_layout, ((units - 1) >> a.upw_log) + 1);
   const int li = (int)blockIdx.x - layout_wg;  // this workgroup's layout share, if 0 <= li < n_layout
-  const bool participant = blockIdx.x == 0 || ((int)blockIdx.x << a.upw_log) < units || (li >= 0 && li < n_layout);
+  // Small mode: the gate workgroup (topk_ids, topk_w, logits, epoch) is the
+  // first one past the layout workgroups if the grid has it, else 0.
+  const int q_wgs = ((units - 1) >> a.upw_log) + 1;
+  const int gate_wg = (a.small && layout_wg + n_layout < (int)gridDim.x) ? layout_wg + n_layout : 0;
+  const bool gate_here = (int)blockIdx.x == gate_wg;
+  const bool quant_wg = (int)blockIdx.x < q_wgs;
+  const bool participant = gate_here || quant_wg || (li >= 0 && li < n_layout);
   const int P = m * k;
   int* s_e = smem;
   u32* s_key = reinterpret_cast<u32*>(s_e + P);
@@ -328,7 +337,7 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
         s_e[row * k + lane] = id;
         s_key[row * k + lane] = key;
         hist_add(id, row * k + lane, p0, n, s_cnt, s_pre);
-        if (blockIdx.x == 0) a.topk_ids[row * k + lane] = id;
+        if (gate_here) a.topk_ids[row * k + lane] = id;
       }
     };
     for (int row = wave; row < m; row += 4) {
@@ -338,9 +347,15 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
       row_select<NV, 1>(a, rows, id, key);
       keep(row, id[0], key[0]);
     }
-    if (blockIdx.x == 0 && a.logits_out)
+    if (gate_here && a.logits_out)
       for (int i = threadIdx.x; i < m * n; i += 256) a.logits_out[i] = s_log[i];
     __syncthreads();
+    if (gate_here && gate_wg != 0) {
+      // Every partial has been seen, so every wave has read the epoch.
+      if (threadIdx.x == 0) st_agent(a.ctl + kCtlEpoch, tag);
+      rows_weights(a, s_key, wave, 4);
+      return;
+    }
     RGT_STAMP(a.trace, 6);
   } else {
     // Step 2 (large): workgroup r gathers row r, runs its gate and publishes
@@ -372,15 +387,16 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
   }
   RGT_STAMP(a.trace, 7);
   // Every wave of the grid has read the epoch (see the top of this file):
-  // advance it for the next call.
-  if (blockIdx.x == 0 && threadIdx.x == 0) st_agent(a.ctl + kCtlEpoch, tag);
+  // advance it for the next call (large mode, or small mode without a spare
+  // gate workgroup).
+  if (gate_here && threadIdx.x == 0) st_agent(a.ctl + kCtlEpoch, tag);
   // Step 3: positions of the pairs of this workgroup's tokens (a counting
   // sort from the expert histogram), then the workgroup stores its quantised
   // chunk to the padded rows of those pairs. The token's pairs' sorted_ids
   // entries are written by the workgroup holding its first quant unit; the
   // layout workgroup writes offsets, expert_ids and the pads.
   if (threadIdx.x < 64) pair_positions<NV>(P, n, a.block, p0, p1, s_e, s_cnt, s_pre, s_off, s_pos);
-  else if (a.small && blockIdx.x == 0) rows_weights(a, s_key, wave - 1, 3);  // while wave 0 works
+  else if (a.small && gate_here) rows_weights(a, s_key, wave - 1, 3);  // while wave 0 works
   __syncthreads();
   RGT_STAMP(a.trace, 8);
   if (li >= 0 && li < n_layout)

@@ -510,40 +510,51 @@ __device__ __forceinline__ u32 pack_scales(u32 sb) {
   return (sb & 0xffu) | ((s2 & 0xffu) << 8) | ((s4 & 0xffu) << 16) | ((s6 & 0xffu) << 24);
 }
 
-// Store unit u's 16 codes to the padded rows pos[t*k + j] of its token's pairs;
+// Store unit u's codes to the padded rows pos[t*k + j] of its token's pairs;
 // lanes with u % 8 == 0 also store the packed scales of their 4 blocks. All
 // KMAX >= k positions are read (clamped addresses, no branch between the
-// reads) before the first store, so their latencies overlap.
-// MXFP4 rows are K/2 bytes and a unit's codes 8 bytes.
-template <int KMAX, typename PosPtr>
-__device__ __forceinline__ void store_unit_k(uint8_t* a_q, uint8_t* a_scale, int K, int k, int u, PosPtr pos,
-                                             const uint4& codes, u32 scales4, u32 cpr_magic, bool fp4) {
-  const int cpr = K >> 4;  // 16-element chunks per row
-  const int t = cpr_magic ? div_magic(u, cpr_magic) : u / cpr, c = u - t * cpr;
-  const int64_t kscale = K >> 5;
-  const int64_t row_bytes = fp4 ? (K >> 1) : K;
+// reads) before the first store, so their latencies overlap. Row offsets are
+// one 32 x 32 -> 64-bit product each. MXFP4 rows are K/2 bytes and a unit's
+// codes 8 bytes.
+template <int KMAX, bool FP4, typename PosPtr>
+__device__ __forceinline__ void store_unit_kf(uint8_t* a_q, uint8_t* a_scale, int K, int k, int t, int c,
+                                              PosPtr pos, const uint4& codes, u32 scales4) {
+  const u32 row_bytes = FP4 ? (u32)K >> 1 : (u32)K;
+  const u32 kscale = (u32)K >> 5;
+  uint8_t* q_col = a_q + (FP4 ? 8 * c : 16 * c);
+  uint8_t* s_col = a_scale + (c >> 1);
+  const bool lead = (c & 7) == 0;
   int d[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) d[j] = pos[t * k + min(j, k - 1)];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
     if (j < k && d[j] >= 0) {
-      uint8_t* row = a_q + (int64_t)d[j] * row_bytes;
-      if (fp4) *reinterpret_cast<uint2*>(row + 8 * c) = make_uint2(codes.x, codes.y);
-      else *reinterpret_cast<uint4*>(row + 16 * c) = codes;
-      if ((c & 7) == 0) *reinterpret_cast<u32*>(a_scale + (int64_t)d[j] * kscale + (c >> 1)) = scales4;
+      const u32 r = (u32)d[j];
+      uint8_t* row = q_col + (uint64_t)r * row_bytes;
+      if (FP4) *reinterpret_cast<uint2*>(row) = make_uint2(codes.x, codes.y);
+      else *reinterpret_cast<uint4*>(row) = codes;
+      if (lead) *reinterpret_cast<u32*>(s_col + (uint64_t)r * kscale) = scales4;
     }
   }
 }
 
 // cpr_magic: ceil(2^32 / (K/16)) for a multiply in place of the division of
-// u by the chunks per row, or 0.
+// u by the chunks per row, or 0. fp4 is uniform across the wave.
 template <typename PosPtr>
 __device__ __forceinline__ void store_unit(uint8_t* a_q, uint8_t* a_scale, int K, int k, int u, PosPtr pos,
                                            const uint4& codes, u32 scales4, u32 cpr_magic, bool fp4) {
-  if (k <= 8) store_unit_k<8>(a_q, a_scale, K, k, u, pos, codes, scales4, cpr_magic, fp4);
-  else if (k <= 16) store_unit_k<16>(a_q, a_scale, K, k, u, pos, codes, scales4, cpr_magic, fp4);
-  else store_unit_k<32>(a_q, a_scale, K, k, u, pos, codes, scales4, cpr_magic, fp4);
+  const int cpr = K >> 4;  // 16-element chunks per row
+  const int t = cpr_magic ? div_magic(u, cpr_magic) : u / cpr, c = u - t * cpr;
+  if (fp4) {
+    if (k <= 8) store_unit_kf<8, true>(a_q, a_scale, K, k, t, c, pos, codes, scales4);
+    else if (k <= 16) store_unit_kf<16, true>(a_q, a_scale, K, k, t, c, pos, codes, scales4);
+    else store_unit_kf<32, true>(a_q, a_scale, K, k, t, c, pos, codes, scales4);
+  } else {
+    if (k <= 8) store_unit_kf<8, false>(a_q, a_scale, K, k, t, c, pos, codes, scales4);
+    else if (k <= 16) store_unit_kf<16, false>(a_q, a_scale, K, k, t, c, pos, codes, scales4);
+    else store_unit_kf<32, false>(a_q, a_scale, K, k, t, c, pos, codes, scales4);
+  }
 }
 
 }  // namespace rgt
