@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -37,6 +38,7 @@ constexpr int kLargeSortChunk = 512;       // pairs per workgroup in the large s
 constexpr int kFusedMaxM = 64;
 
 thread_local int g_last_launches = 0;
+std::atomic<bool> g_sort_lds_set{false};  // the one-workgroup sort may use more than 64 KB of LDS
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -172,7 +174,7 @@ Layout make_layout(int m, int n, int k, int topk) {
   L.pos = o; o = align_up(o + sizeof(int32_t) * (size_t)P, kAlign);
   L.ghist = o;
   if (P > kSmallSortMaxP) o = align_up(o + sizeof(int32_t) * (size_t)large_sort_groups(P) * n, kAlign);
-  L.offws = o; o = align_up(o + sizeof(int32_t) * (size_t)(n + 1), kAlign);
+  L.offws = o; o = align_up(o + sizeof(int32_t) * (size_t)(2 * n + 1), kAlign);  // offsets, then counts
 #ifdef RGT_TRACE
   L.trace = o; o = align_up(o + sizeof(u64) * 16 * (size_t)p.grid, kAlign);
 #endif
@@ -290,8 +292,13 @@ int launch_sort_quant(const int32_t* ids, const uint16_t* x, int64_t ldx, int m,
   int32_t* pos = reinterpret_cast<int32_t*>(ws + L.pos);
   int launches = 0;
   if (P <= kSmallSortMaxP) {
-    const size_t lds = sizeof(int) * ((size_t)P + std::max<size_t>(P, 4 * (size_t)n) + n + (n + 1) + 256);
-    hipLaunchKernelGGL(sort_small_kernel, dim3(1), dim3(256), lds, st, ids, P, n, block, sorted_ids, expert_ids,
+    const int threads = P <= kWaveSortMaxP ? 256 : 1024;
+    const size_t lds =
+        sizeof(int) * ((size_t)P + std::max<size_t>(P, (size_t)(threads / 64) * n) + n + (n + 1) + threads);
+    if (lds > 65536 && !g_sort_lds_set.exchange(true))
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(sort_small_kernel),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    hipLaunchKernelGGL(sort_small_kernel, dim3(1), dim3(threads), lds, st, ids, P, n, block, sorted_ids, expert_ids,
                        offsets, pos);
     ++launches;
   } else {
@@ -301,10 +308,10 @@ int launch_sort_quant(const int32_t* ids, const uint16_t* x, int64_t ldx, int m,
     hipLaunchKernelGGL(sort_hist_kernel, dim3(G), dim3(256), sizeof(int) * n, st, ids, P, n, kLargeSortChunk,
                        ghist);
     hipLaunchKernelGGL(sort_colscan_kernel, dim3((n + 63) / 64), dim3(256), 0, st, ghist, G, n, offws);
-    hipLaunchKernelGGL(sort_scan_kernel, dim3(1), dim3(1024), sizeof(int) * ((size_t)n + (n + 1) + 1024), st, P, n,
-                       block, sorted_ids, expert_ids, offsets, offws);
-    hipLaunchKernelGGL(sort_scatter_kernel, dim3(G), dim3(256), sizeof(int) * (4 * (size_t)n + n), st, ids, P, n,
-                       kLargeSortChunk, ghist, offws, sorted_ids, pos);
+    hipLaunchKernelGGL(sort_scan_kernel, dim3(1), dim3(1024), sizeof(int) * ((size_t)(n + 1) + 1024), st, n, block,
+                       offws);
+    hipLaunchKernelGGL(sort_scatter_kernel, dim3(G), dim3(256), sizeof(int) * (4 * (size_t)n + n + (n + 1) + n), st,
+                       ids, P, n, block, kLargeSortChunk, ghist, offws, sorted_ids, expert_ids, offsets, pos);
     launches += 4;
   }
   const int units = m * (k / 16);

@@ -451,9 +451,9 @@ __device__ __forceinline__ void write_sort_outputs(const int* s_e, PosPtr pos, c
   }
 }
 
-// Decode-size sort: one workgroup (one wave sorts up to kWaveSortMaxP pairs,
-// the whole workgroup above). pos goes to the workspace for the quant.
-constexpr int kWaveSortMaxP = 2048;
+// Pairs up to which one wave sorts alone (decode sizes: a few batches of 64);
+// above, every wave of the workgroup takes a contiguous share.
+constexpr int kWaveSortMaxP = 512;
 
 // ---------------------------------------------------------------------------
 // MX quantisation of 16 consecutive bf16 elements (two 16-byte loads). The

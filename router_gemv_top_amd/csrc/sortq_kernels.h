@@ -8,15 +8,18 @@
 
 namespace rgt {
 
-// Decode-size sort in one workgroup (one wave up to kWaveSortMaxP pairs, the
-// whole workgroup above); the pair positions go to pos_ws for the quant.
-__global__ void __launch_bounds__(256) sort_small_kernel(const int32_t* ids, int P, int N, int B,
-                                                         int32_t* sorted_ids, int32_t* expert_ids,
-                                                         int32_t* offsets, int32_t* pos_ws) {
+// Sort of up to a few thousand pairs in one workgroup: one wave up to
+// kWaveSortMaxP pairs, every wave of the workgroup above (launched with 1024
+// threads, so each wave walks a sixteenth of the pairs in 64-pair batches);
+// the pair positions go to pos_ws for the quant.
+__global__ void __launch_bounds__(1024) sort_small_kernel(const int32_t* ids, int P, int N, int B,
+                                                          int32_t* sorted_ids, int32_t* expert_ids,
+                                                          int32_t* offsets, int32_t* pos_ws) {
   extern __shared__ int smem[];
+  const int nw = blockDim.x >> 6;
   int* s_e = smem;
   int* s_hist = s_e + P;          // wave sort: per-pair ranks; workgroup sort: per-wave counts
-  int* s_cnt = s_hist + (P > 4 * N ? P : 4 * N);
+  int* s_cnt = s_hist + (P > nw * N ? P : nw * N);
   int* s_off = s_cnt + N;
   int* s_scr = s_off + N + 1;
   if (P <= kWaveSortMaxP) {
@@ -88,17 +91,16 @@ __global__ void __launch_bounds__(256) sort_colscan_kernel(int32_t* ghist, int G
   }
 }
 
-// Padded offsets and the layout of the large sort from the per-expert
-// totals in off_ws (replaced by the offsets).
-__global__ void __launch_bounds__(1024) sort_scan_kernel(int P, int N, int B, int32_t* sorted_ids,
-                                                         int32_t* expert_ids, int32_t* offsets, int32_t* off_ws) {
+// Padded offsets of the large sort from the per-expert totals in off_ws:
+// off_ws[0..N] becomes the offsets and off_ws[N+1+e] keeps the count of
+// expert e, for the scatter workgroups that write the layout.
+__global__ void __launch_bounds__(1024) sort_scan_kernel(int N, int B, int32_t* off_ws) {
   extern __shared__ int smem[];
-  int* s_cnt = smem;
-  int* s_off = s_cnt + N;
+  int* s_off = smem;
   int* s_scr = s_off + N + 1;
   for (int e = threadIdx.x; e < N; e += blockDim.x) {
     const int c = off_ws[e];
-    s_cnt[e] = c;
+    off_ws[N + 1 + e] = c;
     s_off[e] = pad_to(c, B);
   }
   __syncthreads();
@@ -106,19 +108,31 @@ __global__ void __launch_bounds__(1024) sort_scan_kernel(int P, int N, int B, in
   if (threadIdx.x == 0) s_off[N] = total;
   __syncthreads();
   for (int e = threadIdx.x; e <= N; e += blockDim.x) off_ws[e] = s_off[e];
-  write_sort_layout(s_cnt, s_off, N, B, P, sorted_ids, expert_ids, offsets);
 }
 
-__global__ void __launch_bounds__(256) sort_scatter_kernel(const int32_t* ids, int P, int N, int chunk,
+// Workgroup g scatters the pairs [g*chunk, (g+1)*chunk) to their padded
+// positions, then writes the layout (offsets, expert_ids, pads) of its slice
+// of ceil(N / gridDim.x) experts, so that work is spread over the grid with
+// each expert's pads stored by consecutive lanes.
+__global__ void __launch_bounds__(256) sort_scatter_kernel(const int32_t* ids, int P, int N, int B, int chunk,
                                                            const int32_t* ghist, const int32_t* off_ws,
-                                                           int32_t* sorted_ids, int32_t* pos_ws) {
+                                                           int32_t* sorted_ids, int32_t* expert_ids,
+                                                           int32_t* offsets, int32_t* pos_ws) {
   extern __shared__ int smem[];
   int* s_hist = smem;            // [4][N] per-wave counts -> bases
   int* s_base = s_hist + 4 * N;  // [N] offsets + this workgroup's global base
+  int* s_off = s_base + N;       // [N+1] offsets of the layout slice
+  int* s_cnt = s_off + N + 1;    // [N] counts of the layout slice
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int p0 = blockIdx.x * chunk, p1 = min(P, p0 + chunk);
+  const int ls = (N + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int e0 = min(N, (int)blockIdx.x * ls), e1 = min(N, e0 + ls);
   for (int i = t; i < 4 * N; i += blockDim.x) s_hist[i] = 0;
   for (int e = t; e < N; e += blockDim.x) s_base[e] = off_ws[e] + ghist[(int64_t)blockIdx.x * N + e];
+  for (int e = e0 + t; e <= e1; e += blockDim.x) {
+    s_off[e] = off_ws[e];
+    if (e < e1) s_cnt[e] = off_ws[N + 1 + e];
+  }
   __syncthreads();
   const int sub = ((p1 - p0 + 3) / 4 + 63) & ~63;
   const int c0 = min(p1, p0 + wave * sub), c1 = min(p1, c0 + sub);
@@ -151,6 +165,7 @@ __global__ void __launch_bounds__(256) sort_scatter_kernel(const int32_t* ids, i
     }
     if (valid && (peers & lanemask_lt()) == 0ull) s_hist[wave * N + e] += __popcll(peers);
   }
+  if (e0 < e1) write_layout<256>(s_cnt, s_off, N, B, P, e0, e1, sorted_ids, expert_ids, offsets);
 }
 
 // fp4: MXFP4 rows (K/2 bytes of packed e2m1 codes), else MXFP8.
