@@ -188,6 +188,31 @@ def topk_gate(logits: np.ndarray, bias: np.ndarray | None, k: int):
     return ids, topk_weights(sel)
 
 
+def sum_partials(part: np.ndarray) -> np.ndarray:
+    """logits [M][N] fp32 from split-K partials part [S][M][N] fp32, added in
+    k-slice order: ((p_0 + p_1) + p_2) + ... , each add one IEEE fp32 add.
+
+    [GEMV] opening summary: the split-K reduction sums the partials of every
+    k-slice; [M31K] Summary: Router, the gate can take the partials and sum
+    them itself. The slice order is the fixed, deterministic reduction order
+    (our reading: ascending slice index, as the last arriver sums them).
+    """
+    p = np.asarray(part, dtype=np.float32)
+    assert p.ndim == 3 and np.all(np.isfinite(p))
+    acc = p[0].copy()
+    for s in range(1, p.shape[0]):
+        acc = (acc + p[s]).astype(np.float32)   # float32 + float32: one rounding per add
+    return acc
+
+
+def topk_gate_partials(part: np.ndarray, bias: np.ndarray | None, k: int):
+    """(logits, ids, w) of the softmax top-k gate fed the split-K partials:
+    the logits are sum_partials(part), then the gate as topk_gate."""
+    logits = sum_partials(part)
+    ids, w = topk_gate(logits, bias, k)
+    return logits, ids, w
+
+
 # ---------------------------------------------------------------------------
 # Token -> expert sort [M31K, K3]
 # ---------------------------------------------------------------------------
