@@ -107,7 +107,10 @@ rgt_status rgt_check_workspace(const void* ws, size_t ws_bytes, hipStream_t stre
  *   logits : fp32 [M][N] row-major, device, written
  * One launch for M <= 64 (the split-K partials are reduced in order by the
  * last workgroup to arrive at each output tile, which then zeroes its
- * counter); larger M uses the MFMA path. */
+ * counter). Larger M uses an LDS-tiled MFMA GEMM: one launch when its
+ * 128 x 128 tiles fill the chip, else two (the GEMM writes k-slice partials
+ * to the workspace and a second launch sums them in slice order, the order
+ * the launch chain of rgt_route_sort_quant uses, so the bits agree). */
 rgt_status rgt_router_logits(const void* x, int64_t ldx, const void* w, int64_t ldw,
                              float* logits, int m, int n, int k,
                              void* ws, size_t ws_bytes, hipStream_t stream);
@@ -121,6 +124,18 @@ rgt_status rgt_router_logits(const void* x, int64_t ldx, const void* w, int64_t 
  *   topk_ids : int32 [M][topk], written  topk_w : fp32 [M][topk], written */
 rgt_status rgt_topk_gate(const float* logits, const float* bias, int m, int n, int topk,
                          int32_t* topk_ids, float* topk_w, hipStream_t stream);
+
+/* Softmax top-k gate fed the router's split-K partials (MiniMax-M3.1-Flash
+ * MoE/GEMM kernels page, Summary: Router: the gate can take the partials; the
+ * sum is the split-K reduction of the split-K GEMV page, opening summary).
+ * For each row: logits = ((p_0 + p_1) + p_2) + ... + p_{S-1} in fp32, one IEEE
+ * add per k-slice in ascending slice order; then exactly rgt_topk_gate.
+ *   part     : fp32 [S][M][N], device (slice s at part + s*M*N)
+ *   logits   : fp32 [M][N], device, written if not NULL
+ *   bias, topk_ids, topk_w : as rgt_topk_gate
+ * One launch. S in [1, 1024]; otherwise as rgt_topk_gate. */
+rgt_status rgt_topk_gate_partials(const float* part, int s, const float* bias, int m, int n, int topk,
+                                  float* logits, int32_t* topk_ids, float* topk_w, hipStream_t stream);
 
 /* Sort (token, slot) pairs into block-padded expert segments and quantise
  * the gathered activations to MXFP8. Pair p = m*topk + j has expert

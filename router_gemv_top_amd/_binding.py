@@ -63,6 +63,7 @@ def lib() -> ctypes.CDLL:
             "rgt_check_workspace": ([vp, sz, vp], i32),
             "rgt_router_logits": ([vp, i64, vp, i64, vp, i32, i32, i32, vp, sz, vp], i32),
             "rgt_topk_gate": ([vp, vp, i32, i32, i32, vp, vp, vp], i32),
+            "rgt_topk_gate_partials": ([vp, i32, vp, i32, i32, i32, vp, vp, vp, vp], i32),
             "rgt_moe_sort_quant": ([vp, vp, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp], i32),
             "rgt_route_sort_quant": ([vp, i64, vp, i64, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
                                       vp, vp, vp, sz, vp], i32),
@@ -183,6 +184,21 @@ def topk_gate(logits, topk: int, bias=None, ids=None, weights=None, stream=None)
         weights = torch.empty((m, topk), dtype=torch.float32, device=logits.device)
     _check(lib().rgt_topk_gate(_ptr(logits), _ptr(bias), m, n, topk, _ptr(ids), _ptr(weights), _stream(stream)),
            "topk_gate")
+    return ids, weights
+
+
+def topk_gate_partials(part, topk: int, bias=None, logits=None, ids=None, weights=None, stream=None):
+    """(topk_ids, topk_w) of the gate fed split-K partials part [S][M][N] fp32,
+    summed in slice order; logits (if given, [M][N] fp32) receives the sum."""
+    if part.dtype != torch.float32 or part.dim() != 3 or not part.is_contiguous():
+        raise ValueError("part must be a contiguous [S][M][N] float32 tensor")
+    s, m, n = part.shape
+    if ids is None:
+        ids = torch.empty((m, topk), dtype=torch.int32, device=part.device)
+    if weights is None:
+        weights = torch.empty((m, topk), dtype=torch.float32, device=part.device)
+    _check(lib().rgt_topk_gate_partials(_ptr(part), s, _ptr(bias), m, n, topk, _ptr(logits), _ptr(ids),
+                                        _ptr(weights), _stream(stream)), "topk_gate_partials")
     return ids, weights
 
 

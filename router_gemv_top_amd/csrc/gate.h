@@ -294,6 +294,52 @@ __device__ __forceinline__ void wave_topk_row(const float* logits_row, const flo
   }
 }
 
+// Gate fed the split-K partials part[S][M][N] of the router: each lane sums
+// its experts' partials in k-slice order (one fp32 add per slice; SB slices
+// are loaded at a time, 32 for two experts a lane, so a wide batch's slices
+// cost one memory round trip), optionally writes the
+// logits, then selects as the plain gate. One wave per row.
+template <int NV>
+__global__ void __launch_bounds__(256) topk_gate_partials_kernel(const float* part, int S, float* logits_out,
+                                                                 const float* bias, int m, int n, int k,
+                                                                 int32_t* ids, float* w) {
+  constexpr int SB = NV <= 2 ? 32 : (NV <= 4 ? 16 : (NV <= 8 ? 8 : 4));
+  __shared__ __align__(16) int s_slot[4][64];
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= m) return;
+  const int c0 = lane_id() * NV;
+  const int64_t slice = (int64_t)m * n;
+  const float* src = part + (int64_t)row * n;
+  float sv[NV];
+  for (int s0 = 0; s0 < S; s0 += SB) {
+    float v[SB][NV];
+#pragma unroll
+    for (int j = 0; j < SB; ++j)
+#pragma unroll
+      for (int i = 0; i < NV; ++i) v[j][i] = src[(int64_t)min(s0 + j, S - 1) * slice + min(c0 + i, n - 1)];
+#pragma unroll
+    for (int j = 0; j < SB; ++j)
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        if (s0 + j == 0) sv[i] = v[j][i];
+        else if (s0 + j < S) sv[i] = __fadd_rn(sv[i], v[j][i]);
+      }
+  }
+  if (logits_out) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (c0 + i < n) logits_out[(int64_t)row * n + c0 + i] = sv[i];
+  }
+  add_bias<NV>(sv, bias, n);
+  int id;
+  float wt;
+  wave_topk_regs<NV>(sv, n, k, id, wt, s_slot[threadIdx.x >> 6]);
+  if (lane_id() < k) {
+    ids[(int64_t)row * k + lane_id()] = id;
+    w[(int64_t)row * k + lane_id()] = wt;
+  }
+}
+
 template <int NV>
 __global__ void __launch_bounds__(256) topk_gate_kernel(const float* logits, const float* bias, int m, int n, int k,
                                                         int32_t* ids, float* w) {

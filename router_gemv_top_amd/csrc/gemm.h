@@ -2,10 +2,15 @@
 //
 // logits[M][N] fp32 = x[M][K] bf16 . W[N][K]^T bf16, the same contraction as
 // the split-K GEMV ("MiniMax-M3: Triton split-K router GEMV with in-kernel
-// split-K fixup", opening summary) at a size where every workgroup already
-// has the whole k range to itself (prefill: thousands of tokens), so there is
-// no split and no fixup: the dense-GEMM regime the configurations name for
-// prefill routing.
+// split-K fixup", opening summary) for batches of more than 64 tokens.
+// Prefill (thousands of tokens) has tiles enough for every workgroup to take
+// the whole k range: no split, the dense-GEMM regime the configurations name
+// for prefill routing. Wide batches (128-512 tokens) have a handful of tiles,
+// so the k range is split into S slices of ksl elements and workgroup
+// (slice s, tile) writes its fp32 partial to out + s*M*N; the gate of the
+// next launch sums the slices in order (the gate taking the partials, as the
+// MiniMax-M3.1-Flash MoE/GEMM kernels page's router does). A 128 x 128 tile
+// reads each x row once per 128 experts.
 //
 // Workgroup tile 128 rows of x by 128 experts, k-step 64. The next k-step's
 // tiles are loaded into registers while the current one is multiplied from
@@ -25,12 +30,22 @@ constexpr int kGemmLds = kGemmBK + 8;  // bf16 per LDS row
 // Tiles (row block, expert block) are numbered row-block major, and the
 // XCD-aware map gives each XCD a contiguous run of them, so the x rows a run
 // shares stay in one L2.
+// ksl: k elements per slice (a multiple of kGemmBK dividing K); the grid is
+// (K / ksl) x tiles workgroups. PRE > 1: the slice is exactly PRE k-steps and
+// all of them are loaded at once (one memory round trip for the slice instead
+// of one per step: with a few k-steps per workgroup, each step's compute is
+// far shorter than the latency its prefetch would have to hide).
+template <int PRE>
 __global__ void __launch_bounds__(256) router_gemm_kernel(const uint16_t* x, int64_t ldx, const uint16_t* w,
-                                                          int64_t ldw, float* logits, int M, int N, int K) {
+                                                          int64_t ldw, float* out, int M, int N, int ksl) {
   __shared__ __align__(16) uint16_t sA[kGemmBM * kGemmLds];
   __shared__ __align__(16) uint16_t sB[kGemmBN * kGemmLds];
   const int nbn = (N + kGemmBN - 1) / kGemmBN;
-  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int tiles = ((M + kGemmBM - 1) / kGemmBM) * nbn;
+  const int job = xcd_tile(blockIdx.x, gridDim.x);
+  const int slice = job / tiles, tile = job - slice * tiles;
+  const int kb = slice * ksl;
+  float* logits = out + (int64_t)slice * M * N;
   const int m0 = (tile / nbn) * kGemmBM, n0 = (tile % nbn) * kGemmBN;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int r16 = lane & 15, grp = lane >> 4;
@@ -40,17 +55,21 @@ __global__ void __launch_bounds__(256) router_gemm_kernel(const uint16_t* x, int
   // last row (never stored). Named registers, not arrays: the values cross
   // the loop's back edge, and an array there ends up in scratch memory.
   const int lc = t & 7, lr = t >> 3;
-  const uint16_t* ga0 = x + (int64_t)min(m0 + lr, M - 1) * ldx + 8 * lc;
-  const uint16_t* ga1 = x + (int64_t)min(m0 + lr + 32, M - 1) * ldx + 8 * lc;
-  const uint16_t* ga2 = x + (int64_t)min(m0 + lr + 64, M - 1) * ldx + 8 * lc;
-  const uint16_t* ga3 = x + (int64_t)min(m0 + lr + 96, M - 1) * ldx + 8 * lc;
-  const uint16_t* gb0 = w + (int64_t)min(n0 + lr, N - 1) * ldw + 8 * lc;
-  const uint16_t* gb1 = w + (int64_t)min(n0 + lr + 32, N - 1) * ldw + 8 * lc;
-  const uint16_t* gb2 = w + (int64_t)min(n0 + lr + 64, N - 1) * ldw + 8 * lc;
-  const uint16_t* gb3 = w + (int64_t)min(n0 + lr + 96, N - 1) * ldw + 8 * lc;
+  const uint16_t* ga0 = x + (int64_t)min(m0 + lr, M - 1) * ldx + kb + 8 * lc;
+  const uint16_t* ga1 = x + (int64_t)min(m0 + lr + 32, M - 1) * ldx + kb + 8 * lc;
+  const uint16_t* ga2 = x + (int64_t)min(m0 + lr + 64, M - 1) * ldx + kb + 8 * lc;
+  const uint16_t* ga3 = x + (int64_t)min(m0 + lr + 96, M - 1) * ldx + kb + 8 * lc;
+  const uint16_t* gb0 = w + (int64_t)min(n0 + lr, N - 1) * ldw + kb + 8 * lc;
+  const uint16_t* gb1 = w + (int64_t)min(n0 + lr + 32, N - 1) * ldw + kb + 8 * lc;
+  const uint16_t* gb2 = w + (int64_t)min(n0 + lr + 64, N - 1) * ldw + kb + 8 * lc;
+  const uint16_t* gb3 = w + (int64_t)min(n0 + lr + 96, N - 1) * ldw + kb + 8 * lc;
   auto ld = [](const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); };
-  uint4 ra0 = ld(ga0), ra1 = ld(ga1), ra2 = ld(ga2), ra3 = ld(ga3);
-  uint4 rb0 = ld(gb0), rb1 = ld(gb1), rb2 = ld(gb2), rb3 = ld(gb3);
+  // one-step prefetch: the first step's loads go out before anything else
+  uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
+  if constexpr (PRE == 1) {
+    ra0 = ld(ga0), ra1 = ld(ga1), ra2 = ld(ga2), ra3 = ld(ga3);
+    rb0 = ld(gb0), rb1 = ld(gb1), rb2 = ld(gb2), rb3 = ld(gb3);
+  }
   floatx4_t acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -58,27 +77,18 @@ __global__ void __launch_bounds__(256) router_gemm_kernel(const uint16_t* x, int
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   uint16_t* la = sA + lr * kGemmLds + 8 * lc;
   uint16_t* lb = sB + lr * kGemmLds + 8 * lc;
-  for (int k0 = 0; k0 < K; k0 += kGemmBK) {
-    __syncthreads();  // the previous step's LDS reads are done
-    *reinterpret_cast<uint4*>(la) = ra0;
-    *reinterpret_cast<uint4*>(la + 32 * kGemmLds) = ra1;
-    *reinterpret_cast<uint4*>(la + 64 * kGemmLds) = ra2;
-    *reinterpret_cast<uint4*>(la + 96 * kGemmLds) = ra3;
-    *reinterpret_cast<uint4*>(lb) = rb0;
-    *reinterpret_cast<uint4*>(lb + 32 * kGemmLds) = rb1;
-    *reinterpret_cast<uint4*>(lb + 64 * kGemmLds) = rb2;
-    *reinterpret_cast<uint4*>(lb + 96 * kGemmLds) = rb3;
-    __syncthreads();
-    // prefetch the next step (the last step reloads itself: no branch)
-    const int kn = min(k0 + kGemmBK, K - kGemmBK);
-    ra0 = ld(ga0 + kn);
-    ra1 = ld(ga1 + kn);
-    ra2 = ld(ga2 + kn);
-    ra3 = ld(ga3 + kn);
-    rb0 = ld(gb0 + kn);
-    rb1 = ld(gb1 + kn);
-    rb2 = ld(gb2 + kn);
-    rb3 = ld(gb3 + kn);
+  auto stage = [&](const uint4& a0, const uint4& a1, const uint4& a2, const uint4& a3, const uint4& b0,
+                   const uint4& b1, const uint4& b2, const uint4& b3) {
+    *reinterpret_cast<uint4*>(la) = a0;
+    *reinterpret_cast<uint4*>(la + 32 * kGemmLds) = a1;
+    *reinterpret_cast<uint4*>(la + 64 * kGemmLds) = a2;
+    *reinterpret_cast<uint4*>(la + 96 * kGemmLds) = a3;
+    *reinterpret_cast<uint4*>(lb) = b0;
+    *reinterpret_cast<uint4*>(lb + 32 * kGemmLds) = b1;
+    *reinterpret_cast<uint4*>(lb + 64 * kGemmLds) = b2;
+    *reinterpret_cast<uint4*>(lb + 96 * kGemmLds) = b3;
+  };
+  auto step = [&]() {
 #pragma unroll
     for (int kk = 0; kk < kGemmBK; kk += 32) {
       uint4 fa[4], fb[4];
@@ -94,6 +104,44 @@ __global__ void __launch_bounds__(256) router_gemm_kernel(const uint16_t* x, int
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fa[i]),
                                                              __builtin_bit_cast(bf16x8_t, fb[j]), acc[i][j], 0, 0, 0);
     }
+  };
+  if constexpr (PRE > 1) {
+    uint4 ra[PRE][4], rb[PRE][4];
+#pragma unroll
+    for (int j = 0; j < PRE; ++j) {
+      ra[j][0] = ld(ga0 + kGemmBK * j);
+      ra[j][1] = ld(ga1 + kGemmBK * j);
+      ra[j][2] = ld(ga2 + kGemmBK * j);
+      ra[j][3] = ld(ga3 + kGemmBK * j);
+      rb[j][0] = ld(gb0 + kGemmBK * j);
+      rb[j][1] = ld(gb1 + kGemmBK * j);
+      rb[j][2] = ld(gb2 + kGemmBK * j);
+      rb[j][3] = ld(gb3 + kGemmBK * j);
+    }
+#pragma unroll
+    for (int j = 0; j < PRE; ++j) {
+      if (j) __syncthreads();  // the previous step's LDS reads are done
+      stage(ra[j][0], ra[j][1], ra[j][2], ra[j][3], rb[j][0], rb[j][1], rb[j][2], rb[j][3]);
+      __syncthreads();
+      step();
+    }
+  } else {
+    for (int k0 = 0; k0 < ksl; k0 += kGemmBK) {
+      __syncthreads();  // the previous step's LDS reads are done
+      stage(ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3);
+      __syncthreads();
+      // prefetch the next step (the last step reloads itself: no branch)
+      const int kn = min(k0 + kGemmBK, ksl - kGemmBK);
+      ra0 = ld(ga0 + kn);
+      ra1 = ld(ga1 + kn);
+      ra2 = ld(ga2 + kn);
+      ra3 = ld(ga3 + kn);
+      rb0 = ld(gb0 + kn);
+      rb1 = ld(gb1 + kn);
+      rb2 = ld(gb2 + kn);
+      rb3 = ld(gb3 + kn);
+      step();
+    }
   }
   // D lane l: rows 4*(l/16) + r of the 16 x 16 tile, column l % 16
 #pragma unroll
@@ -107,6 +155,34 @@ __global__ void __launch_bounds__(256) router_gemm_kernel(const uint16_t* x, int
         if (row < M && col < N) logits[(int64_t)row * N + col] = acc[i][j][r];
       }
     }
+}
+
+// logits = the k-slice partials part[S][count] summed in slice order, one
+// fp32 add per slice (the order of the gate that takes the partials, so the
+// two give the same bits). Four consecutive values per thread (count is a
+// multiple of 4; part is 16-byte aligned, out only 4-byte aligned), slices
+// loaded eight at a time so their latencies overlap.
+__global__ void __launch_bounds__(256) sum_partials_kernel(const float* part, int S, int64_t count, float* out) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= count) return;
+  float4 acc = *reinterpret_cast<const float4*>(part + i);
+  for (int s0 = 1; s0 < S; s0 += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = *reinterpret_cast<const float4*>(part + (int64_t)min(s0 + j, S - 1) * count + i);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (s0 + j < S) {
+        acc.x = __fadd_rn(acc.x, v[j].x);
+        acc.y = __fadd_rn(acc.y, v[j].y);
+        acc.z = __fadd_rn(acc.z, v[j].z);
+        acc.w = __fadd_rn(acc.w, v[j].w);
+      }
+  }
+  out[i] = acc.x;
+  out[i + 1] = acc.y;
+  out[i + 2] = acc.z;
+  out[i + 3] = acc.w;
 }
 
 }  // namespace rgt

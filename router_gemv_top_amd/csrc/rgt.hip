@@ -146,6 +146,28 @@ Plan make_plan(int m, int n, int k) {
   return p;
 }
 
+// Wide batches (more than 64 rows, too few 128 x 128 tiles to fill the chip)
+// whose router runs as the k-split GEMM: from 384 rows at 128 experts, or
+// more than 128 experts (where the split-K GEMV's 16-expert tiles re-read
+// each x row N/16 times). Below, at N = 128, the split-K GEMV with its
+// in-launch fixup measured faster (M = 128: 12 vs 13.5 us router + gate).
+bool wide_gemm(int m, int n) {
+  const int tiles = ((m + kGemmBM - 1) / kGemmBM) * ((n + kGemmBN - 1) / kGemmBN);
+  return m > kFusedMaxM && tiles < kGemmMinTiles && (m >= 384 || n > 128);
+}
+
+// k-slices of the router GEMM for a wide batch: the most slices that still
+// leave each workgroup four k-steps (at most 32), so a handful of 128 x 128
+// tiles spread over more CUs; the gate (or a sum launch) adds the slices.
+int chain_gemm_slices(int m, int n, int k) {
+  const int tiles = ((m + kGemmBM - 1) / kGemmBM) * ((n + kGemmBN - 1) / kGemmBN);
+  if (tiles >= kGemmMinTiles) return 1;
+  const int steps = k / kGemmBK;
+  for (int d = 32; d > 1; --d)
+    if (steps % d == 0 && steps / d >= 4) return d;
+  return 1;
+}
+
 // ---------------------------------------------------------------------------
 // Workspace layout for one call (offsets depend on the call's own shape,
 // except the control words and tile counters, which sit at fixed offsets and
@@ -164,7 +186,8 @@ Layout make_layout(int m, int n, int k, int topk) {
   size_t o = 0;
   L.ctl = o; o += kCtlBytes;
   L.ctr = o; o = align_up(o + sizeof(u32) * kCtrStride * (size_t)kMaxTileCounters, kAlign);
-  L.part = o; o = align_up(o + sizeof(float) * (size_t)p.s * m * n, kAlign);
+  const int part_slices = std::max(p.s, wide_gemm(m, n) ? chain_gemm_slices(m, n, k) : 1);
+  L.part = o; o = align_up(o + sizeof(float) * (size_t)part_slices * m * n, kAlign);
   L.logits = o; o = align_up(o + sizeof(float) * (size_t)m * n, kAlign);
   L.tpart = L.tids = o;
   if (m <= kFusedMaxM) {  // tagged hand-off words of the one-launch path
@@ -251,8 +274,8 @@ void launch_router_mfma(const GemvArgs& a, const Plan& p, hipStream_t st) {
 
 void launch_router(const GemvArgs& a, const Plan& p, hipStream_t st) {
   if (p.gemm) {
-    hipLaunchKernelGGL(router_gemm_kernel, dim3(p.grid), dim3(256), 0, st, a.x, a.ldx, a.w, a.ldw, a.logits, a.m,
-                       a.n, a.k);
+    hipLaunchKernelGGL(router_gemm_kernel<1>, dim3(p.grid), dim3(256), 0, st, a.x, a.ldx, a.w, a.ldw, a.logits,
+                       a.m, a.n, a.k);
     return;
   }
   if (p.valu) {
@@ -281,6 +304,33 @@ void launch_gate(const float* logits, const float* bias, int m, int n, int k, in
     case 8: hipLaunchKernelGGL((topk_gate_kernel<8>), grid, blk, 0, st, logits, bias, m, n, k, ids, w); break;
     case 14: hipLaunchKernelGGL((topk_gate_kernel<14>), grid, blk, 0, st, logits, bias, m, n, k, ids, w); break;
     default: hipLaunchKernelGGL((topk_gate_kernel<16>), grid, blk, 0, st, logits, bias, m, n, k, ids, w); break;
+  }
+}
+
+// The router GEMM of wide batches: k-slice partials to a.part (or the
+// logits directly for one slice). Returns the number of launches (1).
+int launch_chain_gemm(const GemvArgs& a, int m, int n, int k, hipStream_t st) {
+  const int S = chain_gemm_slices(m, n, k);
+  const int tiles = ((m + kGemmBM - 1) / kGemmBM) * ((n + kGemmBN - 1) / kGemmBN);
+  float* out = S > 1 ? a.part : a.logits;
+  if (k / S == 4 * kGemmBK)
+    hipLaunchKernelGGL(router_gemm_kernel<4>, dim3(tiles * S), dim3(256), 0, st, a.x, a.ldx, a.w, a.ldw, out, m, n,
+                       k / S);
+  else
+    hipLaunchKernelGGL(router_gemm_kernel<1>, dim3(tiles * S), dim3(256), 0, st, a.x, a.ldx, a.w, a.ldw, out, m, n,
+                       k / S);
+  return 1;
+}
+
+void launch_gate_partials(const float* part, int S, float* logits, const float* bias, int m, int n, int k,
+                          int32_t* ids, float* w, hipStream_t st) {
+  const dim3 grid((m + 3) / 4), blk(256);
+  switch (nv_bucket(n)) {
+    case 2: hipLaunchKernelGGL((topk_gate_partials_kernel<2>), grid, blk, 0, st, part, S, logits, bias, m, n, k, ids, w); break;
+    case 4: hipLaunchKernelGGL((topk_gate_partials_kernel<4>), grid, blk, 0, st, part, S, logits, bias, m, n, k, ids, w); break;
+    case 8: hipLaunchKernelGGL((topk_gate_partials_kernel<8>), grid, blk, 0, st, part, S, logits, bias, m, n, k, ids, w); break;
+    case 14: hipLaunchKernelGGL((topk_gate_partials_kernel<14>), grid, blk, 0, st, part, S, logits, bias, m, n, k, ids, w); break;
+    default: hipLaunchKernelGGL((topk_gate_partials_kernel<16>), grid, blk, 0, st, part, S, logits, bias, m, n, k, ids, w); break;
   }
 }
 
@@ -453,6 +503,19 @@ rgt_status rgt_router_logits(const void* x, int64_t ldx, const void* w, int64_t 
   char* base = static_cast<char*>(ws);
   GemvArgs a{static_cast<const u16*>(x), ldx, static_cast<const u16*>(w), ldw, logits,
              reinterpret_cast<float*>(base + L.part), reinterpret_cast<u32*>(base + L.ctr), m, n, k, p.s, p.nb};
+  if (wide_gemm(m, n)) {
+    // Wide batch: the same k-slice partials as the launch chain of
+    // rgt_route_sort_quant, summed in the same order (same bits).
+    g_last_launches = launch_chain_gemm(a, m, n, k, stream);
+    const int S = chain_gemm_slices(m, n, k);
+    if (S > 1) {
+      const int64_t count = (int64_t)m * n;
+      hipLaunchKernelGGL(sum_partials_kernel, dim3((unsigned)((count / 4 + 255) / 256)), dim3(256), 0, stream, a.part,
+                         S, count, logits);
+      ++g_last_launches;
+    }
+    return launched();
+  }
   launch_router(a, p, stream);
   g_last_launches = 1;
   return launched();
@@ -467,6 +530,20 @@ rgt_status rgt_topk_gate(const float* logits, const float* bias, int m, int n, i
       (bias && !aligned(bias, 4)))
     return RGT_ERR_INVALID;
   launch_gate(logits, bias, m, n, topk, topk_ids, topk_w, stream);
+  g_last_launches = 1;
+  return launched();
+}
+
+rgt_status rgt_topk_gate_partials(const float* part, int s, const float* bias, int m, int n, int topk,
+                                  float* logits, int32_t* topk_ids, float* topk_w, hipStream_t stream) {
+  g_last_launches = 0;
+  if (m < 0 || m > 8192 || n < 16 || n > 1024 || n % 16 || !gate_covered(n, topk) || s < 1 || s > 1024)
+    return RGT_ERR_UNSUPPORTED;
+  if (m == 0) return RGT_OK;
+  if (!part || !topk_ids || !topk_w || !aligned(part, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) ||
+      (bias && !aligned(bias, 4)) || (logits && !aligned(logits, 4)))
+    return RGT_ERR_INVALID;
+  launch_gate_partials(part, s, logits, bias, m, n, topk, topk_ids, topk_w, stream);
   g_last_launches = 1;
   return launched();
 }
@@ -575,8 +652,17 @@ static rgt_status route_sort_quant_impl(const void* x, int64_t ldx, const void* 
     g_last_launches = 1;
     return launched();
   }
-  launch_router(g, p, stream);
-  launch_gate(lg, bias, m, n, topk, topk_ids, topk_w, stream);
+  if (wide_gemm(m, n)) {
+    // Wide batch: the router GEMM writes k-slice partials, the gate sums them
+    // in slice order and writes the logits.
+    const int S = chain_gemm_slices(m, n, k);
+    launch_chain_gemm(g, m, n, k, stream);
+    if (S > 1) launch_gate_partials(g.part, S, logits, bias, m, n, topk, topk_ids, topk_w, stream);
+    else launch_gate(lg, bias, m, n, topk, topk_ids, topk_w, stream);
+  } else {
+    launch_router(g, p, stream);
+    launch_gate(lg, bias, m, n, topk, topk_ids, topk_w, stream);
+  }
   const int nl = launch_sort_quant(topk_ids, static_cast<const uint16_t*>(x), ldx, m, n, k, topk, block, sorted_ids,
                                    expert_ids, offsets, a_q, a_scale, fp4, base, L, stream);
   g_last_launches = 2 + nl;

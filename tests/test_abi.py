@@ -137,3 +137,20 @@ def test_workspace_helpers_reject_bad_buffers(L):
     assert L.rgt_reset_workspace(None, 1024, None) == 3
     assert L.rgt_check_workspace(FAKE + 8, 1024, None) == 3
     assert L.rgt_check_workspace(FAKE, 16, None) == 3
+
+
+def test_gate_partials_argument_errors(L):
+    f = L.rgt_topk_gate_partials
+
+    def call(part=FAKE, s=4, bias=None, m=4, n=128, topk=8, logits=None, ids=FAKE, w=FAKE):
+        return f(part, s, bias, m, n, topk, logits, ids, w, None)
+
+    assert call(m=0) == 0
+    assert call(s=0) == 1
+    assert call(s=1025) == 1
+    assert call(n=100) == 1
+    assert call(topk=33) == 1
+    assert call(part=None) == 2
+    assert call(part=FAKE + 2) == 2
+    assert call(logits=FAKE + 1) == 2
+    assert call(w=None) == 2

@@ -153,13 +153,19 @@ def test_fused_deterministic_and_skewed(R):
     check_sort_quant(sort_out(outs[0]), ids, x, n, block)
 
 
-@pytest.mark.parametrize("wl", workloads_wide_128(), ids=lambda w: w.name)
+@pytest.mark.parametrize("wl", workloads_wide_128() + [Workload("wide896_M200", 200, 896, 3584, 16, 16, bias=True),
+                                                      Workload("wide_k512_M400", 400, 144, 512, 8, 32)],
+                         ids=lambda w: w.name)
 def test_route_sort_quant_wide(R, wl):
     say(f"route_sort_quant wide {wl.name}")
     x, w, b = wl.make()
     ws = R.Workspace(wl.m, wl.n, wl.k, wl.topk, wl.block)
     f, launches = fused(R, x, w, b, wl.topk, wl.block, ws)
     fo = np_out(f)
+    # the chain's logits are the standalone router's, bit for bit
+    ref = R.router_logits(to_dev_bf16(x), to_dev_bf16(w), ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(fo["logits"].view(np.uint32), ref.cpu().numpy().view(np.uint32))
     ids = check_against_oracle(x, w, b, wl.topk, wl.block, fo)
     rng = np.random.default_rng(3)
     check_sort_quant(sort_out(fo), ids, x, wl.n, wl.block,

@@ -86,3 +86,44 @@ def test_gate_extreme_spread(R):
     logits[:, 9] = -250.0
     logits[1] *= -1
     check_gate(R, logits, 8)
+
+
+# The gate fed split-K partials (rgt_topk_gate_partials): logits bit-exact
+# against the oracle's slice-ordered fp32 sum, ids and weights against the
+# oracle gate on those logits. Partials are k-slices of a real router product
+# (so the sum matters to the selection), with signed zeros and exact
+# cancellations planted.
+@pytest.mark.parametrize("m,n,k,S,bias", [(1, 128, 8, 1, False), (4, 128, 8, 24, False), (512, 128, 8, 24, False),
+                                          (128, 128, 8, 12, True), (33, 896, 16, 7, True), (9, 1024, 32, 40, False),
+                                          (5, 16, 4, 3, False)])
+def test_gate_partials_parity(R, m, n, k, S, bias):
+    say(f"gate partials M={m} N={n} k={k} S={S} bias={bias}")
+    kdim = 64 * S
+    rng = np.random.default_rng(m * 7 + S)
+    x = gen_x(m, kdim, seed=m + S)
+    w = gen_w(n, kdim, seed=n + S)
+    part = np.stack([O.router_logits(x[:, s * 64:(s + 1) * 64], w[:, s * 64:(s + 1) * 64]) for s in range(S)])
+    part[0, 0, :4] = -0.0
+    if S > 2:
+        part[1, 0, 4:8] = 1e8
+        part[2, 0, 4:8] = -1e8        # exact cancellation in slice order
+    b = gen_bias(n, seed=3) if bias else None
+    lg = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    ids, tw = R.topk_gate_partials(to_dev(part), k, bias=None if b is None else to_dev(b), logits=lg)
+    torch.cuda.synchronize()
+    assert R.last_launch_count() == 1
+    ref_lg, rid, rw = O.topk_gate_partials(part, b, k)
+    np.testing.assert_array_equal(lg.cpu().numpy().view(np.uint32), ref_lg.view(np.uint32))
+    np.testing.assert_array_equal(ids.cpu().numpy(), rid)
+    np.testing.assert_array_equal(tw.cpu().numpy().view(np.uint32), rw.view(np.uint32))
+
+
+def test_gate_partials_without_logits(R):
+    say("gate partials without logits output")
+    rng = np.random.default_rng(9)
+    part = rng.standard_normal((5, 16, 256)).astype(np.float32)
+    ids, tw = R.topk_gate_partials(to_dev(part), 8)
+    torch.cuda.synchronize()
+    _, rid, rw = O.topk_gate_partials(part, None, 8)
+    np.testing.assert_array_equal(ids.cpu().numpy(), rid)
+    np.testing.assert_array_equal(tw.cpu().numpy().view(np.uint32), rw.view(np.uint32))
