@@ -23,6 +23,9 @@ Sources (titles of the pages this follows):
   [MONO]  "minimax_m31: Run MiniMax-M3.1-Flash's decode FFN as one monokernel
           launch a layer" (sgl-amd-mono PR #56), the MXFP8 shared-expert
           commit (group-32 scales).
+  [M3R]   sglang PR #46691 (MiniMax-M3.1-Flash MoE/GEMM kernels), Summary:
+          fp8 producers (the Gemma RMSNorm (+ residual) producers in front of
+          the next GEMM) and the measured gain of those producers.
   [OCP]   OCP Microscaling Formats (MX) v1.0: e4m3 element format (bias 7,
           max normal 448, no infinities), e8m0 shared scale (bias 127), shared
           exponent = floor(log2(amax)) - emax_elem with emax_elem = 8 for e4m3;
@@ -43,6 +46,11 @@ notes):
     size with the sentinel P = M*k; empty experts get no block.
   * MXFP8: OCP floor rule for the shared exponent, round to nearest even,
     saturation to +-448, sign kept (so -0 encodes as 0x80).
+  * RMSNorm producer ([M3R]; [MONO] "route on the norm's scale": the norm
+    publishes each token's rstd): h = bf16(x + residual) with one fp32 add,
+    rstd = 1/sqrt(mean(h^2) + eps), xn = bf16((h * rstd) * (1 + gamma)) with
+    fp32 steps (Gemma weights). rstd is compared within its rounding; xn is
+    exact given the rstd used.
   * MXFP4 (the stage-1 activation quant of [M31K], Summary: MoE sorting +
     quant): the same floor rule with emax_elem = 2 for e2m1, round to nearest
     even, saturation to +-6, sign kept (-0 -> 0x8); two codes a byte, the
@@ -211,6 +219,57 @@ def topk_gate_partials(part: np.ndarray, bias: np.ndarray | None, k: int):
     logits = sum_partials(part)
     ids, w = topk_gate(logits, bias, k)
     return logits, ids, w
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm producer in front of the router [M3R], [MONO]
+# ---------------------------------------------------------------------------
+
+
+def bf16_round(v: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns of finite fp32 values, rounded to nearest, ties to
+    even: 8 significant bits (spacing 2^-133 below the normal range), from the
+    exact fp64 value."""
+    a = np.asarray(v, dtype=np.float32).astype(np.float64)
+    _, ex = np.frexp(a)                        # |a| = f * 2^ex, f in [0.5, 1)
+    qexp = np.maximum(ex - 8, -133)            # spacing of bf16 values near a
+    q = np.rint(np.ldexp(a, -qexp))            # RNE to a multiple of the spacing
+    r = np.ldexp(q, qexp).astype(np.float32)   # exact: a bf16 value
+    return (r.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def residual_add(x_bits: np.ndarray, r_bits: np.ndarray) -> np.ndarray:
+    """h = bf16(fp32(x) + fp32(r)): one fp32 add, then rounded to bf16 (the
+    producer's residual stream)."""
+    x = bf16_bits_to_f64(x_bits).astype(np.float32)
+    r = bf16_bits_to_f64(r_bits).astype(np.float32)
+    return bf16_round((x + r).astype(np.float32))
+
+
+def rmsnorm_rstd(h_bits: np.ndarray, eps: float) -> np.ndarray:
+    """rstd[m] = 1 / sqrt(mean_i h[m][i]^2 + eps), in fp64, rounded once to
+    fp32 (the per-token scale the norm publishes)."""
+    h = bf16_bits_to_f64(h_bits)
+    ms = (h * h).sum(axis=1) / h.shape[1]
+    return (1.0 / np.sqrt(ms + float(np.float32(eps)))).astype(np.float32)
+
+
+def rmsnorm_apply(h_bits: np.ndarray, rstd: np.ndarray, gamma_bits: np.ndarray) -> np.ndarray:
+    """xn = bf16( fp32( fp32(h * rstd) * fp32(1 + gamma) ) ): the Gemma form
+    (weight 1 + gamma), each step one IEEE fp32 operation, then rounded to
+    bf16. rstd is fp32 [M]; the result is bf16 bits [M][K]."""
+    h = bf16_bits_to_f64(h_bits).astype(np.float32)
+    g = (np.float32(1.0) + bf16_bits_to_f64(gamma_bits).astype(np.float32)).astype(np.float32)
+    t = (h * np.asarray(rstd, np.float32)[:, None]).astype(np.float32)
+    return bf16_round((t * g[None, :]).astype(np.float32))
+
+
+def rmsnorm(x_bits, r_bits, gamma_bits, eps: float):
+    """(xn bits, rstd fp32, h bits): h = residual_add(x, r) (or x without a
+    residual), rstd = rmsnorm_rstd(h), xn = rmsnorm_apply(h, rstd, gamma)."""
+    h = x_bits if r_bits is None else residual_add(x_bits, r_bits)
+    rstd = rmsnorm_rstd(h, eps)
+    return rmsnorm_apply(h, rstd, gamma_bits), rstd, h
 
 
 # ---------------------------------------------------------------------------
