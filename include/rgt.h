@@ -199,6 +199,28 @@ rgt_status rgt_route_sort_quant_mxfp4(const void* x, int64_t ldx, const void* w,
                                       uint8_t* a_q, uint8_t* a_scale,
                                       void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* RMSNorm producer in front of the router (the Gemma RMSNorm (+ residual)
+ * producers of the MiniMax-M3.1-Flash MoE/GEMM kernels page, Summary: fp8
+ * producers; the per-token rstd it publishes is the scale the "route on the
+ * norm's scale" commit of the MiniMax-M3.1 FFN monokernel page routes on).
+ * For each row m:
+ *   h    = bf16(fp32(x) + fp32(residual)) with one fp32 add and round to
+ *          nearest even, or h = x when residual is NULL
+ *   rstd = 1 / sqrt(sum_i h_i^2 / K + eps), fp32 (the sum in this library's
+ *          order: compared with a reference within its rounding, not bit for bit)
+ *   xn_i = bf16(fp32(fp32(h_i * rstd) * fp32(1 + gamma_i)))   (Gemma weights)
+ *   x, residual : bf16 [M][ld], device, 16-byte aligned, ld >= K, ld % 8 == 0
+ *   gamma       : bf16 [K], device, 16-byte aligned
+ *   xn          : bf16 [M][ldxn], written (the router's input)
+ *   residual_out: bf16 [M][ldro], written with h if not NULL (needs residual)
+ *   rstd        : fp32 [M], written if not NULL
+ * Coverage: 8 <= K <= 16384, K % 8 == 0, M <= 65535. One launch. The sum of
+ * squares is accumulated in fp32: rows whose sum of squares overflows fp32
+ * (|h| beyond ~1e17) are outside the contract. */
+rgt_status rgt_rmsnorm(const void* x, int64_t ldx, const void* residual, int64_t ldr, const void* gamma, float eps,
+                       int m, int k, void* xn, int64_t ldxn, void* residual_out, int64_t ldro, float* rstd,
+                       hipStream_t stream);
+
 /* Number of kernel launches the last successful call of each entry point made
  * on this thread (diagnostics for launch-count checks). */
 int rgt_last_launch_count(void);

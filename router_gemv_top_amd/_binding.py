@@ -71,6 +71,7 @@ def lib() -> ctypes.CDLL:
                                          i32),
             "rgt_route_sort_quant_mxfp4": ([vp, i64, vp, i64, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
                                             vp, vp, vp, sz, vp], i32),
+            "rgt_rmsnorm": ([vp, i64, vp, i64, vp, ctypes.c_float, i32, i32, vp, i64, vp, i64, vp, vp], i32),
             "rgt_last_launch_count": ([], i32),
             "rgt_diag_read": ([vp, sz, vp, i32, vp], i32),
             "rgt_diag_copy": ([vp, vp, sz, i32, vp], i32),
@@ -286,6 +287,29 @@ def _route_sort_quant(fn, fmt, x, w, topk, block, ws, bias, out, want_logits, st
               _ptr(out["a_q"]), _ptr(out["a_scale"]), _ptr(ws.buf), ws.nbytes,
               _stream(stream)), fn.__name__[4:])
     return out
+
+
+def rmsnorm(x, gamma, eps: float, residual=None, xn=None, residual_out=None, rstd=None, stream=None):
+    """Gemma RMSNorm producer: (xn bf16 [M][K], rstd fp32 [M], residual_out or
+    None). residual_out (bf16, h = x + residual) is allocated when a residual
+    is given and none is passed."""
+    _bf16_2d(x, "x")
+    m, k = x.shape
+    if gamma.dtype != torch.bfloat16 or gamma.dim() != 1 or not gamma.is_contiguous():
+        raise ValueError("gamma must be a contiguous 1-D bfloat16 tensor")
+    if residual is not None:
+        _bf16_2d(residual, "residual")
+        if residual_out is None:
+            residual_out = torch.empty((m, k), dtype=torch.bfloat16, device=x.device)
+    if xn is None:
+        xn = torch.empty((m, k), dtype=torch.bfloat16, device=x.device)
+    if rstd is None:
+        rstd = torch.empty((m,), dtype=torch.float32, device=x.device)
+    _check(lib().rgt_rmsnorm(_ptr(x), x.stride(0), _ptr(residual), 0 if residual is None else residual.stride(0),
+                             _ptr(gamma), float(eps), m, k, _ptr(xn), xn.stride(0), _ptr(residual_out),
+                             0 if residual_out is None else residual_out.stride(0), _ptr(rstd), _stream(stream)),
+           "rmsnorm")
+    return xn, rstd, residual_out
 
 
 def diag_read(src, sink, grid: int, nbytes: int | None = None, stream=None):

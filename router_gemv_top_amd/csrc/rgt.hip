@@ -22,6 +22,7 @@
 #include "gate.h"
 #include "gemm.h"
 #include "gemv.h"
+#include "norm.h"
 #include "sortq.h"
 #include "sortq_kernels.h"
 
@@ -544,6 +545,32 @@ rgt_status rgt_topk_gate_partials(const float* part, int s, const float* bias, i
       (bias && !aligned(bias, 4)) || (logits && !aligned(logits, 4)))
     return RGT_ERR_INVALID;
   launch_gate_partials(part, s, logits, bias, m, n, topk, topk_ids, topk_w, stream);
+  g_last_launches = 1;
+  return launched();
+}
+
+rgt_status rgt_rmsnorm(const void* x, int64_t ldx, const void* residual, int64_t ldr, const void* gamma, float eps,
+                       int m, int k, void* xn, int64_t ldxn, void* residual_out, int64_t ldro, float* rstd,
+                       hipStream_t stream) {
+  g_last_launches = 0;
+  if (m < 0 || m > 65535 || k < 8 || k > 16384 || k % 8) return RGT_ERR_UNSUPPORTED;
+  if (m == 0) return RGT_OK;
+  if (!x || !gamma || !xn || !aligned(x, 16) || !aligned(gamma, 16) || !aligned(xn, 16)) return RGT_ERR_INVALID;
+  if (ldx < k || ldx % 8 || ldxn < k || ldxn % 8 || !(eps >= 0.f)) return RGT_ERR_INVALID;
+  if (residual && (!aligned(residual, 16) || ldr < k || ldr % 8)) return RGT_ERR_INVALID;
+  if (residual_out && (!residual || !aligned(residual_out, 16) || ldro < k || ldro % 8)) return RGT_ERR_INVALID;
+  if (rstd && !aligned(rstd, 4)) return RGT_ERR_INVALID;
+  const int ch = (k + 2047) / 2048;  // 8-element chunks per thread
+  const auto* xs = static_cast<const uint16_t*>(x);
+  const auto* rs = static_cast<const uint16_t*>(residual);
+  const auto* gs = static_cast<const uint16_t*>(gamma);
+  auto* xo = static_cast<uint16_t*>(xn);
+  auto* ro = static_cast<uint16_t*>(residual_out);
+  const dim3 grid(m), blk(256);
+  if (ch <= 1) hipLaunchKernelGGL(rmsnorm_kernel<1>, grid, blk, 0, stream, xs, ldx, rs, ldr, gs, eps, k, xo, ldxn, ro, ldro, rstd);
+  else if (ch <= 2) hipLaunchKernelGGL(rmsnorm_kernel<2>, grid, blk, 0, stream, xs, ldx, rs, ldr, gs, eps, k, xo, ldxn, ro, ldro, rstd);
+  else if (ch <= 4) hipLaunchKernelGGL(rmsnorm_kernel<4>, grid, blk, 0, stream, xs, ldx, rs, ldr, gs, eps, k, xo, ldxn, ro, ldro, rstd);
+  else hipLaunchKernelGGL(rmsnorm_kernel<8>, grid, blk, 0, stream, xs, ldx, rs, ldr, gs, eps, k, xo, ldxn, ro, ldro, rstd);
   g_last_launches = 1;
   return launched();
 }

@@ -154,3 +154,20 @@ def test_gate_partials_argument_errors(L):
     assert call(part=FAKE + 2) == 2
     assert call(logits=FAKE + 1) == 2
     assert call(w=None) == 2
+
+
+def test_rmsnorm_argument_errors(L):
+    f = L.rgt_rmsnorm
+
+    def call(x=FAKE, ldx=6144, r=None, ldr=0, g=FAKE, eps=1e-6, m=4, k=6144, xn=FAKE, ldxn=6144, ro=None, ldro=0,
+             rstd=None):
+        return f(x, ldx, r, ldr, g, eps, m, k, xn, ldxn, ro, ldro, rstd, None)
+
+    assert call(m=0) == 0
+    assert call(k=6) == 1 and call(k=16392) == 1 and call(k=100) == 1
+    assert call(x=None) == 2 and call(g=FAKE + 2) == 2 and call(xn=FAKE + 8) == 2
+    assert call(ldx=100) == 2 and call(ldxn=6146) == 2
+    assert call(eps=-1.0) == 2
+    assert call(ro=FAKE, ldro=6144) == 2          # residual_out without a residual
+    assert call(r=FAKE, ldr=6100) == 2
+    assert call(rstd=FAKE + 1) == 2
