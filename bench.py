@@ -17,8 +17,8 @@ Prints ONE JSON line: value = algorithmic bytes of the K steps / their time
 and the CPU oracle's rate on a bounded sample. Secondary figures ride along
 in the same line: the resident-W (hot) times, the wide-batch and many-expert
 shapes, the MXFP4 variant at the 128-expert top-4 point, the prefill call with
-its router GEMM against the bf16 MFMA peak, and the host cost of one eager
-call.
+its router GEMM against the bf16 MFMA peak, the RMSNorm producer (alone and in
+front of the routing call), and the host cost of one eager call.
 """
 from __future__ import annotations
 
@@ -156,6 +156,42 @@ def secondary(torch, R, dev, stream, copies_128: int):
     res["prefill_M8192_N896_K3584_top16_B64_dup5pct"] = {
         "us": round(full, 2), "launches": launches, "router_gemm_us": round(router, 2),
         "router_gemm_tflops": round(tflops, 1), "mfma_frac_bf16": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+    # The RMSNorm producer (Gemma weights, residual add, rstd published) in
+    # front of the routing call: decode sizes alone and followed by the fused
+    # call (two launches), and the prefill size against the HBM peak.
+    from router_gemv_top_amd.inputs import gen_x as _gx
+    rng = np.random.default_rng([0, 9])
+    gam6 = torch.from_numpy(np.asarray(rng.standard_normal(K) * 0.1, np.float32)).to(dev).to(torch.bfloat16)
+    w_r = dev_bf16(_gx(N, K, seed=5))
+    norm = {}
+    for m in (1, 8, 64):
+        xa, ra = dev_bf16(_gx(m, K, seed=m)), dev_bf16(_gx(m, K, seed=m + 1))
+        xn = torch.empty_like(xa)
+        rs = torch.empty((m,), dtype=torch.float32, device=dev)
+        ro = torch.empty_like(xa)
+        us_n = _graph_us(torch, stream, 64, lambda i: R.rmsnorm(xa, gam6, 1e-6, residual=ra, xn=xn, rstd=rs,
+                                                                residual_out=ro))
+        wl = type("W", (), {"m": m, "n": N, "k": K, "topk": TOPK, "block": BLOCK})
+        ws = R.Workspace(m, N, K, TOPK, BLOCK, device=dev)
+        o = outputs(wl)
+
+        def both(i):
+            R.rmsnorm(xa, gam6, 1e-6, residual=ra, xn=xn, rstd=rs, residual_out=ro)
+            R.route_sort_quant(xn, w_r, TOPK, BLOCK, ws, out=o)
+        us_b = _graph_us(torch, stream, 64, both)
+        norm[str(m)] = {"norm_us": round(us_n, 3), "norm_plus_route_us": round(us_b, 3)}
+    mp, kp = 8192, 3584
+    gamp = torch.from_numpy(np.asarray(rng.standard_normal(kp) * 0.1, np.float32)).to(dev).to(torch.bfloat16)
+    xa, ra = dev_bf16(_gx(mp, kp, seed=7)), dev_bf16(_gx(mp, kp, seed=8))
+    xn, ro = torch.empty_like(xa), torch.empty_like(xa)
+    rs = torch.empty((mp,), dtype=torch.float32, device=dev)
+    us_p = _graph_us(torch, stream, 10, lambda i: R.rmsnorm(xa, gamp, 1e-6, residual=ra, xn=xn, rstd=rs,
+                                                            residual_out=ro))
+    nbytes = 8 * mp * kp + 4 * mp + 2 * kp     # x, residual read; xn, residual_out written; rstd; gamma
+    res["rmsnorm_K6144_residual"] = {"per_m": norm, "hot_inputs": True}
+    res["rmsnorm_M8192_K3584_residual"] = {"us": round(us_p, 2), "gbs": round(nbytes / (us_p * 1e-6) / 1e9, 1),
+                                           "hbm_frac": round(nbytes / (us_p * 1e-6) / 1e9 / HBM_PEAK_GBS, 3)}
 
     # Host cost of one eager call at M=1 (argument marshalling + launch), and
     # the eager wall time per call once the queue has drained.
