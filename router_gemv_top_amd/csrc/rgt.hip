@@ -40,6 +40,7 @@ constexpr int kFusedMaxM = 64;
 
 thread_local int g_last_launches = 0;
 std::atomic<bool> g_sort_lds_set{false};  // the one-workgroup sort may use more than 64 KB of LDS
+constexpr int kSortSmallMaxLds = 120 * 1024;
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -335,7 +336,8 @@ void launch_gate_partials(const float* part, int S, float* logits, const float* 
   }
 }
 
-// Sort + quant as separate launches. Returns the number of launches.
+// Sort + quant as separate launches. Returns the number of launches, or -1
+// if the sort's LDS allowance could not be set (nothing launched).
 int launch_sort_quant(const int32_t* ids, const uint16_t* x, int64_t ldx, int m, int n, int k, int topk, int block,
                       int32_t* sorted_ids, int32_t* expert_ids, int32_t* offsets, uint8_t* a_q, uint8_t* a_scale,
                       bool fp4, char* ws, const Layout& L, hipStream_t st) {
@@ -346,9 +348,15 @@ int launch_sort_quant(const int32_t* ids, const uint16_t* x, int64_t ldx, int m,
     const int threads = P <= kWaveSortMaxP ? 256 : 1024;
     const size_t lds =
         sizeof(int) * ((size_t)P + std::max<size_t>(P, (size_t)(threads / 64) * n) + n + (n + 1) + threads);
-    if (lds > 65536 && !g_sort_lds_set.exchange(true))
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(sort_small_kernel),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    // Above 64 KB of dynamic LDS the kernel must be allowed more: the largest
+    // need (P = 8192, N = 1024, sixteen waves) is 110.6 KB, which with the
+    // kernel's static LDS stays under the 160 KB of a CU.
+    if (lds > 65536 && !g_sort_lds_set.load()) {
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(sort_small_kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kSortSmallMaxLds) != hipSuccess)
+        return -1;
+      g_sort_lds_set.store(true);
+    }
     hipLaunchKernelGGL(sort_small_kernel, dim3(1), dim3(threads), lds, st, ids, P, n, block, sorted_ids, expert_ids,
                        offsets, pos);
     ++launches;
@@ -598,9 +606,10 @@ static rgt_status moe_sort_quant_impl(const int32_t* topk_ids, const void* x, in
   if (!topk_ids || !aligned(topk_ids, 4)) return RGT_ERR_INVALID;
   const Layout L = make_layout(m, n, k, topk);
   if ((st = check_ws(ws, ws_bytes, L.total)) != RGT_OK) return st;
-  g_last_launches = launch_sort_quant(topk_ids, static_cast<const uint16_t*>(x), ldx, m, n, k, topk, block,
-                                      sorted_ids, expert_ids, offsets, a_q, a_scale, fp4, static_cast<char*>(ws), L,
-                                      stream);
+  const int nl = launch_sort_quant(topk_ids, static_cast<const uint16_t*>(x), ldx, m, n, k, topk, block, sorted_ids,
+                                   expert_ids, offsets, a_q, a_scale, fp4, static_cast<char*>(ws), L, stream);
+  if (nl < 0) return RGT_ERR_HIP;
+  g_last_launches = nl;
   return launched();
 }
 
@@ -692,6 +701,7 @@ static rgt_status route_sort_quant_impl(const void* x, int64_t ldx, const void* 
   }
   const int nl = launch_sort_quant(topk_ids, static_cast<const uint16_t*>(x), ldx, m, n, k, topk, block, sorted_ids,
                                    expert_ids, offsets, a_q, a_scale, fp4, base, L, stream);
+  if (nl < 0) return RGT_ERR_HIP;
   g_last_launches = 2 + nl;
   return launched();
 }

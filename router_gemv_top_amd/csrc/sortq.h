@@ -60,9 +60,14 @@ __device__ __forceinline__ int ceil_log2(int n) { return n <= 1 ? 0 : 32 - __clz
 __device__ __forceinline__ int pad_to(int c, int B) { return (c + B - 1) & -B; }
 __device__ __forceinline__ int div_pow2(int a, int B) { return a >> (__ffs(B) - 1); }
 
-// Exclusive scan of vals[0..n) in LDS (in place), n <= 4 * blockDim.x.
-// Returns the total. Uses scratch[blockDim.x] of LDS.
+// Exclusive scan of vals[0..n) in LDS (in place). Returns the total. Each
+// thread sums a contiguous run of ceil(n / blockDim.x) values; wave 0 scans
+// the thread sums (each lane a contiguous run of blockDim.x / 64 of them, then
+// a DPP wave scan) and every thread writes its run's prefixes: two barriers
+// whatever the workgroup size (a tree over the threads would need two per
+// level). blockDim.x is a multiple of 64. Uses scratch[blockDim.x] of LDS.
 __device__ __forceinline__ int block_exclusive_scan(int* vals, int n, int* scratch) {
+  __shared__ int s_total;
   const int t = threadIdx.x, nt = blockDim.x;
   const int per = (n + nt - 1) / nt;
   const int b0 = min(n, t * per), b1 = min(n, b0 + per);
@@ -70,20 +75,27 @@ __device__ __forceinline__ int block_exclusive_scan(int* vals, int n, int* scrat
   for (int i = b0; i < b1; ++i) local += vals[i];
   scratch[t] = local;
   __syncthreads();
-  // Hillis-Steele inclusive scan of the thread sums.
-  for (int o = 1; o < nt; o <<= 1) {
-    const int v = t >= o ? scratch[t - o] : 0;
-    __syncthreads();
-    scratch[t] += v;
-    __syncthreads();
+  if (t < 64) {
+    const int q = nt >> 6;
+    int sum = 0;
+    for (int i = 0; i < q; ++i) sum += scratch[t * q + i];
+    const int incl = wave_inclusive_scan(sum);
+    int run = incl - sum;
+    for (int i = 0; i < q; ++i) {
+      const int v = scratch[t * q + i];
+      scratch[t * q + i] = run;
+      run += v;
+    }
+    if (t == 63) s_total = incl;
   }
-  int run = scratch[t] - local;
-  const int total = scratch[nt - 1];
+  __syncthreads();
+  int run = scratch[t];
   for (int i = b0; i < b1; ++i) {
     const int v = vals[i];
     vals[i] = run;
     run += v;
   }
+  const int total = s_total;
   __syncthreads();
   return total;
 }
