@@ -193,6 +193,14 @@ def secondary(torch, R, dev, stream, copies_128: int):
     res["rmsnorm_M8192_K3584_residual"] = {"us": round(us_p, 2), "gbs": round(nbytes / (us_p * 1e-6) / 1e9, 1),
                                            "hbm_frac": round(nbytes / (us_p * 1e-6) / 1e9 / HBM_PEAK_GBS, 3)}
 
+    # Practical HBM rate of a plain device copy (256 MiB each way), the
+    # context for the write-heavy quant of the prefill call.
+    src = torch.randint(0, 255, (256 << 20,), dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    us_c = _graph_us(torch, stream, 5, lambda i: R.diag_copy(src, dst, 2048))
+    res["copy_256MiB"] = {"us": round(us_c, 2), "gbs_read_plus_write": round(2 * (256 << 20) / (us_c * 1e-6) / 1e9, 1)}
+    del src, dst
+
     # Host cost of one eager call at M=1 (argument marshalling + launch), and
     # the eager wall time per call once the queue has drained.
     wl = workloads_decode_896((1,))[0]
@@ -432,6 +440,9 @@ def main():
         "launches_per_call": {str(m): launches[m] for m in SWEEP},
         "floor_us": {"empty_launch": round(launch_floor_us, 3),
                      "stream_read_W": round(read_floor_us, 3)},
+        # one launch that must read W cannot beat the streaming read of W:
+        # the fraction of that latency floor each call reaches
+        "floor_frac": {str(m): round(read_floor_us / us_per_call[m], 3) for m in SWEEP},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": traffic,
                      "algorithmic_bytes_per_launch": round(sum(sweep_bytes.values()) / len(SWEEP), 1),
