@@ -111,7 +111,7 @@ __device__ __forceinline__ int block_exclusive_scan(int* vals, int n, int* scrat
 // COH: the ids were written by other workgroups of the same launch.
 template <bool COH, typename PosPtr>
 __device__ int wg_sort(const int32_t* ids, int P, int N, int B, int* s_e, int* s_hist, int* s_cnt, int* s_off,
-                       int* s_scr, PosPtr pos) {
+                       int* s_scr, PosPtr pos, int32_t* sorted_ids = nullptr) {
   const int t = threadIdx.x, nt = blockDim.x, nw = nt >> 6;
   const int wave = t >> 6, lane = t & 63;
   for (int p = t; p < P; p += nt) s_e[p] = COH ? ld_agent(ids + p) : ids[p];
@@ -126,15 +126,34 @@ __device__ int wg_sort(const int32_t* ids, int P, int N, int B, int* s_e, int* s
   }
   __syncthreads();
   // Per-expert totals; per-wave counts become exclusive per-wave bases.
-  for (int e = t; e < N; e += nt) {
-    int run = 0;
-    for (int w = 0; w < nw; ++w) {
-      const int c = s_hist[w * N + e];
-      s_hist[w * N + e] = run;
-      run += c;
+  if (nw == 16) {
+    // One 16-lane row per expert (lane = wave index w): a DPP scan inside the
+    // row. N*16 is a multiple of 256, so whole waves take part.
+    for (int idx = t; idx < N * 16; idx += nt) {
+      const int e = idx >> 4, w = idx & 15;
+      const int v = s_hist[w * N + e];
+      int incl = v;
+      incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xF, 0xF, true);  // row_shr:1
+      incl += __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xF, 0xF, true);  // row_shr:2
+      incl += __builtin_amdgcn_update_dpp(0, incl, 0x114, 0xF, 0xF, true);  // row_shr:4
+      incl += __builtin_amdgcn_update_dpp(0, incl, 0x118, 0xF, 0xF, true);  // row_shr:8
+      s_hist[w * N + e] = incl - v;
+      if (w == 15) {
+        s_cnt[e] = incl;
+        s_off[e] = pad_to(incl, B);
+      }
     }
-    s_cnt[e] = run;
-    s_off[e] = pad_to(run, B);
+  } else {
+    for (int e = t; e < N; e += nt) {
+      int run = 0;
+      for (int w = 0; w < nw; ++w) {
+        const int c = s_hist[w * N + e];
+        s_hist[w * N + e] = run;
+        run += c;
+      }
+      s_cnt[e] = run;
+      s_off[e] = pad_to(run, B);
+    }
   }
   __syncthreads();
   const int total = block_exclusive_scan(s_off, N, s_scr);
@@ -151,7 +170,9 @@ __device__ int wg_sort(const int32_t* ids, int P, int N, int B, int* s_e, int* s
     const u64 peers = match_peers(e, valid, bits);
     if (valid) {
       const int rank = __popcll(peers & lanemask_lt());
-      pos[p] = s_off[e] + s_hist[wave * N + e] + rank;
+      const int q = s_off[e] + s_hist[wave * N + e] + rank;
+      pos[p] = q;
+      if (sorted_ids) sorted_ids[q] = p;
     } else if (p < c1) {
       pos[p] = -1;
     }

@@ -26,14 +26,18 @@ __global__ void __launch_bounds__(1024) sort_small_kernel(const int32_t* ids, in
     if (threadIdx.x < 64) wave_sort<16>(ids, P, N, B, s_e, s_hist, s_cnt, s_off, pos_ws);
     vm_drain();
     __syncthreads();
+    for (int p = threadIdx.x; p < P; p += blockDim.x) {
+      const int q = pos_ws[p];
+      if (q >= 0) sorted_ids[q] = p;
+    }
+    write_sort_layout(s_cnt, s_off, N, B, P, sorted_ids, expert_ids, offsets);
   } else {
-    wg_sort<false>(ids, P, N, B, s_e, s_hist, s_cnt, s_off, s_scr, pos_ws);
+    // Every wave (launched with 1024 threads): the pairs' sorted_ids entries
+    // go out as their positions are found, the pads and expert_ids one item
+    // per (expert, slot) from consecutive lanes.
+    wg_sort<false>(ids, P, N, B, s_e, s_hist, s_cnt, s_off, s_scr, pos_ws, sorted_ids);
+    write_layout<1024>(s_cnt, s_off, N, B, P, 0, N, sorted_ids, expert_ids, offsets);
   }
-  for (int p = threadIdx.x; p < P; p += blockDim.x) {
-    const int q = pos_ws[p];
-    if (q >= 0) sorted_ids[q] = p;
-  }
-  write_sort_layout(s_cnt, s_off, N, B, P, sorted_ids, expert_ids, offsets);
 }
 
 // ---------------------------------------------------------------------------
