@@ -366,7 +366,8 @@ int launch_sort_quant(const int32_t* ids, const uint16_t* x, int64_t ldx, int m,
     int32_t* offws = reinterpret_cast<int32_t*>(ws + L.offws);
     hipLaunchKernelGGL(sort_hist_kernel, dim3(G), dim3(256), sizeof(int) * n, st, ids, P, n, kLargeSortChunk,
                        ghist);
-    hipLaunchKernelGGL(sort_colscan_kernel, dim3((n + 63) / 64), dim3(256), 0, st, ghist, G, n, offws);
+    hipLaunchKernelGGL(sort_colscan_kernel, dim3((n + 63) / 64), dim3(64 * kColscanWaves), 0, st, ghist, G, n,
+                       offws);
     hipLaunchKernelGGL(sort_scan_kernel, dim3(1), dim3(1024), sizeof(int) * ((size_t)(n + 1) + 1024), st, n, block,
                        offws);
     hipLaunchKernelGGL(sort_scatter_kernel, dim3(G), dim3(256), sizeof(int) * (4 * (size_t)n + n + (n + 1) + n), st,

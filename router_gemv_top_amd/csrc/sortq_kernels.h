@@ -59,15 +59,17 @@ __global__ void __launch_bounds__(256) sort_hist_kernel(const int32_t* ids, int 
 
 // Per-group bases of the large sort: for every expert, an exclusive prefix
 // of its counts over the G groups (in place in ghist) and its total (to
-// cnt[e]). Workgroup b takes experts [64b, 64b + 64) (lane = expert); wave w
-// takes a quarter of the groups, and the four quarters are joined through
-// LDS. Loads go 8 at a time so their latencies overlap.
-__global__ void __launch_bounds__(256) sort_colscan_kernel(int32_t* ghist, int G, int N, int32_t* cnt) {
-  __shared__ int s_part[4][64];
+// cnt[e]). Workgroup b takes experts [64b, 64b + 64) (lane = expert) with
+// sixteen waves; wave w takes a sixteenth of the groups, and the sixteen parts
+// are joined through LDS. Loads go 8 at a time so their latencies overlap
+// (at the prefill size each lane walks 16 groups: two batches a pass).
+constexpr int kColscanWaves = 16;
+__global__ void __launch_bounds__(1024) sort_colscan_kernel(int32_t* ghist, int G, int N, int32_t* cnt) {
+  __shared__ int s_part[kColscanWaves][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int e = blockIdx.x * 64 + lane;
   const int ec = min(e, N - 1);
-  const int gq = (G + 3) >> 2, g0 = min(G, wave * gq), g1 = min(G, g0 + gq);
+  const int gq = (G + kColscanWaves - 1) / kColscanWaves, g0 = min(G, wave * gq), g1 = min(G, g0 + gq);
   int sum = 0;
   for (int g = g0; g < g1; g += 8) {
     int v[8];
@@ -80,7 +82,11 @@ __global__ void __launch_bounds__(256) sort_colscan_kernel(int32_t* ghist, int G
   __syncthreads();
   int run = 0;
   for (int w = 0; w < wave; ++w) run += s_part[w][lane];
-  if (wave == 0 && e < N) cnt[e] = s_part[0][lane] + s_part[1][lane] + s_part[2][lane] + s_part[3][lane];
+  if (wave == 0 && e < N) {
+    int total = 0;
+    for (int w = 0; w < kColscanWaves; ++w) total += s_part[w][lane];
+    cnt[e] = total;
+  }
   if (e >= N) return;
   for (int g = g0; g < g1; g += 8) {
     int v[8];
