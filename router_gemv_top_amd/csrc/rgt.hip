@@ -387,10 +387,15 @@ int launch_sort_quant(const int32_t* ids, const uint16_t* x, int64_t ldx, int m,
 // ---------------------------------------------------------------------------
 // Fused launch (M <= 64).
 // ---------------------------------------------------------------------------
-// Small mode when one gather of every row fits the per-thread loads.
-// (and while every wave has at most one row's gate to run: beyond that, one
-// more hand-off costs less than a second gate in series).
-bool fused_small(const Plan& p, int m, int n) { return m <= 4 && gather_loads(m, n, p.s) <= kPollLoads; }
+// Small mode when one gather of every row fits the per-thread loads (and
+// while every wave has at most one row's gate to run: beyond that, one more
+// hand-off costs less than a second gate in series). Measured on MI355X: at N = 128 small mode wins up to M = 4; at N = 896
+// (top-16) it wins up to M = 2 and large mode beyond (M = 3, 4: 13.4, 13.8
+// -> 12.4, 12.5 us), where each participant's gates of many experts cost more
+// than the ids hand-off.
+bool fused_small(const Plan& p, int m, int n) {
+  return m <= (n > 256 ? 2 : 4) && gather_loads(m, n, p.s) <= kPollLoads;
+}
 
 size_t fused_lds_bytes(const Plan& p, int m, int n, int topk, bool small) {
   const int P = m * topk;
