@@ -66,7 +66,7 @@ struct FusedArgs {
   int topk, block;
   int small;           // 1: small mode, 0: large mode (chosen by the host)
   int fp4;             // 1: MXFP4 rows (K/2 bytes of packed e2m1 codes), 0: MXFP8
-  int upw_log;         // log2 of the quant units per participating workgroup (6, 7 or 8)
+  int upw_log;         // log2 of the quant units per quant workgroup (6, 7 or 8)
   u32 cpr_magic;       // ceil(2^32 / (K/16)): token of a quant unit by multiplication
   float* logits_out;   // [M][N] or null
   int32_t* topk_ids;
@@ -450,8 +450,10 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, Tile t
 
 // Quant units (16-element chunks of x, row-major) go 2^upw_log to a
 // workgroup, to its first threads (the host guarantees M*K/16 <= grid *
-// 2^upw_log): fewer units per workgroup spread the stores of the tail over
-// more CUs.
+// 2^upw_log). Small mode takes the fewest units per workgroup that cover
+// them all (the tail's stores spread over more CUs); large mode the most
+// whose token pairs fit one wave (fewer quant workgroups, each with its rows
+// gated sooner).
 template <int NV, int MT, int RPW, int L>
 __global__ void __launch_bounds__(256) fused_valu_kernel(FusedArgs a) {
   extern __shared__ int smem[];

@@ -669,13 +669,24 @@ static rgt_status route_sort_quant_impl(const void* x, int64_t ldx, const void* 
     fn = fused_kernel_for(p, n);
     lds = fused_lds_bytes(p, m, n, topk, small);
     const int units = m * (k / 16);
-    upw_log = 6;
-    while (upw_log < 8 && ((units + (1 << upw_log) - 1) >> upw_log) > p.grid) ++upw_log;
     // A workgroup's quant units cover at most this many tokens; their pairs
     // must fit one wave.
     const int cpr = k / 16;
-    const bool pairs_fit = (((1 << upw_log) - 1) / cpr + 2) * topk <= 64 &&
-                           (uint64_t)(p.grid << upw_log) * (uint64_t)cpr < (1ull << 32);  // exact magic division
+    auto pairs_fit_at = [&](int ul) {
+      return (((1 << ul) - 1) / cpr + 2) * topk <= 64 &&
+             (uint64_t)(p.grid << ul) * (uint64_t)cpr < (1ull << 32);  // exact magic division
+    };
+    if (small) {
+      // the fewest units per workgroup that cover every unit
+      upw_log = 6;
+      while (upw_log < 8 && ((units + (1 << upw_log) - 1) >> upw_log) > p.grid) ++upw_log;
+    } else {
+      // large mode: the most units per workgroup whose pairs fit one wave
+      // (fewer, fuller quant workgroups start their units sooner)
+      upw_log = 8;
+      while (upw_log > 6 && !pairs_fit_at(upw_log) && units <= (p.grid << (upw_log - 1))) --upw_log;
+    }
+    const bool pairs_fit = pairs_fit_at(upw_log);
     // Co-residency is required for the device-side waits; each thread owns at
     // most one quant unit; in large mode workgroup r gathers row r.
     if (p.grid > coresident_blocks(fn, lds, di.cus) || units > (p.grid << upw_log) || !pairs_fit ||
