@@ -26,6 +26,11 @@ Sources (titles of the pages this follows):
   [M3R]   sglang PR #46691 (MiniMax-M3.1-Flash MoE/GEMM kernels), Summary:
           fp8 producers (the Gemma RMSNorm (+ residual) producers in front of
           the next GEMM) and the measured gain of those producers.
+  [FUSE]  sglang PR #46691 (MiniMax-M3.1-Flash MoE/GEMM kernels), Summary:
+          Router (the split-K partials exposed and fused with the shared
+          expert's fp8 SwiGLU in one launch) and GEMM (the M3.1 shared
+          expert's 1536 x 6144 gate_up); [MONO] MXFP8 shared-expert commit
+          (fp8 values with one scale per 32 elements along K).
   [OCP]   OCP Microscaling Formats (MX) v1.0: e4m3 element format (bias 7,
           max normal 448, no infinities), e8m0 shared scale (bias 127), shared
           exponent = floor(log2(amax)) - emax_elem with emax_elem = 8 for e4m3;
@@ -55,6 +60,14 @@ notes):
     quant): the same floor rule with emax_elem = 2 for e2m1, round to nearest
     even, saturation to +-6, sign kept (-0 -> 0x8); two codes a byte, the
     even element in the low nibble.
+
+  * Shared expert ([FUSE]): gate_up is [2I][K] MXFP8, the I gate rows first,
+    then the I up rows; element (r, i) = e4m3(code) * 2^(scale[r][i/32] - 127).
+    g = x . Wg^T, u = x . Wu^T (exact products, fp64 sums); SwiGLU
+    h = silu(g) * u with silu(g) = g / (1 + exp(-g)), no clamp; the kernel
+    rounds h once to bf16.
+  * Router partials: k-slice s covers K/S consecutive elements
+    [s*K/S, (s+1)*K/S); part[s] = fp32(sum over the slice), summed in fp64.
 
 Parity pins: every function here is checked by the ``-m "not gpu"`` tests
 against brute force, exact rationals, closed forms or invariants.
@@ -466,3 +479,80 @@ def route_sort_quant(x_bits, w_bits, bias, k: int, block: int, fmt: str = "mxfp8
     out = moe_sort_quant(ids, x_bits, w_bits.shape[0], block, fmt=fmt)
     out.update(logits=logits, topk_ids=ids, topk_w=w)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Router split-K partials and the shared expert's SwiGLU [FUSE], [MONO], [OCP]
+# ---------------------------------------------------------------------------
+
+
+def router_partials(x_bits: np.ndarray, w_bits: np.ndarray, s: int) -> np.ndarray:
+    """part [S][M][N] fp32: part[s] = fp32( sum over k-slice s of x * W ), the
+    slice being K/S consecutive elements (fp64 sums of exact products, rounded
+    once). Summed over s they give the logits ([GEMV] opening summary)."""
+    x = bf16_bits_to_f64(x_bits)
+    w = bf16_bits_to_f64(w_bits)
+    k = x.shape[1]
+    assert k % s == 0
+    ks = k // s
+    return np.stack([(x[:, i * ks:(i + 1) * ks] @ w[:, i * ks:(i + 1) * ks].T).astype(np.float32)
+                     for i in range(s)])
+
+
+def e4m3_value(codes: np.ndarray) -> np.ndarray:
+    """Exact fp64 value of e4m3fn codes [OCP]: bit 7 the sign, bits 6..3 the
+    exponent (bias 7), bits 2..0 the mantissa; exponent field 0 holds the
+    subnormals mant * 2^-9; 0x7F and 0xFF are NaN (no infinities)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    e = (c >> 3) & 0xF
+    mant = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(mant, -9), np.ldexp(8.0 + mant, e - 10))
+    val = np.where(c & 0x80, -mag, mag)
+    return np.where((c & 0x7F) == 0x7F, np.nan, val)
+
+
+def e8m0_value(scales: np.ndarray) -> np.ndarray:
+    """2^(b - 127) for the e8m0 scale byte b [OCP]; 255 is NaN."""
+    b = np.asarray(scales, dtype=np.uint8).astype(np.int64)
+    return np.where(b == 255, np.nan, np.ldexp(1.0, b - 127))
+
+
+def mxfp8_dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """fp64 [R][K] values of MXFP8 rows: code [R][K] e4m3fn, scale [R][K/32]
+    e8m0, element (r, i) = e4m3(code[r][i]) * 2^(scale[r][i // 32] - 127)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    sc = np.asarray(scales, dtype=np.uint8)
+    assert c.ndim == 2 and sc.shape == (c.shape[0], c.shape[1] // MX_BLOCK) and c.shape[1] % MX_BLOCK == 0
+    return e4m3_value(c) * np.repeat(e8m0_value(sc), MX_BLOCK, axis=1)
+
+
+def shared_gate_up(x_bits: np.ndarray, wq: np.ndarray, ws: np.ndarray) -> np.ndarray:
+    """gu [M][2I] fp64 = x . W^T with W the dequantised MXFP8 gate_up
+    weights (bf16 x e4m3 * 2^e products are exact in fp64)."""
+    x = bf16_bits_to_f64(x_bits)
+    w = mxfp8_dequant(wq, ws)
+    assert np.all(np.isfinite(x)) and np.all(np.isfinite(w))
+    return x @ w.T
+
+
+def silu(g: np.ndarray) -> np.ndarray:
+    """silu(g) = g / (1 + exp(-g)) in fp64 (g * sigmoid(g))."""
+    g = np.asarray(g, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def swiglu(gu: np.ndarray, inter: int) -> np.ndarray:
+    """h [M][I] = silu(g) * u with g = gu[:, :I] (gate rows first) and
+    u = gu[:, I:2I] (up rows), in fp64."""
+    gu = np.asarray(gu, dtype=np.float64)
+    assert gu.shape[1] == 2 * inter
+    return silu(gu[:, :inter]) * gu[:, inter:]
+
+
+def shared_swiglu(x_bits: np.ndarray, wq: np.ndarray, ws: np.ndarray):
+    """(h fp64 [M][I], g [M][I], u [M][I]) of the shared expert's gate/up and
+    SwiGLU on MXFP8 gate_up weights wq [2I][K], ws [2I][K/32]."""
+    gu = shared_gate_up(x_bits, wq, ws)
+    inter = gu.shape[1] // 2
+    return swiglu(gu, inter), gu[:, :inter], gu[:, inter:]

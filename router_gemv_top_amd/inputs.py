@@ -13,7 +13,10 @@ Modifications).
 Random streams: ``numpy.random.default_rng([seed, stream])`` with one
 independent stream per tensor, so W does not change when M changes:
 stream 0 = x, 1 = W, 2 = bias, 3 = the duplicated-row choice, 4 = W-row ties,
-5 = skew bias.
+5 = skew bias, 6 = the shared expert's MXFP8 gate_up weights.
+
+The shared expert's shape is MiniMax-M3.1's 1536 x 6144 gate_up (768 gate
+rows, then 768 up rows; "MiniMax-M3.1-Flash MoE/GEMM kernels", Summary: GEMM).
 """
 from __future__ import annotations
 
@@ -22,7 +25,7 @@ from typing import Optional
 
 import numpy as np
 
-STREAM_X, STREAM_W, STREAM_BIAS, STREAM_DUP, STREAM_WTIE, STREAM_SKEW = range(6)
+STREAM_X, STREAM_W, STREAM_BIAS, STREAM_DUP, STREAM_WTIE, STREAM_SKEW, STREAM_SHARED = range(7)
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -114,6 +117,18 @@ class Workload:
         w = gen_w(self.n, self.k, self.seed)
         b = gen_bias(self.n, self.seed) if self.bias else None
         return x, w, b
+
+
+def gen_mxfp8_weights(rows: int, k: int, seed: int = 0, scale_lo: int = 110, scale_hi: int = 116):
+    """(codes uint8 [rows][K], scales uint8 [rows][K/32]) of random MXFP8
+    weights: element codes uniform over the 254 non-NaN e4m3fn bytes (the NaN
+    bytes 0x7F and 0xFF are redrawn as 0x00), scale bytes uniform in
+    [scale_lo, scale_hi), so elements are at most 448 * 2^(scale_hi - 128)."""
+    rng = _rng(seed, STREAM_SHARED)
+    codes = rng.integers(0, 256, size=(rows, k), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0
+    scales = rng.integers(scale_lo, scale_hi, size=(rows, k // 32), dtype=np.uint8)
+    return codes, scales
 
 
 def workloads_decode_128(ms=(1, 2, 4, 8, 16, 32, 64)):
