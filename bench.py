@@ -141,6 +141,33 @@ def secondary(torch, R, dev, stream, copies_128: int):
         res[group] = {"w_copies": copies, "per_m": per}
         del w_all
 
+    # Router k-slice partials + the shared expert's MXFP8 gate/up SwiGLU in one
+    # launch (MiniMax-M3.1 decode: 128 experts, hidden 6144, gate_up 1536 x
+    # 6144), router W and shared-expert weights cold (rotating copies).
+    from router_gemv_top_amd.inputs import gen_mxfp8_weights, gen_w as _gw, gen_x as _gx0
+    inter = 768
+    wq, wsc = gen_mxfp8_weights(2 * inter, K, seed=3)
+    w_r = _gw(N, K, seed=3)
+    w_bytes = w_r.size * 2 + wq.size + wsc.size
+    copies = min(copies_128, int(np.ceil(2 * MALL_BYTES / w_bytes)))
+    wr_all = dev_bf16(w_r).unsqueeze(0).repeat(copies, 1, 1)
+    wq_all = torch.from_numpy(wq).to(dev).unsqueeze(0).repeat(copies, 1, 1)
+    ws_all = torch.from_numpy(wsc).to(dev).unsqueeze(0).repeat(copies, 1, 1)
+    per = {}
+    for m in (1, 2, 4, 8, 16):
+        xw = dev_bf16(_gx0(m, K, seed=m))
+        s = R.router_partial_slices(m, N, K)
+        part = torch.empty((s, m, N), dtype=torch.float32, device=dev)
+        h = torch.empty((m, inter), dtype=torch.bfloat16, device=dev)
+        us = _graph_us(torch, stream, copies, lambda i: R.router_shared_swiglu(
+            xw, wr_all[i], wq_all[i], ws_all[i], part=part, h=h))
+        nbytes = w_bytes + m * K * 2 + s * m * N * 4 + m * inter * 2
+        gbs = nbytes / (us * 1e-6) / 1e9
+        per[str(m)] = {"us": round(us, 3), "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 3),
+                       "launches": R.last_launch_count(), "slices": s}
+    res["router_partials_shared_swiglu_N128_K6144_I768_mxfp8"] = {"w_copies": copies, "per_m": per}
+    del wr_all, wq_all, ws_all
+
     wl = workload_prefill_896()
     x, w, _ = wl.make()
     xd, wd = dev_bf16(x), dev_bf16(w)

@@ -137,6 +137,38 @@ rgt_status rgt_topk_gate(const float* logits, const float* bias, int m, int n, i
 rgt_status rgt_topk_gate_partials(const float* part, int s, const float* bias, int m, int n, int topk,
                                   float* logits, int32_t* topk_ids, float* topk_w, hipStream_t stream);
 
+/* Number of k-slices S of the router partials rgt_router_shared_swiglu
+ * writes for this shape (each slice K/S consecutive elements), or 0 for a
+ * shape it does not cover (M outside 1..16, K above 8192, or outside the
+ * router's shapes). Size part as S*M*N floats. */
+int rgt_router_partial_slices(int m, int n, int k);
+
+/* Router split-K partials and the shared expert's gate/up SwiGLU in one
+ * launch (MiniMax-M3.1-Flash MoE/GEMM kernels page, Summary: Router: the
+ * router's split-K partials, summed in order by the gate, fused with the
+ * shared expert's fp8 SwiGLU; Summary: GEMM: the 1536 x 6144 gate_up;
+ * MXFP8 shared-expert weights: monokernel page, MXFP8 shared-expert commit).
+ *   x         : bf16 [M][ldx], device (read by both parts)
+ *   w         : bf16 [N][ldw], device (router weights)
+ *   part      : fp32 [S][M][N], device, 16-byte aligned, written:
+ *               part[s][m][n] = fp32 sum over k in [s*K/S, (s+1)*K/S) of
+ *               x[m][k]*W[n][k]; S must equal rgt_router_partial_slices(M, N,
+ *               K). Feed it to rgt_topk_gate_partials.
+ *   wsh_q     : uint8 [2I][K] e4m3fn codes, device, 16-byte aligned, rows
+ *               K bytes apart: rows 0..I-1 the gate projection, I..2I-1 up.
+ *   wsh_scale : uint8 [2I][K/32] e8m0 scale bytes (element (r, i) is
+ *               e4m3(code) * 2^(scale[r][i/32] - 127)), device.
+ *   h         : bf16 [M][ldh], device, written for columns < I:
+ *               h[m][j] = bf16_rne( silu(g) * u ), g = x[m].Wg[j],
+ *               u = x[m].Wu[j], silu(g) = g / (1 + exp(-g)), fp32 sums.
+ * 0 <= M <= 16, K <= 8192 and the router's shape rules (N a multiple of 16
+ * in [16, 1024], K a multiple of 512), 1 <= I <= 2^20, ldh >= I; otherwise
+ * RGT_ERR_UNSUPPORTED or RGT_ERR_INVALID and nothing is launched. NaN codes
+ * or a 255 scale give NaN outputs. One launch, no workspace. */
+rgt_status rgt_router_shared_swiglu(const void* x, int64_t ldx, const void* w, int64_t ldw, int m, int n, int k,
+                                    float* part, int s, const uint8_t* wsh_q, const uint8_t* wsh_scale, int inter,
+                                    void* h, int64_t ldh, hipStream_t stream);
+
 /* Sort (token, slot) pairs into block-padded expert segments and quantise
  * the gathered activations to MXFP8. Pair p = m*topk + j has expert
  * topk_ids[m][j] (each in [0, N)).

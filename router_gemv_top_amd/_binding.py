@@ -71,6 +71,8 @@ def lib() -> ctypes.CDLL:
                                          i32),
             "rgt_route_sort_quant_mxfp4": ([vp, i64, vp, i64, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
                                             vp, vp, vp, sz, vp], i32),
+            "rgt_router_partial_slices": ([i32, i32, i32], i32),
+            "rgt_router_shared_swiglu": ([vp, i64, vp, i64, i32, i32, i32, vp, i32, vp, vp, i32, vp, i64, vp], i32),
             "rgt_rmsnorm": ([vp, i64, vp, i64, vp, ctypes.c_float, i32, i32, vp, i64, vp, i64, vp, vp], i32),
             "rgt_last_launch_count": ([], i32),
             "rgt_diag_read": ([vp, sz, vp, i32, vp], i32),
@@ -174,6 +176,42 @@ def router_logits(x, w, ws: Workspace, logits=None, stream=None):
     _check(lib().rgt_router_logits(_ptr(x), x.stride(0), _ptr(w), w.stride(0), _ptr(logits), m, n, k,
                                    _ptr(ws.buf), ws.nbytes, _stream(stream)), "router_logits")
     return logits
+
+
+def router_partial_slices(m: int, n: int, k: int) -> int:
+    """S of the router partials router_shared_swiglu writes (0: not covered)."""
+    return int(lib().rgt_router_partial_slices(m, n, k))
+
+
+def router_shared_swiglu(x, w, wsh_q, wsh_scale, part=None, h=None, stream=None):
+    """(part fp32 [S][M][N], h bf16 [M][I]) from one launch: the router's
+    k-slice partials of x . W^T and the shared expert's SwiGLU
+    h = silu(x . Wg^T) * (x . Wu^T) on MXFP8 gate_up weights wsh_q uint8
+    [2I][K] (gate rows first) with e8m0 scales wsh_scale uint8 [2I][K/32]."""
+    _bf16_2d(x, "x"), _bf16_2d(w, "w")
+    m, k = x.shape
+    n = w.shape[0]
+    if wsh_q.dtype != torch.uint8 or wsh_q.dim() != 2 or not wsh_q.is_contiguous() or wsh_q.shape[1] != k:
+        raise ValueError("wsh_q must be a contiguous [2I][K] uint8 tensor")
+    if (wsh_scale.dtype != torch.uint8 or not wsh_scale.is_contiguous()
+            or tuple(wsh_scale.shape) != (wsh_q.shape[0], k // 32)):
+        raise ValueError("wsh_scale must be a contiguous [2I][K/32] uint8 tensor")
+    inter = wsh_q.shape[0] // 2
+    s = router_partial_slices(m, n, k) if m > 0 else 1
+    if s <= 0:
+        raise RgtUnsupported(RGT_ERR_UNSUPPORTED, "router_partial_slices")
+    if part is None:
+        part = torch.empty((s, m, n), dtype=torch.float32, device=x.device)
+    if h is None:
+        h = torch.empty((m, inter), dtype=torch.bfloat16, device=x.device)
+    if part.dtype != torch.float32 or not part.is_contiguous() or tuple(part.shape) != (s, m, n):
+        raise ValueError(f"part must be a contiguous [{s}][{m}][{n}] float32 tensor")
+    if h.dtype != torch.bfloat16 or h.dim() != 2 or h.stride(1) != 1 or h.shape[0] != m or h.shape[1] < inter:
+        raise ValueError("h must be a [M][>= I] bfloat16 tensor with unit column stride")
+    _check(lib().rgt_router_shared_swiglu(_ptr(x), x.stride(0), _ptr(w), w.stride(0), m, n, k, _ptr(part), s,
+                                          _ptr(wsh_q), _ptr(wsh_scale), inter, _ptr(h), h.stride(0),
+                                          _stream(stream)), "router_shared_swiglu")
+    return part, h
 
 
 def topk_gate(logits, topk: int, bias=None, ids=None, weights=None, stream=None):

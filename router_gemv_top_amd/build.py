@@ -54,6 +54,7 @@ def units(trace: bool):
     for nv in NV_BUCKETS:
         out.append((os.path.join(CSRC, "fused_inst.hip"), os.path.join(d, f"fused_nv{nv}.o"),
                     extra + [f"-DRGT_NV={nv}"]))
+    out.append((os.path.join(CSRC, "shared_inst.hip"), os.path.join(d, "shared_inst.o"), extra))
     return out
 
 

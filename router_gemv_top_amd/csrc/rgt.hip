@@ -23,6 +23,8 @@
 #include "gemm.h"
 #include "gemv.h"
 #include "norm.h"
+#include "shared.h"
+#include "shared_pick.h"
 #include "sortq.h"
 #include "sortq_kernels.h"
 
@@ -589,6 +591,34 @@ rgt_status rgt_rmsnorm(const void* x, int64_t ldx, const void* residual, int64_t
   else if (ch <= 2) hipLaunchKernelGGL(rmsnorm_kernel<2>, grid, blk, 0, stream, xs, ldx, rs, ldr, gs, eps, k, xo, ldxn, ro, ldro, rstd);
   else if (ch <= 4) hipLaunchKernelGGL(rmsnorm_kernel<4>, grid, blk, 0, stream, xs, ldx, rs, ldr, gs, eps, k, xo, ldxn, ro, ldro, rstd);
   else hipLaunchKernelGGL(rmsnorm_kernel<8>, grid, blk, 0, stream, xs, ldx, rs, ldr, gs, eps, k, xo, ldxn, ro, ldro, rstd);
+  g_last_launches = 1;
+  return launched();
+}
+
+int rgt_router_partial_slices(int m, int n, int k) {
+  if (m < 1 || m > kSharedMaxM || k > kSharedMaxK || !covered(m, n, k)) return 0;
+  return make_plan(m, n, k).s;
+}
+
+rgt_status rgt_router_shared_swiglu(const void* x, int64_t ldx, const void* w, int64_t ldw, int m, int n, int k,
+                                    float* part, int s, const uint8_t* wsh_q, const uint8_t* wsh_scale, int inter,
+                                    void* h, int64_t ldh, hipStream_t stream) {
+  g_last_launches = 0;
+  if (m < 0 || m > kSharedMaxM || k > kSharedMaxK || inter < 1 || inter > (1 << 20)) return RGT_ERR_UNSUPPORTED;
+  rgt_status st = check_gemv_args(x, ldx, w, ldw, m, n, k);
+  if (st != RGT_OK || m == 0) return st;
+  const Plan p = make_plan(m, n, k);
+  if (s != p.s || !part || !aligned(part, 16)) return RGT_ERR_INVALID;
+  if (!wsh_q || !aligned(wsh_q, 16) || !wsh_scale || !h || !aligned(h, 2) || ldh < inter) return RGT_ERR_INVALID;
+  const void* fn = shared_pick(p.valu, p.mt, p.l, p.ks);
+  if (!fn) return RGT_ERR_UNSUPPORTED;
+  GemvArgs a{static_cast<const u16*>(x), ldx, static_cast<const u16*>(w), ldw, nullptr, part, nullptr, m, n, k,
+             p.s, p.nb};
+  SharedArgs b{static_cast<const u16*>(x), ldx, wsh_q, wsh_scale, static_cast<u16*>(h), ldh, m, k, inter};
+  int router_wgs = p.grid;
+  void* args[] = {&a, &b, &router_wgs};
+  const int grid = p.grid + (inter + 1) / 2;
+  if (hipLaunchKernel(fn, dim3(grid), dim3(256), args, 0, stream) != hipSuccess) return RGT_ERR_HIP;
   g_last_launches = 1;
   return launched();
 }

@@ -1,0 +1,158 @@
+// shared.h - the router's split-K partials and the shared expert's gate/up
+// SwiGLU on MXFP8 weights, in one launch.
+//
+// MiniMax-M3.1-Flash MoE/GEMM kernels page, Summary: Router: the split-K
+// router exposes its partials (the gate sums them in order) and shares one
+// launch with the shared expert's fp8 SwiGLU; Summary: GEMM: that shared
+// expert's gate_up is 1536 x 6144. Its weights are MXFP8 (monokernel page,
+// MXFP8 shared-expert commit): e4m3fn codes [2I][K], the I gate rows first,
+// then the I up rows, and one e8m0 scale per 32 codes along K.
+//
+//   h[m][j] = bf16( silu(g) * u ),  g = x[m] . Wg[j],  u = x[m] . Wu[j]
+//   silu(g) = g / (1 + exp(-g)), all in fp32.
+//
+// The grid is the router's VALU or MFMA tiles (their partials go straight to
+// the caller's part[S][M][N]; no fixup) followed by the shared expert's
+// workgroups. A shared workgroup (4 waves) takes two columns j: waves 0 and 1
+// column 2*job, waves 2 and 3 column 2*job + 1, one half of K each. Lane l of
+// a wave takes the 16-code chunks c = c0 + l + 64 i of the gate row and of
+// the up row (16-byte loads: one wave load covers 1 KiB of a row), all
+// issued before any arithmetic. A code widens exactly to bf16 (an e4m3 value
+// has at most 4 significant bits and an exponent inside bf16's range), so
+// v_dot2_f32_bf16 forms each chunk's dot product with the x row, and the
+// chunk's power-of-two scale multiplies that sum into the fp32 accumulator
+// (exact while the scaled sum stays above 2^-126). A wave butterfly reduces
+// each half; the halves meet in LDS (lower + upper), and lane m of the
+// lower-half wave finishes row m.
+#pragma once
+
+#include "gemv.h"
+#include "norm.h"
+
+namespace rgt {
+
+struct SharedArgs {
+  const u16* x;
+  int64_t ldx;
+  const uint8_t* wq;  // [2I][K] e4m3fn codes, rows K bytes apart
+  const uint8_t* ws;  // [2I][K/32] e8m0 scale bytes, rows K/32 bytes apart
+  u16* h;             // [M][ldh] bf16
+  int64_t ldh;
+  int m, k, inter;
+};
+
+constexpr int kSharedMaxM = 16;
+constexpr int kSharedMaxK = 8192;  // at most four 16-code chunks per lane
+constexpr int kSharedChunks = kSharedMaxK / 2048;
+
+// e8m0 scale byte -> fp32 2^(b - 127): 0 is the subnormal 2^-127, 255 NaN.
+__device__ __forceinline__ float e8m0_f32(u32 b) {
+  return b == 0u ? __uint_as_float(0x00400000u) : (b == 255u ? __uint_as_float(0x7fc00000u) : __uint_as_float(b << 23));
+}
+
+// Two e4m3fn codes (16-bit word HIW of d) -> one bf16 pair, the lower byte in the
+// low half. The fp32 conversion is exact and its low 16 bits are zero.
+template <bool HIW>
+__device__ __forceinline__ u32 e4m3x2_bf16(u32 d) {
+  const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)d, HIW);
+  return (__float_as_uint(f[1]) & 0xffff0000u) | (__float_as_uint(f[0]) >> 16);
+}
+
+// Sixteen codes (memory order) -> codes 0..7 and 8..15 as bf16 vectors.
+__device__ __forceinline__ void e4m3x16_bf16(uint4 c, uint4& lo, uint4& hi) {
+  lo = make_uint4(e4m3x2_bf16<false>(c.x), e4m3x2_bf16<true>(c.x), e4m3x2_bf16<false>(c.y), e4m3x2_bf16<true>(c.y));
+  hi = make_uint4(e4m3x2_bf16<false>(c.z), e4m3x2_bf16<true>(c.z), e4m3x2_bf16<false>(c.w), e4m3x2_bf16<true>(c.w));
+}
+
+// lds: at least 2 * 2 * MT floats.
+template <int MT>
+__device__ __forceinline__ void shared_swiglu(const SharedArgs& b, int job, float* lds) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int slot = wave >> 1, half = wave & 1;
+  const int j = 2 * job + slot;
+  const bool col_ok = j < b.inter;
+  const int jc = col_ok ? j : b.inter - 1;  // an idle column loads a valid row and stores nothing
+  const int ch = b.k >> 5;                  // chunks per half: (K / 16) / 2
+  const int kq = b.k >> 5;                  // scale bytes per row
+  const uint8_t* rg = b.wq + (int64_t)jc * b.k;
+  const uint8_t* ru = b.wq + (int64_t)(b.inter + jc) * b.k;
+  const uint8_t* sg = b.ws + (int64_t)jc * kq;
+  const uint8_t* su = b.ws + (int64_t)(b.inter + jc) * kq;
+  uint4 cg[kSharedChunks], cu[kSharedChunks];
+  u32 eg[kSharedChunks], eu[kSharedChunks];
+#pragma unroll
+  for (int i = 0; i < kSharedChunks; ++i) {
+    if (64 * i >= ch) break;  // uniform: no lane has chunk i
+    const int q = lane + 64 * i;               // chunk index inside the half
+    const int c = half * ch + min(q, ch - 1);  // lanes past the half reload its last chunk (not used)
+    cg[i] = *reinterpret_cast<const uint4*>(rg + 16 * c);
+    cu[i] = *reinterpret_cast<const uint4*>(ru + 16 * c);
+    eg[i] = sg[c >> 1];
+    eu[i] = su[c >> 1];
+  }
+  float accg[MT], accu[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) accg[m] = accu[m] = 0.f;
+#pragma unroll
+  for (int i = 0; i < kSharedChunks; ++i) {
+    const int q = lane + 64 * i;
+    if (64 * i >= ch) break;  // uniform: no lane has chunk i
+    if (q < ch) {
+      const int c = half * ch + q;
+      uint4 glo, ghi, ulo, uhi;
+      e4m3x16_bf16(cg[i], glo, ghi);
+      e4m3x16_bf16(cu[i], ulo, uhi);
+      const float fg = e8m0_f32(eg[i]), fu = e8m0_f32(eu[i]);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (m < b.m) {
+          const u16* xr = b.x + (int64_t)m * b.ldx + 16 * c;
+          const uint4 xa = ld16(xr), xb = ld16(xr + 8);
+          const float pg = dot8_bf16(xb, ghi, dot8_bf16(xa, glo, 0.f));
+          const float pu = dot8_bf16(xb, uhi, dot8_bf16(xa, ulo, 0.f));
+          accg[m] = __fmaf_rn(fg, pg, accg[m]);
+          accu[m] = __fmaf_rn(fu, pu, accu[m]);
+        }
+      }
+    }
+  }
+  // wave totals (uniform), then lane m keeps row m's
+  float gm = 0.f, um = 0.f;
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const float tg = wave_sum(accg[m]), tu = wave_sum(accu[m]);
+    if (lane == m) gm = tg, um = tu;
+  }
+  float* ex = lds + slot * 2 * MT;
+  if (half == 1 && lane < MT) {
+    ex[lane] = gm;
+    ex[MT + lane] = um;
+  }
+  __syncthreads();
+  if (half == 0 && lane < MT && lane < b.m && col_ok) {
+    const float g = gm + ex[lane], u = um + ex[MT + lane];
+    const float sg_ = g / (1.f + expf(-g));
+    b.h[(int64_t)lane * b.ldh + j] = (u16)bf16_rne(sg_ * u);
+  }
+}
+
+// Router tiles first (blocks [0, router_wgs)), then ceil(I / 2) shared
+// workgroups. KS == 0: VALU router tile <MT, 1, L>; else the 16-row MFMA tile
+// with KS k-steps (M 9..16). The shared part takes MT rows (16 with MFMA).
+template <int MT, int L, int KS>
+__global__ void __launch_bounds__(256) router_shared_kernel(GemvArgs a, SharedArgs b, int router_wgs) {
+  constexpr int SM = KS ? 16 : MT;
+  __shared__ float lds[KS ? 4 * 256 : 4 * SM];
+  if ((int)blockIdx.x < router_wgs) {
+    const int t = xcd_tile(blockIdx.x, router_wgs);
+    const int nb = t % a.nb_count, s = t / a.nb_count;
+    if constexpr (KS == 0)
+      valu_tile<MT, 1, L>(a, nb, s, PartialSink{a.part, a.m, a.n});
+    else
+      mfma_tile<1, KS>(a, 0, nb, s, lds, PartialSink{a.part, a.m, a.n});
+    return;
+  }
+  shared_swiglu<SM>(b, (int)blockIdx.x - router_wgs, lds);
+}
+
+}  // namespace rgt

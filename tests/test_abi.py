@@ -171,3 +171,23 @@ def test_rmsnorm_argument_errors(L):
     assert call(ro=FAKE, ldro=6144) == 2          # residual_out without a residual
     assert call(r=FAKE, ldr=6100) == 2
     assert call(rstd=FAKE + 1) == 2
+
+
+def test_router_shared_swiglu_argument_errors(L):
+    S = L.rgt_router_partial_slices
+    # VALU plan at M = 4 (three slices of 2048), MFMA plan at M = 16 (twelve of 512)
+    assert S(4, 128, 6144) == 3 and S(16, 128, 6144) == 12
+    assert S(0, 128, 6144) == 0 and S(17, 128, 6144) == 0 and S(4, 100, 6144) == 0
+    assert S(4, 128, 8704) == 0 and S(4, 128, 6000) == 0
+    f = L.rgt_router_shared_swiglu
+
+    def call(x=FAKE, ldx=6144, w=FAKE, ldw=6144, m=4, n=128, k=6144, part=FAKE, s=3, q=FAKE, sc=FAKE, inter=768,
+             h=FAKE, ldh=768):
+        return f(x, ldx, w, ldw, m, n, k, part, s, q, sc, inter, h, ldh, None)
+
+    assert call(m=0) == 0
+    assert call(m=17) == 1 and call(n=100) == 1 and call(k=8704) == 1 and call(inter=0) == 1
+    assert call(s=4) == 2 and call(part=None) == 2 and call(part=FAKE + 4) == 2
+    assert call(q=None) == 2 and call(q=FAKE + 8) == 2 and call(sc=None) == 2
+    assert call(h=None) == 2 and call(h=FAKE + 1) == 2 and call(ldh=767) == 2
+    assert call(x=FAKE + 2) == 2 and call(ldx=6000) == 2
