@@ -617,7 +617,8 @@ rgt_status rgt_router_shared_swiglu(const void* x, int64_t ldx, const void* w, i
   SharedArgs b{static_cast<const u16*>(x), ldx, wsh_q, wsh_scale, static_cast<u16*>(h), ldh, m, k, inter};
   int router_wgs = p.grid;
   void* args[] = {&a, &b, &router_wgs};
-  const int grid = p.grid + (inter + 1) / 2;
+  const int cols = 4 / shared_kw(p.valu ? p.mt : 16);  // shared-expert columns per workgroup
+  const int grid = p.grid + (inter + cols - 1) / cols;
   if (hipLaunchKernel(fn, dim3(grid), dim3(256), args, 0, stream) != hipSuccess) return RGT_ERR_HIP;
   g_last_launches = 1;
   return launched();

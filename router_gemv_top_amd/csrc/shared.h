@@ -13,17 +13,17 @@
 //
 // The grid is the router's VALU or MFMA tiles (their partials go straight to
 // the caller's part[S][M][N]; no fixup) followed by the shared expert's
-// workgroups. A shared workgroup (4 waves) takes two columns j: waves 0 and 1
-// column 2*job, waves 2 and 3 column 2*job + 1, one half of K each. Lane l of
-// a wave takes the 16-code chunks c = c0 + l + 64 i of the gate row and of
-// the up row (16-byte loads: one wave load covers 1 KiB of a row), all
+// workgroups. A shared workgroup (4 waves) takes 4 / KW columns j, KW waves
+// a column, each wave 1/KW of K (KW = 2 for M <= 2, else 4). Lane l of a
+// wave takes the 16-code chunks c = c0 + l + 64 i of the gate row and of the
+// up row (16-byte loads: one wave load covers 1 KiB of a row), all
 // issued before any arithmetic. A code widens exactly to bf16 (an e4m3 value
 // has at most 4 significant bits and an exponent inside bf16's range), so
 // v_dot2_f32_bf16 forms each chunk's dot product with the x row, and the
 // chunk's power-of-two scale multiplies that sum into the fp32 accumulator
 // (exact while the scaled sum stays above 2^-126). A wave butterfly reduces
-// each half; the halves meet in LDS (lower + upper), and lane m of the
-// lower-half wave finishes row m.
+// each part; the parts meet in LDS (added in part order), and lane m of the
+// first part's wave finishes row m.
 #pragma once
 
 #include "gemv.h"
@@ -64,15 +64,21 @@ __device__ __forceinline__ void e4m3x16_bf16(uint4 c, uint4& lo, uint4& hi) {
   hi = make_uint4(e4m3x2_bf16<false>(c.z), e4m3x2_bf16<true>(c.z), e4m3x2_bf16<false>(c.w), e4m3x2_bf16<true>(c.w));
 }
 
-// lds: at least 2 * 2 * MT floats.
+// Waves per column (each takes 1/KW of K): two for M <= 2, four from M = 4,
+// where the per-row work grows and more, shorter waves hide the x loads'
+// latency better. (The host sizes the grid with the same function.)
+constexpr int shared_kw(int mt) { return mt >= 4 ? 4 : 2; }
+
+// lds: at least 4 * 2 * MT floats.
 template <int MT>
 __device__ __forceinline__ void shared_swiglu(const SharedArgs& b, int job, float* lds) {
+  constexpr int KW = shared_kw(MT), COLS = 4 / KW;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int slot = wave >> 1, half = wave & 1;
-  const int j = 2 * job + slot;
+  const int slot = wave / KW, part = wave % KW;
+  const int j = COLS * job + slot;
   const bool col_ok = j < b.inter;
   const int jc = col_ok ? j : b.inter - 1;  // an idle column loads a valid row and stores nothing
-  const int ch = b.k >> 5;                  // chunks per half: (K / 16) / 2
+  const int ch = (b.k >> 4) / KW;           // chunks per wave
   const int kq = b.k >> 5;                  // scale bytes per row
   const uint8_t* rg = b.wq + (int64_t)jc * b.k;
   const uint8_t* ru = b.wq + (int64_t)(b.inter + jc) * b.k;
@@ -83,8 +89,8 @@ __device__ __forceinline__ void shared_swiglu(const SharedArgs& b, int job, floa
 #pragma unroll
   for (int i = 0; i < kSharedChunks; ++i) {
     if (64 * i >= ch) break;  // uniform: no lane has chunk i
-    const int q = lane + 64 * i;               // chunk index inside the half
-    const int c = half * ch + min(q, ch - 1);  // lanes past the half reload its last chunk (not used)
+    const int q = lane + 64 * i;               // chunk index inside the wave's part
+    const int c = part * ch + min(q, ch - 1);  // lanes past the part reload its last chunk (not used)
     cg[i] = *reinterpret_cast<const uint4*>(rg + 16 * c);
     cu[i] = *reinterpret_cast<const uint4*>(ru + 16 * c);
     eg[i] = sg[c >> 1];
@@ -98,21 +104,27 @@ __device__ __forceinline__ void shared_swiglu(const SharedArgs& b, int job, floa
     const int q = lane + 64 * i;
     if (64 * i >= ch) break;  // uniform: no lane has chunk i
     if (q < ch) {
-      const int c = half * ch + q;
+      const int c = part * ch + q;
       uint4 glo, ghi, ulo, uhi;
       e4m3x16_bf16(cg[i], glo, ghi);
       e4m3x16_bf16(cu[i], ulo, uhi);
       const float fg = e8m0_f32(eg[i]), fu = e8m0_f32(eu[i]);
+      // every row's x loads first, rows past M reading row M-1 (no branch
+      // between the loads, so they are all in flight together; their sums
+      // are never stored)
+      uint4 xa[MT], xb[MT];
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        if (m < b.m) {
-          const u16* xr = b.x + (int64_t)m * b.ldx + 16 * c;
-          const uint4 xa = ld16(xr), xb = ld16(xr + 8);
-          const float pg = dot8_bf16(xb, ghi, dot8_bf16(xa, glo, 0.f));
-          const float pu = dot8_bf16(xb, uhi, dot8_bf16(xa, ulo, 0.f));
-          accg[m] = __fmaf_rn(fg, pg, accg[m]);
-          accu[m] = __fmaf_rn(fu, pu, accu[m]);
-        }
+        const u16* xr = b.x + (int64_t)min(m, b.m - 1) * b.ldx + 16 * c;
+        xa[m] = ld16(xr);
+        xb[m] = ld16(xr + 8);
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const float pg = dot8_bf16(xb[m], ghi, dot8_bf16(xa[m], glo, 0.f));
+        const float pu = dot8_bf16(xb[m], uhi, dot8_bf16(xa[m], ulo, 0.f));
+        accg[m] = __fmaf_rn(fg, pg, accg[m]);
+        accu[m] = __fmaf_rn(fu, pu, accu[m]);
       }
     }
   }
@@ -123,26 +135,33 @@ __device__ __forceinline__ void shared_swiglu(const SharedArgs& b, int job, floa
     const float tg = wave_sum(accg[m]), tu = wave_sum(accu[m]);
     if (lane == m) gm = tg, um = tu;
   }
-  float* ex = lds + slot * 2 * MT;
-  if (half == 1 && lane < MT) {
-    ex[lane] = gm;
-    ex[MT + lane] = um;
+  // parts 1..KW-1 hand their totals to part 0, which adds them in part order
+  float* ex = lds + slot * (KW - 1) * 2 * MT;
+  if (part > 0 && lane < MT) {
+    ex[(part - 1) * 2 * MT + lane] = gm;
+    ex[(part - 1) * 2 * MT + MT + lane] = um;
   }
   __syncthreads();
-  if (half == 0 && lane < MT && lane < b.m && col_ok) {
-    const float g = gm + ex[lane], u = um + ex[MT + lane];
+  if (part == 0 && lane < MT && lane < b.m && col_ok) {
+    float g = gm, u = um;
+#pragma unroll
+    for (int q = 0; q < KW - 1; ++q) {
+      g += ex[q * 2 * MT + lane];
+      u += ex[q * 2 * MT + MT + lane];
+    }
     const float sg_ = g / (1.f + expf(-g));
     b.h[(int64_t)lane * b.ldh + j] = (u16)bf16_rne(sg_ * u);
   }
 }
 
-// Router tiles first (blocks [0, router_wgs)), then ceil(I / 2) shared
-// workgroups. KS == 0: VALU router tile <MT, 1, L>; else the 16-row MFMA tile
+// Router tiles first (blocks [0, router_wgs)), then ceil(I / (4 / KW))
+// shared workgroups (KW = shared_kw of the shared part's rows). KS == 0:
+// VALU router tile <MT, 1, L>; else the 16-row MFMA tile
 // with KS k-steps (M 9..16). The shared part takes MT rows (16 with MFMA).
 template <int MT, int L, int KS>
 __global__ void __launch_bounds__(256) router_shared_kernel(GemvArgs a, SharedArgs b, int router_wgs) {
   constexpr int SM = KS ? 16 : MT;
-  __shared__ float lds[KS ? 4 * 256 : 4 * SM];
+  __shared__ float lds[KS ? 4 * 256 : 4 * 2 * SM];
   if ((int)blockIdx.x < router_wgs) {
     const int t = xcd_tile(blockIdx.x, router_wgs);
     const int nb = t % a.nb_count, s = t / a.nb_count;
