@@ -94,6 +94,39 @@ def _graph_us(torch, stream, calls, fn):
     return e0.elapsed_time(e1) * 1e3 / calls
 
 
+def shared_swiglu_line(torch, R, dev, stream, copies_128: int):
+    """Router k-slice partials + the shared expert's MXFP8 gate/up SwiGLU in
+    one launch (MiniMax-M3.1 decode: 128 experts, hidden 6144, gate_up
+    1536 x 6144), router W and shared-expert weights cold (rotating copies)."""
+    from router_gemv_top_amd.inputs import gen_mxfp8_weights, gen_w as _gw, gen_x as _gx0
+
+    def dev_bf16(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    inter = 768
+    wq, wsc = gen_mxfp8_weights(2 * inter, K, seed=3)
+    w_r = _gw(N, K, seed=3)
+    w_bytes = w_r.size * 2 + wq.size + wsc.size
+    copies = min(copies_128, int(np.ceil(2 * MALL_BYTES / w_bytes)))
+    wr_all = dev_bf16(w_r).unsqueeze(0).repeat(copies, 1, 1)
+    wq_all = torch.from_numpy(wq).to(dev).unsqueeze(0).repeat(copies, 1, 1)
+    ws_all = torch.from_numpy(wsc).to(dev).unsqueeze(0).repeat(copies, 1, 1)
+    per = {}
+    for m in (1, 2, 4, 8, 16):
+        xw = dev_bf16(_gx0(m, K, seed=m))
+        s = R.router_partial_slices(m, N, K)
+        part = torch.empty((s, m, N), dtype=torch.float32, device=dev)
+        h = torch.empty((m, inter), dtype=torch.bfloat16, device=dev)
+        us = _graph_us(torch, stream, copies, lambda i: R.router_shared_swiglu(
+            xw, wr_all[i], wq_all[i], ws_all[i], part=part, h=h))
+        nbytes = w_bytes + m * K * 2 + s * m * N * 4 + m * inter * 2
+        gbs = nbytes / (us * 1e-6) / 1e9
+        per[str(m)] = {"us": round(us, 3), "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 3),
+                       "launches": R.last_launch_count(), "slices": s}
+    del wr_all, wq_all, ws_all
+    return {"w_copies": copies, "per_m": per}
+
+
 def secondary(torch, R, dev, stream, copies_128: int):
     """The other routing shapes, timed like the headline sweep (graph replay,
     cold W by rotating copies), plus the prefill router GEMM alone against the
@@ -141,32 +174,8 @@ def secondary(torch, R, dev, stream, copies_128: int):
         res[group] = {"w_copies": copies, "per_m": per}
         del w_all
 
-    # Router k-slice partials + the shared expert's MXFP8 gate/up SwiGLU in one
-    # launch (MiniMax-M3.1 decode: 128 experts, hidden 6144, gate_up 1536 x
-    # 6144), router W and shared-expert weights cold (rotating copies).
-    from router_gemv_top_amd.inputs import gen_mxfp8_weights, gen_w as _gw, gen_x as _gx0
-    inter = 768
-    wq, wsc = gen_mxfp8_weights(2 * inter, K, seed=3)
-    w_r = _gw(N, K, seed=3)
-    w_bytes = w_r.size * 2 + wq.size + wsc.size
-    copies = min(copies_128, int(np.ceil(2 * MALL_BYTES / w_bytes)))
-    wr_all = dev_bf16(w_r).unsqueeze(0).repeat(copies, 1, 1)
-    wq_all = torch.from_numpy(wq).to(dev).unsqueeze(0).repeat(copies, 1, 1)
-    ws_all = torch.from_numpy(wsc).to(dev).unsqueeze(0).repeat(copies, 1, 1)
-    per = {}
-    for m in (1, 2, 4, 8, 16):
-        xw = dev_bf16(_gx0(m, K, seed=m))
-        s = R.router_partial_slices(m, N, K)
-        part = torch.empty((s, m, N), dtype=torch.float32, device=dev)
-        h = torch.empty((m, inter), dtype=torch.bfloat16, device=dev)
-        us = _graph_us(torch, stream, copies, lambda i: R.router_shared_swiglu(
-            xw, wr_all[i], wq_all[i], ws_all[i], part=part, h=h))
-        nbytes = w_bytes + m * K * 2 + s * m * N * 4 + m * inter * 2
-        gbs = nbytes / (us * 1e-6) / 1e9
-        per[str(m)] = {"us": round(us, 3), "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 3),
-                       "launches": R.last_launch_count(), "slices": s}
-    res["router_partials_shared_swiglu_N128_K6144_I768_mxfp8"] = {"w_copies": copies, "per_m": per}
-    del wr_all, wq_all, ws_all
+    res["router_partials_shared_swiglu_N128_K6144_I768_mxfp8"] = shared_swiglu_line(torch, R, dev, stream,
+                                                                                     copies_128)
 
     wl = workload_prefill_896()
     x, w, _ = wl.make()
@@ -267,6 +276,9 @@ def main():
     ap.add_argument("--only-prefill", action="store_true",
                     help="profiling mode: --calls prefill calls (M=8192, N=896, K=3584, top-16, B=64), "
                          "then --calls router GEMM calls alone")
+    ap.add_argument("--only-shared", action="store_true",
+                    help="profiling mode: the router partials + shared-expert SwiGLU line alone "
+                         "(M=1,2,4,8,16, N=128, K=6144, I=768), printed as one JSON line")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="profiling mode: one plain device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
@@ -292,6 +304,13 @@ def main():
         assert torch.equal(src, dst)
         print(json.dumps({"mode": "calibrate_copy", "bytes_read": args.calibrate_copy,
                           "bytes_written": args.calibrate_copy}), flush=True)
+        return
+
+    if args.only_shared:
+        copies_128 = args.copies or int(np.ceil(2 * MALL_BYTES / (N * K * 2)))
+        line = shared_swiglu_line(torch, R, dev, stream, copies_128)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "only_shared", **line}), flush=True)
         return
 
     if args.only_prefill:

@@ -452,8 +452,8 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, Tile t
 // workgroup, to its first threads (the host guarantees M*K/16 <= grid *
 // 2^upw_log). Small mode takes the fewest units per workgroup that cover
 // them all (the tail's stores spread over more CUs); large mode the most
-// whose token pairs fit one wave (fewer quant workgroups, each with its rows
-// gated sooner).
+// whose token pairs fit one wave (fewer quant workgroups; measured faster
+// there, slower in small mode).
 template <int NV, int MT, int RPW, int L>
 __global__ void __launch_bounds__(256) fused_valu_kernel(FusedArgs a) {
   extern __shared__ int smem[];

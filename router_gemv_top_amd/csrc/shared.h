@@ -154,14 +154,116 @@ __device__ __forceinline__ void shared_swiglu(const SharedArgs& b, int job, floa
   }
 }
 
-// Router tiles first (blocks [0, router_wgs)), then ceil(I / (4 / KW))
-// shared workgroups (KW = shared_kw of the shared part's rows). KS == 0:
+// Sixteen codes times their power-of-two scale -> two bf16x8 MFMA operands
+// (codes 0..7 and 8..15). Exact while each scaled value is zero or at least
+// 2^-126 in magnitude (4 significant bits then fit bf16).
+template <bool HIW>
+__device__ __forceinline__ u32 e4m3x2_bf16_scaled(u32 d, float sc) {
+  const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)d, HIW);
+  return (__float_as_uint(f[1] * sc) & 0xffff0000u) | (__float_as_uint(f[0] * sc) >> 16);
+}
+__device__ __forceinline__ void e4m3x16_bf16_scaled(uint4 c, float sc, uint4& lo, uint4& hi) {
+  lo = make_uint4(e4m3x2_bf16_scaled<false>(c.x, sc), e4m3x2_bf16_scaled<true>(c.x, sc),
+                  e4m3x2_bf16_scaled<false>(c.y, sc), e4m3x2_bf16_scaled<true>(c.y, sc));
+  hi = make_uint4(e4m3x2_bf16_scaled<false>(c.z, sc), e4m3x2_bf16_scaled<true>(c.z, sc),
+                  e4m3x2_bf16_scaled<false>(c.w, sc), e4m3x2_bf16_scaled<true>(c.w, sc));
+}
+
+// MFMA form for up to 16 rows of x: a workgroup takes 8 columns j0..j0+7 as
+// one 16-row weight tile (B columns 0..7 their gate rows, 8..15 their up
+// rows) and x as the A operand (rows past M read row M-1 and are never
+// stored), so one x load feeds 16 weight rows. Wave w takes the w-th quarter
+// of K in 64-element steps; in a step, lane group g = lane/16 loads 16 codes
+// at k + 16 g of weight row lane%16 (its scale is one byte: the run lies in
+// one 32-group) and the same 16 elements of x row lane%16, which feed two
+// v_mfma_f32_16x16x32_bf16. The four waves' 16 x 16 tiles meet in LDS, added
+// in wave order, and thread t < 128 finishes row t/8, column j0 + t%8.
+// lds: at least 4 * 256 floats.
+constexpr int kSharedMfmaCols = 8;
+constexpr int kSharedMfmaSteps = kSharedMaxK / 256;
+
+__device__ __forceinline__ void shared_swiglu_mfma(const SharedArgs& b, int job, float* lds) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r16 = lane & 15, grp = lane >> 4;
+  const int j0 = job * kSharedMfmaCols;
+  const int jc = min(j0 + (r16 & 7), b.inter - 1);  // idle columns load a valid row and store nothing
+  const int wrow = r16 < 8 ? jc : b.inter + jc;
+  const int kq = b.k >> 5;
+  const uint8_t* wr = b.wq + (int64_t)wrow * b.k;
+  const uint8_t* sr = b.ws + (int64_t)wrow * kq;
+  const u16* xr = b.x + (int64_t)min(r16, b.m - 1) * b.ldx;
+  const int kw = b.k >> 2;    // elements per wave (a multiple of 128)
+  const int nit = kw >> 6;     // 64-element steps (2 .. kSharedMfmaSteps)
+  const int kb0 = wave * kw + 16 * grp;
+  // all of the wave's weight loads first (one memory round trip)
+  uint4 c[kSharedMfmaSteps];
+  u32 e[kSharedMfmaSteps];
+#pragma unroll
+  for (int i = 0; i < kSharedMfmaSteps; ++i) {
+    if (i < nit) {  // uniform; guards, not a break, keep the indexes constant
+      const int kk = kb0 + 64 * i;
+      c[i] = *reinterpret_cast<const uint4*>(wr + kk);
+      e[i] = sr[kk >> 5];
+    }
+  }
+  floatx4_t acc = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i0 = 0; i0 < kSharedMfmaSteps; i0 += 4) {
+    if (i0 < nit) {  // uniform
+      // four steps' x loads together (a step past the last reloads the last)
+      uint4 xa[4], xb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kk = kb0 + 64 * min(i0 + i, nit - 1);
+        xa[i] = ld16(xr + kk);
+        xb[i] = ld16(xr + kk + 8);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i0 + i < nit) {
+          uint4 lo, hi;
+          e4m3x16_bf16_scaled(c[i0 + i], e8m0_f32(e[i0 + i]), lo, hi);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa[i]),
+                                                        __builtin_bit_cast(bf16x8_t, lo), acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xb[i]),
+                                                        __builtin_bit_cast(bf16x8_t, hi), acc, 0, 0, 0);
+        }
+      }
+    }
+  }
+  // D lane l: rows 4*(l/16) + r (x rows), column l%16 (weight row of the tile)
+#pragma unroll
+  for (int r = 0; r < 4; ++r) lds[wave * 256 + (4 * grp + r) * 16 + r16] = acc[r];
+  __syncthreads();
+  const int t = threadIdx.x, m = t >> 3, cc = t & 7, j = j0 + cc;
+  if (t < 128 && m < b.m && j < b.inter) {
+    float g = lds[m * 16 + cc], u = lds[m * 16 + 8 + cc];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      g += lds[w * 256 + m * 16 + cc];
+      u += lds[w * 256 + m * 16 + 8 + cc];
+    }
+    const float sg_ = g / (1.f + expf(-g));
+    b.h[(int64_t)m * b.ldh + j] = (u16)bf16_rne(sg_ * u);
+  }
+}
+
+// Shared part's form: MFMA for 9..16 rows (measured at M = 16, N = 128,
+// K = 6144, I = 768: 13.9 us against 15.8 for the VALU form; at M = 8 the
+// VALU form's 768 workgroups win, 10.5 against 13.4 us, the MFMA form's 96
+// eight-column tiles streaming the weights through too few CUs). The host
+// sizes the grid with the same functions.
+constexpr bool shared_use_mfma(int mt) { return mt >= 16; }
+constexpr int shared_cols_per_wg(int mt) { return shared_use_mfma(mt) ? kSharedMfmaCols : 4 / shared_kw(mt); }
+
+// Router tiles first (blocks [0, router_wgs)), then ceil(I / cols) shared
+// workgroups (cols = shared_cols_per_wg of the shared part's rows). KS == 0:
 // VALU router tile <MT, 1, L>; else the 16-row MFMA tile
 // with KS k-steps (M 9..16). The shared part takes MT rows (16 with MFMA).
 template <int MT, int L, int KS>
 __global__ void __launch_bounds__(256) router_shared_kernel(GemvArgs a, SharedArgs b, int router_wgs) {
   constexpr int SM = KS ? 16 : MT;
-  __shared__ float lds[KS ? 4 * 256 : 4 * 2 * SM];
+  __shared__ float lds[(KS || shared_use_mfma(SM)) ? 4 * 256 : 4 * 2 * SM];
   if ((int)blockIdx.x < router_wgs) {
     const int t = xcd_tile(blockIdx.x, router_wgs);
     const int nb = t % a.nb_count, s = t / a.nb_count;
@@ -171,7 +273,10 @@ __global__ void __launch_bounds__(256) router_shared_kernel(GemvArgs a, SharedAr
       mfma_tile<1, KS>(a, 0, nb, s, lds, PartialSink{a.part, a.m, a.n});
     return;
   }
-  shared_swiglu<SM>(b, (int)blockIdx.x - router_wgs, lds);
+  if constexpr (shared_use_mfma(SM))
+    shared_swiglu_mfma(b, (int)blockIdx.x - router_wgs, lds);
+  else
+    shared_swiglu<SM>(b, (int)blockIdx.x - router_wgs, lds);
 }
 
 }  // namespace rgt

@@ -137,5 +137,34 @@ def recorded_traffic(profiles_dir: str):
     return {int(m): d["bytes"] for m, d in data["per_m"].items()}
 
 
+def build_shared(res: str, out: str):
+    """Kernel durations of the router partials + shared-expert SwiGLU launch
+    (bench.py --only-shared) from RES/prof_shared."""
+    os.makedirs(out, exist_ok=True)
+    rows = list(csv.DictReader(open(_find(os.path.join(res, "prof_shared"), "*kernel_stats.csv"))))
+    lines = ["# Router k-slice partials + shared-expert MXFP8 gate/up SwiGLU: kernel durations (rocprofv3)", "",
+             "Workload: M = 1, 2, 4, 8, 16; router N = 128, K = 6144; shared expert gate_up 1536 x 6144",
+             "(I = 768) MXFP8; router W and shared weights cold (rotating copies). One launch per call;",
+             "the instances are the M values (router tile `<MT, L, KS>`: VALU `<MT, L, 0>` for M <= 8,",
+             "the 16-row MFMA tile `<1, 1, KS>` for M = 16).", "",
+             "Command (from the repository root, results folder RES):", "",
+             "    rocprofv3 --kernel-trace --stats --output-format csv -d RES/prof_shared -o shared "
+             "-- python3 bench.py --only-shared",
+             "    python -m router_gemv_top_amd.profile_report --shared RES profiles", "",
+             "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"].replace("rgt::", "")
+        if "router_shared" not in name:
+            continue
+        short = name.split("(")[0].replace("void ", "")
+        lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
+                     f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} |")
+    with open(os.path.join(out, "router_partials_shared_swiglu_kernel_stats.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
-    build(sys.argv[1], sys.argv[2])
+    if sys.argv[1] == "--shared":
+        build_shared(sys.argv[2], sys.argv[3])
+    else:
+        build(sys.argv[1], sys.argv[2])
