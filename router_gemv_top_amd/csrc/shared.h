@@ -47,7 +47,10 @@ constexpr int kSharedChunks = kSharedMaxK / 2048;
 
 // e8m0 scale byte -> fp32 2^(b - 127): 0 is the subnormal 2^-127, 255 NaN.
 __device__ __forceinline__ float e8m0_f32(u32 b) {
-  return b == 0u ? __uint_as_float(0x00400000u) : (b == 255u ? __uint_as_float(0x7fc00000u) : __uint_as_float(b << 23));
+  u32 bits = b << 23;                        // integer selects, no branches
+  bits = b == 0u ? 0x00400000u : bits;
+  bits = b == 255u ? 0x7fc00000u : bits;
+  return __uint_as_float(bits);
 }
 
 // Two e4m3fn codes (16-bit word HIW of d) -> one bf16 pair, the lower byte in the
@@ -169,25 +172,28 @@ __device__ __forceinline__ void e4m3x16_bf16_scaled(uint4 c, float sc, uint4& lo
                   e4m3x2_bf16_scaled<false>(c.w, sc), e4m3x2_bf16_scaled<true>(c.w, sc));
 }
 
-// MFMA form for up to 16 rows of x: a workgroup takes 8 columns j0..j0+7 as
-// one 16-row weight tile (B columns 0..7 their gate rows, 8..15 their up
-// rows) and x as the A operand (rows past M read row M-1 and are never
+// MFMA form for up to 16 rows of x: a workgroup takes MC columns as one
+// 16-row weight tile (their gate and up rows) and x as the A operand (rows past M read row M-1 and are never
 // stored), so one x load feeds 16 weight rows. Wave w takes the w-th quarter
 // of K in 64-element steps; in a step, lane group g = lane/16 loads 16 codes
 // at k + 16 g of weight row lane%16 (its scale is one byte: the run lies in
 // one 32-group) and the same 16 elements of x row lane%16, which feed two
 // v_mfma_f32_16x16x32_bf16. The four waves' 16 x 16 tiles meet in LDS, added
-// in wave order, and thread t < 128 finishes row t/8, column j0 + t%8.
+// in wave order, and thread t < 16 MC finishes row t/MC, column j0 + t%MC.
 // lds: at least 4 * 256 floats.
-constexpr int kSharedMfmaCols = 8;
 constexpr int kSharedMfmaSteps = kSharedMaxK / 256;
 
+// MC columns a tile (2, 4 or 8): B columns q < MC are their gate rows,
+// MC <= q < 2 MC their up rows, and the rest repeat those (same addresses,
+// so no extra memory traffic): narrower tiles give more workgroups.
+template <int MC>
 __device__ __forceinline__ void shared_swiglu_mfma(const SharedArgs& b, int job, float* lds) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r16 = lane & 15, grp = lane >> 4;
-  const int j0 = job * kSharedMfmaCols;
-  const int jc = min(j0 + (r16 & 7), b.inter - 1);  // idle columns load a valid row and store nothing
-  const int wrow = r16 < 8 ? jc : b.inter + jc;
+  const int q = r16 % (2 * MC);
+  const int j0 = job * MC;
+  const int jc = min(j0 + q % MC, b.inter - 1);  // idle columns load a valid row and store nothing
+  const int wrow = q < MC ? jc : b.inter + jc;
   const int kq = b.k >> 5;
   const uint8_t* wr = b.wq + (int64_t)wrow * b.k;
   const uint8_t* sr = b.ws + (int64_t)wrow * kq;
@@ -207,25 +213,30 @@ __device__ __forceinline__ void shared_swiglu_mfma(const SharedArgs& b, int job,
     }
   }
   floatx4_t acc = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  // x in groups of four steps, double-buffered: group g+1's loads go out
+  // before group g is multiplied (a step past the last reloads the last)
+  uint4 xa[2][4], xb[2][4];
+  auto load_x = [&](int g, uint4(&ya)[4], uint4(&yb)[4]) {
 #pragma unroll
-  for (int i0 = 0; i0 < kSharedMfmaSteps; i0 += 4) {
-    if (i0 < nit) {  // uniform
-      // four steps' x loads together (a step past the last reloads the last)
-      uint4 xa[4], xb[4];
+    for (int i = 0; i < 4; ++i) {
+      const int kk = kb0 + 64 * min(4 * g + i, nit - 1);
+      ya[i] = ld16(xr + kk);
+      yb[i] = ld16(xr + kk + 8);
+    }
+  };
+  load_x(0, xa[0], xb[0]);
+#pragma unroll
+  for (int g = 0; g < kSharedMfmaSteps / 4; ++g) {
+    if (4 * g < nit) {  // uniform
+      if (4 * g + 4 < nit) load_x(g + 1, xa[(g + 1) & 1], xb[(g + 1) & 1]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int kk = kb0 + 64 * min(i0 + i, nit - 1);
-        xa[i] = ld16(xr + kk);
-        xb[i] = ld16(xr + kk + 8);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (i0 + i < nit) {
+        if (4 * g + i < nit) {
           uint4 lo, hi;
-          e4m3x16_bf16_scaled(c[i0 + i], e8m0_f32(e[i0 + i]), lo, hi);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa[i]),
+          e4m3x16_bf16_scaled(c[4 * g + i], e8m0_f32(e[4 * g + i]), lo, hi);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa[g & 1][i]),
                                                         __builtin_bit_cast(bf16x8_t, lo), acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xb[i]),
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xb[g & 1][i]),
                                                         __builtin_bit_cast(bf16x8_t, hi), acc, 0, 0, 0);
         }
       }
@@ -235,13 +246,13 @@ __device__ __forceinline__ void shared_swiglu_mfma(const SharedArgs& b, int job,
 #pragma unroll
   for (int r = 0; r < 4; ++r) lds[wave * 256 + (4 * grp + r) * 16 + r16] = acc[r];
   __syncthreads();
-  const int t = threadIdx.x, m = t >> 3, cc = t & 7, j = j0 + cc;
-  if (t < 128 && m < b.m && j < b.inter) {
-    float g = lds[m * 16 + cc], u = lds[m * 16 + 8 + cc];
+  const int t = threadIdx.x, m = t / MC, cc = t % MC, j = j0 + cc;
+  if (t < 16 * MC && m < b.m && j < b.inter) {
+    float g = lds[m * 16 + cc], u = lds[m * 16 + MC + cc];
 #pragma unroll
     for (int w = 1; w < 4; ++w) {
       g += lds[w * 256 + m * 16 + cc];
-      u += lds[w * 256 + m * 16 + 8 + cc];
+      u += lds[w * 256 + m * 16 + MC + cc];
     }
     const float sg_ = g / (1.f + expf(-g));
     b.h[(int64_t)m * b.ldh + j] = (u16)bf16_rne(sg_ * u);
@@ -254,7 +265,8 @@ __device__ __forceinline__ void shared_swiglu_mfma(const SharedArgs& b, int job,
 // eight-column tiles streaming the weights through too few CUs). The host
 // sizes the grid with the same functions.
 constexpr bool shared_use_mfma(int mt) { return mt >= 16; }
-constexpr int shared_cols_per_wg(int mt) { return shared_use_mfma(mt) ? kSharedMfmaCols : 4 / shared_kw(mt); }
+constexpr int shared_mfma_cols(int mt) { return 8; }
+constexpr int shared_cols_per_wg(int mt) { return shared_use_mfma(mt) ? shared_mfma_cols(mt) : 4 / shared_kw(mt); }
 
 // Router tiles first (blocks [0, router_wgs)), then ceil(I / cols) shared
 // workgroups (cols = shared_cols_per_wg of the shared part's rows). KS == 0:
@@ -274,7 +286,7 @@ __global__ void __launch_bounds__(256) router_shared_kernel(GemvArgs a, SharedAr
     return;
   }
   if constexpr (shared_use_mfma(SM))
-    shared_swiglu_mfma(b, (int)blockIdx.x - router_wgs, lds);
+    shared_swiglu_mfma<shared_mfma_cols(SM)>(b, (int)blockIdx.x - router_wgs, lds);
   else
     shared_swiglu<SM>(b, (int)blockIdx.x - router_wgs, lds);
 }
