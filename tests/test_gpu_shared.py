@@ -146,3 +146,24 @@ def test_router_shared_swiglu_zero_rows(R):
     x = np.zeros((2, 6144), np.uint16)
     part, h, _, _ = run(R, x, w, wq, ws)
     assert np.all(part == 0) and np.all((h & 0x7FFF) == 0)
+
+
+@pytest.mark.parametrize("m,topk", [(1, 8), (4, 4), (16, 8)])
+def test_router_shared_swiglu_partials_feed_the_gate(R, m, topk):
+    # the launch's partials through the gate that sums them equal the router's
+    # logits through the plain gate: same logits bits, ids and weights
+    say(f"router_shared_swiglu -> topk_gate_partials M={m} top-{topk}")
+    n, k, inter = 128, 6144, 768
+    x = gen_x(m, k, seed=40 + m)
+    w = gen_w(n, k, seed=41)
+    wq, ws = gen_mxfp8_weights(2 * inter, k, seed=42)
+    xd, wd = to_dev_bf16(x), to_dev_bf16(w)
+    part, _ = R.router_shared_swiglu(xd, wd, to_dev(wq), to_dev(ws))
+    logits_p = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    ids_p, w_p = R.topk_gate_partials(part, topk, logits=logits_p)
+    ws_ = R.Workspace(max_m=m, n=n, k=k, topk=topk, block=16)
+    logits = R.router_logits(xd, wd, ws_)
+    ids, wts = R.topk_gate(logits, topk)
+    torch.cuda.synchronize()
+    assert torch.equal(logits_p.view(torch.int32), logits.view(torch.int32))
+    assert torch.equal(ids_p, ids) and torch.equal(w_p.view(torch.int32), wts.view(torch.int32))
