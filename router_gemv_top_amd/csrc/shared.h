@@ -13,8 +13,9 @@
 //
 // The grid is the router's VALU or MFMA tiles (their partials go straight to
 // the caller's part[S][M][N]; no fixup) followed by the shared expert's
-// workgroups. A shared workgroup (4 waves) takes 4 / KW columns j, KW waves
-// a column, each wave 1/KW of K (KW = 2 for M <= 2, else 4). Lane l of a
+// workgroups: the VALU form described here up to 8 rows of x, the MFMA form
+// further down for 9 to 16. A VALU-form workgroup (4 waves) takes 4 / KW
+// columns j, KW waves a column, each wave 1/KW of K (KW = 2 for M <= 2, else 4). Lane l of a
 // wave takes the 16-code chunks c = c0 + l + 64 i of the gate row and of the
 // up row (16-byte loads: one wave load covers 1 KiB of a row), all
 // issued before any arithmetic. A code widens exactly to bf16 (an e4m3 value
@@ -67,9 +68,9 @@ __device__ __forceinline__ void e4m3x16_bf16(uint4 c, uint4& lo, uint4& hi) {
   hi = make_uint4(e4m3x2_bf16<false>(c.z), e4m3x2_bf16<true>(c.z), e4m3x2_bf16<false>(c.w), e4m3x2_bf16<true>(c.w));
 }
 
-// Waves per column (each takes 1/KW of K): two for M <= 2, four from M = 4,
-// where the per-row work grows and more, shorter waves hide the x loads'
-// latency better. (The host sizes the grid with the same function.)
+// Waves per column (each takes 1/KW of K): two for M <= 2, four from M = 4
+// (measured at N = 128, K = 6144, I = 768: equal at M = 4, 11.3 -> 10.7 us at
+// M = 8). The host sizes the grid with the same function.
 constexpr int shared_kw(int mt) { return mt >= 4 ? 4 : 2; }
 
 // lds: at least 4 * 2 * MT floats.
