@@ -151,3 +151,71 @@ def test_fp4_with_fp8_emax_is_caught():
     assert se_wrong + 127 != int(case["scale"], 16)
     se_ok = int(np.floor(np.log2(amax))) - O.E2M1_EMAX
     assert se_ok + 127 == int(case["scale"], 16)
+
+
+# --- shared expert: MXFP8 decode, scale groups, gate/up order, silu ----------
+
+import test_oracle_shared as SH  # noqa: E402
+
+
+def _golden_check(h_fn):
+    """The hand-derived shared-expert case, scored with a given h function."""
+    case = json.loads(SH.GOLDEN.read_text())
+    x, wq, ws = SH._golden_weights(case)
+    want = np.array([[float(v) for v in r] for r in case["h"]])
+    return np.allclose(h_fn(x, wq, ws), want, rtol=1e-12, atol=0)
+
+
+def test_shared_pins_accept_the_oracle():
+    assert _golden_check(lambda x, wq, ws: O.shared_swiglu(x, wq, ws)[0])
+
+
+def test_shared_scale_group_of_16_is_caught():
+    # caught by the exact rational dot products on random codes and scales
+    from fractions import Fraction
+    from router_gemv_top_amd.inputs import gen_mxfp8_weights, gen_x
+
+    def mutant(x, wq, ws):
+        w = O.e4m3_value(wq) * O.e8m0_value(ws)[:, np.minimum(np.arange(wq.shape[1]) // 16, ws.shape[1] - 1)]
+        return O.bf16_bits_to_f64(x) @ w.T
+
+    x = gen_x(1, 64, seed=11)
+    wq, ws = gen_mxfp8_weights(2, 64, seed=11)
+    exact = [float(sum(SH._exact_bf16(x[0, i]) * SH._exact_e4m3(wq[r, i]) * Fraction(2) ** (int(ws[r, i // 32]) - 127)
+                       for i in range(64))) for r in range(2)]
+    assert np.allclose(O.shared_gate_up(x, wq, ws)[0], exact, rtol=1e-15)
+    assert not np.allclose(mutant(x, wq, ws)[0], exact, rtol=1e-6)
+
+
+def test_shared_swapped_gate_up_is_caught():
+    def mutant(x, wq, ws):
+        gu = O.shared_gate_up(x, wq, ws)
+        i = gu.shape[1] // 2
+        return O.swiglu(np.concatenate([gu[:, i:], gu[:, :i]], axis=1), i)
+    assert not _golden_check(mutant)
+
+
+def test_shared_interleaved_gate_up_is_caught():
+    # reading gate and up rows as interleaved (gate j at row 2j, up j at 2j + 1)
+    def mutant(x, wq, ws):
+        gu = O.shared_gate_up(x, wq, ws)
+        return O.silu(gu[:, 0::2]) * gu[:, 1::2]
+    assert not _golden_check(mutant)
+
+
+def test_silu_sign_error_is_caught():
+    g = np.linspace(-30, 30, 601)
+    import scipy.special
+    mutant = g / (1.0 + np.exp(g))
+    assert not np.allclose(mutant, g * scipy.special.expit(g), rtol=1e-14, atol=1e-300)
+
+
+def test_e4m3_bias_8_is_caught():
+    # the FNUZ-style exponent bias (8) halves every normal value
+    def mutant(codes):
+        return O.e4m3_value(codes) / 2.0
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    v = mutant(codes)
+    back = O.e4m3_code(np.abs(v), np.signbit(v).astype(np.int64))
+    assert not np.array_equal(back, codes)
+    assert mutant(np.array([0x38], np.uint8))[0] != 1.0
