@@ -43,8 +43,7 @@ struct SharedArgs {
 };
 
 constexpr int kSharedMaxM = 16;
-constexpr int kSharedMaxK = 8192;  // at most four 16-code chunks per lane
-constexpr int kSharedChunks = kSharedMaxK / 2048;
+constexpr int kSharedMaxK = 8192;  // at most 8 / KW 16-code chunks per lane
 
 // e8m0 scale byte -> fp32 2^(b - 127): 0 is the subnormal 2^-127, 255 NaN.
 __device__ __forceinline__ float e8m0_f32(u32 b) {
@@ -77,6 +76,12 @@ constexpr int shared_kw(int mt) { return mt >= 4 ? 4 : 2; }
 template <int MT>
 __device__ __forceinline__ void shared_swiglu(const SharedArgs& b, int job, float* lds) {
   constexpr int KW = shared_kw(MT), COLS = 4 / KW;
+  constexpr int NCH = kSharedMaxK / 1024 / KW;  // chunks per lane, at most
+  // x loads of every chunk up front for up to 4 rows; 8 rows load x per chunk
+  // (up front they take the 8-row instance to 176 VGPRs and 2 waves a SIMD:
+  // measured 10.8 -> 11.3 us at M = 8, while M = 1 gains 5.5 -> 5.25 us)
+  constexpr bool XPRE = MT <= 4;
+  constexpr int XN = XPRE ? NCH : 1;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int slot = wave / KW, part = wave % KW;
   const int j = COLS * job + slot;
@@ -88,45 +93,47 @@ __device__ __forceinline__ void shared_swiglu(const SharedArgs& b, int job, floa
   const uint8_t* ru = b.wq + (int64_t)(b.inter + jc) * b.k;
   const uint8_t* sg = b.ws + (int64_t)jc * kq;
   const uint8_t* su = b.ws + (int64_t)(b.inter + jc) * kq;
-  uint4 cg[kSharedChunks], cu[kSharedChunks];
-  u32 eg[kSharedChunks], eu[kSharedChunks];
+  // every weight load of the lane first (and, XPRE, every x load: one memory
+  // round trip); rows past M read row M-1 (their sums are never stored)
+  uint4 cg[NCH], cu[NCH], xa[XN][MT], xb[XN][MT];
+  auto load_x = [&](int c, uint4(&ya)[MT], uint4(&yb)[MT]) {
 #pragma unroll
-  for (int i = 0; i < kSharedChunks; ++i) {
-    if (64 * i >= ch) break;  // uniform: no lane has chunk i
-    const int q = lane + 64 * i;               // chunk index inside the wave's part
-    const int c = part * ch + min(q, ch - 1);  // lanes past the part reload its last chunk (not used)
-    cg[i] = *reinterpret_cast<const uint4*>(rg + 16 * c);
-    cu[i] = *reinterpret_cast<const uint4*>(ru + 16 * c);
-    eg[i] = sg[c >> 1];
-    eu[i] = su[c >> 1];
+    for (int m = 0; m < MT; ++m) {
+      const u16* xr = b.x + (int64_t)min(m, b.m - 1) * b.ldx + 16 * c;
+      ya[m] = ld16(xr);
+      yb[m] = ld16(xr + 8);
+    }
+  };
+  u32 eg[NCH], eu[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    if (64 * i < ch) {  // uniform; guards, not a break, keep the indexes constant
+      const int q = lane + 64 * i;               // chunk index inside the wave's part
+      const int c = part * ch + min(q, ch - 1);  // lanes past the part reload its last chunk (not used)
+      cg[i] = *reinterpret_cast<const uint4*>(rg + 16 * c);
+      cu[i] = *reinterpret_cast<const uint4*>(ru + 16 * c);
+      eg[i] = sg[c >> 1];
+      eu[i] = su[c >> 1];
+      if constexpr (XPRE) load_x(c, xa[i], xb[i]);
+    }
   }
   float accg[MT], accu[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) accg[m] = accu[m] = 0.f;
 #pragma unroll
-  for (int i = 0; i < kSharedChunks; ++i) {
+  for (int i = 0; i < NCH; ++i) {
     const int q = lane + 64 * i;
-    if (64 * i >= ch) break;  // uniform: no lane has chunk i
-    if (q < ch) {
-      const int c = part * ch + q;
+    if (64 * i < ch && q < ch) {
+      const int xi = XPRE ? i : 0;  // a constant once unrolled
+      if constexpr (!XPRE) load_x(part * ch + q, xa[0], xb[0]);
       uint4 glo, ghi, ulo, uhi;
       e4m3x16_bf16(cg[i], glo, ghi);
       e4m3x16_bf16(cu[i], ulo, uhi);
       const float fg = e8m0_f32(eg[i]), fu = e8m0_f32(eu[i]);
-      // every row's x loads first, rows past M reading row M-1 (no branch
-      // between the loads, so they are all in flight together; their sums
-      // are never stored)
-      uint4 xa[MT], xb[MT];
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        const u16* xr = b.x + (int64_t)min(m, b.m - 1) * b.ldx + 16 * c;
-        xa[m] = ld16(xr);
-        xb[m] = ld16(xr + 8);
-      }
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const float pg = dot8_bf16(xb[m], ghi, dot8_bf16(xa[m], glo, 0.f));
-        const float pu = dot8_bf16(xb[m], uhi, dot8_bf16(xa[m], ulo, 0.f));
+        const float pg = dot8_bf16(xb[xi][m], ghi, dot8_bf16(xa[xi][m], glo, 0.f));
+        const float pu = dot8_bf16(xb[xi][m], uhi, dot8_bf16(xa[xi][m], ulo, 0.f));
         accg[m] = __fmaf_rn(fg, pg, accg[m]);
         accu[m] = __fmaf_rn(fu, pu, accu[m]);
       }
