@@ -163,8 +163,15 @@ int rgt_router_partial_slices(int m, int n, int k);
  *               u = x[m].Wu[j], silu(g) = g / (1 + exp(-g)), fp32 sums.
  * 0 <= M <= 16, K <= 8192 and the router's shape rules (N a multiple of 16
  * in [16, 1024], K a multiple of 512), 1 <= I <= 2^20, ldh >= I; otherwise
- * RGT_ERR_UNSUPPORTED or RGT_ERR_INVALID and nothing is launched. NaN codes
- * or a 255 scale give NaN outputs. One launch, no workspace. */
+ * RGT_ERR_UNSUPPORTED or RGT_ERR_INVALID and nothing is launched.
+ * Covered weight scales: scale bytes 10..246. There every scaled weight is
+ * zero or a normal fp32 and bf16 value (at least 2^-126, below 2^128), and
+ * the two forms of the kernel (up to 8 rows: codes times x in fp32, then the
+ * scale; 9 to 16 rows: the scale folded into bf16 weights) are exact in the
+ * weights and agree within the summation bound. Bytes 0..9 and 247..254 are
+ * accepted but their results are unspecified, as are results whose g, u or h
+ * leave the fp32 / bf16 range. NaN codes or a 255 scale give NaN outputs.
+ * One launch, no workspace. */
 rgt_status rgt_router_shared_swiglu(const void* x, int64_t ldx, const void* w, int64_t ldw, int m, int n, int k,
                                     float* part, int s, const uint8_t* wsh_q, const uint8_t* wsh_scale, int inter,
                                     void* h, int64_t ldh, hipStream_t stream);

@@ -179,6 +179,14 @@ def test_route_sort_quant_prefill(R):
     ws = R.Workspace(wl.m, wl.n, wl.k, wl.topk, wl.block)
     f, launches = fused(R, x, w, b, wl.topk, wl.block, ws)
     fo = np_out(f)
+    # the duplicated tokens (5% of the rows copy another row) get identical
+    # logit bits on the path this size takes (the prefill router GEMM)
+    rows = np.ascontiguousarray(x).view(np.dtype((np.void, 2 * wl.k))).ravel()
+    _, first, inv = np.unique(rows, return_index=True, return_inverse=True)
+    dup = np.nonzero(first[inv] != np.arange(wl.m))[0]
+    assert len(dup) >= int(round(0.05 * wl.m)) - 1
+    lbits = fo["logits"].view(np.uint32)
+    np.testing.assert_array_equal(lbits[dup], lbits[first[inv[dup]]])
     ids = check_against_oracle(x, w, b, wl.topk, wl.block, fo)
     rng = np.random.default_rng(4)
     check_sort_quant(sort_out(fo), ids, x, wl.n, wl.block,

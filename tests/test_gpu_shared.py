@@ -167,3 +167,30 @@ def test_router_shared_swiglu_partials_feed_the_gate(R, m, topk):
     torch.cuda.synchronize()
     assert torch.equal(logits_p.view(torch.int32), logits.view(torch.int32))
     assert torch.equal(ids_p, ids) and torch.equal(w_p.view(torch.int32), wts.view(torch.int32))
+
+
+@pytest.mark.parametrize("m", [8, 16])
+@pytest.mark.parametrize("lo,hi,x_exp", [(10, 20, 90), (236, 247, -100)])
+def test_router_shared_swiglu_scale_range_edges(R, m, lo, hi, x_exp):
+    """Scale bytes at both ends of the covered range [10, 246], where every
+    scaled weight (a code times 2^(b - 127)) is zero or a normal bf16, run
+    by both forms of the shared part (the VALU form at 8 rows, the MFMA
+    form at 16), against the oracle. x is scaled by 2^x_exp so that g, u and
+    h stay finite (a power-of-two scaling of bf16 values is exact)."""
+    say(f"router_shared_swiglu scale bytes [{lo}, {hi}) x*2^{x_exp} M={m}")
+    n, k, inter = 128, 6144, 768
+    x = gen_x(m, k, seed=60 + m)
+    exp_field = ((x >> 7) & 0xFF).astype(np.int64)
+    nz = exp_field != 0
+    x = np.where(nz, (x & 0x807F) | ((exp_field + x_exp) << 7).astype(np.uint16), x).astype(np.uint16)
+    assert np.all(((x >> 7) & 0xFF)[nz] > 0) and np.all(((x >> 7) & 0xFF) < 255)
+    w = gen_w(n, k, seed=61)
+    wq, ws = gen_mxfp8_weights(2 * inter, k, seed=62, scale_lo=lo, scale_hi=hi)
+    wq[0, :] = 0x7E   # 448: the largest code
+    wq[1, :] = 0x01   # 2^-9: the smallest subnormal code
+    ws[0, :] = hi - 1
+    ws[1, :] = lo
+    part, h, _, _ = run(R, x, w, wq, ws)
+    assert np.all(np.isfinite(bf16_bits_to_f32(h)))
+    check_h(x, wq, ws, h)
+    check_part(x, w, part)
