@@ -31,11 +31,17 @@
 //
 // A tagged word is a 32-bit payload plus the tag (epoch + 1) of the call that
 // wrote it, stored as one 8-byte store; readers poll the words themselves, so
-// no hand-off needs a counter. Every wave reads the epoch before it loads its
-// tile; the gate workgroup advances it only after it has seen every partial
-// (small mode), workgroup 0 only after every id (large mode), which implies
-// that every wave has read it.
-// Every wait is bounded by a deadline that sets the workspace error word.
+// no hand-off needs a counter. Wave 0 of every workgroup reads the epoch
+// before it stores its first partial, and the other waves take its value
+// through LDS; the gate workgroup advances the epoch only after it has seen
+// every partial (small mode), workgroup 0 only after every id (large mode),
+// which implies that every workgroup has read it. Tags repeat after 2^32 - 1
+// calls; a rotating window of the tagged-word area outside the call's own
+// words is zeroed every call, so no stale word lives that long.
+// Every wait is bounded by a deadline that sets the workspace error word; a
+// call that finds the error word set waits for nothing and writes defined
+// poison outputs (top-k ids -1, weights 0, offsets 0) until the workspace is
+// reset.
 #pragma once
 
 #include "device.h"
@@ -45,8 +51,9 @@
 
 namespace rgt {
 
-// Control words at the head of the workspace, 128 bytes apart.
-enum : int { kCtlErr = 0, kCtlEpoch = kCtrStride };
+// Control words at the head of the workspace: the error word and the call
+// epoch side by side (one 8-byte load reads both).
+enum : int { kCtlErr = 0, kCtlEpoch = 1 };
 
 // LDS of the tail, in ints: s_e[P], s_key[P], s_pos[64], s_cnt[N], s_pre[N],
 // s_off[N+1], then the gathered logits (16-byte aligned).
@@ -82,14 +89,17 @@ struct FusedArgs {
   u64 budget;          // deadline of each wait, in 100 MHz ticks
   int fault_skip;      // host-forced fault: 1 = no partial is ever published
   u64* trace;          // phase stamps (trace build only), 16 per workgroup
+  u64* scrub;          // the workspace past the tile counters (16-byte aligned)
+  u32 scrub_units;     // its size in 16-byte units (> 0)
+  u32 fp_part0, fp_part1, fp_ids0, fp_ids1;  // this call's tagged words, 16-byte units from scrub
 };
 
-// The call's tag, read by every wave on its own (no barrier): epoch + 1,
-// skipping 0 so zero-filled words never look ready. It stays a per-lane
-// value (every lane loads the same word): moving it to a scalar register
-// would make the wave wait for this load before issuing the tile's loads.
-__device__ __forceinline__ u32 call_tag(const u32* ctl) {
-  const u32 t = ld_agent(ctl + kCtlEpoch) + 1u;
+// The call's tag from the epoch word: epoch + 1, skipping 0 so zero-filled
+// words never look ready. The control words stay per-lane values (every lane
+// loads the same words): moving them to scalar registers would make the wave
+// wait for this load before issuing the tile's loads.
+__device__ __forceinline__ u32 call_tag_of(u32 epoch) {
+  const u32 t = epoch + 1u;
   return t ? t : 1u;
 }
 
@@ -258,24 +268,100 @@ __device__ __forceinline__ bool poll_ids_any(const FusedArgs& a, int P, u32 tag,
   return poll_ids<4>(a, P, tag, s_e, p0, s_cnt, s_pre);
 }
 
-// One wave selects the top-k of R rows held in LDS (lane-major loads);
-// rows[r] is the row's logits.
-template <int NV, int R>
-__device__ __forceinline__ void row_select(const FusedArgs& a, const float* const (&rows)[R], int (&id)[R],
-                                           u32 (&key)[R]) {
-  __shared__ __align__(16) int s_slot[4][64 * R];
-  const int n = a.g.n, c0 = lane_id() * NV;
-  float sv[R][NV];
+// Owner form of the top-k of one row of logits held in LDS, by the calling
+// wave: for each of this lane's NV experts (lane-major, expert lane*NV + i)
+// whether it is selected, its slot and its score key. bv: this lane's bias
+// values. Up to four experts a lane the threshold selection; above, k rounds
+// of a wave maximum whose slot-ordered winners are handed to their owners
+// through s_flag (n ints of LDS owned by the calling wave).
+template <int NV>
+__device__ __forceinline__ void row_topk_owner(const FusedArgs& a, const float* row, const float (&bv)[NV],
+                                               bool (&sel)[NV], int (&slot)[NV], u32 (&key)[NV], int* s_flag) {
+  const int n = a.g.n, k = a.topk, lane = lane_id(), c0 = lane * NV;
+  float sv[NV];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
+  for (int i = 0; i < NV; ++i) sv[i] = row[min(c0 + i, n - 1)];
+  if (a.bias) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) sv[r][i] = rows[r][min(c0 + i, n - 1)];
-    add_bias<NV>(sv[r], a.bias, n);
+    for (int i = 0; i < NV; ++i) sv[i] = __fadd_rn(sv[i], bv[i]);
   }
-  wave_select_rows<NV, R>(sv, n, a.topk, id, key, s_slot[threadIdx.x >> 6]);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) key[i] = c0 + i < n ? score_key(sv[i]) : 0u;
+  RGT_STAMP(a.trace, 12);
+  if constexpr (NV <= 4) {
+    __shared__ __align__(16) u64 s_c[4][32];
+    u64* sc = s_c[threadIdx.x >> 6];
+    if (k <= 8) wave_topk_threshold<NV, 8>(key, k, sel, slot, sc);
+    else if (k <= 16) wave_topk_threshold<NV, 16>(key, k, sel, slot, sc);
+    else wave_topk_threshold<NV, 32>(key, k, sel, slot, sc);
+  } else {
+    __shared__ __align__(16) int s_slot[4][64];
+    float sv1[1][NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) sv1[0][i] = sv[i];
+    int id[1];
+    u32 kk[1];
+    wave_select_rows<NV, 1>(sv1, n, k, id, kk, s_slot[threadIdx.x >> 6]);
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (c0 + i < n) s_flag[c0 + i] = 0;
+    if (lane < k) s_flag[id[0]] = lane + 1;  // one wave: after the zeroing
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int f = c0 + i < n ? s_flag[c0 + i] : 0;
+      sel[i] = f > 0;
+      slot[i] = f - 1;
+    }
+  }
+  RGT_STAMP(a.trace, 13);
 }
 
-// Workgroup 0 of small mode: the weights of rows r0, r0 + step, ... from the
+// The top-k of one row of logits held in LDS, by the calling wave: scores
+// lane-major (expert lane*NV + i), plus the bias (bv: this lane's bias values,
+// loaded at the start of the kernel). emit(j, e, key) runs once for each of
+// the k selected experts, in the lane holding it: slot j, expert e, score key.
+// Up to four experts a lane the threshold selection; above, k rounds of a
+// wave maximum (one expert per round, slot order).
+template <int NV, class Emit>
+__device__ __forceinline__ void row_topk(const FusedArgs& a, const float* row, const float (&bv)[NV], Emit&& emit) {
+  const int n = a.g.n, k = a.topk, lane = lane_id(), c0 = lane * NV;
+  float sv[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) sv[i] = row[min(c0 + i, n - 1)];
+  if (a.bias) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) sv[i] = __fadd_rn(sv[i], bv[i]);
+  }
+  RGT_STAMP(a.trace, 12);
+  if constexpr (NV <= 4) {
+    __shared__ __align__(16) u64 s_c[4][32];
+    u64* sc = s_c[threadIdx.x >> 6];
+    u32 key[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) key[i] = c0 + i < n ? score_key(sv[i]) : 0u;
+    bool sel[NV];
+    int slot[NV];
+    if (k <= 8) wave_topk_threshold<NV, 8>(key, k, sel, slot, sc);
+    else if (k <= 16) wave_topk_threshold<NV, 16>(key, k, sel, slot, sc);
+    else wave_topk_threshold<NV, 32>(key, k, sel, slot, sc);
+    RGT_STAMP(a.trace, 13);
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (sel[i]) emit(slot[i], c0 + i, key[i]);
+  } else {
+    __shared__ __align__(16) int s_slot[4][64];
+    float sv1[1][NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) sv1[0][i] = sv[i];
+    int id[1];
+    u32 key[1];
+    wave_select_rows<NV, 1>(sv1, n, k, id, key, s_slot[threadIdx.x >> 6]);
+    RGT_STAMP(a.trace, 13);
+    if (lane < k) emit(lane, id[0], key[0]);
+  }
+}
+
+// Small mode's gate workgroup: the weights of rows r0, r0 + step, ... from the
 // selected keys in s_key (one wave per row at a time).
 __device__ __forceinline__ void rows_weights(const FusedArgs& a, const u32* s_key, int r0, int step) {
   const int k = a.topk, lane = lane_id();
@@ -285,26 +371,248 @@ __device__ __forceinline__ void rows_weights(const FusedArgs& a, const u32* s_ke
   }
 }
 
+// Zero one window of the workspace's tagged-word area per call (all
+// workgroups' reads and writes of this call stay inside its footprint, which
+// the window skips), so that over a sweep of a few hundred calls every word
+// outside the current footprint is rewritten. Tags repeat only after 2^32 - 1
+// calls, so no word can keep a tag that long and be mistaken for a fresh one.
+__device__ __forceinline__ void scrub_window(const FusedArgs& a, u32 tag) {
+  const u32 units = a.scrub_units;
+  const u32 t = threadIdx.x;
+  const u32 first = (u32)(((u64)tag * 256u) % units);
+  const u32 i = first + t >= units ? first + t - units : first + t;
+  const bool in_fp = (i >= a.fp_part0 && i < a.fp_part1) || (i >= a.fp_ids0 && i < a.fp_ids1);
+  if (t < units && !in_fp) reinterpret_cast<uint4*>(a.scrub)[i] = make_uint4(0, 0, 0, 0);
+}
+
+// Outputs of a call made on a workspace whose error word is set (an earlier
+// wait expired): every top-k id is -1, every weight 0 and every offset 0
+// (a padded total of 0: no row of the sort outputs is valid).
+__device__ __forceinline__ void write_poison(const FusedArgs& a) {
+  const int P = a.g.m * a.topk;
+  for (int i = threadIdx.x; i < P; i += 256) {
+    a.topk_ids[i] = -1;
+    a.topk_w[i] = 0.f;
+  }
+  for (int e = threadIdx.x; e <= a.g.n; e += 256) a.offsets[e] = 0;
+}
+
+// pos(p) of 64-bit lane masks: the set bits of mask below the calling lane.
+__device__ __forceinline__ int mask_below(u64 mask) {
+  return (int)__builtin_amdgcn_mbcnt_hi((u32)(mask >> 32), __builtin_amdgcn_mbcnt_lo((u32)mask, 0u));
+}
+__device__ __forceinline__ u64 uniform_u64(u64 v) {
+  return ((u64)(u32)__builtin_amdgcn_readfirstlane((int)(v >> 32)) << 32) |
+         (u32)__builtin_amdgcn_readfirstlane((int)(u32)v);
+}
+
+// A quant workgroup's chunks stored by all of its 256 threads: item it is
+// chunk slot (it mod 2^upw_log) of the workgroup and slot j = it >> upw_log of
+// its token (consecutive threads take consecutive chunks of one padded row).
+// s_codes / s_sc: the chunks' codes and packed scales by chunk slot; s_pos:
+// the padded row of pair t*k + j.
+__device__ __forceinline__ void store_chunks_spread(const FusedArgs& a, int u0, const int* s_pos,
+                                                    const uint4* s_codes, const u32* s_sc) {
+  const int K = a.g.k, k = a.topk, ul = a.upw_log;
+  const int units = a.g.m * (K >> 4), cpr = K >> 4;
+  const u32 row_bytes = a.fp4 ? (u32)K >> 1 : (u32)K;
+  const u32 kscale = (u32)K >> 5;
+  const int items = k << ul;
+  for (int it = threadIdx.x; it < items; it += 256) {
+    const int us = it & ((1 << ul) - 1), j = it >> ul;
+    const int unit = u0 + us;
+    if (unit < units) {
+      const int t = div_magic(unit, a.cpr_magic), c = unit - t * cpr;
+      const u32 r = (u32)s_pos[t * k + j];
+      const uint4 cd = s_codes[us];
+      uint8_t* row = a.a_q + (u64)r * row_bytes;
+      if (a.fp4) *reinterpret_cast<uint2*>(row + 8 * c) = make_uint2(cd.x, cd.y);
+      else *reinterpret_cast<uint4*>(row + 16 * c) = cd;
+      if ((c & 7) == 0) *reinterpret_cast<u32*>(a.a_scale + (u64)r * kscale + (c >> 1)) = s_sc[us];
+    }
+  }
+}
+
+// Small mode after the partials are seen: every participant has every row's
+// logits; wave r runs row r's gate (M <= 4). With M no larger than the block
+// size (block >= 16), an expert holds at most M pairs, so each selected
+// expert fills exactly one block: its segment starts at block * (number of
+// selected experts below it), and a pair's rank in it is the number of
+// earlier rows that chose the same expert. Both come from the rows' selection
+// masks (one ballot per key slot), so the sort needs no histogram and no
+// scan. The gate workgroup writes topk_ids, the weights, the logits and the
+// epoch; the layout workgroup writes offsets, expert_ids and sorted_ids
+// (pairs and pads); the quant workgroups store their chunks.
 template <int NV>
-__device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 tag, bool have_unit, int unit,
-                                           const uint4& codes_in, u32 sb_in) {
+__device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 tag, bool have_unit, int unit,
+                                           const uint4& codes_in, u32 sb_in, const float (&bv)[NV], bool gate_here,
+                                           bool layout_here, bool quant_wg) {
+  __shared__ __align__(16) u64 s_mask[4][NV];
+  const GemvArgs& g = a.g;
+  const int m = g.m, n = g.n, k = a.topk, B = a.block;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int P = m * k, c0 = lane * NV;
+  int* s_pos = smem;                                  // [P] padded position of pair r*k + j
+  u32* s_key = reinterpret_cast<u32*>(smem + P);      // [P] score key of slot j of row r
+  float* s_log = reinterpret_cast<float*>(smem + fused_log_offset(P, n));
+  int* s_flag = smem + fused_tail_ints(P, n, m) + wave * n;  // above four experts a lane only
+  if (!gather_any(a, 0, m, tag, s_log)) return;
+  RGT_STAMP(a.trace, 5);
+  const int row = wave;
+  bool sel[NV];
+  int slot[NV];
+  u32 key[NV];
+  if (row < m) {
+    row_topk_owner<NV>(a, s_log + row * n, bv, sel, slot, key, s_flag);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const u64 mk = ballot64(sel[i]);
+      if (lane == 0) s_mask[row][i] = mk;
+    }
+    if (gate_here) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+        if (sel[i]) {
+          a.topk_ids[row * k + slot[i]] = c0 + i;
+          s_key[row * k + slot[i]] = key[i];
+        }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      sel[i] = false;
+      slot[i] = 0;
+    }
+  }
+  if (gate_here && a.logits_out)
+    for (int i = threadIdx.x; i < m * n; i += 256) a.logits_out[i] = s_log[i];
+  __syncthreads();
+  RGT_STAMP(a.trace, 14);
+  if (gate_here) {
+    // Every partial has been seen, so every workgroup's tag is read.
+    if (threadIdx.x == 0) st_agent(a.ctl + kCtlEpoch, tag);
+    if (!quant_wg && !layout_here) {
+      if (row < m) {
+        const float w = wave_weights(s_key[row * k + min(lane, k - 1)], k);
+        if (lane < k) a.topk_w[row * k + lane] = w;
+      }
+      return;
+    }
+  }
+  // The rows' masks (uniform) and their union.
+  u64 mr[4][NV], un[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) un[i] = 0ull;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      mr[r][i] = r < m ? uniform_u64(s_mask[r][i]) : 0ull;
+      un[i] |= mr[r][i];
+    }
+  int run = 0, present_total = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    run += mask_below(un[i]);
+    present_total += __popcll(un[i]);
+  }
+  int off[NV], cnt[NV], blk[NV];
+  bool present[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    present[i] = (un[i] >> lane) & 1ull;
+    blk[i] = run;
+    off[i] = run * B;
+    run += present[i] ? 1 : 0;
+    int c = 0, rk = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int bit = (int)((mr[r][i] >> lane) & 1ull);
+      c += bit;
+      rk += r < row ? bit : 0;
+    }
+    cnt[i] = c;
+    if (sel[i]) {
+      const int q = off[i] + rk;
+      s_pos[row * k + slot[i]] = q;
+      if (layout_here) a.sorted_ids[q] = row * k + slot[i];
+    }
+  }
+  if (layout_here) {
+    // offsets of every expert (an absent one's segment is empty), the block
+    // of each present expert and its pads; the four waves split the pads
+    if (wave == 0) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        if (c0 + i < n) a.offsets[c0 + i] = off[i];
+        if (present[i]) a.expert_ids[blk[i]] = c0 + i;
+      }
+      if (lane == 0) a.offsets[n] = present_total * B;
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (present[i])
+        for (int q = cnt[i] + wave; q < B; q += 4) a.sorted_ids[off[i] + q] = P;
+  }
+  // the chunks go to LDS so that all four waves store them
+  __shared__ uint4 s_codes[256];
+  __shared__ u32 s_sc[256];
+  const u32 scales4 = pack_scales(sb_in);  // all lanes: DPP reads neighbouring lanes
+  if (have_unit) {
+    s_codes[threadIdx.x] = codes_in;
+    s_sc[threadIdx.x] = scales4;
+  }
+  __syncthreads();  // s_pos and the chunks complete
+  RGT_STAMP(a.trace, 8);
+  RGT_STAMP(a.trace, 3);
+  if (quant_wg) store_chunks_spread(a, (int)blockIdx.x << a.upw_log, s_pos, s_codes, s_sc);
+  RGT_STAMP(a.trace, 9);
+  if (gate_here && row < m) {  // the gate workgroup had no spare of its own
+    const float w = wave_weights(s_key[row * k + min(lane, k - 1)], k);
+    if (lane < k) a.topk_w[row * k + lane] = w;
+  }
+  if (layout_here) scrub_window(a, tag);
+#ifdef RGT_TRACE
+  vm_drain();  // the stores acknowledged
+  RGT_STAMP(a.trace, 2);
+#endif
+}
+
+template <int NV>
+__device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 tag, bool poisoned, bool have_unit,
+                                           int unit, const uint4& codes_in, u32 sb_in, const float (&bv)[NV]) {
   const GemvArgs& g = a.g;
   const int m = g.m, n = g.n, k = a.topk;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int units = m * (g.k >> 4);
-  // Layout workgroups (one per 256 experts, after the last one with quant
-  // units if the grid has room) write offsets, expert_ids and pads.
-  const int n_layout = (n + 255) >> 8;
-  const int layout_wg = min((int)gridDim.x - n_layout, ((units - 1) >> a.upw_log) + 1);
-  const int li = (int)blockIdx.x - layout_wg;  // this workgroup's layout share, if 0 <= li < n_layout
-  // Small mode: the gate workgroup (topk_ids, topk_w, logits, epoch) is the
-  // first one past the layout workgroups if the grid has it, else 0.
+  // Roles. Quant workgroups [0, q_wgs) hold the quant units; the layout
+  // workgroups (one per 256 experts) follow them if the grid has room, else
+  // they are the last ones; the spare workgroups after them run the gates
+  // that feed the others: small mode's gate workgroup (the first spare, else
+  // workgroup 0) and large mode's row workgroups (spare ones when all M fit,
+  // else workgroup r for row r).
   const int q_wgs = ((units - 1) >> a.upw_log) + 1;
-  const int gate_wg = (a.small && layout_wg + n_layout < (int)gridDim.x) ? layout_wg + n_layout : 0;
+  const int n_layout = (n + 255) >> 8;
+  const int layout_wg = min((int)gridDim.x - n_layout, q_wgs);
+  const int li = (int)blockIdx.x - layout_wg;  // this workgroup's layout share, if 0 <= li < n_layout
+  const int spare0 = layout_wg + n_layout;
+  const int gate_wg = (a.small && spare0 < (int)gridDim.x) ? spare0 : 0;
   const bool gate_here = (int)blockIdx.x == gate_wg;
   const bool quant_wg = (int)blockIdx.x < q_wgs;
-  const bool participant = gate_here || quant_wg || (li >= 0 && li < n_layout);
+  const bool layout_here = li >= 0 && li < n_layout;
+  const bool participant = gate_here || quant_wg || layout_here;
   const int P = m * k;
+  if (poisoned) {
+    // An earlier wait of this workspace expired: no waits, defined outputs.
+    if ((int)blockIdx.x == layout_wg) write_poison(a);
+    return;
+  }
+  if (a.small) {
+    // one layout workgroup writes the whole layout in small mode
+    if (!(gate_here || quant_wg || li == 0)) return;
+    small_tail<NV>(a, smem, tag, have_unit, unit, codes_in, sb_in, bv, gate_here, li == 0, quant_wg);
+    return;
+  }
   int* s_e = smem;
   u32* s_key = reinterpret_cast<u32*>(s_e + P);
   int* s_pos = s_e + 2 * P;   // 64 entries
@@ -324,58 +632,23 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
       s_cnt[e] = 0;
       s_pre[e] = 0;
     }
-  if (a.small) {
-    // Step 2 (small): each participant gathers every row and runs every gate;
-    // wave w takes rows w, w + 4, ...
-    if (!participant) return;
-    if (!gather_any(a, 0, m, tag, s_log)) return;
-    RGT_STAMP(a.trace, 5);
-    // (The weights only feed topk_w: workgroup 0 computes them off the
-    // sort-and-store path, below.)
-    auto keep = [&](int row, int id, u32 key) {
-      if (lane < k) {
-        s_e[row * k + lane] = id;
-        s_key[row * k + lane] = key;
-        hist_add(id, row * k + lane, p0, n, s_cnt, s_pre);
-        if (gate_here) a.topk_ids[row * k + lane] = id;
-      }
-    };
-    for (int row = wave; row < m; row += 4) {
-      const float* rows[1] = {s_log + row * n};
-      int id[1];
-      u32 key[1];
-      row_select<NV, 1>(a, rows, id, key);
-      keep(row, id[0], key[0]);
-    }
-    if (gate_here && a.logits_out)
-      for (int i = threadIdx.x; i < m * n; i += 256) a.logits_out[i] = s_log[i];
-    __syncthreads();
-    if (gate_here && gate_wg != 0) {
-      // Every partial has been seen, so every wave has read the epoch.
-      if (threadIdx.x == 0) st_agent(a.ctl + kCtlEpoch, tag);
-      rows_weights(a, s_key, wave, 4);
-      return;
-    }
-    RGT_STAMP(a.trace, 6);
-  } else {
-    // Step 2 (large): workgroup r gathers row r, runs its gate and publishes
-    // the ids; then every participant polls all ids.
-    if ((int)blockIdx.x < m) {
-      const int row = blockIdx.x;
+  {
+    // Step 2 (large): row workgroups gather their row, run its gate and
+    // publish the ids; then every participant polls all ids.
+    const int row_wg0 = spare0 + m <= (int)gridDim.x ? spare0 : 0;
+    const int row = (int)blockIdx.x - row_wg0;
+    if (row >= 0 && row < m) {
       if (!gather_any(a, row, 1, tag, s_log)) return;
       RGT_STAMP(a.trace, 5);
       if (wave == 0) {
-        const float* rows[1] = {s_log};
-        int ids[1];
-        u32 keys[1];
-        row_select<NV, 1>(a, rows, ids, keys);
-        const int id = ids[0];
-        const u32 key = keys[0];
-        if (lane < k) {
-          st_agent(a.tids + row * k + lane, tag_word((u32)id, tag));
-          a.topk_ids[row * k + lane] = id;
-        }
-        const float w = wave_weights(key, k);  // after the ids are published
+        // (s_key is free in large mode: its first k entries hold the row's
+        // keys in slot order for the weights)
+        row_topk<NV>(a, s_log, bv, [&](int j, int e, u32 key) {
+          st_agent(a.tids + row * k + j, tag_word((u32)e, tag));
+          a.topk_ids[row * k + j] = e;
+          s_key[j] = key;
+        });
+        const float w = wave_weights(s_key[min(lane, k - 1)], k);  // after the ids are published
         if (lane < k) a.topk_w[row * k + lane] = w;
       }
       if (a.logits_out)
@@ -386,9 +659,9 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
     if (!poll_ids_any(a, P, tag, s_e, p0, s_cnt, s_pre)) return;
   }
   RGT_STAMP(a.trace, 7);
-  // Every wave of the grid has read the epoch (see the top of this file):
-  // advance it for the next call (large mode, or small mode without a spare
-  // gate workgroup).
+  // Every workgroup's tag is read (see the top of this file): advance the
+  // epoch for the next call (large mode, or small mode without a spare gate
+  // workgroup).
   if (gate_here && threadIdx.x == 0) st_agent(a.ctl + kCtlEpoch, tag);
   // Step 3: positions of the pairs of this workgroup's tokens (a counting
   // sort from the expert histogram), then the workgroup stores its quantised
@@ -396,10 +669,9 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
   // entries are written by the workgroup holding its first quant unit; the
   // layout workgroup writes offsets, expert_ids and the pads.
   if (threadIdx.x < 64) pair_positions<NV>(P, n, a.block, p0, p1, s_e, s_cnt, s_pre, s_off, s_pos);
-  else if (a.small && gate_here) rows_weights(a, s_key, wave - 1, 3);  // while wave 0 works
   __syncthreads();
   RGT_STAMP(a.trace, 8);
-  if (li >= 0 && li < n_layout)
+  if (layout_here)
     write_layout<256>(s_cnt, s_off, n, a.block, P, li << 8, min(n, (li + 1) << 8), a.sorted_ids, a.expert_ids,
                       a.offsets);
   if ((int)threadIdx.x < p1 - p0) {
@@ -407,45 +679,76 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
     const int tok = p / k;
     if (q >= 0 && (tok * cpr) >> a.upw_log == (int)blockIdx.x) a.sorted_ids[q] = p;
   }
+  RGT_STAMP(a.trace, 3);
   const u32 scales4 = pack_scales(sb_in);  // all lanes: DPP reads neighbouring lanes
   if (have_unit) store_unit(a.a_q, a.a_scale, g.k, k, unit, OffsetPos{s_pos, p0}, codes_in, scales4, a.cpr_magic,
                              a.fp4 != 0);
   RGT_STAMP(a.trace, 9);
+  if (li == 0) scrub_window(a, tag);
+#ifdef RGT_TRACE
+  vm_drain();  // the stores acknowledged
+  RGT_STAMP(a.trace, 2);
+#endif
 }
 
-// Shared head of both kernels: read the tag, run the tile, quantise, then the
-// tail. tile(nb, s, sink) computes this workgroup's GEMV tile.
+// Shared head of both kernels: read the control words, run the tile,
+// quantise, then the tail. tile(nb, s, sink) computes this workgroup's GEMV
+// tile.
 template <int NV, class Tile>
 __device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, Tile tile) {
+  __shared__ u32 s_ctl[2];
   const GemvArgs& g = a.g;
   const int units = g.m * (g.k >> 4);
   const int unit = ((int)blockIdx.x << a.upw_log) + threadIdx.x;
   const bool have_unit = (int)threadIdx.x < (1 << a.upw_log) && unit < units;
   const int tile_id = xcd_tile(blockIdx.x, gridDim.x);
   RGT_STAMP(a.trace, 0);
-  // Right after the tile's W loads are issued: the call's tag (loads return
-  // in order, so issued earlier it would hold up the tile's arithmetic) and
-  // the thread's quant chunk of x, quantised once the tile is done.
-  u32 tag = 0;
+  // Right after the tile's W loads are issued: the control words (loads
+  // return in order, so issued earlier they would hold up the tile's
+  // arithmetic), the thread's quant chunk of x, quantised once the tile is
+  // done, and the lane's bias values for the gate.
+  u32 tag = 0, err = 0;
   uint4 xa = make_uint4(0, 0, 0, 0), xb = make_uint4(0, 0, 0, 0);
+  float bv[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) bv[i] = 0.f;
   auto prefetch = [&]() {
-    tag = call_tag(a.ctl);
+    const u64 cw = ld_agent(reinterpret_cast<const u64*>(a.ctl));
+    err = (u32)cw;
+    tag = call_tag_of((u32)(cw >> 32));
     if (have_unit) {
       const int cpr = g.k >> 4, t = div_magic(unit, a.cpr_magic), c = unit - t * cpr;
       const u16* src = g.x + (int64_t)t * g.ldx + 16 * c;
       xa = ld16(src);
       xb = ld16(src + 8);
     }
+    if (a.bias) {
+      const int c0 = lane_id() * NV;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) bv[i] = a.bias[min(c0 + i, g.n - 1)];
+    }
   };
   tile(tile_id, [&](int s, int row, int col, float v) {
-    if (!a.fault_skip) st_agent(a.tpart + ((int64_t)s * g.m + row) * g.n + col, tag_word(__float_as_uint(v), tag));
+    if (!a.fault_skip && err == 0u)
+      st_agent(a.tpart + ((int64_t)s * g.m + row) * g.n + col, tag_word(__float_as_uint(v), tag));
   }, prefetch);
   RGT_STAMP(a.trace, 1);
   u32 sb = 0;
   const uint4 codes = mx_quant16_fmt(xa, xb, sb, a.fp4 != 0);  // all lanes: the scale exchange reads the partner lane
-  __syncthreads();  // the tile's LDS is reused below
+  // Every wave takes wave 0's control words. Wave 0 stores at least one
+  // partial (row 0 of its tile) with its tag, so once every partial of the
+  // call has been seen, every workgroup's read of the epoch is complete and
+  // it may advance; the other waves may store no partial (rows past M), and
+  // a read of their own could return the advanced epoch.
+  if (threadIdx.x == 0) {
+    s_ctl[0] = tag;
+    s_ctl[1] = err;
+  }
+  __syncthreads();  // also: the tile's LDS is reused below
+  tag = s_ctl[0];
+  err = s_ctl[1];
   RGT_STAMP(a.trace, 4);
-  fused_tail<NV>(a, smem, tag, have_unit, unit, codes, sb);
+  fused_tail<NV>(a, smem, tag, err != 0u, have_unit, unit, codes, sb, bv);
 }
 
 // Quant units (16-element chunks of x, row-major) go 2^upw_log to a
@@ -466,9 +769,11 @@ template <int NV, int MT, int KS>
 __global__ void __launch_bounds__(256) fused_mfma_kernel(FusedArgs a) {
   extern __shared__ int smem[];
   fused_body<NV>(a, smem, [&](int t, auto&& sink, auto&& pre) {
-    const int nb = t % a.g.nb_count;
-    const int s = (t / a.g.nb_count) % a.g.s_count;
-    const int mb = t / (a.g.nb_count * a.g.s_count);
+    // row block fastest: the row blocks of one W tile run side by side
+    const int mbc = (int)gridDim.x / (a.g.nb_count * a.g.s_count);
+    const int mb = t % mbc, r = t / mbc;
+    const int nb = r % a.g.nb_count;
+    const int s = r / a.g.nb_count;
     mfma_tile<MT, KS>(a.g, mb, nb, s, reinterpret_cast<float*>(smem), sink, pre);
   });
 }

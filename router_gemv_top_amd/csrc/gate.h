@@ -206,6 +206,86 @@ __device__ __forceinline__ bool select_fast_sorted(const u32 (&key)[NV], int k, 
   return false;
 }
 
+// Top-k by threshold, for up to four keys per lane (lane-major: the key of
+// expert lane*NV + i in key[i], 0 for an absent expert). The selected set is
+// fixed by the largest T with #{key >= T} >= k, found bit by bit from the top
+// bit: a candidate T | 2^b is kept when at least k keys reach it (one ballot
+// count per key slot, uniform scalar work), and the search stops at the first
+// T that exactly k keys reach. Without such a T (equal keys straddle the k-th
+// place) T ends as the k-th largest key: every key above it is selected, and
+// of the keys equal to it the ones with the lowest expert index, as many as
+// are missing. The winners' slots (the number of selected keys that rank
+// above, by key, then expert index) come from one compare against the k
+// selected keys, compacted in expert order through s_c (KMAX u64 of LDS
+// owned by the calling wave; k <= KMAX). Lane-local results: sel[i] and, for
+// a selected key, slot[i].
+template <int NV, int KMAX>
+__device__ __forceinline__ void wave_topk_threshold(const u32 (&key)[NV], int k, bool (&sel)[NV], int (&slot)[NV],
+                                                    u64* s_c) {
+  static_assert(NV <= 4, "the threshold selection takes up to four keys per lane");
+  const int lane = lane_id();
+  u32 T = 0;
+  bool exact = false;
+  for (int b = 31; b >= 0; --b) {
+    const u32 c = T | (1u << b);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) cnt += __popcll(ballot64(key[i] >= c));
+    if (cnt >= k) {
+      T = c;
+      if (cnt == k) {
+        exact = true;
+        break;
+      }
+    }
+  }
+  if (exact) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) sel[i] = key[i] >= T;
+  } else {
+    int ngt = 0, below = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      ngt += __popcll(ballot64(key[i] > T));
+      below += __popcll(ballot64(key[i] == T) & lanemask_lt());
+    }
+    const int need = k - ngt;  // >= 1: at least k keys reach T, fewer exceed it
+    int run = below;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const bool eq = key[i] == T;
+      sel[i] = key[i] > T || (eq && run < need);
+      run += eq ? 1 : 0;
+    }
+  }
+  // compaction in expert order: position = selected keys of lower lanes, then
+  // of lower slots of this lane
+  int cpos = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) cpos += __popcll(ballot64(sel[i]) & lanemask_lt());
+  u64 comp[NV];
+  if (lane < KMAX) s_c[lane] = 0ull;  // entries past k never rank above anything
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    // key first; among equal keys the lower expert (lower position) ranks higher
+    comp[i] = ((u64)key[i] << 32) | (u64)(~(u32)cpos);
+    if (sel[i]) s_c[cpos] = comp[i];
+    cpos += sel[i] ? 1 : 0;
+  }
+  // one wave: its LDS writes above land before these reads
+  int cntv[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) cntv[i] = 0;
+#pragma unroll
+  for (int q = 0; q < KMAX; q += 2) {
+    const ulonglong2 v = *reinterpret_cast<const ulonglong2*>(s_c + q);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) cntv[i] += (v.x > comp[i] ? 1 : 0) + (v.y > comp[i] ? 1 : 0);
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) slot[i] = cntv[i];
+}
+
 // Selection only for R rows at once (R = 1 or 2): lane j < k ends with the
 // j-th expert of row r in my_id[r] and its score key in my_key[r]. s_slot:
 // 64*R ints of LDS owned by the calling wave (16-byte aligned).

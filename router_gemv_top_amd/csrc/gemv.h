@@ -238,9 +238,12 @@ template <int MT, int KS>
 __global__ void __launch_bounds__(256) router_mfma_kernel(GemvArgs a) {
   __shared__ float lds[4 * MT * 256];
   const int t = xcd_tile(blockIdx.x, gridDim.x);
-  const int nb = t % a.nb_count;
-  const int s = (t / a.nb_count) % a.s_count;
-  const int mb = t / (a.nb_count * a.s_count);
+  // row block fastest: the row blocks of one W tile run side by side on one
+  // XCD, so W streams from HBM once and the second block reads it from L2
+  const int mbc = (int)gridDim.x / (a.nb_count * a.s_count);
+  const int mb = t % mbc, r = t / mbc;
+  const int nb = r % a.nb_count;
+  const int s = r / a.nb_count;
   mfma_tile<MT, KS>(a, mb, nb, s, lds, PartialSink{a.part, a.m, a.n});
   u32* ctr = a.ctr + (mb * a.nb_count + nb) * kCtrStride;
   if (arrive_last(ctr, (u32)a.s_count)) {

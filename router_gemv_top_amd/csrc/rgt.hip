@@ -132,6 +132,10 @@ Plan make_plan(int m, int n, int k) {
     // Fewest k-slices that give RGT_MIN_GRID workgroups with the tallest row
     // tile; then shorter row tiles while the grid stays under
     // RGT_MFMA_ROWS_GRID (each workgroup streams 16*MT rows of x from L2).
+    // The row blocks of one W tile are neighbouring workgroups on one XCD
+    // (the kernels take the row block as the fastest index), so the second
+    // block's W loads are served by that XCD's L2 and W still streams from
+    // HBM once.
     p.valu = false;
     p.bn = 16;
     p.nb = n / 16;
@@ -402,7 +406,10 @@ bool fused_small(const Plan& p, int m, int n) {
 size_t fused_lds_bytes(const Plan& p, int m, int n, int topk, bool small) {
   const int P = m * topk;
   const int rows = small ? m : 1;
-  const size_t tail = sizeof(int) * (size_t)fused_tail_ints(P, n, rows);
+  // small mode above four experts a lane: n ints a wave to hand the winners
+  // to their owner lanes
+  const size_t flags = (small && n > 256) ? 4 * (size_t)n : 0;
+  const size_t tail = sizeof(int) * ((size_t)fused_tail_ints(P, n, rows) + flags);
   const size_t tile = p.valu ? 0 : sizeof(float) * 4 * p.mt * 256;
   return std::max(tail, tile);
 }
@@ -726,15 +733,25 @@ static rgt_status route_sort_quant_impl(const void* x, int64_t ldx, const void* 
   }
   if (fuse) {
     const u32 cpr_magic = 0xFFFFFFFFu / (u32)(k / 16) + 1u;  // exact for unit * (K/16) < 2^32
+    // The scrub sweeps the workspace past the tile counters (in the trace
+    // build, up to the phase stamps); this call's tagged words are skipped.
+#ifdef RGT_TRACE
+    const size_t scrub_end = L.trace;
+#else
+    const size_t scrub_end = ws_bytes / 16 * 16;
+#endif
+    const u32 part0 = (u32)((L.tpart - L.part) / 16), ids0 = (u32)((L.tids - L.part) / 16);
     FusedArgs a{g, bias, topk, block, small ? 1 : 0, fp4 ? 1 : 0, upw_log, cpr_magic, logits, topk_ids, topk_w, sorted_ids, expert_ids, offsets,
                 a_q, a_scale, reinterpret_cast<u32*>(base + L.ctl), reinterpret_cast<u64*>(base + L.tpart),
                 reinterpret_cast<u64*>(base + L.tids), wait_budget_ticks(), env_int("RGT_FAULT_INJECT", 0),
 #ifdef RGT_TRACE
-                reinterpret_cast<u64*>(base + L.trace)
+                reinterpret_cast<u64*>(base + L.trace),
 #else
-                nullptr
+                nullptr,
 #endif
-    };
+                reinterpret_cast<u64*>(base + L.part), (u32)((scrub_end - L.part) / 16),
+                part0, part0 + (u32)(((size_t)p.s * m * n * 8 + 15) / 16),
+                ids0, ids0 + (u32)(((size_t)(m * topk + 1) * 8 + 15) / 16)};
     void* args[] = {&a};
     if (hipLaunchKernel(fn, dim3(p.grid), dim3(256), args, lds, stream) != hipSuccess) return RGT_ERR_HIP;
     g_last_launches = 1;

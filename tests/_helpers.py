@@ -13,7 +13,7 @@ from router_gemv_top_amd.inputs import bf16_bits_to_f32
 CANARY = 0xA5
 
 # Workspace control layout (white-box): control words 128 bytes apart (error
-# word, call epoch of the one-launch path), then one tile counter per 128 bytes.
+# word and call epoch of the one-launch path, side by side), then one tile counter per 128 bytes.
 CTL_BYTES, CTR_STRIDE_BYTES, MAX_TILES = 512, 128, 8192
 
 
@@ -22,7 +22,7 @@ def workspace_state(ws):
     import torch
     w = ws.buf[: CTL_BYTES + CTR_STRIDE_BYTES * MAX_TILES].view(torch.int32).cpu().numpy()
     tiles = w[CTL_BYTES // 4:].reshape(MAX_TILES, CTR_STRIDE_BYTES // 4)
-    return int(w[0]), int(w[32]), int(w[64]), tiles
+    return int(w[0]), int(w[1]), int(w[64]), tiles
 
 
 def say(msg: str):

@@ -209,6 +209,18 @@ def test_fused_wait_deadline_sets_error_and_reset_recovers(R, monkeypatch):
     assert R.check_workspace(ws) == 5, "expected RGT_ERR_TIMEOUT in the workspace error word"
     monkeypatch.delenv("RGT_FAULT_INJECT")
     monkeypatch.delenv("RGT_WAIT_BUDGET_US")
+    # fail-stop: a further call on the timed-out workspace waits for nothing
+    # and writes the poison outputs (ids -1, weights 0, offsets 0), whatever
+    # tagged words the failed call left behind
+    say("fused call on a timed-out workspace (poison outputs)")
+    p, launches = fused(R, x, w, b, wl.topk, wl.block, ws)
+    assert launches == 1
+    po = np_out(p)
+    assert np.all(po["topk_ids"] == -1) and np.all(po["topk_w"] == 0)
+    assert np.all(po["offsets"] == 0)
+    assert np.all(po["sorted_ids"].view(np.uint32) == CANARY * 0x01010101)
+    assert np.all(po["a_q"] == CANARY)
+    assert R.check_workspace(ws) == 5
     R.reset_workspace(ws)
     f, _ = fused(R, x, w, b, wl.topk, wl.block, ws)
     assert R.check_workspace(ws) == 0
@@ -290,3 +302,53 @@ def test_fused_formats_share_routing(R):
     ids = check_against_oracle(x, w, None, wl.topk, wl.block, o4)
     check_sort_quant(sort_out(o4), ids, x, wl.n, wl.block, fmt="mxfp4")
     check_sort_quant(sort_out(o8b), ids, x, wl.n, wl.block, fmt="mxfp8")
+
+
+def test_fused_tag_wrap_and_stale_words(R):
+    """The call epoch set just below its 32-bit wrap, then words carrying the
+    tag of a later call planted over the whole tagged-word area (a stale word
+    outliving 2^32 - 1 calls would look like that). Small calls run until the
+    per-call scrub window has swept the area, crossing the wrap; each call's
+    outputs stay equal to a fresh workspace's, and the later call whose tag
+    the planted words carry still reads only its own words."""
+    say("fused tag wrap and stale tagged words")
+    n, kdim, k, block = 128, 6144, 8, 16
+    ref = {}
+    for m in (1, 4, 64):
+        x, w, _ = Workload(f"wrap_M{m}", m, n, kdim, k, block).make()
+        fresh = R.Workspace(m, n, kdim, k, block)
+        o, _ = fused(R, x, w, None, k, block, fresh)
+        ref[m] = (x, w, np_out(o))
+    ws = R.Workspace(64, n, kdim, k, block)
+    words = ws.buf.view(torch.int32)
+    e0 = 0xFFFFFF00
+    words[1] = int(np.array([e0], np.uint32).view(np.int32)[0])
+    ctl_bytes, ctr_bytes = 512, 128 * 8192
+    area = ws.buf[ctl_bytes + ctr_bytes:]
+    units = area.numel() // 16
+    calls = -(-units // 256) + 2
+    # tag of the call after `calls` small calls: epoch + 1, and 0 is skipped
+    # at the wrap
+    v = e0 + 1 + calls
+    t = v - (1 << 32) + 1 if v >= (1 << 32) else v
+    planted = np.zeros(area.numel() // 8, np.uint64)
+    planted[:] = (np.uint64(t) << np.uint64(32)) | np.uint64(0x7F000000)
+    area.copy_(torch.from_numpy(planted.view(np.uint8)).cuda())
+    torch.cuda.synchronize()
+    for i in range(calls):
+        m = (1, 4)[i % 2]
+        x, w, r = ref[m]
+        o, _ = fused(R, x, w, None, k, block, ws)
+        if i % 97 == 0 or i == calls - 1:
+            torch.cuda.synchronize()
+            got = np_out(o)
+            for key in ("logits", "topk_ids", "topk_w", "offsets"):
+                np.testing.assert_array_equal(got[key], r[key], err_msg=f"call {i} M={m} {key}")
+    x, w, r = ref[64]
+    o, _ = fused(R, x, w, None, k, block, ws)
+    torch.cuda.synchronize()
+    assert R.check_workspace(ws) == 0
+    got = np_out(o)
+    for key in ("logits", "topk_ids", "topk_w", "offsets", "sorted_ids"):
+        np.testing.assert_array_equal(got[key], r[key], err_msg=key)
+    assert int(words[1].item()) & 0xFFFFFFFF == t
