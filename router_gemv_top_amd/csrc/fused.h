@@ -113,14 +113,15 @@ constexpr int kPollLoads = 16;
 // one row: item it of the gathered rows sits at byte 16*it of every k-slice
 // and lands at s_log[2*it]. Thread t takes items t, t + 256, ... and their S
 // slices, nl <= NL loads in all (a thread with fewer items repeats its last
-// one). Each thread polls its own loads until every word carries the tag,
+// one). during() runs in every thread once the first poll is issued. Each thread polls its own loads until every word carries the tag,
 // re-issuing them as soon as they return short of it (one poll in flight: a
 // second poll issued with the first sees the same memory state, and the loads
 // it leaves in flight at the exit cost a wait at the next register reuse),
 // then sums each item's slices in k-slice order. Returns false (error word
 // set) if the deadline passes.
-template <int NL>
-__device__ __forceinline__ bool gather_logits(const FusedArgs& a, int r0, int rows, u32 tag, float* s_log) {
+template <int NL, class During>
+__device__ __forceinline__ bool gather_logits(const FusedArgs& a, int r0, int rows, u32 tag, float* s_log,
+                                              During&& during) {
   __shared__ u32 s_bad;
   const int n = a.g.n, S = a.g.s_count;
   const int items = rows * (n >> 1);
@@ -129,11 +130,15 @@ __device__ __forceinline__ bool gather_logits(const FusedArgs& a, int r0, int ro
   const int t = threadIdx.x;
   if (t == 0) s_bad = 0u;
   __syncthreads();
-  if (t < items) {
+  {
+    // Only threads with items poll; during() runs in every thread between the
+    // first issue and the poll loop (uniform there, so it may exchange values
+    // between lanes).
+    const bool poller = t < items;
     const auto rsrc = coherent_rsrc(a.tpart, slice * (u32)S);
     u32 off[NL];
     {
-      int it = t, s = 0;
+      int it = min(t, items - 1), s = 0;
 #pragma unroll
       for (int l = 0; l < NL; ++l) {
         off[l] = row_base + 16u * (u32)it + (u32)s * slice;
@@ -170,11 +175,12 @@ __device__ __forceinline__ bool gather_logits(const FusedArgs& a, int r0, int ro
     };
     const u64 t0 = rt_clock();
     u32x4_t va[NL];
-    issue(va);
+    if (poller) issue(va);
+    during();  // other work while the first poll is in flight
 #ifdef RGT_TRACE
     int polls = 0;
 #endif
-    for (;;) {
+    while (poller) {
 #ifdef RGT_TRACE
       ++polls;
 #endif
@@ -200,11 +206,16 @@ __device__ __forceinline__ bool gather_logits(const FusedArgs& a, int r0, int ro
 // Loads per thread that a gather of `rows` rows needs.
 __host__ __device__ constexpr int gather_loads(int rows, int n, int s) { return (rows * (n / 2) + 255) / 256 * s; }
 
-__device__ __forceinline__ bool gather_any(const FusedArgs& a, int r0, int rows, u32 tag, float* s_log) {
+template <class During>
+__device__ __forceinline__ bool gather_any(const FusedArgs& a, int r0, int rows, u32 tag, float* s_log,
+                                           During&& during) {
   const int nl = gather_loads(rows, a.g.n, a.g.s_count);
-  if (nl <= 4) return gather_logits<4>(a, r0, rows, tag, s_log);
-  if (nl <= 8) return gather_logits<8>(a, r0, rows, tag, s_log);
-  return gather_logits<kPollLoads>(a, r0, rows, tag, s_log);
+  if (nl <= 4) return gather_logits<4>(a, r0, rows, tag, s_log, during);
+  if (nl <= 8) return gather_logits<8>(a, r0, rows, tag, s_log, during);
+  return gather_logits<kPollLoads>(a, r0, rows, tag, s_log, during);
+}
+__device__ __forceinline__ bool gather_any(const FusedArgs& a, int r0, int rows, u32 tag, float* s_log) {
+  return gather_any(a, r0, rows, tag, s_log, [] {});
 }
 
 // The workgroup polls the P tagged ids (16-byte loads, two words each; thread
@@ -418,6 +429,7 @@ __device__ __forceinline__ void store_chunks_spread(const FusedArgs& a, int u0, 
   const u32 row_bytes = a.fp4 ? (u32)K >> 1 : (u32)K;
   const u32 kscale = (u32)K >> 5;
   const int items = k << ul;
+#pragma unroll 2
   for (int it = threadIdx.x; it < items; it += 256) {
     const int us = it & ((1 << ul) - 1), j = it >> ul;
     const int unit = u0 + us;
@@ -445,7 +457,7 @@ __device__ __forceinline__ void store_chunks_spread(const FusedArgs& a, int u0, 
 // (pairs and pads); the quant workgroups store their chunks.
 template <int NV>
 __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 tag, bool have_unit, int unit,
-                                           const uint4& codes_in, u32 sb_in, const float (&bv)[NV], bool gate_here,
+                                           const uint4& xa, const uint4& xb, const float (&bv)[NV], bool gate_here,
                                            bool layout_here, bool quant_wg) {
   __shared__ __align__(16) u64 s_mask[4][NV];
   const GemvArgs& g = a.g;
@@ -456,7 +468,10 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
   u32* s_key = reinterpret_cast<u32*>(smem + P);      // [P] score key of slot j of row r
   float* s_log = reinterpret_cast<float*>(smem + fused_log_offset(P, n));
   int* s_flag = smem + fused_tail_ints(P, n, m) + wave * n;  // above four experts a lane only
-  if (!gather_any(a, 0, m, tag, s_log)) return;
+  // the thread's quant chunk is encoded while the first poll is in flight
+  u32 sb_in = 0;
+  uint4 codes_in = make_uint4(0, 0, 0, 0);
+  if (!gather_any(a, 0, m, tag, s_log, [&] { codes_in = mx_quant16_fmt(xa, xb, sb_in, a.fp4 != 0); })) return;
   RGT_STAMP(a.trace, 5);
   const int row = wave;
   bool sel[NV];
@@ -467,7 +482,7 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const u64 mk = ballot64(sel[i]);
-      if (lane == 0) s_mask[row][i] = mk;
+      if (m > 1 && lane == 0) s_mask[row][i] = mk;
     }
     if (gate_here) {
 #pragma unroll
@@ -486,7 +501,8 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
   }
   if (gate_here && a.logits_out)
     for (int i = threadIdx.x; i < m * n; i += 256) a.logits_out[i] = s_log[i];
-  __syncthreads();
+  // (one row: wave 0 holds everything the positions need, no barrier here)
+  if (m > 1) __syncthreads();
   RGT_STAMP(a.trace, 14);
   if (gate_here) {
     // Every partial has been seen, so every workgroup's tag is read.
@@ -499,60 +515,70 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
       return;
     }
   }
-  // The rows' masks (uniform) and their union.
-  u64 mr[4][NV], un[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) un[i] = 0ull;
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
+  // Segment layout from the rows' selection masks mr (uniform): for this
+  // lane's experts, the first block (blocks before it: present experts
+  // below), the pair count and the rank of row `row`'s pair among them.
+  struct Seg {
+    int blk[NV], cnt[NV], rk[NV];
+    bool present[NV];
+    int total;  // present experts
+  };
+  auto seg_of = [&](const u64 (&mr)[4][NV]) {
+    Seg sg;
+    u64 un[NV];
+    int run = 0;
+    sg.total = 0;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      mr[r][i] = r < m ? uniform_u64(s_mask[r][i]) : 0ull;
-      un[i] |= mr[r][i];
+      un[i] = mr[0][i] | mr[1][i] | mr[2][i] | mr[3][i];
+      run += mask_below(un[i]);
+      sg.total += __popcll(un[i]);
     }
-  int run = 0, present_total = 0;
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    run += mask_below(un[i]);
-    present_total += __popcll(un[i]);
-  }
-  int off[NV], cnt[NV], blk[NV];
-  bool present[NV];
+    for (int i = 0; i < NV; ++i) {
+      sg.present[i] = (un[i] >> lane) & 1ull;
+      sg.blk[i] = run;
+      run += sg.present[i] ? 1 : 0;
+      int c = 0, rk = 0;
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    present[i] = (un[i] >> lane) & 1ull;
-    blk[i] = run;
-    off[i] = run * B;
-    run += present[i] ? 1 : 0;
-    int c = 0, rk = 0;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int bit = (int)((mr[r][i] >> lane) & 1ull);
-      c += bit;
-      rk += r < row ? bit : 0;
+      for (int r = 0; r < 4; ++r) {
+        const int bit = (int)((mr[r][i] >> lane) & 1ull);
+        c += bit;
+        rk += r < row ? bit : 0;
+      }
+      sg.cnt[i] = c;
+      sg.rk[i] = rk;
     }
-    cnt[i] = c;
-    if (sel[i]) {
-      const int q = off[i] + rk;
-      s_pos[row * k + slot[i]] = q;
-      if (layout_here) a.sorted_ids[q] = row * k + slot[i];
-    }
-  }
-  if (layout_here) {
-    // offsets of every expert (an absent one's segment is empty), the block
-    // of each present expert and its pads; the four waves split the pads
-    if (wave == 0) {
+    return sg;
+  };
+  auto masks_lds = [&](u64 (&mr)[4][NV]) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int i = 0; i < NV; ++i) mr[r][i] = r < m ? uniform_u64(s_mask[r][i]) : 0ull;
+  };
+  // Positions of this wave's row (one row: wave 0's own ballots, no barrier
+  // before; it also leaves its masks for the layout workgroup's other waves).
+  if (row < m) {
+    u64 mr[4][NV];
+    if (m == 1) {
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
-        if (c0 + i < n) a.offsets[c0 + i] = off[i];
-        if (present[i]) a.expert_ids[blk[i]] = c0 + i;
+        mr[0][i] = ballot64(sel[i]);
+        mr[1][i] = mr[2][i] = mr[3][i] = 0ull;
+        if (layout_here && lane == 0) s_mask[0][i] = mr[0][i];
       }
-      if (lane == 0) a.offsets[n] = present_total * B;
+    } else {
+      masks_lds(mr);
     }
+    const Seg sg = seg_of(mr);
 #pragma unroll
     for (int i = 0; i < NV; ++i)
-      if (present[i])
-        for (int q = cnt[i] + wave; q < B; q += 4) a.sorted_ids[off[i] + q] = P;
+      if (sel[i]) {
+        const int q = sg.blk[i] * B + sg.rk[i];
+        s_pos[row * k + slot[i]] = q;
+        if (layout_here) a.sorted_ids[q] = row * k + slot[i];
+      }
   }
   // the chunks go to LDS so that all four waves store them
   __shared__ uint4 s_codes[256];
@@ -562,8 +588,27 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
     s_codes[threadIdx.x] = codes_in;
     s_sc[threadIdx.x] = scales4;
   }
-  __syncthreads();  // s_pos and the chunks complete
+  __syncthreads();  // s_pos, the chunks and the masks complete
   RGT_STAMP(a.trace, 8);
+  if (layout_here) {
+    // offsets of every expert (an absent one's segment is empty), the block
+    // of each present expert and its pads (the four waves split the pads)
+    u64 mr[4][NV];
+    masks_lds(mr);
+    const Seg sg = seg_of(mr);
+    if (wave == 0) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        if (c0 + i < n) a.offsets[c0 + i] = sg.blk[i] * B;
+        if (sg.present[i]) a.expert_ids[sg.blk[i]] = c0 + i;
+      }
+      if (lane == 0) a.offsets[n] = sg.total * B;
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (sg.present[i])
+        for (int q = sg.cnt[i] + wave; q < B; q += 4) a.sorted_ids[sg.blk[i] * B + q] = P;
+  }
   RGT_STAMP(a.trace, 3);
   if (quant_wg) store_chunks_spread(a, (int)blockIdx.x << a.upw_log, s_pos, s_codes, s_sc);
   RGT_STAMP(a.trace, 9);
@@ -580,7 +625,7 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
 
 template <int NV>
 __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 tag, bool poisoned, bool have_unit,
-                                           int unit, const uint4& codes_in, u32 sb_in, const float (&bv)[NV]) {
+                                           int unit, const uint4& xa, const uint4& xb, const float (&bv)[NV]) {
   const GemvArgs& g = a.g;
   const int m = g.m, n = g.n, k = a.topk;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -610,9 +655,11 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
   if (a.small) {
     // one layout workgroup writes the whole layout in small mode
     if (!(gate_here || quant_wg || li == 0)) return;
-    small_tail<NV>(a, smem, tag, have_unit, unit, codes_in, sb_in, bv, gate_here, li == 0, quant_wg);
+    small_tail<NV>(a, smem, tag, have_unit, unit, xa, xb, bv, gate_here, li == 0, quant_wg);
     return;
   }
+  u32 sb_in = 0;
+  const uint4 codes_in = mx_quant16_fmt(xa, xb, sb_in, a.fp4 != 0);  // all lanes: the scale exchange reads the partner lane
   int* s_e = smem;
   u32* s_key = reinterpret_cast<u32*>(s_e + P);
   int* s_pos = s_e + 2 * P;   // 64 entries
@@ -733,8 +780,6 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, Tile t
       st_agent(a.tpart + ((int64_t)s * g.m + row) * g.n + col, tag_word(__float_as_uint(v), tag));
   }, prefetch);
   RGT_STAMP(a.trace, 1);
-  u32 sb = 0;
-  const uint4 codes = mx_quant16_fmt(xa, xb, sb, a.fp4 != 0);  // all lanes: the scale exchange reads the partner lane
   // Every wave takes wave 0's control words. Wave 0 stores at least one
   // partial (row 0 of its tile) with its tag, so once every partial of the
   // call has been seen, every workgroup's read of the epoch is complete and
@@ -748,7 +793,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, Tile t
   tag = s_ctl[0];
   err = s_ctl[1];
   RGT_STAMP(a.trace, 4);
-  fused_tail<NV>(a, smem, tag, err != 0u, have_unit, unit, codes, sb, bv);
+  fused_tail<NV>(a, smem, tag, err != 0u, have_unit, unit, xa, xb, bv);
 }
 
 // Quant units (16-element chunks of x, row-major) go 2^upw_log to a

@@ -211,7 +211,10 @@ __device__ __forceinline__ bool select_fast_sorted(const u32 (&key)[NV], int k, 
 // fixed by the largest T with #{key >= T} >= k, found bit by bit from the top
 // bit: a candidate T | 2^b is kept when at least k keys reach it (one ballot
 // count per key slot, uniform scalar work), and the search stops at the first
-// T that exactly k keys reach. Without such a T (equal keys straddle the k-th
+// T that exactly k keys reach. (Measured slower: two bits a step with three
+// candidates counted at once, and skipping candidates above the largest key;
+// the wave issues one instruction at a time, and the compiler turns either
+// into a loop with more branches and selects than the steps they save.) Without such a T (equal keys straddle the k-th
 // place) T ends as the k-th largest key: every key above it is selected, and
 // of the keys equal to it the ones with the lowest expert index, as many as
 // are missing. The winners' slots (the number of selected keys that rank
