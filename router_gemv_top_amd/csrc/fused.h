@@ -206,9 +206,96 @@ __device__ __forceinline__ bool gather_logits(const FusedArgs& a, int r0, int ro
 // Loads per thread that a gather of `rows` rows needs.
 __host__ __device__ constexpr int gather_loads(int rows, int n, int s) { return (rows * (n / 2) + 255) / 256 * s; }
 
+// Gather with the (item, slice) loads spread over all 256 threads when the
+// items alone would leave most threads idle: items is a power of two below
+// 256 and tpi = 256 / items threads share an item, each polling a run of
+// consecutive slices; the loaded partials meet in LDS, and the item's thread
+// then adds its S slices in k-slice order (the same order as the in-register
+// sum, so the same bits). SP: slices a thread polls, at most.
+// The staged partials share LDS with s_log, which the host sizes to
+// S * rows * n floats in that case: slice s of item it sits at float2 index
+// s * items + it, so slice 0 of an item is where its sum goes, and only that
+// item's thread reads it before writing the sum.
+// (Only for 8 or more slices: with fewer, the extra LDS pass and barrier
+// cost more than the shorter polls save; measured at 1 and 2 rows, 3 slices.)
+__host__ __device__ constexpr bool fused_gather_staged(int rows, int n, int s) {
+  return s >= 8 && rows * (n / 2) < 256 && ((rows * (n / 2)) & (rows * (n / 2) - 1)) == 0 &&
+         s * rows * (n / 2) <= 2048;
+}
+template <int SP, class During>
+__device__ __forceinline__ bool gather_staged(const FusedArgs& a, int r0, int rows, u32 tag, float* s_log,
+                                              During&& during) {
+  __shared__ u32 s_bad;
+  float2* s_stage = reinterpret_cast<float2*>(s_log);
+  const int n = a.g.n, S = a.g.s_count;
+  const int items = rows * (n >> 1);
+  const int lg = 31 - __clz(items);
+  const int tpi = 256 >> lg;
+  const int sp = (S + tpi - 1) / tpi;
+  const u32 slice = (u32)a.g.m * (u32)n * 8u;
+  const u32 row_base = (u32)r0 * (u32)n * 8u;
+  const int t = threadIdx.x;
+  const int it = t & (items - 1), sub = t >> lg;
+  const int s0 = sub * sp;
+  const int ns = max(0, min(sp, S - s0));  // this thread's slices
+  if (t == 0) s_bad = 0u;
+  __syncthreads();
+  const auto rsrc = coherent_rsrc(a.tpart, slice * (u32)S);
+  u32 off[SP];
+#pragma unroll
+  for (int l = 0; l < SP; ++l) off[l] = row_base + 16u * (u32)it + (u32)min(s0 + l, S - 1) * slice;
+  u32x4_t va[SP];
+  auto issue = [&]() {
+#pragma unroll
+    for (int l = 0; l < SP; ++l) va[l] = ld_agent16(rsrc, off[l]);
+  };
+  auto ready = [&]() {
+    bool ok = true;
+#pragma unroll
+    for (int l = 0; l < SP; ++l) ok = ok & ((l >= ns) | ((va[l].y == tag) & (va[l].w == tag)));
+    return ok;
+  };
+  const bool poller = ns > 0;
+  const u64 t0 = rt_clock();
+  if (poller) issue();
+  during();
+  while (poller) {
+    if (ready()) {
+#pragma unroll
+      for (int l = 0; l < SP; ++l)
+        if (l < ns) s_stage[(s0 + l) * items + it] = make_float2(__uint_as_float(va[l].x), __uint_as_float(va[l].z));
+      break;
+    }
+    issue();
+    if (rt_clock() - t0 > a.budget) {
+      set_timeout(a);
+      s_bad = 1u;
+      break;
+    }
+  }
+  __syncthreads();
+  if (t < items && s_bad == 0u) {
+    float2 acc = make_float2(0.f, 0.f);
+    for (int s = 0; s < S; ++s) {
+      const float2 v = s_stage[s * items + t];
+      acc.x += v.x;
+      acc.y += v.y;
+    }
+    s_stage[t] = acc;  // = s_log[2t], 2t+1
+  }
+  __syncthreads();
+  return s_bad == 0u;
+}
+
 template <class During>
 __device__ __forceinline__ bool gather_any(const FusedArgs& a, int r0, int rows, u32 tag, float* s_log,
                                            During&& during) {
+  const int items = rows * (a.g.n >> 1), S = a.g.s_count;
+  if (fused_gather_staged(rows, a.g.n, S)) {
+    const int sp = (S + (256 / items) - 1) / (256 / items);
+    if (sp <= 2) return gather_staged<2>(a, r0, rows, tag, s_log, during);
+    if (sp <= 4) return gather_staged<4>(a, r0, rows, tag, s_log, during);
+  }
   const int nl = gather_loads(rows, a.g.n, a.g.s_count);
   if (nl <= 4) return gather_logits<4>(a, r0, rows, tag, s_log, during);
   if (nl <= 8) return gather_logits<8>(a, r0, rows, tag, s_log, during);
@@ -467,7 +554,8 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
   int* s_pos = smem;                                  // [P] padded position of pair r*k + j
   u32* s_key = reinterpret_cast<u32*>(smem + P);      // [P] score key of slot j of row r
   float* s_log = reinterpret_cast<float*>(smem + fused_log_offset(P, n));
-  int* s_flag = smem + fused_tail_ints(P, n, m) + wave * n;  // above four experts a lane only
+  const int stage = fused_gather_staged(m, n, g.s_count) ? (g.s_count - 1) * m * n : 0;
+  int* s_flag = smem + fused_tail_ints(P, n, m) + stage + wave * n;  // above four experts a lane only
   // the thread's quant chunk is encoded while the first poll is in flight
   u32 sb_in = 0;
   uint4 codes_in = make_uint4(0, 0, 0, 0);

@@ -409,7 +409,9 @@ size_t fused_lds_bytes(const Plan& p, int m, int n, int topk, bool small) {
   // small mode above four experts a lane: n ints a wave to hand the winners
   // to their owner lanes
   const size_t flags = (small && n > 256) ? 4 * (size_t)n : 0;
-  const size_t tail = sizeof(int) * ((size_t)fused_tail_ints(P, n, rows) + flags);
+  // a staged gather keeps every slice's partials in the logits' place
+  const size_t stage = fused_gather_staged(rows, n, p.s) ? (size_t)(p.s - 1) * rows * n : 0;
+  const size_t tail = sizeof(int) * ((size_t)fused_tail_ints(P, n, rows) + stage + flags);
   const size_t tile = p.valu ? 0 : sizeof(float) * 4 * p.mt * 256;
   return std::max(tail, tile);
 }
