@@ -213,6 +213,28 @@ rgt_status rgt_route_sort_quant(const void* x, int64_t ldx, const void* w, int64
                                 uint8_t* a_q, uint8_t* a_scale,
                                 void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* rgt_route_sort_quant without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). The workspace is an 8 MiB array inside
+ * the library, one per GPU, held until the process ends; the call allocates
+ * nothing and frees nothing. Arguments, outputs, launch counts and errors are
+ * those of rgt_route_sort_quant, plus: a shape whose workspace
+ * (rgt_workspace_bytes at M = m) exceeds 8 MiB returns RGT_ERR_UNSUPPORTED
+ * and launches nothing (every shape with M <= 64 fits: 2.2 MiB at N = 128,
+ * K = 6144, top-8; 5.9 MiB at N = 896, K = 3584, top-16; 7.3 MiB at
+ * N = 1024, K = 8192, top-32). The first call on a GPU also zero-fills the
+ * array with one kernel on `stream` (counted in rgt_last_launch_count).
+ * Every call on a GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (two streams, two threads) race and give undefined results; run
+ * them in one stream. A device-side deadline expiry poisons the array: every
+ * later call on that GPU writes the poison outputs (top-k ids -1, weights 0,
+ * offsets 0) for the rest of the process. */
+rgt_status rgt_route_sort_quant_noalloc(const void* x, int64_t ldx, const void* w, int64_t ldw,
+                                        const float* bias, int m, int n, int k, int topk, int block,
+                                        float* logits, int32_t* topk_ids, float* topk_w,
+                                        int32_t* sorted_ids, int32_t* expert_ids, int32_t* offsets,
+                                        uint8_t* a_q, uint8_t* a_scale, hipStream_t stream);
+
 /* MXFP4 variants (the stage-1 activation quant of the MoE sort; MiniMax-M3.1-
  * Flash MoE/GEMM kernels page, Summary: MoE sorting + quant, and "Changes to
  * existing kernels": 128-expert top-4 routing at hidden 6144 sorted in one

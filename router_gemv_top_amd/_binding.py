@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
             "rgt_moe_sort_quant": ([vp, vp, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp], i32),
             "rgt_route_sort_quant": ([vp, i64, vp, i64, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
                                       vp, vp, vp, sz, vp], i32),
+            "rgt_route_sort_quant_noalloc": ([vp, i64, vp, i64, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                              vp, vp, vp, vp], i32),
             "rgt_moe_sort_quant_mxfp4": ([vp, vp, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp],
                                          i32),
             "rgt_route_sort_quant_mxfp4": ([vp, i64, vp, i64, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
@@ -310,6 +312,13 @@ def route_sort_quant_mxfp4(x, w, topk: int, block: int, ws: Workspace, bias=None
                              want_logits, stream)
 
 
+def route_sort_quant_noalloc(x, w, topk: int, block: int, bias=None, out=None, want_logits=True, stream=None):
+    """As route_sort_quant, on the library's own per-GPU scratch array (no
+    workspace argument; the call allocates no device memory)."""
+    return _route_sort_quant(lib().rgt_route_sort_quant_noalloc, "mxfp8", x, w, topk, block, None, bias, out,
+                             want_logits, stream)
+
+
 def _route_sort_quant(fn, fmt, x, w, topk, block, ws, bias, out, want_logits, stream):
     _bf16_2d(x, "x"), _bf16_2d(w, "w")
     m, k = x.shape
@@ -319,11 +328,13 @@ def _route_sort_quant(fn, fmt, x, w, topk, block, ws, bias, out, want_logits, st
         out["topk_ids"] = torch.empty((m, topk), dtype=torch.int32, device=x.device)
         out["topk_w"] = torch.empty((m, topk), dtype=torch.float32, device=x.device)
         out["logits"] = torch.empty((m, n), dtype=torch.float32, device=x.device) if want_logits else None
-    _check(fn(_ptr(x), x.stride(0), _ptr(w), w.stride(0), _ptr(bias), m, n, k, topk, block,
-              _ptr(out.get("logits")), _ptr(out["topk_ids"]), _ptr(out["topk_w"]),
-              _ptr(out["sorted_ids"]), _ptr(out["expert_ids"]), _ptr(out["offsets"]),
-              _ptr(out["a_q"]), _ptr(out["a_scale"]), _ptr(ws.buf), ws.nbytes,
-              _stream(stream)), fn.__name__[4:])
+    args = [_ptr(x), x.stride(0), _ptr(w), w.stride(0), _ptr(bias), m, n, k, topk, block,
+            _ptr(out.get("logits")), _ptr(out["topk_ids"]), _ptr(out["topk_w"]),
+            _ptr(out["sorted_ids"]), _ptr(out["expert_ids"]), _ptr(out["offsets"]),
+            _ptr(out["a_q"]), _ptr(out["a_scale"])]
+    if ws is not None:
+        args += [_ptr(ws.buf), ws.nbytes]
+    _check(fn(*args, _stream(stream)), fn.__name__[4:])
     return out
 
 

@@ -452,6 +452,42 @@ int coresident_blocks(const void* fn, size_t lds, int cus) {
   return blocks;
 }
 
+// ---------------------------------------------------------------------------
+// Allocation-free variant of rgt_route_sort_quant: its workspace is this
+// file-scope device array, one copy per GPU, held until the process ends.
+// Host code never passes the array's name to the device: the address comes
+// from hipGetSymbolAddress, taken once per device with that device current.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = 8u << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+void* g_scratch_ptr[64];
+
+__global__ void __launch_bounds__(256) fill_zero_kernel(uint4* p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
+// This device's scratch address. The first call on a device takes the
+// symbol's address and zero-fills the array with a kernel on `stream` (one
+// launch, counted in *launches).
+rgt_status scratch_for(hipStream_t stream, void** out, int* launches) {
+  int d = 0;
+  if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= 64) return RGT_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_scratch_ptr[d]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return RGT_ERR_HIP;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(256), dim3(256), 0, stream, static_cast<uint4*>(p),
+                       kScratchBytes / 16);
+    if (hipGetLastError() != hipSuccess) return RGT_ERR_HIP;
+    g_scratch_ptr[d] = p;
+    ++*launches;
+  }
+  *out = g_scratch_ptr[d];
+  return RGT_OK;
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -792,6 +828,27 @@ rgt_status rgt_route_sort_quant_mxfp4(const void* x, int64_t ldx, const void* w,
                                       hipStream_t stream) {
   return route_sort_quant_impl(x, ldx, w, ldw, bias, m, n, k, topk, block, logits, topk_ids, topk_w, sorted_ids,
                                expert_ids, offsets, a_q, a_scale, true, ws, ws_bytes, stream);
+}
+
+rgt_status rgt_route_sort_quant_noalloc(const void* x, int64_t ldx, const void* w, int64_t ldw, const float* bias,
+                                        int m, int n, int k, int topk, int block, float* logits, int32_t* topk_ids,
+                                        float* topk_w, int32_t* sorted_ids, int32_t* expert_ids, int32_t* offsets,
+                                        uint8_t* a_q, uint8_t* a_scale, hipStream_t stream) {
+  g_last_launches = 0;
+  rgt_status st = check_gemv_args(x, ldx, w, ldw, m, n, k);
+  if (st != RGT_OK) return st;
+  st = check_sort_args(x, ldx, m, n, k, topk, block, sorted_ids, expert_ids, offsets, a_q, a_scale);
+  if (st != RGT_OK || m == 0) return st;
+  if (!topk_ids || !topk_w || !aligned(topk_ids, 4) || !aligned(topk_w, 4)) return RGT_ERR_INVALID;
+  if ((logits && !aligned(logits, 4)) || (bias && !aligned(bias, 4))) return RGT_ERR_INVALID;
+  if (ws_need(m, n, k, topk) > kScratchBytes) return RGT_ERR_UNSUPPORTED;  // beyond the scratch array
+  void* ws = nullptr;
+  int fills = 0;
+  if ((st = scratch_for(stream, &ws, &fills)) != RGT_OK) return st;
+  st = route_sort_quant_impl(x, ldx, w, ldw, bias, m, n, k, topk, block, logits, topk_ids, topk_w, sorted_ids,
+                             expert_ids, offsets, a_q, a_scale, false, ws, kScratchBytes, stream);
+  g_last_launches += fills;
+  return st;
 }
 
 #ifdef RGT_TRACE

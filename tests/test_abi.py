@@ -191,3 +191,20 @@ def test_router_shared_swiglu_argument_errors(L):
     assert call(q=None) == 2 and call(q=FAKE + 8) == 2 and call(sc=None) == 2
     assert call(h=None) == 2 and call(h=FAKE + 1) == 2 and call(ldh=767) == 2
     assert call(x=FAKE + 2) == 2 and call(ldx=6000) == 2
+
+
+def test_route_sort_quant_noalloc_argument_errors(L):
+    f = L.rgt_route_sort_quant_noalloc
+
+    def call(x=FAKE, w=FAKE, bias=None, m=4, n=128, k=6144, topk=8, block=16, logits=None, ids=FAKE, tw=FAKE):
+        return f(x, k, w, k, bias, m, n, k, topk, block, logits, ids, tw, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+
+    assert call(m=0) == 0
+    assert call(n=100) == 1
+    assert call(block=128) == 1
+    assert call(tw=None) == 2
+    assert call(x=FAKE + 2) == 2
+    assert call(bias=FAKE + 2) == 2
+    # a workspace beyond the library's 8 MiB scratch array: unsupported, nothing launched
+    assert call(m=1024, n=1024, k=8192, topk=32, block=64) == 1
+    assert L.rgt_last_launch_count() == 0
