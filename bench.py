@@ -50,31 +50,66 @@ def algorithmic_bytes(m: int, total: int) -> int:
             p * K + p * (K // 32))
 
 
-def cpu_baseline(budget_s: float = 12.0):
-    """The oracle (numpy, fp64) on the host: whole sweeps until ~budget_s."""
+def _host_identity():
+    """Logical CPUs this process may use, and the CPU model string."""
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except Exception:
+        usable = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return usable, model
+
+
+def cpu_baseline(calls: int = 20):
+    """The oracle (numpy, fp64) on the host cores, per M of the sweep: the
+    median of `calls` whole route_sort_quant calls, once with the BLAS pool
+    limited to one thread and once with every usable core (the rest of the
+    oracle is single-threaded numpy either way). `value` is the all-core
+    sweep rate: algorithmic bytes of one sweep / the sum of the per-M medians."""
+    import statistics
     from oracle import rgt_oracle as O
     from router_gemv_top_amd.inputs import gen_w, gen_x
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # threadpoolctl missing: numpy BLAS threads unknown
-        threads = os.cpu_count() or 1
+    from threadpoolctl import threadpool_info, threadpool_limits
+    usable, model = _host_identity()
     w = gen_w(N, K)
     xs = {m: gen_x(m, K) for m in SWEEP}
-    nbytes, sweeps = 0, 0
-    t0 = time.perf_counter()
-    while True:
-        for m in SWEEP:
-            out = O.route_sort_quant(xs[m], w, None, TOPK, BLOCK)
-            nbytes += algorithmic_bytes(m, out["total"])
-        sweeps += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": round(nbytes / dt / 1e9, 6), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{sweeps} full sweeps (M=1..64, N=128, K=6144, top-8, B=16) of the fp64 numpy oracle, "
-                      f"{dt:.1f} s; BLAS matmul multithreaded, the rest single-threaded",
-            "seconds": round(dt, 2)}
+    res = {}
+    t_all = time.perf_counter()
+    for label, threads in (("1_thread", 1), ("all_cores", usable)):
+        per_m = {}
+        with threadpool_limits(limits=threads):
+            used = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+            for m in SWEEP:
+                O.route_sort_quant(xs[m], w, None, TOPK, BLOCK)  # warm
+                ts = []
+                for _ in range(calls):
+                    t0 = time.perf_counter()
+                    out = O.route_sort_quant(xs[m], w, None, TOPK, BLOCK)
+                    ts.append(time.perf_counter() - t0)
+                per_m[m] = (statistics.median(ts) * 1e6, algorithmic_bytes(m, out["total"]))
+        res[label] = {"threads": used, "per_m": per_m}
+    secs = time.perf_counter() - t_all
+
+    def rate(per_m):
+        return sum(b for _, b in per_m.values()) / (sum(us for us, _ in per_m.values()) * 1e-6) / 1e9
+
+    allc = res["all_cores"]
+    return {"value": round(rate(allc["per_m"]), 6), "unit": "GB/s", "cores": int(allc["threads"]), "kind": "oracle",
+            "sample": f"the M=1..64 sweep (N=128, K=6144, top-8, B=16) of the fp64 numpy oracle, median of {calls} "
+                      f"calls per M, single-threaded and on {allc['threads']} BLAS threads; {secs:.1f} s in all",
+            "host": {"usable_cpus": usable, "cpu_model": model},
+            "us_per_call_1_thread": {str(m): round(v[0], 1) for m, v in res["1_thread"]["per_m"].items()},
+            "us_per_call_all_cores": {str(m): round(v[0], 1) for m, v in allc["per_m"].items()},
+            "gbs_1_thread": round(rate(res["1_thread"]["per_m"]), 6),
+            "seconds": round(secs, 2)}
 
 
 def _graph_us(torch, stream, calls, fn):
@@ -266,7 +301,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--copies", type=int, default=0, help="W/x copies to rotate over (0 = enough to evict the MALL)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-calls", type=int, default=20, help="oracle calls per M for the CPU baseline medians")
     ap.add_argument("--no-hot", action="store_true", help="skip the resident-W (hot) timing")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the other routing shapes (wide, many-expert, prefill) and host timing")
@@ -499,7 +534,7 @@ def main():
     if not args.no_secondary:
         line["secondary"] = secondary(torch, R, dev, stream, copies)
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(args.cpu_calls)
     print(json.dumps(line), flush=True)
 
 
