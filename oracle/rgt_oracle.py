@@ -31,6 +31,12 @@ Sources (titles of the pages this follows):
           expert's fp8 SwiGLU in one launch) and GEMM (the M3.1 shared
           expert's 1536 x 6144 gate_up); [MONO] MXFP8 shared-expert commit
           (fp8 values with one scale per 32 elements along K).
+  [K3S1]  "Kimi-K3: fused MoE routing, sort, quant and epilogue" (sglang PR
+          #46652), Modifications: the sorted, quantised activations feed the
+          routed experts' stage-1 GEMM of AITER's fused MoE, A8W4 (8-bit
+          activations, 4-bit weights); MiniMax-M3.1-Flash MoE/GEMM kernels
+          (sglang PR #46691), Summary: MoE sorting + quant (the stage-1
+          activations).
   [OCP]   OCP Microscaling Formats (MX) v1.0: e4m3 element format (bias 7,
           max normal 448, no infinities), e8m0 shared scale (bias 127), shared
           exponent = floor(log2(amax)) - emax_elem with emax_elem = 8 for e4m3;
@@ -68,6 +74,13 @@ notes):
     rounds h once to bf16.
   * Router partials: k-slice s covers K/S consecutive elements
     [s*K/S, (s+1)*K/S); part[s] = fp32(sum over the slice), summed in fp64.
+  * Stage-1 grouped MoE GEMM ([K3S1]): every valid padded row p (a real
+    pair) of the sort, with expert e = expert_ids[p // B], takes its MXFP8 row
+    a = dequant(a_q[p], a_scale[p]) against expert e's MXFP4 gate_up weights
+    W_e [2I][K] (e2m1 codes two a byte, low nibble first, e8m0 scale per 32
+    along K; the I gate rows first): g = a . W_e[:I], u = a . W_e[I:] (exact
+    products, fp64 sums), h = silu(g) * u (the shared expert's SwiGLU
+    reading). Pad rows have no output.
 
 Parity pins: every function here is checked by the ``-m "not gpu"`` tests
 against brute force, exact rationals, closed forms or invariants.
@@ -556,3 +569,67 @@ def shared_swiglu(x_bits: np.ndarray, wq: np.ndarray, ws: np.ndarray):
     gu = shared_gate_up(x_bits, wq, ws)
     inter = gu.shape[1] // 2
     return swiglu(gu, inter), gu[:, :inter], gu[:, inter:]
+
+
+# ---------------------------------------------------------------------------
+# Stage-1 grouped MoE GEMM on the sorted segments [K3S1], [OCP]
+# ---------------------------------------------------------------------------
+
+
+def e2m1_value(codes: np.ndarray) -> np.ndarray:
+    """Exact fp64 value of 4-bit e2m1 codes [OCP]: bit 3 the sign, bits 2..1
+    the exponent (bias 1), bit 0 the mantissa; exponent field 0 holds the
+    subnormals 0 and 0.5. No infinities or NaN."""
+    c = np.asarray(codes, dtype=np.int64) & 0xF
+    e = (c >> 1) & 3
+    f = (c & 1).astype(np.float64)
+    mag = np.where(e == 0, 0.5 * f, np.ldexp(1.0 + 0.5 * f, e - 1))
+    return np.where(c & 8, -mag, mag)
+
+
+def mxfp4_dequant(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """fp64 [R][K] values of MXFP4 rows: packed [R][K/2] (byte j holds
+    element 2j in its low nibble and 2j+1 in its high nibble), scales
+    [R][K/32] e8m0; element (r, i) = e2m1(code) * 2^(scale[r][i // 32] - 127)."""
+    pk = np.asarray(packed, dtype=np.uint8)
+    sc = np.asarray(scales, dtype=np.uint8)
+    r, half = pk.shape
+    k = 2 * half
+    assert sc.shape == (r, k // MX_BLOCK) and k % MX_BLOCK == 0
+    codes = np.empty((r, k), dtype=np.uint8)
+    codes[:, 0::2] = pk & 0xF
+    codes[:, 1::2] = pk >> 4
+    return e2m1_value(codes) * np.repeat(e8m0_value(sc), MX_BLOCK, axis=1)
+
+
+def moe_stage1_swiglu(a_q, a_scale, sorted_ids, expert_ids, total: int, n_pairs: int, block: int,
+                      w_q, w_scale, rows=None):
+    """Stage-1 of the routed experts on the sorted, padded MXFP8 rows.
+
+    For each padded row p < total whose sorted_ids entry is a pair (not the
+    sentinel n_pairs): e = expert_ids[p // block], a = the row's MXFP8 values,
+    W = expert e's MXFP4 gate_up weights [2I][K]; g = a . W[:I], u = a . W[I:]
+    in fp64 (exact products), h = silu(g) * u. Returns (h, g, u) fp64
+    [total][I], NaN in pad rows. `rows`: only these padded rows (others NaN).
+    """
+    w_q = np.asarray(w_q, np.uint8)
+    inter = w_q.shape[1] // 2
+    h = np.full((total, inter), np.nan)
+    g = np.full((total, inter), np.nan)
+    u = np.full((total, inter), np.nan)
+    sid = np.asarray(sorted_ids)[:total]
+    eid = np.asarray(expert_ids)
+    want = np.arange(total) if rows is None else np.asarray(rows)
+    valid = [p for p in want if sid[p] != n_pairs]
+    by_expert = {}
+    for p in valid:
+        by_expert.setdefault(int(eid[p // block]), []).append(p)
+    for e, ps in by_expert.items():
+        w = mxfp4_dequant(w_q[e], w_scale[e])
+        a = mxfp8_dequant(a_q[ps], a_scale[ps])
+        assert np.all(np.isfinite(a)) and np.all(np.isfinite(w))
+        gu = a @ w.T
+        g[ps] = gu[:, :inter]
+        u[ps] = gu[:, inter:]
+        h[ps] = silu(g[ps]) * u[ps]
+    return h, g, u
