@@ -260,6 +260,35 @@ rgt_status rgt_route_sort_quant_mxfp4(const void* x, int64_t ldx, const void* w,
                                       uint8_t* a_q, uint8_t* a_scale,
                                       void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Stage-1 GEMM of the routed experts on the sorted segments (the A8W4 fused
+ * MoE that runs on the sort's outputs: "Kimi-K3: fused MoE routing, sort,
+ * quant and epilogue", Modifications; the stage-1 activations of the
+ * MiniMax-M3.1-Flash MoE/GEMM kernels page, Summary: MoE sorting + quant).
+ * Reads the outputs of rgt_moe_sort_quant / rgt_route_sort_quant (MXFP8) in
+ * place. For every padded row p < offsets[N] whose sorted_ids entry is a
+ * pair (not the sentinel M*topk), with e = expert_ids[p / block]:
+ *   g = a . W_e[j], u = a . W_e[I + j]  (a: the row's MXFP8 values; W_e:
+ *       expert e's gate_up weights, fp32 sums in the MFMA's own order),
+ *   h[p][j] = bf16_rne( silu(g) * u ), silu(g) = g / (1 + exp(-g)), j < I.
+ *   a_q, a_scale, sorted_ids, expert_ids, offsets : as rgt_moe_sort_quant
+ *                 wrote them (M, N, K, topk, block: that call's arguments)
+ *   w_q     : uint8 [N][2I][K/2] e2m1 codes, byte i of a row holding
+ *             elements 2i (low nibble) and 2i+1 (high nibble); rows 0..I-1 of
+ *             an expert the gate projection, I..2I-1 up; 16-byte aligned
+ *   w_scale : uint8 [N][2I][K/32] e8m0 scales (element (r, i) of expert e is
+ *             e2m1(code) * 2^(w_scale[e][r][i/32] - 127))
+ *   h       : bf16 [cap][ldh], device, written for the pair rows and j < I;
+ *             pad rows and rows at or past offsets[N] are not written
+ * Coverage: the sort's shapes (K % 512 == 0, N <= 1024, topk <= 32, block in
+ * {16, 32, 64}, M <= 8192) and 16 <= I <= 65536, I % 16 == 0; otherwise
+ * RGT_ERR_UNSUPPORTED. One launch, no workspace. Scale bytes 255 or NaN
+ * activation codes give NaN outputs; results whose g, u or h leave the fp32 /
+ * bf16 range are unspecified. */
+rgt_status rgt_moe_stage1_swiglu(const uint8_t* a_q, const uint8_t* a_scale, const int32_t* sorted_ids,
+                                 const int32_t* expert_ids, const int32_t* offsets, int m, int n, int k,
+                                 int topk, int block, const uint8_t* w_q, const uint8_t* w_scale, int inter,
+                                 void* h, int64_t ldh, hipStream_t stream);
+
 /* RMSNorm producer in front of the router (the Gemma RMSNorm (+ residual)
  * producers of the MiniMax-M3.1-Flash MoE/GEMM kernels page, Summary: fp8
  * producers; the per-token rstd it publishes is the scale the "route on the

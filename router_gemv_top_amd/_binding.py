@@ -74,6 +74,7 @@ def lib() -> ctypes.CDLL:
             "rgt_route_sort_quant_mxfp4": ([vp, i64, vp, i64, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
                                             vp, vp, vp, sz, vp], i32),
             "rgt_router_partial_slices": ([i32, i32, i32], i32),
+            "rgt_moe_stage1_swiglu": ([vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, i32, vp, i64, vp], i32),
             "rgt_router_shared_swiglu": ([vp, i64, vp, i64, i32, i32, i32, vp, i32, vp, vp, i32, vp, i64, vp], i32),
             "rgt_rmsnorm": ([vp, i64, vp, i64, vp, ctypes.c_float, i32, i32, vp, i64, vp, i64, vp, vp], i32),
             "rgt_last_launch_count": ([], i32),
@@ -336,6 +337,29 @@ def _route_sort_quant(fn, fmt, x, w, topk, block, ws, bias, out, want_logits, st
         args += [_ptr(ws.buf), ws.nbytes]
     _check(fn(*args, _stream(stream)), fn.__name__[4:])
     return out
+
+
+def moe_stage1_swiglu(sort_out, m: int, n: int, topk: int, block: int, w_q, w_scale, h=None, stream=None):
+    """Stage-1 GEMM of the routed experts on the sorted MXFP8 rows of
+    sort_out (a dict with a_q, a_scale, sorted_ids, expert_ids, offsets, as
+    moe_sort_quant / route_sort_quant fill it): h bf16 [cap][I] with
+    h[p] = silu(a . W_e[:I]) * (a . W_e[I:]) for the pair rows p. w_q uint8
+    [N][2I][K/2] (e2m1 codes, low nibble first), w_scale uint8 [N][2I][K/32]."""
+    a_q = sort_out["a_q"]
+    k = a_q.shape[1]
+    if w_q.dtype != torch.uint8 or w_q.dim() != 3 or not w_q.is_contiguous() or w_q.shape[2] * 2 != k:
+        raise ValueError("w_q must be a contiguous uint8 [N][2I][K/2] tensor")
+    inter = w_q.shape[1] // 2
+    if w_scale.dtype != torch.uint8 or tuple(w_scale.shape) != (w_q.shape[0], 2 * inter, k // 32) or \
+            not w_scale.is_contiguous():
+        raise ValueError("w_scale must be a contiguous uint8 [N][2I][K/32] tensor")
+    if h is None:
+        h = torch.zeros((a_q.shape[0], inter), dtype=torch.bfloat16, device=a_q.device)
+    _check(lib().rgt_moe_stage1_swiglu(_ptr(a_q), _ptr(sort_out["a_scale"]), _ptr(sort_out["sorted_ids"]),
+                                       _ptr(sort_out["expert_ids"]), _ptr(sort_out["offsets"]), m, n, k, topk, block,
+                                       _ptr(w_q), _ptr(w_scale), inter, _ptr(h), h.stride(0), _stream(stream)),
+           "moe_stage1_swiglu")
+    return h
 
 
 def rmsnorm(x, gamma, eps: float, residual=None, xn=None, residual_out=None, rstd=None, stream=None):

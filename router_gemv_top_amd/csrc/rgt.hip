@@ -27,6 +27,7 @@
 #include "shared_pick.h"
 #include "sortq.h"
 #include "sortq_kernels.h"
+#include "stage1.h"
 
 using namespace rgt;
 
@@ -849,6 +850,28 @@ rgt_status rgt_route_sort_quant_noalloc(const void* x, int64_t ldx, const void* 
                              expert_ids, offsets, a_q, a_scale, false, ws, kScratchBytes, stream);
   g_last_launches += fills;
   return st;
+}
+
+rgt_status rgt_moe_stage1_swiglu(const uint8_t* a_q, const uint8_t* a_scale, const int32_t* sorted_ids,
+                                 const int32_t* expert_ids, const int32_t* offsets, int m, int n, int k, int topk,
+                                 int block, const uint8_t* w_q, const uint8_t* w_scale, int inter, void* h,
+                                 int64_t ldh, hipStream_t stream) {
+  g_last_launches = 0;
+  if (!covered(m, n, k) || !gate_covered(n, topk) || !block_covered(block) || inter < 16 || inter > (1 << 16) ||
+      inter % 16)
+    return RGT_ERR_UNSUPPORTED;
+  if (m == 0) return RGT_OK;
+  if (!a_q || !a_scale || !sorted_ids || !expert_ids || !offsets || !w_q || !w_scale || !h) return RGT_ERR_INVALID;
+  if (!aligned(a_q, 16) || !aligned(w_q, 16) || !aligned(sorted_ids, 4) || !aligned(expert_ids, 4) ||
+      !aligned(offsets, 4) || !aligned(h, 2) || ldh < inter)
+    return RGT_ERR_INVALID;
+  const int64_t cap = rgt_sort_capacity(m, n, topk, block);
+  Stage1Args a{a_q, a_scale, sorted_ids, expert_ids, offsets, w_q, w_scale, static_cast<uint16_t*>(h), ldh,
+               n, k, inter, block, m * topk};
+  hipLaunchKernelGGL(moe_stage1_kernel, dim3((unsigned)(cap / 16), (unsigned)((inter + 63) / 64)), dim3(256), 0,
+                     stream, a);
+  g_last_launches = 1;
+  return launched();
 }
 
 #ifdef RGT_TRACE

@@ -13,7 +13,8 @@ Modifications).
 Random streams: ``numpy.random.default_rng([seed, stream])`` with one
 independent stream per tensor, so W does not change when M changes:
 stream 0 = x, 1 = W, 2 = bias, 3 = the duplicated-row choice, 4 = W-row ties,
-5 = skew bias, 6 = the shared expert's MXFP8 gate_up weights.
+5 = skew bias, 6 = the shared expert's MXFP8 gate_up weights, 7 = the routed
+experts' MXFP4 gate_up weights.
 
 The shared expert's shape is MiniMax-M3.1's 1536 x 6144 gate_up (768 gate
 rows, then 768 up rows; "MiniMax-M3.1-Flash MoE/GEMM kernels", Summary: GEMM).
@@ -25,7 +26,7 @@ from typing import Optional
 
 import numpy as np
 
-STREAM_X, STREAM_W, STREAM_BIAS, STREAM_DUP, STREAM_WTIE, STREAM_SKEW, STREAM_SHARED = range(7)
+STREAM_X, STREAM_W, STREAM_BIAS, STREAM_DUP, STREAM_WTIE, STREAM_SKEW, STREAM_SHARED, STREAM_EXPERTS = range(8)
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -128,6 +129,17 @@ def gen_mxfp8_weights(rows: int, k: int, seed: int = 0, scale_lo: int = 110, sca
     codes = rng.integers(0, 256, size=(rows, k), dtype=np.uint8)
     codes[(codes & 0x7F) == 0x7F] = 0
     scales = rng.integers(scale_lo, scale_hi, size=(rows, k // 32), dtype=np.uint8)
+    return codes, scales
+
+
+def gen_mxfp4_expert_weights(n: int, rows: int, k: int, seed: int = 0, scale_lo: int = 118, scale_hi: int = 122):
+    """(codes uint8 [n][rows][k/2], scales uint8 [n][rows][k/32]) of random
+    MXFP4 expert weights: every byte holds two e2m1 codes drawn uniformly over
+    all 16 (the format has no NaN), scale bytes uniform in [scale_lo,
+    scale_hi), so elements are at most 6 * 2^(scale_hi - 128)."""
+    rng = _rng(seed, STREAM_EXPERTS)
+    codes = rng.integers(0, 256, size=(n, rows, k // 2), dtype=np.uint8)
+    scales = rng.integers(scale_lo, scale_hi, size=(n, rows, k // 32), dtype=np.uint8)
     return codes, scales
 
 

@@ -104,3 +104,17 @@ def check_sort_quant(out, ids, x_bits, n, block, sample_rows=None, fmt="mxfp8"):
     assert np.all(a_q[total:] == CANARY), "a_q written past the padded total"
     assert np.all(a_sc[total:] == CANARY), "a_scale written past the padded total"
     return total
+
+
+def swiglu_tolerance(g, u, abs_g, abs_u, k):
+    """Bound on |bf16(silu(g) * u) - silu(g) * u| for a kernel whose g and u are
+    fp32 sums of k exact products in any order (abs_g, abs_u: the sums of the
+    products' magnitudes): E = (k - 1) * 2^-24 * abs on each sum; |silu'| <= 1.1;
+    the fp32 exp, add, divide and product add at most 6 ulps; the bf16
+    rounding half an ulp (2^-8 relative)."""
+    u2 = 2.0 ** -24
+    h64 = O.silu(g) * u
+    eg = 1.01 * (k - 1) * u2 * abs_g
+    eu = 1.01 * (k - 1) * u2 * abs_u
+    tol = 1.1 * eg * (np.abs(u) + eu) + np.abs(O.silu(g)) * eu + 6 * u2 * np.abs(h64)
+    return h64, tol + 2.0 ** -8 * (np.abs(h64) + tol) + 1e-37
