@@ -162,6 +162,45 @@ def shared_swiglu_line(torch, R, dev, stream, copies_128: int):
     return {"w_copies": copies, "per_m": per}
 
 
+def stage1_line(torch, R, dev, stream, rot: int = 16):
+    """The routed experts' stage-1 GEMM (MXFP8 rows x MXFP4 gate_up, SwiGLU)
+    on the front end's sort outputs, at the 128-expert / hidden-6144 (I = 768)
+    and 896-expert / hidden-3584 (I = 384, top-16) decode shapes. Each timed
+    call takes the sort of one of `rot` different token batches, so the
+    experts it reads change from call to call (the weights of all experts are
+    2-3x the 256 MB last-level cache). Bytes: the weights and scales of every
+    distinct expert a call touches, its pair rows of a_q and a_scale, its h."""
+    from router_gemv_top_amd.inputs import gen_mxfp4_expert_weights, gen_w as _gw, gen_x as _gx
+    out = {}
+    for (n, k, topk, inter, ms) in ((128, 6144, 8, 768, (1, 8, 64)), (896, 3584, 16, 384, (1, 32))):
+        wq, wsc = gen_mxfp4_expert_weights(n, 2 * inter, k, seed=11)
+        wqd, wsd = torch.from_numpy(wq).to(dev), torch.from_numpy(wsc).to(dev)
+        wr = torch.from_numpy(_gw(n, k, seed=12).view(np.int16)).view(torch.bfloat16).to(dev)
+        per_expert = 2 * inter * (k // 2 + k // 32)
+        per = {}
+        for m in ms:
+            ws = R.Workspace(m, n, k, topk, 16, device=dev)
+            sorts, nbytes = [], 0
+            for i in range(rot):
+                xd = torch.from_numpy(_gx(m, k, seed=100 + i).view(np.int16)).view(torch.bfloat16).to(dev)
+                o = R.route_sort_quant(xd, wr, topk, 16, ws)
+                torch.cuda.synchronize()
+                total = int(o["offsets"][-1].item())
+                ex = torch.unique(o["expert_ids"][: total // 16]).numel()
+                nbytes += ex * per_expert + m * topk * (k + k // 32 + 2 * inter)
+                o["h"] = torch.empty((o["a_q"].shape[0], inter), dtype=torch.bfloat16, device=dev)
+                sorts.append(o)
+            us = _graph_us(torch, stream, rot, lambda i: R.moe_stage1_swiglu(sorts[i], m, n, topk, 16, wqd, wsd,
+                                                                             h=sorts[i]["h"]))
+            gbs = nbytes / rot / (us * 1e-6) / 1e9
+            per[str(m)] = {"us": round(us, 2), "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 3),
+                           "launches": R.last_launch_count()}
+            del sorts
+        out[f"N{n}_K{k}_top{topk}_I{inter}"] = per
+        del wqd, wsd
+    return out
+
+
 def secondary(torch, R, dev, stream, copies_128: int):
     """The other routing shapes, timed like the headline sweep (graph replay,
     cold W by rotating copies), plus the prefill router GEMM alone against the
@@ -211,6 +250,8 @@ def secondary(torch, R, dev, stream, copies_128: int):
 
     res["router_partials_shared_swiglu_N128_K6144_I768_mxfp8"] = shared_swiglu_line(torch, R, dev, stream,
                                                                                      copies_128)
+
+    res["stage1_moe_gemm_a8w4"] = stage1_line(torch, R, dev, stream)
 
     wl = workload_prefill_896()
     x, w, _ = wl.make()
@@ -314,6 +355,8 @@ def main():
     ap.add_argument("--only-shared", action="store_true",
                     help="profiling mode: the router partials + shared-expert SwiGLU line alone "
                          "(M=1,2,4,8,16, N=128, K=6144, I=768), printed as one JSON line")
+    ap.add_argument("--only-stage1", action="store_true",
+                    help="profiling mode: the stage-1 MoE GEMM line alone, printed as one JSON line")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="profiling mode: one plain device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
@@ -339,6 +382,12 @@ def main():
         assert torch.equal(src, dst)
         print(json.dumps({"mode": "calibrate_copy", "bytes_read": args.calibrate_copy,
                           "bytes_written": args.calibrate_copy}), flush=True)
+        return
+
+    if args.only_stage1:
+        line = stage1_line(torch, R, dev, stream)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "only_stage1", **line}), flush=True)
         return
 
     if args.only_shared:

@@ -95,6 +95,12 @@ int pow2_at_least(int v) {
 #define RGT_MFMA_ROWS_GRID 192
 #endif
 
+// The stage-1 GEMM splits K over a workgroup's waves below this many
+// (row tile, 64-column group) pairs.
+#ifndef RGT_STAGE1_KSPLIT_BELOW
+#define RGT_STAGE1_KSPLIT_BELOW 1024
+#endif
+
 // Batches with at least this many 128 x 128 output tiles use the GEMM.
 constexpr int kGemmMinTiles = 256;
 
@@ -868,8 +874,16 @@ rgt_status rgt_moe_stage1_swiglu(const uint8_t* a_q, const uint8_t* a_scale, con
   const int64_t cap = rgt_sort_capacity(m, n, topk, block);
   Stage1Args a{a_q, a_scale, sorted_ids, expert_ids, offsets, w_q, w_scale, static_cast<uint16_t*>(h), ldh,
                n, k, inter, block, m * topk};
-  hipLaunchKernelGGL(moe_stage1_kernel, dim3((unsigned)(cap / 16), (unsigned)((inter + 63) / 64)), dim3(256), 0,
-                     stream, a);
+  // Few row tiles (small batches): the four waves of a workgroup split K for
+  // 16 columns. Else two column tiles a wave (the A fragment feeds four MFMAs)
+  // once the grid has enough workgroups without it, one below.
+  const unsigned tiles = (unsigned)(cap / 16);
+  if ((int64_t)tiles * ((inter + 63) / 64) < RGT_STAGE1_KSPLIT_BELOW)
+    hipLaunchKernelGGL(moe_stage1_ksplit_kernel, dim3(tiles, (unsigned)((inter + 15) / 16)), dim3(256), 0, stream, a);
+  else if ((int64_t)tiles * ((inter + 127) / 128) >= 512)
+    hipLaunchKernelGGL(moe_stage1_kernel<2>, dim3(tiles, (unsigned)((inter + 127) / 128)), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(moe_stage1_kernel<1>, dim3(tiles, (unsigned)((inter + 63) / 64)), dim3(256), 0, stream, a);
   g_last_launches = 1;
   return launched();
 }

@@ -22,12 +22,13 @@
 // [32g, 32g + 32) for both sides; D lane l holds rows 4g + i, column r.
 //
 // A workgroup takes one 16-row tile of padded rows (inside one expert's
-// segment: block sizes are multiples of 16) and 64 output columns; wave w
-// takes the columns j0 + 16w .. + 16 as two MFMA tiles, the gate rows and the
+// segment: block sizes are multiples of 16) and 64 * JT output columns; wave
+// w takes JT column tiles of 16, each as two MFMA tiles, the gate rows and the
 // up rows, so g and u of an output land in the same lane and register and the
-// SwiGLU needs no exchange. Weights stream once per tile of rows; the 16 rows
-// of a come from L2. Loads go four k steps (512 elements) at a time, the next
-// group's loads issued before the current group's MFMAs.
+// SwiGLU needs no exchange (JT = 2 when the grid is large enough: the A
+// fragment then feeds four MFMAs). Weights stream once per tile of rows; the
+// 16 rows of a come from L2. Loads go four k steps (512 elements) at a time,
+// the next group's loads issued before the current group's MFMAs.
 #pragma once
 
 #include "device.h"
@@ -50,81 +51,158 @@ struct Stage1Args {
   int n, k, inter, block, pairs;  // pairs = M * topk (the sentinel)
 };
 
-constexpr int kStage1Group = 4;  // k steps of 128 per load group
+constexpr int kStage1Group = 4;  // k steps of 128 per load group (512 elements, 16 scale blocks)
 
-template <int NG>
-__device__ __forceinline__ void stage1_tile(const Stage1Args& a, int p0, int e, int j) {
+// Step S of a load group: every tile's MFMA on the step's A fragment; op_sel
+// S picks byte S of the scale words.
+template <int S, int JT>
+__device__ __forceinline__ void stage1_step(const uint4& a0, const uint4& a1, const uint4 (&b)[2 * JT][kStage1Group],
+                                            u32 sa, const u32 (&sw)[2 * JT], floatx4_t (&acc)[2 * JT]) {
+  const i32x8_t av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+#pragma unroll
+  for (int t = 0; t < 2 * JT; ++t) {
+    const i32x8_t bv = {(int)b[t][S].x, (int)b[t][S].y, (int)b[t][S].z, (int)b[t][S].w, 0, 0, 0, 0};
+    acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[t], 0, 4, S, (int)sa, S, (int)sw[t]);
+  }
+}
+
+// One wave: 16 padded rows (p0 ..) x JT column tiles of 16 outputs (j, j + 16,
+// ...), each tile a gate MFMA and an up MFMA on the same A fragment.
+//
+// K order inside a load group (any order works as long as A, B and the
+// scales agree): at step s, hardware k block hb (the MFMA's k [32hb,
+// 32hb + 32)) carries data block 4hb + s of the group. Then a lane's B bytes
+// for the four steps are one contiguous 64-byte run, its scale bytes for the
+// four steps one 4-byte word (the MFMA picks byte s with op_sel), and its A
+// bytes two runs of four 16-byte chunks 32 bytes apart.
+template <int JT>
+__device__ __forceinline__ void stage1_tile(const Stage1Args& a, int p0, int e, int j, int g0, int g1,
+                                            floatx4_t (&acc)[2 * JT]) {
   const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   const int K = a.k;
-  const uint8_t* arow = a.a_q + (int64_t)(p0 + r) * K;
-  const uint8_t* asc = a.a_scale + (int64_t)(p0 + r) * (K >> 5);
+  const uint8_t* arow = a.a_q + (int64_t)(p0 + r) * K + 128 * (g >> 1) + 16 * (g & 1);
+  const u32* asc = reinterpret_cast<const u32*>(a.a_scale + (int64_t)(p0 + r) * (K >> 5)) + g;
   const int64_t wrows = 2 * (int64_t)a.inter;
-  const uint8_t* wg = a.w_q + ((int64_t)e * wrows + j + r) * (K >> 1);
-  const uint8_t* wu = a.w_q + ((int64_t)e * wrows + a.inter + j + r) * (K >> 1);
-  const uint8_t* sg = a.w_scale + ((int64_t)e * wrows + j + r) * (K >> 5);
-  const uint8_t* su = a.w_scale + ((int64_t)e * wrows + a.inter + j + r) * (K >> 5);
-  floatx4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-  // one group: 4 steps of A (two 16-byte halves each), B gate and up (16
-  // bytes each), and the scale byte of block 4s + g of every side
-  struct Grp {
-    uint4 a0[kStage1Group], a1[kStage1Group], bg[kStage1Group], bu[kStage1Group];
-    uint8_t sa[kStage1Group], sg[kStage1Group], su[kStage1Group];
-  };
-  auto load = [&](Grp& q, int grp) {
+  const uint8_t* wb[2 * JT];
+  const u32* sb[2 * JT];
 #pragma unroll
-    for (int s = 0; s < kStage1Group; ++s) {
-      const int k0 = (grp * kStage1Group + s) * 128;
-      q.a0[s] = *reinterpret_cast<const uint4*>(arow + k0 + 16 * g);
-      q.a1[s] = *reinterpret_cast<const uint4*>(arow + k0 + 64 + 16 * g);
-      q.bg[s] = *reinterpret_cast<const uint4*>(wg + (k0 >> 1) + 16 * g);
-      q.bu[s] = *reinterpret_cast<const uint4*>(wu + (k0 >> 1) + 16 * g);
-      const int blk = (k0 >> 5) + g;
-      q.sa[s] = asc[blk];
-      q.sg[s] = sg[blk];
-      q.su[s] = su[blk];
-    }
-  };
-  auto mma = [&](const Grp& q) {
-#pragma unroll
-    for (int s = 0; s < kStage1Group; ++s) {
-      const i32x8_t av = {(int)q.a0[s].x, (int)q.a0[s].y, (int)q.a0[s].z, (int)q.a0[s].w,
-                          (int)q.a1[s].x, (int)q.a1[s].y, (int)q.a1[s].z, (int)q.a1[s].w};
-      const i32x8_t bgv = {(int)q.bg[s].x, (int)q.bg[s].y, (int)q.bg[s].z, (int)q.bg[s].w, 0, 0, 0, 0};
-      const i32x8_t buv = {(int)q.bu[s].x, (int)q.bu[s].y, (int)q.bu[s].z, (int)q.bu[s].w, 0, 0, 0, 0};
-      accg = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bgv, accg, 0, 4, 0, (int)q.sa[s], 0,
-                                                             (int)q.sg[s]);
-      accu = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, buv, accu, 0, 4, 0, (int)q.sa[s], 0,
-                                                             (int)q.su[s]);
-    }
-  };
-  const int groups = K / (128 * kStage1Group);
-  Grp q[2];
-  load(q[0], 0);
-  for (int grp = 0; grp < groups; ++grp) {
-    if (grp + 1 < groups) load(q[(grp + 1) & 1], grp + 1);
-    mma(q[grp & 1]);
+  for (int t = 0; t < JT; ++t) {
+    const int64_t rg = (int64_t)e * wrows + j + 16 * t + r, ru = rg + a.inter;
+    wb[2 * t] = a.w_q + rg * (K >> 1) + 64 * g;
+    wb[2 * t + 1] = a.w_q + ru * (K >> 1) + 64 * g;
+    sb[2 * t] = reinterpret_cast<const u32*>(a.w_scale + rg * (K >> 5)) + g;
+    sb[2 * t + 1] = reinterpret_cast<const u32*>(a.w_scale + ru * (K >> 5)) + g;
   }
-  // D lane l: rows 4g + i, column r: output column j + r of padded rows p0 + 4g + i
+#pragma unroll
+  for (int t = 0; t < 2 * JT; ++t) acc[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  if (g0 >= g1) return;
+  // The current group's operands and the next group's, as plain register
+  // arrays with constant indices (a struct passed around by reference ends up
+  // in scratch memory); the next group's loads go out before this group's
+  // MFMAs, then the registers move over.
+  uint4 a0[kStage1Group], a1[kStage1Group], b[2 * JT][kStage1Group];
+  uint4 na0[kStage1Group], na1[kStage1Group], nb[2 * JT][kStage1Group];
+  u32 sa, sw[2 * JT], nsa = 0, nsw[2 * JT];
+#define RGT_STAGE1_LOAD(A0, A1, B, SA, SW, GRP)                                              \
+  do {                                                                                     \
+    const uint8_t* ar_ = arow + 512 * (GRP);                                               \
+    _Pragma("unroll") for (int s_ = 0; s_ < kStage1Group; ++s_) {                          \
+      A0[s_] = *reinterpret_cast<const uint4*>(ar_ + 32 * s_);                             \
+      A1[s_] = *reinterpret_cast<const uint4*>(ar_ + 256 + 32 * s_);                       \
+    }                                                                                      \
+    SA = asc[4 * (GRP)];                                                                   \
+    _Pragma("unroll") for (int t_ = 0; t_ < 2 * JT; ++t_) {                                \
+      _Pragma("unroll") for (int s_ = 0; s_ < kStage1Group; ++s_)                          \
+        B[t_][s_] = *reinterpret_cast<const uint4*>(wb[t_] + 256 * (GRP) + 16 * s_);        \
+      SW[t_] = sb[t_][4 * (GRP)];                                                          \
+    }                                                                                      \
+  } while (0)
+  RGT_STAGE1_LOAD(a0, a1, b, sa, sw, g0);
+  for (int grp = g0; grp < g1; ++grp) {
+    if (grp + 1 < g1) RGT_STAGE1_LOAD(na0, na1, nb, nsa, nsw, grp + 1);
+    stage1_step<0, JT>(a0[0], a1[0], b, sa, sw, acc);
+    stage1_step<1, JT>(a0[1], a1[1], b, sa, sw, acc);
+    stage1_step<2, JT>(a0[2], a1[2], b, sa, sw, acc);
+    stage1_step<3, JT>(a0[3], a1[3], b, sa, sw, acc);
+#pragma unroll
+    for (int s = 0; s < kStage1Group; ++s) {
+      a0[s] = na0[s];
+      a1[s] = na1[s];
+#pragma unroll
+      for (int t = 0; t < 2 * JT; ++t) b[t][s] = nb[t][s];
+    }
+    sa = nsa;
+#pragma unroll
+    for (int t = 0; t < 2 * JT; ++t) sw[t] = nsw[t];
+  }
+#undef RGT_STAGE1_LOAD
+}
+
+// SwiGLU of a finished tile pair and the store of the pair rows. D lane l:
+// rows 4g + i, column r of each tile.
+template <int JT>
+__device__ __forceinline__ void stage1_store(const Stage1Args& a, int p0, int j, const floatx4_t (&acc)[2 * JT]) {
+  const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int p = p0 + 4 * g + i;
     if (a.sorted_ids[p] < a.pairs) {
-      const float gv = accg[i], uv = accu[i];
-      const float sgl = gv / (1.f + expf(-gv));
-      a.h[(int64_t)p * a.ldh + j + r] = (uint16_t)bf16_rne(sgl * uv);
+#pragma unroll
+      for (int t = 0; t < JT; ++t) {
+        const int col = j + 16 * t + r;
+        if (col < a.inter) {
+          const float gv = acc[2 * t][i], uv = acc[2 * t + 1][i];
+          const float sgl = gv / (1.f + expf(-gv));
+          a.h[(int64_t)p * a.ldh + col] = (uint16_t)bf16_rne(sgl * uv);
+        }
+      }
     }
   }
 }
 
-// Grid: (cap / 16) row tiles x ceil(I / 64) column groups, 256 threads.
+// Grid: (cap / 16) row tiles x ceil(I / (64 * JT)) column groups, 256
+// threads; wave w takes output columns j0 + 16 * JT * w ...
+template <int JT>
 __global__ void __launch_bounds__(256) moe_stage1_kernel(Stage1Args a) {
   const int p0 = (int)blockIdx.x * 16;
   const int total = a.offsets[a.n];
   if (p0 >= total) return;  // past the padded total: no segment here
   const int e = a.expert_ids[p0 >> (__ffs(a.block) - 1)];
-  const int j = ((int)blockIdx.y * 4 + (threadIdx.x >> 6)) * 16;
+  const int j = ((int)blockIdx.y * 4 + (threadIdx.x >> 6)) * 16 * JT;
   if (j >= a.inter) return;
-  stage1_tile<kStage1Group>(a, p0, e, j);
+  floatx4_t acc[2 * JT];
+  stage1_tile<JT>(a, p0, e, j, 0, a.k / 512, acc);
+  stage1_store<JT>(a, p0, j, acc);
+}
+
+// Small grids: the four waves of a workgroup split K (load groups w*G/4 ..
+// (w+1)*G/4) for the same 16 output columns, and wave 0 adds the four parts
+// in wave order through LDS (fixed order: deterministic). Grid: (cap / 16)
+// row tiles x ceil(I / 16) column tiles.
+__global__ void __launch_bounds__(256) moe_stage1_ksplit_kernel(Stage1Args a) {
+  __shared__ floatx4_t s_part[3][2][64];
+  const int p0 = (int)blockIdx.x * 16;
+  const int total = a.offsets[a.n];
+  if (p0 >= total) return;
+  const int e = a.expert_ids[p0 >> (__ffs(a.block) - 1)];
+  const int j = (int)blockIdx.y * 16;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int G = a.k / 512;
+  floatx4_t acc[2];
+  stage1_tile<1>(a, p0, e, j, wave * G / 4, (wave + 1) * G / 4, acc);
+  if (wave > 0) {
+    s_part[wave - 1][0][lane] = acc[0];
+    s_part[wave - 1][1][lane] = acc[1];
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int w = 0; w < 3; ++w) {
+      acc[0] += s_part[w][0][lane];
+      acc[1] += s_part[w][1][lane];
+    }
+    stage1_store<1>(a, p0, j, acc);
+  }
 }
 
 }  // namespace rgt
