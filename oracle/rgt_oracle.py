@@ -633,3 +633,26 @@ def moe_stage1_swiglu(a_q, a_scale, sorted_ids, expert_ids, total: int, n_pairs:
         u[ps] = gu[:, inter:]
         h[ps] = silu(g[ps]) * u[ps]
     return h, g, u
+
+
+# ---------------------------------------------------------------------------
+# Routing on the norm's scale [MONO] "route on the norm's scale", [M3R]
+# ---------------------------------------------------------------------------
+
+
+def rmsnorm_route_sort_quant(x_bits, r_bits, gamma_bits, eps: float, w_bits, bias, k: int, block: int,
+                             rstd=None, fmt: str = "mxfp8"):
+    """The front end fed by the RMSNorm producer: h = x (+ residual), rstd,
+    xn = bf16((h * rstd) * (1 + gamma)), then route_sort_quant on xn (router
+    logits, gate, sort and the MX quant of the gathered xn rows). The router
+    routes on the norm's published scale: its activations are exactly the
+    norm's xn. `rstd`: the per-token scale to use (a kernel's own, whose fp32
+    sum order is its own); None takes the oracle's fp64 value. Returns the
+    route_sort_quant dict plus xn, rstd and h."""
+    h = x_bits if r_bits is None else residual_add(x_bits, r_bits)
+    if rstd is None:
+        rstd = rmsnorm_rstd(h, eps)
+    xn = rmsnorm_apply(h, rstd, gamma_bits)
+    out = route_sort_quant(xn, w_bits, bias, k, block, fmt=fmt)
+    out.update(xn=xn, rstd=np.asarray(rstd, np.float32), h=h)
+    return out

@@ -136,3 +136,34 @@ def test_route_sort_quant_equals_its_stages(fmt, with_bias):
         for key in ("sorted_ids", "expert_ids", "offsets", "a_q", "a_scale", "valid"):
             np.testing.assert_array_equal(out[key], sq[key], err_msg=key)
         assert out["total"] == sq["total"] and len(out["offsets"]) == n + 1
+
+
+@pytest.mark.parametrize("with_res", [True, False])
+def test_rmsnorm_route_sort_quant_equals_its_stages(with_res):
+    """Routing on the norm's scale is the norm's xn routed: every field equals
+    the pinned RMSNorm stages followed by the pinned chain, on random tiny
+    shapes (N != K), with and without a residual, with the oracle's own rstd
+    and with a given one."""
+    rng = np.random.default_rng(21)
+    for (m, n, k, topk, block) in [(1, 8, 64, 2, 4), (6, 12, 96, 3, 16)]:
+        x = f32_to_bf16_bits(rng.standard_normal((m, k), dtype=np.float32))
+        r = f32_to_bf16_bits(rng.standard_normal((m, k), dtype=np.float32)) if with_res else None
+        gamma = f32_to_bf16_bits(0.1 * rng.standard_normal(k).astype(np.float32))
+        w = f32_to_bf16_bits(0.5 * rng.standard_normal((n, k), dtype=np.float32))
+        bias = (0.3 * rng.standard_normal(n)).astype(np.float32)
+        for given in (None, (1.0 + 0.01 * rng.standard_normal(m)).astype(np.float32)):
+            out = O.rmsnorm_route_sort_quant(x, r, gamma, 1e-6, w, bias, topk, block, rstd=given)
+            xn, rstd, h = O.rmsnorm(x, r, gamma, 1e-6)
+            if given is not None:
+                rstd = given
+                xn = O.rmsnorm_apply(h, given, gamma)
+            ref = O.route_sort_quant(xn, w, bias, topk, block)
+            np.testing.assert_array_equal(out["xn"], xn)
+            np.testing.assert_array_equal(out["h"], h)
+            np.testing.assert_array_equal(out["rstd"], rstd)
+            for key in ("logits", "topk_ids", "topk_w", "sorted_ids", "expert_ids", "offsets", "a_q", "a_scale"):
+                np.testing.assert_array_equal(out[key], ref[key], err_msg=key)
+            # the quantised rows are the normed activations, not the raw x
+            if given is None and not np.array_equal(xn, x):
+                q_raw = O.route_sort_quant(x, w, bias, topk, block)
+                assert not np.array_equal(out["a_q"], q_raw["a_q"]) or out["total"] != q_raw["total"]
