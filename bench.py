@@ -292,7 +292,13 @@ def secondary(torch, R, dev, stream, copies_128: int):
             R.rmsnorm(xa, gam6, 1e-6, residual=ra, xn=xn, rstd=rs, residual_out=ro)
             R.route_sort_quant(xn, w_r, TOPK, BLOCK, ws, out=o)
         us_b = _graph_us(torch, stream, 64, both)
-        norm[str(m)] = {"norm_us": round(us_n, 3), "norm_plus_route_us": round(us_b, 3)}
+        # the same work through the one entry (one launch at M = 1, where the
+        # router routes on the norm's scale; the norm's launch first above)
+        o1 = dict(o, xn=xn, rstd=rs, residual_out=ro)
+        us_1 = _graph_us(torch, stream, 64, lambda i: R.rmsnorm_route_sort_quant(
+            xa, gam6, 1e-6, w_r, TOPK, BLOCK, ws, residual=ra, out=o1))
+        norm[str(m)] = {"norm_us": round(us_n, 3), "norm_plus_route_us": round(us_b, 3),
+                        "rmsnorm_route_sort_quant_us": round(us_1, 3)}
     mp, kp = 8192, 3584
     gamp = torch.from_numpy(np.asarray(rng.standard_normal(kp) * 0.1, np.float32)).to(dev).to(torch.bfloat16)
     xa, ra = dev_bf16(_gx(mp, kp, seed=7)), dev_bf16(_gx(mp, kp, seed=8))

@@ -311,6 +311,42 @@ rgt_status rgt_rmsnorm(const void* x, int64_t ldx, const void* residual, int64_t
                        int m, int k, void* xn, int64_t ldxn, void* residual_out, int64_t ldro, float* rstd,
                        hipStream_t stream);
 
+/* The front end behind its RMSNorm producer: rgt_rmsnorm, then
+ * rgt_route_sort_quant (or _mxfp4) on its xn, with every output bit-identical
+ * to that two-call chain on the same inputs (xn, residual_out and rstd as
+ * rgt_rmsnorm writes them; logits, gate, sort and quant as the route call
+ * writes them from xn). The router routes on the norm's scale ("route on the
+ * norm's scale", MiniMax-M3.1 FFN monokernel page, Modifications): in the
+ * one-launch form (M <= 64, K <= 8192) workgroup m takes row m's rstd and
+ * publishes it (with M = 1 every workgroup takes it itself), and every
+ * router tile normalises its own columns of x (and the residual) with that
+ * rstd instead of reading a written xn. Otherwise the norm's own launch comes
+ * first and the route call reads its xn (rgt_last_launch_count tells which).
+ * The one-launch form is taken at M = 1, where it is faster; the environment
+ * variable RGT_NORM_IN_LAUNCH=1 takes it for every M it covers, =0 never.
+ * Arguments: those of rgt_rmsnorm (x, residual, gamma, eps, xn,
+ * residual_out, rstd; xn is required and must not overlap x or residual)
+ * and of rgt_route_sort_quant (w, bias, sizes, outputs, workspace: the same
+ * rgt_workspace_bytes); `x` is the raw input, not the router's. Coverage and
+ * errors: the union of both calls' rules. The one-launch form waits on
+ * device words like rgt_route_sort_quant; after an expired wait the route
+ * outputs are the poison values and xn, residual_out and rstd are
+ * unspecified. */
+rgt_status rgt_rmsnorm_route_sort_quant(const void* x, int64_t ldx, const void* residual, int64_t ldr,
+                                        const void* gamma, float eps, const void* w, int64_t ldw, const float* bias,
+                                        int m, int n, int k, int topk, int block, void* xn, int64_t ldxn,
+                                        void* residual_out, int64_t ldro, float* rstd, float* logits,
+                                        int32_t* topk_ids, float* topk_w, int32_t* sorted_ids, int32_t* expert_ids,
+                                        int32_t* offsets, uint8_t* a_q, uint8_t* a_scale, void* ws, size_t ws_bytes,
+                                        hipStream_t stream);
+rgt_status rgt_rmsnorm_route_sort_quant_mxfp4(const void* x, int64_t ldx, const void* residual, int64_t ldr,
+                                              const void* gamma, float eps, const void* w, int64_t ldw,
+                                              const float* bias, int m, int n, int k, int topk, int block, void* xn,
+                                              int64_t ldxn, void* residual_out, int64_t ldro, float* rstd,
+                                              float* logits, int32_t* topk_ids, float* topk_w, int32_t* sorted_ids,
+                                              int32_t* expert_ids, int32_t* offsets, uint8_t* a_q, uint8_t* a_scale,
+                                              void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Number of kernel launches the last successful call of each entry point made
  * on this thread (diagnostics for launch-count checks). */
 int rgt_last_launch_count(void);

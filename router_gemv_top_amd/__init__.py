@@ -9,7 +9,7 @@ loading the HIP library.
 
 _API = (
     "rmsnorm", "router_logits", "router_partial_slices", "router_shared_swiglu", "topk_gate", "topk_gate_partials", "moe_sort_quant", "route_sort_quant", "moe_sort_quant_mxfp4",
-    "route_sort_quant_mxfp4", "route_sort_quant_noalloc", "moe_stage1_swiglu", "Workspace",
+    "route_sort_quant_mxfp4", "route_sort_quant_noalloc", "rmsnorm_route_sort_quant", "moe_stage1_swiglu", "Workspace",
     "workspace_bytes", "sort_capacity", "router_supported", "reset_workspace", "check_workspace",
     "status_string", "last_launch_count", "alloc_sort_outputs", "RgtError", "RgtUnsupported", "lib",
     "exported_symbols", "version", "diag_read", "diag_copy",

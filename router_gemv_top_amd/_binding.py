@@ -77,6 +77,12 @@ def lib() -> ctypes.CDLL:
             "rgt_moe_stage1_swiglu": ([vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, i32, vp, i64, vp], i32),
             "rgt_router_shared_swiglu": ([vp, i64, vp, i64, i32, i32, i32, vp, i32, vp, vp, i32, vp, i64, vp], i32),
             "rgt_rmsnorm": ([vp, i64, vp, i64, vp, ctypes.c_float, i32, i32, vp, i64, vp, i64, vp, vp], i32),
+            "rgt_rmsnorm_route_sort_quant": ([vp, i64, vp, i64, vp, ctypes.c_float, vp, i64, vp, i32, i32, i32, i32,
+                                              i32, vp, i64, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                              ctypes.c_size_t, vp], i32),
+            "rgt_rmsnorm_route_sort_quant_mxfp4": ([vp, i64, vp, i64, vp, ctypes.c_float, vp, i64, vp, i32, i32, i32,
+                                                    i32, i32, vp, i64, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                    vp, ctypes.c_size_t, vp], i32),
             "rgt_last_launch_count": ([], i32),
             "rgt_diag_read": ([vp, sz, vp, i32, vp], i32),
             "rgt_diag_copy": ([vp, vp, sz, i32, vp], i32),
@@ -383,6 +389,40 @@ def rmsnorm(x, gamma, eps: float, residual=None, xn=None, residual_out=None, rst
                              0 if residual_out is None else residual_out.stride(0), _ptr(rstd), _stream(stream)),
            "rmsnorm")
     return xn, rstd, residual_out
+
+
+def rmsnorm_route_sort_quant(x, gamma, eps: float, w, topk: int, block: int, ws: Workspace, residual=None,
+                             bias=None, out=None, want_logits=True, fmt: str = "mxfp8", stream=None):
+    """The front end behind its RMSNorm producer (one launch for M <= 64 and
+    K <= 8192): x and residual are the raw inputs; returns the route dict of
+    route_sort_quant plus xn, rstd and residual_out (h, with a residual)."""
+    _bf16_2d(x, "x"), _bf16_2d(w, "w")
+    m, k = x.shape
+    n = w.shape[0]
+    if gamma.dtype != torch.bfloat16 or gamma.dim() != 1 or not gamma.is_contiguous():
+        raise ValueError("gamma must be a contiguous 1-D bfloat16 tensor")
+    if residual is not None:
+        _bf16_2d(residual, "residual")
+    if fmt not in ("mxfp8", "mxfp4"):
+        raise ValueError("fmt must be 'mxfp8' or 'mxfp4'")
+    if out is None:
+        out = alloc_sort_outputs(m, n, k, topk, block, x.device, fmt=fmt)
+        out["topk_ids"] = torch.empty((m, topk), dtype=torch.int32, device=x.device)
+        out["topk_w"] = torch.empty((m, topk), dtype=torch.float32, device=x.device)
+        out["logits"] = torch.empty((m, n), dtype=torch.float32, device=x.device) if want_logits else None
+        out["xn"] = torch.empty((m, k), dtype=torch.bfloat16, device=x.device)
+        out["rstd"] = torch.empty((m,), dtype=torch.float32, device=x.device)
+        out["residual_out"] = None if residual is None else torch.empty((m, k), dtype=torch.bfloat16,
+                                                                        device=x.device)
+    ro = out.get("residual_out")
+    fn = lib().rgt_rmsnorm_route_sort_quant if fmt == "mxfp8" else lib().rgt_rmsnorm_route_sort_quant_mxfp4
+    _check(fn(_ptr(x), x.stride(0), _ptr(residual), 0 if residual is None else residual.stride(0), _ptr(gamma),
+              float(eps), _ptr(w), w.stride(0), _ptr(bias), m, n, k, topk, block, _ptr(out["xn"]), out["xn"].stride(0),
+              _ptr(ro), 0 if ro is None else ro.stride(0), _ptr(out.get("rstd")), _ptr(out.get("logits")),
+              _ptr(out["topk_ids"]), _ptr(out["topk_w"]), _ptr(out["sorted_ids"]), _ptr(out["expert_ids"]),
+              _ptr(out["offsets"]), _ptr(out["a_q"]), _ptr(out["a_scale"]), _ptr(ws.buf), ws.nbytes,
+              _stream(stream)), fn.__name__[4:])
+    return out
 
 
 def diag_read(src, sink, grid: int, nbytes: int | None = None, stream=None):

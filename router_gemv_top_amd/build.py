@@ -51,9 +51,11 @@ def units(trace: bool):
     d = os.path.join(OBJ_DIR, tag)
     extra = ["-DRGT_TRACE"] if trace else []
     out = [(os.path.join(CSRC, "rgt.hip"), os.path.join(d, "rgt.o"), extra)]
-    for nv in NV_BUCKETS:
-        out.append((os.path.join(CSRC, "fused_inst.hip"), os.path.join(d, f"fused_nv{nv}.o"),
-                    extra + [f"-DRGT_NV={nv}"]))
+    for norm in (0, 1):
+        for nv in NV_BUCKETS:
+            name = f"fused_norm_nv{nv}.o" if norm else f"fused_nv{nv}.o"
+            out.append((os.path.join(CSRC, "fused_inst.hip"), os.path.join(d, name),
+                        extra + [f"-DRGT_NV={nv}", f"-DRGT_NORM={norm}"]))
     out.append((os.path.join(CSRC, "shared_inst.hip"), os.path.join(d, "shared_inst.o"), extra))
     return out
 

@@ -47,6 +47,7 @@
 #include "device.h"
 #include "gate.h"
 #include "gemv.h"
+#include "norm.h"
 #include "sortq.h"
 
 namespace rgt {
@@ -92,6 +93,18 @@ struct FusedArgs {
   u64* scrub;          // the workspace past the tile counters (16-byte aligned)
   u32 scrub_units;     // its size in 16-byte units (> 0)
   u32 fp_part0, fp_part1, fp_ids0, fp_ids1;  // this call's tagged words, 16-byte units from scrub
+  // The RMSNorm producer in front of the router (instances with the norm
+  // only): g.x is the raw x, the router and the quant read xn.
+  const u16* res;      // [M][ldr] residual or null
+  int64_t ldr;
+  const u16* gamma;    // [K]
+  float eps;
+  u16* xn;             // [M][ldxn] written
+  int64_t ldxn;
+  u16* res_out;        // [M][ldro] written with h if not null (needs res)
+  int64_t ldro;
+  float* rstd_out;     // [M] written if not null
+  u64* trs;            // [M] tagged rstd words (workspace, after tids)
 };
 
 // The call's tag from the epoch word: epoch + 1, skipping 0 so zero-filled
@@ -542,10 +555,10 @@ __device__ __forceinline__ void store_chunks_spread(const FusedArgs& a, int u0, 
 // scan. The gate workgroup writes topk_ids, the weights, the logits and the
 // epoch; the layout workgroup writes offsets, expert_ids and sorted_ids
 // (pairs and pads); the quant workgroups store their chunks.
-template <int NV>
+template <int NV, class Quant>
 __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 tag, bool have_unit, int unit,
-                                           const uint4& xa, const uint4& xb, const float (&bv)[NV], bool gate_here,
-                                           bool layout_here, bool quant_wg) {
+                                           Quant&& quant, const float (&bv)[NV], bool gate_here, bool layout_here,
+                                           bool quant_wg) {
   __shared__ __align__(16) u64 s_mask[4][NV];
   const GemvArgs& g = a.g;
   const int m = g.m, n = g.n, k = a.topk, B = a.block;
@@ -559,7 +572,7 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
   // the thread's quant chunk is encoded while the first poll is in flight
   u32 sb_in = 0;
   uint4 codes_in = make_uint4(0, 0, 0, 0);
-  if (!gather_any(a, 0, m, tag, s_log, [&] { codes_in = mx_quant16_fmt(xa, xb, sb_in, a.fp4 != 0); })) return;
+  if (!gather_any(a, 0, m, tag, s_log, [&] { codes_in = quant(sb_in); })) return;
   RGT_STAMP(a.trace, 5);
   const int row = wave;
   bool sel[NV];
@@ -711,9 +724,11 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
 #endif
 }
 
-template <int NV>
+// quant(sb) returns the thread's encoded quant chunk and its scale byte(s);
+// every lane of a wave calls it together.
+template <int NV, class Quant>
 __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 tag, bool poisoned, bool have_unit,
-                                           int unit, const uint4& xa, const uint4& xb, const float (&bv)[NV]) {
+                                           int unit, Quant&& quant, const float (&bv)[NV]) {
   const GemvArgs& g = a.g;
   const int m = g.m, n = g.n, k = a.topk;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -743,11 +758,11 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
   if (a.small) {
     // one layout workgroup writes the whole layout in small mode
     if (!(gate_here || quant_wg || li == 0)) return;
-    small_tail<NV>(a, smem, tag, have_unit, unit, xa, xb, bv, gate_here, li == 0, quant_wg);
+    small_tail<NV>(a, smem, tag, have_unit, unit, quant, bv, gate_here, li == 0, quant_wg);
     return;
   }
   u32 sb_in = 0;
-  const uint4 codes_in = mx_quant16_fmt(xa, xb, sb_in, a.fp4 != 0);  // all lanes: the scale exchange reads the partner lane
+  const uint4 codes_in = quant(sb_in);  // all lanes: the scale exchange reads the partner lane
   int* s_e = smem;
   u32* s_key = reinterpret_cast<u32*>(s_e + P);
   int* s_pos = s_e + 2 * P;   // 64 entries
@@ -783,6 +798,9 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
           a.topk_ids[row * k + j] = e;
           s_key[j] = key;
         });
+        // the pad word of an odd pair count: every word of the call's
+        // footprint carries its tag
+        if (row == m - 1 && lane == 0 && (P & 1)) st_agent(a.tids + P, tag_word(0u, tag));
         const float w = wave_weights(s_key[min(lane, k - 1)], k);  // after the ids are published
         if (lane < k) a.topk_w[row * k + lane] = w;
       }
@@ -826,10 +844,158 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
 #endif
 }
 
-// Shared head of both kernels: read the control words, run the tile,
-// quantise, then the tail. tile(nb, s, sink) computes this workgroup's GEMV
-// tile.
-template <int NV, class Tile>
+// The router behind the RMSNorm producer ("route on the norm's scale",
+// MiniMax-M3.1 FFN monokernel page, Modifications): workgroup r < M is row
+// r's norm workgroup; it loads that row of x (and the residual) before its
+// tile's loads, and once its tile's loads are out takes the row's rstd with
+// the norm kernel's own reduction and publishes it as a tagged word. Every
+// tile loads the raw x, residual and gamma chunks of its own columns, takes
+// its rows' rstd words and normalises those columns itself (h, then xn, as
+// the norm kernel computes them), so its products are those of the router
+// fed the norm's xn. The norm workgroups publish before they wait, and the
+// launch is co-resident, so every wait ends. With one row every workgroup
+// takes the row's rstd itself (the same reduction, so the same bits) and
+// nothing is published or waited for: the row is 2K bytes (4K with the
+// residual) served by L2, cheaper than a hand-off.
+constexpr int kNormChunks = 4;  // 8-element chunks a thread holds of a norm row: K <= 8192
+
+struct NormX {
+  static constexpr bool kOn = true;
+  const FusedArgs& a;
+  const u32& tag;  // the wave's control words, read by prefetch before row_work
+  u32& err;
+  float& rs_own;   // the rstd this workgroup took (its norm row's)
+  uint4 hv[kNormChunks];
+  uint4 rv[kNormChunks];
+
+  __device__ __forceinline__ NormX(const FusedArgs& args, const u32& t, u32& e, float& r)
+      : a(args), tag(t), err(e), rs_own(r) {}
+
+  __device__ __forceinline__ bool local() const { return a.g.m == 1; }
+  __device__ __forceinline__ bool norm_wg() const { return local() || (int)blockIdx.x < a.g.m; }
+  __device__ __forceinline__ int norm_row() const { return local() ? 0 : (int)blockIdx.x; }
+
+  // Before the tile's loads: the norm row's x and residual.
+  __device__ __forceinline__ void begin() {
+    if (!norm_wg()) return;
+    const int nch = a.g.k >> 3, row = norm_row();
+#pragma unroll
+    for (int c = 0; c < kNormChunks; ++c) {
+      const int idx = min((int)threadIdx.x + 256 * c, nch - 1);
+      hv[c] = ld16(a.g.x + (int64_t)row * a.g.ldx + 8 * idx);
+      if (a.res) rv[c] = ld16(a.res + (int64_t)row * a.ldr + 8 * idx);
+    }
+  }
+  __device__ __forceinline__ uint4 res(int row, int k) const {
+    return a.res ? ld16(a.res + (int64_t)row * a.ldr + k) : make_uint4(0, 0, 0, 0);
+  }
+  __device__ __forceinline__ uint4 gamma(int k) const { return ld16(a.gamma + k); }
+  // The norm workgroup's rstd, published (whole workgroup: one barrier).
+  __device__ __forceinline__ void row_work() {
+    if (!norm_wg()) return;
+    if (a.res) {
+#pragma unroll
+      for (int c = 0; c < kNormChunks; ++c) hv[c] = add_bf16x8(hv[c], rv[c]);
+    }
+    const float rs = row_rstd<kNormChunks>(hv, a.g.k >> 3, a.g.k, a.eps);
+    rs_own = rs;
+    if (threadIdx.x == 0) {
+      if (!local() && !a.fault_skip && err == 0u) {
+        st_agent(a.trs + blockIdx.x, tag_word(__float_as_uint(rs), tag));
+        // the pad word of an odd M: every word of the call's footprint
+        // carries its tag
+        if ((int)blockIdx.x == a.g.m - 1 && (a.g.m & 1)) st_agent(a.trs + a.g.m, tag_word(0u, tag));
+      }
+      if (a.rstd_out && (int)blockIdx.x < a.g.m) a.rstd_out[blockIdx.x] = rs;
+    }
+    RGT_STAMP(a.trace, 11);
+  }
+  // The rows' published rstd (lanes may ask for different rows), all words
+  // polled together. On an expired wait the error word is set and this wave
+  // publishes nothing; a workspace already in error waits for nothing (no
+  // word is published).
+  template <int R>
+  __device__ __forceinline__ void rstd_rows(const int (&rows)[R], float (&out)[R]) {
+    if (local()) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) out[i] = rs_own;
+      return;
+    }
+    u64 v[R];
+    auto issue = [&]() {
+#pragma unroll
+      for (int i = 0; i < R; ++i) v[i] = ld_agent(a.trs + rows[i]);
+    };
+    auto ready = [&]() {
+      bool ok = true;
+#pragma unroll
+      for (int i = 0; i < R; ++i) ok = ok & tag_ok(v[i], tag);
+      return ok;
+    };
+    issue();
+    if (err == 0u && ballot64(!ready())) {
+      const u64 t0 = rt_clock();
+      for (;;) {
+        issue();
+        if (!ballot64(!ready())) break;
+        if (rt_clock() - t0 > a.budget) {
+          set_timeout(a);
+          err = kErrTimeout;
+          break;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i) out[i] = __uint_as_float((u32)v[i]);
+    RGT_STAMP(a.trace, 15);
+  }
+  __device__ __forceinline__ uint4 residual(uint4 x, uint4 r) const { return a.res ? add_bf16x8(x, r) : x; }
+  __device__ __forceinline__ uint4 apply(uint4 h, uint4 g, float rs) const { return norm_bf16x8(h, g, rs); }
+};
+
+// A quant unit of the norm variant: its chunk of xn (and h), from the raw x
+// and residual chunks and the token's rstd (with one row the workgroup's
+// own, else the published word: it is out before any tile of the token ends,
+// so it is there by the tail); stores both. One lane's wait; false if it
+// expired.
+__device__ __forceinline__ bool norm_unit(const FusedArgs& a, int unit, u32 tag, float rs_own, uint4& xa, uint4& xb,
+                                          const uint4& ra, const uint4& rb, const uint4& ga, const uint4& gb) {
+  const int cpr = a.g.k >> 4, t = div_magic(unit, a.cpr_magic), c = unit - t * cpr;
+  float rs = rs_own;
+  if (a.g.m > 1) {
+    u64 v = ld_agent(a.trs + t);
+    if (!tag_ok(v, tag)) {
+      const u64 t0 = rt_clock();
+      while (!tag_ok(v = ld_agent(a.trs + t), tag)) {
+        if (rt_clock() - t0 > a.budget) {
+          set_timeout(a);
+          return false;
+        }
+      }
+    }
+    rs = __uint_as_float((u32)v);
+  }
+  if (a.res) {
+    xa = add_bf16x8(xa, ra);
+    xb = add_bf16x8(xb, rb);
+    if (a.res_out) {
+      uint4* ro = reinterpret_cast<uint4*>(a.res_out + (int64_t)t * a.ldro + 16 * c);
+      ro[0] = xa;
+      ro[1] = xb;
+    }
+  }
+  xa = norm_bf16x8(xa, ga, rs);
+  xb = norm_bf16x8(xb, gb, rs);
+  uint4* xo = reinterpret_cast<uint4*>(a.xn + (int64_t)t * a.ldxn + 16 * c);
+  xo[0] = xa;
+  xo[1] = xb;
+  return true;
+}
+
+// Shared head of the kernels: read the control words, run the tile, then the
+// tail. tile(t, sink, pre, xf) computes this workgroup's GEMV tile; with NORM
+// the tile and the quant units read the RMSNorm of x (NormX).
+template <int NV, bool NORM, class Tile>
 __device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, Tile tile) {
   __shared__ u32 s_ctl[2];
   const GemvArgs& g = a.g;
@@ -840,10 +1006,12 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, Tile t
   RGT_STAMP(a.trace, 0);
   // Right after the tile's W loads are issued: the control words (loads
   // return in order, so issued earlier they would hold up the tile's
-  // arithmetic), the thread's quant chunk of x, quantised once the tile is
-  // done, and the lane's bias values for the gate.
+  // arithmetic), the thread's quant chunk of x (with the norm: and of the
+  // residual and gamma), quantised once the tile is done, and the lane's bias
+  // values for the gate.
   u32 tag = 0, err = 0;
   uint4 xa = make_uint4(0, 0, 0, 0), xb = make_uint4(0, 0, 0, 0);
+  [[maybe_unused]] uint4 ra = xa, rb = xa, ga = xa, gb = xa;
   float bv[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) bv[i] = 0.f;
@@ -856,6 +1024,15 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, Tile t
       const u16* src = g.x + (int64_t)t * g.ldx + 16 * c;
       xa = ld16(src);
       xb = ld16(src + 8);
+      if constexpr (NORM) {
+        if (a.res) {
+          const u16* rsrc = a.res + (int64_t)t * a.ldr + 16 * c;
+          ra = ld16(rsrc);
+          rb = ld16(rsrc + 8);
+        }
+        ga = ld16(a.gamma + 16 * c);
+        gb = ld16(a.gamma + 16 * c + 8);
+      }
     }
     if (a.bias) {
       const int c0 = lane_id() * NV;
@@ -863,10 +1040,18 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, Tile t
       for (int i = 0; i < NV; ++i) bv[i] = a.bias[min(c0 + i, g.n - 1)];
     }
   };
-  tile(tile_id, [&](int s, int row, int col, float v) {
+  auto sink = [&](int s, int row, int col, float v) {
     if (!a.fault_skip && err == 0u)
       st_agent(a.tpart + ((int64_t)s * g.m + row) * g.n + col, tag_word(__float_as_uint(v), tag));
-  }, prefetch);
+  };
+  [[maybe_unused]] float rs_own = 0.f;
+  if constexpr (NORM) {
+    NormX xf(a, tag, err, rs_own);
+    xf.begin();
+    tile(tile_id, sink, prefetch, xf);
+  } else {
+    tile(tile_id, sink, prefetch, NoNorm());
+  }
   RGT_STAMP(a.trace, 1);
   // Every wave takes wave 0's control words. Wave 0 stores at least one
   // partial (row 0 of its tile) with its tag, so once every partial of the
@@ -881,7 +1066,14 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, Tile t
   tag = s_ctl[0];
   err = s_ctl[1];
   RGT_STAMP(a.trace, 4);
-  fused_tail<NV>(a, smem, tag, err != 0u, have_unit, unit, xa, xb, bv);
+  auto quant = [&](u32& sb) {
+    uint4 c0 = xa, c1 = xb;
+    if constexpr (NORM) {
+      if (have_unit) norm_unit(a, unit, tag, rs_own, c0, c1, ra, rb, ga, gb);
+    }
+    return mx_quant16_fmt(c0, c1, sb, a.fp4 != 0);
+  };
+  fused_tail<NV>(a, smem, tag, err != 0u, have_unit, unit, quant, bv);
 }
 
 // Quant units (16-element chunks of x, row-major) go 2^upw_log to a
@@ -890,24 +1082,24 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, Tile t
 // them all (the tail's stores spread over more CUs); large mode the most
 // whose token pairs fit one wave (fewer quant workgroups; measured faster
 // there, slower in small mode).
-template <int NV, int MT, int RPW, int L>
+template <int NV, bool NORM, int MT, int RPW, int L>
 __global__ void __launch_bounds__(256) fused_valu_kernel(FusedArgs a) {
   extern __shared__ int smem[];
-  fused_body<NV>(a, smem, [&](int t, auto&& sink, auto&& pre) {
-    valu_tile<MT, RPW, L>(a.g, t % a.g.nb_count, t / a.g.nb_count, sink, pre);
+  fused_body<NV, NORM>(a, smem, [&](int t, auto&& sink, auto&& pre, auto&& xf) {
+    valu_tile<MT, RPW, L>(a.g, t % a.g.nb_count, t / a.g.nb_count, sink, pre, xf);
   });
 }
 
-template <int NV, int MT, int KS>
+template <int NV, bool NORM, int MT, int KS>
 __global__ void __launch_bounds__(256) fused_mfma_kernel(FusedArgs a) {
   extern __shared__ int smem[];
-  fused_body<NV>(a, smem, [&](int t, auto&& sink, auto&& pre) {
+  fused_body<NV, NORM>(a, smem, [&](int t, auto&& sink, auto&& pre, auto&& xf) {
     // row block fastest: the row blocks of one W tile run side by side
     const int mbc = (int)gridDim.x / (a.g.nb_count * a.g.s_count);
     const int mb = t % mbc, r = t / mbc;
     const int nb = r % a.g.nb_count;
     const int s = r / a.g.nb_count;
-    mfma_tile<MT, KS>(a.g, mb, nb, s, reinterpret_cast<float*>(smem), sink, pre);
+    mfma_tile<MT, KS>(a.g, mb, nb, s, reinterpret_cast<float*>(smem), sink, pre, xf);
   });
 }
 

@@ -18,6 +18,8 @@
 //     wave order through LDS.
 #pragma once
 
+#include <type_traits>
+
 #include "device.h"
 
 namespace rgt {
@@ -60,16 +62,42 @@ struct NoPrefetch {
   __device__ __forceinline__ void operator()() const {}
 };
 
-template <int MT, int RPW, int L, class Sink, class Pre = NoPrefetch>
-__device__ __forceinline__ void valu_tile(const GemvArgs& a, int nb, int s, const Sink& sink, Pre&& pre = Pre()) {
+// The tile's x as it is in memory. A transform with kOn = true instead has
+// the tile load the residual and gamma chunks beside each x chunk and, after
+// pre(), add the residual (residual(x, r) = h), run its row work, take its
+// rows' scales (rstd_rows) and replace the chunk by apply(h, gamma, scale):
+// the router behind the RMSNorm producer normalises its own columns.
+struct NoNorm {
+  static constexpr bool kOn = false;
+  __device__ __forceinline__ uint4 res(int, int) const { return make_uint4(0, 0, 0, 0); }
+  __device__ __forceinline__ uint4 gamma(int) const { return make_uint4(0, 0, 0, 0); }
+  __device__ __forceinline__ void row_work() {}
+  template <int R>
+  __device__ __forceinline__ void rstd_rows(const int (&)[R], float (&out)[R]) {
+    for (int i = 0; i < R; ++i) out[i] = 0.f;
+  }
+  __device__ __forceinline__ uint4 residual(uint4 x, uint4) const { return x; }
+  __device__ __forceinline__ uint4 apply(uint4 x, uint4, float) const { return x; }
+};
+
+template <int MT, int RPW, int L, class Sink, class Pre = NoPrefetch, class XF = NoNorm>
+__device__ __forceinline__ void valu_tile(const GemvArgs& a, int nb, int s, const Sink& sink, Pre&& pre = Pre(),
+                                          XF&& xf = XF()) {
+  constexpr bool kNorm = std::remove_reference_t<XF>::kOn;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nrow0 = nb * (4 * RPW) + wave * RPW;
   const int kb = s * (512 * L) + lane * 8;
   uint4 wv[RPW][L];
+  auto load_w = [&]() {
 #pragma unroll
-  for (int r = 0; r < RPW; ++r)
+    for (int r = 0; r < RPW; ++r)
 #pragma unroll
-    for (int j = 0; j < L; ++j) wv[r][j] = ld16(a.w + (int64_t)(nrow0 + r) * a.ldw + kb + j * 512);
+      for (int j = 0; j < L; ++j) wv[r][j] = ld16(a.w + (int64_t)(nrow0 + r) * a.ldw + kb + j * 512);
+  };
+  // W first, except behind the norm: there the activation chunks go first,
+  // so that (loads return in order) they can be normalised while W is still
+  // on its way.
+  if constexpr (!kNorm) load_w();
   // x rows past M read row M-1 (no branch between the loads, so they are all
   // in flight together); their sums are never stored.
   uint4 xv[MT][L];
@@ -77,7 +105,33 @@ __device__ __forceinline__ void valu_tile(const GemvArgs& a, int nb, int s, cons
   for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int j = 0; j < L; ++j) xv[m][j] = ld16(a.x + (int64_t)min(m, a.m - 1) * a.ldx + kb + j * 512);
+  [[maybe_unused]] uint4 rv[kNorm ? MT : 1][L], gv[L];
+  if constexpr (kNorm) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int j = 0; j < L; ++j) rv[m][j] = xf.res(min(m, a.m - 1), kb + j * 512);
+#pragma unroll
+    for (int j = 0; j < L; ++j) gv[j] = xf.gamma(kb + j * 512);
+    load_w();
+  }
   pre();
+  if constexpr (kNorm) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int j = 0; j < L; ++j) xv[m][j] = xf.residual(xv[m][j], rv[m][j]);
+    xf.row_work();
+    int rows[MT];
+    float rs[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) rows[m] = min(m, a.m - 1);
+    xf.rstd_rows(rows, rs);
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int j = 0; j < L; ++j) xv[m][j] = xf.apply(xv[m][j], gv[j], rs[m]);
+  }
   float acc[RPW][MT];
 #pragma unroll
   for (int r = 0; r < RPW; ++r)
@@ -110,17 +164,22 @@ __device__ __forceinline__ void valu_tile(const GemvArgs& a, int nb, int s, cons
 // A lane l: x[row0 + l%16][k-run of group l/16]; B lane l: W[n0 + l%16][same k].
 // D lane l: rows 4*(l/16)+i (i < 4) of the 16x16 tile, column l%16.
 // ---------------------------------------------------------------------------
-template <int MT, int KS, class Sink, class Pre = NoPrefetch>
+template <int MT, int KS, class Sink, class Pre = NoPrefetch, class XF = NoNorm>
 __device__ __forceinline__ void mfma_tile(const GemvArgs& a, int mb, int nb, int s, float* lds, const Sink& sink,
-                                          Pre&& pre = Pre()) {
+                                          Pre&& pre = Pre(), XF&& xf = XF()) {
+  constexpr bool kNorm = std::remove_reference_t<XF>::kOn;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r16 = lane & 15, grp = lane >> 4;
   const int kslice = 4 * 32 * KS;
   const int krun = s * kslice + wave * (32 * KS) + grp * (8 * KS);
   const int n = nb * 16 + r16;
   uint4 bw[KS];
+  auto load_w = [&]() {
 #pragma unroll
-  for (int j = 0; j < KS; ++j) bw[j] = ld16(a.w + (int64_t)n * a.ldw + krun + 8 * j);
+    for (int j = 0; j < KS; ++j) bw[j] = ld16(a.w + (int64_t)n * a.ldw + krun + 8 * j);
+  };
+  // W first, except behind the norm (as in the VALU tile)
+  if constexpr (!kNorm) load_w();
   floatx4_t acc[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
@@ -134,7 +193,35 @@ __device__ __forceinline__ void mfma_tile(const GemvArgs& a, int mb, int nb, int
 #pragma unroll
     for (int j = 0; j < KS; ++j) xv[t][j] = ld16(a.x + (int64_t)m * a.ldx + krun + 8 * j);
   }
+  [[maybe_unused]] uint4 rv[kNorm ? MT : 1][KS], gv[KS];
+  if constexpr (kNorm) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const int m = min(row_base + t * 16 + r16, a.m - 1);
+#pragma unroll
+      for (int j = 0; j < KS; ++j) rv[t][j] = xf.res(m, krun + 8 * j);
+    }
+#pragma unroll
+    for (int j = 0; j < KS; ++j) gv[j] = xf.gamma(krun + 8 * j);
+    load_w();
+  }
   pre();
+  if constexpr (kNorm) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int j = 0; j < KS; ++j) xv[t][j] = xf.residual(xv[t][j], rv[t][j]);
+    xf.row_work();
+    int rows[MT];
+    float rs[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) rows[t] = min(row_base + t * 16 + r16, a.m - 1);
+    xf.rstd_rows(rows, rs);
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int j = 0; j < KS; ++j) xv[t][j] = xf.apply(xv[t][j], gv[j], rs[t]);
+  }
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const bool ok = row_base + t * 16 + r16 < a.m;

@@ -193,8 +193,10 @@ int chain_gemm_slices(int m, int n, int k) {
 // are the only state that must stay zero between calls).
 // ---------------------------------------------------------------------------
 struct Layout {
-  size_t ctl, ctr, part, logits, tpart, tids, pos, ghist, offws, trace, total;
+  size_t ctl, ctr, part, logits, tpart, tids, trs, pos, ghist, offws, trace, total;
 };
+
+int even_up(int v) { return (v + 1) & ~1; }
 
 int large_sort_groups(int P) { return (P + kLargeSortChunk - 1) / kLargeSortChunk; }
 
@@ -208,10 +210,14 @@ Layout make_layout(int m, int n, int k, int topk) {
   const int part_slices = std::max(p.s, wide_gemm(m, n) ? chain_gemm_slices(m, n, k) : 1);
   L.part = o; o = align_up(o + sizeof(float) * (size_t)part_slices * m * n, kAlign);
   L.logits = o; o = align_up(o + sizeof(float) * (size_t)m * n, kAlign);
-  L.tpart = L.tids = o;
+  L.tpart = L.tids = L.trs = o;
   if (m <= kFusedMaxM) {  // tagged hand-off words of the one-launch path
     L.tpart = o; o = align_up(o + sizeof(u64) * (size_t)p.s * m * n, kAlign);
-    L.tids = o; o = align_up(o + sizeof(u64) * (size_t)(P + 1), kAlign);
+    // the expert ids, then (behind the RMSNorm producer) the rows' rstd, each
+    // padded to whole 16-byte units (the pad words are written too)
+    L.tids = o;
+    L.trs = o + sizeof(u64) * (size_t)even_up(P);
+    o = align_up(L.trs + sizeof(u64) * (size_t)even_up(m), kAlign);
   }
   L.pos = o; o = align_up(o + sizeof(int32_t) * (size_t)P, kAlign);
   L.ghist = o;
@@ -400,14 +406,15 @@ int launch_sort_quant(const int32_t* ids, const uint16_t* x, int64_t ldx, int m,
 // ---------------------------------------------------------------------------
 // Fused launch (M <= 64).
 // ---------------------------------------------------------------------------
-// Small mode when one gather of every row fits the per-thread loads (and
-// while every wave has at most one row's gate to run: beyond that, one more
-// hand-off costs less than a second gate in series). Measured on MI355X: at N = 128 small mode wins up to M = 4; at N = 896
-// (top-16) it wins up to M = 2 and large mode beyond (M = 3, 4: 13.4, 13.8
-// -> 12.4, 12.5 us), where each participant's gates of many experts cost more
-// than the ids hand-off.
+// Small mode when one gather of every row fits the per-thread loads, every
+// wave has at most one row's gate to run, and a lane holds at most two
+// experts. Measured on MI355X (small vs large mode, us, M = 1 / 2 / 4, W
+// rotating through 8 copies): N = 128, K = 6144: 5.3 / 6.0 / 7.2 vs 6.6 /
+// 6.9 / 7.9; N = 256: 8.8 / 9.6 / 11.0 vs 8.4 / 8.6 / 9.7; N = 896, K = 3584,
+// top-16: 15.9 / 18.5 / 21.4 vs 11.4 / 11.7 / 12.5. With more experts every
+// participant's gate of the whole row costs more than the ids hand-off.
 bool fused_small(const Plan& p, int m, int n) {
-  return m <= (n > 256 ? 2 : 4) && gather_loads(m, n, p.s) <= kPollLoads;
+  return m <= 4 && n <= 128 && gather_loads(m, n, p.s) <= kPollLoads;
 }
 
 size_t fused_lds_bytes(const Plan& p, int m, int n, int topk, bool small) {
@@ -423,7 +430,16 @@ size_t fused_lds_bytes(const Plan& p, int m, int n, int topk, bool small) {
   return std::max(tail, tile);
 }
 
-const void* fused_kernel_for(const Plan& p, int n) {
+const void* fused_kernel_for(const Plan& p, int n, bool norm) {
+  if (norm) {
+    switch (nv_bucket(n)) {
+      case 2: return fused_norm_pick_nv2(p.valu, p.mt, p.l, p.ks);
+      case 4: return fused_norm_pick_nv4(p.valu, p.mt, p.l, p.ks);
+      case 8: return fused_norm_pick_nv8(p.valu, p.mt, p.l, p.ks);
+      case 14: return fused_norm_pick_nv14(p.valu, p.mt, p.l, p.ks);
+      default: return fused_norm_pick_nv16(p.valu, p.mt, p.l, p.ks);
+    }
+  }
   switch (nv_bucket(n)) {
     case 2: return fused_pick_nv2(p.valu, p.mt, p.l, p.ks);
     case 4: return fused_pick_nv4(p.valu, p.mt, p.l, p.ks);
@@ -621,10 +637,9 @@ rgt_status rgt_topk_gate_partials(const float* part, int s, const float* bias, i
   return launched();
 }
 
-rgt_status rgt_rmsnorm(const void* x, int64_t ldx, const void* residual, int64_t ldr, const void* gamma, float eps,
-                       int m, int k, void* xn, int64_t ldxn, void* residual_out, int64_t ldro, float* rstd,
-                       hipStream_t stream) {
-  g_last_launches = 0;
+static rgt_status check_norm_args(const void* x, int64_t ldx, const void* residual, int64_t ldr, const void* gamma,
+                                  float eps, int m, int k, const void* xn, int64_t ldxn, const void* residual_out,
+                                  int64_t ldro, const float* rstd) {
   if (m < 0 || m > 65535 || k < 8 || k > 16384 || k % 8) return RGT_ERR_UNSUPPORTED;
   if (m == 0) return RGT_OK;
   if (!x || !gamma || !xn || !aligned(x, 16) || !aligned(gamma, 16) || !aligned(xn, 16)) return RGT_ERR_INVALID;
@@ -632,17 +647,29 @@ rgt_status rgt_rmsnorm(const void* x, int64_t ldx, const void* residual, int64_t
   if (residual && (!aligned(residual, 16) || ldr < k || ldr % 8)) return RGT_ERR_INVALID;
   if (residual_out && (!residual || !aligned(residual_out, 16) || ldro < k || ldro % 8)) return RGT_ERR_INVALID;
   if (rstd && !aligned(rstd, 4)) return RGT_ERR_INVALID;
+  return RGT_OK;
+}
+
+static void launch_rmsnorm(const uint16_t* xs, int64_t ldx, const uint16_t* rs, int64_t ldr, const uint16_t* gs,
+                           float eps, int m, int k, uint16_t* xo, int64_t ldxn, uint16_t* ro, int64_t ldro, float* rstd,
+                           hipStream_t stream) {
   const int ch = (k + 2047) / 2048;  // 8-element chunks per thread
-  const auto* xs = static_cast<const uint16_t*>(x);
-  const auto* rs = static_cast<const uint16_t*>(residual);
-  const auto* gs = static_cast<const uint16_t*>(gamma);
-  auto* xo = static_cast<uint16_t*>(xn);
-  auto* ro = static_cast<uint16_t*>(residual_out);
   const dim3 grid(m), blk(256);
   if (ch <= 1) hipLaunchKernelGGL(rmsnorm_kernel<1>, grid, blk, 0, stream, xs, ldx, rs, ldr, gs, eps, k, xo, ldxn, ro, ldro, rstd);
   else if (ch <= 2) hipLaunchKernelGGL(rmsnorm_kernel<2>, grid, blk, 0, stream, xs, ldx, rs, ldr, gs, eps, k, xo, ldxn, ro, ldro, rstd);
   else if (ch <= 4) hipLaunchKernelGGL(rmsnorm_kernel<4>, grid, blk, 0, stream, xs, ldx, rs, ldr, gs, eps, k, xo, ldxn, ro, ldro, rstd);
   else hipLaunchKernelGGL(rmsnorm_kernel<8>, grid, blk, 0, stream, xs, ldx, rs, ldr, gs, eps, k, xo, ldxn, ro, ldro, rstd);
+}
+
+rgt_status rgt_rmsnorm(const void* x, int64_t ldx, const void* residual, int64_t ldr, const void* gamma, float eps,
+                       int m, int k, void* xn, int64_t ldxn, void* residual_out, int64_t ldro, float* rstd,
+                       hipStream_t stream) {
+  g_last_launches = 0;
+  const rgt_status st = check_norm_args(x, ldx, residual, ldr, gamma, eps, m, k, xn, ldxn, residual_out, ldro, rstd);
+  if (st != RGT_OK || m == 0) return st;
+  launch_rmsnorm(static_cast<const uint16_t*>(x), ldx, static_cast<const uint16_t*>(residual), ldr,
+                 static_cast<const uint16_t*>(gamma), eps, m, k, static_cast<uint16_t*>(xn), ldxn,
+                 static_cast<uint16_t*>(residual_out), ldro, rstd, stream);
   g_last_launches = 1;
   return launched();
 }
@@ -720,16 +747,33 @@ rgt_status rgt_moe_sort_quant_mxfp4(const int32_t* topk_ids, const void* x, int6
                              true, ws, ws_bytes, stream);
 }
 
+// The RMSNorm producer in front of the router: x is the raw input; xn, h and
+// rstd are written as rgt_rmsnorm writes them, and the router reads xn.
+struct NormIn {
+  const uint16_t* res;
+  int64_t ldr;
+  const uint16_t* gamma;
+  float eps;
+  uint16_t* xn;
+  int64_t ldxn;
+  uint16_t* res_out;
+  int64_t ldro;
+  float* rstd;
+};
+
 static rgt_status route_sort_quant_impl(const void* x, int64_t ldx, const void* w, int64_t ldw, const float* bias,
                                         int m, int n, int k, int topk, int block, float* logits, int32_t* topk_ids,
                                         float* topk_w, int32_t* sorted_ids, int32_t* expert_ids, int32_t* offsets,
                                         uint8_t* a_q, uint8_t* a_scale, bool fp4, void* ws, size_t ws_bytes,
-                                        hipStream_t stream) {
+                                        hipStream_t stream, const NormIn* nrm = nullptr) {
   g_last_launches = 0;
   rgt_status st = check_gemv_args(x, ldx, w, ldw, m, n, k);
   if (st != RGT_OK) return st;
   st = check_sort_args(x, ldx, m, n, k, topk, block, sorted_ids, expert_ids, offsets, a_q, a_scale);
   if (st != RGT_OK || m == 0) return st;
+  if (nrm && (st = check_norm_args(x, ldx, nrm->res, nrm->ldr, nrm->gamma, nrm->eps, m, k, nrm->xn, nrm->ldxn,
+                                   nrm->res_out, nrm->ldro, nrm->rstd)) != RGT_OK)
+    return st;
   if (!topk_ids || !topk_w || !aligned(topk_ids, 4) || !aligned(topk_w, 4)) return RGT_ERR_INVALID;
   if ((logits && !aligned(logits, 4)) || (bias && !aligned(bias, 4))) return RGT_ERR_INVALID;
   const Layout L = make_layout(m, n, k, topk);
@@ -742,6 +786,32 @@ static rgt_status route_sort_quant_impl(const void* x, int64_t ldx, const void* 
              reinterpret_cast<float*>(base + L.part), reinterpret_cast<u32*>(base + L.ctr), m, n, k, p.s, p.nb};
 
   bool fuse = m <= kFusedMaxM && !env_int("RGT_NO_FUSE", 0);
+  // Behind the norm: inside the launch the first M workgroups are the rows'
+  // norm workgroups and hold a row in registers (kNormChunks 8-element chunks
+  // a thread); otherwise the norm's own launch comes first and the route
+  // reads its xn. By default the norm joins the launch for one row only:
+  // there every workgroup takes the row's rstd itself, measured faster than
+  // the two launches (7.5 vs 8.4 us at N = 128, K = 6144); with more rows the
+  // tiles of every n-block normalise the same columns again and wait for the
+  // published rstd, measured slower than the norm's own launch (M = 2..64:
+  // +0.4..+2.7 us). RGT_NORM_IN_LAUNCH = 1 takes the one launch whenever it
+  // fits, 0 never.
+  const long norm_pref = env_int("RGT_NORM_IN_LAUNCH", -1);
+  bool norm_in = nrm && fuse && m <= p.grid && k <= 2048 * kNormChunks &&
+                 (norm_pref > 0 || (norm_pref < 0 && m == 1));
+  int n_norm = 0;
+  auto norm_first = [&]() {
+    norm_in = false;
+    if (!nrm || n_norm) return;
+    launch_rmsnorm(g.x, ldx, nrm->res, nrm->ldr, nrm->gamma, nrm->eps, m, k, nrm->xn, nrm->ldxn, nrm->res_out,
+                   nrm->ldro, nrm->rstd, stream);
+    n_norm = 1;
+    g.x = nrm->xn;
+    g.ldx = nrm->ldxn;
+    x = nrm->xn;
+    ldx = nrm->ldxn;
+  };
+  if (!norm_in) norm_first();
   const bool small = fused_small(p, m, n);
   int upw_log = 8;
   const void* fn = nullptr;
@@ -749,7 +819,7 @@ static rgt_status route_sort_quant_impl(const void* x, int64_t ldx, const void* 
   if (fuse) {
     DevInfo di;
     if (!dev_info(di)) return RGT_ERR_HIP;
-    fn = fused_kernel_for(p, n);
+    fn = fused_kernel_for(p, n, norm_in);
     lds = fused_lds_bytes(p, m, n, topk, small);
     const int units = m * (k / 16);
     // A workgroup's quant units cover at most this many tokens; their pairs
@@ -785,7 +855,14 @@ static rgt_status route_sort_quant_impl(const void* x, int64_t ldx, const void* 
 #else
     const size_t scrub_end = ws_bytes / 16 * 16;
 #endif
-    const u32 part0 = (u32)((L.tpart - L.part) / 16), ids0 = (u32)((L.tids - L.part) / 16);
+    // This call's footprint: the words it writes with its tag, all of them
+    // (the scrub leaves them alone; a word in the footprint left unwritten
+    // would keep an old tag for good): the partials; in large mode the
+    // expert ids; behind the norm the rstd words (contiguous with the ids;
+    // none with one row, whose rstd every workgroup takes itself).
+    const u32 part0 = (u32)((L.tpart - L.part) / 16);
+    const u32 ids0 = (u32)(((small ? L.trs : L.tids) - L.part) / 16);
+    const u32 ids1 = (u32)((L.trs - L.part) / 16) + (norm_in && m > 1 ? (u32)(even_up(m) / 2) : 0u);
     FusedArgs a{g, bias, topk, block, small ? 1 : 0, fp4 ? 1 : 0, upw_log, cpr_magic, logits, topk_ids, topk_w, sorted_ids, expert_ids, offsets,
                 a_q, a_scale, reinterpret_cast<u32*>(base + L.ctl), reinterpret_cast<u64*>(base + L.tpart),
                 reinterpret_cast<u64*>(base + L.tids), wait_budget_ticks(), env_int("RGT_FAULT_INJECT", 0),
@@ -796,12 +873,25 @@ static rgt_status route_sort_quant_impl(const void* x, int64_t ldx, const void* 
 #endif
                 reinterpret_cast<u64*>(base + L.part), (u32)((scrub_end - L.part) / 16),
                 part0, part0 + (u32)(((size_t)p.s * m * n * 8 + 15) / 16),
-                ids0, ids0 + (u32)(((size_t)(m * topk + 1) * 8 + 15) / 16)};
+                ids0, std::max(ids0, ids1)};
+    if (norm_in) {
+      a.res = nrm->res;
+      a.ldr = nrm->ldr;
+      a.gamma = nrm->gamma;
+      a.eps = nrm->eps;
+      a.xn = nrm->xn;
+      a.ldxn = nrm->ldxn;
+      a.res_out = nrm->res_out;
+      a.ldro = nrm->ldro;
+      a.rstd_out = nrm->rstd;
+      a.trs = reinterpret_cast<u64*>(base + L.trs);
+    }
     void* args[] = {&a};
     if (hipLaunchKernel(fn, dim3(p.grid), dim3(256), args, lds, stream) != hipSuccess) return RGT_ERR_HIP;
-    g_last_launches = 1;
+    g_last_launches = n_norm + 1;
     return launched();
   }
+  norm_first();  // the one-launch form did not fit: the norm's launch, then the chain
   if (wide_gemm(m, n)) {
     // Wide batch: the router GEMM writes k-slice partials, the gate sums them
     // in slice order and writes the logits.
@@ -816,7 +906,7 @@ static rgt_status route_sort_quant_impl(const void* x, int64_t ldx, const void* 
   const int nl = launch_sort_quant(topk_ids, static_cast<const uint16_t*>(x), ldx, m, n, k, topk, block, sorted_ids,
                                    expert_ids, offsets, a_q, a_scale, fp4, base, L, stream);
   if (nl < 0) return RGT_ERR_HIP;
-  g_last_launches = 2 + nl;
+  g_last_launches = n_norm + 2 + nl;
   return launched();
 }
 
@@ -835,6 +925,43 @@ rgt_status rgt_route_sort_quant_mxfp4(const void* x, int64_t ldx, const void* w,
                                       hipStream_t stream) {
   return route_sort_quant_impl(x, ldx, w, ldw, bias, m, n, k, topk, block, logits, topk_ids, topk_w, sorted_ids,
                                expert_ids, offsets, a_q, a_scale, true, ws, ws_bytes, stream);
+}
+
+static rgt_status rmsnorm_route_impl(const void* x, int64_t ldx, const void* residual, int64_t ldr,
+                                     const void* gamma, float eps, const void* w, int64_t ldw, const float* bias,
+                                     int m, int n, int k, int topk, int block, void* xn, int64_t ldxn,
+                                     void* residual_out, int64_t ldro, float* rstd, float* logits, int32_t* topk_ids,
+                                     float* topk_w, int32_t* sorted_ids, int32_t* expert_ids, int32_t* offsets,
+                                     uint8_t* a_q, uint8_t* a_scale, bool fp4, void* ws, size_t ws_bytes,
+                                     hipStream_t stream) {
+  const NormIn nrm{static_cast<const uint16_t*>(residual), ldr, static_cast<const uint16_t*>(gamma), eps,
+                   static_cast<uint16_t*>(xn), ldxn, static_cast<uint16_t*>(residual_out), ldro, rstd};
+  return route_sort_quant_impl(x, ldx, w, ldw, bias, m, n, k, topk, block, logits, topk_ids, topk_w, sorted_ids,
+                               expert_ids, offsets, a_q, a_scale, fp4, ws, ws_bytes, stream, &nrm);
+}
+
+rgt_status rgt_rmsnorm_route_sort_quant(const void* x, int64_t ldx, const void* residual, int64_t ldr,
+                                        const void* gamma, float eps, const void* w, int64_t ldw, const float* bias,
+                                        int m, int n, int k, int topk, int block, void* xn, int64_t ldxn,
+                                        void* residual_out, int64_t ldro, float* rstd, float* logits,
+                                        int32_t* topk_ids, float* topk_w, int32_t* sorted_ids, int32_t* expert_ids,
+                                        int32_t* offsets, uint8_t* a_q, uint8_t* a_scale, void* ws, size_t ws_bytes,
+                                        hipStream_t stream) {
+  return rmsnorm_route_impl(x, ldx, residual, ldr, gamma, eps, w, ldw, bias, m, n, k, topk, block, xn, ldxn,
+                            residual_out, ldro, rstd, logits, topk_ids, topk_w, sorted_ids, expert_ids, offsets, a_q,
+                            a_scale, false, ws, ws_bytes, stream);
+}
+
+rgt_status rgt_rmsnorm_route_sort_quant_mxfp4(const void* x, int64_t ldx, const void* residual, int64_t ldr,
+                                              const void* gamma, float eps, const void* w, int64_t ldw,
+                                              const float* bias, int m, int n, int k, int topk, int block, void* xn,
+                                              int64_t ldxn, void* residual_out, int64_t ldro, float* rstd,
+                                              float* logits, int32_t* topk_ids, float* topk_w, int32_t* sorted_ids,
+                                              int32_t* expert_ids, int32_t* offsets, uint8_t* a_q, uint8_t* a_scale,
+                                              void* ws, size_t ws_bytes, hipStream_t stream) {
+  return rmsnorm_route_impl(x, ldx, residual, ldr, gamma, eps, w, ldw, bias, m, n, k, topk, block, xn, ldxn,
+                            residual_out, ldro, rstd, logits, topk_ids, topk_w, sorted_ids, expert_ids, offsets, a_q,
+                            a_scale, true, ws, ws_bytes, stream);
 }
 
 rgt_status rgt_route_sort_quant_noalloc(const void* x, int64_t ldx, const void* w, int64_t ldw, const float* bias,

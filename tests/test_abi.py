@@ -173,6 +173,28 @@ def test_rmsnorm_argument_errors(L):
     assert call(rstd=FAKE + 1) == 2
 
 
+@pytest.mark.parametrize("entry", ["rgt_rmsnorm_route_sort_quant", "rgt_rmsnorm_route_sort_quant_mxfp4"])
+def test_rmsnorm_route_sort_quant_argument_errors(L, entry):
+    """Both calls' argument rules apply, checked before any launch."""
+    f = getattr(L, entry)
+
+    def call(x=FAKE, r=None, ldr=0, g=FAKE, eps=1e-6, m=4, n=128, k=6144, topk=8, block=16, xn=FAKE, ldxn=6144,
+             ro=None, ldro=0, rstd=None, tw=FAKE, wsb=1 << 30):
+        return f(x, k, r, ldr, g, eps, FAKE, k, None, m, n, k, topk, block, xn, ldxn, ro, ldro, rstd, None, FAKE,
+                 tw, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wsb, None)
+
+    assert call(m=0) == 0
+    assert call(n=100) == 1 and call(block=128) == 1
+    assert call(tw=None) == 2
+    assert call(g=None) == 2 and call(g=FAKE + 2) == 2
+    assert call(xn=None) == 2 and call(xn=FAKE + 8) == 2 and call(ldxn=6146) == 2
+    assert call(eps=-1.0) == 2
+    assert call(ro=FAKE, ldro=6144) == 2          # residual_out without a residual
+    assert call(r=FAKE, ldr=6100) == 2
+    assert call(rstd=FAKE + 1) == 2
+    assert call(wsb=256) == 3
+
+
 def test_router_shared_swiglu_argument_errors(L):
     S = L.rgt_router_partial_slices
     # VALU plan at M = 4 (three slices of 2048), MFMA plan at M = 16 (twelve of 512)
