@@ -347,6 +347,25 @@ rgt_status rgt_rmsnorm_route_sort_quant_mxfp4(const void* x, int64_t ldx, const 
                                               int32_t* expert_ids, int32_t* offsets, uint8_t* a_q, uint8_t* a_scale,
                                               void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Settings are read from the environment at the first call of the process
+ * and again by this call, never on the call path (so a call costs no
+ * getenv); call it after changing them, with no call of the library in
+ * flight on any thread:
+ *   RGT_WAIT_BUDGET_US  deadline of each device-side wait, in us (100000)
+ *   RGT_NO_FUSE=1       never the one-launch form of the route calls
+ *   RGT_NORM_IN_LAUNCH  1: the norm joins the route's launch whenever it
+ *                       fits, 0: never (default: at M = 1)
+ *   RGT_FORCE_BUCKET    comma-separated, for experiments and tests: valu or
+ *                       mfma (the router tile; valu only up to M = 8), small
+ *                       or large (the one-launch form's mode); a workspace
+ *                       must be sized under the same setting
+ *   RGT_LOG=1           one line on stderr per new shape with the plan taken
+ *   RGT_FAULT_INJECT=1  host-forced fault for tests: no tagged word is
+ *                       published, so every device-side wait runs into its
+ *                       deadline
+ * Settings apply to every device. */
+void rgt_reload_env(void);
+
 /* Number of kernel launches the last successful call of each entry point made
  * on this thread (diagnostics for launch-count checks). */
 int rgt_last_launch_count(void);

@@ -12,7 +12,7 @@ _API = (
     "route_sort_quant_mxfp4", "route_sort_quant_noalloc", "rmsnorm_route_sort_quant", "moe_stage1_swiglu", "Workspace",
     "workspace_bytes", "sort_capacity", "router_supported", "reset_workspace", "check_workspace",
     "status_string", "last_launch_count", "alloc_sort_outputs", "RgtError", "RgtUnsupported", "lib",
-    "exported_symbols", "version", "diag_read", "diag_copy",
+    "exported_symbols", "version", "diag_read", "diag_copy", "reload_env",
 )
 
 

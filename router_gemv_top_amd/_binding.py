@@ -77,6 +77,7 @@ def lib() -> ctypes.CDLL:
             "rgt_moe_stage1_swiglu": ([vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, i32, vp, i64, vp], i32),
             "rgt_router_shared_swiglu": ([vp, i64, vp, i64, i32, i32, i32, vp, i32, vp, vp, i32, vp, i64, vp], i32),
             "rgt_rmsnorm": ([vp, i64, vp, i64, vp, ctypes.c_float, i32, i32, vp, i64, vp, i64, vp, vp], i32),
+            "rgt_reload_env": ([], None),
             "rgt_rmsnorm_route_sort_quant": ([vp, i64, vp, i64, vp, ctypes.c_float, vp, i64, vp, i32, i32, i32, i32,
                                               i32, vp, i64, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                               ctypes.c_size_t, vp], i32),
@@ -423,6 +424,12 @@ def rmsnorm_route_sort_quant(x, gamma, eps: float, w, topk: int, block: int, ws:
               _ptr(out["offsets"]), _ptr(out["a_q"]), _ptr(out["a_scale"]), _ptr(ws.buf), ws.nbytes,
               _stream(stream)), fn.__name__[4:])
     return out
+
+
+def reload_env():
+    """Re-read the RGT_* environment settings (the library reads them at its
+    first call and here only)."""
+    lib().rgt_reload_env()
 
 
 def diag_read(src, sink, grid: int, nbytes: int | None = None, stream=None):

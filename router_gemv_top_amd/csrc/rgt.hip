@@ -52,6 +52,64 @@ int env_int(const char* name, int dflt) {
   return v && *v ? std::atoi(v) : dflt;
 }
 
+// Environment settings, read at the first call and again by rgt_reload_env
+// (so that no call pays for getenv):
+//   RGT_WAIT_BUDGET_US  deadline of each device-side wait (default 100000)
+//   RGT_NO_FUSE=1       never the one-launch form
+//   RGT_NORM_IN_LAUNCH  1: the norm joins the launch whenever it fits, 0: never
+//   RGT_FORCE_BUCKET    comma-separated: valu | mfma (router tile, M <= 8 for
+//                       valu), small | large (the one-launch tail's mode)
+//   RGT_LOG=1           one stderr line per new shape with the plan chosen
+//   RGT_FAULT_INJECT=1  host-forced fault: nothing is published (tests)
+enum { kForceNone = 0, kForceValu = 1, kForceMfma = 2 };
+enum { kModeAuto = 0, kModeSmall = 1, kModeLarge = 2 };
+struct Config {
+  long wait_budget_us = 100000;
+  int no_fuse = 0;
+  int norm_in_launch = -1;
+  int force_tile = kForceNone;
+  int force_mode = kModeAuto;
+  int log = 0;
+  int fault_inject = 0;
+  unsigned gen = 0;  // bumped by every reload (plan cache key)
+};
+Config g_cfg;
+std::once_flag g_cfg_once;
+std::mutex g_cfg_mu;
+
+void load_config() {
+  Config c;
+  c.wait_budget_us = env_int("RGT_WAIT_BUDGET_US", 100000);
+  c.no_fuse = env_int("RGT_NO_FUSE", 0);
+  c.norm_in_launch = env_int("RGT_NORM_IN_LAUNCH", -1);
+  c.log = env_int("RGT_LOG", 0);
+  c.fault_inject = env_int("RGT_FAULT_INJECT", 0);
+  if (const char* f = std::getenv("RGT_FORCE_BUCKET")) {
+    const char* q = f;
+    while (*q) {
+      const char* e = q;
+      while (*e && *e != ',') ++e;
+      const size_t len = (size_t)(e - q);
+      auto is = [&](const char* w) { return std::strlen(w) == len && std::strncmp(q, w, len) == 0; };
+      if (is("valu")) c.force_tile = kForceValu;
+      else if (is("mfma")) c.force_tile = kForceMfma;
+      else if (is("small")) c.force_mode = kModeSmall;
+      else if (is("large")) c.force_mode = kModeLarge;
+      q = *e ? e + 1 : e;
+    }
+  }
+  c.gen = g_cfg.gen + 1;
+  g_cfg = c;
+}
+
+const Config& config() {
+  std::call_once(g_cfg_once, [] {
+    std::lock_guard<std::mutex> lk(g_cfg_mu);
+    load_config();
+  });
+  return g_cfg;
+}
+
 bool covered(int m, int n, int k) {
   return m >= 0 && m <= 8192 && n >= 16 && n <= 1024 && n % 16 == 0 && k >= 512 && k % 512 == 0;
 }
@@ -115,7 +173,8 @@ Plan make_plan(int m, int n, int k) {
     p.grid = p.mb * p.nb;
     return p;
   }
-  if (m <= 8) {
+  const int force = config().force_tile;
+  if (m <= 8 && force != kForceMfma) {
     p.valu = true;
     p.mt = pow2_at_least(std::max(m, 1));
     p.rpw = 1;
@@ -256,10 +315,8 @@ bool dev_info(DevInfo& out) {
   return true;
 }
 
-// Read at every call, so a process can change it between calls.
 u64 wait_budget_ticks() {
-  const long us = env_int("RGT_WAIT_BUDGET_US", 100000);  // 100 ms default
-  return (u64)std::max(1L, us) * 100ull;                   // 100 MHz clock
+  return (u64)std::max(1L, config().wait_budget_us) * 100ull;  // 100 MHz clock
 }
 
 rgt_status launched() {
@@ -361,6 +418,8 @@ void launch_gate_partials(const float* part, int S, float* logits, const float* 
 
 // Sort + quant as separate launches. Returns the number of launches, or -1
 // if the sort's LDS allowance could not be set (nothing launched).
+bool wave_sort_fits(int P, int n) { return P <= std::min(kWaveSortMaxP, std::max(128, 5 * n / 8)); }
+
 int launch_sort_quant(const int32_t* ids, const uint16_t* x, int64_t ldx, int m, int n, int k, int topk, int block,
                       int32_t* sorted_ids, int32_t* expert_ids, int32_t* offsets, uint8_t* a_q, uint8_t* a_scale,
                       bool fp4, char* ws, const Layout& L, hipStream_t st) {
@@ -368,7 +427,11 @@ int launch_sort_quant(const int32_t* ids, const uint16_t* x, int64_t ldx, int m,
   int32_t* pos = reinterpret_cast<int32_t*>(ws + L.pos);
   int launches = 0;
   if (P <= kSmallSortMaxP) {
-    const int threads = P <= kWaveSortMaxP ? 256 : 1024;
+    // One wave sorts up to max(128, 5N/8) pairs, every wave above. Measured
+    // (sort + quant, us, one wave vs sixteen): N = 128: P = 128: 8.4 / 8.5,
+    // P = 256: 9.9 / 8.8, P = 512: 12.6 / 8.9; N = 896: P = 512: 15.2 / 16.5,
+    // P = 1024: 17.1 / 17.1. The sixteen waves' per-expert scans grow with N.
+    const int threads = wave_sort_fits(P, n) ? 256 : 1024;
     const size_t lds =
         sizeof(int) * ((size_t)P + std::max<size_t>(P, (size_t)(threads / 64) * n) + n + (n + 1) + threads);
     // Above 64 KB of dynamic LDS the kernel must be allowed more: the largest
@@ -414,7 +477,9 @@ int launch_sort_quant(const int32_t* ids, const uint16_t* x, int64_t ldx, int m,
 // top-16: 15.9 / 18.5 / 21.4 vs 11.4 / 11.7 / 12.5. With more experts every
 // participant's gate of the whole row costs more than the ids hand-off.
 bool fused_small(const Plan& p, int m, int n) {
-  return m <= 4 && n <= 128 && gather_loads(m, n, p.s) <= kPollLoads;
+  const int mode = config().force_mode;
+  if (mode == kModeLarge) return false;
+  return m <= 4 && (n <= 128 || mode == kModeSmall) && gather_loads(m, n, p.s) <= kPollLoads;
 }
 
 size_t fused_lds_bytes(const Plan& p, int m, int n, int topk, bool small) {
@@ -661,6 +726,12 @@ static void launch_rmsnorm(const uint16_t* xs, int64_t ldx, const uint16_t* rs, 
   else hipLaunchKernelGGL(rmsnorm_kernel<8>, grid, blk, 0, stream, xs, ldx, rs, ldr, gs, eps, k, xo, ldxn, ro, ldro, rstd);
 }
 
+void rgt_reload_env(void) {
+  config();
+  std::lock_guard<std::mutex> lk(g_cfg_mu);
+  load_config();
+}
+
 rgt_status rgt_rmsnorm(const void* x, int64_t ldx, const void* residual, int64_t ldr, const void* gamma, float eps,
                        int m, int k, void* xn, int64_t ldxn, void* residual_out, int64_t ldro, float* rstd,
                        hipStream_t stream) {
@@ -747,6 +818,110 @@ rgt_status rgt_moe_sort_quant_mxfp4(const int32_t* topk_ids, const void* x, int6
                              true, ws, ws_bytes, stream);
 }
 
+// Everything a route call decides from its shape, computed once per (device,
+// M, N, K, top-k, norm in the launch, settings) and kept: the plan, the
+// workspace layout and, for the one-launch form, the kernel, its LDS, the
+// tail's mode and quant units per workgroup, and whether it fits at all
+// (co-residency, per-thread loads, quant units, wave-sized pair lists).
+struct ShapeEntry {
+  int dev, m, n, k, topk;
+  bool want_norm;
+  unsigned gen;
+  Plan p;
+  Layout L;
+  bool fuse, norm_in, small;
+  int upw_log;
+  const void* fn;
+  size_t lds;
+};
+constexpr int kShapeCache = 1024;
+static ShapeEntry g_shapes[kShapeCache];
+static int g_shapes_n = 0;
+
+static ShapeEntry compute_shape(int dev, int m, int n, int k, int topk, bool want_norm) {
+  const Config& cfg = config();
+  ShapeEntry e{};
+  e.dev = dev, e.m = m, e.n = n, e.k = k, e.topk = topk, e.want_norm = want_norm, e.gen = cfg.gen;
+  e.p = make_plan(m, n, k);
+  e.L = make_layout(m, n, k, topk);
+  const Plan& p = e.p;
+  e.fuse = m <= kFusedMaxM && !cfg.no_fuse;
+  e.norm_in = want_norm && e.fuse && m <= p.grid;
+  e.small = fused_small(p, m, n);
+  e.upw_log = 8;
+  if (e.fuse) {
+    DevInfo di;
+    if (!dev_info(di)) {
+      e.fuse = e.norm_in = false;
+      return e;
+    }
+    e.fn = fused_kernel_for(p, n, e.norm_in);
+    e.lds = fused_lds_bytes(p, m, n, topk, e.small);
+    const int units = m * (k / 16);
+    // A workgroup's quant units cover at most this many tokens; their pairs
+    // must fit one wave.
+    const int cpr = k / 16;
+    auto pairs_fit_at = [&](int ul) {
+      return (((1 << ul) - 1) / cpr + 2) * topk <= 64 &&
+             (uint64_t)(p.grid << ul) * (uint64_t)cpr < (1ull << 32);  // exact magic division
+    };
+    if (e.small) {
+      // the fewest units per workgroup that cover every unit
+      e.upw_log = 6;
+      while (e.upw_log < 8 && ((units + (1 << e.upw_log) - 1) >> e.upw_log) > p.grid) ++e.upw_log;
+    } else {
+      // large mode: the most units per workgroup whose pairs fit one wave
+      // (fewer, fuller quant workgroups; measured faster at M >= 16)
+      while (e.upw_log > 6 && !pairs_fit_at(e.upw_log) && units <= (p.grid << (e.upw_log - 1))) --e.upw_log;
+    }
+    // Co-residency is required for the device-side waits; each thread owns at
+    // most one quant unit; in large mode workgroup r gathers row r.
+    if (p.grid > coresident_blocks(e.fn, e.lds, di.cus) || units > (p.grid << e.upw_log) ||
+        !pairs_fit_at(e.upw_log) || (!e.small && (m > p.grid || gather_loads(1, n, p.s) > kPollLoads)))
+      e.fuse = false;
+  }
+  if (!e.fuse) e.norm_in = false;
+  if (cfg.log) {
+    if (e.fuse)
+      std::fprintf(stderr,
+                   "rgt: route M=%d N=%d K=%d top-%d%s: one launch, %s tile (mt %d, %s %d), %d k-slices, grid %d, "
+                   "%s mode, %d quant units a workgroup\n",
+                   m, n, k, topk, want_norm ? (e.norm_in ? " behind the norm" : " (norm launch first)") : "",
+                   p.valu ? "VALU" : "MFMA", p.mt, p.valu ? "l" : "ks", p.valu ? p.l : p.ks, p.s, p.grid,
+                   e.small ? "small" : "large", 1 << e.upw_log);
+    else
+      std::fprintf(stderr, "rgt: route M=%d N=%d K=%d top-%d%s: launch chain (%s)\n", m, n, k, topk,
+                   want_norm ? " (norm launch first)" : "", wide_gemm(m, n) ? "GEMM" : p.valu ? "VALU tile" : "MFMA tile");
+  }
+  return e;
+}
+
+// The cached entry (entries are never changed once in the table), or one
+// held in a thread-local slot when the table is full.
+static const ShapeEntry* shape_entry(int m, int n, int k, int topk, bool want_norm) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;  // no device: no one-launch form (argument checks still run)
+  const unsigned gen = config().gen;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    for (int i = 0; i < g_shapes_n; ++i) {
+      const ShapeEntry& e = g_shapes[i];
+      if (e.m == m && e.n == n && e.k == k && e.topk == topk && e.want_norm == want_norm && e.dev == dev &&
+          e.gen == gen)
+        return &e;
+    }
+  }
+  const ShapeEntry e = compute_shape(dev, m, n, k, topk, want_norm);
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (g_shapes_n < kShapeCache) {
+    g_shapes[g_shapes_n] = e;
+    return &g_shapes[g_shapes_n++];
+  }
+  thread_local ShapeEntry spill;
+  spill = e;
+  return &spill;
+}
+
 // The RMSNorm producer in front of the router: x is the raw input; xn, h and
 // rstd are written as rgt_rmsnorm writes them, and the router reads xn.
 struct NormIn {
@@ -776,16 +951,7 @@ static rgt_status route_sort_quant_impl(const void* x, int64_t ldx, const void* 
     return st;
   if (!topk_ids || !topk_w || !aligned(topk_ids, 4) || !aligned(topk_w, 4)) return RGT_ERR_INVALID;
   if ((logits && !aligned(logits, 4)) || (bias && !aligned(bias, 4))) return RGT_ERR_INVALID;
-  const Layout L = make_layout(m, n, k, topk);
-  if ((st = check_ws(ws, ws_bytes, L.total)) != RGT_OK) return st;
-  const Plan p = make_plan(m, n, k);
-  if (p.mb * p.nb > kMaxTileCounters) return RGT_ERR_UNSUPPORTED;
-  char* base = static_cast<char*>(ws);
-  float* lg = logits ? logits : reinterpret_cast<float*>(base + L.logits);
-  GemvArgs g{static_cast<const u16*>(x), ldx, static_cast<const u16*>(w), ldw, lg,
-             reinterpret_cast<float*>(base + L.part), reinterpret_cast<u32*>(base + L.ctr), m, n, k, p.s, p.nb};
-
-  bool fuse = m <= kFusedMaxM && !env_int("RGT_NO_FUSE", 0);
+  const Config& cfg = config();
   // Behind the norm: inside the launch the first M workgroups are the rows'
   // norm workgroups and hold a row in registers (kNormChunks 8-element chunks
   // a thread); otherwise the norm's own launch comes first and the route
@@ -796,9 +962,20 @@ static rgt_status route_sort_quant_impl(const void* x, int64_t ldx, const void* 
   // published rstd, measured slower than the norm's own launch (M = 2..64:
   // +0.4..+2.7 us). RGT_NORM_IN_LAUNCH = 1 takes the one launch whenever it
   // fits, 0 never.
-  const long norm_pref = env_int("RGT_NORM_IN_LAUNCH", -1);
-  bool norm_in = nrm && fuse && m <= p.grid && k <= 2048 * kNormChunks &&
-                 (norm_pref > 0 || (norm_pref < 0 && m == 1));
+  const bool want_norm = nrm && m <= kFusedMaxM && !cfg.no_fuse && k <= 2048 * kNormChunks &&
+                         (cfg.norm_in_launch > 0 || (cfg.norm_in_launch < 0 && m == 1));
+  const ShapeEntry* se = shape_entry(m, n, k, topk, want_norm);
+  if (!se) return RGT_ERR_HIP;
+  const Plan& p = se->p;
+  const Layout& L = se->L;
+  if ((st = check_ws(ws, ws_bytes, L.total)) != RGT_OK) return st;
+  if (p.mb * p.nb > kMaxTileCounters) return RGT_ERR_UNSUPPORTED;
+  char* base = static_cast<char*>(ws);
+  float* lg = logits ? logits : reinterpret_cast<float*>(base + L.logits);
+  GemvArgs g{static_cast<const u16*>(x), ldx, static_cast<const u16*>(w), ldw, lg,
+             reinterpret_cast<float*>(base + L.part), reinterpret_cast<u32*>(base + L.ctr), m, n, k, p.s, p.nb};
+  const bool fuse = se->fuse;
+  bool norm_in = se->norm_in;
   int n_norm = 0;
   auto norm_first = [&]() {
     norm_in = false;
@@ -812,40 +989,10 @@ static rgt_status route_sort_quant_impl(const void* x, int64_t ldx, const void* 
     ldx = nrm->ldxn;
   };
   if (!norm_in) norm_first();
-  const bool small = fused_small(p, m, n);
-  int upw_log = 8;
-  const void* fn = nullptr;
-  size_t lds = 0;
-  if (fuse) {
-    DevInfo di;
-    if (!dev_info(di)) return RGT_ERR_HIP;
-    fn = fused_kernel_for(p, n, norm_in);
-    lds = fused_lds_bytes(p, m, n, topk, small);
-    const int units = m * (k / 16);
-    // A workgroup's quant units cover at most this many tokens; their pairs
-    // must fit one wave.
-    const int cpr = k / 16;
-    auto pairs_fit_at = [&](int ul) {
-      return (((1 << ul) - 1) / cpr + 2) * topk <= 64 &&
-             (uint64_t)(p.grid << ul) * (uint64_t)cpr < (1ull << 32);  // exact magic division
-    };
-    if (small) {
-      // the fewest units per workgroup that cover every unit
-      upw_log = 6;
-      while (upw_log < 8 && ((units + (1 << upw_log) - 1) >> upw_log) > p.grid) ++upw_log;
-    } else {
-      // large mode: the most units per workgroup whose pairs fit one wave
-      // (fewer, fuller quant workgroups; measured faster at M >= 16)
-      upw_log = 8;
-      while (upw_log > 6 && !pairs_fit_at(upw_log) && units <= (p.grid << (upw_log - 1))) --upw_log;
-    }
-    const bool pairs_fit = pairs_fit_at(upw_log);
-    // Co-residency is required for the device-side waits; each thread owns at
-    // most one quant unit; in large mode workgroup r gathers row r.
-    if (p.grid > coresident_blocks(fn, lds, di.cus) || units > (p.grid << upw_log) || !pairs_fit ||
-        (!small && (m > p.grid || gather_loads(1, n, p.s) > kPollLoads)))
-      fuse = false;
-  }
+  const bool small = se->small;
+  const int upw_log = se->upw_log;
+  const void* fn = se->fn;
+  const size_t lds = se->lds;
   if (fuse) {
     const u32 cpr_magic = 0xFFFFFFFFu / (u32)(k / 16) + 1u;  // exact for unit * (K/16) < 2^32
     // The scrub sweeps the workspace past the tile counters (in the trace
@@ -865,7 +1012,7 @@ static rgt_status route_sort_quant_impl(const void* x, int64_t ldx, const void* 
     const u32 ids1 = (u32)((L.trs - L.part) / 16) + (norm_in && m > 1 ? (u32)(even_up(m) / 2) : 0u);
     FusedArgs a{g, bias, topk, block, small ? 1 : 0, fp4 ? 1 : 0, upw_log, cpr_magic, logits, topk_ids, topk_w, sorted_ids, expert_ids, offsets,
                 a_q, a_scale, reinterpret_cast<u32*>(base + L.ctl), reinterpret_cast<u64*>(base + L.tpart),
-                reinterpret_cast<u64*>(base + L.tids), wait_budget_ticks(), env_int("RGT_FAULT_INJECT", 0),
+                reinterpret_cast<u64*>(base + L.tids), wait_budget_ticks(), cfg.fault_inject,
 #ifdef RGT_TRACE
                 reinterpret_cast<u64*>(base + L.trace),
 #else

@@ -8,10 +8,11 @@
 
 namespace rgt {
 
-// Sort of up to a few thousand pairs in one workgroup: one wave up to
-// kWaveSortMaxP pairs, every wave of the workgroup above (launched with 1024
-// threads, so each wave walks a sixteenth of the pairs in 64-pair batches);
-// the pair positions go to pos_ws for the quant.
+// Sort of up to a few thousand pairs in one workgroup: one wave when launched
+// with 256 threads (the host does so for small P, at most kWaveSortMaxP),
+// every wave of the workgroup when launched with 1024 (each wave walks a
+// sixteenth of the pairs in 64-pair batches); the pair positions go to pos_ws
+// for the quant.
 __global__ void __launch_bounds__(1024) sort_small_kernel(const int32_t* ids, int P, int N, int B,
                                                           int32_t* sorted_ids, int32_t* expert_ids,
                                                           int32_t* offsets, int32_t* pos_ws) {
@@ -22,7 +23,7 @@ __global__ void __launch_bounds__(1024) sort_small_kernel(const int32_t* ids, in
   int* s_cnt = s_hist + (P > nw * N ? P : nw * N);
   int* s_off = s_cnt + N;
   int* s_scr = s_off + N + 1;
-  if (P <= kWaveSortMaxP) {
+  if (blockDim.x == 256) {
     if (threadIdx.x < 64) wave_sort<16>(ids, P, N, B, s_e, s_hist, s_cnt, s_off, pos_ws);
     vm_drain();
     __syncthreads();

@@ -193,7 +193,7 @@ def test_route_sort_quant_prefill(R):
                      sample_rows=lambda nv: rng.choice(nv, size=800, replace=False))
 
 
-def test_fused_wait_deadline_sets_error_and_reset_recovers(R, monkeypatch):
+def test_fused_wait_deadline_sets_error_and_reset_recovers(R, rgt_env):
     """A host-forced fault: the tiles publish nothing, so every device-side
     wait runs into its (shortened) deadline and exits; the error word
     reports RGT_ERR_TIMEOUT, and after a reset the same workspace gives
@@ -202,13 +202,11 @@ def test_fused_wait_deadline_sets_error_and_reset_recovers(R, monkeypatch):
     wl = Workload("deadline_M4", 4, 128, 6144, 8, 16)
     x, w, b = wl.make()
     ws = R.Workspace(wl.m, wl.n, wl.k, wl.topk, wl.block)
-    monkeypatch.setenv("RGT_FAULT_INJECT", "1")
-    monkeypatch.setenv("RGT_WAIT_BUDGET_US", "2000")
+    rgt_env(RGT_FAULT_INJECT=1, RGT_WAIT_BUDGET_US=2000)
     _, launches = fused(R, x, w, b, wl.topk, wl.block, ws)
     assert launches == 1
     assert R.check_workspace(ws) == 5, "expected RGT_ERR_TIMEOUT in the workspace error word"
-    monkeypatch.delenv("RGT_FAULT_INJECT")
-    monkeypatch.delenv("RGT_WAIT_BUDGET_US")
+    rgt_env(RGT_FAULT_INJECT=None, RGT_WAIT_BUDGET_US=None)
     # fail-stop: a further call on the timed-out workspace waits for nothing
     # and writes the poison outputs (ids -1, weights 0, offsets 0), whatever
     # tagged words the failed call left behind
@@ -352,3 +350,46 @@ def test_fused_tag_wrap_and_stale_words(R):
     for key in ("logits", "topk_ids", "topk_w", "offsets", "sorted_ids"):
         np.testing.assert_array_equal(got[key], r[key], err_msg=key)
     assert int(words[1].item()) & 0xFFFFFFFF == t
+
+
+# RGT_FORCE_BUCKET: the one-launch form's other mode and tile kind at shapes
+# whose default differs (small mode above 128 experts, large mode and the
+# MFMA tile at M <= 8), each equal to the chain and the oracle; RGT_LOG names
+# the plan taken.
+FORCED = [("small", Workload("force_small_n896_M1", 1, 896, 3584, 16, 16, bias=True)),
+          ("small", Workload("force_small_n896_M2", 2, 896, 3584, 16, 16, bias=True)),
+          ("small", Workload("force_small_n256_M4", 4, 256, 2048, 8, 16)),
+          ("large", Workload("force_large_M1", 1, 128, 6144, 8, 16)),
+          ("large", Workload("force_large_M4", 4, 128, 6144, 8, 16)),
+          ("mfma", Workload("force_mfma_M1", 1, 128, 6144, 8, 16)),
+          ("mfma,large", Workload("force_mfma_large_M8", 8, 128, 6144, 8, 16))]
+
+
+@pytest.mark.parametrize("force,wl", FORCED, ids=lambda c: getattr(c, "name", str(c)))
+def test_fused_forced_buckets(R, rgt_env, capfd, force, wl):
+    say(f"fused forced {force} {wl.name} M={wl.m} N={wl.n} K={wl.k}")
+    rgt_env(RGT_FORCE_BUCKET=force, RGT_LOG=1)
+    x, w, b = wl.make()
+    ws = R.Workspace(wl.m, wl.n, wl.k, wl.topk, wl.block)
+    f, launches = fused(R, x, w, b, wl.topk, wl.block, ws)
+    assert launches == 1
+    log = capfd.readouterr().err
+    mode = "large" if "large" in force else "small" if "small" in force else None
+    line = [ln for ln in log.splitlines() if ln.startswith(f"rgt: route M={wl.m} N={wl.n} K={wl.k}")]
+    assert line, log
+    if mode:
+        assert f"{mode} mode" in line[0], line[0]
+    if "mfma" in force:
+        assert "MFMA tile" in line[0], line[0]
+    fo = np_out(f)
+    c = np_out(chain(R, x, w, b, wl.topk, wl.block, ws))
+    for key in ("logits", "topk_ids", "topk_w", "offsets"):
+        np.testing.assert_array_equal(fo[key].view(np.uint32) if fo[key].dtype == np.float32 else fo[key],
+                                      c[key].view(np.uint32) if c[key].dtype == np.float32 else c[key],
+                                      err_msg=key)
+    total = int(fo["offsets"][-1])
+    for key in ("sorted_ids", "a_q", "a_scale"):
+        np.testing.assert_array_equal(fo[key][:total], c[key][:total], err_msg=key)
+    ids = check_against_oracle(x, w, b, wl.topk, wl.block, fo)
+    check_sort_quant(sort_out(fo), ids, x, wl.n, wl.block)
+    assert_workspace_ready(ws)

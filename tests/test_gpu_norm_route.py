@@ -144,10 +144,10 @@ CHAIN_CASES = [(Workload("m3_M65", 65, 128, 6144, 8, 16), True, "mxfp8"),
 
 
 @pytest.fixture(autouse=True)
-def one_launch_everywhere(monkeypatch):
+def one_launch_everywhere(rgt_env):
     """The one-launch form at every M it covers (by default only M = 1 takes
     it; the default choice has its own test below)."""
-    monkeypatch.setenv("RGT_NORM_IN_LAUNCH", "1")
+    rgt_env(RGT_NORM_IN_LAUNCH=1)
 
 
 @pytest.mark.parametrize("wl,residual,fmt", CASES, ids=lambda c: getattr(c, "name", str(c)))
@@ -167,10 +167,10 @@ def test_norm_route_one_launch_matches_chain_and_oracle(R, wl, residual, fmt):
 
 
 @pytest.mark.parametrize("m", [1, 2, 8, 64])
-def test_norm_route_default_choice(R, monkeypatch, m):
+def test_norm_route_default_choice(R, rgt_env, m):
     """Without the override: one launch at M = 1, the norm's launch then the
     one-launch route above; the same bits either way."""
-    monkeypatch.delenv("RGT_NORM_IN_LAUNCH")
+    rgt_env(RGT_NORM_IN_LAUNCH=None)
     wl = Workload(f"default_M{m}", m, 128, 6144, 8, 16, seed=400 + m)
     say(f"norm+route default choice M={m}")
     x, r, g, w, b = inputs(wl, True)
@@ -180,7 +180,7 @@ def test_norm_route_default_choice(R, monkeypatch, m):
     fo = host(f)
     assert_same(fo, host(chain(R, x, r, g, w, b, wl, ws, "mxfp8")), wl.block)
     check_oracle(x, r, g, w, b, wl, fo, "mxfp8")
-    monkeypatch.setenv("RGT_NORM_IN_LAUNCH", "0")
+    rgt_env(RGT_NORM_IN_LAUNCH=0)
     f0, launches0 = fused(R, x, r, g, w, b, wl, ws, "mxfp8")
     assert launches0 == 2
     assert_same(host(f0), fo, wl.block)
@@ -223,7 +223,7 @@ def test_norm_route_varying_m_on_one_workspace(R):
     assert R.check_workspace(ws) == 0
 
 
-def test_norm_route_wait_deadline_sets_error_and_reset_recovers(R, monkeypatch):
+def test_norm_route_wait_deadline_sets_error_and_reset_recovers(R, rgt_env):
     """Host-forced fault: neither rstd words nor partials are published, so
     every device-side wait runs into its (shortened) deadline and exits; the
     error word reports RGT_ERR_TIMEOUT and a reset restores correct results."""
@@ -231,13 +231,11 @@ def test_norm_route_wait_deadline_sets_error_and_reset_recovers(R, monkeypatch):
     wl = Workload("deadline_M4", 4, 128, 6144, 8, 16)
     x, r, g, w, b = inputs(wl, True)
     ws = R.Workspace(wl.m, wl.n, wl.k, wl.topk, wl.block)
-    monkeypatch.setenv("RGT_FAULT_INJECT", "1")
-    monkeypatch.setenv("RGT_WAIT_BUDGET_US", "2000")
+    rgt_env(RGT_FAULT_INJECT=1, RGT_WAIT_BUDGET_US=2000)
     _, launches = fused(R, x, r, g, w, b, wl, ws, "mxfp8")
     assert launches == 1
     assert R.check_workspace(ws) == 5
-    monkeypatch.delenv("RGT_FAULT_INJECT")
-    monkeypatch.delenv("RGT_WAIT_BUDGET_US")
+    rgt_env(RGT_FAULT_INJECT=None, RGT_WAIT_BUDGET_US=None)
     say("norm+route on a timed-out workspace (poison outputs)")
     p, _ = fused(R, x, r, g, w, b, wl, ws, "mxfp8")
     po = host(p)
