@@ -354,10 +354,31 @@ void launch_router_mfma(const GemvArgs& a, const Plan& p, hipStream_t st) {
   }
 }
 
+// The prefill GEMM with 32*NJ experts a tile (its two LDS buffers need more
+// than the default 64 KB of dynamic LDS: allowed once per instance).
+template <int NJ>
+bool launch_gemm_big(const GemvArgs& a, hipStream_t st) {
+  static std::atomic<bool> lds_set{false};
+  constexpr int bytes = gemm_big_lds_bytes<NJ>();
+  if (bytes > 65536 && !lds_set.load()) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(router_gemm_big_kernel<NJ>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
+      return false;
+    lds_set.store(true);
+  }
+  const int tiles = ((a.m + kGemmBM - 1) / kGemmBM) * ((a.n + 32 * NJ - 1) / (32 * NJ));
+  hipLaunchKernelGGL(router_gemm_big_kernel<NJ>, dim3(tiles), dim3(256), bytes, st, a.x, a.ldx, a.w, a.ldw, a.logits,
+                     a.m, a.n, a.k);
+  return true;
+}
+
 void launch_router(const GemvArgs& a, const Plan& p, hipStream_t st) {
   if (p.gemm) {
-    hipLaunchKernelGGL(router_gemm_kernel<1>, dim3(p.grid), dim3(256), 0, st, a.x, a.ldx, a.w, a.ldw, a.logits,
-                       a.m, a.n, a.k);
+    // 224 experts a tile where N is a multiple of it (N = 896: four tiles a
+    // row block), 256 where N is one of that, 128 otherwise
+    if (a.n % 224 == 0) launch_gemm_big<7>(a, st);
+    else if (a.n % 256 == 0) launch_gemm_big<8>(a, st);
+    else launch_gemm_big<4>(a, st);
     return;
   }
   if (p.valu) {
