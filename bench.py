@@ -245,7 +245,13 @@ def secondary(torch, R, dev, stream, copies_128: int):
             per[str(wl.m)] = {"us": round(us, 3), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
                               "launches": R.last_launch_count()}
             del xw
-        res[group] = {"w_copies": copies, "per_m": per}
+        # the streaming-read floor of this W (one cold copy a launch, 384
+        # workgroups), as for the headline sweep
+        sink = torch.zeros(384 * 256, dtype=torch.int32, device=dev)
+        floor_us = _graph_us(torch, stream, copies, lambda i: R.diag_read(w_all[i], sink, 384, nbytes=w_bytes))
+        for d in per.values():
+            d["floor_frac"] = round(floor_us / d["us"], 3)
+        res[group] = {"w_copies": copies, "stream_read_W_us": round(floor_us, 3), "per_m": per}
         del w_all
 
     res["router_partials_shared_swiglu_N128_K6144_I768_mxfp8"] = shared_swiglu_line(torch, R, dev, stream,

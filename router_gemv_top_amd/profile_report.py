@@ -163,8 +163,106 @@ def build_shared(res: str, out: str):
         f.write("\n".join(lines) + "\n")
 
 
+def _stats_rows(folder: str, keep):
+    rows = list(csv.DictReader(open(_find(folder, "*kernel_stats.csv"))))
+    out = []
+    for r in rows:
+        name = r["Name"].replace("rgt::", "")
+        if not keep(name):
+            continue
+        short = name.split("(")[0].replace("void ", "")
+        out.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
+                   f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} |")
+    return out
+
+
+def build_stage1(res: str, out: str):
+    """Kernel durations of the stage-1 grouped MoE GEMM (bench.py --only-stage1)
+    from RES/prof_stage1."""
+    os.makedirs(out, exist_ok=True)
+    lines = ["# Stage-1 grouped MoE GEMM (MXFP8 rows x MXFP4 expert gate_up, SwiGLU): kernel durations (rocprofv3)", "",
+             "Workloads: N = 128 experts, K = 6144, top-8, I = 768 and N = 896, K = 3584, top-16, I = 384;",
+             "block 16; M = 1, 8, 64; the sort's rows and the expert weights as bench.py's stage-1 line draws",
+             "them (weights rotating through copies, so they stream from HBM). `moe_stage1_ksplit_kernel` is",
+             "the four-way K split for small grids, `moe_stage1_kernel<JT>` the column-tile forms.", "",
+             "Command (from the repository root, results folder RES):", "",
+             "    rocprofv3 --kernel-trace --stats --output-format csv -d RES/prof_stage1 -o s1 "
+             "-- python3 bench.py --only-stage1",
+             "    python -m router_gemv_top_amd.profile_report --stage1 RES profiles", "",
+             "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    lines += _stats_rows(os.path.join(res, "prof_stage1"), lambda n: "stage1" in n)
+    with open(os.path.join(out, "stage1_moe_gemm_a8w4_kernel_stats.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def build_prefill(res: str, out: str):
+    """Kernel durations of the prefill call (bench.py --only-prefill) and the
+    router GEMM's MFMA counters, from RES/prefill_stats, RES/prefill_busy and
+    RES/prefill_mops."""
+    os.makedirs(out, exist_ok=True)
+    lines = ["# Prefill routing (M=8192, N=896, K=3584, top-16, block 64, 5% duplicate rows): kernels and MFMA "
+             "counters", "",
+             "Chain path (seven launches per call): router GEMM, top-k gate, the four-kernel large sort (the",
+             "scatter workgroups also write the layout of their expert slices), MXFP8 quant.", "",
+             "Commands (from the repository root, results folder RES):", "",
+             "    rocprofv3 --kernel-trace --stats --output-format csv -d RES/prefill_stats -o c5 "
+             "-- python3 bench.py --only-prefill --calls 10",
+             "    rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv "
+             "-d RES/prefill_busy -o p -- python3 bench.py --only-prefill --calls 3",
+             "    rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 --output-format csv -d RES/prefill_mops -o p "
+             "-- python3 bench.py --only-prefill --calls 3",
+             "    python -m router_gemv_top_amd.profile_report --prefill RES profiles", "",
+             "`--only-prefill` runs the full call --calls times, then the router GEMM alone --calls times",
+             "(so the GEMM shows twice the calls of the other kernels).", "",
+             "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    rows = list(csv.DictReader(open(_find(os.path.join(res, "prefill_stats"), "*kernel_stats.csv"))))
+    gemm_us = None
+    for r in rows:
+        name = r["Name"].replace("rgt::", "")
+        if not any(t in name for t in ("gemm", "quant", "topk", "sort")):
+            continue
+        short = name.split("(")[0].replace("void ", "")
+        lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
+                     f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} |")
+        if "gemm" in name:
+            gemm_us = float(r["AverageNs"]) / 1e3
+    med = {}
+    for folder, names in (("prefill_busy", ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE")),
+                          ("prefill_mops", ("SQ_INSTS_VALU_MFMA_MOPS_BF16",))):
+        path = _find(os.path.join(res, folder), "*counter_collection.csv")
+        for c in names:
+            vals = []
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    if "gemm" in r["Kernel_Name"] and r["Counter_Name"] == c:
+                        vals.append(float(r["Counter_Value"]))
+            if vals:
+                med[c] = statistics.median(vals)
+    flops = 2 * 8192 * 896 * 3584
+    lines += ["", "Router GEMM counters (median over the profiled dispatches):", "", "| counter | value |", "|---|---|"]
+    for c, v in med.items():
+        lines.append(f"| {c} | {v:.0f} |")
+    if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in med:
+        lines.append("")
+        lines.append(f"- MOPS x 512 = {med['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512:.3e} flop against the algorithmic "
+                     f"2*M*N*K = {flops:.3e}.")
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in med and "GRBM_GUI_ACTIVE" in med:
+        frac = med["SQ_VALU_MFMA_BUSY_CYCLES"] / (med["GRBM_GUI_ACTIVE"] / 8 * 1024)
+        lines.append(f"- MFMA busy fraction = busy / (GRBM_GUI_ACTIVE/8 x 1024 SIMDs) = {frac:.3f} "
+                     "(GRBM_GUI_ACTIVE taken as summed over the 8 XCDs).")
+    if gemm_us:
+        lines.append(f"- Time-based: {flops / (gemm_us * 1e-6) / 1e12:.0f} TFLOP/s at {gemm_us:.1f} us = "
+                     f"{flops / (gemm_us * 1e-6) / 2.5e15:.3f} of the 2.5 PFLOP/s dense bf16 peak.")
+    with open(os.path.join(out, "prefill_M8192_N896_kernel_stats_mfma.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "--shared":
         build_shared(sys.argv[2], sys.argv[3])
+    elif sys.argv[1] == "--stage1":
+        build_stage1(sys.argv[2], sys.argv[3])
+    elif sys.argv[1] == "--prefill":
+        build_prefill(sys.argv[2], sys.argv[3])
     else:
         build(sys.argv[1], sys.argv[2])
