@@ -160,14 +160,16 @@ __global__ void __launch_bounds__(256) router_gemm_kernel(const uint16_t* x, int
 // ---------------------------------------------------------------------------
 // Prefill GEMM (every workgroup the whole k range): workgroup tile 128 rows of
 // x by 32*NJ experts (NJ = 7: 224, so N = 896 is four tiles and M = 8192
-// gives 256 workgroups, one per CU), k-step 64, two LDS buffers and one
-// barrier per step: step s+1's tiles are loaded into registers, step s is
-// multiplied from its buffer, then step s+1 goes into the other buffer (last
-// read in step s-1, before the barrier that ended it). 4 waves in 2 x 2, each
-// 64 rows by 16*NJ experts as 4 x NJ v_mfma_f32_16x16x32_bf16 tiles: per 32
-// of k a wave reads 4 + NJ fragments for 4*NJ products. LDS rows as above
-// (72 bf16). Tiles are numbered row-block major and spread over the XCDs in
-// contiguous runs, so the n-blocks of one row block share x in one L2.
+// gives 256 workgroups, one per CU), k-step 64. Eight waves, two a SIMD (so
+// one wave's products run while the other waits on LDS or memory), as 4 x 2,
+// each 32 rows by 16*NJ experts as 2 x NJ v_mfma_f32_16x16x32_bf16 tiles.
+// Two LDS buffers and one barrier a step: the loads of steps s+1 and s+2 are
+// in flight in two named register sets while step s is multiplied, and step
+// s+1 goes into the other buffer (last read in step s-1, before the barrier
+// that ended it). LDS rows as above (72 bf16). Tiles are numbered row-block
+// major and spread over the XCDs in contiguous runs, so the n-blocks of one
+// row block share x in one L2. Measured at M = 8192, N = 896, K = 3584: four
+// waves of 64 x 112 took 74 us, these eight 66 us (the same bits).
 // ---------------------------------------------------------------------------
 template <int NJ>
 constexpr int gemm_big_lds_bytes() {
@@ -175,13 +177,12 @@ constexpr int gemm_big_lds_bytes() {
 }
 
 template <int NJ>
-__global__ void __launch_bounds__(256) router_gemm_big_kernel(const uint16_t* x, int64_t ldx, const uint16_t* w,
+__global__ void __launch_bounds__(512) router_gemm_big_kernel(const uint16_t* x, int64_t ldx, const uint16_t* w,
                                                               int64_t ldw, float* out, int M, int N, int K) {
   constexpr int BN = 32 * NJ;
-  constexpr int A_LD = kGemmBM * 8 / 256;           // 16-byte chunks a thread moves per step: 4
-  constexpr int B_LD = BN * 8 / 256;                // 7 at NJ = 7
-  static_assert(BN * 8 % 256 == 0, "whole 16-byte chunks a thread");
+  constexpr int B_LD = (BN * 8 + 511) / 512;        // 16-byte chunks of W a thread moves per step
   constexpr int BUF = (kGemmBM + BN) * kGemmLds;    // bf16 per buffer
+  static_assert(kGemmBM * 8 == 2 * 512 && B_LD >= 2 && B_LD <= 4, "two x chunks, two to four W chunks a thread");
   extern __shared__ __align__(16) uint16_t smem_g[];
   const int nbn = (N + BN - 1) / BN;
   const int tiles = ((M + kGemmBM - 1) / kGemmBM) * nbn;
@@ -192,27 +193,28 @@ __global__ void __launch_bounds__(256) router_gemm_big_kernel(const uint16_t* x,
   const int r16 = lane & 15, grp = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
   // global -> register -> LDS: chunk c of a step is row c / 8, 16-byte column
-  // c % 8; thread t moves chunks t + 256*i. Rows past M or N read the last
-  // row (never stored).
-  // The registers of a step are named values local to one loop iteration
-  // (arrays of them, even unrolled, were kept in scratch memory), and the
-  // source addresses are recomputed per step (a few integer operations).
+  // c % 8; thread t moves chunks t + 512*i. Rows past M or N read the last
+  // row (never stored); W chunks past the tile (224 rows: 3.5 a thread) read
+  // its last row and are not stored. Named registers, recomputed addresses:
+  // arrays of them that cross the loop's back edge end up in scratch memory.
   const int lc = t & 7, lr = t >> 3;
+  const int steps = K / kGemmBK;  // a multiple of 8
   auto lda = [&](int i, int k0) {
-    return *reinterpret_cast<const uint4*>(x + (int64_t)min(m0 + lr + 32 * i, M - 1) * ldx + k0 + 8 * lc);
+    return *reinterpret_cast<const uint4*>(x + (int64_t)min(m0 + lr + 64 * i, M - 1) * ldx + k0 + 8 * lc);
   };
   auto ldb = [&](int i, int k0) {
-    return *reinterpret_cast<const uint4*>(w + (int64_t)min(n0 + lr + 32 * i, N - 1) * ldw + k0 + 8 * lc);
+    return *reinterpret_cast<const uint4*>(w + (int64_t)min(n0 + min(lr + 64 * i, BN - 1), N - 1) * ldw + k0 +
+                                           8 * lc);
   };
   auto sta = [&](int b, int i, const uint4& v) {
-    *reinterpret_cast<uint4*>(smem_g + b * BUF + (lr + 32 * i) * kGemmLds + 8 * lc) = v;
+    *reinterpret_cast<uint4*>(smem_g + b * BUF + (lr + 64 * i) * kGemmLds + 8 * lc) = v;
   };
   auto stb = [&](int b, int i, const uint4& v) {
-    *reinterpret_cast<uint4*>(smem_g + b * BUF + (kGemmBM + lr + 32 * i) * kGemmLds + 8 * lc) = v;
+    if (lr + 64 * i < BN) *reinterpret_cast<uint4*>(smem_g + b * BUF + (kGemmBM + lr + 64 * i) * kGemmLds + 8 * lc) = v;
   };
-  floatx4_t acc[4][NJ];
+  floatx4_t acc[2][NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   auto compute = [&](int b) {
@@ -220,81 +222,63 @@ __global__ void __launch_bounds__(256) router_gemm_big_kernel(const uint16_t* x,
     const uint16_t* sb = sa + kGemmBM * kGemmLds;
 #pragma unroll
     for (int kk = 0; kk < kGemmBK; kk += 32) {
-      uint4 fa[4], fb[NJ];
+      uint4 fa[2], fb[NJ];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        fa[i] = *reinterpret_cast<const uint4*>(sa + (wm * 64 + 16 * i + r16) * kGemmLds + kk + 8 * grp);
+      for (int i = 0; i < 2; ++i)
+        fa[i] = *reinterpret_cast<const uint4*>(sa + (wm * 32 + 16 * i + r16) * kGemmLds + kk + 8 * grp);
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
         fb[j] = *reinterpret_cast<const uint4*>(sb + (wn * 16 * NJ + 16 * j + r16) * kGemmLds + kk + 8 * grp);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fa[i]),
                                                              __builtin_bit_cast(bf16x8_t, fb[j]), acc[i][j], 0, 0, 0);
     }
   };
-  static_assert(A_LD == 4 && B_LD >= 4 && B_LD <= 8, "four A chunks and four to eight B chunks a thread");
-  // Two register sets, P and Q, take turns: while step s is multiplied, the
-  // loads of steps s+1 and s+2 are in flight (a step's loads have two steps
-  // of arithmetic to arrive in, since one wave a SIMD hides no latency).
-  const int steps = K / kGemmBK;  // >= 2 (K >= 512)
-#define RGT_GEMM_REGS(P) uint4 P##a0, P##a1, P##a2, P##a3, P##b0, P##b1, P##b2, P##b3, P##b4, P##b5, P##b6, P##b7;
-#define RGT_GEMM_LOAD(P, k0)                                                                        \
-  P##a0 = lda(0, k0), P##a1 = lda(1, k0), P##a2 = lda(2, k0), P##a3 = lda(3, k0);                  \
-  P##b0 = ldb(0, k0), P##b1 = ldb(1, k0), P##b2 = ldb(2, k0), P##b3 = ldb(3, k0);                  \
-  if constexpr (B_LD > 4) P##b4 = ldb(4, k0);                                                       \
-  if constexpr (B_LD > 5) P##b5 = ldb(5, k0);                                                       \
-  if constexpr (B_LD > 6) P##b6 = ldb(6, k0);                                                       \
-  if constexpr (B_LD > 7) P##b7 = ldb(7, k0);
+  // past the last step the loads repeat it and the stage fills a buffer
+  // nobody reads (no branch, so the compiler counts the loads in flight)
+#define RGT_GEMM_REGS(P) uint4 P##a0, P##a1, P##b0, P##b1, P##b2, P##b3;
+#define RGT_GEMM_LOAD(P, st)                                                                        \
+  {                                                                                                 \
+    const int k0 = min(st, steps - 1) * kGemmBK;                                                   \
+    P##a0 = lda(0, k0), P##a1 = lda(1, k0), P##b0 = ldb(0, k0), P##b1 = ldb(1, k0);                \
+    if constexpr (B_LD > 2) P##b2 = ldb(2, k0);                                                     \
+    if constexpr (B_LD > 3) P##b3 = ldb(3, k0);                                                     \
+  }
 #define RGT_GEMM_STAGE(P, b)                                                                        \
-  sta(b, 0, P##a0), sta(b, 1, P##a1), sta(b, 2, P##a2), sta(b, 3, P##a3);                           \
-  stb(b, 0, P##b0), stb(b, 1, P##b1), stb(b, 2, P##b2), stb(b, 3, P##b3);                           \
-  if constexpr (B_LD > 4) stb(b, 4, P##b4);                                                         \
-  if constexpr (B_LD > 5) stb(b, 5, P##b5);                                                         \
-  if constexpr (B_LD > 6) stb(b, 6, P##b6);                                                         \
-  if constexpr (B_LD > 7) stb(b, 7, P##b7);
+  sta(b, 0, P##a0), sta(b, 1, P##a1), stb(b, 0, P##b0), stb(b, 1, P##b1);                           \
+  if constexpr (B_LD > 2) stb(b, 2, P##b2);                                                         \
+  if constexpr (B_LD > 3) stb(b, 3, P##b3);
   RGT_GEMM_REGS(p_)
   RGT_GEMM_REGS(q_)
   RGT_GEMM_LOAD(p_, 0)
-  RGT_GEMM_LOAD(q_, kGemmBK)
+  RGT_GEMM_LOAD(q_, 1)
   RGT_GEMM_STAGE(p_, 0)
   __syncthreads();
-  // invariant at the top: step s is in LDS buffer s & 1, step s+1 in flight
-  // in q_ (s even) or p_ (s odd)
-  int s = 0;
-  for (; s + 2 < steps; s += 2) {
-    RGT_GEMM_LOAD(p_, (s + 2) * kGemmBK)
+  for (int s = 0; s < steps; s += 2) {
+    RGT_GEMM_LOAD(p_, s + 2)
     compute(0);
     RGT_GEMM_STAGE(q_, 1)
     __syncthreads();
-    if (s + 3 < steps) {
-      RGT_GEMM_LOAD(q_, (s + 3) * kGemmBK)
-    }
+    RGT_GEMM_LOAD(q_, s + 3)
     compute(1);
     RGT_GEMM_STAGE(p_, 0)
     __syncthreads();
-  }
-  // s + 2 >= steps: step s in buffer 0 (s even), step s+1 in q_ if it exists
-  compute(0);
-  if (s + 1 < steps) {
-    RGT_GEMM_STAGE(q_, 1)
-    __syncthreads();
-    compute(1);
   }
 #undef RGT_GEMM_REGS
 #undef RGT_GEMM_LOAD
 #undef RGT_GEMM_STAGE
   // D lane l: rows 4*(l/16) + r of the 16 x 16 tile, column l % 16
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int col = n0 + wn * 16 * NJ + 16 * j + r16;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = m0 + wm * 64 + 16 * i + 4 * grp + r;
+        const int row = m0 + wm * 32 + 16 * i + 4 * grp + r;
         if (row < M && col < N) out[(int64_t)row * N + col] = acc[i][j][r];
       }
     }

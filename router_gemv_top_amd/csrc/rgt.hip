@@ -367,7 +367,7 @@ bool launch_gemm_big(const GemvArgs& a, hipStream_t st) {
     lds_set.store(true);
   }
   const int tiles = ((a.m + kGemmBM - 1) / kGemmBM) * ((a.n + 32 * NJ - 1) / (32 * NJ));
-  hipLaunchKernelGGL(router_gemm_big_kernel<NJ>, dim3(tiles), dim3(256), bytes, st, a.x, a.ldx, a.w, a.ldw, a.logits,
+  hipLaunchKernelGGL(router_gemm_big_kernel<NJ>, dim3(tiles), dim3(512), bytes, st, a.x, a.ldx, a.w, a.ldw, a.logits,
                      a.m, a.n, a.k);
   return true;
 }
