@@ -75,13 +75,21 @@ __device__ __forceinline__ void stage1_step(const uint4& a0, const uint4& a1, co
 // for the four steps are one contiguous 64-byte run, its scale bytes for the
 // four steps one 4-byte word (the MFMA picks byte s with op_sel), and its A
 // bytes two runs of four 16-byte chunks 32 bytes apart.
-template <int JT>
+//
+// Pad rows (sorted_ids = the sentinel) have no output, so their lanes read
+// the tile's first row instead of their own (same addresses within the wave:
+// one fetch), which at decode sizes, where most rows of a block are pads,
+// cuts the A traffic from L2 several times over; their products are dropped.
+// PF: load groups in flight ahead of the one being multiplied (1 or 2).
+template <int JT, int PF = 1>
 __device__ __forceinline__ void stage1_tile(const Stage1Args& a, int p0, int e, int j, int g0, int g1,
                                             floatx4_t (&acc)[2 * JT]) {
+  static_assert(PF == 1 || PF == 2, "one or two load groups ahead");
   const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   const int K = a.k;
-  const uint8_t* arow = a.a_q + (int64_t)(p0 + r) * K + 128 * (g >> 1) + 16 * (g & 1);
-  const u32* asc = reinterpret_cast<const u32*>(a.a_scale + (int64_t)(p0 + r) * (K >> 5)) + g;
+  const int prow = a.sorted_ids[p0 + r] < a.pairs ? p0 + r : p0;
+  const uint8_t* arow = a.a_q + (int64_t)prow * K + 128 * (g >> 1) + 16 * (g & 1);
+  const u32* asc = reinterpret_cast<const u32*>(a.a_scale + (int64_t)prow * (K >> 5)) + g;
   const int64_t wrows = 2 * (int64_t)a.inter;
   const uint8_t* wb[2 * JT];
   const u32* sb[2 * JT];
@@ -102,7 +110,9 @@ __device__ __forceinline__ void stage1_tile(const Stage1Args& a, int p0, int e, 
   // MFMAs, then the registers move over.
   uint4 a0[kStage1Group], a1[kStage1Group], b[2 * JT][kStage1Group];
   uint4 na0[kStage1Group], na1[kStage1Group], nb[2 * JT][kStage1Group];
+  [[maybe_unused]] uint4 qa0[kStage1Group], qa1[kStage1Group], qb[2 * JT][kStage1Group];
   u32 sa, sw[2 * JT], nsa = 0, nsw[2 * JT];
+  [[maybe_unused]] u32 qsa = 0, qsw[2 * JT];
 #define RGT_STAGE1_LOAD(A0, A1, B, SA, SW, GRP)                                              \
   do {                                                                                     \
     const uint8_t* ar_ = arow + 512 * (GRP);                                               \
@@ -118,8 +128,15 @@ __device__ __forceinline__ void stage1_tile(const Stage1Args& a, int p0, int e, 
     }                                                                                      \
   } while (0)
   RGT_STAGE1_LOAD(a0, a1, b, sa, sw, g0);
+  if constexpr (PF == 2) {
+    if (g0 + 1 < g1) RGT_STAGE1_LOAD(na0, na1, nb, nsa, nsw, g0 + 1);
+  }
   for (int grp = g0; grp < g1; ++grp) {
-    if (grp + 1 < g1) RGT_STAGE1_LOAD(na0, na1, nb, nsa, nsw, grp + 1);
+    if constexpr (PF == 2) {
+      if (grp + 2 < g1) RGT_STAGE1_LOAD(qa0, qa1, qb, qsa, qsw, grp + 2);
+    } else {
+      if (grp + 1 < g1) RGT_STAGE1_LOAD(na0, na1, nb, nsa, nsw, grp + 1);
+    }
     stage1_step<0, JT>(a0[0], a1[0], b, sa, sw, acc);
     stage1_step<1, JT>(a0[1], a1[1], b, sa, sw, acc);
     stage1_step<2, JT>(a0[2], a1[2], b, sa, sw, acc);
@@ -130,10 +147,21 @@ __device__ __forceinline__ void stage1_tile(const Stage1Args& a, int p0, int e, 
       a1[s] = na1[s];
 #pragma unroll
       for (int t = 0; t < 2 * JT; ++t) b[t][s] = nb[t][s];
+      if constexpr (PF == 2) {
+        na0[s] = qa0[s];
+        na1[s] = qa1[s];
+#pragma unroll
+        for (int t = 0; t < 2 * JT; ++t) nb[t][s] = qb[t][s];
+      }
     }
     sa = nsa;
 #pragma unroll
     for (int t = 0; t < 2 * JT; ++t) sw[t] = nsw[t];
+    if constexpr (PF == 2) {
+      nsa = qsa;
+#pragma unroll
+      for (int t = 0; t < 2 * JT; ++t) nsw[t] = qsw[t];
+    }
   }
 #undef RGT_STAGE1_LOAD
 }
@@ -167,6 +195,7 @@ __global__ void __launch_bounds__(256) moe_stage1_kernel(Stage1Args a) {
   const int p0 = (int)blockIdx.x * 16;
   const int total = a.offsets[a.n];
   if (p0 >= total) return;  // past the padded total: no segment here
+  if (a.sorted_ids[p0] >= a.pairs) return;  // pads only (pairs come first in a segment)
   const int e = a.expert_ids[p0 >> (__ffs(a.block) - 1)];
   const int j = ((int)blockIdx.y * 4 + (threadIdx.x >> 6)) * 16 * JT;
   if (j >= a.inter) return;
@@ -184,12 +213,13 @@ __global__ void __launch_bounds__(256) moe_stage1_ksplit_kernel(Stage1Args a) {
   const int p0 = (int)blockIdx.x * 16;
   const int total = a.offsets[a.n];
   if (p0 >= total) return;
+  if (a.sorted_ids[p0] >= a.pairs) return;  // pads only
   const int e = a.expert_ids[p0 >> (__ffs(a.block) - 1)];
   const int j = (int)blockIdx.y * 16;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int G = a.k / 512;
   floatx4_t acc[2];
-  stage1_tile<1>(a, p0, e, j, wave * G / 4, (wave + 1) * G / 4, acc);
+  stage1_tile<1, 2>(a, p0, e, j, wave * G / 4, (wave + 1) * G / 4, acc);
   if (wave > 0) {
     s_part[wave - 1][0][lane] = acc[0];
     s_part[wave - 1][1][lane] = acc[1];
