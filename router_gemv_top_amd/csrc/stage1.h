@@ -200,7 +200,7 @@ __global__ void __launch_bounds__(256) moe_stage1_kernel(Stage1Args a) {
   const int j = ((int)blockIdx.y * 4 + (threadIdx.x >> 6)) * 16 * JT;
   if (j >= a.inter) return;
   floatx4_t acc[2 * JT];
-  stage1_tile<JT>(a, p0, e, j, 0, a.k / 512, acc);
+  stage1_tile<JT, 2>(a, p0, e, j, 0, a.k / 512, acc);
   stage1_store<JT>(a, p0, j, acc);
 }
 
