@@ -659,27 +659,52 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
       for (int i = 0; i < NV; ++i) mr[r][i] = r < m ? uniform_u64(s_mask[r][i]) : 0ull;
   };
   // Positions of this wave's row (one row: wave 0's own ballots, no barrier
-  // before; it also leaves its masks for the layout workgroup's other waves).
-  if (row < m) {
+  // before). The layout workgroup writes the layout here too, from the same
+  // masks, before the chunk exchange: offsets of every expert (an absent
+  // one's segment is empty), the block of each present expert and its pads.
+  if (row < m || (layout_here && m > 1)) {
     u64 mr[4][NV];
     if (m == 1) {
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         mr[0][i] = ballot64(sel[i]);
         mr[1][i] = mr[2][i] = mr[3][i] = 0ull;
-        if (layout_here && lane == 0) s_mask[0][i] = mr[0][i];
       }
     } else {
       masks_lds(mr);
     }
     const Seg sg = seg_of(mr);
+    if (row < m) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i)
-      if (sel[i]) {
-        const int q = sg.blk[i] * B + sg.rk[i];
-        s_pos[row * k + slot[i]] = q;
-        if (layout_here) a.sorted_ids[q] = row * k + slot[i];
+      for (int i = 0; i < NV; ++i)
+        if (sel[i]) {
+          const int q = sg.blk[i] * B + sg.rk[i];
+          s_pos[row * k + slot[i]] = q;
+          if (layout_here) a.sorted_ids[q] = row * k + slot[i];
+        }
+    }
+    if (layout_here) {
+      if (wave == 0) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          if (c0 + i < n) a.offsets[c0 + i] = sg.blk[i] * B;
+          if (sg.present[i]) a.expert_ids[sg.blk[i]] = c0 + i;
+        }
+        if (lane == 0) a.offsets[n] = sg.total * B;
       }
+      if (m == 1) {
+        // every block holds one pair (its first row) and B - 1 pads: the
+        // rows below k * B that are not a multiple of B (wave 0 alone)
+        for (int q = lane; q < sg.total * B; q += 64)
+          if (q & (B - 1)) a.sorted_ids[q] = P;
+      } else {
+        // the four waves split the pads
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+          if (sg.present[i])
+            for (int q = sg.cnt[i] + wave; q < B; q += 4) a.sorted_ids[sg.blk[i] * B + q] = P;
+      }
+    }
   }
   // the chunks go to LDS so that all four waves store them
   __shared__ uint4 s_codes[256];
@@ -691,25 +716,6 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
   }
   __syncthreads();  // s_pos, the chunks and the masks complete
   RGT_STAMP(a.trace, 8);
-  if (layout_here) {
-    // offsets of every expert (an absent one's segment is empty), the block
-    // of each present expert and its pads (the four waves split the pads)
-    u64 mr[4][NV];
-    masks_lds(mr);
-    const Seg sg = seg_of(mr);
-    if (wave == 0) {
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        if (c0 + i < n) a.offsets[c0 + i] = sg.blk[i] * B;
-        if (sg.present[i]) a.expert_ids[sg.blk[i]] = c0 + i;
-      }
-      if (lane == 0) a.offsets[n] = sg.total * B;
-    }
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-      if (sg.present[i])
-        for (int q = sg.cnt[i] + wave; q < B; q += 4) a.sorted_ids[sg.blk[i] * B + q] = P;
-  }
   RGT_STAMP(a.trace, 3);
   if (quant_wg) store_chunks_spread(a, (int)blockIdx.x << a.upw_log, s_pos, s_codes, s_sc);
   RGT_STAMP(a.trace, 9);
