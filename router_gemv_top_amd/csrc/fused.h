@@ -683,6 +683,7 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
           if (layout_here) a.sorted_ids[q] = row * k + slot[i];
         }
     }
+    RGT_STAMP(a.trace, 6);
     if (layout_here) {
       if (wave == 0) {
 #pragma unroll
@@ -704,6 +705,7 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
           if (sg.present[i])
             for (int q = sg.cnt[i] + wave; q < B; q += 4) a.sorted_ids[sg.blk[i] * B + q] = P;
       }
+      RGT_STAMP(a.trace, 7);
     }
   }
   // the chunks go to LDS so that all four waves store them
