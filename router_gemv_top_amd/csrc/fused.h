@@ -190,6 +190,7 @@ __device__ __forceinline__ bool gather_logits(const FusedArgs& a, int r0, int ro
     u32x4_t va[NL];
     if (poller) issue(va);
     during();  // other work while the first poll is in flight
+    RGT_STAMP(a.trace, 3);
 #ifdef RGT_TRACE
     int polls = 0;
 #endif
@@ -205,6 +206,7 @@ __device__ __forceinline__ bool gather_logits(const FusedArgs& a, int r0, int ro
         break;
       }
     }
+    RGT_STAMP(a.trace, 15);
 #ifdef RGT_TRACE
     if (t == 0 && a.trace) {  // poll rounds and the gather's start time
       a.trace[blockIdx.x * 16 + 10] = (u64)polls;
@@ -384,10 +386,13 @@ __device__ __forceinline__ bool poll_ids_any(const FusedArgs& a, int P, u32 tag,
 // whether it is selected, its slot and its score key. bv: this lane's bias
 // values. Up to four experts a lane the threshold selection; above, k rounds
 // of a wave maximum whose slot-ordered winners are handed to their owners
-// through s_flag (n ints of LDS owned by the calling wave).
+// through s_flag (n ints of LDS owned by the calling wave). With slots false
+// (a caller that only needs the selected set, one position per winner) the
+// threshold selection numbers the winners in expert order instead of by rank.
 template <int NV>
 __device__ __forceinline__ void row_topk_owner(const FusedArgs& a, const float* row, const float (&bv)[NV],
-                                               bool (&sel)[NV], int (&slot)[NV], u32 (&key)[NV], int* s_flag) {
+                                               bool (&sel)[NV], int (&slot)[NV], u32 (&key)[NV], int* s_flag,
+                                               bool slots) {
   const int n = a.g.n, k = a.topk, lane = lane_id(), c0 = lane * NV;
   float sv[NV];
 #pragma unroll
@@ -402,9 +407,11 @@ __device__ __forceinline__ void row_topk_owner(const FusedArgs& a, const float* 
   if constexpr (NV <= 4) {
     __shared__ __align__(16) u64 s_c[4][32];
     u64* sc = s_c[threadIdx.x >> 6];
-    if (k <= 8) wave_topk_threshold<NV, 8>(key, k, sel, slot, sc);
-    else if (k <= 16) wave_topk_threshold<NV, 16>(key, k, sel, slot, sc);
-    else wave_topk_threshold<NV, 32>(key, k, sel, slot, sc);
+    wave_threshold_select<NV>(key, k, sel);
+    if (!slots) wave_select_order<NV>(sel, slot);
+    else if (k <= 8) wave_select_slots<NV, 8>(key, sel, slot, sc);
+    else if (k <= 16) wave_select_slots<NV, 16>(key, sel, slot, sc);
+    else wave_select_slots<NV, 32>(key, sel, slot, sc);
   } else {
     __shared__ __align__(16) int s_slot[4][64];
     float sv1[1][NV];
@@ -517,31 +524,58 @@ __device__ __forceinline__ u64 uniform_u64(u64 v) {
          (u32)__builtin_amdgcn_readfirstlane((int)(u32)v);
 }
 
-// A quant workgroup's chunks stored by all of its 256 threads: item it is
-// chunk slot (it mod 2^upw_log) of the workgroup and slot j = it >> upw_log of
-// its token (consecutive threads take consecutive chunks of one padded row).
+// A quant workgroup's chunks stored by all of its 256 threads: thread t
+// keeps chunk slot us = t mod 2^upw_log of the workgroup (its codes and
+// packed scales read from LDS once) and stores it to the padded rows of
+// pairs j = t >> upw_log, + 256 >> upw_log, ... of its token (consecutive
+// threads take consecutive chunks of one padded row). All of the thread's
+// positions are read before its first store, so the LDS latencies overlap.
 // s_codes / s_sc: the chunks' codes and packed scales by chunk slot; s_pos:
 // the padded row of pair t*k + j.
+template <int JN, bool FP4>
+__device__ __forceinline__ void store_chunk_rows(const FusedArgs& a, int t, int c, int j0, int js, const int* s_pos,
+                                                 const uint4& cd, u32 sc) {
+  const int k = a.topk;
+  const u32 row_bytes = FP4 ? (u32)a.g.k >> 1 : (u32)a.g.k;
+  const u32 kscale = (u32)a.g.k >> 5;
+  uint8_t* q_col = a.a_q + (FP4 ? 8 * c : 16 * c);
+  uint8_t* s_col = a.a_scale + (c >> 1);
+  const bool lead = (c & 7) == 0;
+  int r[JN];
+#pragma unroll
+  for (int i = 0; i < JN; ++i) r[i] = s_pos[t * k + min(j0 + i * js, k - 1)];
+#pragma unroll
+  for (int i = 0; i < JN; ++i) {
+    if (j0 + i * js < k) {
+      uint8_t* row = q_col + (u64)(u32)r[i] * row_bytes;
+      if (FP4) *reinterpret_cast<uint2*>(row) = make_uint2(cd.x, cd.y);
+      else *reinterpret_cast<uint4*>(row) = cd;
+      if (lead) *reinterpret_cast<u32*>(s_col + (u64)(u32)r[i] * kscale) = sc;
+    }
+  }
+}
 __device__ __forceinline__ void store_chunks_spread(const FusedArgs& a, int u0, const int* s_pos,
                                                     const uint4* s_codes, const u32* s_sc) {
-  const int K = a.g.k, k = a.topk, ul = a.upw_log;
-  const int units = a.g.m * (K >> 4), cpr = K >> 4;
-  const u32 row_bytes = a.fp4 ? (u32)K >> 1 : (u32)K;
-  const u32 kscale = (u32)K >> 5;
-  const int items = k << ul;
-#pragma unroll 2
-  for (int it = threadIdx.x; it < items; it += 256) {
-    const int us = it & ((1 << ul) - 1), j = it >> ul;
-    const int unit = u0 + us;
-    if (unit < units) {
-      const int t = div_magic(unit, a.cpr_magic), c = unit - t * cpr;
-      const u32 r = (u32)s_pos[t * k + j];
-      const uint4 cd = s_codes[us];
-      uint8_t* row = a.a_q + (u64)r * row_bytes;
-      if (a.fp4) *reinterpret_cast<uint2*>(row + 8 * c) = make_uint2(cd.x, cd.y);
-      else *reinterpret_cast<uint4*>(row + 16 * c) = cd;
-      if ((c & 7) == 0) *reinterpret_cast<u32*>(a.a_scale + (u64)r * kscale + (c >> 1)) = s_sc[us];
-    }
+  const int k = a.topk, ul = a.upw_log;
+  const int cpr = a.g.k >> 4, units = a.g.m * cpr;
+  const int us = (int)threadIdx.x & ((1 << ul) - 1);
+  const int j0 = (int)threadIdx.x >> ul, js = 256 >> ul;  // js = 4, 2 or 1
+  const int unit = u0 + us;
+  if (unit >= units || j0 >= k) return;
+  const int t = div_magic(unit, a.cpr_magic), c = unit - t * cpr;
+  const uint4 cd = s_codes[us];
+  const u32 sc = s_sc[us];
+  const int jn = (k - j0 + js - 1) / js;  // this thread's pairs
+  if (a.fp4) {
+    if (jn <= 2) store_chunk_rows<2, true>(a, t, c, j0, js, s_pos, cd, sc);
+    else if (jn <= 4) store_chunk_rows<4, true>(a, t, c, j0, js, s_pos, cd, sc);
+    else if (jn <= 8) store_chunk_rows<8, true>(a, t, c, j0, js, s_pos, cd, sc);
+    else store_chunk_rows<32, true>(a, t, c, j0, js, s_pos, cd, sc);
+  } else {
+    if (jn <= 2) store_chunk_rows<2, false>(a, t, c, j0, js, s_pos, cd, sc);
+    else if (jn <= 4) store_chunk_rows<4, false>(a, t, c, j0, js, s_pos, cd, sc);
+    else if (jn <= 8) store_chunk_rows<8, false>(a, t, c, j0, js, s_pos, cd, sc);
+    else store_chunk_rows<32, false>(a, t, c, j0, js, s_pos, cd, sc);
   }
 }
 
@@ -579,7 +613,9 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
   int slot[NV];
   u32 key[NV];
   if (row < m) {
-    row_topk_owner<NV>(a, s_log + row * n, bv, sel, slot, key, s_flag);
+    // quant-only workgroups need the selected set, not the slots: their
+    // positions are indexed by winner order, the same k rows either way
+    row_topk_owner<NV>(a, s_log + row * n, bv, sel, slot, key, s_flag, gate_here || layout_here);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const u64 mk = ballot64(sel[i]);
@@ -718,7 +754,6 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
   }
   __syncthreads();  // s_pos, the chunks and the masks complete
   RGT_STAMP(a.trace, 8);
-  RGT_STAMP(a.trace, 3);
   if (quant_wg) store_chunks_spread(a, (int)blockIdx.x << a.upw_log, s_pos, s_codes, s_sc);
   RGT_STAMP(a.trace, 9);
   if (gate_here && row < m) {  // the gate workgroup had no spare of its own

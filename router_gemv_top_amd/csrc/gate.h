@@ -214,19 +214,14 @@ __device__ __forceinline__ bool select_fast_sorted(const u32 (&key)[NV], int k, 
 // T that exactly k keys reach. (Measured slower: two bits a step with three
 // candidates counted at once, and skipping candidates above the largest key;
 // the wave issues one instruction at a time, and the compiler turns either
-// into a loop with more branches and selects than the steps they save.) Without such a T (equal keys straddle the k-th
-// place) T ends as the k-th largest key: every key above it is selected, and
-// of the keys equal to it the ones with the lowest expert index, as many as
-// are missing. The winners' slots (the number of selected keys that rank
-// above, by key, then expert index) come from one compare against the k
-// selected keys, compacted in expert order through s_c (KMAX u64 of LDS
-// owned by the calling wave; k <= KMAX). Lane-local results: sel[i] and, for
-// a selected key, slot[i].
-template <int NV, int KMAX>
-__device__ __forceinline__ void wave_topk_threshold(const u32 (&key)[NV], int k, bool (&sel)[NV], int (&slot)[NV],
-                                                    u64* s_c) {
+// into a loop with more branches and selects than the steps they save.)
+// Without such a T (equal keys straddle the k-th place) T ends as the k-th
+// largest key: every key above it is selected, and of the keys equal to it
+// the ones with the lowest expert index, as many as are missing. Lane-local
+// result: sel[i].
+template <int NV>
+__device__ __forceinline__ void wave_threshold_select(const u32 (&key)[NV], int k, bool (&sel)[NV]) {
   static_assert(NV <= 4, "the threshold selection takes up to four keys per lane");
-  const int lane = lane_id();
   u32 T = 0;
   bool exact = false;
   for (int b = 31; b >= 0; --b) {
@@ -261,19 +256,41 @@ __device__ __forceinline__ void wave_topk_threshold(const u32 (&key)[NV], int k,
       run += eq ? 1 : 0;
     }
   }
-  // compaction in expert order: position = selected keys of lower lanes, then
-  // of lower slots of this lane
+}
+
+// Position of each selected key in expert order among the selected ones
+// (selected keys of lower lanes, then of lower slots of this lane): a
+// one-to-one map of the selection onto 0 .. k-1, for callers to which the
+// order of the k winners does not matter.
+template <int NV>
+__device__ __forceinline__ void wave_select_order(const bool (&sel)[NV], int (&pos)[NV]) {
   int cpos = 0;
 #pragma unroll
   for (int i = 0; i < NV; ++i) cpos += __popcll(ballot64(sel[i]) & lanemask_lt());
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    pos[i] = cpos;
+    cpos += sel[i] ? 1 : 0;
+  }
+}
+
+// The winners' slots (the number of selected keys that rank above, by key,
+// then expert index) from one compare against the k selected keys, compacted
+// in expert order through s_c (KMAX u64 of LDS owned by the calling wave;
+// k <= KMAX). Lane-local: for a selected key, slot[i].
+template <int NV, int KMAX>
+__device__ __forceinline__ void wave_select_slots(const u32 (&key)[NV], const bool (&sel)[NV], int (&slot)[NV],
+                                                  u64* s_c) {
+  const int lane = lane_id();
+  int cpos[NV];
+  wave_select_order<NV>(sel, cpos);
   u64 comp[NV];
   if (lane < KMAX) s_c[lane] = 0ull;  // entries past k never rank above anything
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     // key first; among equal keys the lower expert (lower position) ranks higher
-    comp[i] = ((u64)key[i] << 32) | (u64)(~(u32)cpos);
-    if (sel[i]) s_c[cpos] = comp[i];
-    cpos += sel[i] ? 1 : 0;
+    comp[i] = ((u64)key[i] << 32) | (u64)(~(u32)cpos[i]);
+    if (sel[i]) s_c[cpos[i]] = comp[i];
   }
   // one wave: its LDS writes above land before these reads
   int cntv[NV];
@@ -287,6 +304,14 @@ __device__ __forceinline__ void wave_topk_threshold(const u32 (&key)[NV], int k,
   }
 #pragma unroll
   for (int i = 0; i < NV; ++i) slot[i] = cntv[i];
+}
+
+// Selection and slots together (k <= KMAX).
+template <int NV, int KMAX>
+__device__ __forceinline__ void wave_topk_threshold(const u32 (&key)[NV], int k, bool (&sel)[NV], int (&slot)[NV],
+                                                    u64* s_c) {
+  wave_threshold_select<NV>(key, k, sel);
+  wave_select_slots<NV, KMAX>(key, sel, slot, s_c);
 }
 
 // Selection only for R rows at once (R = 1 or 2): lane j < k ends with the
