@@ -198,6 +198,21 @@ __device__ __forceinline__ u64 ld_agent(const u64* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// A kernel argument read from the kernarg segment where it is used. For
+// values only the end of a kernel needs, in kernels whose arguments exceed
+// the scalar register budget: loaded at the start, they are spilled to
+// vector lanes and restored as a whole 16-register group before each use
+// (16 v_readlane a store). The empty asm makes the segment pointer opaque,
+// so the load stays where it is written (a scalar load, normally a hit in
+// the scalar cache). off: the byte offset of the value in the segment.
+template <class T>
+__device__ __forceinline__ T kernarg_at(unsigned off) {
+  typedef const __attribute__((address_space(4))) char* seg_ptr;
+  seg_ptr p = (seg_ptr)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(p));
+  return *(const __attribute__((address_space(4))) T*)(p + off);
+}
+
 // Tagged words: a 32-bit payload and the 32-bit tag of the call that wrote
 // it, stored and loaded as one 8-byte atomic. A reader polls the word itself
 // until the tag is its own call's, so data and "ready" arrive together and no

@@ -107,6 +107,10 @@ struct FusedArgs {
   u64* trs;            // [M] tagged rstd words (workspace, after tids)
 };
 
+// An output pointer of the call, read from the kernel's argument block where
+// the tail uses it (the kernels take FusedArgs as their only argument).
+#define RGT_OUT(field) ::rgt::kernarg_at<decltype(::rgt::FusedArgs::field)>(offsetof(::rgt::FusedArgs, field))
+
 // The call's tag from the epoch word: epoch + 1, skipping 0 so zero-filled
 // words never look ready. The control words stay per-lane values (every lane
 // loads the same words): moving them to scalar registers would make the wave
@@ -483,9 +487,10 @@ __device__ __forceinline__ void row_topk(const FusedArgs& a, const float* row, c
 // selected keys in s_key (one wave per row at a time).
 __device__ __forceinline__ void rows_weights(const FusedArgs& a, const u32* s_key, int r0, int step) {
   const int k = a.topk, lane = lane_id();
+  float* const topk_w = RGT_OUT(topk_w);
   for (int row = r0; row < a.g.m; row += step) {
     const float w = wave_weights(s_key[row * k + min(lane, k - 1)], k);
-    if (lane < k) a.topk_w[row * k + lane] = w;
+    if (lane < k) topk_w[row * k + lane] = w;
   }
 }
 
@@ -508,11 +513,14 @@ __device__ __forceinline__ void scrub_window(const FusedArgs& a, u32 tag) {
 // (a padded total of 0: no row of the sort outputs is valid).
 __device__ __forceinline__ void write_poison(const FusedArgs& a) {
   const int P = a.g.m * a.topk;
+  int32_t* const topk_ids = RGT_OUT(topk_ids);
+  float* const topk_w = RGT_OUT(topk_w);
+  int32_t* const offsets = RGT_OUT(offsets);
   for (int i = threadIdx.x; i < P; i += 256) {
-    a.topk_ids[i] = -1;
-    a.topk_w[i] = 0.f;
+    topk_ids[i] = -1;
+    topk_w[i] = 0.f;
   }
-  for (int e = threadIdx.x; e <= a.g.n; e += 256) a.offsets[e] = 0;
+  for (int e = threadIdx.x; e <= a.g.n; e += 256) offsets[e] = 0;
 }
 
 // pos(p) of 64-bit lane masks: the set bits of mask below the calling lane.
@@ -538,12 +546,13 @@ __device__ __forceinline__ void store_chunk_rows(const FusedArgs& a, int t, int 
   const int k = a.topk;
   const u32 row_bytes = FP4 ? (u32)a.g.k >> 1 : (u32)a.g.k;
   const u32 kscale = (u32)a.g.k >> 5;
-  uint8_t* q_col = a.a_q + (FP4 ? 8 * c : 16 * c);
-  uint8_t* s_col = a.a_scale + (c >> 1);
+  uint8_t* q_col = RGT_OUT(a_q) + (FP4 ? 8 * c : 16 * c);
+  uint8_t* s_col = RGT_OUT(a_scale) + (c >> 1);
   const bool lead = (c & 7) == 0;
   int r[JN];
 #pragma unroll
   for (int i = 0; i < JN; ++i) r[i] = s_pos[t * k + min(j0 + i * js, k - 1)];
+  // (Write-through stores, agent-scope or non-temporal, measured no faster.)
 #pragma unroll
   for (int i = 0; i < JN; ++i) {
     if (j0 + i * js < k) {
@@ -588,9 +597,14 @@ __device__ __forceinline__ void store_chunks_spread(const FusedArgs& a, int u0, 
 // masks (one ballot per key slot), so the sort needs no histogram and no
 // scan. The gate workgroup writes topk_ids, the weights, the logits and the
 // epoch; the layout workgroup writes offsets, expert_ids and sorted_ids
-// (pairs and pads); the quant workgroups store their chunks.
+// (pairs and pads); the quant workgroups store their chunks. With one row
+// the pairs' padded rows are 0, B, ..., (k-1)B whichever experts win (the
+// row's pair is the first row of each of the k blocks): the quant-only
+// workgroups store at once, with no gather and no gate, and the gate
+// workgroup, which has the slots, writes the pairs' sorted_ids entries, so
+// the layout workgroup needs only the selected set.
 template <int NV, class Quant>
-__device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 tag, bool have_unit, int unit,
+__device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 tag, int role, bool have_unit, int unit,
                                            Quant&& quant, const float (&bv)[NV], bool gate_here, bool layout_here,
                                            bool quant_wg) {
   __shared__ __align__(16) u64 s_mask[4][NV];
@@ -603,9 +617,29 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
   float* s_log = reinterpret_cast<float*>(smem + fused_log_offset(P, n));
   const int stage = fused_gather_staged(m, n, g.s_count) ? (g.s_count - 1) * m * n : 0;
   int* s_flag = smem + fused_tail_ints(P, n, m) + stage + wave * n;  // above four experts a lane only
-  // the thread's quant chunk is encoded while the first poll is in flight
+  // the chunks go to LDS so that all four waves store them
+  __shared__ uint4 s_codes[256];
+  __shared__ u32 s_sc[256];
   u32 sb_in = 0;
   uint4 codes_in = make_uint4(0, 0, 0, 0);
+  if (m == 1 && quant_wg && !gate_here && !layout_here) {
+    codes_in = quant(sb_in);
+    const u32 scales4 = pack_scales(sb_in);  // all lanes: DPP reads neighbouring lanes
+    if (have_unit) {
+      s_codes[threadIdx.x] = codes_in;
+      s_sc[threadIdx.x] = scales4;
+    }
+    if ((int)threadIdx.x < k) s_pos[threadIdx.x] = (int)threadIdx.x * B;
+    __syncthreads();
+    RGT_STAMP(a.trace, 8);
+    store_chunks_spread(a, role << a.upw_log, s_pos, s_codes, s_sc);
+#ifdef RGT_TRACE
+    vm_drain();  // the stores acknowledged
+    RGT_STAMP(a.trace, 2);
+#endif
+    return;
+  }
+  // the thread's quant chunk is encoded while the first poll is in flight
   if (!gather_any(a, 0, m, tag, s_log, [&] { codes_in = quant(sb_in); })) return;
   RGT_STAMP(a.trace, 5);
   const int row = wave;
@@ -613,21 +647,32 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
   int slot[NV];
   u32 key[NV];
   if (row < m) {
-    // quant-only workgroups need the selected set, not the slots: their
-    // positions are indexed by winner order, the same k rows either way
-    row_topk_owner<NV>(a, s_log + row * n, bv, sel, slot, key, s_flag, gate_here || layout_here);
+    // quant-only workgroups (and the layout workgroup of one row) need the
+    // selected set, not the slots: their positions are indexed by winner
+    // order, the same k rows either way
+    row_topk_owner<NV>(a, s_log + row * n, bv, sel, slot, key, s_flag, gate_here || (layout_here && m > 1));
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const u64 mk = ballot64(sel[i]);
       if (m > 1 && lane == 0) s_mask[row][i] = mk;
     }
     if (gate_here) {
+      int32_t* const topk_ids = RGT_OUT(topk_ids);
 #pragma unroll
       for (int i = 0; i < NV; ++i)
         if (sel[i]) {
-          a.topk_ids[row * k + slot[i]] = c0 + i;
+          topk_ids[row * k + slot[i]] = c0 + i;
           s_key[row * k + slot[i]] = key[i];
         }
+      if (m == 1) {
+        // the pair of winner j (expert order) sits at row j * B
+        int32_t* const sorted_ids = RGT_OUT(sorted_ids);
+        int ord[NV];
+        wave_select_order<NV>(sel, ord);
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+          if (sel[i]) sorted_ids[ord[i] * B] = slot[i];
+      }
     }
   } else {
 #pragma unroll
@@ -636,8 +681,11 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
       slot[i] = 0;
     }
   }
-  if (gate_here && a.logits_out)
-    for (int i = threadIdx.x; i < m * n; i += 256) a.logits_out[i] = s_log[i];
+  if (gate_here) {
+    float* const logits_out = RGT_OUT(logits_out);
+    if (logits_out)
+      for (int i = threadIdx.x; i < m * n; i += 256) logits_out[i] = s_log[i];
+  }
   // (one row: wave 0 holds everything the positions need, no barrier here)
   if (m > 1) __syncthreads();
   RGT_STAMP(a.trace, 14);
@@ -647,7 +695,7 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
     if (!quant_wg && !layout_here) {
       if (row < m) {
         const float w = wave_weights(s_key[row * k + min(lane, k - 1)], k);
-        if (lane < k) a.topk_w[row * k + lane] = w;
+        if (lane < k) RGT_OUT(topk_w)[row * k + lane] = w;
       }
       return;
     }
@@ -710,43 +758,43 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
       masks_lds(mr);
     }
     const Seg sg = seg_of(mr);
+    int32_t* const sorted_ids = layout_here ? RGT_OUT(sorted_ids) : nullptr;
     if (row < m) {
 #pragma unroll
       for (int i = 0; i < NV; ++i)
         if (sel[i]) {
           const int q = sg.blk[i] * B + sg.rk[i];
           s_pos[row * k + slot[i]] = q;
-          if (layout_here) a.sorted_ids[q] = row * k + slot[i];
+          if (layout_here && m > 1) sorted_ids[q] = row * k + slot[i];
         }
     }
     RGT_STAMP(a.trace, 6);
     if (layout_here) {
       if (wave == 0) {
+        int32_t* const offsets = RGT_OUT(offsets);
+        int32_t* const expert_ids = RGT_OUT(expert_ids);
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-          if (c0 + i < n) a.offsets[c0 + i] = sg.blk[i] * B;
-          if (sg.present[i]) a.expert_ids[sg.blk[i]] = c0 + i;
+          if (c0 + i < n) offsets[c0 + i] = sg.blk[i] * B;
+          if (sg.present[i]) expert_ids[sg.blk[i]] = c0 + i;
         }
-        if (lane == 0) a.offsets[n] = sg.total * B;
+        if (lane == 0) offsets[n] = sg.total * B;
       }
       if (m == 1) {
         // every block holds one pair (its first row) and B - 1 pads: the
         // rows below k * B that are not a multiple of B (wave 0 alone)
         for (int q = lane; q < sg.total * B; q += 64)
-          if (q & (B - 1)) a.sorted_ids[q] = P;
+          if (q & (B - 1)) sorted_ids[q] = P;
       } else {
         // the four waves split the pads
 #pragma unroll
         for (int i = 0; i < NV; ++i)
           if (sg.present[i])
-            for (int q = sg.cnt[i] + wave; q < B; q += 4) a.sorted_ids[sg.blk[i] * B + q] = P;
+            for (int q = sg.cnt[i] + wave; q < B; q += 4) sorted_ids[sg.blk[i] * B + q] = P;
       }
       RGT_STAMP(a.trace, 7);
     }
   }
-  // the chunks go to LDS so that all four waves store them
-  __shared__ uint4 s_codes[256];
-  __shared__ u32 s_sc[256];
   const u32 scales4 = pack_scales(sb_in);  // all lanes: DPP reads neighbouring lanes
   if (have_unit) {
     s_codes[threadIdx.x] = codes_in;
@@ -754,11 +802,11 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
   }
   __syncthreads();  // s_pos, the chunks and the masks complete
   RGT_STAMP(a.trace, 8);
-  if (quant_wg) store_chunks_spread(a, (int)blockIdx.x << a.upw_log, s_pos, s_codes, s_sc);
+  if (quant_wg) store_chunks_spread(a, role << a.upw_log, s_pos, s_codes, s_sc);
   RGT_STAMP(a.trace, 9);
   if (gate_here && row < m) {  // the gate workgroup had no spare of its own
     const float w = wave_weights(s_key[row * k + min(lane, k - 1)], k);
-    if (lane < k) a.topk_w[row * k + lane] = w;
+    if (lane < k) RGT_OUT(topk_w)[row * k + lane] = w;
   }
   if (layout_here) scrub_window(a, tag);
 #ifdef RGT_TRACE
@@ -770,8 +818,8 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
 // quant(sb) returns the thread's encoded quant chunk and its scale byte(s);
 // every lane of a wave calls it together.
 template <int NV, class Quant>
-__device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 tag, bool poisoned, bool have_unit,
-                                           int unit, Quant&& quant, const float (&bv)[NV]) {
+__device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 tag, bool poisoned, int role,
+                                           bool have_unit, int unit, Quant&& quant, const float (&bv)[NV]) {
   const GemvArgs& g = a.g;
   const int m = g.m, n = g.n, k = a.topk;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -785,23 +833,23 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
   const int q_wgs = ((units - 1) >> a.upw_log) + 1;
   const int n_layout = (n + 255) >> 8;
   const int layout_wg = min((int)gridDim.x - n_layout, q_wgs);
-  const int li = (int)blockIdx.x - layout_wg;  // this workgroup's layout share, if 0 <= li < n_layout
+  const int li = role - layout_wg;  // this workgroup's layout share, if 0 <= li < n_layout
   const int spare0 = layout_wg + n_layout;
   const int gate_wg = (a.small && spare0 < (int)gridDim.x) ? spare0 : 0;
-  const bool gate_here = (int)blockIdx.x == gate_wg;
-  const bool quant_wg = (int)blockIdx.x < q_wgs;
+  const bool gate_here = role == gate_wg;
+  const bool quant_wg = role < q_wgs;
   const bool layout_here = li >= 0 && li < n_layout;
   const bool participant = gate_here || quant_wg || layout_here;
   const int P = m * k;
   if (poisoned) {
     // An earlier wait of this workspace expired: no waits, defined outputs.
-    if ((int)blockIdx.x == layout_wg) write_poison(a);
+    if (role == layout_wg) write_poison(a);
     return;
   }
   if (a.small) {
     // one layout workgroup writes the whole layout in small mode
     if (!(gate_here || quant_wg || li == 0)) return;
-    small_tail<NV>(a, smem, tag, have_unit, unit, quant, bv, gate_here, li == 0, quant_wg);
+    small_tail<NV>(a, smem, tag, role, have_unit, unit, quant, bv, gate_here, li == 0, quant_wg);
     return;
   }
   u32 sb_in = 0;
@@ -815,7 +863,7 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
   float* s_log = reinterpret_cast<float*>(smem + fused_log_offset(P, n));
   // This workgroup's tokens (those its quant units touch) and their pairs.
   const int cpr = g.k >> 4;
-  const int u0 = (int)blockIdx.x << a.upw_log;
+  const int u0 = role << a.upw_log;
   const int t0 = min(m, div_magic(u0, a.cpr_magic)), t1 = min(m, div_magic(u0 + (1 << a.upw_log) - 1, a.cpr_magic) + 1);
   const int p0 = u0 < units ? t0 * k : 0, p1 = u0 < units ? t1 * k : 0;
   // The expert histograms are filled as the ids become known (zeroed here;
@@ -829,26 +877,28 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
     // Step 2 (large): row workgroups gather their row, run its gate and
     // publish the ids; then every participant polls all ids.
     const int row_wg0 = spare0 + m <= (int)gridDim.x ? spare0 : 0;
-    const int row = (int)blockIdx.x - row_wg0;
+    const int row = role - row_wg0;
     if (row >= 0 && row < m) {
       if (!gather_any(a, row, 1, tag, s_log)) return;
       RGT_STAMP(a.trace, 5);
       if (wave == 0) {
         // (s_key is free in large mode: its first k entries hold the row's
         // keys in slot order for the weights)
+        int32_t* const topk_ids = RGT_OUT(topk_ids);
         row_topk<NV>(a, s_log, bv, [&](int j, int e, u32 key) {
           st_agent(a.tids + row * k + j, tag_word((u32)e, tag));
-          a.topk_ids[row * k + j] = e;
+          topk_ids[row * k + j] = e;
           s_key[j] = key;
         });
         // the pad word of an odd pair count: every word of the call's
         // footprint carries its tag
         if (row == m - 1 && lane == 0 && (P & 1)) st_agent(a.tids + P, tag_word(0u, tag));
         const float w = wave_weights(s_key[min(lane, k - 1)], k);  // after the ids are published
-        if (lane < k) a.topk_w[row * k + lane] = w;
+        if (lane < k) RGT_OUT(topk_w)[row * k + lane] = w;
       }
-      if (a.logits_out)
-        for (int i = threadIdx.x; i < n; i += 256) a.logits_out[(int64_t)row * n + i] = s_log[i];
+      float* const logits_out = RGT_OUT(logits_out);
+      if (logits_out)
+        for (int i = threadIdx.x; i < n; i += 256) logits_out[(int64_t)row * n + i] = s_log[i];
       RGT_STAMP(a.trace, 6);
     }
     if (!participant) return;
@@ -867,18 +917,20 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
   if (threadIdx.x < 64) pair_positions<NV>(P, n, a.block, p0, p1, s_e, s_cnt, s_pre, s_off, s_pos);
   __syncthreads();
   RGT_STAMP(a.trace, 8);
+  int32_t* const sorted_ids = RGT_OUT(sorted_ids);
   if (layout_here)
-    write_layout<256>(s_cnt, s_off, n, a.block, P, li << 8, min(n, (li + 1) << 8), a.sorted_ids, a.expert_ids,
-                      a.offsets);
+    write_layout<256>(s_cnt, s_off, n, a.block, P, li << 8, min(n, (li + 1) << 8), sorted_ids,
+                      RGT_OUT(expert_ids), RGT_OUT(offsets));
   if ((int)threadIdx.x < p1 - p0) {
     const int p = p0 + threadIdx.x, q = s_pos[threadIdx.x];
     const int tok = p / k;
-    if (q >= 0 && (tok * cpr) >> a.upw_log == (int)blockIdx.x) a.sorted_ids[q] = p;
+    if (q >= 0 && (tok * cpr) >> a.upw_log == role) sorted_ids[q] = p;
   }
   RGT_STAMP(a.trace, 3);
   const u32 scales4 = pack_scales(sb_in);  // all lanes: DPP reads neighbouring lanes
-  if (have_unit) store_unit(a.a_q, a.a_scale, g.k, k, unit, OffsetPos{s_pos, p0}, codes_in, scales4, a.cpr_magic,
-                             a.fp4 != 0);
+  if (have_unit)
+    store_unit(RGT_OUT(a_q), RGT_OUT(a_scale), g.k, k, unit, OffsetPos{s_pos, p0}, codes_in, scales4, a.cpr_magic,
+               a.fp4 != 0);
   RGT_STAMP(a.trace, 9);
   if (li == 0) scrub_window(a, tag);
 #ifdef RGT_TRACE
@@ -908,15 +960,16 @@ struct NormX {
   const u32& tag;  // the wave's control words, read by prefetch before row_work
   u32& err;
   float& rs_own;   // the rstd this workgroup took (its norm row's)
+  const int role;  // the workgroup's role index (see fused_body)
   uint4 hv[kNormChunks];
   uint4 rv[kNormChunks];
 
-  __device__ __forceinline__ NormX(const FusedArgs& args, const u32& t, u32& e, float& r)
-      : a(args), tag(t), err(e), rs_own(r) {}
+  __device__ __forceinline__ NormX(const FusedArgs& args, const u32& t, u32& e, float& r, int ro)
+      : a(args), tag(t), err(e), rs_own(r), role(ro) {}
 
   __device__ __forceinline__ bool local() const { return a.g.m == 1; }
-  __device__ __forceinline__ bool norm_wg() const { return local() || (int)blockIdx.x < a.g.m; }
-  __device__ __forceinline__ int norm_row() const { return local() ? 0 : (int)blockIdx.x; }
+  __device__ __forceinline__ bool norm_wg() const { return local() || role < a.g.m; }
+  __device__ __forceinline__ int norm_row() const { return local() ? 0 : role; }
 
   // Before the tile's loads: the norm row's x and residual.
   __device__ __forceinline__ void begin() {
@@ -944,12 +997,12 @@ struct NormX {
     rs_own = rs;
     if (threadIdx.x == 0) {
       if (!local() && !a.fault_skip && err == 0u) {
-        st_agent(a.trs + blockIdx.x, tag_word(__float_as_uint(rs), tag));
+        st_agent(a.trs + role, tag_word(__float_as_uint(rs), tag));
         // the pad word of an odd M: every word of the call's footprint
         // carries its tag
-        if ((int)blockIdx.x == a.g.m - 1 && (a.g.m & 1)) st_agent(a.trs + a.g.m, tag_word(0u, tag));
+        if (role == a.g.m - 1 && (a.g.m & 1)) st_agent(a.trs + a.g.m, tag_word(0u, tag));
       }
-      if (a.rstd_out && (int)blockIdx.x < a.g.m) a.rstd_out[blockIdx.x] = rs;
+      if (a.rstd_out && role < a.g.m) a.rstd_out[role] = rs;
     }
     RGT_STAMP(a.trace, 11);
   }
@@ -1043,9 +1096,16 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, Tile t
   __shared__ u32 s_ctl[2];
   const GemvArgs& g = a.g;
   const int units = g.m * (g.k >> 4);
-  const int unit = ((int)blockIdx.x << a.upw_log) + threadIdx.x;
-  const bool have_unit = (int)threadIdx.x < (1 << a.upw_log) && unit < units;
+  // The workgroup's place among the quant, layout, gate, row and norm
+  // workgroups: its block index, so the tail's workgroups spread over the
+  // XCDs (block b runs on XCD b % 8). (The XCDs' first workgroups start up to
+  // ~0.55 us apart, XCD 0 first; placing the tail's roles on the first XCDs
+  // instead, all on XCD 0 or spread over XCDs 0-3, measured slower at one
+  // and at 64 rows, faster at 8-16, +-0.1-0.4 us.)
+  const int role = (int)blockIdx.x;
   const int tile_id = xcd_tile(blockIdx.x, gridDim.x);
+  const int unit = (role << a.upw_log) + threadIdx.x;
+  const bool have_unit = (int)threadIdx.x < (1 << a.upw_log) && unit < units;
   RGT_STAMP(a.trace, 0);
   // Right after the tile's W loads are issued: the control words (loads
   // return in order, so issued earlier they would hold up the tile's
@@ -1089,7 +1149,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, Tile t
   };
   [[maybe_unused]] float rs_own = 0.f;
   if constexpr (NORM) {
-    NormX xf(a, tag, err, rs_own);
+    NormX xf(a, tag, err, rs_own, role);
     xf.begin();
     tile(tile_id, sink, prefetch, xf);
   } else {
@@ -1116,7 +1176,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, Tile t
     }
     return mx_quant16_fmt(c0, c1, sb, a.fp4 != 0);
   };
-  fused_tail<NV>(a, smem, tag, err != 0u, have_unit, unit, quant, bv);
+  fused_tail<NV>(a, smem, tag, err != 0u, role, have_unit, unit, quant, bv);
 }
 
 // Quant units (16-element chunks of x, row-major) go 2^upw_log to a
