@@ -222,6 +222,55 @@ __device__ __forceinline__ bool gather_logits(const FusedArgs& a, int r0, int ro
   return s_bad == 0u;
 }
 
+// One row of 128 experts gathered by the calling wave alone (no LDS, no
+// barrier): lane l polls the k-slices of column pair l (NL >= S loads, the
+// ones past S repeat the last slice) and sums them in k-slice order, the
+// same bits as gather_logits. false (error word set) if the deadline passes.
+template <int NL>
+__device__ __forceinline__ bool wave_gather_pairs(const FusedArgs& a, u32 tag, float (&sv)[2]) {
+  const int S = a.g.s_count;
+  const u32 slice = (u32)a.g.m * (u32)a.g.n * 8u;
+  const auto rsrc = coherent_rsrc(a.tpart, slice * (u32)S);
+  const u32 base = 16u * (u32)lane_id();
+  u32x4_t v[NL];
+  auto issue = [&] {
+#pragma unroll
+    for (int l = 0; l < NL; ++l) v[l] = ld_agent16(rsrc, base + (u32)min(l, S - 1) * slice);
+  };
+  auto ready = [&] {
+    bool ok = true;
+#pragma unroll
+    for (int l = 0; l < NL; ++l) ok = ok & (v[l].y == tag) & (v[l].w == tag);
+    return ok;
+  };
+  const u64 t0 = rt_clock();
+  issue();
+  RGT_STAMP(a.trace, 11);
+  bool ok = true;
+  for (;;) {
+    if (ready()) {
+      float x0 = 0.f, x1 = 0.f;
+#pragma unroll
+      for (int l = 0; l < NL; ++l)
+        if (l < S) {
+          x0 += __uint_as_float(v[l].x);
+          x1 += __uint_as_float(v[l].z);
+        }
+      sv[0] = x0;
+      sv[1] = x1;
+      break;
+    }
+    issue();
+    if (rt_clock() - t0 > a.budget) {
+      set_timeout(a);
+      ok = false;
+      break;
+    }
+  }
+  RGT_STAMP(a.trace, 15);
+  return ballot64(!ok) == 0ull;
+}
+
 // Loads per thread that a gather of `rows` rows needs.
 __host__ __device__ constexpr int gather_loads(int rows, int n, int s) { return (rows * (n / 2) + 255) / 256 * s; }
 
@@ -394,13 +443,10 @@ __device__ __forceinline__ bool poll_ids_any(const FusedArgs& a, int P, u32 tag,
 // (a caller that only needs the selected set, one position per winner) the
 // threshold selection numbers the winners in expert order instead of by rank.
 template <int NV>
-__device__ __forceinline__ void row_topk_owner(const FusedArgs& a, const float* row, const float (&bv)[NV],
+__device__ __forceinline__ void row_topk_owner(const FusedArgs& a, float (&sv)[NV], const float (&bv)[NV],
                                                bool (&sel)[NV], int (&slot)[NV], u32 (&key)[NV], int* s_flag,
                                                bool slots) {
   const int n = a.g.n, k = a.topk, lane = lane_id(), c0 = lane * NV;
-  float sv[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) sv[i] = row[min(c0 + i, n - 1)];
   if (a.bias) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) sv[i] = __fadd_rn(sv[i], bv[i]);
@@ -436,6 +482,16 @@ __device__ __forceinline__ void row_topk_owner(const FusedArgs& a, const float* 
     }
   }
   RGT_STAMP(a.trace, 13);
+}
+template <int NV>
+__device__ __forceinline__ void row_topk_owner(const FusedArgs& a, const float* row, const float (&bv)[NV],
+                                               bool (&sel)[NV], int (&slot)[NV], u32 (&key)[NV], int* s_flag,
+                                               bool slots) {
+  const int n = a.g.n, c0 = lane_id() * NV;
+  float sv[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) sv[i] = row[min(c0 + i, n - 1)];
+  row_topk_owner<NV>(a, sv, bv, sel, slot, key, s_flag, slots);
 }
 
 // The top-k of one row of logits held in LDS, by the calling wave: scores
@@ -499,13 +555,15 @@ __device__ __forceinline__ void rows_weights(const FusedArgs& a, const u32* s_ke
 // the window skips), so that over a sweep of a few hundred calls every word
 // outside the current footprint is rewritten. Tags repeat only after 2^32 - 1
 // calls, so no word can keep a tag that long and be mistaken for a fresh one.
-__device__ __forceinline__ void scrub_window(const FusedArgs& a, u32 tag) {
+// Threads t0, t0 + nt, ... take its 256 units.
+__device__ __forceinline__ void scrub_window(const FusedArgs& a, u32 tag, u32 t0 = threadIdx.x, u32 nt = 256u) {
   const u32 units = a.scrub_units;
-  const u32 t = threadIdx.x;
   const u32 first = (u32)(((u64)tag * 256u) % units);
-  const u32 i = first + t >= units ? first + t - units : first + t;
-  const bool in_fp = (i >= a.fp_part0 && i < a.fp_part1) || (i >= a.fp_ids0 && i < a.fp_ids1);
-  if (t < units && !in_fp) reinterpret_cast<uint4*>(a.scrub)[i] = make_uint4(0, 0, 0, 0);
+  for (u32 t = t0; t < 256u; t += nt) {
+    const u32 i = first + t >= units ? first + t - units : first + t;
+    const bool in_fp = (i >= a.fp_part0 && i < a.fp_part1) || (i >= a.fp_ids0 && i < a.fp_ids1);
+    if (t < units && !in_fp) reinterpret_cast<uint4*>(a.scrub)[i] = make_uint4(0, 0, 0, 0);
+  }
 }
 
 // Outputs of a call made on a workspace whose error word is set (an earlier
@@ -599,11 +657,14 @@ __device__ __forceinline__ void store_chunks_spread(const FusedArgs& a, int u0, 
 // epoch; the layout workgroup writes offsets, expert_ids and sorted_ids
 // (pairs and pads); the quant workgroups store their chunks. With one row
 // the pairs' padded rows are 0, B, ..., (k-1)B whichever experts win (the
-// row's pair is the first row of each of the k blocks): the quant-only
-// workgroups store at once, with no gather and no gate, and the gate
+// row's pair is the first row of each of the k blocks), and the gate
 // workgroup, which has the slots, writes the pairs' sorted_ids entries, so
-// the layout workgroup needs only the selected set.
-template <int NV, class Quant>
+// the layout workgroup needs only the selected set. The instances built for
+// one row (ONE) go further: the quant-only workgroups store at once, with no
+// gather and no gate, and at 128 experts the gate and layout workgroups run
+// on one wave with no LDS pass or barrier. (Only there: the extra code costs
+// the other instances scalar-register spills, +0.4 us at two rows.)
+template <int NV, bool ONE, class Quant>
 __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 tag, int role, bool have_unit, int unit,
                                            Quant&& quant, const float (&bv)[NV], bool gate_here, bool layout_here,
                                            bool quant_wg) {
@@ -622,7 +683,7 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
   __shared__ u32 s_sc[256];
   u32 sb_in = 0;
   uint4 codes_in = make_uint4(0, 0, 0, 0);
-  if (m == 1 && quant_wg && !gate_here && !layout_here) {
+  if (ONE && m == 1 && quant_wg && !gate_here && !layout_here) {
     codes_in = quant(sb_in);
     const u32 scales4 = pack_scales(sb_in);  // all lanes: DPP reads neighbouring lanes
     if (have_unit) {
@@ -638,6 +699,70 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
     RGT_STAMP(a.trace, 2);
 #endif
     return;
+  }
+  if constexpr (ONE && NV == 2) {
+    if (m == 1 && n == 128 && !quant_wg && !fused_gather_staged(1, n, g.s_count)) {
+      // The gate or layout workgroup of one row of 128 experts: wave 0 alone
+      // (lane l holds experts 2l and 2l + 1, as its gather leaves them), with
+      // no LDS pass and no barrier; the other waves take the layout
+      // workgroup's scrub and end.
+      if (wave != 0) {
+        if (layout_here) scrub_window(a, tag, threadIdx.x - 64u, 192u);
+        return;
+      }
+      float sv[2];
+      const bool ok = g.s_count <= 4 ? wave_gather_pairs<4>(a, tag, sv) : wave_gather_pairs<8>(a, tag, sv);
+      if (!ok) return;
+      RGT_STAMP(a.trace, 5);
+      const float lg[2] = {sv[0], sv[1]};  // the logits (the gate adds the bias to sv)
+      bool sel[2];
+      int slot[2], ord[2];
+      u32 key[2];
+      row_topk_owner<2>(a, sv, bv, sel, slot, key, nullptr, gate_here);
+      wave_select_order<2>(sel, ord);  // winners below, = the block of each expert
+      RGT_STAMP(a.trace, 14);
+      if (gate_here) {
+        int32_t* const topk_ids = RGT_OUT(topk_ids);
+        int32_t* const sorted_ids = RGT_OUT(sorted_ids);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          if (sel[i]) {
+            topk_ids[slot[i]] = c0 + i;
+            s_key[slot[i]] = key[i];
+            sorted_ids[ord[i] * B] = slot[i];  // the pair of slot j leads its expert's block
+          }
+        float* const logits_out = RGT_OUT(logits_out);
+        if (logits_out) {
+          logits_out[c0] = lg[0];
+          logits_out[c0 + 1] = lg[1];
+        }
+        // every partial has been seen, so every workgroup's tag is read
+        if (lane == 0) st_agent(a.ctl + kCtlEpoch, tag);
+        const float w = wave_weights(s_key[min(lane, k - 1)], k);  // one wave: after its LDS writes
+        if (lane < k) RGT_OUT(topk_w)[lane] = w;
+      }
+      if (layout_here) {
+        // offsets: the k present experts fill one block each; the pads are
+        // the rows of the k blocks past their first
+        int32_t* const offsets = RGT_OUT(offsets);
+        int32_t* const expert_ids = RGT_OUT(expert_ids);
+        int32_t* const sorted_ids = RGT_OUT(sorted_ids);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          offsets[c0 + i] = ord[i] * B;
+          if (sel[i]) expert_ids[ord[i]] = c0 + i;
+        }
+        if (lane == 0) offsets[n] = k * B;
+        for (int q = lane; q < k * B; q += 64)
+          if (q & (B - 1)) sorted_ids[q] = P;
+        RGT_STAMP(a.trace, 7);
+      }
+#ifdef RGT_TRACE
+      vm_drain();  // the stores acknowledged
+      RGT_STAMP(a.trace, 2);
+#endif
+      return;
+    }
   }
   // the thread's quant chunk is encoded while the first poll is in flight
   if (!gather_any(a, 0, m, tag, s_log, [&] { codes_in = quant(sb_in); })) return;
@@ -817,7 +942,7 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
 
 // quant(sb) returns the thread's encoded quant chunk and its scale byte(s);
 // every lane of a wave calls it together.
-template <int NV, class Quant>
+template <int NV, bool ONE, class Quant>
 __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 tag, bool poisoned, int role,
                                            bool have_unit, int unit, Quant&& quant, const float (&bv)[NV]) {
   const GemvArgs& g = a.g;
@@ -849,7 +974,7 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
   if (a.small) {
     // one layout workgroup writes the whole layout in small mode
     if (!(gate_here || quant_wg || li == 0)) return;
-    small_tail<NV>(a, smem, tag, role, have_unit, unit, quant, bv, gate_here, li == 0, quant_wg);
+    small_tail<NV, ONE>(a, smem, tag, role, have_unit, unit, quant, bv, gate_here, li == 0, quant_wg);
     return;
   }
   u32 sb_in = 0;
@@ -1091,7 +1216,7 @@ __device__ __forceinline__ bool norm_unit(const FusedArgs& a, int unit, u32 tag,
 // Shared head of the kernels: read the control words, run the tile, then the
 // tail. tile(t, sink, pre, xf) computes this workgroup's GEMV tile; with NORM
 // the tile and the quant units read the RMSNorm of x (NormX).
-template <int NV, bool NORM, class Tile>
+template <int NV, bool NORM, bool ONE, class Tile>
 __device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, Tile tile) {
   __shared__ u32 s_ctl[2];
   const GemvArgs& g = a.g;
@@ -1176,7 +1301,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, Tile t
     }
     return mx_quant16_fmt(c0, c1, sb, a.fp4 != 0);
   };
-  fused_tail<NV>(a, smem, tag, err != 0u, role, have_unit, unit, quant, bv);
+  fused_tail<NV, ONE>(a, smem, tag, err != 0u, role, have_unit, unit, quant, bv);
 }
 
 // Quant units (16-element chunks of x, row-major) go 2^upw_log to a
@@ -1188,7 +1313,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, Tile t
 template <int NV, bool NORM, int MT, int RPW, int L>
 __global__ void __launch_bounds__(256) fused_valu_kernel(FusedArgs a) {
   extern __shared__ int smem[];
-  fused_body<NV, NORM>(a, smem, [&](int t, auto&& sink, auto&& pre, auto&& xf) {
+  fused_body<NV, NORM, MT == 1>(a, smem, [&](int t, auto&& sink, auto&& pre, auto&& xf) {
     valu_tile<MT, RPW, L>(a.g, t % a.g.nb_count, t / a.g.nb_count, sink, pre, xf);
   });
 }
@@ -1196,7 +1321,7 @@ __global__ void __launch_bounds__(256) fused_valu_kernel(FusedArgs a) {
 template <int NV, bool NORM, int MT, int KS>
 __global__ void __launch_bounds__(256) fused_mfma_kernel(FusedArgs a) {
   extern __shared__ int smem[];
-  fused_body<NV, NORM>(a, smem, [&](int t, auto&& sink, auto&& pre, auto&& xf) {
+  fused_body<NV, NORM, false>(a, smem, [&](int t, auto&& sink, auto&& pre, auto&& xf) {
     // row block fastest: the row blocks of one W tile run side by side
     const int mbc = (int)gridDim.x / (a.g.nb_count * a.g.s_count);
     const int mb = t % mbc, r = t / mbc;
