@@ -668,6 +668,7 @@ template <int NV, bool ONE, class Quant>
 __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 tag, int role, bool have_unit, int unit,
                                            Quant&& quant, const float (&bv)[NV], bool gate_here, bool layout_here,
                                            bool quant_wg) {
+  RGT_STAMP(a.trace, 9);
   __shared__ __align__(16) u64 s_mask[4][NV];
   const GemvArgs& g = a.g;
   const int m = g.m, n = g.n, k = a.topk, B = a.block;
@@ -702,14 +703,25 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
   }
   if constexpr (ONE && NV == 2) {
     if (m == 1 && n == 128 && !quant_wg && !fused_gather_staged(1, n, g.s_count)) {
-      // The gate or layout workgroup of one row of 128 experts: wave 0 alone
-      // (lane l holds experts 2l and 2l + 1, as its gather leaves them), with
-      // no LDS pass and no barrier; the other waves take the layout
-      // workgroup's scrub and end.
-      if (wave != 0) {
-        if (layout_here) scrub_window(a, tag, threadIdx.x - 64u, 192u);
-        return;
+      // The gate or layout workgroup of one row of 128 experts: its parts run
+      // on separate waves, each gathering the row for itself (lane l holds
+      // experts 2l and 2l + 1, as its gather leaves them) with no LDS pass
+      // and no barrier. Gate: wave 0 the ids, the pairs' sorted_ids entries,
+      // the logits and the epoch, wave 1 the weights; layout: one wave the
+      // offsets and expert_ids, one the pads (which do not depend on the
+      // winners) and the scrub.
+      const int wl = wave - (gate_here ? 2 : 0);
+      const bool do_ids = gate_here && wave == 0, do_w = gate_here && wave == 1;
+      const bool do_off = layout_here && wl == 0, do_pad = layout_here && wl == 1;
+      if (do_pad) {
+        int32_t* const sorted_ids = RGT_OUT(sorted_ids);
+        for (int q = lane; q < k * B; q += 64)
+          if (q & (B - 1)) sorted_ids[q] = P;
+        if (lane == 0) RGT_OUT(offsets)[n] = k * B;
+        scrub_window(a, tag, lane, 64u);
       }
+      if (!(do_ids || do_w || do_off)) return;
+      RGT_STAMP(a.trace, 6);
       float sv[2];
       const bool ok = g.s_count <= 4 ? wave_gather_pairs<4>(a, tag, sv) : wave_gather_pairs<8>(a, tag, sv);
       if (!ok) return;
@@ -718,17 +730,16 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
       bool sel[2];
       int slot[2], ord[2];
       u32 key[2];
-      row_topk_owner<2>(a, sv, bv, sel, slot, key, nullptr, gate_here);
+      row_topk_owner<2>(a, sv, bv, sel, slot, key, nullptr, do_ids || do_w);
       wave_select_order<2>(sel, ord);  // winners below, = the block of each expert
       RGT_STAMP(a.trace, 14);
-      if (gate_here) {
+      if (do_ids) {
         int32_t* const topk_ids = RGT_OUT(topk_ids);
         int32_t* const sorted_ids = RGT_OUT(sorted_ids);
 #pragma unroll
         for (int i = 0; i < 2; ++i)
           if (sel[i]) {
             topk_ids[slot[i]] = c0 + i;
-            s_key[slot[i]] = key[i];
             sorted_ids[ord[i] * B] = slot[i];  // the pair of slot j leads its expert's block
           }
         float* const logits_out = RGT_OUT(logits_out);
@@ -738,23 +749,23 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
         }
         // every partial has been seen, so every workgroup's tag is read
         if (lane == 0) st_agent(a.ctl + kCtlEpoch, tag);
+      }
+      if (do_w) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          if (sel[i]) s_key[slot[i]] = key[i];
         const float w = wave_weights(s_key[min(lane, k - 1)], k);  // one wave: after its LDS writes
         if (lane < k) RGT_OUT(topk_w)[lane] = w;
       }
-      if (layout_here) {
-        // offsets: the k present experts fill one block each; the pads are
-        // the rows of the k blocks past their first
+      if (do_off) {
+        // the k present experts fill one block each
         int32_t* const offsets = RGT_OUT(offsets);
         int32_t* const expert_ids = RGT_OUT(expert_ids);
-        int32_t* const sorted_ids = RGT_OUT(sorted_ids);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           offsets[c0 + i] = ord[i] * B;
           if (sel[i]) expert_ids[ord[i]] = c0 + i;
         }
-        if (lane == 0) offsets[n] = k * B;
-        for (int q = lane; q < k * B; q += 64)
-          if (q & (B - 1)) sorted_ids[q] = P;
         RGT_STAMP(a.trace, 7);
       }
 #ifdef RGT_TRACE
@@ -966,6 +977,7 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
   const bool layout_here = li >= 0 && li < n_layout;
   const bool participant = gate_here || quant_wg || layout_here;
   const int P = m * k;
+  RGT_STAMP(a.trace, 3);
   if (poisoned) {
     // An earlier wait of this workspace expired: no waits, defined outputs.
     if (role == layout_wg) write_poison(a);
