@@ -111,6 +111,10 @@ struct FusedArgs {
 // the tail uses it (the kernels take FusedArgs as their only argument).
 #define RGT_OUT(field) ::rgt::kernarg_at<decltype(::rgt::FusedArgs::field)>(offsetof(::rgt::FusedArgs, field))
 
+// Set by a wave of the small-mode tail whose own gather expired; zeroed at
+// the kernel's start, read by all waves after the tail's mask barrier.
+__shared__ u32 s_tail_err;
+
 // The call's tag from the epoch word: epoch + 1, skipping 0 so zero-filled
 // words never look ready. The control words stay per-lane values (every lane
 // loads the same words): moving them to scalar registers would make the wave
@@ -225,13 +229,15 @@ __device__ __forceinline__ bool gather_logits(const FusedArgs& a, int r0, int ro
 // One row of 128 experts gathered by the calling wave alone (no LDS, no
 // barrier): lane l polls the k-slices of column pair l (NL >= S loads, the
 // ones past S repeat the last slice) and sums them in k-slice order, the
-// same bits as gather_logits. false (error word set) if the deadline passes.
-template <int NL>
-__device__ __forceinline__ bool wave_gather_pairs(const FusedArgs& a, u32 tag, float (&sv)[2]) {
+// same bits as gather_logits. during() runs once the first poll is issued.
+// false (error word set) if the deadline passes.
+template <int NL, class During>
+__device__ __forceinline__ bool wave_gather_pairs(const FusedArgs& a, u32 tag, int row, float (&sv)[2],
+                                                  During&& during) {
   const int S = a.g.s_count;
   const u32 slice = (u32)a.g.m * (u32)a.g.n * 8u;
   const auto rsrc = coherent_rsrc(a.tpart, slice * (u32)S);
-  const u32 base = 16u * (u32)lane_id();
+  const u32 base = (u32)row * (u32)a.g.n * 8u + 16u * (u32)lane_id();
   u32x4_t v[NL];
   auto issue = [&] {
 #pragma unroll
@@ -246,6 +252,7 @@ __device__ __forceinline__ bool wave_gather_pairs(const FusedArgs& a, u32 tag, f
   const u64 t0 = rt_clock();
   issue();
   RGT_STAMP(a.trace, 11);
+  during();
   bool ok = true;
   for (;;) {
     if (ready()) {
@@ -723,7 +730,8 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
       if (!(do_ids || do_w || do_off)) return;
       RGT_STAMP(a.trace, 6);
       float sv[2];
-      const bool ok = g.s_count <= 4 ? wave_gather_pairs<4>(a, tag, sv) : wave_gather_pairs<8>(a, tag, sv);
+      const bool ok = g.s_count <= 4 ? wave_gather_pairs<4>(a, tag, 0, sv, [] {})
+                                     : wave_gather_pairs<8>(a, tag, 0, sv, [] {});
       if (!ok) return;
       RGT_STAMP(a.trace, 5);
       const float lg[2] = {sv[0], sv[1]};  // the logits (the gate adds the bias to sv)
@@ -775,18 +783,47 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
       return;
     }
   }
-  // the thread's quant chunk is encoded while the first poll is in flight
-  if (!gather_any(a, 0, m, tag, s_log, [&] { codes_in = quant(sb_in); })) return;
-  RGT_STAMP(a.trace, 5);
+  // The thread's quant chunk is encoded while the first poll is in flight.
+  // With 128 experts and two to four rows each row wave gathers its own row
+  // into registers (thread t of a workgroup gather would hold item t, i.e.
+  // the same values), so the rows need no LDS pass and the gather no
+  // barrier; a wave whose wait expires flags it, and every wave leaves after
+  // the mask barrier below.
   const int row = wave;
+  float rv[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) rv[i] = 0.f;
+  bool wave_rows = false, wave_ok = true;
+  if constexpr (!ONE && NV == 2) {
+    if (n == 128 && m >= 2 && !fused_gather_staged(m, n, g.s_count)) {
+      wave_rows = true;
+      auto enc = [&] { codes_in = quant(sb_in); };
+      if (row < m)
+        wave_ok = g.s_count <= 4 ? wave_gather_pairs<4>(a, tag, row, rv, enc)
+                                 : wave_gather_pairs<8>(a, tag, row, rv, enc);
+      else
+        enc();
+      if (!wave_ok && lane == 0) s_tail_err = 1u;
+    }
+  }
+  if (!wave_rows && !gather_any(a, 0, m, tag, s_log, [&] { codes_in = quant(sb_in); })) return;
+  RGT_STAMP(a.trace, 5);
   bool sel[NV];
   int slot[NV];
   u32 key[NV];
-  if (row < m) {
+  if (row < m && wave_ok) {
     // quant-only workgroups (and the layout workgroup of one row) need the
     // selected set, not the slots: their positions are indexed by winner
     // order, the same k rows either way
-    row_topk_owner<NV>(a, s_log + row * n, bv, sel, slot, key, s_flag, gate_here || (layout_here && m > 1));
+    const bool slots = gate_here || (layout_here && m > 1);
+    if (wave_rows) {
+      float sv[NV];
+#pragma unroll
+      for (int i = 0; i < NV; ++i) sv[i] = rv[i];
+      row_topk_owner<NV>(a, sv, bv, sel, slot, key, s_flag, slots);
+    } else {
+      row_topk_owner<NV>(a, s_log + row * n, bv, sel, slot, key, s_flag, slots);
+    }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const u64 mk = ballot64(sel[i]);
@@ -819,11 +856,19 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
   }
   if (gate_here) {
     float* const logits_out = RGT_OUT(logits_out);
-    if (logits_out)
-      for (int i = threadIdx.x; i < m * n; i += 256) logits_out[i] = s_log[i];
+    if (logits_out) {
+      if (wave_rows) {
+        if (row < m)
+#pragma unroll
+          for (int i = 0; i < NV; ++i) logits_out[row * n + c0 + i] = rv[i];
+      } else {
+        for (int i = threadIdx.x; i < m * n; i += 256) logits_out[i] = s_log[i];
+      }
+    }
   }
   // (one row: wave 0 holds everything the positions need, no barrier here)
   if (m > 1) __syncthreads();
+  if (wave_rows && s_tail_err) return;  // every wave, after the barrier
   RGT_STAMP(a.trace, 14);
   if (gate_here) {
     // Every partial has been seen, so every workgroup's tag is read.
@@ -1301,6 +1346,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, Tile t
   if (threadIdx.x == 0) {
     s_ctl[0] = tag;
     s_ctl[1] = err;
+    s_tail_err = 0u;
   }
   __syncthreads();  // also: the tile's LDS is reused below
   tag = s_ctl[0];

@@ -193,13 +193,15 @@ def test_route_sort_quant_prefill(R):
                      sample_rows=lambda nv: rng.choice(nv, size=800, replace=False))
 
 
-def test_fused_wait_deadline_sets_error_and_reset_recovers(R, rgt_env):
+@pytest.mark.parametrize("m", [1, 4, 64])
+def test_fused_wait_deadline_sets_error_and_reset_recovers(R, rgt_env, m):
     """A host-forced fault: the tiles publish nothing, so every device-side
     wait runs into its (shortened) deadline and exits; the error word
     reports RGT_ERR_TIMEOUT, and after a reset the same workspace gives
-    correct results again."""
-    say("fused wait deadline (host-forced: nothing published)")
-    wl = Workload("deadline_M4", 4, 128, 6144, 8, 16)
+    correct results again. One row (the gate and layout waves wait alone),
+    four rows (each row wave waits for its own row) and 64 (large mode)."""
+    say(f"fused wait deadline M={m} (host-forced: nothing published)")
+    wl = Workload(f"deadline_M{m}", m, 128, 6144, 8, 16)
     x, w, b = wl.make()
     ws = R.Workspace(wl.m, wl.n, wl.k, wl.topk, wl.block)
     rgt_env(RGT_FAULT_INJECT=1, RGT_WAIT_BUDGET_US=2000)
