@@ -1034,6 +1034,52 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
     small_tail<NV, ONE>(a, smem, tag, role, have_unit, unit, quant, bv, gate_here, li == 0, quant_wg);
     return;
   }
+  // Step 2 (large): row workgroups gather their row, run its gate and
+  // publish the ids; then every participant polls all ids.
+  const int row_wg0 = spare0 + m <= (int)gridDim.x ? spare0 : 0;
+  const int row = role - row_wg0;
+  u32* s_key1 = reinterpret_cast<u32*>(smem);  // a spare row workgroup's k keys
+  if constexpr (NV == 2) {
+    if (row >= 0 && row < m && !participant && n == 128 && g.s_count <= 12) {
+      // A spare row workgroup at 128 experts: wave 0 alone gathers the row
+      // into registers (lane l: experts 2l, 2l + 1), runs its gate and
+      // publishes the ids; no LDS pass, no barrier.
+      if (wave != 0) return;
+      float sv[2];
+      const int S = g.s_count;
+      const bool ok = S <= 4   ? wave_gather_pairs<4>(a, tag, row, sv, [] {})
+                      : S <= 8 ? wave_gather_pairs<8>(a, tag, row, sv, [] {})
+                               : wave_gather_pairs<12>(a, tag, row, sv, [] {});
+      if (!ok) return;
+      RGT_STAMP(a.trace, 5);
+      const int c0 = lane * 2;
+      const float lg[2] = {sv[0], sv[1]};  // the logits (the gate adds the bias to sv)
+      bool sel[2];
+      int slot[2];
+      u32 key[2];
+      row_topk_owner<2>(a, sv, bv, sel, slot, key, nullptr, true);
+      int32_t* const topk_ids = RGT_OUT(topk_ids);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        if (sel[i]) {
+          st_agent(a.tids + row * k + slot[i], tag_word((u32)(c0 + i), tag));
+          topk_ids[row * k + slot[i]] = c0 + i;
+          s_key1[slot[i]] = key[i];
+        }
+      // the pad word of an odd pair count: every word of the call's
+      // footprint carries its tag
+      if (row == m - 1 && lane == 0 && (P & 1)) st_agent(a.tids + P, tag_word(0u, tag));
+      float* const logits_out = RGT_OUT(logits_out);
+      if (logits_out) {
+        logits_out[(int64_t)row * n + c0] = lg[0];
+        logits_out[(int64_t)row * n + c0 + 1] = lg[1];
+      }
+      const float w = wave_weights(s_key1[min(lane, k - 1)], k);  // one wave: after its LDS writes
+      if (lane < k) RGT_OUT(topk_w)[row * k + lane] = w;
+      RGT_STAMP(a.trace, 6);
+      return;
+    }
+  }
   u32 sb_in = 0;
   const uint4 codes_in = quant(sb_in);  // all lanes: the scale exchange reads the partner lane
   int* s_e = smem;
@@ -1056,10 +1102,6 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
       s_pre[e] = 0;
     }
   {
-    // Step 2 (large): row workgroups gather their row, run its gate and
-    // publish the ids; then every participant polls all ids.
-    const int row_wg0 = spare0 + m <= (int)gridDim.x ? spare0 : 0;
-    const int row = role - row_wg0;
     if (row >= 0 && row < m) {
       if (!gather_any(a, row, 1, tag, s_log)) return;
       RGT_STAMP(a.trace, 5);
