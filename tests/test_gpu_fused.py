@@ -108,6 +108,35 @@ def test_fused_decode_matches_chain_and_oracle(R, wl):
     assert_workspace_ready(ws)
 
 
+@pytest.mark.parametrize("m", [1, 2, 4, 8, 64])
+def test_fused_ties_and_hot_bias_128(R, m):
+    """128 experts, top-8, with 100 W rows copied from the other 28 (experts
+    that score alike in every token, so equal scores straddle the k-th place
+    in nearly every row) and a bias that lifts six experts above the rest
+    (every token routes to them, and the other two slots go to tied ones): the
+    one-row, per-wave-row and spare-row-workgroup paths of the one-launch
+    kernel, bit-equal to the chain and checked against the oracle."""
+    say(f"fused ties + hot bias M={m} N=128 K=6144 k=8 B=16")
+    x = gen_x(m, 6144, seed=7)
+    w = gen_w(128, 6144, seed=7, tie_rows=100)
+    b = gen_skew_bias(128, 6, seed=7)
+    ws = R.Workspace(m, 128, 6144, 8, 16)
+    f, launches = fused(R, x, w, b, 8, 16, ws)
+    assert launches == 1
+    fo = np_out(f)
+    c = np_out(chain(R, x, w, b, 8, 16, ws))
+    for key in ("logits", "topk_ids", "topk_w", "offsets"):
+        np.testing.assert_array_equal(fo[key].view(np.uint32) if fo[key].dtype == np.float32 else fo[key],
+                                      c[key].view(np.uint32) if c[key].dtype == np.float32 else c[key],
+                                      err_msg=key)
+    total = int(fo["offsets"][-1])
+    for key in ("sorted_ids", "a_q", "a_scale"):
+        np.testing.assert_array_equal(fo[key][:total], c[key][:total], err_msg=key)
+    ids = check_against_oracle(x, w, b, 8, 16, fo)
+    check_sort_quant(sort_out(fo), ids, x, 128, 16)
+    assert_workspace_ready(ws)
+
+
 def test_fused_without_logits_output(R):
     say("fused without logits output")
     wl = Workload("nolog_M16", 16, 896, 3584, 16, 16, bias=True)
