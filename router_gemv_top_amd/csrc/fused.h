@@ -967,11 +967,18 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
         for (int q = lane; q < sg.total * B; q += 64)
           if (q & (B - 1)) sorted_ids[q] = P;
       } else {
-        // the four waves split the pads
+        // Each wave writes the pair count of every block (its lanes hold all
+        // the experts) to a table of its own and reads only its own writes,
+        // so no barrier; then thread t pads rows t, t + 256, ... of the
+        // blocks (a row past its block's pairs).
+        __shared__ int s_bcnt[4][128];  // blocks <= M * k <= 4 * 32
+        int* bc = s_bcnt[wave];
 #pragma unroll
         for (int i = 0; i < NV; ++i)
-          if (sg.present[i])
-            for (int q = sg.cnt[i] + wave; q < B; q += 4) sorted_ids[sg.blk[i] * B + q] = P;
+          if (sg.present[i]) bc[sg.blk[i]] = sg.cnt[i];
+        const int lb = __ffs(B) - 1;
+        for (int q = threadIdx.x; q < sg.total * B; q += 256)
+          if ((q & (B - 1)) >= bc[q >> lb]) sorted_ids[q] = P;
       }
       RGT_STAMP(a.trace, 7);
     }
