@@ -278,6 +278,52 @@ __device__ __forceinline__ bool wave_gather_pairs(const FusedArgs& a, u32 tag, i
   return ballot64(!ok) == 0ull;
 }
 
+// One row gathered by the calling wave alone when the partials are one
+// k-slice (no sum): lane l takes experts [l*NV, l*NV + NV) as NV/2 column
+// pairs (pairs past the row repeat its last one; their experts are absent),
+// polling until every word carries the tag. false (error word set) if the
+// deadline passes.
+template <int NV>
+__device__ __forceinline__ bool wave_gather_row1(const FusedArgs& a, u32 tag, int row, float (&sv)[NV]) {
+  static_assert(NV % 2 == 0, "column pairs");
+  constexpr int NP = NV / 2;
+  const int np = a.g.n >> 1;
+  const auto rsrc = coherent_rsrc(a.tpart, (u32)a.g.m * (u32)a.g.n * 8u);
+  const u32 base = (u32)row * (u32)a.g.n * 8u;
+  const int p0 = lane_id() * NP;
+  u32x4_t v[NP];
+  auto issue = [&] {
+#pragma unroll
+    for (int c = 0; c < NP; ++c) v[c] = ld_agent16(rsrc, base + 16u * (u32)min(p0 + c, np - 1));
+  };
+  auto ready = [&] {
+    bool ok = true;
+#pragma unroll
+    for (int c = 0; c < NP; ++c) ok = ok & (v[c].y == tag) & (v[c].w == tag);
+    return ok;
+  };
+  const u64 t0 = rt_clock();
+  issue();
+  bool ok = true;
+  for (;;) {
+    if (ready()) {
+#pragma unroll
+      for (int c = 0; c < NP; ++c) {
+        sv[2 * c] = __uint_as_float(v[c].x);
+        sv[2 * c + 1] = __uint_as_float(v[c].z);
+      }
+      break;
+    }
+    issue();
+    if (rt_clock() - t0 > a.budget) {
+      set_timeout(a);
+      ok = false;
+      break;
+    }
+  }
+  return ballot64(!ok) == 0ull;
+}
+
 // Loads per thread that a gather of `rows` rows needs.
 __host__ __device__ constexpr int gather_loads(int rows, int n, int s) { return (rows * (n / 2) + 255) / 256 * s; }
 
@@ -1005,7 +1051,7 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
 
 // quant(sb) returns the thread's encoded quant chunk and its scale byte(s);
 // every lane of a wave calls it together.
-template <int NV, bool ONE, class Quant>
+template <int NV, bool ONE, bool VALU, class Quant>
 __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 tag, bool poisoned, int role,
                                            bool have_unit, int unit, Quant&& quant, const float (&bv)[NV]) {
   const GemvArgs& g = a.g;
@@ -1082,6 +1128,44 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
         logits_out[(int64_t)row * n + c0 + 1] = lg[1];
       }
       const float w = wave_weights(s_key1[min(lane, k - 1)], k);  // one wave: after its LDS writes
+      if (lane < k) RGT_OUT(topk_w)[row * k + lane] = w;
+      RGT_STAMP(a.trace, 6);
+      return;
+    }
+  }
+  if constexpr (VALU && NV > 4 && NV % 2 == 0) {  // (one k-slice: VALU plans only)
+    if (row >= 0 && row < m && !participant && g.s_count == 1 && (n & 1) == 0) {
+      // A spare row workgroup over more than 256 experts with one k-slice:
+      // wave 0 alone gathers the row into registers (lane l: experts
+      // [l*NV, l*NV + NV)), selects with k rounds of a wave maximum (lane j
+      // ends with slot j) and publishes the ids; no LDS pass of the row, no
+      // barrier.
+      if (wave != 0) return;
+      float sv[NV];
+      if (!wave_gather_row1<NV>(a, tag, row, sv)) return;
+      RGT_STAMP(a.trace, 5);
+      const int c0 = lane * NV;
+      float* const logits_out = RGT_OUT(logits_out);
+      if (logits_out) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+          if (c0 + i < n) logits_out[(int64_t)row * n + c0 + i] = sv[i];
+      }
+      float sb[1][NV];
+#pragma unroll
+      for (int i = 0; i < NV; ++i) sb[0][i] = a.bias ? __fadd_rn(sv[i], bv[i]) : sv[i];
+      __shared__ __align__(16) int s_sel[64];
+      int id[1];
+      u32 key[1];
+      wave_select_rows<NV, 1>(sb, n, k, id, key, s_sel);
+      if (lane < k) {
+        st_agent(a.tids + row * k + lane, tag_word((u32)id[0], tag));
+        RGT_OUT(topk_ids)[row * k + lane] = id[0];
+      }
+      // the pad word of an odd pair count: every word of the call's
+      // footprint carries its tag
+      if (row == m - 1 && lane == 0 && (P & 1)) st_agent(a.tids + P, tag_word(0u, tag));
+      const float w = wave_weights(key[0], k);
       if (lane < k) RGT_OUT(topk_w)[row * k + lane] = w;
       RGT_STAMP(a.trace, 6);
       return;
@@ -1322,7 +1406,7 @@ __device__ __forceinline__ bool norm_unit(const FusedArgs& a, int unit, u32 tag,
 // Shared head of the kernels: read the control words, run the tile, then the
 // tail. tile(t, sink, pre, xf) computes this workgroup's GEMV tile; with NORM
 // the tile and the quant units read the RMSNorm of x (NormX).
-template <int NV, bool NORM, bool ONE, class Tile>
+template <int NV, bool NORM, bool ONE, bool VALU, class Tile>
 __device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, Tile tile) {
   __shared__ u32 s_ctl[2];
   const GemvArgs& g = a.g;
@@ -1408,7 +1492,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, Tile t
     }
     return mx_quant16_fmt(c0, c1, sb, a.fp4 != 0);
   };
-  fused_tail<NV, ONE>(a, smem, tag, err != 0u, role, have_unit, unit, quant, bv);
+  fused_tail<NV, ONE, VALU>(a, smem, tag, err != 0u, role, have_unit, unit, quant, bv);
 }
 
 // Quant units (16-element chunks of x, row-major) go 2^upw_log to a
@@ -1420,7 +1504,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, Tile t
 template <int NV, bool NORM, int MT, int RPW, int L>
 __global__ void __launch_bounds__(256) fused_valu_kernel(FusedArgs a) {
   extern __shared__ int smem[];
-  fused_body<NV, NORM, MT == 1>(a, smem, [&](int t, auto&& sink, auto&& pre, auto&& xf) {
+  fused_body<NV, NORM, MT == 1, true>(a, smem, [&](int t, auto&& sink, auto&& pre, auto&& xf) {
     valu_tile<MT, RPW, L>(a.g, t % a.g.nb_count, t / a.g.nb_count, sink, pre, xf);
   });
 }
@@ -1428,7 +1512,7 @@ __global__ void __launch_bounds__(256) fused_valu_kernel(FusedArgs a) {
 template <int NV, bool NORM, int MT, int KS>
 __global__ void __launch_bounds__(256) fused_mfma_kernel(FusedArgs a) {
   extern __shared__ int smem[];
-  fused_body<NV, NORM, false>(a, smem, [&](int t, auto&& sink, auto&& pre, auto&& xf) {
+  fused_body<NV, NORM, false, false>(a, smem, [&](int t, auto&& sink, auto&& pre, auto&& xf) {
     // row block fastest: the row blocks of one W tile run side by side
     const int mbc = (int)gridDim.x / (a.g.nb_count * a.g.s_count);
     const int mb = t % mbc, r = t / mbc;
