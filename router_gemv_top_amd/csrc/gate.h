@@ -219,11 +219,16 @@ __device__ __forceinline__ bool select_fast_sorted(const u32 (&key)[NV], int k, 
 // largest key: every key above it is selected, and of the keys equal to it
 // the ones with the lowest expert index, as many as are missing. Lane-local
 // result: sel[i].
+#ifndef RGT_SELECT_EXIT_BITS
+#define RGT_SELECT_EXIT_BITS 24
+#endif
 template <int NV>
 __device__ __forceinline__ void wave_threshold_select(const u32 (&key)[NV], int k, bool (&sel)[NV]) {
+  constexpr int kExitBits = RGT_SELECT_EXIT_BITS;
   static_assert(NV <= 4, "the threshold selection takes up to four keys per lane");
   u32 T = 0;
   bool exact = false;
+#pragma unroll
   for (int b = 31; b >= 0; --b) {
     const u32 c = T | (1u << b);
     int cnt = 0;
@@ -231,7 +236,12 @@ __device__ __forceinline__ void wave_threshold_select(const u32 (&key)[NV], int 
     for (int i = 0; i < NV; ++i) cnt += __popcll(ballot64(key[i] >= c));
     if (cnt >= k) {
       T = c;
-      if (cnt == k) {
+      // No exit test in the sign and exponent rounds (saves its three
+      // instructions where an exact count is rare). A count of exactly k
+      // reached there stays exact: later candidates are kept only if k keys
+      // still reach them, and if none is, the tie path below selects the
+      // keys >= T, which are then exactly k.
+      if (b < kExitBits && cnt == k) {
         exact = true;
         break;
       }
