@@ -54,8 +54,11 @@ def units(trace: bool):
     for norm in (0, 1):
         for nv in NV_BUCKETS:
             name = f"fused_norm_nv{nv}.o" if norm else f"fused_nv{nv}.o"
+            # the fused kernels' ten leading scalar arguments (the tile's
+            # operands) are preloaded into scalar registers at dispatch
             out.append((os.path.join(CSRC, "fused_inst.hip"), os.path.join(d, name),
-                        extra + [f"-DRGT_NV={nv}", f"-DRGT_NORM={norm}"]))
+                        extra + [f"-DRGT_NV={nv}", f"-DRGT_NORM={norm}", "-mllvm",
+                                 "-amdgpu-kernarg-preload-count=10"]))
     out.append((os.path.join(CSRC, "shared_inst.hip"), os.path.join(d, "shared_inst.o"), extra))
     return out
 

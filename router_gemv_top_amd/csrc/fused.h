@@ -107,9 +107,27 @@ struct FusedArgs {
   u64* trs;            // [M] tagged rstd words (workspace, after tids)
 };
 
-// An output pointer of the call, read from the kernel's argument block where
-// the tail uses it (the kernels take FusedArgs as their only argument).
-#define RGT_OUT(field) ::rgt::kernarg_at<decltype(::rgt::FusedArgs::field)>(offsetof(::rgt::FusedArgs, field))
+// The fused kernels' scalar arguments ahead of FusedArgs (the tile's
+// operands, preloaded into scalar registers; see the kernels below) and the
+// byte offset of FusedArgs in the kernarg segment after them.
+struct TileParams {
+  const u16* x;
+  const u16* w;
+  int ldx, ldw, m, nbc;
+  u32 nbm;
+  int mbc;
+  u32 mbm;
+  int grid;
+};
+constexpr unsigned kFusedArgsAt = (sizeof(TileParams) + alignof(FusedArgs) - 1) / alignof(FusedArgs) * alignof(FusedArgs);
+static_assert(sizeof(TileParams) == 48 && kFusedArgsAt == 48, "kernel argument layout");
+
+// A field of the call's FusedArgs read from the kernarg segment where it is
+// used (output pointers of the tail; values whose use must stay behind the
+// tile's loads).
+#define RGT_ARG(field) \
+  ::rgt::kernarg_at<decltype(::rgt::FusedArgs::field)>(::rgt::kFusedArgsAt + offsetof(::rgt::FusedArgs, field))
+#define RGT_OUT(field) RGT_ARG(field)
 
 // Set by a wave of the small-mode tail whose own gather expired; zeroed at
 // the kernel's start, read by all waves after the tail's mask barrier.
@@ -1407,10 +1425,9 @@ __device__ __forceinline__ bool norm_unit(const FusedArgs& a, int unit, u32 tag,
 // tail. tile(t, sink, pre, xf) computes this workgroup's GEMV tile; with NORM
 // the tile and the quant units read the RMSNorm of x (NormX).
 template <int NV, bool NORM, bool ONE, bool VALU, class Tile>
-__device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, Tile tile) {
+__device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, int grid, Tile tile) {
   __shared__ u32 s_ctl[2];
   const GemvArgs& g = a.g;
-  const int units = g.m * (g.k >> 4);
   // The workgroup's place among the quant, layout, gate, row and norm
   // workgroups: its block index, so the tail's workgroups spread over the
   // XCDs (block b runs on XCD b % 8). (The XCDs' first workgroups start up to
@@ -1418,9 +1435,12 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, Tile t
   // instead, all on XCD 0 or spread over XCDs 0-3, measured slower at one
   // and at 64 rows, faster at 8-16, +-0.1-0.4 us.)
   const int role = (int)blockIdx.x;
-  const int tile_id = xcd_tile(blockIdx.x, gridDim.x);
-  const int unit = (role << a.upw_log) + threadIdx.x;
-  const bool have_unit = (int)threadIdx.x < (1 << a.upw_log) && unit < units;
+  const int tile_id = xcd_tile(blockIdx.x, grid);  // grid = gridDim.x
+  // The thread's quant unit, set once the tile's loads are out (its inputs
+  // are read from the argument block there, so no wait for them comes
+  // ahead of those loads).
+  int unit = 0;
+  bool have_unit = false;
   RGT_STAMP(a.trace, 0);
   // Right after the tile's W loads are issued: the control words (loads
   // return in order, so issued earlier they would hold up the tile's
@@ -1434,6 +1454,9 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, Tile t
 #pragma unroll
   for (int i = 0; i < NV; ++i) bv[i] = 0.f;
   auto prefetch = [&]() {
+    const int ul = RGT_ARG(upw_log), units = RGT_ARG(g.m) * (RGT_ARG(g.k) >> 4);
+    unit = (role << ul) + threadIdx.x;
+    have_unit = (int)threadIdx.x < (1 << ul) && unit < units;
     const u64 cw = ld_agent(reinterpret_cast<const u64*>(a.ctl));
     err = (u32)cw;
     tag = call_tag_of((u32)(cw >> 32));
@@ -1501,25 +1524,50 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, int* smem, Tile t
 // them all (the tail's stores spread over more CUs); large mode the most
 // whose token pairs fit one wave (fewer quant workgroups; measured faster
 // there, slower in small mode).
+// The kernels take the operands of the tile's first loads as scalar
+// arguments ahead of FusedArgs: built with the first ten arguments
+// preloaded into scalar registers when the workgroup starts, the tile's
+// loads go out without waiting for the argument block (a kernarg-segment
+// load takes ~0.2 us at a workgroup's start), and the tile index is split
+// with host-computed reciprocals instead of runtime divisions. x, w, ldx,
+// ldw, m are a.g's; nbc = a.g.nb_count; mbc = the row blocks of the MFMA
+// plan; nbm, mbm = 2^32 / nbc, 2^32 / mbc rounded up (unused for 1); grid = gridDim.x (a
+// hidden argument otherwise, loaded from the segment).
+#define RGT_TILE_PARAMS                                                                                   \
+  const u16 *__restrict__ x, const u16 *__restrict__ w, int ldx, int ldw, int m, int nbc, u32 nbm, int mbc, \
+      u32 mbm, int grid
+// t / d by the host's reciprocal (d = 1 has none that fits 32 bits).
+__device__ __forceinline__ int div_by(int t, int d, u32 magic) { return d == 1 ? t : div_magic(t, magic); }
+__device__ __forceinline__ GemvArgs tile_args(const FusedArgs& a, const u16* x, const u16* w, int ldx, int ldw,
+                                              int m) {
+  GemvArgs g = a.g;
+  g.x = x;
+  g.w = w;
+  g.ldx = ldx;
+  g.ldw = ldw;
+  g.m = m;
+  return g;
+}
+
 template <int NV, bool NORM, int MT, int RPW, int L>
-__global__ void __launch_bounds__(256) fused_valu_kernel(FusedArgs a) {
+__global__ void __launch_bounds__(256) fused_valu_kernel(RGT_TILE_PARAMS, FusedArgs a) {
   extern __shared__ int smem[];
-  fused_body<NV, NORM, MT == 1, true>(a, smem, [&](int t, auto&& sink, auto&& pre, auto&& xf) {
-    valu_tile<MT, RPW, L>(a.g, t % a.g.nb_count, t / a.g.nb_count, sink, pre, xf);
+  fused_body<NV, NORM, MT == 1, true>(a, smem, grid, [&](int t, auto&& sink, auto&& pre, auto&& xf) {
+    const int s = div_by(t, nbc, nbm);
+    valu_tile<MT, RPW, L>(tile_args(a, x, w, ldx, ldw, m), t - s * nbc, s, sink, pre, xf);
   });
 }
 
 template <int NV, bool NORM, int MT, int KS>
-__global__ void __launch_bounds__(256) fused_mfma_kernel(FusedArgs a) {
+__global__ void __launch_bounds__(256) fused_mfma_kernel(RGT_TILE_PARAMS, FusedArgs a) {
   extern __shared__ int smem[];
-  fused_body<NV, NORM, false, false>(a, smem, [&](int t, auto&& sink, auto&& pre, auto&& xf) {
+  fused_body<NV, NORM, false, false>(a, smem, grid, [&](int t, auto&& sink, auto&& pre, auto&& xf) {
     // row block fastest: the row blocks of one W tile run side by side
-    const int mbc = (int)gridDim.x / (a.g.nb_count * a.g.s_count);
-    const int mb = t % mbc, r = t / mbc;
-    const int nb = r % a.g.nb_count;
-    const int s = r / a.g.nb_count;
-    mfma_tile<MT, KS>(a.g, mb, nb, s, reinterpret_cast<float*>(smem), sink, pre, xf);
+    const int r = div_by(t, mbc, mbm), mb = t - r * mbc;
+    const int s = div_by(r, nbc, nbm), nb = r - s * nbc;
+    mfma_tile<MT, KS>(tile_args(a, x, w, ldx, ldw, m), mb, nb, s, reinterpret_cast<float*>(smem), sink, pre, xf);
   });
 }
+#undef RGT_TILE_PARAMS
 
 }  // namespace rgt

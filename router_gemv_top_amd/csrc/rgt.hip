@@ -1014,7 +1014,8 @@ static rgt_status route_sort_quant_impl(const void* x, int64_t ldx, const void* 
   const int upw_log = se->upw_log;
   const void* fn = se->fn;
   const size_t lds = se->lds;
-  if (fuse) {
+  // (the one-launch kernels take the row strides as 32-bit scalars)
+  if (fuse && ldx <= INT32_MAX && ldw <= INT32_MAX) {
     const u32 cpr_magic = 0xFFFFFFFFu / (u32)(k / 16) + 1u;  // exact for unit * (K/16) < 2^32
     // The scrub sweeps the workspace past the tile counters (in the trace
     // build, up to the phase stamps); this call's tagged words are skipped.
@@ -1054,7 +1055,14 @@ static rgt_status route_sort_quant_impl(const void* x, int64_t ldx, const void* 
       a.rstd_out = nrm->rstd;
       a.trs = reinterpret_cast<u64*>(base + L.trs);
     }
-    void* args[] = {&a};
+    // the tile's operands, preloaded into scalar registers (fused.h)
+    const u16* tx = a.g.x;
+    const u16* tw = a.g.w;
+    int tldx = (int)a.g.ldx, tldw = (int)a.g.ldw, tm = a.g.m, nbc = p.nb, mbc = p.valu ? 1 : p.mb;
+    // reciprocals, exact for t * d < 2^32 (a divisor of 1 is not divided by)
+    u32 nbm = nbc > 1 ? 0xFFFFFFFFu / (u32)nbc + 1u : 0u, mbm = mbc > 1 ? 0xFFFFFFFFu / (u32)mbc + 1u : 0u;
+    int tgrid = p.grid;
+    void* args[] = {&tx, &tw, &tldx, &tldw, &tm, &nbc, &nbm, &mbc, &mbm, &tgrid, &a};
     if (hipLaunchKernel(fn, dim3(p.grid), dim3(256), args, lds, stream) != hipSuccess) return RGT_ERR_HIP;
     g_last_launches = n_norm + 1;
     return launched();
