@@ -773,7 +773,7 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
     return;
   }
   if constexpr (ONE && NV == 2) {
-    if (m == 1 && n == 128 && !quant_wg && !fused_gather_staged(1, n, g.s_count)) {
+    if (m == 1 && n == 128 && !quant_wg && g.s_count <= 8 && !fused_gather_staged(1, n, g.s_count)) {
       // The gate or layout workgroup of one row of 128 experts: its parts run
       // on separate waves, each gathering the row for itself (lane l holds
       // experts 2l and 2l + 1, as its gather leaves them) with no LDS pass
@@ -859,12 +859,13 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
   for (int i = 0; i < NV; ++i) rv[i] = 0.f;
   bool wave_rows = false, wave_ok = true;
   if constexpr (!ONE && NV == 2) {
-    if (n == 128 && m >= 2 && !fused_gather_staged(m, n, g.s_count)) {
+    if (n == 128 && m >= 2 && g.s_count <= 12 && !fused_gather_staged(m, n, g.s_count)) {
       wave_rows = true;
       auto enc = [&] { codes_in = quant(sb_in); };
       if (row < m)
-        wave_ok = g.s_count <= 4 ? wave_gather_pairs<4>(a, tag, row, rv, enc)
-                                 : wave_gather_pairs<8>(a, tag, row, rv, enc);
+        wave_ok = g.s_count <= 4   ? wave_gather_pairs<4>(a, tag, row, rv, enc)
+                  : g.s_count <= 8 ? wave_gather_pairs<8>(a, tag, row, rv, enc)
+                                   : wave_gather_pairs<12>(a, tag, row, rv, enc);
       else
         enc();
       if (!wave_ok && lane == 0) s_tail_err = 1u;

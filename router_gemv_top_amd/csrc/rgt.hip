@@ -174,7 +174,12 @@ Plan make_plan(int m, int n, int k) {
     return p;
   }
   const int force = config().force_tile;
-  if (m <= 8 && force != kForceMfma) {
+  // VALU tile to 8 rows; at most 128 experts the 16-row MFMA tile from 5 rows
+  // (12 k-slices, 96 workgroups: M = 5 / 6 / 7 / 8 in 7.41 / 7.55 / 7.65 /
+  // 7.53 us against 7.56 / 7.76 / 7.88 / 7.99 with the 8-row VALU tile; at
+  // 3-4 rows the two are within 0.1 us, at 2 rows the MFMA plan's 12
+  // k-slices cost 1.5 us in the small-mode gather).
+  if (m <= 8 && force != kForceMfma && (force == kForceValu || m <= 4 || n > 128)) {
     p.valu = true;
     p.mt = pow2_at_least(std::max(m, 1));
     p.rpw = 1;

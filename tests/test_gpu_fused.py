@@ -393,7 +393,13 @@ FORCED = [("small", Workload("force_small_n896_M1", 1, 896, 3584, 16, 16, bias=T
           ("large", Workload("force_large_M1", 1, 128, 6144, 8, 16)),
           ("large", Workload("force_large_M4", 4, 128, 6144, 8, 16)),
           ("mfma", Workload("force_mfma_M1", 1, 128, 6144, 8, 16)),
-          ("mfma,large", Workload("force_mfma_large_M8", 8, 128, 6144, 8, 16))]
+          # small mode with 12 k-slices: each row wave polls 12 slices
+          ("mfma", Workload("force_mfma_M3", 3, 128, 6144, 8, 16)),
+          ("mfma", Workload("force_mfma_M4", 4, 128, 6144, 8, 16)),
+          ("mfma,large", Workload("force_mfma_large_M8", 8, 128, 6144, 8, 16)),
+          # the 8-row VALU tile, no longer the default at 128 experts
+          ("valu", Workload("force_valu_M8", 8, 128, 6144, 8, 16)),
+          ("valu", Workload("force_valu_M5", 5, 128, 6144, 8, 16))]
 
 
 @pytest.mark.parametrize("force,wl", FORCED, ids=lambda c: getattr(c, "name", str(c)))
@@ -412,6 +418,8 @@ def test_fused_forced_buckets(R, rgt_env, capfd, force, wl):
         assert f"{mode} mode" in line[0], line[0]
     if "mfma" in force:
         assert "MFMA tile" in line[0], line[0]
+    if "valu" in force:
+        assert "VALU tile" in line[0], line[0]
     fo = np_out(f)
     c = np_out(chain(R, x, w, b, wl.topk, wl.block, ws))
     for key in ("logits", "topk_ids", "topk_w", "offsets"):
