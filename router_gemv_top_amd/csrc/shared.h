@@ -278,11 +278,13 @@ constexpr int shared_cols_per_wg(int mt) { return shared_use_mfma(mt) ? shared_m
 
 // Router tiles first (blocks [0, router_wgs)), then ceil(I / cols) shared
 // workgroups (cols = shared_cols_per_wg of the shared part's rows). KS == 0:
-// VALU router tile <MT, 1, L>; else the 16-row MFMA tile
-// with KS k-steps (M 9..16). The shared part takes MT rows (16 with MFMA).
-template <int MT, int L, int KS>
+// VALU router tile <MT, 1, L>; else the 16-row MFMA tile with KS k-steps
+// (from 5 rows at up to 128 experts, else 9..16). The shared part takes SMR
+// rows if given (8: the VALU form behind an MFMA router tile at 5..8 rows),
+// else MT (16 with MFMA).
+template <int MT, int L, int KS, int SMR = 0>
 __global__ void __launch_bounds__(256) router_shared_kernel(GemvArgs a, SharedArgs b, int router_wgs) {
-  constexpr int SM = KS ? 16 : MT;
+  constexpr int SM = SMR ? SMR : (KS ? 16 : MT);
   __shared__ float lds[(KS || shared_use_mfma(SM)) ? 4 * 256 : 4 * 2 * SM];
   if ((int)blockIdx.x < router_wgs) {
     const int t = xcd_tile(blockIdx.x, router_wgs);

@@ -18,7 +18,7 @@ static const void* pick_valu(int l) {
   }
 }
 
-const void* shared_pick(bool valu, int mt, int l, int ks) {
+const void* shared_pick(bool valu, int mt, int l, int ks, int m) {
   if (valu) {
     switch (mt) {
       case 1: return pick_valu<1>(l);
@@ -29,6 +29,14 @@ const void* shared_pick(bool valu, int mt, int l, int ks) {
     }
   }
   if (mt != 1) return nullptr;
+  if (m <= 8) {  // the shared part's VALU form for up to 8 rows
+    switch (ks) {
+      case 2: return reinterpret_cast<const void*>(&router_shared_kernel<1, 1, 2, 8>);
+      case 4: return reinterpret_cast<const void*>(&router_shared_kernel<1, 1, 4, 8>);
+      case 8: return reinterpret_cast<const void*>(&router_shared_kernel<1, 1, 8, 8>);
+      default: return nullptr;
+    }
+  }
   switch (ks) {
     case 2: return reinterpret_cast<const void*>(&router_shared_kernel<1, 1, 2>);
     case 4: return reinterpret_cast<const void*>(&router_shared_kernel<1, 1, 4>);
