@@ -982,11 +982,19 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
     }
     return sg;
   };
+  // (all rows' words read together, one LDS round trip, and the rows past M
+  // masked off afterwards: a read per row behind its own branch waited a
+  // round trip each)
   auto masks_lds = [&](u64 (&mr)[4][NV]) {
+    u64 v[4][NV];
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int i = 0; i < NV; ++i) mr[r][i] = r < m ? uniform_u64(s_mask[r][i]) : 0ull;
+      for (int i = 0; i < NV; ++i) v[r][i] = s_mask[r][i];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int i = 0; i < NV; ++i) mr[r][i] = uniform_u64(v[r][i]) & (r < m ? ~0ull : 0ull);
   };
   // Positions of this wave's row (one row: wave 0's own ballots, no barrier
   // before). The layout workgroup writes the layout here too, from the same
