@@ -59,7 +59,9 @@ def units(trace: bool):
             out.append((os.path.join(CSRC, "fused_inst.hip"), os.path.join(d, name),
                         extra + [f"-DRGT_NV={nv}", f"-DRGT_NORM={norm}", "-mllvm",
                                  "-amdgpu-kernarg-preload-count=10"]))
-    out.append((os.path.join(CSRC, "shared_inst.hip"), os.path.join(d, "shared_inst.o"), extra))
+    # the router + shared-expert kernel's eight leading scalar arguments
+    out.append((os.path.join(CSRC, "shared_inst.hip"), os.path.join(d, "shared_inst.o"),
+                extra + ["-mllvm", "-amdgpu-kernarg-preload-count=8"]))
     return out
 
 

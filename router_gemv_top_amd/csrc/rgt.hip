@@ -786,13 +786,18 @@ rgt_status rgt_router_shared_swiglu(const void* x, int64_t ldx, const void* w, i
   const Plan p = make_plan(m, n, k);
   if (s != p.s || !part || !aligned(part, 16)) return RGT_ERR_INVALID;
   if (!wsh_q || !aligned(wsh_q, 16) || !wsh_scale || !h || !aligned(h, 2) || ldh < inter) return RGT_ERR_INVALID;
+  if (ldx > INT32_MAX) return RGT_ERR_UNSUPPORTED;  // passed to the kernel as a 32-bit scalar
   const void* fn = shared_pick(p.valu, p.mt, p.l, p.ks, m);
   if (!fn) return RGT_ERR_UNSUPPORTED;
   GemvArgs a{static_cast<const u16*>(x), ldx, static_cast<const u16*>(w), ldw, nullptr, part, nullptr, m, n, k,
              p.s, p.nb};
   SharedArgs b{static_cast<const u16*>(x), ldx, wsh_q, wsh_scale, static_cast<u16*>(h), ldh, m, k, inter};
-  int router_wgs = p.grid;
-  void* args[] = {&a, &b, &router_wgs};
+  // the shared part's operands, preloaded into scalar registers (shared.h)
+  int router_wgs = p.grid, sldx = (int)ldx, sk = k, sinter = inter, sm = m;
+  const uint8_t* swq = wsh_q;
+  const uint8_t* sws = wsh_scale;
+  const u16* sx = static_cast<const u16*>(x);
+  void* args[] = {&router_wgs, &swq, &sws, &sx, &sldx, &sk, &sinter, &sm, &a, &b};
   // shared-expert columns per workgroup, for the shared part's rows (the
   // VALU form of 8 rows up to 8, as shared_pick chooses)
   const int cols = shared_cols_per_wg(p.valu ? p.mt : (m <= 8 ? 8 : 16));

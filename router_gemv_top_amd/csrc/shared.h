@@ -282,9 +282,23 @@ constexpr int shared_cols_per_wg(int mt) { return shared_use_mfma(mt) ? shared_m
 // (from 5 rows at up to 128 experts, else 9..16). The shared part takes SMR
 // rows if given (8: the VALU form behind an MFMA router tile at 5..8 rows),
 // else MT (16 with MFMA).
+// The shared part's operands lead the arguments as scalars (router_wgs, wq,
+// ws, x, ldx, k, inter, m: b's), preloaded into scalar registers at dispatch
+// (the unit is built with eight preloaded arguments), so its workgroups'
+// first loads do not wait ~0.2 us for the argument block.
 template <int MT, int L, int KS, int SMR = 0>
-__global__ void __launch_bounds__(256) router_shared_kernel(GemvArgs a, SharedArgs b, int router_wgs) {
+__global__ void __launch_bounds__(256) router_shared_kernel(int router_wgs, const uint8_t* wq, const uint8_t* ws,
+                                                            const u16* x, int ldx, int k, int inter, int m,
+                                                            GemvArgs a, SharedArgs bk) {
   constexpr int SM = SMR ? SMR : (KS ? 16 : MT);
+  SharedArgs b = bk;
+  b.wq = wq;
+  b.ws = ws;
+  b.x = x;
+  b.ldx = ldx;
+  b.k = k;
+  b.inter = inter;
+  b.m = m;
   __shared__ float lds[(KS || shared_use_mfma(SM)) ? 4 * 256 : 4 * 2 * SM];
   if ((int)blockIdx.x < router_wgs) {
     const int t = xcd_tile(blockIdx.x, router_wgs);
