@@ -145,8 +145,9 @@ def build_shared(res: str, out: str):
     lines = ["# Router k-slice partials + shared-expert MXFP8 gate/up SwiGLU: kernel durations (rocprofv3)", "",
              "Workload: M = 1, 2, 4, 8, 16; router N = 128, K = 6144; shared expert gate_up 1536 x 6144",
              "(I = 768) MXFP8; router W and shared weights cold (rotating copies). One launch per call;",
-             "the instances are the M values (router tile `<MT, L, KS>`: VALU `<MT, L, 0>` for M <= 8,",
-             "the 16-row MFMA tile `<1, 1, KS>` for M = 16).", "",
+             "the instances are the M values (router tile `<MT, L, KS, SM>`: VALU `<MT, L, 0>` for M <= 4;",
+             "the 16-row MFMA tile with the shared part's 8-row VALU form, `<1, 1, KS, 8>`, for M = 5..8;",
+             "`<1, 1, KS>` with the shared part's MFMA form for M = 9..16).", "",
              "Command (from the repository root, results folder RES):", "",
              "    rocprofv3 --kernel-trace --stats --output-format csv -d RES/prof_shared -o shared "
              "-- python3 bench.py --only-shared",
