@@ -50,7 +50,11 @@ def units(trace: bool):
     tag = "trace" if trace else "rel"
     d = os.path.join(OBJ_DIR, tag)
     extra = ["-DRGT_TRACE"] if trace else []
-    out = [(os.path.join(CSRC, "rgt.hip"), os.path.join(d, "rgt.o"), extra)]
+    # the chain's kernels: their first eight arguments preloaded into scalar
+    # registers at dispatch (those that take scalars first; the rest read the
+    # argument block as before)
+    out = [(os.path.join(CSRC, "rgt.hip"), os.path.join(d, "rgt.o"),
+            extra + ["-mllvm", "-amdgpu-kernarg-preload-count=8"])]
     for norm in (0, 1):
         for nv in NV_BUCKETS:
             name = f"fused_norm_nv{nv}.o" if norm else f"fused_nv{nv}.o"
