@@ -154,9 +154,18 @@ int pow2_at_least(int v) {
 #endif
 
 // The stage-1 GEMM splits K over a workgroup's waves below this many
-// (row tile, 64-column group) pairs.
+// (row tile, 64-column group) pairs, and gives each wave two column tiles
+// from this many (row tile, 128-column group) pairs. Measured (N = 128,
+// K = 6144, top-8, I = 768): at M = 8 the K split beats one column tile a
+// wave (62 against 73 us); at M = 64 two column tiles a wave beat one (146-150
+// against 158-160 us) and the K split (157-159 us); at N = 896, K = 3584,
+// top-16, I = 384, M = 32 one column tile would be 3 us faster (124 against
+// 127-129 us).
 #ifndef RGT_STAGE1_KSPLIT_BELOW
 #define RGT_STAGE1_KSPLIT_BELOW 1024
+#endif
+#ifndef RGT_STAGE1_JT2_FROM
+#define RGT_STAGE1_JT2_FROM 512
 #endif
 
 // Batches with at least this many 128 x 128 output tiles use the GEMM.
@@ -1195,7 +1204,7 @@ rgt_status rgt_moe_stage1_swiglu(const uint8_t* a_q, const uint8_t* a_scale, con
   const unsigned tiles = (unsigned)(cap / 16);
   if ((int64_t)tiles * ((inter + 63) / 64) < RGT_STAGE1_KSPLIT_BELOW)
     hipLaunchKernelGGL(moe_stage1_ksplit_kernel, dim3(tiles, (unsigned)((inter + 15) / 16)), dim3(256), 0, stream, a);
-  else if ((int64_t)tiles * ((inter + 127) / 128) >= 512)
+  else if ((int64_t)tiles * ((inter + 127) / 128) >= RGT_STAGE1_JT2_FROM)
     hipLaunchKernelGGL(moe_stage1_kernel<2>, dim3(tiles, (unsigned)((inter + 127) / 128)), dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL(moe_stage1_kernel<1>, dim3(tiles, (unsigned)((inter + 63) / 64)), dim3(256), 0, stream, a);

@@ -167,14 +167,18 @@ __device__ __forceinline__ void stage1_tile(const Stage1Args& a, int p0, int e, 
 }
 
 // SwiGLU of a finished tile pair and the store of the pair rows. D lane l:
-// rows 4g + i, column r of each tile.
+// rows 4g + i, column r of each tile. Which rows are pairs comes from the
+// head's sorted ids (lane r of the wave holds row r's), as a wave ballot:
+// no second read of sorted_ids before the stores. The whole wave calls it.
 template <int JT>
-__device__ __forceinline__ void stage1_store(const Stage1Args& a, int p0, int j, const floatx4_t (&acc)[2 * JT]) {
+__device__ __forceinline__ void stage1_store(const Stage1Args& a, int p0, int j, const floatx4_t (&acc)[2 * JT],
+                                             int sid_r) {
   const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+  const u64 real = ballot64(sid_r < a.pairs);  // bit r (lanes 0..15): row p0 + r is a pair
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int p = p0 + 4 * g + i;
-    if (a.sorted_ids[p] < a.pairs) {
+    if ((real >> (4 * g + i)) & 1) {
 #pragma unroll
       for (int t = 0; t < JT; ++t) {
         const int col = j + 16 * t + r;
@@ -217,7 +221,7 @@ __global__ void __launch_bounds__(256) moe_stage1_kernel(Stage1Args a) {
   if (j >= a.inter) return;
   floatx4_t acc[2 * JT];
   stage1_tile<JT, 2>(a, p0, h.e, j, 0, a.k / 512, acc, h.sid_r);
-  stage1_store<JT>(a, p0, j, acc);
+  stage1_store<JT>(a, p0, j, acc, h.sid_r);
 }
 
 // Small grids: the four waves of a workgroup split K (load groups w*G/4 ..
@@ -246,7 +250,7 @@ __global__ void __launch_bounds__(256) moe_stage1_ksplit_kernel(Stage1Args a) {
       acc[0] += s_part[w][0][lane];
       acc[1] += s_part[w][1][lane];
     }
-    stage1_store<1>(a, p0, j, acc);
+    stage1_store<1>(a, p0, j, acc, h.sid_r);
   }
 }
 
