@@ -253,6 +253,12 @@ __device__ __forceinline__ u64 rt_clock() { return wall_clock64(); }
 
 // Phase stamps of the trace build (compile with -DRGT_TRACE): thread 0 of each
 // workgroup writes the real-time clock into trace[blockIdx.x * 16 + slot].
+// Slots of the one-launch kernel: 0 start; 1 wave 0's tile done; 4 the
+// workgroup's tile done; 3 tail entry; 11 first poll issued (norm path: rstd
+// published); 15 poll loop done; 5 logits gathered; 12 scores + bias; 13 top-k
+// selected; 14 selection ordered; 6 ids / weights written; 10 ids polled;
+// 8 positions ready; 7 layout written; 9 quant stores issued; 2 stores
+// acknowledged.
 #ifdef RGT_TRACE
 #define RGT_STAMP(trace, slot)                                                         \
   do {                                                                                 \

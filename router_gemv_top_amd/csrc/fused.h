@@ -216,14 +216,8 @@ __device__ __forceinline__ bool gather_logits(const FusedArgs& a, int r0, int ro
     u32x4_t va[NL];
     if (poller) issue(va);
     during();  // other work while the first poll is in flight
-    RGT_STAMP(a.trace, 3);
-#ifdef RGT_TRACE
-    int polls = 0;
-#endif
+    RGT_STAMP(a.trace, 11);
     while (poller) {
-#ifdef RGT_TRACE
-      ++polls;
-#endif
       if (ready(va)) { take(va); break; }
       issue(va);
       if (rt_clock() - t0 > a.budget) {
@@ -233,12 +227,6 @@ __device__ __forceinline__ bool gather_logits(const FusedArgs& a, int r0, int ro
       }
     }
     RGT_STAMP(a.trace, 15);
-#ifdef RGT_TRACE
-    if (t == 0 && a.trace) {  // poll rounds and the gather's start time
-      a.trace[blockIdx.x * 16 + 10] = (u64)polls;
-      a.trace[blockIdx.x * 16 + 11] = t0;
-    }
-#endif
   }
   __syncthreads();
   return s_bad == 0u;
@@ -739,7 +727,6 @@ template <int NV, bool ONE, class Quant>
 __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 tag, int role, bool have_unit, int unit,
                                            Quant&& quant, const float (&bv)[NV], bool gate_here, bool layout_here,
                                            bool quant_wg) {
-  RGT_STAMP(a.trace, 9);
   __shared__ __align__(16) u64 s_mask[4][NV];
   const GemvArgs& g = a.g;
   const int m = g.m, n = g.n, k = a.topk, B = a.block;
@@ -792,7 +779,6 @@ __device__ __forceinline__ void small_tail(const FusedArgs& a, int* smem, u32 ta
         scrub_window(a, tag, lane, 64u);
       }
       if (!(do_ids || do_w || do_off)) return;
-      RGT_STAMP(a.trace, 6);
       float sv[2];
       const bool ok = g.s_count <= 4 ? wave_gather_pairs<4>(a, tag, 0, sv, [] {})
                                      : wave_gather_pairs<8>(a, tag, 0, sv, [] {});
@@ -1246,7 +1232,7 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
     if (!participant) return;
     if (!poll_ids_any(a, P, tag, s_e, p0, s_cnt, s_pre)) return;
   }
-  RGT_STAMP(a.trace, 7);
+  RGT_STAMP(a.trace, 10);
   // Every workgroup's tag is read (see the top of this file): advance the
   // epoch for the next call (large mode, or small mode without a spare gate
   // workgroup).
@@ -1268,7 +1254,7 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
     const int tok = p / k;
     if (q >= 0 && (tok * cpr) >> a.upw_log == role) sorted_ids[q] = p;
   }
-  RGT_STAMP(a.trace, 3);
+  RGT_STAMP(a.trace, 7);
   const u32 scales4 = pack_scales(sb_in);  // all lanes: DPP reads neighbouring lanes
   if (have_unit)
     store_unit(RGT_OUT(a_q), RGT_OUT(a_scale), g.k, k, unit, OffsetPos{s_pos, p0}, codes_in, scales4, a.cpr_magic,
