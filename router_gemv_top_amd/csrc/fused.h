@@ -1150,9 +1150,10 @@ __device__ __forceinline__ void fused_tail(const FusedArgs& a, int* smem, u32 ta
     if (row >= 0 && row < m && !participant && g.s_count == 1 && (n & 1) == 0) {
       // A spare row workgroup over more than 256 experts with one k-slice:
       // wave 0 alone gathers the row into registers (lane l: experts
-      // [l*NV, l*NV + NV)), selects with k rounds of a wave maximum (lane j
-      // ends with slot j) and publishes the ids; no LDS pass of the row, no
-      // barrier.
+      // [l*NV, l*NV + NV)), selects (lane j ends with slot j: the keys that
+      // reach the k-th largest lane maximum, one a lane, by threshold; k
+      // rounds of a wave maximum when more than 64 reach it) and publishes
+      // the ids; no LDS pass of the row, no barrier.
       if (wave != 0) return;
       float sv[NV];
       if (!wave_gather_row1<NV>(a, tag, row, sv)) return;

@@ -324,6 +324,66 @@ __device__ __forceinline__ void wave_topk_threshold(const u32 (&key)[NV], int k,
   wave_select_slots<NV, KMAX>(key, sel, slot, s_c);
 }
 
+#ifndef RGT_SELECT_PRUNED
+#define RGT_SELECT_PRUNED 1
+#endif
+// Selection for many keys a lane (NV > 4) by pruning first. L, the k-th
+// largest of the 64 lane maxima, is reached by at least k keys, so the k-th
+// largest key, and with it every selected key, is at least L. The keys >= L
+// are moved to LDS in expert order (lane l's after those of the lanes below
+// it, each lane's in slot order) and, when at most 64 of them, selected one
+// a lane with the threshold selection and its slots: the same set and order
+// (descending key, equal keys by lower expert) as over all keys. Returns
+// true (nothing selected) when more than 64 keys reach L or L is 0 (absent
+// experts among the candidates); the caller then selects over all keys.
+// s_w: 256 u32 of LDS owned by the calling wave (8-byte aligned).
+template <int NV>
+__device__ __forceinline__ bool select_pruned(const u32 (&key)[NV], int k, u32& my_key, int& my_id, u32* s_w) {
+  const int lane = lane_id();
+  u32 mx = key[0];
+#pragma unroll
+  for (int i = 1; i < NV; ++i) mx = umax(mx, key[i]);
+  bool lsel[1];
+  const u32 mk[1] = {mx};
+  wave_threshold_select<1>(mk, k, lsel);
+  const u32 L = ~wave_max_u32(lsel[0] ? ~mx : 0u);  // the smallest selected lane maximum
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) cnt += key[i] >= L ? 1 : 0;
+  const int incl = wave_inclusive_scan(cnt);
+  const int total = __builtin_amdgcn_readlane(incl, 63);
+  if (L == 0u || total > 64) return true;  // uniform
+  u32* const s_key = s_w;        // [64] candidate keys
+  u32* const s_id = s_w + 64;    // [64] candidate experts
+  u64* const s_c = reinterpret_cast<u64*>(s_w + 128);  // [32] slot ranks
+  int p = incl - cnt;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    if (key[i] >= L) {
+      s_key[p] = key[i];
+      s_id[p] = (u32)(lane * NV + i);
+      ++p;
+    }
+  // one wave: the LDS writes above land before these reads
+  const u32 ck[1] = {lane < total ? s_key[lane] : 0u};
+  const u32 cid = s_id[lane];
+  bool sel[1];
+  int slot[1];
+  if (k <= 8) wave_topk_threshold<1, 8>(ck, k, sel, slot, s_c);
+  else if (k <= 16) wave_topk_threshold<1, 16>(ck, k, sel, slot, s_c);
+  else wave_topk_threshold<1, 32>(ck, k, sel, slot, s_c);
+  // slot j's key and expert to lane j (s_key / s_id are read above: reused)
+  if (sel[0]) {
+    s_key[slot[0]] = ck[0];
+    s_id[slot[0]] = cid;
+  }
+  if (lane < k) {
+    my_key = s_key[lane];
+    my_id = (int)s_id[lane];
+  }
+  return false;
+}
+
 // Selection only for R rows at once (R = 1 or 2): lane j < k ends with the
 // j-th expert of row r in my_id[r] and its score key in my_key[r]. s_slot:
 // 64*R ints of LDS owned by the calling wave (16-byte aligned).
@@ -346,8 +406,16 @@ __device__ __forceinline__ void wave_select_rows(const float (&sv)[R][NV], int n
   if constexpr (NV == 2) {
     select_fast2<R>(key, k, my_key, my_id, retry, s_slot);
   } else {
+#if RGT_SELECT_PRUNED
+    if constexpr (NV > 4) {
+      __shared__ __align__(16) u32 s_prune[4][256];
 #pragma unroll
-    for (int r = 0; r < R; ++r) retry[r] = select_fast_sorted<NV>(key[r], k, my_key[r], my_id[r], s_slot + 64 * r);
+      for (int r = 0; r < R; ++r) retry[r] = select_pruned<NV>(key[r], k, my_key[r], my_id[r], s_prune[threadIdx.x >> 6]);
+    }
+#endif
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (retry[r]) retry[r] = select_fast_sorted<NV>(key[r], k, my_key[r], my_id[r], s_slot + 64 * r);
   }
 #pragma unroll
   for (int r = 0; r < R; ++r)

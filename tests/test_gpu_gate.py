@@ -78,6 +78,35 @@ def test_gate_skewed_bias(R):
     assert len(np.unique(ids)) <= 10 + 8 * 64
 
 
+@pytest.mark.parametrize("n,k", [(896, 16), (1024, 32), (320, 8)])
+def test_gate_many_keys_a_lane_paths(R, n, k):
+    """Over more than 256 experts (several keys a lane, expert e in lane
+    e // ceil(n / 64)) the selection prunes to the keys reaching the k-th
+    largest lane maximum; rows that leave more than 64 such keys (descending
+    lane blocks, all equal, mostly signed zeros) take the fallback, rows with
+    few (random, a tie at the threshold across lanes) the pruned path."""
+    say(f"gate many keys a lane N={n} k={k}")
+    nv = -(-n // 64)
+    rng = np.random.default_rng(n)
+    lanes = np.arange(n) // nv
+    rows = []
+    rows.append(100.0 - lanes + rng.uniform(0.0, 0.5, n))            # > 64 candidates
+    rows.append(np.full(n, 1.5))                                      # all tied
+    rows.append(rng.standard_normal(n))                               # pruned
+    r = rng.uniform(0.0, 1.0, n)
+    r[(np.arange(k + 4) * (nv + 3) + 2) % n] = 5.0                    # k + 4 tied keys in distinct lanes
+    rows.append(r)
+    z = rng.choice(np.array([-0.0, 0.0], np.float32), n)
+    z[rng.choice(n, 10, replace=False)] = rng.uniform(1.0, 2.0, 10)   # few positives, the rest +-0
+    rows.append(z)
+    r = rng.uniform(0.0, 1.0, n)
+    r[lanes == lanes[-1]] = 7.0                                       # the top keys all in the last lane
+    rows.append(r)
+    logits = np.stack(rows).astype(np.float32)
+    check_gate(R, logits, k)
+    check_gate(R, logits, k, gen_bias(n, seed=5))
+
+
 def test_gate_extreme_spread(R):
     say("gate with far-apart scores (weights underflow to 0)")
     logits = np.zeros((4, 128), np.float32)
