@@ -496,9 +496,10 @@ __device__ __forceinline__ bool poll_ids_any(const FusedArgs& a, int P, u32 tag,
 // Owner form of the top-k of one row of logits held in LDS, by the calling
 // wave: for each of this lane's NV experts (lane-major, expert lane*NV + i)
 // whether it is selected, its slot and its score key. bv: this lane's bias
-// values. Up to four experts a lane the threshold selection; above, k rounds
-// of a wave maximum whose slot-ordered winners are handed to their owners
-// through s_flag (n ints of LDS owned by the calling wave). With slots false
+// values. Up to four experts a lane the threshold selection; above, the
+// pruned selection (k rounds of a wave maximum when it cannot prune) whose
+// slot-ordered winners are handed to their owners through s_flag (n ints of
+// LDS owned by the calling wave). With slots false
 // (a caller that only needs the selected set, one position per winner) the
 // threshold selection numbers the winners in expert order instead of by rank.
 template <int NV>
@@ -557,8 +558,8 @@ __device__ __forceinline__ void row_topk_owner(const FusedArgs& a, const float* 
 // lane-major (expert lane*NV + i), plus the bias (bv: this lane's bias values,
 // loaded at the start of the kernel). emit(j, e, key) runs once for each of
 // the k selected experts, in the lane holding it: slot j, expert e, score key.
-// Up to four experts a lane the threshold selection; above, k rounds of a
-// wave maximum (one expert per round, slot order).
+// Up to four experts a lane the threshold selection; above, the pruned
+// selection (k rounds of a wave maximum when it cannot prune), slot order.
 template <int NV, class Emit>
 __device__ __forceinline__ void row_topk(const FusedArgs& a, const float* row, const float (&bv)[NV], Emit&& emit) {
   const int n = a.g.n, k = a.topk, lane = lane_id(), c0 = lane * NV;

@@ -14,7 +14,10 @@
 // holding it. Each of the k rounds takes the wave maximum; the lowest lane
 // holding it, at its lowest such slot, is the lowest expert index with that
 // score, so one ballot and one find-first-set name the winner. Only the
-// winner's key is cleared; every lane rescans its slots (no branches).
+// winner's key is cleared; every lane rescans its slots (no branches). That
+// exact selection is the fallback of the faster ones below (a threshold
+// bisection for up to four keys a lane, pruning to the keys that reach the
+// k-th largest lane maximum above), which give the same ids in the same order.
 #pragma once
 
 #include "device.h"
